@@ -1,0 +1,15 @@
+"""fp64 CPU oracle for the gated delta-rule recurrence.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py``, never by the product path.  It shares no code with the
+HIP library or its binding.
+
+Parity pins (see ``tests/test_oracle_pins.py``): brute-force causal linear attention, the
+gated-linear-attention closed form, exact memory with unit keys, the per-step key-readback
+identity, a hand-worked 2x2 example, the explicit matrix forms of the scalar, KDA and
+FG2-GDN updates, the gradient-step reading of the delta rule, linearity, state resume, the
+norm bound and the dk = dv = 1 closed form.  No function here is "parity unpinned".
+"""
+from .recurrence import as_f64, decode_step, recurrence
+
+__all__ = ["recurrence", "decode_step", "as_f64"]

@@ -1,0 +1,140 @@
+"""fp64 CPU oracle for the gated delta-rule recurrence.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path (the HIP library, its C ABI or the
+Python binding in ``gated_delta_rule_dr_amd``) imports, links or calls this module; only the
+test suite, the smoke check in ``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py``
+use it.  It shares no code with the GPU path.
+
+What it computes
+----------------
+Per batch ``b`` and head ``h`` the state is a fixed-size associative memory S (dk x dv) that
+replaces a growing key/value cache ("KronLSTM ... delta rule", section "The problem": linear
+attention keeps a fixed-size matrix, the delta rule first subtracts what is already associated
+with the key and then writes the new value).  One token step, in the general form that covers
+every variant on the pages:
+
+    S'  = Diag(a_t) S_{t-1}                      (decay, a_t = exp(log_decay_t))
+    S_t = S' - (e_t * k_t) (k_t^T S') + k_t (w_t * v_t)^T
+    o_t = S_t^T q_t
+
+* erase gate e_t acts on the key side and write gate w_t on the value side, with the decay
+  inherited from KDA ("Gated DeltaNet-2: decoupling erase and write in linear attention",
+  section "Gated DeltaNet-2: the solution", gate table; "FG2-GDN", section 2, FG2-GDN+ variant
+  with separate erase and write strengths).
+* KDA: channel decay vector, one scalar beta used for both erase and write, giving
+  S_t = (I - beta k k^T) Diag(a_t) S_{t-1} + beta k v^T ("FG2-GDN", section 1 and section 2
+  update rule with a scalar beta).
+* scalar-gate Gated DeltaNet: a_t = alpha_t * 1; the scalar commutes with (I - beta k k^T).
+* the output reads the state after the token's own write (o_t = S_t^T q_t).
+
+Readings taken where the pages are silent (each is listed with its reason in the design notes):
+decay is applied before the erase and the write; the decay is passed in log space and
+exponentiated here in fp64 from the stored fp32 value; no query scaling and no key
+normalisation happen inside the operation (the caller supplies normalised k); ``write=None``
+means the write gate equals the erase gate.
+
+Precision: every input is upcast to fp64 as stored (bf16 or fp32 values), and all arithmetic
+is fp64.  The loop is the plain token-by-token definition; it is vectorised only across the
+independent (b, h) pairs.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["recurrence", "decode_step", "as_f64"]
+
+
+def as_f64(x):
+    """Return ``x`` as a float64 numpy array (torch tensors are moved to the CPU first)."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # a torch tensor; keep torch optional for the oracle itself
+        import torch
+
+        return x.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _gate(g, B, T, H, d, name):
+    """Broadcast a per-head gate [B,T,H] or per-channel gate [B,T,H,d] to [B,H,T,d|1]."""
+    if g.ndim == 3:
+        if g.shape != (B, T, H):
+            raise ValueError(f"{name}: per-head gate must be [B,T,H], got {g.shape}")
+        return np.transpose(g, (0, 2, 1))[..., None]
+    if g.ndim == 4:
+        if g.shape != (B, T, H, d):
+            raise ValueError(f"{name}: per-channel gate must be [B,T,H,{d}], got {g.shape}")
+        return np.transpose(g, (0, 2, 1, 3))
+    raise ValueError(f"{name}: gate must have 3 or 4 dims, got {g.ndim}")
+
+
+def recurrence(q, k, v, log_decay, erase, write=None, S0=None, return_states=False):
+    """Run the general gated delta-rule recurrence token by token in fp64.
+
+    Args:
+      q, k: [B, T, H, dk];  v: [B, T, H, dv]
+      log_decay: log a_t <= 0, [B, T, H] (scalar per head) or [B, T, H, dk] (per channel)
+      erase: e_t, [B, T, H] or [B, T, H, dk]
+      write: w_t, [B, T, H] or [B, T, H, dv]; ``None`` means the write gate is the erase gate
+        (then a per-channel erase gate needs dk == dv)
+      S0: initial state [B, H, dk, dv] or ``None`` for zeros
+      return_states: also return every S_t as [B, H, T, dk, dv] (small cases only)
+
+    Returns:
+      (o [B, T, H, dv], S_T [B, H, dk, dv]) as float64, plus the states if requested.
+    """
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    log_decay, erase, write, S0 = as_f64(log_decay), as_f64(erase), as_f64(write), as_f64(S0)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != (B, T, H, dk) or v.shape[:3] != (B, T, H):
+        raise ValueError("q, k, v shapes disagree")
+    if write is None:
+        write = erase
+        if write.ndim == 4 and dk != dv:
+            raise ValueError("write=None with a per-channel erase gate needs dk == dv")
+
+    a = np.exp(_gate(log_decay, B, T, H, dk, "log_decay"))  # [B,H,T,dk|1]
+    e = _gate(erase, B, T, H, dk, "erase")
+    w = _gate(write, B, T, H, dv, "write")
+    qh = np.transpose(q, (0, 2, 1, 3))  # [B,H,T,dk]
+    kh = np.transpose(k, (0, 2, 1, 3))
+    vh = np.transpose(v, (0, 2, 1, 3))
+
+    S = np.zeros((B, H, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64, copy=True)
+    if S.shape != (B, H, dk, dv):
+        raise ValueError(f"S0 must be [B,H,dk,dv]={B, H, dk, dv}, got {S.shape}")
+    o = np.empty((B, H, T, dv))
+    states = np.empty((B, H, T, dk, dv)) if return_states else None
+
+    for t in range(T):
+        kt = kh[:, :, t, :]  # [B,H,dk]
+        S = a[:, :, t, :][..., :, None] * S  # S' = Diag(a_t) S_{t-1}
+        m = np.matmul(kt[..., None, :], S)[..., 0, :]  # k_t^T S'        [B,H,dv]
+        u = e[:, :, t, :] * kt  # erase acts on the key side   [B,H,dk]
+        vw = w[:, :, t, :] * vh[:, :, t, :]  # write acts on the value side [B,H,dv]
+        S = S - u[..., :, None] * m[..., None, :] + kt[..., :, None] * vw[..., None, :]
+        o[:, :, t, :] = np.matmul(qh[:, :, t, :][..., None, :], S)[..., 0, :]  # S_t^T q_t
+        if return_states:
+            states[:, :, t] = S
+
+    o = np.transpose(o, (0, 2, 1, 3))
+    if return_states:
+        return o, S, states
+    return o, S
+
+
+def decode_step(q, k, v, log_decay, erase, write, S):
+    """One token of the recurrence for a batch of independent sequences.
+
+    Args use the single-token layout [N, H, d] (gates [N, H] or [N, H, d]); S is [N, H, dk, dv].
+    Returns (o [N, H, dv], S_new [N, H, dk, dv]) in fp64; the input state is not modified.
+    """
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    log_decay, erase, write = as_f64(log_decay), as_f64(erase), as_f64(write)
+
+    def tok(x):
+        return None if x is None else x[:, None]
+
+    o, S_new = recurrence(tok(q), tok(k), tok(v), tok(log_decay), tok(erase), tok(write), S)
+    return o[:, 0], S_new
