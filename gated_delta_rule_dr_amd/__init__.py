@@ -1,0 +1,152 @@
+"""Gated delta-rule recurrence on MI355X (gfx950): Python binding of libdr.
+
+``chunk_fwd`` is the prefill / training forward and ``decode_step`` the single-token update;
+both call the C ABI (include/dr.h) on torch's current HIP stream.  Tensors must live on the
+GPU and be contiguous; the functions only check and marshal arguments, allocate outputs with
+torch and pass raw device pointers.  No step of the recurrence runs in Python, and there is
+no CPU fallback: without the built library every call raises.
+
+The operation (per batch b and head h, state S of dk x dv in fp32):
+    S' = Diag(a_t) S,   S = S' - (e_t * k_t)(k_t^T S') + k_t (w_t * v_t)^T,   o_t = S^T q_t
+with a_t = exp(log_decay_t).  Gates are per head ([B, T, H]) or per channel ([B, T, H, d]);
+``write=None`` means the write gate is the erase gate.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _abi
+
+__all__ = ["chunk_fwd", "decode_step", "workspace_bytes", "abi_version", "DrError"]
+
+DrError = _abi.DrError
+
+
+def abi_version() -> int:
+    return _abi.lib().dr_abi_version()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check_tensor(name, t, dtypes, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on the GPU with the other inputs (got {t.device})")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dtype_code(dt):
+    if dt == torch.float32:
+        return _abi.DR_F32
+    if dt == torch.bfloat16:
+        return _abi.DR_BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _gate_kind(name, g, lead, d):
+    if tuple(g.shape) == lead:
+        return _abi.DR_GATE_HEAD
+    if tuple(g.shape) == lead + (d,):
+        return _abi.DR_GATE_CHANNEL
+    raise ValueError(f"{name} must have shape {lead} or {lead + (d,)}, got {tuple(g.shape)}")
+
+
+def _desc(B, T, H, dk, dv, chunk, qkv_dtype, o_dtype, log_decay, erase, write, lead):
+    d = _abi.DrDesc()
+    d.B, d.T, d.H, d.dk, d.dv, d.chunk = B, T, H, dk, dv, chunk
+    d.qkv_dtype = _dtype_code(qkv_dtype)
+    d.o_dtype = _dtype_code(o_dtype)
+    d.decay_kind = _gate_kind("log_decay", log_decay, lead, dk)
+    d.erase_kind = _gate_kind("erase", erase, lead, dk)
+    if write is None:
+        d.write_is_erase, d.write_kind = 1, d.erase_kind
+    else:
+        d.write_is_erase, d.write_kind = 0, _gate_kind("write", write, lead, dv)
+    return d
+
+
+def workspace_bytes(desc) -> int:
+    return int(_abi.lib().dr_chunk_fwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def chunk_fwd(q, k, v, log_decay, erase, write=None, S0=None, *, chunk=64,
+              o_dtype=torch.float32, out=None, S_T=None, return_state=True):
+    """Chunked forward over T tokens.
+
+    q, k: [B, T, H, dk]; v: [B, T, H, dv] (bf16 or fp32, same dtype); log_decay, erase:
+    [B, T, H] or [B, T, H, dk] fp32; write: None, [B, T, H] or [B, T, H, dv] fp32;
+    S0: None or [B, H, dk, dv] fp32.  ``chunk=1`` selects the token-by-token kernel.
+    Returns (o [B, T, H, dv], S_T [B, H, dk, dv] or None).  ``out`` / ``S_T`` may supply
+    preallocated outputs (S_T may be S0 itself for an in-place carry)."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, (torch.float32, torch.bfloat16), dev)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B, T, H, dk] and v [B, T, H, dv]")
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    for name, t in (("log_decay", log_decay), ("erase", erase), ("write", write), ("S0", S0)):
+        if t is not None:
+            _check_tensor(name, t, (torch.float32,), dev)
+    desc = _desc(B, T, H, dk, dv, chunk, q.dtype, o_dtype, log_decay, erase, write, (B, T, H))
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=o_dtype, device=dev)
+    else:
+        _check_tensor("out", out, (o_dtype,), dev)
+    if S_T is None and return_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _check_tensor("S_T", S_T, (torch.float32,), dev)
+    ws_n = workspace_bytes(desc)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    st = _abi.lib().dr_chunk_fwd(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(erase),
+        _ptr(write), _ptr(S0), _ptr(out), _ptr(S_T), _ptr(ws), ws_n, _stream(),
+    )
+    _abi.check("dr_chunk_fwd", st)
+    return out, S_T
+
+
+def decode_step(q, k, v, log_decay, erase, write=None, *, S, o=None, o_dtype=torch.float32):
+    """One decode token for N sequences: q, k [N, H, dk]; v [N, H, dv]; gates [N, H] or
+    [N, H, d]; S [N, H, dk, dv] fp32 updated in place.  Returns o [N, H, dv]."""
+    dev = S.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, (torch.float32, torch.bfloat16), dev)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    _check_tensor("S", S, (torch.float32,), dev)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("q, k must be [N, H, dk] and v [N, H, dv]")
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    if tuple(S.shape) != (N, H, dk, dv):
+        raise ValueError(f"S must be [N, H, dk, dv] = {(N, H, dk, dv)}")
+    for name, t in (("log_decay", log_decay), ("erase", erase), ("write", write)):
+        if t is not None:
+            _check_tensor(name, t, (torch.float32,), dev)
+    desc = _desc(N, 1, H, dk, dv, 0, q.dtype, o_dtype, log_decay, erase, write, (N, H))
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=o_dtype, device=dev)
+    else:
+        _check_tensor("o", o, (o_dtype,), dev)
+    st = _abi.lib().dr_decode_step(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(erase),
+        _ptr(write), _ptr(S), _ptr(o), _stream(),
+    )
+    _abi.check("dr_decode_step", st)
+    return o

@@ -1,0 +1,211 @@
+// C-ABI layer of libdr: argument validation, path selection and launch.
+//
+// Validation is synchronous and touches no HIP API, so every error path can be exercised on
+// a host without a GPU; nothing is enqueued unless all checks pass.
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dr.h"
+#include "dr_internal.h"
+
+namespace {
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+};
+
+Range range_of(const void* p, uint64_t bytes) {
+  Range r;
+  if (p != nullptr && bytes > 0) {
+    r.lo = reinterpret_cast<uintptr_t>(p);
+    r.hi = r.lo + bytes;
+  }
+  return r;
+}
+
+bool overlaps(const Range& a, const Range& b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_width(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Byte extents of every array of a problem.
+struct Extents {
+  uint64_t qk, v, o, decay, erase, write, state;
+};
+
+// Element counts are bounded so that every index the kernels form fits in int64 and every
+// per-(b,h) offset fits in int32 arithmetic where the kernels use it.
+constexpr uint64_t kMaxElems = uint64_t(1) << 40;
+
+int check_desc(const dr_desc* d, bool decode, Extents* ex) {
+  if (d == nullptr) return DR_E_NULL;
+  if (d->B < 1 || d->H < 1 || d->T < 0 || d->dk < 1 || d->dv < 1) return DR_E_SHAPE;
+  if (decode && d->T != 1) return DR_E_SHAPE;
+  if (d->qkv_dtype != DR_F32 && d->qkv_dtype != DR_BF16) return DR_E_DTYPE;
+  if (d->o_dtype != DR_F32 && d->o_dtype != DR_BF16) return DR_E_DTYPE;
+  auto kind_ok = [](int k) { return k == DR_GATE_HEAD || k == DR_GATE_CHANNEL; };
+  if (!kind_ok(d->decay_kind) || !kind_ok(d->erase_kind)) return DR_E_DTYPE;
+  if (!d->write_is_erase && !kind_ok(d->write_kind)) return DR_E_DTYPE;
+  if (!supported_width(d->dk) || !supported_width(d->dv)) return DR_E_UNSUPPORTED;
+  if (!decode && d->chunk != 0 && d->chunk != 1 && d->chunk != 64) return DR_E_UNSUPPORTED;
+  if (d->write_is_erase && d->erase_kind == DR_GATE_CHANNEL && d->dk != d->dv) return DR_E_SHAPE;
+
+  const uint64_t B = uint64_t(d->B), T = uint64_t(d->T), H = uint64_t(d->H);
+  const uint64_t dk = uint64_t(d->dk), dv = uint64_t(d->dv);
+  const uint64_t bth = B * T * H;  // < 2^93 impossible: each factor < 2^31, check stepwise
+  if (B * H > kMaxElems || (T > 0 && bth / T != B * H) || bth > kMaxElems / 128)
+    return DR_E_SHAPE;
+  if (B * H * dk * dv > kMaxElems) return DR_E_SHAPE;
+  const uint64_t qkv_sz = d->qkv_dtype == DR_BF16 ? 2 : 4;
+  const uint64_t o_sz = d->o_dtype == DR_BF16 ? 2 : 4;
+  ex->qk = bth * dk * qkv_sz;
+  ex->v = bth * dv * qkv_sz;
+  ex->o = bth * dv * o_sz;
+  ex->decay = bth * (d->decay_kind == DR_GATE_CHANNEL ? dk : 1) * 4;
+  ex->erase = bth * (d->erase_kind == DR_GATE_CHANNEL ? dk : 1) * 4;
+  if (d->write_is_erase)
+    ex->write = 0;
+  else
+    ex->write = bth * (d->write_kind == DR_GATE_CHANNEL ? dv : 1) * 4;
+  ex->state = B * H * dk * dv * 4;
+  return DR_OK;
+}
+
+// A required array must be non-null unless it is empty; every non-null pointer is 16-byte
+// aligned.
+int check_ptr(const void* p, uint64_t bytes, bool required) {
+  if (p == nullptr) return (required && bytes > 0) ? DR_E_NULL : DR_OK;
+  return aligned16(p) ? DR_OK : DR_E_ALIGN;
+}
+
+dr::Problem make_problem(const dr_desc* d, const void* q, const void* k, const void* v,
+                         const float* log_decay, const float* erase, const float* write,
+                         const float* S0, void* o, float* S_T) {
+  dr::Problem p;
+  p.B = d->B;
+  p.T = d->T;
+  p.H = d->H;
+  p.dk = d->dk;
+  p.dv = d->dv;
+  p.qkv_bf16 = d->qkv_dtype == DR_BF16;
+  p.o_bf16 = d->o_dtype == DR_BF16;
+  p.decay_channel = d->decay_kind == DR_GATE_CHANNEL;
+  p.erase_channel = d->erase_kind == DR_GATE_CHANNEL;
+  p.write_channel = d->write_is_erase ? p.erase_channel : (d->write_kind == DR_GATE_CHANNEL);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.log_decay = log_decay;
+  p.erase = erase;
+  p.write = d->write_is_erase ? erase : write;
+  p.S0 = S0;
+  p.o = o;
+  p.S_T = S_T;
+  return p;
+}
+
+int launched(hipError_t launch_err) {
+  if (launch_err != hipSuccess) return DR_E_HIP;
+  return hipGetLastError() == hipSuccess ? DR_OK : DR_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dr_abi_version(void) { return DR_ABI_VERSION; }
+
+const char* dr_status_str(int status) {
+  switch (status) {
+    case DR_OK: return "ok";
+    case DR_E_NULL: return "a required pointer or the descriptor is NULL";
+    case DR_E_SHAPE: return "invalid or overflowing size";
+    case DR_E_DTYPE: return "unknown dtype or gate kind";
+    case DR_E_ALIGN: return "pointer not 16-byte aligned";
+    case DR_E_ALIAS: return "an output overlaps an input";
+    case DR_E_UNSUPPORTED: return "combination not supported by this build";
+    case DR_E_WORKSPACE: return "workspace missing or too small";
+    case DR_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t dr_chunk_fwd_workspace_bytes(const dr_desc* desc) {
+  Extents ex;
+  if (check_desc(desc, false, &ex) != DR_OK) return 0;
+  return 0;
+}
+
+int dr_chunk_fwd(const dr_desc* d, const void* q, const void* k, const void* v,
+                 const float* log_decay, const float* erase, const float* write,
+                 const float* S0, void* o, float* S_T, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  Extents ex;
+  int st = check_desc(d, false, &ex);
+  if (st != DR_OK) return st;
+  const bool need_write = !d->write_is_erase;
+  if ((st = check_ptr(q, ex.qk, true)) || (st = check_ptr(k, ex.qk, true)) ||
+      (st = check_ptr(v, ex.v, true)) || (st = check_ptr(log_decay, ex.decay, true)) ||
+      (st = check_ptr(erase, ex.erase, true)) ||
+      (st = check_ptr(need_write ? write : nullptr, ex.write, need_write)) ||
+      (st = check_ptr(S0, ex.state, false)) || (st = check_ptr(o, ex.o, true)) ||
+      (st = check_ptr(S_T, ex.state, false)) || (st = check_ptr(workspace, workspace_bytes, false)))
+    return st;
+  if (workspace_bytes < dr_chunk_fwd_workspace_bytes(d)) return DR_E_WORKSPACE;
+
+  const Range rin[] = {range_of(q, ex.qk),         range_of(k, ex.qk),
+                       range_of(v, ex.v),          range_of(log_decay, ex.decay),
+                       range_of(erase, ex.erase),  range_of(need_write ? write : nullptr, ex.write),
+                       range_of(S0, ex.state)};
+  const Range ro = range_of(o, ex.o), rs = range_of(S_T, ex.state);
+  for (const Range& r : rin)
+    if (overlaps(ro, r)) return DR_E_ALIAS;
+  if (overlaps(ro, rs)) return DR_E_ALIAS;
+  for (int i = 0; i < 6; ++i)
+    if (overlaps(rs, rin[i])) return DR_E_ALIAS;
+  if (S0 != nullptr && S_T != nullptr && S0 != S_T && overlaps(rs, rin[6])) return DR_E_ALIAS;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (d->T == 0) {
+    if (S_T == nullptr || S_T == S0) return DR_OK;
+    return launched(dr::launch_state_copy(S0, S_T, int64_t(ex.state / 4), s));
+  }
+  dr::Problem p = make_problem(d, q, k, v, log_decay, erase, write, S0, o, S_T);
+  const bool mfma_path = d->qkv_dtype == DR_BF16 && d->dk == 128 && d->dv == 128 && d->chunk != 1;
+  if (mfma_path) return launched(dr::launch_chunk128(p, s));
+  return launched(dr::launch_recurrent(p, s));
+}
+
+int dr_decode_step(const dr_desc* d, const void* q, const void* k, const void* v,
+                   const float* log_decay, const float* erase, const float* write, float* S,
+                   void* o, void* stream) {
+  Extents ex;
+  int st = check_desc(d, true, &ex);
+  if (st != DR_OK) return st;
+  const bool need_write = !d->write_is_erase;
+  if ((st = check_ptr(q, ex.qk, true)) || (st = check_ptr(k, ex.qk, true)) ||
+      (st = check_ptr(v, ex.v, true)) || (st = check_ptr(log_decay, ex.decay, true)) ||
+      (st = check_ptr(erase, ex.erase, true)) ||
+      (st = check_ptr(need_write ? write : nullptr, ex.write, need_write)) ||
+      (st = check_ptr(S, ex.state, true)) || (st = check_ptr(o, ex.o, true)))
+    return st;
+  const Range rin[] = {range_of(q, ex.qk),        range_of(k, ex.qk),
+                       range_of(v, ex.v),         range_of(log_decay, ex.decay),
+                       range_of(erase, ex.erase), range_of(need_write ? write : nullptr, ex.write)};
+  const Range ro = range_of(o, ex.o), rs = range_of(S, ex.state);
+  for (const Range& r : rin)
+    if (overlaps(ro, r) || overlaps(rs, r)) return DR_E_ALIAS;
+  if (overlaps(ro, rs)) return DR_E_ALIAS;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  dr::Problem p = make_problem(d, q, k, v, log_decay, erase, write, S, o, S);
+  if (d->dk == 128 && d->dv == 128) return launched(dr::launch_decode128(p, s));
+  return launched(dr::launch_recurrent(p, s));
+}
+
+}  // extern "C"

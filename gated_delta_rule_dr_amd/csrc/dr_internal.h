@@ -1,0 +1,43 @@
+// Internal launch interface between the C-ABI layer (dr_api.cpp) and the kernels.
+// Every launcher enqueues on `stream`, never synchronises and returns the hipError_t of the
+// launch.  Arguments have been validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dr {
+
+// One problem, already validated.  Gate pointers may be per head or per channel.
+struct Problem {
+  int B, T, H, dk, dv;
+  int qkv_bf16;        // 1: q, k, v are bf16; 0: fp32
+  int o_bf16;          // 1: o is bf16; 0: fp32
+  int decay_channel;   // log_decay is [B,T,H,dk]
+  int erase_channel;   // erase is [B,T,H,dk]
+  int write_channel;   // write is [B,T,H,dv]
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_decay;
+  const float* erase;
+  const float* write;  // == erase when the write gate is the erase gate
+  const float* S0;     // may be null (zeros)
+  void* o;
+  float* S_T;          // may be null (skip)
+};
+
+// fp32 token-by-token recurrence: any supported dk/dv/dtypes.  Reads S0 before writing S_T
+// element by element in the same thread, so S0 == S_T is safe.
+hipError_t launch_recurrent(const Problem& p, hipStream_t stream);
+
+// Single-token decode with the state updated in place (S0 == S_T == S), dk == dv == 128.
+hipError_t launch_decode128(const Problem& p, hipStream_t stream);
+
+// MFMA chunked forward, bf16 q/k/v, dk == dv == 128, chunk 64.
+hipError_t launch_chunk128(const Problem& p, hipStream_t stream);
+
+// S_T = S0 (copy) or zeros when S0 is null: n floats.
+hipError_t launch_state_copy(const float* S0, float* S_T, int64_t n, hipStream_t stream);
+
+}  // namespace dr

@@ -1,0 +1,129 @@
+/*
+ * dr.h -- C ABI of the gated delta-rule recurrence library (libdr.so, gfx950).
+ *
+ * The operation.  Per batch b and head h a fixed-size associative memory S (dk x dv, fp32)
+ * replaces a growing key/value cache; each token decays it, erases along the current key and
+ * writes a new key/value association, and the output reads the updated memory
+ * ("KronLSTM ...", The problem; "Gated DeltaNet-2: decoupling erase and write in linear
+ * attention", the solution and its gate table; "FG2-GDN: Enhancing Long-Context Gated Delta
+ * Networks with Doubly Fine-Grained Control", section 2, update rule and FG2-GDN+):
+ *
+ *     S'  = Diag(a_t) S_{t-1},            a_t = exp(log_decay_t)   (log-space decay, <= 0)
+ *     S_t = S' - (e_t * k_t)(k_t^T S') + k_t (w_t * v_t)^T          (erase e_t, write w_t)
+ *     o_t = S_t^T q_t
+ *
+ * Scalar-gate Gated DeltaNet is a per-head decay with e_t = w_t = beta_t; KDA is a per-channel
+ * decay with e_t = w_t = beta_t; Gated DeltaNet-2 / FG2-GDN+ use per-channel erase and write
+ * gates.  FG2-GDN's symmetric per-channel rate (k~ = sqrt(beta) k, v~ = sqrt(beta) v) is
+ * reached by passing the pre-scaled k and v with erase = write = 1.  The operation applies no
+ * query scale and no key normalisation: the caller supplies them.
+ *
+ * Layouts (row-major, contiguous, no strides):
+ *     q, k      [B, T, H, dk]        qkv_dtype (fp32 or bf16)
+ *     v         [B, T, H, dv]        qkv_dtype
+ *     o         [B, T, H, dv]        o_dtype (fp32 default, or bf16)
+ *     log_decay [B, T, H] (DR_GATE_HEAD) or [B, T, H, dk] (DR_GATE_CHANNEL), fp32
+ *     erase     [B, T, H] or [B, T, H, dk], fp32
+ *     write     [B, T, H] or [B, T, H, dv], fp32; ignored when write_is_erase != 0
+ *     S0, S_T   [B, H, dk, dv], fp32
+ *
+ * Ownership and threading.  Every pointer is a device pointer that the caller allocated and
+ * keeps alive until the enqueued work has finished.  The library allocates nothing, never
+ * synchronises, keeps no mutable global state and enqueues all work on `stream` (a
+ * hipStream_t; NULL = the default stream), so calls on distinct streams may run concurrently.
+ *
+ * Errors.  Argument errors are detected synchronously, before anything is enqueued, and the
+ * call returns a negative dr_status with no device work issued.  A failed launch returns
+ * DR_E_HIP.  Faults inside a kernel surface at the caller's next synchronisation.  NaN and Inf
+ * inputs are not checked; they stay inside the (b, h) they occur in.
+ */
+#ifndef GATED_DELTA_RULE_DR_H_
+#define GATED_DELTA_RULE_DR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DR_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+typedef enum {
+  DR_OK = 0,
+  DR_E_NULL = -1,        /* a required pointer (or the descriptor) is NULL */
+  DR_E_SHAPE = -2,       /* a size is negative, zero where it must not be, or overflows */
+  DR_E_DTYPE = -3,       /* unknown dtype or gate-kind code */
+  DR_E_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  DR_E_ALIAS = -5,       /* an output overlaps an input (other than the allowed S0 == S_T) */
+  DR_E_UNSUPPORTED = -6, /* a valid combination this build does not implement */
+  DR_E_WORKSPACE = -7,   /* workspace missing or smaller than dr_chunk_fwd_workspace_bytes */
+  DR_E_HIP = -8          /* a HIP launch failed */
+} dr_status;
+
+typedef enum { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
+
+typedef enum {
+  DR_GATE_HEAD = 0,    /* one fp32 value per (b, t, h): [B, T, H] */
+  DR_GATE_CHANNEL = 1  /* one fp32 value per channel: [B, T, H, dk] (decay, erase) or dv (write) */
+} dr_gate_kind;
+
+/* Problem descriptor.  All fields are 32-bit integers so the struct has one layout on every
+ * compiler: 12 x int32, no padding. */
+typedef struct {
+  int32_t B, T, H;        /* batch, tokens (T >= 0), heads */
+  int32_t dk, dv;         /* key and value widths: each one of 16, 32, 64, 128 */
+  int32_t chunk;          /* dr_chunk_fwd: 0 = default (64); 1 = token-by-token path; else 64 */
+  int32_t qkv_dtype;      /* dr_dtype of q, k, v */
+  int32_t o_dtype;        /* dr_dtype of o (DR_F32 recommended) */
+  int32_t decay_kind;     /* dr_gate_kind of log_decay */
+  int32_t erase_kind;     /* dr_gate_kind of erase */
+  int32_t write_kind;     /* dr_gate_kind of write (ignored when write_is_erase) */
+  int32_t write_is_erase; /* nonzero: the write gate is the erase gate (`write` is ignored);
+                             with a per-channel erase gate this needs dk == dv */
+} dr_desc;
+
+/* Returns DR_ABI_VERSION of the built library. */
+int dr_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char* dr_status_str(int status);
+
+/* Bytes of device workspace dr_chunk_fwd needs for `desc` (0 when none), or 0 for an invalid
+ * descriptor.  The current kernels need none; callers pass what this returns. */
+size_t dr_chunk_fwd_workspace_bytes(const dr_desc* desc);
+
+/* Prefill / training forward over T tokens (the chunkwise-parallel form the pages describe:
+ * the in-chunk rank-1 erases are folded into dense products via a triangular solve (WY/UT),
+ * and the fp32 state is carried from chunk to chunk).
+ *
+ *   S0    initial state, or NULL for zeros.  May be the same pointer as S_T (in-place carry);
+ *         any other overlap between S0 and S_T is DR_E_ALIAS.
+ *   o     output; must not overlap any input or S_T.
+ *   S_T   final state, or NULL to skip writing it.
+ *   workspace, workspace_bytes: device scratch of at least dr_chunk_fwd_workspace_bytes(desc)
+ *         (NULL / 0 when that is 0).
+ * T == 0 leaves o untouched and writes S_T = S0 (zeros when S0 is NULL).
+ * Paths: bf16 q/k/v with dk == dv == 128 and chunk 0/64 run the MFMA chunk kernel (fp16
+ * operands, fp32 accumulation and fp32 state); every other supported combination, and
+ * chunk == 1, runs the fp32 token-by-token kernel.
+ * Pointers must be 16-byte aligned. */
+int dr_chunk_fwd(const dr_desc* desc, const void* q, const void* k, const void* v,
+                 const float* log_decay, const float* erase, const float* write,
+                 const float* S0, void* o, float* S_T, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* One decode token for B independent sequences (desc->T must be 1): reads q, k, v, gates in
+ * the [B, 1, H, d] layouts above, updates S [B, H, dk, dv] in place and writes o [B, 1, H, dv].
+ * The state streams through once (read once, written once).  o must not overlap any input
+ * or S.  Pointers must be 16-byte aligned. */
+int dr_decode_step(const dr_desc* desc, const void* q, const void* k, const void* v,
+                   const float* log_decay, const float* erase, const float* write, float* S,
+                   void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GATED_DELTA_RULE_DR_H_ */

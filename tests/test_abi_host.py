@@ -1,0 +1,138 @@
+"""Host-only checks of libdr's C ABI: the library loads, exports every symbol include/dr.h
+declares, and rejects invalid arguments synchronously.  No call here reaches a kernel: every
+call either fails validation (pointers are fake, never dereferenced) or only queries sizes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_dr_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dr.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_abi.LIB_PATH), reason="libdr.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(dr_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) == set(_abi.EXPORTS)
+    lib = ctypes.CDLL(_abi.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    L = _abi.lib()
+    assert L.dr_abi_version() == 1
+    for code in range(-8, 1):
+        assert _abi.status_str(code)
+    assert _abi.status_str(-99) == "unknown status"
+    assert _abi.status_str(0) == "ok"
+
+
+def _good_desc(**kw):
+    d = _abi.DrDesc()
+    vals = dict(B=2, T=100, H=4, dk=128, dv=128, chunk=0, qkv_dtype=_abi.DR_BF16, o_dtype=_abi.DR_F32,
+                decay_kind=_abi.DR_GATE_HEAD, erase_kind=_abi.DR_GATE_HEAD, write_kind=_abi.DR_GATE_HEAD,
+                write_is_erase=1)
+    vals.update(kw)
+    for k, v in vals.items():
+        setattr(d, k, v)
+    return d
+
+
+GB = 1 << 30
+# Fake, 16-byte aligned, widely separated addresses: validation never dereferences them.
+P = {name: (i + 1) * 64 * GB for i, name in enumerate(["q", "k", "v", "ld", "e", "w", "S0", "o", "ST", "ws"])}
+
+
+def _fwd(desc, **over):
+    ptr = dict(P)
+    ptr.update(over)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return _abi.lib().dr_chunk_fwd(ctypes.byref(desc) if desc is not None else None,
+                                   vp(ptr["q"]), vp(ptr["k"]), vp(ptr["v"]), vp(ptr["ld"]), vp(ptr["e"]),
+                                   vp(ptr["w"]), vp(ptr["S0"]), vp(ptr["o"]), vp(ptr["ST"]),
+                                   vp(ptr.get("wsp")), ptr.get("wsn", 0), None)
+
+
+def _dec(desc, **over):
+    ptr = dict(P)
+    ptr.update(over)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return _abi.lib().dr_decode_step(ctypes.byref(desc), vp(ptr["q"]), vp(ptr["k"]), vp(ptr["v"]),
+                                     vp(ptr["ld"]), vp(ptr["e"]), vp(ptr["w"]), vp(ptr["S0"]), vp(ptr["o"]), None)
+
+
+def test_null_arguments():
+    assert _fwd(None) == _abi.DR_E_NULL
+    d = _good_desc()
+    for name in ("q", "k", "v", "ld", "e", "o"):
+        assert _fwd(d, **{name: None}) == _abi.DR_E_NULL, name
+    assert _fwd(_good_desc(write_is_erase=0), w=None) == _abi.DR_E_NULL
+    assert _dec(_good_desc(T=1), S0=None) == _abi.DR_E_NULL
+
+
+def test_shape_errors():
+    for kw in (dict(B=0), dict(H=0), dict(T=-1), dict(dk=0), dict(dv=-4)):
+        assert _fwd(_good_desc(**kw)) == _abi.DR_E_SHAPE, kw
+    # per-channel erase reused as the write gate needs dk == dv
+    assert _fwd(_good_desc(dk=64, dv=128, erase_kind=_abi.DR_GATE_CHANNEL)) == _abi.DR_E_SHAPE
+    # decode is exactly one token
+    assert _dec(_good_desc(T=2)) == _abi.DR_E_SHAPE
+    # element counts that overflow
+    assert _fwd(_good_desc(B=2**30, T=2**30, H=2**30)) == _abi.DR_E_SHAPE
+
+
+def test_dtype_and_kind_errors():
+    assert _fwd(_good_desc(qkv_dtype=7)) == _abi.DR_E_DTYPE
+    assert _fwd(_good_desc(o_dtype=-1)) == _abi.DR_E_DTYPE
+    assert _fwd(_good_desc(decay_kind=2)) == _abi.DR_E_DTYPE
+    assert _fwd(_good_desc(erase_kind=5)) == _abi.DR_E_DTYPE
+    assert _fwd(_good_desc(write_is_erase=0, write_kind=3)) == _abi.DR_E_DTYPE
+
+
+def test_unsupported():
+    assert _fwd(_good_desc(dk=96)) == _abi.DR_E_UNSUPPORTED
+    assert _fwd(_good_desc(dv=256)) == _abi.DR_E_UNSUPPORTED
+    assert _fwd(_good_desc(chunk=32)) == _abi.DR_E_UNSUPPORTED
+
+
+def test_alignment():
+    d = _good_desc()
+    for name in ("q", "k", "v", "ld", "e", "S0", "o", "ST"):
+        assert _fwd(d, **{name: P[name] + 4}) == _abi.DR_E_ALIGN, name
+
+
+def test_aliasing():
+    d = _good_desc()
+    assert _fwd(d, o=P["q"]) == _abi.DR_E_ALIAS
+    assert _fwd(d, o=P["v"] + 1024) == _abi.DR_E_ALIAS  # partial overlap
+    assert _fwd(d, ST=P["k"]) == _abi.DR_E_ALIAS
+    assert _fwd(d, ST=P["o"]) == _abi.DR_E_ALIAS
+    assert _fwd(d, ST=P["S0"] + 4096) == _abi.DR_E_ALIAS  # overlapping but not identical
+    assert _dec(_good_desc(T=1), o=P["S0"]) == _abi.DR_E_ALIAS
+    assert _dec(_good_desc(T=1), S0=P["e"]) == _abi.DR_E_ALIAS
+
+
+def test_workspace_query():
+    L = _abi.lib()
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc())) == 0
+    assert L.dr_chunk_fwd_workspace_bytes(None) == 0
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(B=0))) == 0
+
+
+def test_descriptor_layout():
+    assert ctypes.sizeof(_abi.DrDesc) == 48
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} dr_desc;", src, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(\w+)\s*[,;]", body)
+    assert fields == [f[0] for f in _abi.DrDesc._fields_]

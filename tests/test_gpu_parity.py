@@ -1,0 +1,149 @@
+"""GPU parity: libdr (through the C ABI) against the fp64 oracle on identical seeded inputs.
+
+Tolerances (normwise per (b, h), tests/metrics.py): 1e-5 where q/k/v are fp32 or where the
+fp32 token-by-token kernel runs, 3e-3 for the bf16 matrix-core chunk path."""
+import numpy as np
+import pytest
+import torch
+
+from metrics import err_S, err_o
+from oracle import decode_step as oracle_decode
+from oracle import recurrence
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 3e-3
+
+
+@pytest.fixture(scope="module")
+def dr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_dr_amd as m
+
+    m.abi_version()  # raises if libdr.so is missing
+    return m
+
+
+def _dev(d):
+    return {k: (None if v is None else v.cuda()) for k, v in d.items()}
+
+
+def _case(B, T, H, dk, dv, dtype, variant, s0, seed):
+    from gated_delta_rule_dr_amd.workloads import Workload
+
+    decay_ch = variant != "scalar"
+    wl = Workload("case", B, T, H, dk, dv, dtype, "softplus", decay_ch, -4.0, 1.5,
+                  variant == "decoupled", "channel" if variant == "decoupled" else "erase",
+                  0.05 if s0 else 0.0, seed)
+    from gated_delta_rule_dr_amd.workloads import generate
+
+    return generate(wl)
+
+
+def _run(dr, inp, chunk=64, o_dtype=torch.float32):
+    d = _dev(inp)
+    o, S = dr.chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], d["S0"],
+                        chunk=chunk, o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def _oracle(inp):
+    return recurrence(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"], inp["S0"])
+
+
+def test_scalar_gdn_fp32_workload(dr):
+    from gated_delta_rule_dr_amd.workloads import generate, workload
+
+    inp = generate(workload("gdn_scalar_f32_d32"))
+    o, S = _run(dr, inp)
+    ro, rS = _oracle(inp)
+    eo, eS = err_o(o, ro), err_S(S, rS)
+    print(f"gdn_scalar_f32_d32: err_o={eo:.3e} err_S={eS:.3e}")
+    assert eo <= TOL_F32 and eS <= TOL_F32
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 128)])
+@pytest.mark.parametrize("variant", ["scalar", "kda", "decoupled"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_token_kernel_variants(dr, dk, dv, variant, dtype):
+    if variant == "kda" and dk != dv:
+        pass  # KDA's write gate is the (per-head) erase gate: any dk, dv
+    inp = _case(2, 37, 3, dk, dv, dtype, variant, True, 100 + dk + dv)
+    o, S = _run(dr, inp, chunk=1)
+    ro, rS = _oracle(inp)
+    eo, eS = err_o(o, ro), err_S(S, rS)
+    assert eo <= TOL_F32 and eS <= TOL_F32, (eo, eS)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
+@pytest.mark.parametrize("variant", ["scalar", "kda", "decoupled"])
+def test_chunk_path_bf16_d128(dr, T, variant):
+    inp = _case(1, T, 2, 128, 128, "bf16", variant, T % 2 == 1, 7 + T)
+    o, S = _run(dr, inp)
+    ro, rS = _oracle(inp)
+    eo, eS = err_o(o, ro), err_S(S, rS)
+    print(f"chunk {variant} T={T}: err_o={eo:.3e} err_S={eS:.3e}")
+    assert eo <= TOL_BF16 and eS <= TOL_BF16, (eo, eS)
+
+
+def test_zero_length(dr):
+    inp = _case(1, 0, 2, 128, 128, "bf16", "kda", True, 3)
+    d = _dev(inp)
+    o = torch.full((1, 0, 2, 128), 7.0, device="cuda")
+    S_T = torch.full((1, 2, 128, 128), 7.0, device="cuda")
+    dr.chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], None, d["S0"], out=o, S_T=S_T)
+    torch.cuda.synchronize()
+    assert torch.equal(S_T, d["S0"])
+    S_T.fill_(7.0)
+    dr.chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], None, None, S_T=S_T)
+    torch.cuda.synchronize()
+    assert float(S_T.abs().max()) == 0.0
+
+
+def test_bf16_output(dr):
+    inp = _case(1, 50, 2, 64, 64, "bf16", "kda", False, 5)
+    o, S = _run(dr, inp, chunk=1, o_dtype=torch.bfloat16)
+    ro, _ = _oracle(inp)
+    assert o.dtype == torch.bfloat16
+    assert err_o(o.float(), ro) <= 2 ** -8
+
+
+def test_in_place_state_carry(dr):
+    inp = _case(2, 90, 2, 128, 128, "bf16", "kda", True, 9)
+    d = _dev(inp)
+    o1, S1 = dr.chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], None, d["S0"])
+    S = d["S0"].clone()
+    o2, _ = dr.chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], None, S, S_T=S)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S)
+
+
+@pytest.mark.parametrize("variant", ["scalar", "kda", "decoupled"])
+@pytest.mark.parametrize("d", [128, 64])
+def test_decode_steps_match_oracle(dr, variant, d):
+    from gated_delta_rule_dr_amd.workloads import generate_decode, workload
+
+    wl = workload("decode_kda_n256_h32", B=5, H=3, dk=d, dv=d, decay_channel=variant != "scalar",
+                  erase_channel=variant == "decoupled", write="channel" if variant == "decoupled" else "erase")
+    inp = generate_decode(wl, steps=6)
+    S = inp["S0"].cuda()
+    S_ref = inp["S0"].double().numpy()
+    for s in range(6):
+        g = lambda key: None if inp[key] is None else inp[key][s]
+        o = dr.decode_step(g("q").cuda(), g("k").cuda(), g("v").cuda(), g("log_decay").cuda(), g("erase").cuda(),
+                           None if g("write") is None else g("write").cuda(), S=S)
+        ro, S_ref = oracle_decode(g("q"), g("k"), g("v"), g("log_decay"), g("erase"), g("write"), S_ref)
+        torch.cuda.synchronize()
+        eo = err_o(o[:, None], ro[:, None])
+        assert eo <= TOL_F32, (s, eo)
+    assert err_S(S, S_ref) <= TOL_F32
+
+
+def test_determinism(dr):
+    inp = _case(1, 130, 2, 128, 128, "bf16", "decoupled", True, 11)
+    o1, S1 = _run(dr, inp)
+    o2, S2 = _run(dr, inp)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
