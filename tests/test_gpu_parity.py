@@ -89,6 +89,26 @@ def test_chunk_path_bf16_d128(dr, T, variant):
     assert eo <= TOL_BF16 and eS <= TOL_BF16, (eo, eS)
 
 
+@pytest.mark.parametrize("B,H,T", [(1, 64, 100), (2, 64, 70), (2, 3, 300)])
+@pytest.mark.parametrize("variant", ["scalar", "kda", "decoupled"])
+def test_chunk_path_slice_widths(dr, B, H, T, variant):
+    # B*H selects the value-slice width of the chunk kernel (64, 32 or 16 columns)
+    inp = _case(B, T, H, 128, 128, "bf16", variant, True, 17 + T + H)
+    o, S = _run(dr, inp)
+    ro, rS = _oracle(inp)
+    eo, eS = err_o(o, ro), err_S(S, rS)
+    print(f"chunk {variant} B={B} H={H} T={T}: err_o={eo:.3e} err_S={eS:.3e}")
+    assert eo <= TOL_BF16 and eS <= TOL_BF16, (eo, eS)
+
+
+def test_chunk_matches_token_kernel(dr):
+    # the two GPU paths agree with each other as well as with the oracle
+    inp = _case(1, 257, 4, 128, 128, "bf16", "decoupled", True, 23)
+    o1, S1 = _run(dr, inp)
+    o2, S2 = _run(dr, inp, chunk=1)
+    assert err_o(o1, o2) <= TOL_BF16 and err_S(S1, S2) <= TOL_BF16
+
+
 def test_zero_length(dr):
     inp = _case(1, 0, 2, 128, 128, "bf16", "kda", True, 3)
     d = _dev(inp)
