@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated delta-rule hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--all]
+
+One step is one chunked forward (dr_chunk_fwd) over the scalar-gate Gated DeltaNet prefill
+batch B=4, H=16, T=4096, dk=dv=128, bf16 q/k/v, fp32 gates and state, chunk 64.  W untimed
+warm-up steps run first; K steps are then timed between two device synchronisations with HIP
+events on the stream the kernels are launched on.  Two independently drawn input sets
+alternate so that the 194 MiB batch is not served from the 256 MB last-level cache.
+
+The single JSON line printed at the end carries:
+  value        prefill tokens/s (B*H*T per second of kernel time)
+  roofline     the chunk kernel against HBM bandwidth: algorithmic bytes per launch (compulsory
+               input/output bytes) / average launch duration, peak 8 TB/s, plus the counter-
+               measured HBM traffic when a counter summary for the current kernel source is
+               committed under profiles/
+  mfma         algorithmic matrix flops / time against the 2.5 PFLOP/s dense fp16/bf16 peak
+  decode       1000 single-token steps for 256 sequences x 32 heads (steps/s, GB/s, fraction
+               of HBM peak)
+  cpu_baseline the fp64 oracle on a bounded sample of the same workload, one thread
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16
+METRIC = "prefill tokens/s (B·H·T/s) + MFMA % peak; decode steps/s + HBM GB/s % peak"
+PREFILL = "gdn_scalar_bf16_t4k"
+DECODE = "decode_kda_n256_h32"
+CHUNK_SRC = os.path.join(ROOT, "gated_delta_rule_dr_amd", "csrc", "chunk.hip")
+DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_dr_amd", "csrc", "decode.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def algorithmic_bytes(wl) -> int:
+    """Compulsory HBM bytes of one forward: q, k, v in their storage type, every gate once, the
+    fp32 output, S0 when given and S_T."""
+    th = wl.B * wl.T * wl.H
+    qkv = 2 if wl.qkv_dtype == "bf16" else 4
+    per_tok = qkv * (2 * wl.dk + wl.dv) + 4 * wl.dv
+    per_tok += 4 * (wl.dk if wl.decay_channel else 1)
+    per_tok += 4 * (wl.dk if wl.erase_channel else 1)
+    per_tok += 4 * wl.dv if wl.write == "channel" else 0
+    state = wl.B * wl.H * wl.dk * wl.dv * 4
+    return th * per_tok + state * (2 if wl.s0_std > 0 else 1)
+
+
+def algorithmic_flops(wl) -> float:
+    """Matrix flops of the chunk form per chunk of C = 64 (fixed for counting):
+    symmetric gates 10 C^2 d + 6 C d^2 + C^3 / 3, separate erase/write 16 C^2 d + 8 C d^2 + C^3 / 3."""
+    C, d = 64, wl.dk
+    general = wl.erase_channel or wl.write == "channel"
+    per_chunk = (16 * C * C * d + 8 * C * d * d) if general else (10 * C * C * d + 6 * C * d * d)
+    per_chunk += C ** 3 / 3
+    return wl.B * wl.H * (wl.T / C) * per_chunk
+
+
+def decode_bytes(wl) -> int:
+    """Per decode step: the fp32 state read and written once, q/k/v, gates and the output."""
+    n = wl.B * wl.H
+    state = n * wl.dk * wl.dv * 4 * 2
+    io = n * (2 * (2 * wl.dk + wl.dv) + 4 * wl.dv)
+    io += n * 4 * (wl.dk if wl.decay_channel else 1)
+    io += n * 4 * (wl.dk if wl.erase_channel else 1)
+    io += n * 4 * wl.dv if wl.write == "channel" else 0
+    return state + io
+
+
+def source_hash(path) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic(kernel: str, workload: str, src: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken on the current
+    kernel source; otherwise None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_prefill(dr, torch, wl, steps, warmup):
+    from gated_delta_rule_dr_amd.workloads import generate
+
+    sets = [generate(wl, device="cuda"), generate(wl.replace(seed=wl.seed + 1000), device="cuda")]
+    o = torch.empty((wl.B, wl.T, wl.H, wl.dv), device="cuda")
+    S_T = torch.empty((wl.B, wl.H, wl.dk, wl.dv), device="cuda")
+
+    def step(i):
+        x = sets[i % 2]
+        dr.chunk_fwd(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"], x["S0"], out=o, S_T=S_T)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return e0.elapsed_time(e1) / 1e3 / steps, wall
+
+
+def time_decode(dr, torch, wl, steps):
+    from gated_delta_rule_dr_amd.workloads import generate_decode
+
+    inp = generate_decode(wl, steps=steps, device="cuda")
+    S = inp["S0"]
+    o = torch.empty((wl.B, wl.H, wl.dv), device="cuda")
+    w = inp["write"]
+
+    def step(s):
+        dr.decode_step(inp["q"][s], inp["k"][s], inp["v"][s], inp["log_decay"][s], inp["erase"][s],
+                       None if w is None else w[s], S=S, o=o)
+
+    for s in range(3):  # warm-up on the first inputs; the state keeps evolving
+        step(s)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(steps):
+        step(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3
+    del inp
+    return sec / steps
+
+
+def cpu_baseline(wl, tokens):
+    """The fp64 oracle on the first `tokens` tokens of every (b, h) of the workload."""
+    from threadpoolctl import threadpool_limits
+
+    from gated_delta_rule_dr_amd.workloads import generate
+    from oracle import recurrence
+
+    sample = wl.replace(T=tokens)
+    inp = generate(sample)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        recurrence(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"], inp["S0"])
+        sec = time.perf_counter() - t0
+    return dict(value=sample.token_heads / sec, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{sample.B}x{sample.H} heads x first {tokens} tokens of {wl.name} "
+                       f"({sample.token_heads} token-heads, {sec:.1f} s, fp64 numpy, 1 thread)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also time the KDA and decoupled prefill workloads")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="also run one plain elementwise copy of this many MiB (a known-size "
+                         "reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the recurrence shards over (batch, head) pairs with no "
+              "communication, so only --gpus 1 is supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_dr_amd as dr
+    from gated_delta_rule_dr_amd.workloads import workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dr.abi_version()
+
+    if args.copy_ref_mib:
+        n = args.copy_ref_mib * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)  # reads and writes copy_ref_mib MiB each
+        torch.cuda.synchronize()
+        del src, dst
+
+    wl = workload(PREFILL)
+    sec, wall = time_prefill(dr, torch, wl, args.steps, args.warmup)
+    tok_s = wl.token_heads / sec
+    nbytes = algorithmic_bytes(wl)
+    flops = algorithmic_flops(wl)
+    achieved = nbytes / sec / 1e9
+    traffic = counter_traffic("chunk_kernel", PREFILL, CHUNK_SRC)
+    line = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 matrix operands, fp32 accumulate and state (bf16 inputs)",
+        "data": "synthetic (seeded; two alternating input sets)",
+        "config": {"workload": PREFILL, "B": wl.B, "H": wl.H, "T": wl.T, "dk": wl.dk, "dv": wl.dv,
+                   "chunk": wl.chunk, "qkv": "bf16", "gates": "fp32 per head", "o": "fp32"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "chunk_kernel", "algorithmic_bytes_per_launch": nbytes},
+        "mfma": {"achieved_tflops": flops / sec / 1e12, "peak_tflops": MFMA_PEAK_TFLOPS,
+                 "frac": flops / sec / 1e12 / MFMA_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops},
+        "timed_wall_s": wall,
+    }
+    if args.all:
+        extra = {}
+        for name in ("kda_channel_bf16_t16k", "gdn2_decoupled_bf16_t64k"):
+            w2 = workload(name)
+            s2, _ = time_prefill(dr, torch, w2, max(3, args.steps // 10), 2)
+            extra[name] = {"tokens_per_s": w2.token_heads / s2, "ms": s2 * 1e3,
+                           "hbm_frac": algorithmic_bytes(w2) / s2 / 1e9 / HBM_PEAK_GBS,
+                           "mfma_frac": algorithmic_flops(w2) / s2 / 1e12 / MFMA_PEAK_TFLOPS}
+            torch.cuda.empty_cache()
+        line["other_prefill"] = extra
+    if not args.no_decode:
+        dwl = workload(DECODE)
+        dsec = time_decode(dr, torch, dwl, args.decode_steps)
+        dbytes = decode_bytes(dwl)
+        line["decode"] = {"workload": DECODE, "steps": args.decode_steps, "steps_per_s": 1.0 / dsec,
+                          "us_per_step": dsec * 1e6, "GB_per_s": dbytes / dsec / 1e9,
+                          "hbm_frac": dbytes / dsec / 1e9 / HBM_PEAK_GBS, "bytes_per_step": dbytes,
+                          "traffic": counter_traffic("decode128_kernel", DECODE, DECODE_SRC)}
+        torch.cuda.empty_cache()
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
