@@ -39,6 +39,9 @@ def common_flags():
         "-Wall",
         "-Wno-unused-function",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # keep small per-thread arrays (prefetch buffers) in registers: promoting them to LDS
+        # turns every prefetch into a load followed by an immediate wait
+        "-mllvm", "-disable-promote-alloca-to-lds",
         "-I", os.path.join(ROOT, "include"),
         "-I", CSRC,
     ]

@@ -9,7 +9,7 @@
 // Attention", method: architecture and implementation).
 //
 // Per chunk, with incoming state S, chunk-local cumulative log-decay g_t (per channel) and a
-// per-channel reference gm (g at the chunk midpoint), the kernel forms
+// per-channel reference gm (g at the chunk midpoint):
 //   K+ = k e^{g - gm}, Q+ = q e^{g - gm}, K- = k e^{gm - g}, U- = (e * k) e^{gm - g}
 //   A_kk = strict_lower(K+ K-^T)  A_ku = strict_lower(K+ U-^T)  A_qk = lower(Q+ K-^T)
 //   A_qu = lower(Q+ U-^T)          X_K = K+ S~,  X_Q = Q+ S~,  S~ = Diag(e^{gm}) S
@@ -19,14 +19,19 @@
 // general gates (erase e, write w; Vt = w * v):
 //   T = (I + A_ku)^{-1},  M = T (X_K + A_kk Vt)
 //   O = X_Q + A_qk Vt - A_qu M,  S <- Diag(e^{g_C}) S + Diag(e^{g_C - gm}) (K-^T Vt - U-^T M)
-// Products use v_mfma_f32_16x16x32_f16 (fp16 operands, fp32 accumulation); the triangular
-// solve is fp32 forward substitution on the four 16x16 diagonal blocks plus 16x16x16 matrix-
-// core products for the off-diagonal blocks; the state stays fp32 in registers for the whole
-// sequence.  One workgroup (4 waves) owns one (b, h) and DVS value columns of its state.
+//
+// Two kernels.  chunk_prep_kernel runs one workgroup per chunk (all chunks of all heads in
+// parallel) and computes the only state-independent factor that needs a serial algorithm,
+// T, into the caller's workspace (fp16, 64 x 64 per chunk).  chunk_scan_kernel then walks the
+// chunks of one (b, h, value slice) in order, carrying the fp32 state in registers: it builds
+// the decayed operand tiles, the remaining Gram matrices and every state-dependent product.
+// Products use v_mfma_f32_16x16x32_f16 (fp16 operands, fp32 accumulation).  Gram tiles are
+// computed transposed (A^T = K- Q+^T) so that each lane owns four consecutive columns of one
+// row of A and stores them with one vector write.
 //
 // Range: the midpoint reference keeps every fp16 operand within e^{+-(half-chunk decay)}.  The
-// exponents are clamped at 11 (e^11 < 65504), so a per-channel log-decay sum over half a chunk
-// below -11 loses accuracy (the token-by-token path has no such limit).
+// exponents are clamped at 11 (e^11 < 65504), so a per-channel log-decay sum below -11 over half
+// a chunk loses accuracy (the token-by-token path has no such limit).
 
 #include "dr_device.h"
 #include "dr_internal.h"
@@ -40,32 +45,9 @@ constexpr int C = 64;      // chunk length
 constexpr int D = 128;     // dk == dv
 constexpr int KS = 136;    // row stride (halves) of [64][128] tiles: 16-byte pad
 constexpr int CS = 72;     // row stride (halves) of [*][64] tiles
-constexpr int AFS = 65;    // row stride (floats) of the fp32 64 x 64 matrix
+constexpr int AFS = 68;    // row stride (floats) of the fp32 64 x 64 matrix (16-byte rows)
 constexpr int kThreads = 256;
 constexpr float kExpClamp = 11.f;
-
-template <bool GEN, int DVS>
-struct Layout {
-  static constexpr int kp = 0;                          // K+  [64][KS] half
-  static constexpr int qp = kp + C * KS * 2;            // Q+  [64][KS]
-  static constexpr int km = qp + C * KS * 2;            // K-  [64][KS]
-  static constexpr int um = km + C * KS * 2;            // U-  [64][KS]      (general)
-  static constexpr int st = um + (GEN ? C * KS * 2 : 0);  // S~^T [DVS][KS]
-  static constexpr int af = st + DVS * KS * 2;          // A for the solve, fp32 [64][AFS]
-  static constexpr int th = af + C * AFS * 4;           // T      [64][CS] half
-  static constexpr int aq = th + C * CS * 2;            // A_qk   [64][CS]
-  static constexpr int akk = aq + C * CS * 2;           // A_kk   [64][CS]   (general)
-  static constexpr int aqu = akk + (GEN ? C * CS * 2 : 0);  // A_qu [64][CS] (general)
-  static constexpr int rt = aqu + (GEN ? C * CS * 2 : 0);   // R^T / Y^T [DVS][CS]
-  static constexpr int dt = rt + DVS * CS * 2;          // delta^T / (-M)^T [DVS][CS]
-  static constexpr int vt = dt + DVS * CS * 2;          // V [64][DVS+8] or Vt^T [DVS][CS]
-  static constexpr int vstride = GEN ? CS : DVS + 8;
-  static constexpr int vbytes = GEN ? DVS * CS * 2 : C * (DVS + 8) * 2;
-  static constexpr int gb = vt + vbytes;                // per-token erase / beta [64] f32
-  static constexpr int gw = gb + C * 4;                 // per-token write [64] f32 (general)
-  static constexpr int gsc = gw + C * 4;                // scan partials [4][128] f32
-  static constexpr int total = gsc + 4 * D * 4;
-};
 
 // Lower-triangular 16x16 tile (I, J), I >= J, enumerated row by row.
 __device__ __forceinline__ void tile_ij(int idx, int& I, int& J) {
@@ -93,11 +75,10 @@ __device__ __forceinline__ f32x4 mfma16(half4v a, half4v b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ half8 cvt8(float x0, float x1, float x2, float x3, float x4, float x5,
-                                      float x6, float x7) {
+__device__ __forceinline__ half8 cvt8(const float* x) {
   half8 h;
-  h[0] = (_Float16)x0; h[1] = (_Float16)x1; h[2] = (_Float16)x2; h[3] = (_Float16)x3;
-  h[4] = (_Float16)x4; h[5] = (_Float16)x5; h[6] = (_Float16)x6; h[7] = (_Float16)x7;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (_Float16)x[i];
   return h;
 }
 
@@ -110,49 +91,366 @@ __device__ __forceinline__ void bf16x8_to_f32(uint4 u, float* f) {
 
 __device__ __forceinline__ float clamped_exp(float x) { return __expf(fminf(x, kExpClamp)); }
 
-// Value-slice words per thread: DVS/4 bf16 values.
-template <int DVS> struct VRaw;
-template <> struct VRaw<16> { uint2 w; };
-template <> struct VRaw<32> { uint4 w; };
-template <> struct VRaw<64> { uint4 w[2]; };
+__device__ __forceinline__ float4 ld4(const float* p, bool ok) {
+  return ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+__device__ __forceinline__ float4 gld4(gptr<const float> p, int64_t i, bool ok) {
+  return ok ? gload_f4(p, i) : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+__device__ __forceinline__ void unpack8(float4 a, float4 b, float* f) {
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// Chunk-local inclusive prefix sums of the log-decay.  Thread (token quad tg, channel octet
+// d8) holds its 4 x 8 (per channel) or 4 (per head: wave 0 lane t holds token t) log-decays;
+// on return g[r][ch] (per head: g[r][0]) is the cumulative log-decay of its tokens and GSC holds
+// per-wave totals (per channel, [4][128]) or the 64 per-token prefixes (per head).
+template <bool DCH>
+__device__ __forceinline__ void chunk_cumsum(const float (&ldr)[DCH ? 4 : 1][DCH ? 8 : 1], float lds,
+                                             float (&g)[4][DCH ? 8 : 1], float* GSC, int tid) {
+  const int lane = tid & 63, wave = tid >> 6, lg = lane >> 4, d8 = tid & 15, tg = tid >> 4;
+  if constexpr (DCH) {
+    float ex[8];
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) {
+      float acc = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        acc += ldr[r][ch];
+        g[r][ch] = acc;
+      }
+      // inclusive scan of the quad totals over the 4 token quads of this wave (lanes 16 apart)
+      float x = acc, y;
+      y = __shfl_up(x, 16);
+      if (lg >= 1) x += y;
+      y = __shfl_up(x, 32);
+      if (lg >= 2) x += y;
+      ex[ch] = x - acc;
+      if (lg == 3) GSC[wave * D + 8 * d8 + ch] = x;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) {
+      float pre = ex[ch];
+      for (int w = 0; w < wave; ++w) pre += GSC[w * D + 8 * d8 + ch];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) g[r][ch] += pre;
+    }
+  } else {
+    if (wave == 0) {
+      float x = lds;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+      }
+      GSC[lane] = x;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) g[r][0] = GSC[4 * tg + r];
+  }
+}
+
+template <bool DCH>
+__device__ __forceinline__ float chunk_gmid(const float* GSC, int d) {
+  return DCH ? GSC[d] + GSC[D + d] : GSC[31];
+}
+
+template <bool DCH>
+__device__ __forceinline__ float chunk_gend(const float* GSC, int d) {
+  return DCH ? GSC[d] + GSC[D + d] + GSC[2 * D + d] + GSC[3 * D + d] : GSC[63];
+}
+
+// ------------------------------------------------------------------------------------------
+// Prep: T = (I + A)^{-1} for one chunk, A = Diag(beta) A_kk (symmetric) or A_ku (general).
+// ------------------------------------------------------------------------------------------
+template <bool DCH, bool GEN>
+__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, _Float16* __restrict__ tws,
+                                                              int nchunks) {
+  __shared__ __attribute__((aligned(16))) _Float16 KP[C * KS];   // K+
+  __shared__ __attribute__((aligned(16))) _Float16 KB[C * KS];   // K- (symmetric) or U- (general)
+  __shared__ __attribute__((aligned(16))) float AF[C * AFS];
+  __shared__ __attribute__((aligned(16))) _Float16 TH[C * CS];
+  __shared__ float GB[C];
+  __shared__ float GSC[4 * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, lg = lane >> 4;
+  const int d8 = tid & 15, tg = tid >> 4;
+  const int64_t blk = blockIdx.x;            // (b, h) * nchunks + chunk
+  const int bh = int(blk / nchunks), c = int(blk - int64_t(bh) * nchunks);
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int T = p.T, H = p.H;
+  const uint16_t* kin = static_cast<const uint16_t*>(p.k);
+  auto tok = [&](int t) { return (int64_t(b) * T + t) * H + h; };
+
+  for (int i = tid; i < C * CS; i += kThreads) TH[i] = (_Float16)0.f;
+
+  uint4 kr[4];
+  float ldr[DCH ? 4 : 1][DCH ? 8 : 1];
+  float err[GEN ? 4 : 1][GEN ? 8 : 1];
+  float lds = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = c * C + 4 * tg + r;
+    const bool ok = t < T;
+    const int64_t base = ok ? tok(t) * D + 8 * d8 : 0;
+    kr[r] = ok ? *reinterpret_cast<const uint4*>(kin + base) : make_uint4(0, 0, 0, 0);
+    if constexpr (DCH) unpack8(ld4(p.log_decay + base, ok), ld4(p.log_decay + base + 4, ok), ldr[r]);
+    if constexpr (GEN) {
+      if (p.erase_channel) unpack8(ld4(p.erase + base, ok), ld4(p.erase + base + 4, ok), err[r]);
+    }
+  }
+  if (tid < C) {
+    const int t = c * C + tid;
+    const bool ok = t < T;
+    const int64_t ti = ok ? tok(t) : 0;
+    if constexpr (!DCH) lds = ok ? p.log_decay[ti] : 0.f;
+    GB[tid] = (ok && !(GEN && p.erase_channel)) ? p.erase[ti] : 0.f;
+  }
+
+  float g[4][DCH ? 8 : 1];
+  chunk_cumsum<DCH>(ldr, lds, g, GSC, tid);
+
+  {
+    float gm[8];
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) gm[ch] = chunk_gmid<DCH>(GSC, 8 * d8 + ch);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * tg + r;
+      float kf[8], kp[8], kb[8];
+      bf16x8_to_f32(kr[r], kf);
+#pragma unroll
+      for (int ch = 0; ch < 8; ++ch) {
+        const float gg = DCH ? g[r][ch] : g[r][0];
+        kp[ch] = kf[ch] * clamped_exp(gg - gm[ch]);
+        float e = 1.f;
+        if constexpr (GEN) e = p.erase_channel ? err[r][ch] : GB[t];
+        kb[ch] = e * kf[ch] * clamped_exp(gm[ch] - gg);
+      }
+      *reinterpret_cast<half8*>(KP + t * KS + 8 * d8) = cvt8(kp);
+      *reinterpret_cast<half8*>(KB + t * KS + 8 * d8) = cvt8(kb);
+    }
+  }
+  lds_barrier();
+
+  // Gram tiles, transposed: lane gets A[t = 16 I + l16][i = 16 J + 4 lg + r].
+#pragma unroll
+  for (int n = 0; n < 3; ++n) {
+    const int idx = wave + 4 * n;
+    if (idx < 10) {
+      int I, J;
+      tile_ij(idx, I, J);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc = mfma16x16x32(frag(KB, KS, 16 * J, 32 * ks, lane), frag(KP, KS, 16 * I, 32 * ks, lane), acc);
+      const int t = 16 * I + l16;
+      const float sc = GEN ? 1.f : GB[t];
+      float4 v;
+      v.x = (16 * J + 4 * lg + 0 < t) ? sc * acc[0] : 0.f;
+      v.y = (16 * J + 4 * lg + 1 < t) ? sc * acc[1] : 0.f;
+      v.z = (16 * J + 4 * lg + 2 < t) ? sc * acc[2] : 0.f;
+      v.w = (16 * J + 4 * lg + 3 < t) ? sc * acc[3] : 0.f;
+      *reinterpret_cast<float4*>(AF + t * AFS + 16 * J + 4 * lg) = v;
+    }
+  }
+  lds_barrier();
+
+  // Diagonal 16x16 blocks: fp32 forward substitution, one lane per (block, column).
+  if (wave == 0) {
+    const int bl = lg, col = l16;
+    const float* Ab = AF + (16 * bl) * AFS + 16 * bl;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s0 = (r == col) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < r; i += 2) {
+        s0 = fmaf(-Ab[r * AFS + i], x[i], s0);
+        if (i + 1 < r) s1 = fmaf(-Ab[r * AFS + i + 1], x[i + 1], s1);
+      }
+      x[r] = s0 + s1;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) TH[(16 * bl + r) * CS + 16 * bl + col] = (_Float16)x[r];
+  }
+  lds_barrier();
+
+  // Off-diagonal blocks, level by level: T_JI = -T_JJ sum_{K=I}^{J-1} A_JK T_KI.
+#pragma unroll
+  for (int Jb = 1; Jb < 4; ++Jb) {
+    if (wave < Jb) {
+      const int Ib = wave;
+      f32x4 P = {0.f, 0.f, 0.f, 0.f};
+      for (int Kb = Ib; Kb < Jb; ++Kb) {
+        const float4 a4 = *reinterpret_cast<const float4*>(AF + (16 * Jb + l16) * AFS + 16 * Kb + 4 * lg);
+        half4v a, bt;
+        a[0] = (_Float16)a4.x; a[1] = (_Float16)a4.y; a[2] = (_Float16)a4.z; a[3] = (_Float16)a4.w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bt[i] = TH[(16 * Kb + 4 * lg + i) * CS + 16 * Ib + l16];
+        P = mfma16(a, bt, P);
+      }
+      half4v nb, a2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) nb[i] = (_Float16)(-P[i]);
+      a2 = *reinterpret_cast<const half4v*>(TH + (16 * Jb + l16) * CS + 16 * Jb + 4 * lg);
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 Tji = mfma16(a2, nb, z);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) TH[(16 * Jb + 4 * lg + r) * CS + 16 * Ib + l16] = (_Float16)Tji[r];
+    }
+    lds_barrier();
+  }
+
+  // T (64 x 64 fp16, row-major) to the workspace: 32 bytes per thread.
+  {
+    const int t = tid >> 2, c0 = (tid & 3) * 16;
+    const uint4* src = reinterpret_cast<const uint4*>(TH + t * CS + c0);
+    uint4* dst = reinterpret_cast<uint4*>(tws + blk * (C * C) + t * C + c0);
+    dst[0] = src[0];
+    dst[1] = src[1];
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Scan: the chunks of one (b, h, value slice) in order, eight waves per workgroup.
+// ------------------------------------------------------------------------------------------
+constexpr int kScanWaves = 8;
+constexpr int kScanThreads = 64 * kScanWaves;
+
+template <bool GEN, int DVS>
+struct ScanLayout {
+  static constexpr int kp = 0;                          // K+  [64][KS] half
+  static constexpr int qp = kp + C * KS * 2;            // Q+  [64][KS]
+  static constexpr int km = qp + C * KS * 2;            // K-  [64][KS]
+  static constexpr int um = km + C * KS * 2;            // U-  [64][KS]      (general)
+  static constexpr int st = um + (GEN ? C * KS * 2 : 0);  // S~^T [DVS][KS]
+  static constexpr int th = st + DVS * KS * 2;          // T      [64][CS] half
+  static constexpr int aq = th + C * CS * 2;            // A_qk   [64][CS]
+  static constexpr int akk = aq + C * CS * 2;           // A_kk   [64][CS]   (general)
+  static constexpr int aqu = akk + (GEN ? C * CS * 2 : 0);  // A_qu [64][CS] (general)
+  static constexpr int rt = aqu + (GEN ? C * CS * 2 : 0);   // R^T / Y^T [DVS][CS]
+  static constexpr int dt = rt + DVS * CS * 2;          // delta^T / (-M)^T [DVS][CS]
+  static constexpr int vt = dt + DVS * CS * 2;          // V [64][DVS+8] or Vt^T [DVS][CS]
+  static constexpr int vstride = GEN ? CS : DVS + 8;
+  static constexpr int vbytes = GEN ? DVS * CS * 2 : C * (DVS + 8) * 2;
+  static constexpr int gb = vt + vbytes;                // per-token erase / beta [64] f32
+  static constexpr int gw = gb + C * 4;                 // per-token write [64] f32 (general)
+  static constexpr int gsc = gw + C * 4;                // per-wave log-decay totals [8][128] f32
+  static constexpr int total = gsc + kScanWaves * D * 4;
+};
+
+// Value-slice words per thread: DVS/8 bf16 values (and DVS/8 fp32 write gates).
+template <int DVS> struct VSlice;
+template <> struct VSlice<16> { uint32_t w; };
+template <> struct VSlice<32> { uint2 w; };
+template <> struct VSlice<64> { uint4 w; };
 
 template <int DVS>
-__device__ __forceinline__ void vraw_load(VRaw<DVS>& v, const uint16_t* p, bool valid) {
+__device__ __forceinline__ void vslice_load(VSlice<DVS>& v, gptr<const uint16_t> base, int64_t i, bool ok) {
   if constexpr (DVS == 16) {
-    v.w = valid ? *reinterpret_cast<const uint2*>(p) : make_uint2(0, 0);
+    v.w = ok ? *(gptr<const uint32_t>)(base + i) : 0u;
   } else if constexpr (DVS == 32) {
-    v.w = valid ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+    v.w = ok ? gload_u2(base, i) : make_uint2(0, 0);
   } else {
-    v.w[0] = valid ? reinterpret_cast<const uint4*>(p)[0] : make_uint4(0, 0, 0, 0);
-    v.w[1] = valid ? reinterpret_cast<const uint4*>(p)[1] : make_uint4(0, 0, 0, 0);
+    v.w = ok ? gload_u4(base, i) : make_uint4(0, 0, 0, 0);
   }
 }
 
 template <int DVS>
-__device__ __forceinline__ void vraw_f32(const VRaw<DVS>& v, float* f) {
+__device__ __forceinline__ void vslice_f32(const VSlice<DVS>& v, float* f) {
   if constexpr (DVS == 16) {
+    f[0] = __uint_as_float(v.w << 16); f[1] = __uint_as_float(v.w & 0xffff0000u);
+  } else if constexpr (DVS == 32) {
     f[0] = __uint_as_float(v.w.x << 16); f[1] = __uint_as_float(v.w.x & 0xffff0000u);
     f[2] = __uint_as_float(v.w.y << 16); f[3] = __uint_as_float(v.w.y & 0xffff0000u);
-  } else if constexpr (DVS == 32) {
-    bf16x8_to_f32(v.w, f);
   } else {
-    bf16x8_to_f32(v.w[0], f);
-    bf16x8_to_f32(v.w[1], f + 8);
+    bf16x8_to_f32(v.w, f);
+  }
+}
+
+// Chunk-local prefix sums of the log-decay for the eight-wave layout: thread (token pair tg,
+// channel octet d8) holds tokens 2 tg and 2 tg + 1.  On return g[r][ch] (per head: g[r][0]) is
+// the cumulative log-decay of its tokens, and GSC holds the per-wave totals ([8][128]; wave w
+// covers tokens 8 w .. 8 w + 7) or, per head, the 64 per-token prefixes.
+template <bool DCH>
+__device__ __forceinline__ void scan_cumsum(const float (&ldr)[DCH ? 2 : 1][DCH ? 8 : 1], float lds,
+                                            float (&g)[2][DCH ? 8 : 1], float* GSC, int tid) {
+  const int lane = tid & 63, wave = tid >> 6, lg = lane >> 4, d8 = tid & 15, tg = tid >> 4;
+  if constexpr (DCH) {
+    float ex[8];
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) {
+      g[0][ch] = ldr[0][ch];
+      const float acc = ldr[0][ch] + ldr[1][ch];
+      g[1][ch] = acc;
+      float x = acc, y;
+      y = __shfl_up(x, 16);
+      if (lg >= 1) x += y;
+      y = __shfl_up(x, 32);
+      if (lg >= 2) x += y;
+      ex[ch] = x - acc;
+      if (lg == 3) GSC[wave * D + 8 * d8 + ch] = x;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) {
+      float pre = ex[ch];
+#pragma unroll
+      for (int w = 0; w < kScanWaves - 1; ++w)
+        if (w < wave) pre += GSC[w * D + 8 * d8 + ch];
+      g[0][ch] += pre;
+      g[1][ch] += pre;
+    }
+  } else {
+    if (wave == 0) {
+      float x = lds;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+      }
+      GSC[lane] = x;
+    }
+    lds_barrier();
+    g[0][0] = GSC[2 * tg];
+    g[1][0] = GSC[2 * tg + 1];
+  }
+}
+
+template <bool DCH>
+__device__ __forceinline__ float scan_gmid(const float* GSC, int d) {
+  return DCH ? GSC[d] + GSC[D + d] + GSC[2 * D + d] + GSC[3 * D + d] : GSC[31];
+}
+
+template <bool DCH>
+__device__ __forceinline__ float scan_gend(const float* GSC, int d) {
+  if constexpr (DCH) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kScanWaves; ++w) s += GSC[w * D + d];
+    return s;
+  } else {
+    return GSC[63];
   }
 }
 
 template <bool DCH, bool GEN, int DVS>
-__global__ __launch_bounds__(kThreads) void chunk_kernel(Problem p) {
-  using L = Layout<GEN, DVS>;
+__global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, const _Float16* __restrict__ tws) {
+  using L = ScanLayout<GEN, DVS>;
   constexpr int NCT = DVS / 16;   // 16-column tiles of the value slice
-  constexpr int VPT = DVS / 4;    // value columns per thread in the V load
+  constexpr int VPT = DVS / 8;    // value columns per thread in the V load
   __shared__ __attribute__((aligned(16))) char smem[L::total];
   _Float16* KP = reinterpret_cast<_Float16*>(smem + L::kp);
   _Float16* QP = reinterpret_cast<_Float16*>(smem + L::qp);
   _Float16* KM = reinterpret_cast<_Float16*>(smem + L::km);
   _Float16* UM = reinterpret_cast<_Float16*>(smem + L::um);
   _Float16* ST = reinterpret_cast<_Float16*>(smem + L::st);
-  float* AF = reinterpret_cast<float*>(smem + L::af);
   _Float16* TH = reinterpret_cast<_Float16*>(smem + L::th);
   _Float16* AQ = reinterpret_cast<_Float16*>(smem + L::aq);
   _Float16* AKK = reinterpret_cast<_Float16*>(smem + L::akk);
@@ -172,14 +470,16 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Problem p) {
   const int j0 = blockIdx.y * DVS;
   const int T = p.T, H = p.H;
   const int nchunks = (T + C - 1) / C;
-  const uint16_t* kin = static_cast<const uint16_t*>(p.k);
-  const uint16_t* qin = static_cast<const uint16_t*>(p.q);
-  const uint16_t* vin = static_cast<const uint16_t*>(p.v);
-  float* out = static_cast<float*>(p.o);
+  const gptr<const uint16_t> kin = opaque_gptr(static_cast<const uint16_t*>(p.k));
+  const gptr<const uint16_t> qin = opaque_gptr(static_cast<const uint16_t*>(p.q));
+  const gptr<const uint16_t> vin = opaque_gptr(static_cast<const uint16_t*>(p.v));
+  const gptr<const float> ldin = opaque_gptr(p.log_decay);
+  const gptr<const float> erin = opaque_gptr(p.erase);
+  const gptr<const float> wrin = opaque_gptr(p.write);
+  const gptr<const _Float16> tbase = opaque_gptr(tws) + int64_t(bh) * nchunks * (C * C);
 
   // Matrices whose upper-triangular blocks are read as zeros by full-width fragments.
-  for (int i = tid; i < C * CS; i += kThreads) {
-    TH[i] = (_Float16)0.f;
+  for (int i = tid; i < C * CS; i += kScanThreads) {
     AQ[i] = (_Float16)0.f;
     if constexpr (GEN) {
       AKK[i] = (_Float16)0.f;
@@ -187,187 +487,138 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Problem p) {
     }
   }
 
-  // State: wave w owns rows [32 w, 32 w + 32) x the DVS columns, as 2 x NCT accumulator tiles
-  // (lane: column 16 ct + l16, rows 32 w + 16 rt + 4 lg + r).
-  f32x4 S[2][NCT];
+  // State: wave w owns rows [16 w, 16 w + 16) x the DVS columns as NCT accumulator tiles
+  // (lane: column 16 ct + l16, rows 16 w + 4 lg + r).
+  f32x4 S[NCT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d = 32 * wave + 16 * rt + 4 * lg + r;
-        S[rt][ct][r] = p.S0 ? p.S0[(int64_t(bh) * D + d) * D + j0 + 16 * ct + l16] : 0.f;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int d = 16 * wave + 4 * lg + r;
+      S[ct][r] = p.S0 ? p.S0[(int64_t(bh) * D + d) * D + j0 + 16 * ct + l16] : 0.f;
+    }
 
-  // Load mapping: thread = (token quad tg, channel octet d8): tokens 4 tg + r, channels
-  // 8 d8 .. 8 d8 + 7; value slice: token tid / 4, columns VPT (tid % 4) .. + VPT - 1.
+  // Load mapping: thread = (token pair tg, channel octet d8): tokens 2 tg + r, channels
+  // 8 d8 .. 8 d8 + 7; value slice: token tid / 8, columns VPT (tid % 8) .. + VPT - 1;
+  // T: row tid / 8, columns 8 (tid % 8) .. + 7.
   const int d8 = tid & 15, tg = tid >> 4;
-  const int vtok = tid >> 2, vcol = (tid & 3) * VPT;
+  const int vtok = tid >> 3, vcol = (tid & 7) * VPT;
 
   // Prefetch registers.
-  uint4 kr[4], qr[4];
-  float ldr[DCH ? 4 : 1][DCH ? 8 : 1];
-  float err[GEN ? 4 : 1][GEN ? 8 : 1];
+  uint4 kr[2], qr[2], tr;
+  float ldr[DCH ? 2 : 1][DCH ? 8 : 1];
+  float err[GEN ? 2 : 1][GEN ? 8 : 1];
   float lds = 0.f, gbs = 0.f, gws = 0.f;  // per-token (head) gates for token tid (< 64)
-  VRaw<DVS> vr;
+  VSlice<DVS> vr;
   float wr[GEN ? VPT : 1];
 
   auto tok = [&](int t) { return (int64_t(b) * T + t) * H + h; };
 
   auto load = [&](int c) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = c * C + 4 * tg + r;
+    for (int r = 0; r < 2; ++r) {
+      const int t = c * C + 2 * tg + r;
       const bool ok = t < T;
       const int64_t base = ok ? tok(t) * D + 8 * d8 : 0;
-      kr[r] = ok ? *reinterpret_cast<const uint4*>(kin + base) : make_uint4(0, 0, 0, 0);
-      qr[r] = ok ? *reinterpret_cast<const uint4*>(qin + base) : make_uint4(0, 0, 0, 0);
-      if constexpr (DCH) {
-        float4 a0 = ok ? *reinterpret_cast<const float4*>(p.log_decay + base) : make_float4(0, 0, 0, 0);
-        float4 a1 = ok ? *reinterpret_cast<const float4*>(p.log_decay + base + 4) : make_float4(0, 0, 0, 0);
-        ldr[r][0] = a0.x; ldr[r][1] = a0.y; ldr[r][2] = a0.z; ldr[r][3] = a0.w;
-        ldr[r][4] = a1.x; ldr[r][5] = a1.y; ldr[r][6] = a1.z; ldr[r][7] = a1.w;
-      }
+      kr[r] = ok ? gload_u4(kin, base) : make_uint4(0, 0, 0, 0);
+      qr[r] = ok ? gload_u4(qin, base) : make_uint4(0, 0, 0, 0);
+      if constexpr (DCH) unpack8(gld4(ldin, base, ok), gld4(ldin, base + 4, ok), ldr[r]);
       if constexpr (GEN) {
-        if (p.erase_channel) {
-          float4 e0 = ok ? *reinterpret_cast<const float4*>(p.erase + base) : make_float4(0, 0, 0, 0);
-          float4 e1 = ok ? *reinterpret_cast<const float4*>(p.erase + base + 4) : make_float4(0, 0, 0, 0);
-          err[r][0] = e0.x; err[r][1] = e0.y; err[r][2] = e0.z; err[r][3] = e0.w;
-          err[r][4] = e1.x; err[r][5] = e1.y; err[r][6] = e1.z; err[r][7] = e1.w;
-        }
+        if (p.erase_channel) unpack8(gld4(erin, base, ok), gld4(erin, base + 4, ok), err[r]);
       }
     }
     if (tid < C) {
       const int t = c * C + tid;
       const bool ok = t < T;
       const int64_t ti = ok ? tok(t) : 0;
-      if constexpr (!DCH) lds = ok ? p.log_decay[ti] : 0.f;
+      if constexpr (!DCH) lds = ok ? ldin[ti] : 0.f;
       if constexpr (GEN) {
-        gbs = (ok && !p.erase_channel) ? p.erase[ti] : 0.f;
-        gws = (ok && !p.write_channel) ? p.write[ti] : 0.f;
+        gbs = (ok && !p.erase_channel) ? erin[ti] : 0.f;
+        gws = (ok && !p.write_channel) ? wrin[ti] : 0.f;
       } else {
-        gbs = ok ? p.erase[ti] : 0.f;
+        gbs = ok ? erin[ti] : 0.f;
       }
     }
     {
       const int t = c * C + vtok;
       const bool ok = t < T;
       const int64_t vb = ok ? tok(t) * D + j0 + vcol : 0;
-      vraw_load<DVS>(vr, vin + vb, ok);
+      vslice_load<DVS>(vr, vin, vb, ok);
       if constexpr (GEN) {
         if (p.write_channel) {
+          if constexpr (VPT == 2) {
+            wr[0] = ok ? wrin[vb] : 0.f;
+            wr[1] = ok ? wrin[vb + 1] : 0.f;
+          } else {
 #pragma unroll
-          for (int i = 0; i < VPT; i += 4) {
-            float4 w4 = ok ? *reinterpret_cast<const float4*>(p.write + vb + i) : make_float4(0, 0, 0, 0);
-            wr[i] = w4.x; wr[i + 1] = w4.y; wr[i + 2] = w4.z; wr[i + 3] = w4.w;
+            for (int i = 0; i < VPT; i += 4) {
+              const float4 w4 = gld4(wrin, vb + i, ok);
+              wr[i] = w4.x; wr[i + 1] = w4.y; wr[i + 2] = w4.z; wr[i + 3] = w4.w;
+            }
           }
         }
       }
     }
+    tr = gload_u4(tbase, int64_t(c) * (C * C) + vtok * C + (tid & 7) * 8);
   };
 
   load(0);
 
   for (int c = 0; c < nchunks; ++c) {
     // ---- L1: chunk-local cumulative log-decay ------------------------------------------
-    float g[4][DCH ? 8 : 1];
     if (tid < C) {
       GB[tid] = gbs;
       if constexpr (GEN) GW[tid] = gws;
     }
-    if constexpr (DCH) {
-      float ex[8];
-#pragma unroll
-      for (int ch = 0; ch < 8; ++ch) {
-        float acc = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc += ldr[r][ch];
-          g[r][ch] = acc;
-        }
-        // inclusive scan of the quad totals over the 4 token quads of this wave (lanes 16 apart)
-        float x = acc, y;
-        y = __shfl_up(x, 16);
-        if (lg >= 1) x += y;
-        y = __shfl_up(x, 32);
-        if (lg >= 2) x += y;
-        ex[ch] = x - acc;
-        if (lg == 3) GSC[wave * D + 8 * d8 + ch] = x;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int ch = 0; ch < 8; ++ch) {
-        float pre = ex[ch];
-        for (int w = 0; w < wave; ++w) pre += GSC[w * D + 8 * d8 + ch];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) g[r][ch] += pre;
-      }
-    } else {
-      if (wave == 0) {
-        float x = lds;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float y = __shfl_up(x, off);
-          if (lane >= off) x += y;
-        }
-        GSC[lane] = x;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int r = 0; r < 4; ++r) g[r][0] = GSC[4 * tg + r];
-    }
-    auto gmid = [&](int d) { return DCH ? GSC[d] + GSC[D + d] : GSC[31]; };
-    auto gend = [&](int d) {
-      return DCH ? GSC[d] + GSC[D + d] + GSC[2 * D + d] + GSC[3 * D + d] : GSC[63];
-    };
+    float g[2][DCH ? 8 : 1];
+    scan_cumsum<DCH>(ldr, lds, g, GSC, tid);
 
-    // ---- L2: operand tiles ---------------------------------------------------------------
+    // ---- L2: operand tiles, T, value slice, S~^T ------------------------------------------
     {
       float gm[8];
 #pragma unroll
-      for (int ch = 0; ch < 8; ++ch) gm[ch] = gmid(8 * d8 + ch);
+      for (int ch = 0; ch < 8; ++ch) gm[ch] = scan_gmid<DCH>(GSC, 8 * d8 + ch);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * tg + r;
-        float kf[8], qf[8], fp[8], fm[8];
+      for (int r = 0; r < 2; ++r) {
+        const int t = 2 * tg + r;
+        float kf[8], qf[8], fp[8], fm[8], tmp[8];
         bf16x8_to_f32(kr[r], kf);
         bf16x8_to_f32(qr[r], qf);
+        if constexpr (DCH) {
 #pragma unroll
-        for (int ch = 0; ch < 8; ++ch) {
-          const float gg = DCH ? g[r][ch] : g[r][0];
-          fp[ch] = clamped_exp(gg - gm[ch]);
-          fm[ch] = clamped_exp(gm[ch] - gg);
+          for (int ch = 0; ch < 8; ++ch) {
+            fp[ch] = clamped_exp(g[r][ch] - gm[ch]);
+            fm[ch] = clamped_exp(gm[ch] - g[r][ch]);
+          }
+        } else {
+          const float a = clamped_exp(g[r][0] - gm[0]), bb = clamped_exp(gm[0] - g[r][0]);
+#pragma unroll
+          for (int ch = 0; ch < 8; ++ch) {
+            fp[ch] = a;
+            fm[ch] = bb;
+          }
         }
-        *reinterpret_cast<half8*>(KP + t * KS + 8 * d8) =
-            cvt8(kf[0] * fp[0], kf[1] * fp[1], kf[2] * fp[2], kf[3] * fp[3], kf[4] * fp[4],
-                 kf[5] * fp[5], kf[6] * fp[6], kf[7] * fp[7]);
-        *reinterpret_cast<half8*>(QP + t * KS + 8 * d8) =
-            cvt8(qf[0] * fp[0], qf[1] * fp[1], qf[2] * fp[2], qf[3] * fp[3], qf[4] * fp[4],
-                 qf[5] * fp[5], qf[6] * fp[6], qf[7] * fp[7]);
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) tmp[ch] = kf[ch] * fp[ch];
+        *reinterpret_cast<half8*>(KP + t * KS + 8 * d8) = cvt8(tmp);
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) tmp[ch] = qf[ch] * fp[ch];
+        *reinterpret_cast<half8*>(QP + t * KS + 8 * d8) = cvt8(tmp);
         float km[8];
 #pragma unroll
         for (int ch = 0; ch < 8; ++ch) km[ch] = kf[ch] * fm[ch];
-        *reinterpret_cast<half8*>(KM + t * KS + 8 * d8) =
-            cvt8(km[0], km[1], km[2], km[3], km[4], km[5], km[6], km[7]);
+        *reinterpret_cast<half8*>(KM + t * KS + 8 * d8) = cvt8(km);
         if constexpr (GEN) {
-          float e[8];
-          if (p.erase_channel) {
+          const float eb = GB[t];
 #pragma unroll
-            for (int ch = 0; ch < 8; ++ch) e[ch] = err[r][ch];
-          } else {
-            const float eb = GB[t];
-#pragma unroll
-            for (int ch = 0; ch < 8; ++ch) e[ch] = eb;
-          }
-          *reinterpret_cast<half8*>(UM + t * KS + 8 * d8) =
-              cvt8(e[0] * km[0], e[1] * km[1], e[2] * km[2], e[3] * km[3], e[4] * km[4],
-                   e[5] * km[5], e[6] * km[6], e[7] * km[7]);
+          for (int ch = 0; ch < 8; ++ch) tmp[ch] = (p.erase_channel ? err[r][ch] : eb) * km[ch];
+          *reinterpret_cast<half8*>(UM + t * KS + 8 * d8) = cvt8(tmp);
         }
       }
+      *reinterpret_cast<uint4*>(TH + vtok * CS + (tid & 7) * 8) = tr;
       // value slice
       float vf[VPT];
-      vraw_f32<DVS>(vr, vf);
+      vslice_f32<DVS>(vr, vf);
       if constexpr (GEN) {
         const float wb = GW[vtok];
 #pragma unroll
@@ -381,191 +632,155 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Problem p) {
       }
     }
     // S~^T = (Diag(e^{gm}) S)^T and the per-row end-of-chunk factors of this wave's rows.
-    float fC[2][4], fCm[2][4];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    float fC[4], fCm[4];
+    {
       float em[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int d = 32 * wave + 16 * rt + 4 * lg + r;
-        const float gmd = gmid(d), gCd = gend(d);
+        const int d = 16 * wave + 4 * lg + r;
+        const float gmd = scan_gmid<DCH>(GSC, d), gCd = scan_gend<DCH>(GSC, d);
         em[r] = clamped_exp(gmd);
-        fC[rt][r] = expf(gCd);
-        fCm[rt][r] = clamped_exp(gCd - gmd);
+        fC[r] = expf(gCd);
+        fCm[r] = clamped_exp(gCd - gmd);
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         half4v hv;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(em[r] * S[rt][ct][r]);
-        *reinterpret_cast<half4v*>(ST + (16 * ct + l16) * KS + 32 * wave + 16 * rt + 4 * lg) = hv;
+        for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(em[r] * S[ct][r]);
+        *reinterpret_cast<half4v*>(ST + (16 * ct + l16) * KS + 16 * wave + 4 * lg) = hv;
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (c + 1 < nchunks) load(c + 1);  // overlaps the matrix work of this chunk
 
-    // ---- G: Gram matrices and X = [K+; Q+] S~ ------------------------------------------
-    constexpr int NG = GEN ? 40 : 20;
-    for (int idx = wave; idx < NG; idx += 4) {
-      const int which = idx / 10;  // 0: A_kk, 1: A_qk, 2: A_ku, 3: A_qu
-      int I, J;
-      tile_ij(idx - 10 * which, I, J);
-      const _Float16* Ab = (which == 1 || which == 3) ? QP : KP;
-      const _Float16* Bb = (which >= 2) ? UM : KM;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // ---- G: Gram matrices (transposed tiles) and X = [K+; Q+] S~ -------------------------
+    constexpr int NG = GEN ? 30 : 10;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        acc = mfma16x16x32(frag(Ab, KS, 16 * I, 32 * ks, lane), frag(Bb, KS, 16 * J, 32 * ks, lane), acc);
-      const int i = 16 * J + l16;
+    for (int n = 0; n < (NG + kScanWaves - 1) / kScanWaves; ++n) {
+      const int idx = wave + kScanWaves * n;
+      if (idx < NG) {
+        const int which = idx / 10;  // 0: A_qk, 1: A_kk, 2: A_qu
+        int I, J;
+        tile_ij(idx - 10 * which, I, J);
+        const _Float16* Ab = which == 2 ? UM : KM;
+        const _Float16* Bb = which == 1 ? KP : QP;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * I + 4 * lg + r;
-        if (which == 0) {
-          const float v = (i < t) ? acc[r] : 0.f;
-          if constexpr (GEN)
-            AKK[t * CS + i] = (_Float16)v;
-          else
-            AF[t * AFS + i] = GB[t] * v;
-        } else if (which == 1) {
-          AQ[t * CS + i] = (_Float16)((i <= t) ? acc[r] : 0.f);
-        } else if (which == 2) {
-          AF[t * AFS + i] = (i < t) ? acc[r] : 0.f;
-        } else {
-          AQU[t * CS + i] = (_Float16)((i <= t) ? acc[r] : 0.f);
-        }
-      }
-    }
-    f32x4 XK[NCT], XQ[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      f32x4 xk = {0.f, 0.f, 0.f, 0.f}, xq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const half8 bs = frag(ST, KS, 16 * ct, 32 * ks, lane);
-        xk = mfma16x16x32(frag(KP, KS, 16 * wave, 32 * ks, lane), bs, xk);
-        xq = mfma16x16x32(frag(QP, KS, 16 * wave, 32 * ks, lane), bs, xq);
-      }
-      XK[ct] = xk;
-      XQ[ct] = xq;
-      if constexpr (!GEN) {
-        // R = Diag(beta) (V - X_K), stored transposed
+        for (int ks = 0; ks < 4; ++ks)
+          acc = mfma16x16x32(frag(Ab, KS, 16 * J, 32 * ks, lane), frag(Bb, KS, 16 * I, 32 * ks, lane), acc);
+        const int t = 16 * I + l16;
+        const int i0 = 16 * J + 4 * lg;
+        const bool strict = which == 1;
         half4v hv;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * wave + 4 * lg + r;
-          const float vv = (float)VT[t * L::vstride + 16 * ct + l16];
-          hv[r] = (_Float16)(GB[t] * (vv - xk[r]));
-        }
-        *reinterpret_cast<half4v*>(RT + (16 * ct + l16) * CS + 16 * wave + 4 * lg) = hv;
+        for (int r = 0; r < 4; ++r) hv[r] = (_Float16)((strict ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f);
+        _Float16* dstm = which == 0 ? AQ : which == 1 ? AKK : AQU;
+        *reinterpret_cast<half4v*>(dstm + t * CS + i0) = hv;
       }
     }
-    __syncthreads();
-
-    // ---- S1: inverse of the four 16x16 diagonal blocks (fp32 forward substitution) --------
-    if (wave == 0) {
-      const int blk = lg, col = l16;
-      const float* Ab = AF + (16 * blk) * AFS + 16 * blk;
-      float x[16];
+    // X: waves 0-3 compute X_K rows [16 w, +16), waves 4-7 X_Q rows [16 (w - 4), +16).
+    const int xrow = 16 * (wave & 3);
+    const bool xq_wave = wave >= 4;
+    f32x4 XR[NCT];
+    {
+      const _Float16* Xa = xq_wave ? QP : KP;
+      half8 af[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s0 = (r == col) ? 1.f : 0.f, s1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < r; i += 2) {
-          s0 = fmaf(-Ab[r * AFS + i], x[i], s0);
-          if (i + 1 < r) s1 = fmaf(-Ab[r * AFS + i + 1], x[i + 1], s1);
-        }
-        x[r] = s0 + s1;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) TH[(16 * blk + r) * CS + 16 * blk + col] = (_Float16)x[r];
-    }
-    if constexpr (GEN) {
-      // Y = X_K + A_kk Vt, stored transposed (B operand of M = T Y)
+      for (int ks = 0; ks < 4; ++ks) af[ks] = frag(Xa, KS, xrow, 32 * ks, lane);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        f32x4 y = XK[ct];
-        for (int ks = 0; ks <= (wave >> 1); ++ks)
-          y = mfma16x16x32(frag(AKK, CS, 16 * wave, 32 * ks, lane), frag(VT, CS, 16 * ct, 32 * ks, lane), y);
-        half4v hv;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hv[r] = (_Float16)y[r];
-        *reinterpret_cast<half4v*>(RT + (16 * ct + l16) * CS + 16 * wave + 4 * lg) = hv;
+        for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(af[ks], frag(ST, KS, 16 * ct, 32 * ks, lane), acc);
+        XR[ct] = acc;
+        if constexpr (!GEN) {
+          if (!xq_wave) {
+            // R = Diag(beta) (V - X_K), stored transposed
+            half4v hv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = xrow + 4 * lg + r;
+              const float vv = (float)VT[t * L::vstride + 16 * ct + l16];
+              hv[r] = (_Float16)(GB[t] * (vv - acc[r]));
+            }
+            *reinterpret_cast<half4v*>(RT + (16 * ct + l16) * CS + xrow + 4 * lg) = hv;
+          }
+        }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- S2: off-diagonal blocks, T_JI = -T_JJ sum_{K=I}^{J-1} A_JK T_KI -----------------
+    if constexpr (GEN) {
+      // Y = X_K + A_kk Vt, stored transposed (B operand of M = T Y)
+      if (!xq_wave) {
 #pragma unroll
-    for (int Jb = 1; Jb < 4; ++Jb) {
-      if (wave < Jb) {
-        const int Ib = wave;
-        f32x4 P = {0.f, 0.f, 0.f, 0.f};
-        for (int Kb = Ib; Kb < Jb; ++Kb) {
-          // the fp32 rows are 65 floats apart (bank spread), so read them one by one
-          const float* arow = AF + (16 * Jb + l16) * AFS + 16 * Kb + 4 * lg;
-          half4v a, bt;
+        for (int ct = 0; ct < NCT; ++ct) {
+          f32x4 y = XR[ct];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            a[i] = (_Float16)arow[i];
-            bt[i] = TH[(16 * Kb + 4 * lg + i) * CS + 16 * Ib + l16];
-          }
-          P = mfma16(a, bt, P);
+          for (int ks = 0; ks < 2; ++ks)
+            if (ks <= (wave >> 1))
+              y = mfma16x16x32(frag(AKK, CS, xrow, 32 * ks, lane), frag(VT, CS, 16 * ct, 32 * ks, lane), y);
+          half4v hv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) hv[r] = (_Float16)y[r];
+          *reinterpret_cast<half4v*>(RT + (16 * ct + l16) * CS + xrow + 4 * lg) = hv;
         }
-        half4v nb, a2;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) nb[i] = (_Float16)(-P[i]);
-        a2 = *reinterpret_cast<const half4v*>(TH + (16 * Jb + l16) * CS + 16 * Jb + 4 * lg);
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 Tji = mfma16(a2, nb, z);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) TH[(16 * Jb + 4 * lg + r) * CS + 16 * Ib + l16] = (_Float16)Tji[r];
       }
-      __syncthreads();
+      lds_barrier();
     }
 
     // ---- D: delta = T R (symmetric) or -M = -(T Y) (general), stored transposed ---------
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
+    for (int n = wave; n < 4 * NCT; n += kScanWaves) {
+      const int i = n & 3, ct = n >> 2;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks <= (wave >> 1); ++ks)
-        acc = mfma16x16x32(frag(TH, CS, 16 * wave, 32 * ks, lane), frag(RT, CS, 16 * ct, 32 * ks, lane), acc);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        if (ks <= (i >> 1))
+          acc = mfma16x16x32(frag(TH, CS, 16 * i, 32 * ks, lane), frag(RT, CS, 16 * ct, 32 * ks, lane), acc);
       half4v hv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(GEN ? -acc[r] : acc[r]);
-      *reinterpret_cast<half4v*>(DT + (16 * ct + l16) * CS + 16 * wave + 4 * lg) = hv;
+      *reinterpret_cast<half4v*>(DT + (16 * ct + l16) * CS + 16 * i + 4 * lg) = hv;
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- O: chunk output rows [16 w, 16 w + 16) ------------------------------------------
+    // ---- O: chunk output rows [16 (w - 4), +16), waves 4-7 --------------------------------
+    if (xq_wave) {
+      const int i = wave & 3;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      f32x4 acc = XQ[ct];
-      for (int ks = 0; ks <= (wave >> 1); ++ks) {
-        if constexpr (GEN) {
-          acc = mfma16x16x32(frag(AQ, CS, 16 * wave, 32 * ks, lane), frag(VT, CS, 16 * ct, 32 * ks, lane), acc);
-          acc = mfma16x16x32(frag(AQU, CS, 16 * wave, 32 * ks, lane), frag(DT, CS, 16 * ct, 32 * ks, lane), acc);
-        } else {
-          acc = mfma16x16x32(frag(AQ, CS, 16 * wave, 32 * ks, lane), frag(DT, CS, 16 * ct, 32 * ks, lane), acc);
+      for (int ct = 0; ct < NCT; ++ct) {
+        f32x4 acc = XR[ct];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if (ks <= (i >> 1)) {
+            if constexpr (GEN) {
+              acc = mfma16x16x32(frag(AQ, CS, 16 * i, 32 * ks, lane), frag(VT, CS, 16 * ct, 32 * ks, lane), acc);
+              acc = mfma16x16x32(frag(AQU, CS, 16 * i, 32 * ks, lane), frag(DT, CS, 16 * ct, 32 * ks, lane), acc);
+            } else {
+              acc = mfma16x16x32(frag(AQ, CS, 16 * i, 32 * ks, lane), frag(DT, CS, 16 * ct, 32 * ks, lane), acc);
+            }
+          }
         }
-      }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = c * C + 16 * wave + 4 * lg + r;
-        if (t < T) out[tok(t) * D + j0 + 16 * ct + l16] = acc[r];
+        for (int r = 0; r < 4; ++r) {
+          const int t = c * C + 16 * i + 4 * lg + r;
+          if (t < T) store_o(p.o, tok(t) * D + j0 + 16 * ct + l16, acc[r], p.o_bf16);
+        }
       }
     }
 
     // ---- S: state update for this wave's rows ---------------------------------------------
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    {
       f32x4 acc[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const half8 ak = frag_t(KM, 32 * wave + 16 * rt, 32 * ks, lane);
+        const half8 ak = frag_t(KM, 16 * wave, 32 * ks, lane);
         half8 au;
-        if constexpr (GEN) au = frag_t(UM, 32 * wave + 16 * rt, 32 * ks, lane);
+        if constexpr (GEN) au = frag_t(UM, 16 * wave, 32 * ks, lane);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const half8 bd = frag(DT, CS, 16 * ct, 32 * ks, lane);
@@ -580,50 +795,62 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Problem p) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[rt][ct][r] = fmaf(fC[rt][r], S[rt][ct][r], fCm[rt][r] * acc[ct][r]);
+        for (int r = 0; r < 4; ++r) S[ct][r] = fmaf(fC[r], S[ct][r], fCm[r] * acc[ct][r]);
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   if (p.S_T) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int d = 32 * wave + 16 * rt + 4 * lg + r;
-          p.S_T[(int64_t(bh) * D + d) * D + j0 + 16 * ct + l16] = S[rt][ct][r];
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int d = 16 * wave + 4 * lg + r;
+        p.S_T[(int64_t(bh) * D + d) * D + j0 + 16 * ct + l16] = S[ct][r];
+      }
   }
 }
 
 template <bool DCH, bool GEN, int DVS>
-hipError_t launch_cfg(const Problem& p, hipStream_t stream) {
+hipError_t launch_scan(const Problem& p, const _Float16* tws, hipStream_t stream) {
   dim3 grid(unsigned(p.B * p.H), unsigned(D / DVS));
-  hipLaunchKernelGGL((chunk_kernel<DCH, GEN, DVS>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((chunk_scan_kernel<DCH, GEN, DVS>), grid, dim3(kScanThreads), 0, stream, p, tws);
   return hipGetLastError();
 }
 
 template <bool DCH, bool GEN>
-hipError_t launch_dvs(const Problem& p, hipStream_t stream) {
+hipError_t launch_variant(const Problem& p, void* workspace, hipStream_t stream) {
+  const int nchunks = (p.T + C - 1) / C;
+  _Float16* tws = static_cast<_Float16*>(workspace);
+  const int64_t nblk = int64_t(p.B) * p.H * nchunks;
+  hipLaunchKernelGGL((chunk_prep_kernel<DCH, GEN>), dim3(unsigned(nblk)), dim3(kThreads), 0, stream, p, tws,
+                     nchunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   // Fill the 256 compute units with (b, h, value-slice) workgroups while keeping the slices
-  // (each recomputes its chunk's Gram matrices and solve) as wide as that allows.
+  // (each rebuilds its chunk's operand tiles and Gram matrices) as wide as that allows.
   const int64_t bh = int64_t(p.B) * p.H;
   if constexpr (!GEN) {
-    if (bh >= 128) return launch_cfg<DCH, GEN, 64>(p, stream);
+    if (bh >= 128) return launch_scan<DCH, GEN, 64>(p, tws, stream);
   }
-  if (bh >= 64) return launch_cfg<DCH, GEN, 32>(p, stream);
-  return launch_cfg<DCH, GEN, 16>(p, stream);
+  if (bh >= 64) return launch_scan<DCH, GEN, 32>(p, tws, stream);
+  return launch_scan<DCH, GEN, 16>(p, tws, stream);
 }
 
 }  // namespace
 
-hipError_t launch_chunk128(const Problem& p, hipStream_t stream) {
+size_t chunk128_workspace_bytes(int B, int T, int H) {
+  const int64_t nchunks = (int64_t(T) + C - 1) / C;
+  return size_t(int64_t(B) * H * nchunks * C * C * sizeof(_Float16));
+}
+
+hipError_t launch_chunk128(const Problem& p, void* workspace, hipStream_t stream) {
   const bool symmetric = !p.erase_channel && !p.write_channel && p.write == p.erase;
   if (p.decay_channel)
-    return symmetric ? launch_dvs<true, false>(p, stream) : launch_dvs<true, true>(p, stream);
-  return symmetric ? launch_dvs<false, false>(p, stream) : launch_dvs<false, true>(p, stream);
+    return symmetric ? launch_variant<true, false>(p, workspace, stream)
+                     : launch_variant<true, true>(p, workspace, stream);
+  return symmetric ? launch_variant<false, false>(p, workspace, stream)
+                   : launch_variant<false, true>(p, workspace, stream);
 }
 
 }  // namespace dr

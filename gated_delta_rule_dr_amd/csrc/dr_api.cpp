@@ -109,6 +109,11 @@ dr::Problem make_problem(const dr_desc* d, const void* q, const void* k, const v
   return p;
 }
 
+// The matrix-core path: bf16 q/k/v, dk == dv == 128, chunk 0 or 64, at least one token.
+bool uses_chunk128(const dr_desc* d) {
+  return d->qkv_dtype == DR_BF16 && d->dk == 128 && d->dv == 128 && d->chunk != 1 && d->T > 0;
+}
+
 int launched(hipError_t launch_err) {
   if (launch_err != hipSuccess) return DR_E_HIP;
   return hipGetLastError() == hipSuccess ? DR_OK : DR_E_HIP;
@@ -138,7 +143,8 @@ const char* dr_status_str(int status) {
 size_t dr_chunk_fwd_workspace_bytes(const dr_desc* desc) {
   Extents ex;
   if (check_desc(desc, false, &ex) != DR_OK) return 0;
-  return 0;
+  if (!uses_chunk128(desc)) return 0;
+  return dr::chunk128_workspace_bytes(desc->B, desc->T, desc->H);
 }
 
 int dr_chunk_fwd(const dr_desc* d, const void* q, const void* k, const void* v,
@@ -169,6 +175,10 @@ int dr_chunk_fwd(const dr_desc* d, const void* q, const void* k, const void* v,
   for (int i = 0; i < 6; ++i)
     if (overlaps(rs, rin[i])) return DR_E_ALIAS;
   if (S0 != nullptr && S_T != nullptr && S0 != S_T && overlaps(rs, rin[6])) return DR_E_ALIAS;
+  const Range rw = range_of(workspace, workspace_bytes);
+  for (const Range& r : rin)
+    if (overlaps(rw, r)) return DR_E_ALIAS;
+  if (overlaps(rw, ro) || overlaps(rw, rs)) return DR_E_ALIAS;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (d->T == 0) {
@@ -176,8 +186,7 @@ int dr_chunk_fwd(const dr_desc* d, const void* q, const void* k, const void* v,
     return launched(dr::launch_state_copy(S0, S_T, int64_t(ex.state / 4), s));
   }
   dr::Problem p = make_problem(d, q, k, v, log_decay, erase, write, S0, o, S_T);
-  const bool mfma_path = d->qkv_dtype == DR_BF16 && d->dk == 128 && d->dv == 128 && d->chunk != 1;
-  if (mfma_path) return launched(dr::launch_chunk128(p, s));
+  if (uses_chunk128(d)) return launched(dr::launch_chunk128(p, workspace, s));
   return launched(dr::launch_recurrent(p, s));
 }
 

@@ -41,4 +41,46 @@ __device__ __forceinline__ f32x4 mfma16x16x32(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations and meets the
+// other waves, but leaves global loads in flight (a __syncthreads() fence would also wait for
+// every outstanding global load, which defeats prefetching the next chunk across stages).  The
+// memory clobber keeps the compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Global-address-space pointer.
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
+
+// Returns `p` as a global pointer passed through an empty asm, so the compiler no longer knows
+// the pointee is read-only for the whole kernel.  Loads through the result are then ordinary
+// global loads that lds_barrier() keeps in place, instead of invariant loads the compiler may
+// sink to their first use (which would turn a next-chunk prefetch into a stall).
+template <typename T>
+__device__ __forceinline__ gptr<T> opaque_gptr(T* p) {
+  gptr<T> g = (gptr<T>)p;
+  asm volatile("" : "+s"(g));
+  return g;
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Vector loads from global element `i` of `base` (16 or 8 bytes, element type T).
+template <typename T>
+__device__ __forceinline__ uint4 gload_u4(gptr<const T> base, int64_t i) {
+  const u32x4 x = *(gptr<const u32x4>)(base + i);
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+template <typename T>
+__device__ __forceinline__ uint2 gload_u2(gptr<const T> base, int64_t i) {
+  const u32x2 x = *(gptr<const u32x2>)(base + i);
+  return make_uint2(x.x, x.y);
+}
+__device__ __forceinline__ float4 gload_f4(gptr<const float> base, int64_t i) {
+  const f32x4 x = *(gptr<const f32x4>)(base + i);
+  return make_float4(x.x, x.y, x.z, x.w);
+}
+
 }  // namespace dr

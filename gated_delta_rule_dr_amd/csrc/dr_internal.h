@@ -34,8 +34,10 @@ hipError_t launch_recurrent(const Problem& p, hipStream_t stream);
 // Single-token decode with the state updated in place (S0 == S_T == S), dk == dv == 128.
 hipError_t launch_decode128(const Problem& p, hipStream_t stream);
 
-// MFMA chunked forward, bf16 q/k/v, dk == dv == 128, chunk 64.
-hipError_t launch_chunk128(const Problem& p, hipStream_t stream);
+// MFMA chunked forward, bf16 q/k/v, dk == dv == 128, chunk 64.  `workspace` holds at least
+// chunk128_workspace_bytes(B, T, H) bytes (one fp16 64 x 64 matrix per chunk).
+size_t chunk128_workspace_bytes(int B, int T, int H);
+hipError_t launch_chunk128(const Problem& p, void* workspace, hipStream_t stream);
 
 // S_T = S0 (copy) or zeros when S0 is null: n floats.
 hipError_t launch_state_copy(const float* S0, float* S_T, int64_t n, hipStream_t stream);

@@ -91,7 +91,10 @@ int dr_abi_version(void);
 const char* dr_status_str(int status);
 
 /* Bytes of device workspace dr_chunk_fwd needs for `desc` (0 when none), or 0 for an invalid
- * descriptor.  The current kernels need none; callers pass what this returns. */
+ * descriptor.  The matrix-core path stores one fp16 64 x 64 matrix (the chunk's triangular-solve
+ * factor, 8 KiB) per 64-token chunk of every (b, h): B * H * ceil(T / 64) * 8192 bytes; the
+ * token-by-token path needs none.  The caller allocates it (any device memory, 16-byte aligned,
+ * not overlapping the other arguments) and may reuse it once the call's work has finished. */
 size_t dr_chunk_fwd_workspace_bytes(const dr_desc* desc);
 
 /* Prefill / training forward over T tokens (the chunkwise-parallel form the pages describe:

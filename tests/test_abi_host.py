@@ -60,7 +60,7 @@ def _fwd(desc, **over):
     return _abi.lib().dr_chunk_fwd(ctypes.byref(desc) if desc is not None else None,
                                    vp(ptr["q"]), vp(ptr["k"]), vp(ptr["v"]), vp(ptr["ld"]), vp(ptr["e"]),
                                    vp(ptr["w"]), vp(ptr["S0"]), vp(ptr["o"]), vp(ptr["ST"]),
-                                   vp(ptr.get("wsp")), ptr.get("wsn", 0), None)
+                                   vp(ptr["ws"]), ptr.get("wsn", 1 << 30), None)
 
 
 def _dec(desc, **over):
@@ -122,11 +122,23 @@ def test_aliasing():
     assert _dec(_good_desc(T=1), S0=P["e"]) == _abi.DR_E_ALIAS
 
 
-def test_workspace_query():
+def test_workspace_query_and_errors():
     L = _abi.lib()
-    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc())) == 0
+    # matrix-core path: one 64 x 64 fp16 matrix per chunk of every (b, h)
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc())) == 2 * 4 * 2 * 64 * 64 * 2
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(T=64))) == 2 * 4 * 1 * 64 * 64 * 2
+    # token path and empty sequences need none
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(chunk=1))) == 0
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(qkv_dtype=_abi.DR_F32))) == 0
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(T=0))) == 0
     assert L.dr_chunk_fwd_workspace_bytes(None) == 0
     assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(B=0))) == 0
+    need = L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc()))
+    assert _fwd(_good_desc(), wsn=need - 1) == _abi.DR_E_WORKSPACE
+    assert _fwd(_good_desc(), ws=None, wsn=0) == _abi.DR_E_WORKSPACE
+    assert _fwd(_good_desc(), ws=P["ws"] + 8, wsn=need) == _abi.DR_E_ALIGN
+    assert _fwd(_good_desc(), ws=P["q"], wsn=need) == _abi.DR_E_ALIAS
+    assert _fwd(_good_desc(), ws=P["o"] + 4096, wsn=need) == _abi.DR_E_ALIAS
 
 
 def test_descriptor_layout():

@@ -131,6 +131,14 @@ def test_bf16_output(dr):
     assert err_o(o.float(), ro) <= 2 ** -8
 
 
+def test_bf16_output_chunk_path(dr):
+    inp = _case(1, 130, 2, 128, 128, "bf16", "kda", True, 6)
+    o, S = _run(dr, inp, o_dtype=torch.bfloat16)
+    ro, rS = _oracle(inp)
+    assert o.dtype == torch.bfloat16
+    assert err_o(o.float(), ro) <= TOL_BF16 + 2 ** -8 and err_S(S, rS) <= TOL_BF16
+
+
 def test_in_place_state_carry(dr):
     inp = _case(2, 90, 2, 128, 128, "bf16", "kda", True, 9)
     d = _dev(inp)
