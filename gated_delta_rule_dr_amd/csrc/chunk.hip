@@ -165,13 +165,22 @@ __device__ __forceinline__ float chunk_gend(const float* GSC, int d) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Prep: T = (I + A)^{-1} for one chunk, A = Diag(beta) A_kk (symmetric) or A_ku (general).
+// Prep: per chunk, the state-independent matrices, written to the workspace as fp16 64 x 64
+// row-major (upper triangles zero), in this order per chunk:
+//   symmetric gates: T = (I + Diag(beta) A_kk)^{-1}, A_qk
+//   general gates:   T = (I + A_ku)^{-1},           A_qk, A_kk, A_qu
 // ------------------------------------------------------------------------------------------
+template <bool GEN>
+constexpr int prep_mats() { return GEN ? 4 : 2; }
+
 template <bool DCH, bool GEN>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, _Float16* __restrict__ tws,
                                                               int nchunks) {
-  __shared__ __attribute__((aligned(16))) _Float16 KP[C * KS];   // K+
-  __shared__ __attribute__((aligned(16))) _Float16 KB[C * KS];   // K- (symmetric) or U- (general)
+  constexpr int NM = prep_mats<GEN>();
+  __shared__ __attribute__((aligned(16))) _Float16 KP[C * KS];                 // K+
+  __shared__ __attribute__((aligned(16))) _Float16 KM[C * KS];                 // K-
+  __shared__ __attribute__((aligned(16))) _Float16 QP[C * KS];                 // Q+
+  __shared__ __attribute__((aligned(16))) _Float16 UM[GEN ? C * KS : 8];       // U- (general)
   __shared__ __attribute__((aligned(16))) float AF[C * AFS];
   __shared__ __attribute__((aligned(16))) _Float16 TH[C * CS];
   __shared__ float GB[C];
@@ -185,11 +194,13 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, _Float1
   const int b = bh / p.H, h = bh - b * p.H;
   const int T = p.T, H = p.H;
   const uint16_t* kin = static_cast<const uint16_t*>(p.k);
+  const uint16_t* qin = static_cast<const uint16_t*>(p.q);
+  _Float16* wsc = tws + blk * (NM * C * C);  // this chunk's matrices
   auto tok = [&](int t) { return (int64_t(b) * T + t) * H + h; };
 
   for (int i = tid; i < C * CS; i += kThreads) TH[i] = (_Float16)0.f;
 
-  uint4 kr[4];
+  uint4 kr[4], qr[4];
   float ldr[DCH ? 4 : 1][DCH ? 8 : 1];
   float err[GEN ? 4 : 1][GEN ? 8 : 1];
   float lds = 0.f;
@@ -199,6 +210,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, _Float1
     const bool ok = t < T;
     const int64_t base = ok ? tok(t) * D + 8 * d8 : 0;
     kr[r] = ok ? *reinterpret_cast<const uint4*>(kin + base) : make_uint4(0, 0, 0, 0);
+    qr[r] = ok ? *reinterpret_cast<const uint4*>(qin + base) : make_uint4(0, 0, 0, 0);
     if constexpr (DCH) unpack8(ld4(p.log_decay + base, ok), ld4(p.log_decay + base + 4, ok), ldr[r]);
     if constexpr (GEN) {
       if (p.erase_channel) unpack8(ld4(p.erase + base, ok), ld4(p.erase + base + 4, ok), err[r]);
@@ -222,42 +234,73 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, _Float1
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 4 * tg + r;
-      float kf[8], kp[8], kb[8];
+      float kf[8], qf[8], kp[8], km[8], qp[8];
       bf16x8_to_f32(kr[r], kf);
+      bf16x8_to_f32(qr[r], qf);
 #pragma unroll
       for (int ch = 0; ch < 8; ++ch) {
         const float gg = DCH ? g[r][ch] : g[r][0];
-        kp[ch] = kf[ch] * clamped_exp(gg - gm[ch]);
-        float e = 1.f;
-        if constexpr (GEN) e = p.erase_channel ? err[r][ch] : GB[t];
-        kb[ch] = e * kf[ch] * clamped_exp(gm[ch] - gg);
+        const float fp = clamped_exp(gg - gm[ch]), fm = clamped_exp(gm[ch] - gg);
+        kp[ch] = kf[ch] * fp;
+        qp[ch] = qf[ch] * fp;
+        km[ch] = kf[ch] * fm;
       }
       *reinterpret_cast<half8*>(KP + t * KS + 8 * d8) = cvt8(kp);
-      *reinterpret_cast<half8*>(KB + t * KS + 8 * d8) = cvt8(kb);
+      *reinterpret_cast<half8*>(QP + t * KS + 8 * d8) = cvt8(qp);
+      *reinterpret_cast<half8*>(KM + t * KS + 8 * d8) = cvt8(km);
+      if constexpr (GEN) {
+        float um[8];
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) um[ch] = (p.erase_channel ? err[r][ch] : GB[t]) * km[ch];
+        *reinterpret_cast<half8*>(UM + t * KS + 8 * d8) = cvt8(um);
+      }
     }
   }
   lds_barrier();
 
   // Gram tiles, transposed: lane gets A[t = 16 I + l16][i = 16 J + 4 lg + r].
+  //   0: A for the solve (symmetric: beta_t A_kk; general: A_ku), strict, fp32 to LDS
+  //   1: A_qk (lower), 2: A_kk (strict), 3: A_qu (lower), fp16 to the workspace
+  constexpr int NG = 10 * NM;
 #pragma unroll
-  for (int n = 0; n < 3; ++n) {
+  for (int n = 0; n < (NG + 3) / 4; ++n) {
     const int idx = wave + 4 * n;
-    if (idx < 10) {
+    if (idx < NG) {
+      const int which = idx / 10;
       int I, J;
-      tile_ij(idx, I, J);
+      tile_ij(idx - 10 * which, I, J);
+      const _Float16* Ab = (which == 3 || (GEN && which == 0)) ? UM : KM;
+      const _Float16* Bb = (which == 1 || which == 3) ? QP : KP;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        acc = mfma16x16x32(frag(KB, KS, 16 * J, 32 * ks, lane), frag(KP, KS, 16 * I, 32 * ks, lane), acc);
+        acc = mfma16x16x32(frag(Ab, KS, 16 * J, 32 * ks, lane), frag(Bb, KS, 16 * I, 32 * ks, lane), acc);
       const int t = 16 * I + l16;
-      const float sc = GEN ? 1.f : GB[t];
-      float4 v;
-      v.x = (16 * J + 4 * lg + 0 < t) ? sc * acc[0] : 0.f;
-      v.y = (16 * J + 4 * lg + 1 < t) ? sc * acc[1] : 0.f;
-      v.z = (16 * J + 4 * lg + 2 < t) ? sc * acc[2] : 0.f;
-      v.w = (16 * J + 4 * lg + 3 < t) ? sc * acc[3] : 0.f;
-      *reinterpret_cast<float4*>(AF + t * AFS + 16 * J + 4 * lg) = v;
+      const int i0 = 16 * J + 4 * lg;
+      if (which == 0) {
+        const float sc = GEN ? 1.f : GB[t];
+        float4 v;
+        v.x = (i0 + 0 < t) ? sc * acc[0] : 0.f;
+        v.y = (i0 + 1 < t) ? sc * acc[1] : 0.f;
+        v.z = (i0 + 2 < t) ? sc * acc[2] : 0.f;
+        v.w = (i0 + 3 < t) ? sc * acc[3] : 0.f;
+        *reinterpret_cast<float4*>(AF + t * AFS + i0) = v;
+      } else {
+        const bool strict = which == 2;
+        half4v hv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hv[r] = (_Float16)((strict ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f);
+        *reinterpret_cast<half4v*>(wsc + which * (C * C) + t * C + i0) = hv;
+      }
     }
+  }
+  // upper-triangular 16 x 16 tiles of the workspace matrices after T are zero
+  for (int n = wave; n < 6 * (NM - 1); n += 4) {
+    const int m = 1 + n / 6, u = n % 6;
+    const int I = u < 3 ? 0 : u < 5 ? 1 : 2;           // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+    const int J = u < 3 ? 1 + u : u < 5 ? u - 1 : 3;
+    const half4v z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+    *reinterpret_cast<half4v*>(wsc + m * (C * C) + (16 * I + l16) * C + 16 * J + 4 * lg) = z;
   }
   lds_barrier();
 
@@ -311,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, _Float1
   {
     const int t = tid >> 2, c0 = (tid & 3) * 16;
     const uint4* src = reinterpret_cast<const uint4*>(TH + t * CS + c0);
-    uint4* dst = reinterpret_cast<uint4*>(tws + blk * (C * C) + t * C + c0);
+    uint4* dst = reinterpret_cast<uint4*>(wsc + t * C + c0);
     dst[0] = src[0];
     dst[1] = src[1];
   }
@@ -476,16 +519,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   const gptr<const float> ldin = opaque_gptr(p.log_decay);
   const gptr<const float> erin = opaque_gptr(p.erase);
   const gptr<const float> wrin = opaque_gptr(p.write);
-  const gptr<const _Float16> tbase = opaque_gptr(tws) + int64_t(bh) * nchunks * (C * C);
-
-  // Matrices whose upper-triangular blocks are read as zeros by full-width fragments.
-  for (int i = tid; i < C * CS; i += kScanThreads) {
-    AQ[i] = (_Float16)0.f;
-    if constexpr (GEN) {
-      AKK[i] = (_Float16)0.f;
-      AQU[i] = (_Float16)0.f;
-    }
-  }
+  constexpr int NM = prep_mats<GEN>();
+  const gptr<const _Float16> tbase = opaque_gptr(tws) + int64_t(bh) * nchunks * (NM * C * C);
 
   // State: wave w owns rows [16 w, 16 w + 16) x the DVS columns as NCT accumulator tiles
   // (lane: column 16 ct + l16, rows 16 w + 4 lg + r).
@@ -504,74 +539,89 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   const int d8 = tid & 15, tg = tid >> 4;
   const int vtok = tid >> 3, vcol = (tid & 7) * VPT;
 
-  // Prefetch registers.
-  uint4 kr[2], qr[2], tr;
-  float ldr[DCH ? 2 : 1][DCH ? 8 : 1];
-  float err[GEN ? 2 : 1][GEN ? 8 : 1];
-  float lds = 0.f, gbs = 0.f, gws = 0.f;  // per-token (head) gates for token tid (< 64)
-  VSlice<DVS> vr;
-  float wr[GEN ? VPT : 1];
+  // Prefetch registers for one chunk; two sets alternate so that each chunk's loads are
+  // issued two chunks ahead of their use.
+  struct Pref {
+    uint4 kr[2], qr[2], mr[NM];  // mr: this thread's 16 bytes of T, A_qk (, A_kk, A_qu)
+    float ldr[DCH ? 2 : 1][DCH ? 8 : 1];
+    float err[GEN ? 2 : 1][GEN ? 8 : 1];
+    float lds, gbs, gws;  // per-token (head) gates for token tid (< 64)
+    VSlice<DVS> vr;
+    float wr[GEN ? VPT : 1];
+  };
 
   auto tok = [&](int t) { return (int64_t(b) * T + t) * H + h; };
 
-  auto load = [&](int c) {
+  // The loads of one chunk are issued in three batches, one per compute stage, so that the
+  // vector-memory path stays busy without stalling every wave at one point.
+  auto load_kq = [&](Pref& P, int c) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int t = c * C + 2 * tg + r;
       const bool ok = t < T;
       const int64_t base = ok ? tok(t) * D + 8 * d8 : 0;
-      kr[r] = ok ? gload_u4(kin, base) : make_uint4(0, 0, 0, 0);
-      qr[r] = ok ? gload_u4(qin, base) : make_uint4(0, 0, 0, 0);
-      if constexpr (DCH) unpack8(gld4(ldin, base, ok), gld4(ldin, base + 4, ok), ldr[r]);
+      P.kr[r] = ok ? gload_u4(kin, base) : make_uint4(0, 0, 0, 0);
+      P.qr[r] = ok ? gload_u4(qin, base) : make_uint4(0, 0, 0, 0);
+      if constexpr (DCH) unpack8(gld4(ldin, base, ok), gld4(ldin, base + 4, ok), P.ldr[r]);
       if constexpr (GEN) {
-        if (p.erase_channel) unpack8(gld4(erin, base, ok), gld4(erin, base + 4, ok), err[r]);
+        if (p.erase_channel) unpack8(gld4(erin, base, ok), gld4(erin, base + 4, ok), P.err[r]);
       }
     }
+  };
+  auto load_mats = [&](Pref& P, int c) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+      P.mr[m] = gload_u4(tbase, (int64_t(c) * NM + m) * (C * C) + vtok * C + (tid & 7) * 8);
+  };
+  auto load_rest = [&](Pref& P, int c) {
     if (tid < C) {
       const int t = c * C + tid;
       const bool ok = t < T;
       const int64_t ti = ok ? tok(t) : 0;
-      if constexpr (!DCH) lds = ok ? ldin[ti] : 0.f;
+      P.lds = (!DCH && ok) ? ldin[ti] : 0.f;
       if constexpr (GEN) {
-        gbs = (ok && !p.erase_channel) ? erin[ti] : 0.f;
-        gws = (ok && !p.write_channel) ? wrin[ti] : 0.f;
+        P.gbs = (ok && !p.erase_channel) ? erin[ti] : 0.f;
+        P.gws = (ok && !p.write_channel) ? wrin[ti] : 0.f;
       } else {
-        gbs = ok ? erin[ti] : 0.f;
+        P.gbs = ok ? erin[ti] : 0.f;
+        P.gws = 0.f;
       }
     }
     {
       const int t = c * C + vtok;
       const bool ok = t < T;
       const int64_t vb = ok ? tok(t) * D + j0 + vcol : 0;
-      vslice_load<DVS>(vr, vin, vb, ok);
+      vslice_load<DVS>(P.vr, vin, vb, ok);
       if constexpr (GEN) {
         if (p.write_channel) {
           if constexpr (VPT == 2) {
-            wr[0] = ok ? wrin[vb] : 0.f;
-            wr[1] = ok ? wrin[vb + 1] : 0.f;
+            P.wr[0] = ok ? wrin[vb] : 0.f;
+            P.wr[1] = ok ? wrin[vb + 1] : 0.f;
           } else {
 #pragma unroll
             for (int i = 0; i < VPT; i += 4) {
               const float4 w4 = gld4(wrin, vb + i, ok);
-              wr[i] = w4.x; wr[i + 1] = w4.y; wr[i + 2] = w4.z; wr[i + 3] = w4.w;
+              P.wr[i] = w4.x; P.wr[i + 1] = w4.y; P.wr[i + 2] = w4.z; P.wr[i + 3] = w4.w;
             }
           }
         }
       }
     }
-    tr = gload_u4(tbase, int64_t(c) * (C * C) + vtok * C + (tid & 7) * 8);
+  };
+  auto load = [&](Pref& P, int c) {
+    load_kq(P, c);
+    load_mats(P, c);
+    load_rest(P, c);
   };
 
-  load(0);
-
-  for (int c = 0; c < nchunks; ++c) {
+  auto step = [&](int c, Pref& P) {
     // ---- L1: chunk-local cumulative log-decay ------------------------------------------
     if (tid < C) {
-      GB[tid] = gbs;
-      if constexpr (GEN) GW[tid] = gws;
+      GB[tid] = P.gbs;
+      if constexpr (GEN) GW[tid] = P.gws;
     }
     float g[2][DCH ? 8 : 1];
-    scan_cumsum<DCH>(ldr, lds, g, GSC, tid);
+    scan_cumsum<DCH>(P.ldr, P.lds, g, GSC, tid);
 
     // ---- L2: operand tiles, T, value slice, S~^T ------------------------------------------
     {
@@ -582,8 +632,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       for (int r = 0; r < 2; ++r) {
         const int t = 2 * tg + r;
         float kf[8], qf[8], fp[8], fm[8], tmp[8];
-        bf16x8_to_f32(kr[r], kf);
-        bf16x8_to_f32(qr[r], qf);
+        bf16x8_to_f32(P.kr[r], kf);
+        bf16x8_to_f32(P.qr[r], qf);
         if constexpr (DCH) {
 #pragma unroll
           for (int ch = 0; ch < 8; ++ch) {
@@ -611,19 +661,24 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
         if constexpr (GEN) {
           const float eb = GB[t];
 #pragma unroll
-          for (int ch = 0; ch < 8; ++ch) tmp[ch] = (p.erase_channel ? err[r][ch] : eb) * km[ch];
+          for (int ch = 0; ch < 8; ++ch) tmp[ch] = (p.erase_channel ? P.err[r][ch] : eb) * km[ch];
           *reinterpret_cast<half8*>(UM + t * KS + 8 * d8) = cvt8(tmp);
         }
       }
-      *reinterpret_cast<uint4*>(TH + vtok * CS + (tid & 7) * 8) = tr;
+      *reinterpret_cast<uint4*>(TH + vtok * CS + (tid & 7) * 8) = P.mr[0];
+      *reinterpret_cast<uint4*>(AQ + vtok * CS + (tid & 7) * 8) = P.mr[1];
+      if constexpr (GEN) {
+        *reinterpret_cast<uint4*>(AKK + vtok * CS + (tid & 7) * 8) = P.mr[2 % NM];
+        *reinterpret_cast<uint4*>(AQU + vtok * CS + (tid & 7) * 8) = P.mr[3 % NM];
+      }
       // value slice
       float vf[VPT];
-      vslice_f32<DVS>(vr, vf);
+      vslice_f32<DVS>(P.vr, vf);
       if constexpr (GEN) {
         const float wb = GW[vtok];
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-          const float w = p.write_channel ? wr[i] : wb;
+          const float w = p.write_channel ? P.wr[i] : wb;
           VT[(vcol + i) * CS + vtok] = (_Float16)(w * vf[i]);
         }
       } else {
@@ -652,33 +707,10 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       }
     }
     lds_barrier();
-    if (c + 1 < nchunks) load(c + 1);  // overlaps the matrix work of this chunk
+    const bool pf = c + 2 < nchunks;  // prefetch chunk c + 2, in flight for two chunks
+    if (pf) load_kq(P, c + 2);
 
-    // ---- G: Gram matrices (transposed tiles) and X = [K+; Q+] S~ -------------------------
-    constexpr int NG = GEN ? 30 : 10;
-#pragma unroll
-    for (int n = 0; n < (NG + kScanWaves - 1) / kScanWaves; ++n) {
-      const int idx = wave + kScanWaves * n;
-      if (idx < NG) {
-        const int which = idx / 10;  // 0: A_qk, 1: A_kk, 2: A_qu
-        int I, J;
-        tile_ij(idx - 10 * which, I, J);
-        const _Float16* Ab = which == 2 ? UM : KM;
-        const _Float16* Bb = which == 1 ? KP : QP;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          acc = mfma16x16x32(frag(Ab, KS, 16 * J, 32 * ks, lane), frag(Bb, KS, 16 * I, 32 * ks, lane), acc);
-        const int t = 16 * I + l16;
-        const int i0 = 16 * J + 4 * lg;
-        const bool strict = which == 1;
-        half4v hv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hv[r] = (_Float16)((strict ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f);
-        _Float16* dstm = which == 0 ? AQ : which == 1 ? AKK : AQU;
-        *reinterpret_cast<half4v*>(dstm + t * CS + i0) = hv;
-      }
-    }
+    // ---- X = [K+; Q+] S~ ----------------------------------------------------------------
     // X: waves 0-3 compute X_K rows [16 w, +16), waves 4-7 X_Q rows [16 (w - 4), +16).
     const int xrow = 16 * (wave & 3);
     const bool xq_wave = wave >= 4;
@@ -691,8 +723,13 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // X_K as is (lane: rows t, column j); X_Q transposed (lane: rows j, column t) so that
+        // the output tile it seeds can be stored as 16-byte rows of o.
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(af[ks], frag(ST, KS, 16 * ct, 32 * ks, lane), acc);
+        for (int ks = 0; ks < 4; ++ks) {
+          const half8 bs = frag(ST, KS, 16 * ct, 32 * ks, lane);
+          acc = xq_wave ? mfma16x16x32(bs, af[ks], acc) : mfma16x16x32(af[ks], bs, acc);
+        }
         XR[ct] = acc;
         if constexpr (!GEN) {
           if (!xq_wave) {
@@ -730,6 +767,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       lds_barrier();
     }
 
+    if (pf) load_mats(P, c + 2);
     // ---- D: delta = T R (symmetric) or -M = -(T Y) (general), stored transposed ---------
 #pragma unroll
     for (int n = wave; n < 4 * NCT; n += kScanWaves) {
@@ -746,28 +784,28 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
     }
     lds_barrier();
 
+    if (pf) load_rest(P, c + 2);
     // ---- O: chunk output rows [16 (w - 4), +16), waves 4-7 --------------------------------
     if (xq_wave) {
+      // O^T tile: lane holds O[t = 16 i + l16][j = 16 ct + 4 lg + 0..3]
       const int i = wave & 3;
+      const int t = c * C + 16 * i + l16;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         f32x4 acc = XR[ct];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           if (ks <= (i >> 1)) {
+            const half8 bq = frag(AQ, CS, 16 * i, 32 * ks, lane);
             if constexpr (GEN) {
-              acc = mfma16x16x32(frag(AQ, CS, 16 * i, 32 * ks, lane), frag(VT, CS, 16 * ct, 32 * ks, lane), acc);
-              acc = mfma16x16x32(frag(AQU, CS, 16 * i, 32 * ks, lane), frag(DT, CS, 16 * ct, 32 * ks, lane), acc);
+              acc = mfma16x16x32(frag(VT, CS, 16 * ct, 32 * ks, lane), bq, acc);
+              acc = mfma16x16x32(frag(DT, CS, 16 * ct, 32 * ks, lane), frag(AQU, CS, 16 * i, 32 * ks, lane), acc);
             } else {
-              acc = mfma16x16x32(frag(AQ, CS, 16 * i, 32 * ks, lane), frag(DT, CS, 16 * ct, 32 * ks, lane), acc);
+              acc = mfma16x16x32(frag(DT, CS, 16 * ct, 32 * ks, lane), bq, acc);
             }
           }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = c * C + 16 * i + 4 * lg + r;
-          if (t < T) store_o(p.o, tok(t) * D + j0 + 16 * ct + l16, acc[r], p.o_bf16);
-        }
+        if (t < T) store_o4(p.o, tok(t) * D + j0 + 16 * ct + 4 * lg, acc, p.o_bf16);
       }
     }
 
@@ -798,6 +836,14 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
         for (int r = 0; r < 4; ++r) S[ct][r] = fmaf(fC[r], S[ct][r], fCm[r] * acc[ct][r]);
     }
     lds_barrier();
+  };
+
+  Pref PA, PB;
+  load(PA, 0);
+  if (nchunks > 1) load(PB, 1);
+  for (int c = 0; c < nchunks; c += 2) {
+    step(c, PA);
+    if (c + 1 < nchunks) step(c + 1, PB);
   }
 
   if (p.S_T) {
@@ -839,13 +885,14 @@ hipError_t launch_variant(const Problem& p, void* workspace, hipStream_t stream)
 
 }  // namespace
 
-size_t chunk128_workspace_bytes(int B, int T, int H) {
+size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric) {
   const int64_t nchunks = (int64_t(T) + C - 1) / C;
-  return size_t(int64_t(B) * H * nchunks * C * C * sizeof(_Float16));
+  const int64_t nmat = symmetric ? prep_mats<false>() : prep_mats<true>();
+  return size_t(int64_t(B) * H * nchunks * nmat * C * C * sizeof(_Float16));
 }
 
 hipError_t launch_chunk128(const Problem& p, void* workspace, hipStream_t stream) {
-  const bool symmetric = !p.erase_channel && !p.write_channel && p.write == p.erase;
+  const bool symmetric = p.symmetric;
   if (p.decay_channel)
     return symmetric ? launch_variant<true, false>(p, workspace, stream)
                      : launch_variant<true, true>(p, workspace, stream);

@@ -83,6 +83,9 @@ int check_ptr(const void* p, uint64_t bytes, bool required) {
   return aligned16(p) ? DR_OK : DR_E_ALIGN;
 }
 
+// One per-head gate serves as both erase and write gate.
+bool is_symmetric(const dr_desc* d) { return d->write_is_erase && d->erase_kind == DR_GATE_HEAD; }
+
 dr::Problem make_problem(const dr_desc* d, const void* q, const void* k, const void* v,
                          const float* log_decay, const float* erase, const float* write,
                          const float* S0, void* o, float* S_T) {
@@ -103,6 +106,7 @@ dr::Problem make_problem(const dr_desc* d, const void* q, const void* k, const v
   p.log_decay = log_decay;
   p.erase = erase;
   p.write = d->write_is_erase ? erase : write;
+  p.symmetric = is_symmetric(d);
   p.S0 = S0;
   p.o = o;
   p.S_T = S_T;
@@ -144,7 +148,7 @@ size_t dr_chunk_fwd_workspace_bytes(const dr_desc* desc) {
   Extents ex;
   if (check_desc(desc, false, &ex) != DR_OK) return 0;
   if (!uses_chunk128(desc)) return 0;
-  return dr::chunk128_workspace_bytes(desc->B, desc->T, desc->H);
+  return dr::chunk128_workspace_bytes(desc->B, desc->T, desc->H, is_symmetric(desc));
 }
 
 int dr_chunk_fwd(const dr_desc* d, const void* q, const void* k, const void* v,

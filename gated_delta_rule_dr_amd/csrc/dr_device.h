@@ -34,6 +34,18 @@ __device__ __forceinline__ void store_o(void* p, int64_t i, float x, bool bf16) 
     static_cast<float*>(p)[i] = x;
 }
 
+// Four consecutive outputs (16-byte aligned for fp32, 8-byte for bf16).
+__device__ __forceinline__ void store_o4(void* p, int64_t i, f32x4 x, bool bf16) {
+  if (bf16) {
+    uint2 w;
+    w.x = uint32_t(f32_to_bf16(x[0])) | (uint32_t(f32_to_bf16(x[1])) << 16);
+    w.y = uint32_t(f32_to_bf16(x[2])) | (uint32_t(f32_to_bf16(x[3])) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = w;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(p) + i) = x;
+  }
+}
+
 // 16x16x32 fp16 matrix-core product with fp32 accumulation (CDNA4).
 // Lane l supplies A[row = l % 16][k = 8 * (l / 16) + 0..7] and B[k = 8 * (l / 16) + 0..7]
 // [col = l % 16]; it receives D[row = 4 * (l / 16) + 0..3][col = l % 16].

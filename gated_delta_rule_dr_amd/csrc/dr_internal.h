@@ -16,6 +16,7 @@ struct Problem {
   int decay_channel;   // log_decay is [B,T,H,dk]
   int erase_channel;   // erase is [B,T,H,dk]
   int write_channel;   // write is [B,T,H,dv]
+  int symmetric;       // one per-head gate is both erase and write (write is erase)
   const void* q;
   const void* k;
   const void* v;
@@ -35,8 +36,9 @@ hipError_t launch_recurrent(const Problem& p, hipStream_t stream);
 hipError_t launch_decode128(const Problem& p, hipStream_t stream);
 
 // MFMA chunked forward, bf16 q/k/v, dk == dv == 128, chunk 64.  `workspace` holds at least
-// chunk128_workspace_bytes(B, T, H) bytes (one fp16 64 x 64 matrix per chunk).
-size_t chunk128_workspace_bytes(int B, int T, int H);
+// chunk128_workspace_bytes(B, T, H, symmetric) bytes: per chunk, 2 (symmetric gates) or 4
+// (general gates) fp16 64 x 64 matrices.
+size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric);
 hipError_t launch_chunk128(const Problem& p, void* workspace, hipStream_t stream);
 
 // S_T = S0 (copy) or zeros when S0 is null: n floats.

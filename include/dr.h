@@ -91,8 +91,10 @@ int dr_abi_version(void);
 const char* dr_status_str(int status);
 
 /* Bytes of device workspace dr_chunk_fwd needs for `desc` (0 when none), or 0 for an invalid
- * descriptor.  The matrix-core path stores one fp16 64 x 64 matrix (the chunk's triangular-solve
- * factor, 8 KiB) per 64-token chunk of every (b, h): B * H * ceil(T / 64) * 8192 bytes; the
+ * descriptor.  The matrix-core path stores, per 64-token chunk of every (b, h), the chunk's
+ * state-independent fp16 64 x 64 matrices (the triangular-solve factor and the in-chunk
+ * decay-weighted Gram matrices): 2 of them (16 KiB) when one per-head gate is both erase and
+ * write gate, 4 (32 KiB) otherwise, i.e. B * H * ceil(T / 64) * 16384 or 32768 bytes; the
  * token-by-token path needs none.  The caller allocates it (any device memory, 16-byte aligned,
  * not overlapping the other arguments) and may reuse it once the call's work has finished. */
 size_t dr_chunk_fwd_workspace_bytes(const dr_desc* desc);

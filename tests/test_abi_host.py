@@ -124,9 +124,13 @@ def test_aliasing():
 
 def test_workspace_query_and_errors():
     L = _abi.lib()
-    # matrix-core path: one 64 x 64 fp16 matrix per chunk of every (b, h)
-    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc())) == 2 * 4 * 2 * 64 * 64 * 2
-    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(T=64))) == 2 * 4 * 1 * 64 * 64 * 2
+    # matrix-core path: per chunk of every (b, h), 2 (symmetric gates) or 4 fp16 64 x 64 matrices
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc())) == 2 * 4 * 2 * 2 * 64 * 64 * 2
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(T=64))) == 2 * 4 * 1 * 2 * 64 * 64 * 2
+    gen = _good_desc(erase_kind=_abi.DR_GATE_CHANNEL)
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(gen)) == 2 * 4 * 2 * 4 * 64 * 64 * 2
+    gen2 = _good_desc(write_is_erase=0)
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(gen2)) == 2 * 4 * 2 * 4 * 64 * 64 * 2
     # token path and empty sequences need none
     assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(chunk=1))) == 0
     assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(qkv_dtype=_abi.DR_F32))) == 0
