@@ -21,10 +21,16 @@
 //   O = X_Q + A_qk Vt - A_qu M,  S <- Diag(e^{g_C}) S + Diag(e^{g_C - gm}) (K-^T Vt - U-^T M)
 //
 // Two kernels.  chunk_prep_kernel runs one workgroup per chunk (all chunks of all heads in
-// parallel) and computes the only state-independent factor that needs a serial algorithm,
-// T, into the caller's workspace (fp16, 64 x 64 per chunk).  chunk_scan_kernel then walks the
-// chunks of one (b, h, value slice) in order, carrying the fp32 state in registers: it builds
-// the decayed operand tiles, the remaining Gram matrices and every state-dependent product.
+// parallel) and writes everything that does not depend on the state into a per-chunk packet
+// in the caller's workspace: T (the only factor that needs a serial algorithm), the Gram
+// matrices, the gate factors and, unless the decay is one scalar per token, the decayed fp16
+// operand tiles K+, Q+, K-^T (and U-^T).  chunk_scan_kernel then walks the chunks of one
+// (b, h, value slice) in order, carrying the fp32 state in registers; per chunk it copies the
+// packet into LDS and runs only the state-dependent products, so no exponential, prefix sum
+// or format conversion is repeated by the value slices of a head.  With a scalar decay the
+// packet holds no operand tiles: the scan stages the plain k and q and applies the per-token
+// factors e^{+-(g_t - gm)} to product rows instead.
+//
 // Products use v_mfma_f32_16x16x32_f16 (fp16 operands, fp32 accumulation).  Gram tiles are
 // computed transposed (A^T = K- Q+^T) so that each lane owns four consecutive columns of one
 // row of A and stores them with one vector write.
@@ -40,6 +46,7 @@ namespace dr {
 namespace {
 
 typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int C = 64;      // chunk length
 constexpr int D = 128;     // dk == dv
@@ -101,6 +108,16 @@ __device__ __forceinline__ float4 gld4(gptr<const float> p, int64_t i, bool ok) 
 
 __device__ __forceinline__ void unpack8(float4 a, float4 b, float* f) {
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// 16 bytes at byte offset `off` of a global byte pointer.
+__device__ __forceinline__ uint4 ldb16(gptr<const char> base, int64_t off) {
+  const u32x4 x = *(gptr<const u32x4>)(base + off);
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ float4 ldf16(gptr<const char> base, int64_t off) {
+  const f32x4 x = *(gptr<const f32x4>)(base + off);
+  return make_float4(x.x, x.y, x.z, x.w);
 }
 
 // Chunk-local inclusive prefix sums of the log-decay.  Thread (token quad tg, channel octet
@@ -165,18 +182,36 @@ __device__ __forceinline__ float chunk_gend(const float* GSC, int d) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Prep: per chunk, the state-independent matrices, written to the workspace as fp16 64 x 64
-// row-major (upper triangles zero), in this order per chunk:
-//   symmetric gates: T = (I + Diag(beta) A_kk)^{-1}, A_qk
-//   general gates:   T = (I + A_ku)^{-1},           A_qk, A_kk, A_qu
+// Per-chunk packet in the workspace (byte offsets).  Matrices are fp16 64 x 64 row-major with
+// zero upper triangles, in the order T, A_qk (, A_kk, A_qu for general gates); tiles are fp16
+// row-major without padding; the gate vector is fp32.
+//   scalar decay, symmetric gates: matrices, gates {beta[64], e^{g-gm}[64], e^{gm-g}[64],
+//                                  e^{gm}, e^{gC}, e^{gC-gm}}
+//   otherwise: matrices, K+ [64][128], Q+ [64][128], K-^T [128][64] (, U-^T [128][64]),
+//              gates {beta[64] (symmetric gates), e^{gm}[128], e^{gC}[128], e^{gC-gm}[128]}
 // ------------------------------------------------------------------------------------------
-template <bool GEN>
-constexpr int prep_mats() { return GEN ? 4 : 2; }
+template <bool DCH, bool GEN>
+struct Packet {
+  static constexpr bool kScal = !DCH && !GEN;
+  static constexpr int nmat = GEN ? 4 : 2;
+  static constexpr int mat = 0;
+  static constexpr int kp = mat + nmat * C * C * 2;
+  static constexpr int qp = kp + (kScal ? 0 : C * D * 2);
+  static constexpr int kmt = qp + (kScal ? 0 : C * D * 2);
+  static constexpr int umt = kmt + (kScal ? 0 : D * C * 2);
+  static constexpr int gate = umt + (GEN ? D * C * 2 : 0);
+  static constexpr int ngate = 512;  // floats
+  static constexpr int bytes = gate + ngate * 4;
+};
+// gate-vector slots (floats)
+constexpr int GV_BETA = 0;                            // [64]
+constexpr int GV_FP = 64, GV_FM = 128, GV_SC = 192;   // scalar decay
+constexpr int GV_EM = 64, GV_FC = 192, GV_FCM = 320;  // per-channel decay, [128] each
 
 template <bool DCH, bool GEN>
-__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, _Float16* __restrict__ tws,
-                                                              int nchunks) {
-  constexpr int NM = prep_mats<GEN>();
+__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, char* __restrict__ ws, int nchunks) {
+  using PK = Packet<DCH, GEN>;
+  constexpr int NM = PK::nmat;
   __shared__ __attribute__((aligned(16))) _Float16 KP[C * KS];                 // K+
   __shared__ __attribute__((aligned(16))) _Float16 KM[C * KS];                 // K-
   __shared__ __attribute__((aligned(16))) _Float16 QP[C * KS];                 // Q+
@@ -195,7 +230,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, _Float1
   const int T = p.T, H = p.H;
   const uint16_t* kin = static_cast<const uint16_t*>(p.k);
   const uint16_t* qin = static_cast<const uint16_t*>(p.q);
-  _Float16* wsc = tws + blk * (NM * C * C);  // this chunk's matrices
+  char* pk = ws + blk * PK::bytes;           // this chunk's packet
+  _Float16* wsc = reinterpret_cast<_Float16*>(pk + PK::mat);
+  float* gv = reinterpret_cast<float*>(pk + PK::gate);
   auto tok = [&](int t) { return (int64_t(b) * T + t) * H + h; };
 
   for (int i = tid; i < C * CS; i += kThreads) TH[i] = (_Float16)0.f;
@@ -256,6 +293,27 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, _Float1
       }
     }
   }
+  // gate vector
+  if constexpr (PK::kScal) {
+    if (tid < C) {
+      const float x = GSC[tid] - GSC[31];
+      gv[GV_BETA + tid] = GB[tid];
+      gv[GV_FP + tid] = clamped_exp(x);
+      gv[GV_FM + tid] = clamped_exp(-x);
+    } else if (tid == C) {
+      const float gmid = GSC[31], gend = GSC[63];
+      *reinterpret_cast<float4*>(gv + GV_SC) =
+          make_float4(clamped_exp(gmid), expf(gend), clamped_exp(gend - gmid), 0.f);
+    }
+  } else {
+    if (tid < C) gv[GV_BETA + tid] = GB[tid];
+    if (tid < D) {
+      const float gmid = chunk_gmid<DCH>(GSC, tid), gend = chunk_gend<DCH>(GSC, tid);
+      gv[GV_EM + tid] = clamped_exp(gmid);
+      gv[GV_FC + tid] = expf(gend);
+      gv[GV_FCM + tid] = clamped_exp(gend - gmid);
+    }
+  }
   lds_barrier();
 
   // Gram tiles, transposed: lane gets A[t = 16 I + l16][i = 16 J + 4 lg + r].
@@ -301,6 +359,29 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, _Float1
     const int J = u < 3 ? 1 + u : u < 5 ? u - 1 : 3;
     const half4v z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
     *reinterpret_cast<half4v*>(wsc + m * (C * C) + (16 * I + l16) * C + 16 * J + 4 * lg) = z;
+  }
+  // operand tiles for the scan: K+, Q+ as is; K-, U- transposed ([channel][token])
+  if constexpr (!PK::kScal) {
+#pragma unroll
+    for (int i = 0; i < C * D / 8 / kThreads; ++i) {
+      const int u = tid + kThreads * i;
+      const int t = u >> 4, c8 = (u & 15) * 8;
+      *reinterpret_cast<uint4*>(pk + PK::kp + 16 * u) = *reinterpret_cast<const uint4*>(KP + t * KS + c8);
+      *reinterpret_cast<uint4*>(pk + PK::qp + 16 * u) = *reinterpret_cast<const uint4*>(QP + t * KS + c8);
+    }
+#pragma unroll
+    for (int i = 0; i < C * D / 8 / kThreads; ++i) {
+      const int d = tid & (D - 1), t0 = 8 * ((tid >> 7) + 2 * i);
+      half8 x;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = KM[(t0 + j) * KS + d];
+      *reinterpret_cast<half8*>(pk + PK::kmt + 2 * (d * C + t0)) = x;
+      if constexpr (GEN) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = UM[(t0 + j) * KS + d];
+        *reinterpret_cast<half8*>(pk + PK::umt + 2 * (d * C + t0)) = x;
+      }
+    }
   }
   lds_barrier();
 
@@ -366,29 +447,29 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, _Float1
 constexpr int kScanWaves = 8;
 constexpr int kScanThreads = 64 * kScanWaves;
 
-template <bool GEN, int DVS>
+// SCAL (scalar decay, symmetric gates): KP / QP hold the plain k and q.
+template <bool GEN, bool SCAL, int DVS>
 struct ScanLayout {
-  static constexpr int kp = 0;                          // K+  [64][KS] half
-  static constexpr int qp = kp + C * KS * 2;            // Q+  [64][KS]
-  static constexpr int km = qp + C * KS * 2;            // K-  [64][KS]
-  static constexpr int um = km + C * KS * 2;            // U-  [64][KS]      (general)
-  static constexpr int st = um + (GEN ? C * KS * 2 : 0);  // S~^T [DVS][KS]
-  static constexpr int th = st + DVS * KS * 2;          // T      [64][CS] half
-  static constexpr int aq = th + C * CS * 2;            // A_qk   [64][CS]
-  static constexpr int akk = aq + C * CS * 2;           // A_kk   [64][CS]   (general)
-  static constexpr int aqu = akk + (GEN ? C * CS * 2 : 0);  // A_qu [64][CS] (general)
-  static constexpr int rt = aqu + (GEN ? C * CS * 2 : 0);   // R^T / Y^T [DVS][CS]
-  static constexpr int dt = rt + DVS * CS * 2;          // delta^T / (-M)^T [DVS][CS]
-  static constexpr int vt = dt + DVS * CS * 2;          // V [64][DVS+8] or Vt^T [DVS][CS]
+  static constexpr int kp = 0;                                // K+ / k   [64][KS] half
+  static constexpr int qp = kp + C * KS * 2;                  // Q+ / q   [64][KS]
+  static constexpr int kmt = qp + C * KS * 2;                 // K-^T     [128][CS] (not SCAL)
+  static constexpr int umt = kmt + (SCAL ? 0 : D * CS * 2);   // U-^T     [128][CS] (general)
+  static constexpr int st = umt + (GEN ? D * CS * 2 : 0);     // S~^T     [DVS][KS]
+  static constexpr int th = st + DVS * KS * 2;                // T        [64][CS]
+  static constexpr int aq = th + C * CS * 2;                  // A_qk     [64][CS]
+  static constexpr int akk = aq + C * CS * 2;                 // A_kk     [64][CS]  (general)
+  static constexpr int aqu = akk + (GEN ? C * CS * 2 : 0);    // A_qu     [64][CS]  (general)
+  static constexpr int rt = aqu + (GEN ? C * CS * 2 : 0);     // R^T / Y^T [DVS][CS]
+  static constexpr int dt = rt + DVS * CS * 2;                // delta^T / (-M)^T [DVS][CS]
+  static constexpr int dt2 = dt + DVS * CS * 2;               // SCAL: (Diag(e^{gm-g}) delta)^T
+  static constexpr int vt = dt2 + (SCAL ? DVS * CS * 2 : 0);  // V [64][DVS+8] or Vt^T [DVS][CS]
   static constexpr int vstride = GEN ? CS : DVS + 8;
   static constexpr int vbytes = GEN ? DVS * CS * 2 : C * (DVS + 8) * 2;
-  static constexpr int gb = vt + vbytes;                // per-token erase / beta [64] f32
-  static constexpr int gw = gb + C * 4;                 // per-token write [64] f32 (general)
-  static constexpr int gsc = gw + C * 4;                // per-wave log-decay totals [8][128] f32
-  static constexpr int total = gsc + kScanWaves * D * 4;
+  static constexpr int gv = vt + vbytes;                      // gate vector [512] f32
+  static constexpr int total = gv + (GEN ? 0 : 512 * 4);
 };
 
-// Value-slice words per thread: DVS/8 bf16 values (and DVS/8 fp32 write gates).
+// Value-slice words per thread: DVS/8 bf16 values.
 template <int DVS> struct VSlice;
 template <> struct VSlice<16> { uint32_t w; };
 template <> struct VSlice<32> { uint2 w; };
@@ -417,82 +498,23 @@ __device__ __forceinline__ void vslice_f32(const VSlice<DVS>& v, float* f) {
   }
 }
 
-// Chunk-local prefix sums of the log-decay for the eight-wave layout: thread (token pair tg,
-// channel octet d8) holds tokens 2 tg and 2 tg + 1.  On return g[r][ch] (per head: g[r][0]) is
-// the cumulative log-decay of its tokens, and GSC holds the per-wave totals ([8][128]; wave w
-// covers tokens 8 w .. 8 w + 7) or, per head, the 64 per-token prefixes.
-template <bool DCH>
-__device__ __forceinline__ void scan_cumsum(const float (&ldr)[DCH ? 2 : 1][DCH ? 8 : 1], float lds,
-                                            float (&g)[2][DCH ? 8 : 1], float* GSC, int tid) {
-  const int lane = tid & 63, wave = tid >> 6, lg = lane >> 4, d8 = tid & 15, tg = tid >> 4;
-  if constexpr (DCH) {
-    float ex[8];
-#pragma unroll
-    for (int ch = 0; ch < 8; ++ch) {
-      g[0][ch] = ldr[0][ch];
-      const float acc = ldr[0][ch] + ldr[1][ch];
-      g[1][ch] = acc;
-      float x = acc, y;
-      y = __shfl_up(x, 16);
-      if (lg >= 1) x += y;
-      y = __shfl_up(x, 32);
-      if (lg >= 2) x += y;
-      ex[ch] = x - acc;
-      if (lg == 3) GSC[wave * D + 8 * d8 + ch] = x;
-    }
-    lds_barrier();
-#pragma unroll
-    for (int ch = 0; ch < 8; ++ch) {
-      float pre = ex[ch];
-#pragma unroll
-      for (int w = 0; w < kScanWaves - 1; ++w)
-        if (w < wave) pre += GSC[w * D + 8 * d8 + ch];
-      g[0][ch] += pre;
-      g[1][ch] += pre;
-    }
-  } else {
-    if (wave == 0) {
-      float x = lds;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-      }
-      GSC[lane] = x;
-    }
-    lds_barrier();
-    g[0][0] = GSC[2 * tg];
-    g[1][0] = GSC[2 * tg + 1];
-  }
-}
-
-template <bool DCH>
-__device__ __forceinline__ float scan_gmid(const float* GSC, int d) {
-  return DCH ? GSC[d] + GSC[D + d] + GSC[2 * D + d] + GSC[3 * D + d] : GSC[31];
-}
-
-template <bool DCH>
-__device__ __forceinline__ float scan_gend(const float* GSC, int d) {
-  if constexpr (DCH) {
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < kScanWaves; ++w) s += GSC[w * D + d];
-    return s;
-  } else {
-    return GSC[63];
-  }
-}
-
-template <bool DCH, bool GEN, int DVS>
-__global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, const _Float16* __restrict__ tws) {
-  using L = ScanLayout<GEN, DVS>;
+// WCH: per-channel write gate (general gates only).
+template <bool DCH, bool GEN, bool WCH, int DVS>
+__global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, const char* __restrict__ ws) {
+  using PK = Packet<DCH, GEN>;
+  constexpr bool SCAL = PK::kScal;
+  using L = ScanLayout<GEN, SCAL, DVS>;
+  constexpr int NM = PK::nmat;
   constexpr int NCT = DVS / 16;   // 16-column tiles of the value slice
   constexpr int VPT = DVS / 8;    // value columns per thread in the V load
+  constexpr int NTU = SCAL ? 4 : (GEN ? 8 : 6);    // 16-byte operand-tile units per thread
+  constexpr bool GVL = !GEN;                       // gate vector kept in LDS (beta, e^{+-(g-gm)})
+  constexpr int PF = SCAL ? 2 : 1;                 // chunks of prefetch in flight
   __shared__ __attribute__((aligned(16))) char smem[L::total];
   _Float16* KP = reinterpret_cast<_Float16*>(smem + L::kp);
   _Float16* QP = reinterpret_cast<_Float16*>(smem + L::qp);
-  _Float16* KM = reinterpret_cast<_Float16*>(smem + L::km);
-  _Float16* UM = reinterpret_cast<_Float16*>(smem + L::um);
+  _Float16* KMT = reinterpret_cast<_Float16*>(smem + L::kmt);
+  _Float16* UMT = reinterpret_cast<_Float16*>(smem + L::umt);
   _Float16* ST = reinterpret_cast<_Float16*>(smem + L::st);
   _Float16* TH = reinterpret_cast<_Float16*>(smem + L::th);
   _Float16* AQ = reinterpret_cast<_Float16*>(smem + L::aq);
@@ -500,10 +522,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   _Float16* AQU = reinterpret_cast<_Float16*>(smem + L::aqu);
   _Float16* RT = reinterpret_cast<_Float16*>(smem + L::rt);
   _Float16* DT = reinterpret_cast<_Float16*>(smem + L::dt);
+  _Float16* DT2 = reinterpret_cast<_Float16*>(smem + L::dt2);
   _Float16* VT = reinterpret_cast<_Float16*>(smem + L::vt);
-  float* GB = reinterpret_cast<float*>(smem + L::gb);
-  float* GW = reinterpret_cast<float*>(smem + L::gw);
-  float* GSC = reinterpret_cast<float*>(smem + L::gsc);
+  float* GV = reinterpret_cast<float*>(smem + L::gv);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -516,11 +537,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   const gptr<const uint16_t> kin = opaque_gptr(static_cast<const uint16_t*>(p.k));
   const gptr<const uint16_t> qin = opaque_gptr(static_cast<const uint16_t*>(p.q));
   const gptr<const uint16_t> vin = opaque_gptr(static_cast<const uint16_t*>(p.v));
-  const gptr<const float> ldin = opaque_gptr(p.log_decay);
-  const gptr<const float> erin = opaque_gptr(p.erase);
   const gptr<const float> wrin = opaque_gptr(p.write);
-  constexpr int NM = prep_mats<GEN>();
-  const gptr<const _Float16> tbase = opaque_gptr(tws) + int64_t(bh) * nchunks * (NM * C * C);
+  const gptr<const char> pbase = opaque_gptr(ws) + int64_t(bh) * nchunks * PK::bytes;
 
   // State: wave w owns rows [16 w, 16 w + 16) x the DVS columns as NCT accumulator tiles
   // (lane: column 16 ct + l16, rows 16 w + 4 lg + r).
@@ -533,152 +551,138 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       S[ct][r] = p.S0 ? p.S0[(int64_t(bh) * D + d) * D + j0 + 16 * ct + l16] : 0.f;
     }
 
-  // Load mapping: thread = (token pair tg, channel octet d8): tokens 2 tg + r, channels
-  // 8 d8 .. 8 d8 + 7; value slice: token tid / 8, columns VPT (tid % 8) .. + VPT - 1;
-  // T: row tid / 8, columns 8 (tid % 8) .. + 7.
+  // Load mapping.  Scalar-decay k / q: thread = (token pair tg, channel octet d8), tokens
+  // 2 tg + r, channels 8 d8 .. 8 d8 + 7.  Packet tiles: 16-byte units tid and tid + 512.
+  // Value slice: token tid / 8, columns VPT (tid % 8) .. + VPT - 1.  Matrices: row tid / 8,
+  // columns 8 (tid % 8) .. + 7.
   const int d8 = tid & 15, tg = tid >> 4;
   const int vtok = tid >> 3, vcol = (tid & 7) * VPT;
-
-  // Prefetch registers for one chunk; two sets alternate so that each chunk's loads are
-  // issued two chunks ahead of their use.
-  struct Pref {
-    uint4 kr[2], qr[2], mr[NM];  // mr: this thread's 16 bytes of T, A_qk (, A_kk, A_qu)
-    float ldr[DCH ? 2 : 1][DCH ? 8 : 1];
-    float err[GEN ? 2 : 1][GEN ? 8 : 1];
-    float lds, gbs, gws;  // per-token (head) gates for token tid (< 64)
-    VSlice<DVS> vr;
-    float wr[GEN ? VPT : 1];
-  };
-
   auto tok = [&](int t) { return (int64_t(b) * T + t) * H + h; };
+  // Per-thread element offsets at chunk 0; chunk c adds c * tstride (tokens are H * D apart).
+  const int64_t tstride = int64_t(C) * H * D;
+  const int64_t kq_off = tok(2 * tg) * D + 8 * d8;
+  const int64_t v_off = tok(vtok) * D + j0 + vcol;
+  const int64_t w_off = tok(vtok);
+  const int64_t o_off = tok(16 * (wave & 3) + l16) * D + j0 + 4 * lg;
+  // Tokens past the end load token T - 1 instead (the values are zeroed where they are used), so
+  // that every load is issued unconditionally and the wait counts stay exact.
+  const int64_t kq_last = tok(T - 1) * D + 8 * d8;
+  const int64_t v_last = tok(T - 1) * D + j0 + vcol;
+  const int64_t w_last = tok(T - 1);
+
+  struct Pref {
+    uint4 mr[NM];             // this thread's 16 bytes of T, A_qk (, A_kk, A_qu)
+    uint4 tl[NTU];            // k, q (scalar decay) or K+, Q+, K-^T (, U-^T) units
+    float gv;                 // gate-vector element tid
+    float4 sc[SCAL ? 1 : 3];  // per-channel e^{gm}, e^{gC}, e^{gC-gm} of this thread's 4 rows
+    float sc3[3];             // scalar decay: e^{gm}, e^{gC}, e^{gC-gm}
+    VSlice<DVS> vr;
+    float wr[GEN ? VPT : 1];  // write gates of the value slice (per channel) or of token vtok
+  };
 
   // The loads of one chunk are issued in three batches, one per compute stage, so that the
   // vector-memory path stays busy without stalling every wave at one point.
-  auto load_kq = [&](Pref& P, int c) {
+  auto load_a = [&](Pref& P, int c) {
+    const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
+    if constexpr (SCAL) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int t = c * C + 2 * tg + r;
-      const bool ok = t < T;
-      const int64_t base = ok ? tok(t) * D + 8 * d8 : 0;
-      P.kr[r] = ok ? gload_u4(kin, base) : make_uint4(0, 0, 0, 0);
-      P.qr[r] = ok ? gload_u4(qin, base) : make_uint4(0, 0, 0, 0);
-      if constexpr (DCH) unpack8(gld4(ldin, base, ok), gld4(ldin, base + 4, ok), P.ldr[r]);
-      if constexpr (GEN) {
-        if (p.erase_channel) unpack8(gld4(erin, base, ok), gld4(erin, base + 4, ok), P.err[r]);
+      for (int r = 0; r < 2; ++r) {
+        const bool ok = c * C + 2 * tg + r < T;
+        const int64_t base = ok ? kq_off + c * tstride + r * (int64_t(H) * D) : kq_last;
+        P.tl[r] = gload_u4(kin, base);
+        P.tl[2 + r] = gload_u4(qin, base);
+      }
+#pragma unroll
+      for (int i = 0; i < 3; ++i) P.sc3[i] = *(gptr<const float>)(pk + PK::gate + 4 * (GV_SC + i));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        P.tl[i] = ldb16(pk, PK::kp + 16 * (tid + kScanThreads * i));
+        P.tl[2 + i] = ldb16(pk, PK::qp + 16 * (tid + kScanThreads * i));
+      }
+      const int d0 = 16 * wave + 4 * lg;
+      P.sc[0] = ldf16(pk, PK::gate + 4 * (GV_EM + d0));
+      P.sc[1] = ldf16(pk, PK::gate + 4 * (GV_FC + d0));
+      P.sc[2] = ldf16(pk, PK::gate + 4 * (GV_FCM + d0));
+    }
+    if constexpr (GVL) P.gv = *(gptr<const float>)(pk + PK::gate + 4 * tid);
+  };
+  auto load_b = [&](Pref& P, int c) {
+    const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) P.mr[m] = ldb16(pk, PK::mat + m * (C * C * 2) + 16 * tid);
+    if constexpr (!SCAL) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        P.tl[4 + i] = ldb16(pk, PK::kmt + 16 * (tid + kScanThreads * i));
+        if constexpr (GEN) P.tl[6 + i] = ldb16(pk, PK::umt + 16 * (tid + kScanThreads * i));
       }
     }
   };
-  auto load_mats = [&](Pref& P, int c) {
+  auto load_c = [&](Pref& P, int c) {
+    const bool ok = c * C + vtok < T;
+    const int64_t vb = ok ? v_off + c * tstride : v_last;
+    vslice_load<DVS>(P.vr, vin, vb, true);
+    if constexpr (GEN) {
+      if constexpr (WCH) {
+        if constexpr (VPT == 2) {
+          const f32x2 w2 = *(gptr<const f32x2>)(wrin + vb);
+          P.wr[0] = w2.x;
+          P.wr[1] = w2.y;
+        } else {
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
-      P.mr[m] = gload_u4(tbase, (int64_t(c) * NM + m) * (C * C) + vtok * C + (tid & 7) * 8);
-  };
-  auto load_rest = [&](Pref& P, int c) {
-    if (tid < C) {
-      const int t = c * C + tid;
-      const bool ok = t < T;
-      const int64_t ti = ok ? tok(t) : 0;
-      P.lds = (!DCH && ok) ? ldin[ti] : 0.f;
-      if constexpr (GEN) {
-        P.gbs = (ok && !p.erase_channel) ? erin[ti] : 0.f;
-        P.gws = (ok && !p.write_channel) ? wrin[ti] : 0.f;
-      } else {
-        P.gbs = ok ? erin[ti] : 0.f;
-        P.gws = 0.f;
-      }
-    }
-    {
-      const int t = c * C + vtok;
-      const bool ok = t < T;
-      const int64_t vb = ok ? tok(t) * D + j0 + vcol : 0;
-      vslice_load<DVS>(P.vr, vin, vb, ok);
-      if constexpr (GEN) {
-        if (p.write_channel) {
-          if constexpr (VPT == 2) {
-            P.wr[0] = ok ? wrin[vb] : 0.f;
-            P.wr[1] = ok ? wrin[vb + 1] : 0.f;
-          } else {
-#pragma unroll
-            for (int i = 0; i < VPT; i += 4) {
-              const float4 w4 = gld4(wrin, vb + i, ok);
-              P.wr[i] = w4.x; P.wr[i + 1] = w4.y; P.wr[i + 2] = w4.z; P.wr[i + 3] = w4.w;
-            }
+          for (int i = 0; i < VPT; i += 4) {
+            const float4 w4 = gload_f4(wrin, vb + i);
+            P.wr[i] = w4.x; P.wr[i + 1] = w4.y; P.wr[i + 2] = w4.z; P.wr[i + 3] = w4.w;
           }
         }
+      } else {
+        P.wr[0] = wrin[ok ? w_off + int64_t(c) * C * H : w_last];
       }
     }
-  };
-  auto load = [&](Pref& P, int c) {
-    load_kq(P, c);
-    load_mats(P, c);
-    load_rest(P, c);
   };
 
   auto step = [&](int c, Pref& P) {
-    // ---- L1: chunk-local cumulative log-decay ------------------------------------------
-    if (tid < C) {
-      GB[tid] = P.gbs;
-      if constexpr (GEN) GW[tid] = P.gws;
-    }
-    float g[2][DCH ? 8 : 1];
-    scan_cumsum<DCH>(P.ldr, P.lds, g, GSC, tid);
-
-    // ---- L2: operand tiles, T, value slice, S~^T ------------------------------------------
-    {
-      float gm[8];
-#pragma unroll
-      for (int ch = 0; ch < 8; ++ch) gm[ch] = scan_gmid<DCH>(GSC, 8 * d8 + ch);
+    // ---- L: the chunk's packet, value slice and S~^T into LDS ------------------------------
+    if constexpr (SCAL) {
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int t = 2 * tg + r;
-        float kf[8], qf[8], fp[8], fm[8], tmp[8];
-        bf16x8_to_f32(P.kr[r], kf);
-        bf16x8_to_f32(P.qr[r], qf);
-        if constexpr (DCH) {
-#pragma unroll
-          for (int ch = 0; ch < 8; ++ch) {
-            fp[ch] = clamped_exp(g[r][ch] - gm[ch]);
-            fm[ch] = clamped_exp(gm[ch] - g[r][ch]);
-          }
-        } else {
-          const float a = clamped_exp(g[r][0] - gm[0]), bb = clamped_exp(gm[0] - g[r][0]);
-#pragma unroll
-          for (int ch = 0; ch < 8; ++ch) {
-            fp[ch] = a;
-            fm[ch] = bb;
-          }
-        }
-#pragma unroll
-        for (int ch = 0; ch < 8; ++ch) tmp[ch] = kf[ch] * fp[ch];
-        *reinterpret_cast<half8*>(KP + t * KS + 8 * d8) = cvt8(tmp);
-#pragma unroll
-        for (int ch = 0; ch < 8; ++ch) tmp[ch] = qf[ch] * fp[ch];
-        *reinterpret_cast<half8*>(QP + t * KS + 8 * d8) = cvt8(tmp);
-        float km[8];
-#pragma unroll
-        for (int ch = 0; ch < 8; ++ch) km[ch] = kf[ch] * fm[ch];
-        *reinterpret_cast<half8*>(KM + t * KS + 8 * d8) = cvt8(km);
-        if constexpr (GEN) {
-          const float eb = GB[t];
-#pragma unroll
-          for (int ch = 0; ch < 8; ++ch) tmp[ch] = (p.erase_channel ? P.err[r][ch] : eb) * km[ch];
-          *reinterpret_cast<half8*>(UM + t * KS + 8 * d8) = cvt8(tmp);
-        }
+        const bool ok = c * C + t < T;
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        float kf[8], qf[8];
+        bf16x8_to_f32(ok ? P.tl[r] : z, kf);
+        bf16x8_to_f32(ok ? P.tl[2 + r] : z, qf);
+        *reinterpret_cast<half8*>(KP + t * KS + 8 * d8) = cvt8(kf);
+        *reinterpret_cast<half8*>(QP + t * KS + 8 * d8) = cvt8(qf);
       }
-      *reinterpret_cast<uint4*>(TH + vtok * CS + (tid & 7) * 8) = P.mr[0];
-      *reinterpret_cast<uint4*>(AQ + vtok * CS + (tid & 7) * 8) = P.mr[1];
-      if constexpr (GEN) {
-        *reinterpret_cast<uint4*>(AKK + vtok * CS + (tid & 7) * 8) = P.mr[2 % NM];
-        *reinterpret_cast<uint4*>(AQU + vtok * CS + (tid & 7) * 8) = P.mr[3 % NM];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int u = tid + kScanThreads * i;
+        *reinterpret_cast<uint4*>(KP + (u >> 4) * KS + (u & 15) * 8) = P.tl[i];
+        *reinterpret_cast<uint4*>(QP + (u >> 4) * KS + (u & 15) * 8) = P.tl[2 + i];
+        *reinterpret_cast<uint4*>(KMT + (u >> 3) * CS + (u & 7) * 8) = P.tl[4 + i];
+        if constexpr (GEN) *reinterpret_cast<uint4*>(UMT + (u >> 3) * CS + (u & 7) * 8) = P.tl[6 + i];
       }
-      // value slice
+    }
+    *reinterpret_cast<uint4*>(TH + vtok * CS + (tid & 7) * 8) = P.mr[0];
+    *reinterpret_cast<uint4*>(AQ + vtok * CS + (tid & 7) * 8) = P.mr[1];
+    if constexpr (GEN) {
+      *reinterpret_cast<uint4*>(AKK + vtok * CS + (tid & 7) * 8) = P.mr[2 % NM];
+      *reinterpret_cast<uint4*>(AQU + vtok * CS + (tid & 7) * 8) = P.mr[3 % NM];
+    }
+    if constexpr (GVL) GV[tid] = P.gv;
+    {
       float vf[VPT];
       vslice_f32<DVS>(P.vr, vf);
+      const bool vok = c * C + vtok < T;
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) vf[i] = vok ? vf[i] : 0.f;
       if constexpr (GEN) {
-        const float wb = GW[vtok];
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-          const float w = p.write_channel ? P.wr[i] : wb;
+          const float w = WCH ? P.wr[i] : P.wr[0];
           VT[(vcol + i) * CS + vtok] = (_Float16)(w * vf[i]);
         }
       } else {
@@ -686,17 +690,21 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
         for (int i = 0; i < VPT; ++i) VT[vtok * L::vstride + vcol + i] = (_Float16)vf[i];
       }
     }
-    // S~^T = (Diag(e^{gm}) S)^T and the per-row end-of-chunk factors of this wave's rows.
+    // S~^T = (Diag(e^{gm}) S)^T; the end-of-chunk factors of this wave's rows stay in registers.
     float fC[4], fCm[4];
     {
       float em[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int d = 16 * wave + 4 * lg + r;
-        const float gmd = scan_gmid<DCH>(GSC, d), gCd = scan_gend<DCH>(GSC, d);
-        em[r] = clamped_exp(gmd);
-        fC[r] = expf(gCd);
-        fCm[r] = clamped_exp(gCd - gmd);
+        if constexpr (SCAL) {
+          em[r] = P.sc3[0];
+          fC[r] = P.sc3[1];
+          fCm[r] = P.sc3[2];
+        } else {
+          em[r] = (&P.sc[0].x)[r];
+          fC[r] = (&P.sc[1].x)[r];
+          fCm[r] = (&P.sc[2].x)[r];
+        }
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -707,11 +715,12 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       }
     }
     lds_barrier();
-    const bool pf = c + 2 < nchunks;  // prefetch chunk c + 2, in flight for two chunks
-    if (pf) load_kq(P, c + 2);
+    // next chunks' loads (past the last chunk: reload the last one, unused)
+    const int cn = c + PF < nchunks ? c + PF : nchunks - 1;
+    load_a(P, cn);
 
     // ---- X = [K+; Q+] S~ ----------------------------------------------------------------
-    // X: waves 0-3 compute X_K rows [16 w, +16), waves 4-7 X_Q rows [16 (w - 4), +16).
+    // waves 0-3: X_K rows [16 w, +16); waves 4-7: X_Q rows [16 (w - 4), +16), transposed.
     const int xrow = 16 * (wave & 3);
     const bool xq_wave = wave >= 4;
     f32x4 XR[NCT];
@@ -730,6 +739,17 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
           const half8 bs = frag(ST, KS, 16 * ct, 32 * ks, lane);
           acc = xq_wave ? mfma16x16x32(bs, af[ks], acc) : mfma16x16x32(af[ks], bs, acc);
         }
+        if constexpr (SCAL) {
+          // rows of X_K are tokens xrow + 4 lg + r; X_Q^T has token xrow + l16 as its column
+          if (xq_wave) {
+            const float f = GV[GV_FP + xrow + l16];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] *= f;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] *= GV[GV_FP + xrow + 4 * lg + r];
+          }
+        }
         XR[ct] = acc;
         if constexpr (!GEN) {
           if (!xq_wave) {
@@ -739,7 +759,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
             for (int r = 0; r < 4; ++r) {
               const int t = xrow + 4 * lg + r;
               const float vv = (float)VT[t * L::vstride + 16 * ct + l16];
-              hv[r] = (_Float16)(GB[t] * (vv - acc[r]));
+              hv[r] = (_Float16)(GV[GV_BETA + t] * (vv - acc[r]));
             }
             *reinterpret_cast<half4v*>(RT + (16 * ct + l16) * CS + xrow + 4 * lg) = hv;
           }
@@ -767,7 +787,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       lds_barrier();
     }
 
-    if (pf) load_mats(P, c + 2);
+    load_b(P, cn);
     // ---- D: delta = T R (symmetric) or -M = -(T Y) (general), stored transposed ---------
 #pragma unroll
     for (int n = wave; n < 4 * NCT; n += kScanWaves) {
@@ -781,10 +801,16 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
 #pragma unroll
       for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(GEN ? -acc[r] : acc[r]);
       *reinterpret_cast<half4v*>(DT + (16 * ct + l16) * CS + 16 * i + 4 * lg) = hv;
+      if constexpr (SCAL) {
+        // K-^T delta = k^T (Diag(e^{gm - g}) delta): the state update takes the scaled copy
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(acc[r] * GV[GV_FM + 16 * i + 4 * lg + r]);
+        *reinterpret_cast<half4v*>(DT2 + (16 * ct + l16) * CS + 16 * i + 4 * lg) = hv;
+      }
     }
     lds_barrier();
 
-    if (pf) load_rest(P, c + 2);
+    load_c(P, cn);
     // ---- O: chunk output rows [16 (w - 4), +16), waves 4-7 --------------------------------
     if (xq_wave) {
       // O^T tile: lane holds O[t = 16 i + l16][j = 16 ct + 4 lg + 0..3]
@@ -805,7 +831,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
             }
           }
         }
-        if (t < T) store_o4(p.o, tok(t) * D + j0 + 16 * ct + 4 * lg, acc, p.o_bf16);
+        if (t < T) store_o4(p.o, o_off + c * tstride + 16 * ct, acc, p.o_bf16);
       }
     }
 
@@ -816,12 +842,16 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const half8 ak = frag_t(KM, 16 * wave, 32 * ks, lane);
-        half8 au;
-        if constexpr (GEN) au = frag_t(UM, 16 * wave, 32 * ks, lane);
+        half8 ak, au;
+        if constexpr (SCAL) {
+          ak = frag_t(KP, 16 * wave, 32 * ks, lane);
+        } else {
+          ak = frag(KMT, CS, 16 * wave, 32 * ks, lane);
+          if constexpr (GEN) au = frag(UMT, CS, 16 * wave, 32 * ks, lane);
+        }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-          const half8 bd = frag(DT, CS, 16 * ct, 32 * ks, lane);
+          const half8 bd = frag(SCAL ? DT2 : DT, CS, 16 * ct, 32 * ks, lane);
           if constexpr (GEN) {
             acc[ct] = mfma16x16x32(ak, frag(VT, CS, 16 * ct, 32 * ks, lane), acc[ct]);
             acc[ct] = mfma16x16x32(au, bd, acc[ct]);
@@ -838,12 +868,24 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
     lds_barrier();
   };
 
+  auto load = [&](Pref& P, int c) {
+    load_a(P, c);
+    load_b(P, c);
+    load_c(P, c);
+  };
   Pref PA, PB;
   load(PA, 0);
-  if (nchunks > 1) load(PB, 1);
-  for (int c = 0; c < nchunks; c += 2) {
-    step(c, PA);
-    if (c + 1 < nchunks) step(c + 1, PB);
+  if constexpr (PF == 2) {
+    load(PB, nchunks > 1 ? 1 : 0);
+    // both halves unconditional inside the loop, so the wait counts at its head are exact
+    int c = 0;
+    for (; c + 1 < nchunks; c += 2) {
+      step(c, PA);
+      step(c + 1, PB);
+    }
+    if (c < nchunks) step(c, PA);
+  } else {
+    for (int c = 0; c < nchunks; ++c) step(c, PA);
   }
 
   if (p.S_T) {
@@ -858,37 +900,45 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
 }
 
 template <bool DCH, bool GEN, int DVS>
-hipError_t launch_scan(const Problem& p, const _Float16* tws, hipStream_t stream) {
+hipError_t launch_scan(const Problem& p, const char* ws, hipStream_t stream) {
   dim3 grid(unsigned(p.B * p.H), unsigned(D / DVS));
-  hipLaunchKernelGGL((chunk_scan_kernel<DCH, GEN, DVS>), grid, dim3(kScanThreads), 0, stream, p, tws);
+  if constexpr (GEN) {
+    if (p.write_channel) {
+      hipLaunchKernelGGL((chunk_scan_kernel<DCH, GEN, true, DVS>), grid, dim3(kScanThreads), 0, stream, p, ws);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((chunk_scan_kernel<DCH, GEN, false, DVS>), grid, dim3(kScanThreads), 0, stream, p, ws);
   return hipGetLastError();
 }
 
 template <bool DCH, bool GEN>
 hipError_t launch_variant(const Problem& p, void* workspace, hipStream_t stream) {
   const int nchunks = (p.T + C - 1) / C;
-  _Float16* tws = static_cast<_Float16*>(workspace);
+  char* ws = static_cast<char*>(workspace);
   const int64_t nblk = int64_t(p.B) * p.H * nchunks;
-  hipLaunchKernelGGL((chunk_prep_kernel<DCH, GEN>), dim3(unsigned(nblk)), dim3(kThreads), 0, stream, p, tws,
+  hipLaunchKernelGGL((chunk_prep_kernel<DCH, GEN>), dim3(unsigned(nblk)), dim3(kThreads), 0, stream, p, ws,
                      nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Fill the 256 compute units with (b, h, value-slice) workgroups while keeping the slices
-  // (each rebuilds its chunk's operand tiles and Gram matrices) as wide as that allows.
+  // (each stages its chunk's operand tiles) as wide as that allows.
   const int64_t bh = int64_t(p.B) * p.H;
   if constexpr (!GEN) {
-    if (bh >= 128) return launch_scan<DCH, GEN, 64>(p, tws, stream);
+    if (bh >= 128) return launch_scan<DCH, GEN, 64>(p, ws, stream);
   }
-  if (bh >= 64) return launch_scan<DCH, GEN, 32>(p, tws, stream);
-  return launch_scan<DCH, GEN, 16>(p, tws, stream);
+  if (bh >= 64) return launch_scan<DCH, GEN, 32>(p, ws, stream);
+  return launch_scan<DCH, GEN, 16>(p, ws, stream);
 }
 
 }  // namespace
 
-size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric) {
+size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric, bool decay_channel) {
   const int64_t nchunks = (int64_t(T) + C - 1) / C;
-  const int64_t nmat = symmetric ? prep_mats<false>() : prep_mats<true>();
-  return size_t(int64_t(B) * H * nchunks * nmat * C * C * sizeof(_Float16));
+  const int64_t per = !symmetric      ? Packet<true, true>::bytes
+                      : decay_channel ? Packet<true, false>::bytes
+                                      : Packet<false, false>::bytes;
+  return size_t(int64_t(B) * H * nchunks * per);
 }
 
 hipError_t launch_chunk128(const Problem& p, void* workspace, hipStream_t stream) {

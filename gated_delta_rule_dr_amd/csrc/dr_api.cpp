@@ -148,7 +148,8 @@ size_t dr_chunk_fwd_workspace_bytes(const dr_desc* desc) {
   Extents ex;
   if (check_desc(desc, false, &ex) != DR_OK) return 0;
   if (!uses_chunk128(desc)) return 0;
-  return dr::chunk128_workspace_bytes(desc->B, desc->T, desc->H, is_symmetric(desc));
+  return dr::chunk128_workspace_bytes(desc->B, desc->T, desc->H, is_symmetric(desc),
+                                      desc->decay_kind == DR_GATE_CHANNEL);
 }
 
 int dr_chunk_fwd(const dr_desc* d, const void* q, const void* k, const void* v,

@@ -36,9 +36,9 @@ hipError_t launch_recurrent(const Problem& p, hipStream_t stream);
 hipError_t launch_decode128(const Problem& p, hipStream_t stream);
 
 // MFMA chunked forward, bf16 q/k/v, dk == dv == 128, chunk 64.  `workspace` holds at least
-// chunk128_workspace_bytes(B, T, H, symmetric) bytes: per chunk, 2 (symmetric gates) or 4
-// (general gates) fp16 64 x 64 matrices.
-size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric);
+// chunk128_workspace_bytes(B, T, H, symmetric, decay_channel) bytes: one packet of
+// state-independent factors per chunk of every (b, h).
+size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric, bool decay_channel);
 hipError_t launch_chunk128(const Problem& p, void* workspace, hipStream_t stream);
 
 // S_T = S0 (copy) or zeros when S0 is null: n floats.

@@ -124,13 +124,21 @@ def test_aliasing():
 
 def test_workspace_query_and_errors():
     L = _abi.lib()
-    # matrix-core path: per chunk of every (b, h), 2 (symmetric gates) or 4 fp16 64 x 64 matrices
-    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc())) == 2 * 4 * 2 * 2 * 64 * 64 * 2
-    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(T=64))) == 2 * 4 * 1 * 2 * 64 * 64 * 2
-    gen = _good_desc(erase_kind=_abi.DR_GATE_CHANNEL)
-    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(gen)) == 2 * 4 * 2 * 4 * 64 * 64 * 2
-    gen2 = _good_desc(write_is_erase=0)
-    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(gen2)) == 2 * 4 * 2 * 4 * 64 * 64 * 2
+    # matrix-core path: one packet per chunk of every (b, h) -- fp16 64 x 64 matrices (2 or 4),
+    # fp16 operand tiles unless the decay is per head with symmetric gates, fp32 gate vector
+    scal = 2 * 64 * 64 * 2 + 512 * 4
+    kda = 2 * 64 * 64 * 2 + 3 * 64 * 128 * 2 + 512 * 4
+    gen = 4 * 64 * 64 * 2 + 4 * 64 * 128 * 2 + 512 * 4
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc())) == 2 * 4 * 2 * scal
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(T=64))) == 2 * 4 * 1 * scal
+    ch = _good_desc(decay_kind=_abi.DR_GATE_CHANNEL)
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(ch)) == 2 * 4 * 2 * kda
+    g1 = _good_desc(erase_kind=_abi.DR_GATE_CHANNEL)
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(g1)) == 2 * 4 * 2 * gen
+    g2 = _good_desc(write_is_erase=0)
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(g2)) == 2 * 4 * 2 * gen
+    g3 = _good_desc(write_is_erase=0, decay_kind=_abi.DR_GATE_CHANNEL, erase_kind=_abi.DR_GATE_CHANNEL)
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(g3)) == 2 * 4 * 2 * gen
     # token path and empty sequences need none
     assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(chunk=1))) == 0
     assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(qkv_dtype=_abi.DR_F32))) == 0
