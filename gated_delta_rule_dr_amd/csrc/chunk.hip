@@ -498,6 +498,11 @@ __device__ __forceinline__ void vslice_f32(const VSlice<DVS>& v, float* f) {
   }
 }
 
+template <bool B>
+struct Tail {
+  static constexpr bool value = B;
+};
+
 // WCH: per-channel write gate (general gates only).
 template <bool DCH, bool GEN, bool WCH, int DVS>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, const char* __restrict__ ws) {
@@ -534,6 +539,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   const int j0 = blockIdx.y * DVS;
   const int T = p.T, H = p.H;
   const int nchunks = (T + C - 1) / C;
+  const int nfull = T / C;  // chunks with C tokens
   const gptr<const uint16_t> kin = opaque_gptr(static_cast<const uint16_t*>(p.k));
   const gptr<const uint16_t> qin = opaque_gptr(static_cast<const uint16_t*>(p.q));
   const gptr<const uint16_t> vin = opaque_gptr(static_cast<const uint16_t*>(p.v));
@@ -642,7 +648,11 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
     }
   };
 
-  auto step = [&](int c, Pref& P) {
+  // TAIL: the chunk may extend past the last token (its output rows are masked).  Full chunks
+  // store unconditionally, so that the stores do not make the wait counts of later loads
+  // conservative.
+  auto step = [&](auto tail, int c, Pref& P) {
+    constexpr bool TAIL = decltype(tail)::value;
     // ---- L: the chunk's packet, value slice and S~^T into LDS ------------------------------
     if constexpr (SCAL) {
 #pragma unroll
@@ -831,7 +841,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
             }
           }
         }
-        if (t < T) store_o4(p.o, o_off + c * tstride + 16 * ct, acc, p.o_bf16);
+        if (!TAIL || t < T) store_o4(p.o, o_off + c * tstride + 16 * ct, acc, p.o_bf16);
       }
     }
 
@@ -876,16 +886,22 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   Pref PA, PB;
   load(PA, 0);
   if constexpr (PF == 2) {
+    // keep the prologue's loads in chunk order: the loop's wait counts assume it
+    asm volatile("" ::: "memory");
     load(PB, nchunks > 1 ? 1 : 0);
+    asm volatile("" ::: "memory");
     // both halves unconditional inside the loop, so the wait counts at its head are exact
     int c = 0;
-    for (; c + 1 < nchunks; c += 2) {
-      step(c, PA);
-      step(c + 1, PB);
+    for (; c + 1 < nfull; c += 2) {
+      step(Tail<false>(), c, PA);
+      step(Tail<false>(), c + 1, PB);
     }
-    if (c < nchunks) step(c, PA);
+    if (c < nchunks) step(Tail<true>(), c, PA);
+    if (c + 1 < nchunks) step(Tail<true>(), c + 1, PB);
   } else {
-    for (int c = 0; c < nchunks; ++c) step(c, PA);
+    int c = 0;
+    for (; c < nfull; ++c) step(Tail<false>(), c, PA);
+    if (c < nchunks) step(Tail<true>(), c, PA);
   }
 
   if (p.S_T) {
