@@ -182,13 +182,17 @@ __device__ __forceinline__ float chunk_gend(const float* GSC, int d) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Per-chunk packet in the workspace (byte offsets).  Matrices are fp16 64 x 64 row-major with
-// zero upper triangles, in the order T, A_qk (, A_kk, A_qu for general gates); tiles are fp16
-// row-major without padding; the gate vector is fp32.
-//   scalar decay, symmetric gates: matrices, gates {beta[64], e^{g-gm}[64], e^{gm-g}[64],
-//                                  e^{gm}, e^{gC}, e^{gC-gm}}
+// Per-chunk packet in the workspace (byte offsets).  Matrices are fp16 64 x 64 with zero upper
+// triangles, in the order T, A_qk (, A_kk, A_qu for general gates); tiles are fp16; the gate
+// vector is fp32 [512].
+//   scalar decay, symmetric gates: matrices, k [64][128], q [64][128] (plain), gates
+//     {beta[64], e^{g-gm}[64], e^{gm-g}[64], e^{gm}, e^{gC}, e^{gC-gm}}
 //   otherwise: matrices, K+ [64][128], Q+ [64][128], K-^T [128][64] (, U-^T [128][64]),
-//              gates {beta[64] (symmetric gates), e^{gm}[128], e^{gC}[128], e^{gC-gm}[128]}
+//     gates {beta[64] (symmetric gates), e^{gm}[128], e^{gC}[128], e^{gC-gm}[128]}
+// Every fp16 row is a run of 16-byte units (16 per 128-wide row, 8 per 64-wide row) stored
+// XOR-swizzled, unit u of row r at position u ^ (r & 7), so that the scan can copy a tile into
+// LDS as is and still read matrix-core fragments (eight rows of one unit) without bank
+// conflicts.
 // ------------------------------------------------------------------------------------------
 template <bool DCH, bool GEN>
 struct Packet {
@@ -196,13 +200,20 @@ struct Packet {
   static constexpr int nmat = GEN ? 4 : 2;
   static constexpr int mat = 0;
   static constexpr int kp = mat + nmat * C * C * 2;
-  static constexpr int qp = kp + (kScal ? 0 : C * D * 2);
-  static constexpr int kmt = qp + (kScal ? 0 : C * D * 2);
+  static constexpr int qp = kp + C * D * 2;
+  static constexpr int kmt = qp + C * D * 2;
   static constexpr int umt = kmt + (kScal ? 0 : D * C * 2);
   static constexpr int gate = umt + (GEN ? D * C * 2 : 0);
   static constexpr int ngate = 512;  // floats
   static constexpr int bytes = gate + ngate * 4;
 };
+
+// Half offset of column `col` of row `r` in a swizzled tile with U 16-byte units per row.
+template <int U>
+__device__ __forceinline__ int swz(int r, int col) {
+  return (r * U + ((col >> 3) ^ (r & 7))) * 8 + (col & 7);
+}
+
 // gate-vector slots (floats)
 constexpr int GV_BETA = 0;                            // [64]
 constexpr int GV_FP = 64, GV_FM = 128, GV_SC = 192;   // scalar decay
@@ -348,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, char* _
         half4v hv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) hv[r] = (_Float16)((strict ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f);
-        *reinterpret_cast<half4v*>(wsc + which * (C * C) + t * C + i0) = hv;
+        *reinterpret_cast<half4v*>(wsc + which * (C * C) + swz<8>(t, i0)) = hv;
       }
     }
   }
@@ -358,14 +369,25 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, char* _
     const int I = u < 3 ? 0 : u < 5 ? 1 : 2;           // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
     const int J = u < 3 ? 1 + u : u < 5 ? u - 1 : 3;
     const half4v z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
-    *reinterpret_cast<half4v*>(wsc + m * (C * C) + (16 * I + l16) * C + 16 * J + 4 * lg) = z;
+    *reinterpret_cast<half4v*>(wsc + m * (C * C) + swz<8>(16 * I + l16, 16 * J + 4 * lg)) = z;
   }
-  // operand tiles for the scan: K+, Q+ as is; K-, U- transposed ([channel][token])
-  if constexpr (!PK::kScal) {
+  // operand tiles for the scan: K+, Q+ (scalar decay: the plain k, q) row-major; K-, U-
+  // transposed ([channel][token]); all swizzled
+  if constexpr (PK::kScal) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * tg + r;
+      float kf[8], qf[8];
+      bf16x8_to_f32(kr[r], kf);
+      bf16x8_to_f32(qr[r], qf);
+      *reinterpret_cast<half8*>(pk + PK::kp + 2 * swz<16>(t, 8 * d8)) = cvt8(kf);
+      *reinterpret_cast<half8*>(pk + PK::qp + 2 * swz<16>(t, 8 * d8)) = cvt8(qf);
+    }
+  } else {
 #pragma unroll
     for (int i = 0; i < C * D / 8 / kThreads; ++i) {
       const int u = tid + kThreads * i;
-      const int t = u >> 4, c8 = (u & 15) * 8;
+      const int t = u >> 4, c8 = (((u & 15) ^ (t & 7))) * 8;  // stored unit u & 15 holds column c8
       *reinterpret_cast<uint4*>(pk + PK::kp + 16 * u) = *reinterpret_cast<const uint4*>(KP + t * KS + c8);
       *reinterpret_cast<uint4*>(pk + PK::qp + 16 * u) = *reinterpret_cast<const uint4*>(QP + t * KS + c8);
     }
@@ -375,11 +397,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, char* _
       half8 x;
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = KM[(t0 + j) * KS + d];
-      *reinterpret_cast<half8*>(pk + PK::kmt + 2 * (d * C + t0)) = x;
+      *reinterpret_cast<half8*>(pk + PK::kmt + 2 * swz<8>(d, t0)) = x;
       if constexpr (GEN) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = UM[(t0 + j) * KS + d];
-        *reinterpret_cast<half8*>(pk + PK::umt + 2 * (d * C + t0)) = x;
+        *reinterpret_cast<half8*>(pk + PK::umt + 2 * swz<8>(d, t0)) = x;
       }
     }
   }
@@ -431,13 +453,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, char* _
     lds_barrier();
   }
 
-  // T (64 x 64 fp16, row-major) to the workspace: 32 bytes per thread.
+  // T (64 x 64 fp16, swizzled) to the workspace: two 16-byte units per thread.
   {
     const int t = tid >> 2, c0 = (tid & 3) * 16;
-    const uint4* src = reinterpret_cast<const uint4*>(TH + t * CS + c0);
-    uint4* dst = reinterpret_cast<uint4*>(wsc + t * C + c0);
-    dst[0] = src[0];
-    dst[1] = src[1];
+    *reinterpret_cast<uint4*>(wsc + swz<8>(t, c0)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0);
+    *reinterpret_cast<uint4*>(wsc + swz<8>(t, c0 + 8)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0 + 8);
   }
 }
 
@@ -498,14 +518,18 @@ __device__ __forceinline__ void vslice_f32(const VSlice<DVS>& v, float* f) {
   }
 }
 
+// Compile-time flag passed to generic lambdas.
 template <bool B>
-struct Tail {
+struct Flag {
   static constexpr bool value = B;
 };
 
-// WCH: per-channel write gate (general gates only).
+// Scan, general gates (separate erase and write gates): the packet (too large for two LDS
+// buffer sets) is staged through registers one or two chunks ahead.  WCH: per-channel write
+// gate.
 template <bool DCH, bool GEN, bool WCH, int DVS>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, const char* __restrict__ ws) {
+  static_assert(GEN, "symmetric gates use chunk_scan_sym_kernel");
   using PK = Packet<DCH, GEN>;
   constexpr bool SCAL = PK::kScal;
   using L = ScanLayout<GEN, SCAL, DVS>;
@@ -667,20 +691,26 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
         *reinterpret_cast<half8*>(QP + t * KS + 8 * d8) = cvt8(qf);
       }
     } else {
+      // packet units are swizzled (unit u of row r at u ^ (r & 7)); LDS rows are padded instead
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int u = tid + kScanThreads * i;
-        *reinterpret_cast<uint4*>(KP + (u >> 4) * KS + (u & 15) * 8) = P.tl[i];
-        *reinterpret_cast<uint4*>(QP + (u >> 4) * KS + (u & 15) * 8) = P.tl[2 + i];
-        *reinterpret_cast<uint4*>(KMT + (u >> 3) * CS + (u & 7) * 8) = P.tl[4 + i];
-        if constexpr (GEN) *reinterpret_cast<uint4*>(UMT + (u >> 3) * CS + (u & 7) * 8) = P.tl[6 + i];
+        const int t = u >> 4, ct = ((u & 15) ^ (t & 7)) * 8;
+        const int d = u >> 3, dt = ((u & 7) ^ (d & 7)) * 8;
+        *reinterpret_cast<uint4*>(KP + t * KS + ct) = P.tl[i];
+        *reinterpret_cast<uint4*>(QP + t * KS + ct) = P.tl[2 + i];
+        *reinterpret_cast<uint4*>(KMT + d * CS + dt) = P.tl[4 + i];
+        if constexpr (GEN) *reinterpret_cast<uint4*>(UMT + d * CS + dt) = P.tl[6 + i];
       }
     }
-    *reinterpret_cast<uint4*>(TH + vtok * CS + (tid & 7) * 8) = P.mr[0];
-    *reinterpret_cast<uint4*>(AQ + vtok * CS + (tid & 7) * 8) = P.mr[1];
-    if constexpr (GEN) {
-      *reinterpret_cast<uint4*>(AKK + vtok * CS + (tid & 7) * 8) = P.mr[2 % NM];
-      *reinterpret_cast<uint4*>(AQU + vtok * CS + (tid & 7) * 8) = P.mr[3 % NM];
+    {
+      const int mc = ((tid & 7) ^ (vtok & 7)) * 8;
+      *reinterpret_cast<uint4*>(TH + vtok * CS + mc) = P.mr[0];
+      *reinterpret_cast<uint4*>(AQ + vtok * CS + mc) = P.mr[1];
+      if constexpr (GEN) {
+        *reinterpret_cast<uint4*>(AKK + vtok * CS + mc) = P.mr[2 % NM];
+        *reinterpret_cast<uint4*>(AQU + vtok * CS + mc) = P.mr[3 % NM];
+      }
     }
     if constexpr (GVL) GV[tid] = P.gv;
     {
@@ -893,15 +923,15 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
     // both halves unconditional inside the loop, so the wait counts at its head are exact
     int c = 0;
     for (; c + 1 < nfull; c += 2) {
-      step(Tail<false>(), c, PA);
-      step(Tail<false>(), c + 1, PB);
+      step(Flag<false>(), c, PA);
+      step(Flag<false>(), c + 1, PB);
     }
-    if (c < nchunks) step(Tail<true>(), c, PA);
-    if (c + 1 < nchunks) step(Tail<true>(), c + 1, PB);
+    if (c < nchunks) step(Flag<true>(), c, PA);
+    if (c + 1 < nchunks) step(Flag<true>(), c + 1, PB);
   } else {
     int c = 0;
-    for (; c < nfull; ++c) step(Tail<false>(), c, PA);
-    if (c < nchunks) step(Tail<true>(), c, PA);
+    for (; c < nfull; ++c) step(Flag<false>(), c, PA);
+    if (c < nchunks) step(Flag<true>(), c, PA);
   }
 
   if (p.S_T) {
@@ -915,16 +945,336 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   }
 }
 
-template <bool DCH, bool GEN, int DVS>
-hipError_t launch_scan(const Problem& p, const char* ws, hipStream_t stream) {
-  dim3 grid(unsigned(p.B * p.H), unsigned(D / DVS));
-  if constexpr (GEN) {
-    if (p.write_channel) {
-      hipLaunchKernelGGL((chunk_scan_kernel<DCH, GEN, true, DVS>), grid, dim3(kScanThreads), 0, stream, p, ws);
-      return hipGetLastError();
+// ------------------------------------------------------------------------------------------
+// Scan, symmetric gates (one per-head erase/write gate): the chunks of one (b, h, value slice)
+// in order, eight waves per workgroup.  The packet tiles of chunk c + 1 are copied global ->
+// LDS by the load-to-LDS path (no registers, no VALU) into the second of two buffer sets while
+// chunk c is computed from the first; each chunk starts with one wait for its own copies.
+// ------------------------------------------------------------------------------------------
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+
+// Lane l copies the 16 bytes at its global address `src` to LDS byte `lds_wave` + 16 l
+// (`lds_wave` is the same for the whole wave).
+__device__ __forceinline__ void dma16(gptr<const char> src, void* lds_wave) {
+  __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)lds_wave, 16, 0, 0);
+}
+
+// Wait for all of this wave's vector-memory operations (loads, stores, copies to LDS).
+__device__ __forceinline__ void vm_wait_all() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
+}
+
+// Fragment (as frag()) of a swizzled tile with U 16-byte units per row.
+template <int U>
+__device__ __forceinline__ half8 frag_s(const _Float16* base, int row0, int k0, int lane) {
+  return *reinterpret_cast<const half8*>(base + swz<U>(row0 + (lane & 15), k0 + 8 * (lane >> 4)));
+}
+
+// A-operand fragment of the transpose of a swizzled [token][128] tile: rows are channels
+// d0 + (lane % 16), contraction over tokens t0 + 8 (lane / 16) + 0..7.
+__device__ __forceinline__ half8 frag_ts(const _Float16* base, int d0, int t0, int lane) {
+  const int d = d0 + (lane & 15), t = t0 + 8 * (lane >> 4);
+  half8 a;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = base[swz<16>(t + i, d)];
+  return a;
+}
+
+template <bool DCH, int DVS>
+__global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p, const char* __restrict__ ws) {
+  using PK = Packet<DCH, false>;
+  constexpr bool SCAL = !DCH;
+  constexpr int NCT = DVS / 16;  // 16-column tiles of the value slice
+  constexpr int VU = DVS / 8;    // 16-byte units per value-slice row
+  // Two buffer sets of copy targets, one array each: reading one set never waits for the
+  // copies into the other.  Set layout (bytes): K+ (scalar decay: k) [64][128], Q+ (q)
+  // [64][128], K-^T [128][64] (per-channel decay), T [64][64], A_qk [64][64], gate vector
+  // [512] f32, v slice [64][DVS] (bf16).
+  constexpr int o_kp = 0, o_qp = o_kp + C * D * 2, o_km = o_qp + C * D * 2;
+  constexpr int o_th = o_km + (SCAL ? 0 : D * C * 2), o_aq = o_th + C * C * 2, o_gv = o_aq + C * C * 2;
+  constexpr int o_vs = o_gv + PK::ngate * 4, set_bytes = o_vs + C * DVS * 2;
+  __shared__ __attribute__((aligned(16))) char BS0[set_bytes];
+  __shared__ __attribute__((aligned(16))) char BS1[set_bytes];
+  // Written by the workgroup itself.
+  __shared__ __attribute__((aligned(16))) _Float16 ST[DVS * KS];  // S~^T
+  __shared__ __attribute__((aligned(16))) _Float16 RT[DVS * CS];  // R^T
+  __shared__ __attribute__((aligned(16))) _Float16 DT[DVS * CS];  // delta^T
+  __shared__ __attribute__((aligned(16))) _Float16 DT2[SCAL ? DVS * CS : 8];  // (Diag(e^{gm-g}) delta)^T
+
+  // Buffer set 0 or 1 (a compile-time choice, so that every access names its array).
+  struct Set {
+    _Float16* kp;
+    _Float16* qp;
+    _Float16* km;
+    _Float16* th;
+    _Float16* aq;
+    float* gv;
+    uint16_t* vs;  // bf16, as in v
+  };
+  auto set_of = [&](auto one) {
+    constexpr bool B1 = decltype(one)::value;
+    char* base = B1 ? BS1 : BS0;
+    Set x;
+    x.kp = reinterpret_cast<_Float16*>(base + o_kp);
+    x.qp = reinterpret_cast<_Float16*>(base + o_qp);
+    x.km = reinterpret_cast<_Float16*>(base + o_km);
+    x.th = reinterpret_cast<_Float16*>(base + o_th);
+    x.aq = reinterpret_cast<_Float16*>(base + o_aq);
+    x.gv = reinterpret_cast<float*>(base + o_gv);
+    x.vs = reinterpret_cast<uint16_t*>(base + o_vs);
+    return x;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int bh = blockIdx.x;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int j0 = blockIdx.y * DVS;
+  const int T = p.T, H = p.H;
+  const int nchunks = (T + C - 1) / C;
+  const gptr<const char> pbase = opaque_gptr(ws) + int64_t(bh) * nchunks * PK::bytes;
+  const gptr<const char> vin = opaque_gptr(static_cast<const char*>(p.v));
+
+  // State: wave w owns rows [16 w, 16 w + 16) x the DVS columns as NCT accumulator tiles
+  // (lane: column 16 ct + l16, rows 16 w + 4 lg + r).
+  f32x4 S[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int d = 16 * wave + 4 * lg + r;
+      S[ct][r] = p.S0 ? p.S0[(int64_t(bh) * D + d) * D + j0 + 16 * ct + l16] : 0.f;
     }
+
+  auto tok = [&](int t) { return (int64_t(b) * T + t) * H + h; };
+  const int64_t tstride = int64_t(C) * H * D;  // elements between chunk c and c + 1
+  // value-slice unit of this thread (threads < 64 VU): token tid / VU, columns 8 (tid % VU) ..
+  const int vt = tid / VU, vc = 8 * (tid % VU);
+  const int64_t v_off = tok(vt) * D + j0 + vc;
+  const int64_t v_last = tok(T - 1) * D + j0 + vc;  // stands in for tokens past the end
+  const int64_t o_off = tok(16 * (wave & 3) + l16) * D + j0 + 4 * lg;
+
+  // Copies of chunk c's packet and value slice into buffer set X, plus the per-row decay
+  // factors of this thread's state rows into registers.
+  struct Fac {  // scalar decay: element 0 only
+    float em[4], fc[4], fcm[4];
+  };
+  auto fetch = [&](const Set& X, Fac& F, int c, bool copy) {
+    const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
+    const int ub = 16 * tid;  // this lane's byte within a 8 KB block
+    const int wb = 1024 * wave;  // this wave's LDS byte within a 8 KB block
+    if (copy) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      dma16(pk + PK::kp + ub + 8192 * i, reinterpret_cast<char*>(X.kp) + wb + 8192 * i);
+      dma16(pk + PK::qp + ub + 8192 * i, reinterpret_cast<char*>(X.qp) + wb + 8192 * i);
+      if constexpr (!SCAL) dma16(pk + PK::kmt + ub + 8192 * i, reinterpret_cast<char*>(X.km) + wb + 8192 * i);
+    }
+    dma16(pk + PK::mat + ub, reinterpret_cast<char*>(X.th) + wb);
+    dma16(pk + PK::mat + C * C * 2 + ub, reinterpret_cast<char*>(X.aq) + wb);
+    if (wave < PK::ngate * 4 / 1024) dma16(pk + PK::gate + ub, reinterpret_cast<char*>(X.gv) + wb);
+    if (tid < C * VU) {
+      const bool ok = c * C + vt < T;
+      const int64_t e = ok ? v_off + c * tstride : v_last;
+      dma16(vin + 2 * e, reinterpret_cast<char*>(X.vs) + wb);
+    }
+    }
+    // the factors are loaded unconditionally (a conditional load would need a register copy,
+    // and with it an immediate wait)
+    const gptr<const float> gv = (gptr<const float>)(pk + PK::gate);
+    if constexpr (SCAL) {
+      F.em[0] = gv[GV_SC];
+      F.fc[0] = gv[GV_SC + 1];
+      F.fcm[0] = gv[GV_SC + 2];
+    } else {
+      const int d0 = 16 * wave + 4 * lg;
+      const float4 a = gload_f4(gv, GV_EM + d0);
+      const float4 bb = gload_f4(gv, GV_FC + d0);
+      const float4 cc = gload_f4(gv, GV_FCM + d0);
+      F.em[0] = a.x; F.em[1] = a.y; F.em[2] = a.z; F.em[3] = a.w;
+      F.fc[0] = bb.x; F.fc[1] = bb.y; F.fc[2] = bb.z; F.fc[3] = bb.w;
+      F.fcm[0] = cc.x; F.fcm[1] = cc.y; F.fcm[2] = cc.z; F.fcm[3] = cc.w;
+    }
+  };
+
+  const int xrow = 16 * (wave & 3);
+  const bool xq_wave = wave >= 4;
+  f32x4 OA[NCT];  // output tile of the previous chunk (waves 4-7), stored one chunk later
+  auto store_out = [&](int c, bool masked) {
+    const int t = c * C + xrow + l16;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+      if (!masked || t < T) store_o4(p.o, o_off + c * tstride + 16 * ct, OA[ct], p.o_bf16);
+  };
+
+  Fac F;
+  auto step = [&](int c, auto one) {
+    constexpr bool B1 = decltype(one)::value;
+    const Set X = set_of(Flag<B1>()), Y = set_of(Flag<!B1>());
+    vm_wait_all();  // this chunk's copies (issued one chunk ago) and the previous stores
+    if (c > 0 && xq_wave) store_out(c - 1, false);
+    float em[4], fC[4], fCm[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      em[r] = F.em[SCAL ? 0 : r];
+      fC[r] = F.fc[SCAL ? 0 : r];
+      fCm[r] = F.fcm[SCAL ? 0 : r];
+    }
+    // S~^T = (Diag(e^{gm}) S)^T
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      half4v hv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(em[r] * S[ct][r]);
+      *reinterpret_cast<half4v*>(ST + (16 * ct + l16) * KS + 16 * wave + 4 * lg) = hv;
+    }
+    lds_barrier();  // every wave's copies of this chunk have landed; S~^T is complete
+    fetch(Y, F, c + 1 < nchunks ? c + 1 : c, c + 1 < nchunks);
+
+    // ---- X = [K+; Q+] S~: waves 0-3 X_K rows [16 w, +16); waves 4-7 X_Q rows, transposed --
+    f32x4 XR[NCT];
+    {
+      // an index, not a choice between two pointers: LDS reads keep their array's alias scope
+      // only through address arithmetic, and without it every read waits for the copies
+      const _Float16* Xa = X.kp + (xq_wave ? (o_qp - o_kp) / 2 : 0);
+      half8 af[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) af[ks] = frag_s<16>(Xa, xrow, 32 * ks, lane);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const half8 bs = frag(ST, KS, 16 * ct, 32 * ks, lane);
+          acc = xq_wave ? mfma16x16x32(bs, af[ks], acc) : mfma16x16x32(af[ks], bs, acc);
+        }
+        if constexpr (SCAL) {
+          // rows of X_K are tokens xrow + 4 lg + r; X_Q^T has token xrow + l16 as its column
+          if (xq_wave) {
+            const float f = X.gv[GV_FP + xrow + l16];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] *= f;
+          } else {
+            // four consecutive floats in one read: a single address keeps the read's alias
+            // scope (per-element addresses would lose it and then wait for the copies)
+            const float4 f = *reinterpret_cast<const float4*>(X.gv + GV_FP + xrow + 4 * lg);
+            acc[0] *= f.x; acc[1] *= f.y; acc[2] *= f.z; acc[3] *= f.w;
+          }
+        }
+        XR[ct] = acc;
+        if (!xq_wave) {
+          // R = Diag(beta) (V - X_K), stored transposed
+          half4v hv;
+          const float4 bt = *reinterpret_cast<const float4*>(X.gv + GV_BETA + xrow + 4 * lg);
+          const float beta[4] = {bt.x, bt.y, bt.z, bt.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = xrow + 4 * lg + r;
+            const float vv = bf16_to_f32(X.vs[t * DVS + 16 * ct + l16]);
+            hv[r] = (_Float16)(beta[r] * (vv - acc[r]));
+          }
+          *reinterpret_cast<half4v*>(RT + (16 * ct + l16) * CS + xrow + 4 * lg) = hv;
+        }
+      }
+    }
+    lds_barrier();
+
+    // ---- D: delta = T R, stored transposed ---------------------------------------------
+#pragma unroll
+    for (int n = wave; n < 4 * NCT; n += kScanWaves) {
+      const int i = n & 3, ct = n >> 2;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        if (ks <= (i >> 1))
+          acc = mfma16x16x32(frag_s<8>(X.th, 16 * i, 32 * ks, lane), frag(RT, CS, 16 * ct, 32 * ks, lane), acc);
+      half4v hv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hv[r] = (_Float16)acc[r];
+      *reinterpret_cast<half4v*>(DT + (16 * ct + l16) * CS + 16 * i + 4 * lg) = hv;
+      if constexpr (SCAL) {
+        // K-^T delta = k^T (Diag(e^{gm - g}) delta): the state update takes the scaled copy
+        const float4 fm = *reinterpret_cast<const float4*>(X.gv + GV_FM + 16 * i + 4 * lg);
+        hv[0] = (_Float16)(acc[0] * fm.x);
+        hv[1] = (_Float16)(acc[1] * fm.y);
+        hv[2] = (_Float16)(acc[2] * fm.z);
+        hv[3] = (_Float16)(acc[3] * fm.w);
+        *reinterpret_cast<half4v*>(DT2 + (16 * ct + l16) * CS + 16 * i + 4 * lg) = hv;
+      }
+    }
+    lds_barrier();
+
+    // ---- O: chunk output rows [16 (w - 4), +16), waves 4-7 (stored with the next chunk) -----
+    if (xq_wave) {
+      const int i = wave & 3;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        f32x4 acc = XR[ct];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          if (ks <= (i >> 1))
+            acc = mfma16x16x32(frag(DT, CS, 16 * ct, 32 * ks, lane), frag_s<8>(X.aq, 16 * i, 32 * ks, lane), acc);
+        OA[ct] = acc;
+      }
+    }
+
+    // ---- S: state update for this wave's rows ---------------------------------------------
+    {
+      f32x4 acc[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const half8 ak = SCAL ? frag_ts(X.kp, 16 * wave, 32 * ks, lane) : frag_s<8>(X.km, 16 * wave, 32 * ks, lane);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          acc[ct] = mfma16x16x32(ak, frag(SCAL ? DT2 : DT, CS, 16 * ct, 32 * ks, lane), acc[ct]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[ct][r] = fmaf(fC[r], S[ct][r], fCm[r] * acc[ct][r]);
+    }
+    lds_barrier();
+  };
+
+  fetch(set_of(Flag<false>()), F, 0, true);
+  int c = 0;
+  for (; c + 1 < nchunks; c += 2) {
+    step(c, Flag<false>());
+    step(c + 1, Flag<true>());
   }
-  hipLaunchKernelGGL((chunk_scan_kernel<DCH, GEN, false, DVS>), grid, dim3(kScanThreads), 0, stream, p, ws);
+  if (c < nchunks) step(c, Flag<false>());
+  vm_wait_all();
+  if (xq_wave) store_out(nchunks - 1, true);
+
+  if (p.S_T) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = 16 * wave + 4 * lg + r;
+        p.S_T[(int64_t(bh) * D + d) * D + j0 + 16 * ct + l16] = S[ct][r];
+      }
+  }
+}
+
+template <bool DCH, int DVS>
+hipError_t launch_scan_sym(const Problem& p, const char* ws, hipStream_t stream) {
+  dim3 grid(unsigned(p.B * p.H), unsigned(D / DVS));
+  hipLaunchKernelGGL((chunk_scan_sym_kernel<DCH, DVS>), grid, dim3(kScanThreads), 0, stream, p, ws);
+  return hipGetLastError();
+}
+
+template <bool DCH, int DVS>
+hipError_t launch_scan_gen(const Problem& p, const char* ws, hipStream_t stream) {
+  dim3 grid(unsigned(p.B * p.H), unsigned(D / DVS));
+  if (p.write_channel)
+    hipLaunchKernelGGL((chunk_scan_kernel<DCH, true, true, DVS>), grid, dim3(kScanThreads), 0, stream, p, ws);
+  else
+    hipLaunchKernelGGL((chunk_scan_kernel<DCH, true, false, DVS>), grid, dim3(kScanThreads), 0, stream, p, ws);
   return hipGetLastError();
 }
 
@@ -940,11 +1290,11 @@ hipError_t launch_variant(const Problem& p, void* workspace, hipStream_t stream)
   // Fill the 256 compute units with (b, h, value-slice) workgroups while keeping the slices
   // (each stages its chunk's operand tiles) as wide as that allows.
   const int64_t bh = int64_t(p.B) * p.H;
-  if constexpr (!GEN) {
-    if (bh >= 128) return launch_scan<DCH, GEN, 64>(p, ws, stream);
+  if constexpr (GEN) {
+    return bh >= 64 ? launch_scan_gen<DCH, 32>(p, ws, stream) : launch_scan_gen<DCH, 16>(p, ws, stream);
+  } else {
+    return bh >= 64 ? launch_scan_sym<DCH, 32>(p, ws, stream) : launch_scan_sym<DCH, 16>(p, ws, stream);
   }
-  if (bh >= 64) return launch_scan<DCH, GEN, 32>(p, ws, stream);
-  return launch_scan<DCH, GEN, 16>(p, ws, stream);
 }
 
 }  // namespace

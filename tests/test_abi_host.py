@@ -126,7 +126,7 @@ def test_workspace_query_and_errors():
     L = _abi.lib()
     # matrix-core path: one packet per chunk of every (b, h) -- fp16 64 x 64 matrices (2 or 4),
     # fp16 operand tiles unless the decay is per head with symmetric gates, fp32 gate vector
-    scal = 2 * 64 * 64 * 2 + 512 * 4
+    scal = 2 * 64 * 64 * 2 + 2 * 64 * 128 * 2 + 512 * 4
     kda = 2 * 64 * 64 * 2 + 3 * 64 * 128 * 2 + 512 * 4
     gen = 4 * 64 * 64 * 2 + 4 * 64 * 128 * 2 + 512 * 4
     assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc())) == 2 * 4 * 2 * scal
