@@ -219,8 +219,23 @@ constexpr int GV_BETA = 0;                            // [64]
 constexpr int GV_FP = 64, GV_FM = 128, GV_SC = 192;   // scalar decay
 constexpr int GV_EM = 64, GV_FC = 192, GV_FCM = 320;  // per-channel decay, [128] each
 
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+
+// Lane l copies the 16 bytes at its global address `src` to LDS byte `lds_wave` + 16 l
+// (`lds_wave` is the same for the whole wave).
+__device__ __forceinline__ void dma16(gptr<const char> src, void* lds_wave) {
+  __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)lds_wave, 16, 0, 0);
+}
+
+// Wait for all of this wave's vector-memory operations (loads, stores, copies to LDS).
+__device__ __forceinline__ void vm_wait_all() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
+}
+
 template <bool DCH, bool GEN>
-__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, char* __restrict__ ws, int nchunks) {
+__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, char* __restrict__ ws, int nchunks,
+                                                              int64_t nblk) {
   using PK = Packet<DCH, GEN>;
   constexpr int NM = PK::nmat;
   __shared__ __attribute__((aligned(16))) _Float16 KP[C * KS];                 // K+
@@ -235,229 +250,271 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, char* _
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, lg = lane >> 4;
   const int d8 = tid & 15, tg = tid >> 4;
-  const int64_t blk = blockIdx.x;            // (b, h) * nchunks + chunk
-  const int bh = int(blk / nchunks), c = int(blk - int64_t(bh) * nchunks);
-  const int b = bh / p.H, h = bh - b * p.H;
   const int T = p.T, H = p.H;
-  const uint16_t* kin = static_cast<const uint16_t*>(p.k);
-  const uint16_t* qin = static_cast<const uint16_t*>(p.q);
-  char* pk = ws + blk * PK::bytes;           // this chunk's packet
-  _Float16* wsc = reinterpret_cast<_Float16*>(pk + PK::mat);
-  float* gv = reinterpret_cast<float*>(pk + PK::gate);
-  auto tok = [&](int t) { return (int64_t(b) * T + t) * H + h; };
+  const gptr<const uint16_t> kin = opaque_gptr(static_cast<const uint16_t*>(p.k));
+  const gptr<const uint16_t> qin = opaque_gptr(static_cast<const uint16_t*>(p.q));
+  const gptr<const float> ldin = opaque_gptr(p.log_decay);
+  const gptr<const float> erin = opaque_gptr(p.erase);
+  const bool erase_ch = GEN && p.erase_channel;
 
-  for (int i = tid; i < C * CS; i += kThreads) TH[i] = (_Float16)0.f;
-
-  uint4 kr[4], qr[4];
-  float ldr[DCH ? 4 : 1][DCH ? 8 : 1];
-  float err[GEN ? 4 : 1][GEN ? 8 : 1];
-  float lds = 0.f;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = c * C + 4 * tg + r;
-    const bool ok = t < T;
-    const int64_t base = ok ? tok(t) * D + 8 * d8 : 0;
-    kr[r] = ok ? *reinterpret_cast<const uint4*>(kin + base) : make_uint4(0, 0, 0, 0);
-    qr[r] = ok ? *reinterpret_cast<const uint4*>(qin + base) : make_uint4(0, 0, 0, 0);
-    if constexpr (DCH) unpack8(ld4(p.log_decay + base, ok), ld4(p.log_decay + base + 4, ok), ldr[r]);
-    if constexpr (GEN) {
-      if (p.erase_channel) unpack8(ld4(p.erase + base, ok), ld4(p.erase + base + 4, ok), err[r]);
-    }
-  }
-  if (tid < C) {
-    const int t = c * C + tid;
-    const bool ok = t < T;
-    const int64_t ti = ok ? tok(t) : 0;
-    if constexpr (!DCH) lds = ok ? p.log_decay[ti] : 0.f;
-    GB[tid] = (ok && !(GEN && p.erase_channel)) ? p.erase[ti] : 0.f;
-  }
-
-  float g[4][DCH ? 8 : 1];
-  chunk_cumsum<DCH>(ldr, lds, g, GSC, tid);
-
-  {
-    float gm[8];
-#pragma unroll
-    for (int ch = 0; ch < 8; ++ch) gm[ch] = chunk_gmid<DCH>(GSC, 8 * d8 + ch);
+  // Inputs of one chunk in registers: thread (token quad tg, channel octet d8) holds tokens
+  // 4 tg + r, channels 8 d8 .. + 7; threads < 64 hold token tid's per-head gates.  Tokens past
+  // the end load token T - 1 (zeroed where they are used), so every load is unconditional.
+  struct In {
+    uint4 kr[4], qr[4];
+    float ldr[DCH ? 4 : 1][DCH ? 8 : 1];
+    float err[GEN ? 4 : 1][GEN ? 8 : 1];
+    float lds, gb;
+  };
+  auto load_in = [&](In& I, int64_t blk) {
+    const int bh = int(blk / nchunks), c = int(blk - int64_t(bh) * nchunks);
+    const int b = bh / H, h = bh - b * H;
+    auto tok = [&](int t) { return (int64_t(b) * T + (t < T ? t : T - 1)) * H + h; };
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = 4 * tg + r;
-      float kf[8], qf[8], kp[8], km[8], qp[8];
-      bf16x8_to_f32(kr[r], kf);
-      bf16x8_to_f32(qr[r], qf);
-#pragma unroll
-      for (int ch = 0; ch < 8; ++ch) {
-        const float gg = DCH ? g[r][ch] : g[r][0];
-        const float fp = clamped_exp(gg - gm[ch]), fm = clamped_exp(gm[ch] - gg);
-        kp[ch] = kf[ch] * fp;
-        qp[ch] = qf[ch] * fp;
-        km[ch] = kf[ch] * fm;
-      }
-      *reinterpret_cast<half8*>(KP + t * KS + 8 * d8) = cvt8(kp);
-      *reinterpret_cast<half8*>(QP + t * KS + 8 * d8) = cvt8(qp);
-      *reinterpret_cast<half8*>(KM + t * KS + 8 * d8) = cvt8(km);
+      const int64_t base = tok(c * C + 4 * tg + r) * D + 8 * d8;
+      I.kr[r] = gload_u4(kin, base);
+      I.qr[r] = gload_u4(qin, base);
+      if constexpr (DCH) unpack8(gload_f4(ldin, base), gload_f4(ldin, base + 4), I.ldr[r]);
       if constexpr (GEN) {
-        float um[8];
-#pragma unroll
-        for (int ch = 0; ch < 8; ++ch) um[ch] = (p.erase_channel ? err[r][ch] : GB[t]) * km[ch];
-        *reinterpret_cast<half8*>(UM + t * KS + 8 * d8) = cvt8(um);
+        if (erase_ch) unpack8(gload_f4(erin, base), gload_f4(erin, base + 4), I.err[r]);
       }
     }
-  }
-  // gate vector
-  if constexpr (PK::kScal) {
     if (tid < C) {
-      const float x = GSC[tid] - GSC[31];
-      gv[GV_BETA + tid] = GB[tid];
-      gv[GV_FP + tid] = clamped_exp(x);
-      gv[GV_FM + tid] = clamped_exp(-x);
-    } else if (tid == C) {
-      const float gmid = GSC[31], gend = GSC[63];
-      *reinterpret_cast<float4*>(gv + GV_SC) =
-          make_float4(clamped_exp(gmid), expf(gend), clamped_exp(gend - gmid), 0.f);
+      const int64_t ti = tok(c * C + tid);
+      if constexpr (!DCH) I.lds = ldin[ti];
+      if (!erase_ch) I.gb = erin[ti];
     }
-  } else {
-    if (tid < C) gv[GV_BETA + tid] = GB[tid];
-    if (tid < D) {
-      const float gmid = chunk_gmid<DCH>(GSC, tid), gend = chunk_gend<DCH>(GSC, tid);
-      gv[GV_EM + tid] = clamped_exp(gmid);
-      gv[GV_FC + tid] = expf(gend);
-      gv[GV_FCM + tid] = clamped_exp(gend - gmid);
-    }
-  }
-  lds_barrier();
+  };
 
-  // Gram tiles, transposed: lane gets A[t = 16 I + l16][i = 16 J + 4 lg + r].
-  //   0: A for the solve (symmetric: beta_t A_kk; general: A_ku), strict, fp32 to LDS
-  //   1: A_qk (lower), 2: A_kk (strict), 3: A_qu (lower), fp16 to the workspace
-  constexpr int NG = 10 * NM;
-#pragma unroll
-  for (int n = 0; n < (NG + 3) / 4; ++n) {
-    const int idx = wave + 4 * n;
-    if (idx < NG) {
-      const int which = idx / 10;
-      int I, J;
-      tile_ij(idx - 10 * which, I, J);
-      const _Float16* Ab = (which == 3 || (GEN && which == 0)) ? UM : KM;
-      const _Float16* Bb = (which == 1 || which == 3) ? QP : KP;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        acc = mfma16x16x32(frag(Ab, KS, 16 * J, 32 * ks, lane), frag(Bb, KS, 16 * I, 32 * ks, lane), acc);
-      const int t = 16 * I + l16;
-      const int i0 = 16 * J + 4 * lg;
-      if (which == 0) {
-        const float sc = GEN ? 1.f : GB[t];
-        float4 v;
-        v.x = (i0 + 0 < t) ? sc * acc[0] : 0.f;
-        v.y = (i0 + 1 < t) ? sc * acc[1] : 0.f;
-        v.z = (i0 + 2 < t) ? sc * acc[2] : 0.f;
-        v.w = (i0 + 3 < t) ? sc * acc[3] : 0.f;
-        *reinterpret_cast<float4*>(AF + t * AFS + i0) = v;
-      } else {
-        const bool strict = which == 2;
-        half4v hv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hv[r] = (_Float16)((strict ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f);
-        *reinterpret_cast<half4v*>(wsc + which * (C * C) + swz<8>(t, i0)) = hv;
-      }
-    }
-  }
-  // upper-triangular 16 x 16 tiles of the workspace matrices after T are zero
-  for (int n = wave; n < 6 * (NM - 1); n += 4) {
-    const int m = 1 + n / 6, u = n % 6;
-    const int I = u < 3 ? 0 : u < 5 ? 1 : 2;           // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-    const int J = u < 3 ? 1 + u : u < 5 ? u - 1 : 3;
-    const half4v z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
-    *reinterpret_cast<half4v*>(wsc + m * (C * C) + swz<8>(16 * I + l16, 16 * J + 4 * lg)) = z;
-  }
-  // operand tiles for the scan: K+, Q+ (scalar decay: the plain k, q) row-major; K-, U-
-  // transposed ([channel][token]); all swizzled
-  if constexpr (PK::kScal) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 4 * tg + r;
-      float kf[8], qf[8];
-      bf16x8_to_f32(kr[r], kf);
-      bf16x8_to_f32(qr[r], qf);
-      *reinterpret_cast<half8*>(pk + PK::kp + 2 * swz<16>(t, 8 * d8)) = cvt8(kf);
-      *reinterpret_cast<half8*>(pk + PK::qp + 2 * swz<16>(t, 8 * d8)) = cvt8(qf);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < C * D / 8 / kThreads; ++i) {
-      const int u = tid + kThreads * i;
-      const int t = u >> 4, c8 = (((u & 15) ^ (t & 7))) * 8;  // stored unit u & 15 holds column c8
-      *reinterpret_cast<uint4*>(pk + PK::kp + 16 * u) = *reinterpret_cast<const uint4*>(KP + t * KS + c8);
-      *reinterpret_cast<uint4*>(pk + PK::qp + 16 * u) = *reinterpret_cast<const uint4*>(QP + t * KS + c8);
-    }
-#pragma unroll
-    for (int i = 0; i < C * D / 8 / kThreads; ++i) {
-      const int d = tid & (D - 1), t0 = 8 * ((tid >> 7) + 2 * i);
-      half8 x;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = KM[(t0 + j) * KS + d];
-      *reinterpret_cast<half8*>(pk + PK::kmt + 2 * swz<8>(d, t0)) = x;
-      if constexpr (GEN) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = UM[(t0 + j) * KS + d];
-        *reinterpret_cast<half8*>(pk + PK::umt + 2 * swz<8>(d, t0)) = x;
-      }
-    }
-  }
-  lds_barrier();
-
-  // Diagonal 16x16 blocks: fp32 forward substitution, one lane per (block, column).
-  if (wave == 0) {
-    const int bl = lg, col = l16;
-    const float* Ab = AF + (16 * bl) * AFS + 16 * bl;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float s0 = (r == col) ? 1.f : 0.f, s1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < r; i += 2) {
-        s0 = fmaf(-Ab[r * AFS + i], x[i], s0);
-        if (i + 1 < r) s1 = fmaf(-Ab[r * AFS + i + 1], x[i + 1], s1);
-      }
-      x[r] = s0 + s1;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) TH[(16 * bl + r) * CS + 16 * bl + col] = (_Float16)x[r];
-  }
-  lds_barrier();
-
-  // Off-diagonal blocks, level by level: T_JI = -T_JJ sum_{K=I}^{J-1} A_JK T_KI.
-#pragma unroll
-  for (int Jb = 1; Jb < 4; ++Jb) {
-    if (wave < Jb) {
-      const int Ib = wave;
-      f32x4 P = {0.f, 0.f, 0.f, 0.f};
-      for (int Kb = Ib; Kb < Jb; ++Kb) {
-        const float4 a4 = *reinterpret_cast<const float4*>(AF + (16 * Jb + l16) * AFS + 16 * Kb + 4 * lg);
-        half4v a, bt;
-        a[0] = (_Float16)a4.x; a[1] = (_Float16)a4.y; a[2] = (_Float16)a4.z; a[3] = (_Float16)a4.w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bt[i] = TH[(16 * Kb + 4 * lg + i) * CS + 16 * Ib + l16];
-        P = mfma16(a, bt, P);
-      }
-      half4v nb, a2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) nb[i] = (_Float16)(-P[i]);
-      a2 = *reinterpret_cast<const half4v*>(TH + (16 * Jb + l16) * CS + 16 * Jb + 4 * lg);
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 Tji = mfma16(a2, nb, z);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) TH[(16 * Jb + 4 * lg + r) * CS + 16 * Ib + l16] = (_Float16)Tji[r];
-    }
-    lds_barrier();
-  }
-
-  // T (64 x 64 fp16, swizzled) to the workspace: two 16-byte units per thread.
-  {
+  // One chunk: prefix sums, operand tiles, gates, Gram matrices, triangular solve.  The solve
+  // factor T stays in TH and is written out by the next chunk (or after the last), so that the
+  // next chunk's wait for its inputs does not also wait for these stores.
+  auto write_t = [&](int64_t blk) {
+    _Float16* wsc = reinterpret_cast<_Float16*>(ws + blk * PK::bytes + PK::mat);
     const int t = tid >> 2, c0 = (tid & 3) * 16;
     *reinterpret_cast<uint4*>(wsc + swz<8>(t, c0)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0);
     *reinterpret_cast<uint4*>(wsc + swz<8>(t, c0 + 8)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0 + 8);
+  };
+
+  In I;
+  int64_t blk = blockIdx.x;
+  const int64_t gstride = gridDim.x;
+  load_in(I, blk);
+  for (int64_t prev = -1; blk < nblk; prev = blk, blk += gstride) {
+    const int c = int(blk - (blk / nchunks) * nchunks);
+    char* pk = ws + blk * PK::bytes;  // this chunk's packet
+    _Float16* wsc = reinterpret_cast<_Float16*>(pk + PK::mat);
+    float* gv = reinterpret_cast<float*>(pk + PK::gate);
+    vm_wait_all();  // this chunk's inputs (loaded one chunk ago) and the older stores
+
+    // ---- inputs, masked past the last token --------------------------------------------
+    uint4 kr[4], qr[4];
+    float ldr[DCH ? 4 : 1][DCH ? 8 : 1];
+    float err[GEN ? 4 : 1][GEN ? 8 : 1];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = c * C + 4 * tg + r < T;
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      kr[r] = ok ? I.kr[r] : z;
+      qr[r] = ok ? I.qr[r] : z;
+      if constexpr (DCH) {
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) ldr[r][ch] = ok ? I.ldr[r][ch] : 0.f;
+      }
+      if constexpr (GEN) {
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) err[r][ch] = (ok && erase_ch) ? I.err[r][ch] : 0.f;
+      }
+    }
+    float lds = 0.f;
+    if (tid < C) {
+      const bool ok = c * C + tid < T;
+      if constexpr (!DCH) lds = ok ? I.lds : 0.f;
+      GB[tid] = (ok && !erase_ch) ? I.gb : 0.f;
+    }
+
+    float g[4][DCH ? 8 : 1];
+    chunk_cumsum<DCH>(ldr, lds, g, GSC, tid);
+
+    {
+      float gm[8];
+#pragma unroll
+      for (int ch = 0; ch < 8; ++ch) gm[ch] = chunk_gmid<DCH>(GSC, 8 * d8 + ch);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * tg + r;
+        float kf[8], qf[8], kp[8], km[8], qp[8];
+        bf16x8_to_f32(kr[r], kf);
+        bf16x8_to_f32(qr[r], qf);
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) {
+          const float gg = DCH ? g[r][ch] : g[r][0];
+          const float fp = clamped_exp(gg - gm[ch]), fm = clamped_exp(gm[ch] - gg);
+          kp[ch] = kf[ch] * fp;
+          qp[ch] = qf[ch] * fp;
+          km[ch] = kf[ch] * fm;
+        }
+        *reinterpret_cast<half8*>(KP + t * KS + 8 * d8) = cvt8(kp);
+        *reinterpret_cast<half8*>(QP + t * KS + 8 * d8) = cvt8(qp);
+        *reinterpret_cast<half8*>(KM + t * KS + 8 * d8) = cvt8(km);
+        if constexpr (GEN) {
+          float um[8];
+#pragma unroll
+          for (int ch = 0; ch < 8; ++ch) um[ch] = (erase_ch ? err[r][ch] : GB[t]) * km[ch];
+          *reinterpret_cast<half8*>(UM + t * KS + 8 * d8) = cvt8(um);
+        }
+        if constexpr (PK::kScal) {
+          // the scan of a scalar decay takes the plain k and q
+          *reinterpret_cast<half8*>(pk + PK::kp + 2 * swz<16>(t, 8 * d8)) = cvt8(kf);
+          *reinterpret_cast<half8*>(pk + PK::qp + 2 * swz<16>(t, 8 * d8)) = cvt8(qf);
+        }
+      }
+    }
+    // the registers are free: fetch the inputs of this workgroup's next chunk
+    if (blk + gstride < nblk) load_in(I, blk + gstride);
+
+    // gate vector
+    if constexpr (PK::kScal) {
+      if (tid < C) {
+        const float x = GSC[tid] - GSC[31];
+        gv[GV_BETA + tid] = GB[tid];
+        gv[GV_FP + tid] = clamped_exp(x);
+        gv[GV_FM + tid] = clamped_exp(-x);
+      } else if (tid == C) {
+        const float gmid = GSC[31], gend = GSC[63];
+        *reinterpret_cast<float4*>(gv + GV_SC) =
+            make_float4(clamped_exp(gmid), expf(gend), clamped_exp(gend - gmid), 0.f);
+      }
+    } else {
+      if (tid < C) gv[GV_BETA + tid] = GB[tid];
+      if (tid < D) {
+        const float gmid = chunk_gmid<DCH>(GSC, tid), gend = chunk_gend<DCH>(GSC, tid);
+        gv[GV_EM + tid] = clamped_exp(gmid);
+        gv[GV_FC + tid] = expf(gend);
+        gv[GV_FCM + tid] = clamped_exp(gend - gmid);
+      }
+    }
+    if (prev >= 0) write_t(prev);  // the previous chunk's T, still in TH
+    lds_barrier();
+    for (int i = tid; i < C * CS; i += kThreads) TH[i] = (_Float16)0.f;
+
+    // Gram tiles, transposed: lane gets A[t = 16 I + l16][i = 16 J + 4 lg + r].
+    //   0: A for the solve (symmetric: beta_t A_kk; general: A_ku), strict, fp32 to LDS
+    //   1: A_qk (lower), 2: A_kk (strict), 3: A_qu (lower), fp16 to the workspace
+    constexpr int NG = 10 * NM;
+#pragma unroll
+    for (int n = 0; n < (NG + 3) / 4; ++n) {
+      const int idx = wave + 4 * n;
+      if (idx < NG) {
+        const int which = idx / 10;
+        int I0, J0;
+        tile_ij(idx - 10 * which, I0, J0);
+        const _Float16* Ab = (which == 3 || (GEN && which == 0)) ? UM : KM;
+        const _Float16* Bb = (which == 1 || which == 3) ? QP : KP;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          acc = mfma16x16x32(frag(Ab, KS, 16 * J0, 32 * ks, lane), frag(Bb, KS, 16 * I0, 32 * ks, lane), acc);
+        const int t = 16 * I0 + l16;
+        const int i0 = 16 * J0 + 4 * lg;
+        if (which == 0) {
+          const float sc = GEN ? 1.f : GB[t];
+          float4 v;
+          v.x = (i0 + 0 < t) ? sc * acc[0] : 0.f;
+          v.y = (i0 + 1 < t) ? sc * acc[1] : 0.f;
+          v.z = (i0 + 2 < t) ? sc * acc[2] : 0.f;
+          v.w = (i0 + 3 < t) ? sc * acc[3] : 0.f;
+          *reinterpret_cast<float4*>(AF + t * AFS + i0) = v;
+        } else {
+          const bool strict = which == 2;
+          half4v hv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) hv[r] = (_Float16)((strict ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f);
+          *reinterpret_cast<half4v*>(wsc + which * (C * C) + swz<8>(t, i0)) = hv;
+        }
+      }
+    }
+    // upper-triangular 16 x 16 tiles of the workspace matrices after T are zero
+    for (int n = wave; n < 6 * (NM - 1); n += 4) {
+      const int m = 1 + n / 6, u = n % 6;
+      const int I0 = u < 3 ? 0 : u < 5 ? 1 : 2;           // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+      const int J0 = u < 3 ? 1 + u : u < 5 ? u - 1 : 3;
+      const half4v z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+      *reinterpret_cast<half4v*>(wsc + m * (C * C) + swz<8>(16 * I0 + l16, 16 * J0 + 4 * lg)) = z;
+    }
+    // operand tiles for the scan (per-channel decay or general gates): K+, Q+ row-major;
+    // K-, U- transposed ([channel][token]); all swizzled
+    if constexpr (!PK::kScal) {
+#pragma unroll
+      for (int i = 0; i < C * D / 8 / kThreads; ++i) {
+        const int u = tid + kThreads * i;
+        const int t = u >> 4, c8 = ((u & 15) ^ (t & 7)) * 8;  // stored unit u & 15 holds column c8
+        *reinterpret_cast<uint4*>(pk + PK::kp + 16 * u) = *reinterpret_cast<const uint4*>(KP + t * KS + c8);
+        *reinterpret_cast<uint4*>(pk + PK::qp + 16 * u) = *reinterpret_cast<const uint4*>(QP + t * KS + c8);
+      }
+#pragma unroll
+      for (int i = 0; i < C * D / 8 / kThreads; ++i) {
+        const int d = tid & (D - 1), t0 = 8 * ((tid >> 7) + 2 * i);
+        half8 x;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = KM[(t0 + j) * KS + d];
+        *reinterpret_cast<half8*>(pk + PK::kmt + 2 * swz<8>(d, t0)) = x;
+        if constexpr (GEN) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = UM[(t0 + j) * KS + d];
+          *reinterpret_cast<half8*>(pk + PK::umt + 2 * swz<8>(d, t0)) = x;
+        }
+      }
+    }
+    lds_barrier();
+
+    // Diagonal 16x16 blocks: fp32 forward substitution, one lane per (block, column).
+    if (wave == 0) {
+      const int bl = lg, col = l16;
+      const float* Ab = AF + (16 * bl) * AFS + 16 * bl;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s0 = (r == col) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < r; i += 2) {
+          s0 = fmaf(-Ab[r * AFS + i], x[i], s0);
+          if (i + 1 < r) s1 = fmaf(-Ab[r * AFS + i + 1], x[i + 1], s1);
+        }
+        x[r] = s0 + s1;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) TH[(16 * bl + r) * CS + 16 * bl + col] = (_Float16)x[r];
+    }
+    lds_barrier();
+
+    // Off-diagonal blocks, level by level: T_JI = -T_JJ sum_{K=I}^{J-1} A_JK T_KI.
+#pragma unroll
+    for (int Jb = 1; Jb < 4; ++Jb) {
+      if (wave < Jb) {
+        const int Ib = wave;
+        f32x4 P = {0.f, 0.f, 0.f, 0.f};
+        for (int Kb = Ib; Kb < Jb; ++Kb) {
+          const float4 a4 = *reinterpret_cast<const float4*>(AF + (16 * Jb + l16) * AFS + 16 * Kb + 4 * lg);
+          half4v a, bt;
+          a[0] = (_Float16)a4.x; a[1] = (_Float16)a4.y; a[2] = (_Float16)a4.z; a[3] = (_Float16)a4.w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bt[i] = TH[(16 * Kb + 4 * lg + i) * CS + 16 * Ib + l16];
+          P = mfma16(a, bt, P);
+        }
+        half4v nb, a2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nb[i] = (_Float16)(-P[i]);
+        a2 = *reinterpret_cast<const half4v*>(TH + (16 * Jb + l16) * CS + 16 * Jb + 4 * lg);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 Tji = mfma16(a2, nb, z);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) TH[(16 * Jb + 4 * lg + r) * CS + 16 * Ib + l16] = (_Float16)Tji[r];
+      }
+      lds_barrier();
+    }
+    if (blk + gstride >= nblk) write_t(blk);  // this workgroup's last chunk
   }
 }
 
@@ -951,20 +1008,6 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
 // LDS by the load-to-LDS path (no registers, no VALU) into the second of two buffer sets while
 // chunk c is computed from the first; each chunk starts with one wait for its own copies.
 // ------------------------------------------------------------------------------------------
-typedef __attribute__((address_space(1))) void gvoid;
-typedef __attribute__((address_space(3))) void lvoid;
-
-// Lane l copies the 16 bytes at its global address `src` to LDS byte `lds_wave` + 16 l
-// (`lds_wave` is the same for the whole wave).
-__device__ __forceinline__ void dma16(gptr<const char> src, void* lds_wave) {
-  __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)lds_wave, 16, 0, 0);
-}
-
-// Wait for all of this wave's vector-memory operations (loads, stores, copies to LDS).
-__device__ __forceinline__ void vm_wait_all() {
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
-}
-
 // Fragment (as frag()) of a swizzled tile with U 16-byte units per row.
 template <int U>
 __device__ __forceinline__ half8 frag_s(const _Float16* base, int row0, int k0, int lane) {
@@ -1283,8 +1326,17 @@ hipError_t launch_variant(const Problem& p, void* workspace, hipStream_t stream)
   const int nchunks = (p.T + C - 1) / C;
   char* ws = static_cast<char*>(workspace);
   const int64_t nblk = int64_t(p.B) * p.H * nchunks;
-  hipLaunchKernelGGL((chunk_prep_kernel<DCH, GEN>), dim3(unsigned(nblk)), dim3(kThreads), 0, stream, p, ws,
-                     nchunks);
+  // Persistent: as many workgroups as fit at once (two per compute unit; one with general
+  // gates, whose tiles need more LDS), each walking every grid-th chunk with its next chunk's
+  // inputs in flight.
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidDevice;
+  const int64_t resident = int64_t(ncu) * (GEN ? 1 : 2);
+  const int64_t grid = nblk < resident ? nblk : resident;
+  hipLaunchKernelGGL((chunk_prep_kernel<DCH, GEN>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p, ws, nchunks,
+                     nblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Fill the 256 compute units with (b, h, value-slice) workgroups while keeping the slices
