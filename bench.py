@@ -11,9 +11,10 @@ alternate so that the 194 MiB batch is not served from the 256 MB last-level cac
 
 The single JSON line printed at the end carries:
   value        prefill tokens/s (B*H*T per second of kernel time)
-  roofline     the chunk kernel against HBM bandwidth: algorithmic bytes per launch (compulsory
-               input/output bytes) / average launch duration, peak 8 TB/s, plus the counter-
-               measured HBM traffic when a counter summary for the current kernel source is
+  roofline     one forward call (its two kernels: the chunk-parallel prep and the chunk scan)
+               against HBM bandwidth: algorithmic bytes per call (compulsory input/output
+               bytes) / average call duration, peak 8 TB/s, plus the counter-measured HBM
+               traffic of both kernels when a counter summary for the current kernel source is
                committed under profiles/
   mfma         algorithmic matrix flops / time against the 2.5 PFLOP/s dense fp16/bf16 peak
   decode       1000 single-token steps for 256 sequences x 32 heads (steps/s, GB/s, fraction
@@ -208,7 +209,7 @@ def main():
     nbytes = algorithmic_bytes(wl)
     flops = algorithmic_flops(wl)
     achieved = nbytes / sec / 1e9
-    traffic = counter_traffic("chunk_kernel", PREFILL, CHUNK_SRC)
+    traffic = counter_traffic("chunk_fwd", PREFILL, CHUNK_SRC)
     line = {
         "metric": METRIC,
         "value": tok_s,
@@ -226,7 +227,8 @@ def main():
                    "chunk": wl.chunk, "qkv": "bf16", "gates": "fp32 per head", "o": "fp32"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "chunk_kernel", "algorithmic_bytes_per_launch": nbytes},
+                     "kernel": "dr_chunk_fwd = chunk_prep_kernel + chunk_scan_sym_kernel (one call)",
+                     "algorithmic_bytes_per_launch": nbytes},
         "mfma": {"achieved_tflops": flops / sec / 1e12, "peak_tflops": MFMA_PEAK_TFLOPS,
                  "frac": flops / sec / 1e12 / MFMA_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops},
         "timed_wall_s": wall,

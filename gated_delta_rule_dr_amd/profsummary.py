@@ -3,11 +3,12 @@
 
     python -m gated_delta_rule_dr_amd.profsummary trace  <kernel_stats.csv> <out.md> "<command>"
     python -m gated_delta_rule_dr_amd.profsummary traffic <fetch_counter_collection.csv> \\
-        <write_counter_collection.csv> <copy_ref_mib> <kernel-substring> <source-file> \\
-        <algorithmic-bytes-per-launch> <out.json> "<fetch command>" "<write command>"
+        <write_counter_collection.csv> <copy_ref_mib> <kernel-substring>[,<kernel-substring>...] \\
+        <source-file> <algorithmic-bytes-per-call> <out.json> "<fetch command>" "<write command>"
 
-``traffic`` converts the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch) of one kernel
-into HBM bytes per launch.  Each counter is scaled by the factor that makes it read the known
+``traffic`` converts the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch) of the kernels
+one call launches (each named by a substring; one dispatch of each per call) into HBM bytes
+per call.  Each counter is scaled by the factor that makes it read the known
 size of a plain elementwise copy profiled in the same run (``bench.py --copy-ref-mib N``:
 N MiB read and N MiB written), and the record carries a hash of the kernel's source so a
 stale record can be recognised.
@@ -63,24 +64,27 @@ def _kernel_avg(rows, counter, pattern):
     return sum(vals) / len(vals), len(vals)
 
 
-def traffic(fetch_csv, write_csv, copy_mib, pattern, source, alg_bytes, out_json, cmd_fetch, cmd_write):
+def traffic(fetch_csv, write_csv, copy_mib, patterns, source, alg_bytes, out_json, cmd_fetch, cmd_write):
     copy_bytes = int(copy_mib) * (1 << 20)
     fr, wr = _rows(fetch_csv), _rows(write_csv)
     f_fac, f_ref = _copy_ref(fr, "FETCH_SIZE", copy_bytes)
     w_fac, w_ref = _copy_ref(wr, "WRITE_SIZE", copy_bytes)
-    f_kib, nf = _kernel_avg(fr, "FETCH_SIZE", pattern)
-    w_kib, nw = _kernel_avg(wr, "WRITE_SIZE", pattern)
-    read_b = f_kib * 1024.0 * f_fac
-    write_b = w_kib * 1024.0 * w_fac
+    kernels = {}
+    read_b = write_b = 0.0
+    for pattern in patterns.split(","):
+        f_kib, nf = _kernel_avg(fr, "FETCH_SIZE", pattern)
+        w_kib, nw = _kernel_avg(wr, "WRITE_SIZE", pattern)
+        kernels[pattern] = {"fetch_size_kib_per_dispatch": f_kib, "write_size_kib_per_dispatch": w_kib,
+                            "dispatches": [nf, nw], "hbm_read_bytes": f_kib * 1024.0 * f_fac,
+                            "hbm_write_bytes": w_kib * 1024.0 * w_fac}
+        read_b += f_kib * 1024.0 * f_fac
+        write_b += w_kib * 1024.0 * w_fac
     with open(source, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()[:16]
     rec = {
-        "kernel": pattern,
+        "kernels": kernels,
         "source": source,
         "source_sha256_16": sha,
-        "fetch_size_kib_per_dispatch": f_kib,
-        "write_size_kib_per_dispatch": w_kib,
-        "dispatches": [nf, nw],
         "copy_reference": {"bytes_each_way": copy_bytes, "fetch_size_kib": f_ref, "write_size_kib": w_ref,
                            "fetch_factor": f_fac, "write_factor": w_fac},
         "hbm_read_bytes_per_launch": read_b,
