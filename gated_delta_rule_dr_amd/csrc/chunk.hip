@@ -1104,17 +1104,32 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   struct Fac {  // scalar decay: element 0 only
     float em[4], fc[4], fcm[4];
   };
-  auto fetch = [&](const Set& X, Fac& F, int c, bool copy) {
+  // Issued in batches (the key/query tiles; matrices, gates and values one stage later; K-^T
+  // one more stage later) so that the vector-memory queue drains between them instead of
+  // stalling every wave on one burst.
+  auto fetch_kq = [&](const Set& X, int c) {
     const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
-    const int ub = 16 * tid;  // this lane's byte within a 8 KB block
+    const int ub = 16 * tid;     // this lane's byte within a 8 KB block
     const int wb = 1024 * wave;  // this wave's LDS byte within a 8 KB block
-    if (copy) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       dma16(pk + PK::kp + ub + 8192 * i, reinterpret_cast<char*>(X.kp) + wb + 8192 * i);
       dma16(pk + PK::qp + ub + 8192 * i, reinterpret_cast<char*>(X.qp) + wb + 8192 * i);
-      if constexpr (!SCAL) dma16(pk + PK::kmt + ub + 8192 * i, reinterpret_cast<char*>(X.km) + wb + 8192 * i);
     }
+  };
+  auto fetch_km = [&](const Set& X, int c) {
+    if constexpr (!SCAL) {
+      const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        dma16(pk + PK::kmt + 16 * tid + 8192 * i, reinterpret_cast<char*>(X.km) + 1024 * wave + 8192 * i);
+    }
+  };
+  auto fetch = [&](const Set& X, Fac& F, int c, bool copy) {
+    const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
+    const int ub = 16 * tid;     // this lane's byte within a 8 KB block
+    const int wb = 1024 * wave;  // this wave's LDS byte within a 8 KB block
+    if (copy) {
     dma16(pk + PK::mat + ub, reinterpret_cast<char*>(X.th) + wb);
     dma16(pk + PK::mat + C * C * 2 + ub, reinterpret_cast<char*>(X.aq) + wb);
     if (wave < PK::ngate * 4 / 1024) dma16(pk + PK::gate + ub, reinterpret_cast<char*>(X.gv) + wb);
@@ -1174,7 +1189,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       *reinterpret_cast<half4v*>(ST + (16 * ct + l16) * KS + 16 * wave + 4 * lg) = hv;
     }
     lds_barrier();  // every wave's copies of this chunk have landed; S~^T is complete
-    fetch(Y, F, c + 1 < nchunks ? c + 1 : c, c + 1 < nchunks);
+    if (c + 1 < nchunks) fetch_kq(Y, c + 1);
 
     // ---- X = [K+; Q+] S~: waves 0-3 X_K rows [16 w, +16); waves 4-7 X_Q rows, transposed --
     f32x4 XR[NCT];
@@ -1223,6 +1238,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       }
     }
     lds_barrier();
+    fetch(Y, F, c + 1 < nchunks ? c + 1 : c, c + 1 < nchunks);
 
     // ---- D: delta = T R, stored transposed ---------------------------------------------
 #pragma unroll
@@ -1248,6 +1264,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       }
     }
     lds_barrier();
+    if (c + 1 < nchunks) fetch_km(Y, c + 1);
 
     // ---- O: chunk output rows [16 (w - 4), +16), waves 4-7 (stored with the next chunk) -----
     if (xq_wave) {
@@ -1283,7 +1300,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     lds_barrier();
   };
 
+  fetch_kq(set_of(Flag<false>()), 0);
   fetch(set_of(Flag<false>()), F, 0, true);
+  fetch_km(set_of(Flag<false>()), 0);
   int c = 0;
   for (; c + 1 < nchunks; c += 2) {
     step(c, Flag<false>());
