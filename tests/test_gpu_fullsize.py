@@ -1,0 +1,107 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+Each prefill workload runs once at full size on the device (inputs drawn with the device
+generator); the fp64 oracle then recomputes a few sampled (b, h) pairs -- first, last and one
+inside -- from the very same input values, over the whole sequence, and o and S_T of those
+pairs must agree to the bf16-path tolerance; every head is checked for finiteness.  The decode
+workload runs its full 256 x 32 heads for a number of steps and samples (n, h) pairs the same
+way.  A linearity identity covers every head of the bench workload."""
+import pytest
+import torch
+
+from metrics import err_S, err_o
+from oracle import decode_step as oracle_decode
+from oracle import recurrence
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 3e-3
+TOL_F32 = 1e-5
+
+
+@pytest.fixture(scope="module")
+def dr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_dr_amd as m
+
+    m.abi_version()
+    return m
+
+
+def _slice(x, b, h):
+    """Inputs of one (b, h) as a [1, T, 1, ...] CPU tensor."""
+    if x is None:
+        return None
+    return x[b:b + 1, :, h:h + 1].cpu()
+
+
+@pytest.mark.parametrize("name,pairs", [
+    ("gdn_scalar_bf16_t4k", [(0, 0), (1, 7), (3, 15)]),
+    ("kda_channel_bf16_t16k", [(0, 0), (1, 31)]),
+    ("gdn2_decoupled_bf16_t64k", [(0, 0), (0, 31)]),
+])
+def test_prefill_full_size_sampled_heads(dr, name, pairs):
+    from gated_delta_rule_dr_amd.workloads import generate, workload
+
+    wl = workload(name)
+    inp = generate(wl, device="cuda")
+    o = torch.empty((wl.B, wl.T, wl.H, wl.dv), device="cuda")
+    S_T = torch.empty((wl.B, wl.H, wl.dk, wl.dv), device="cuda")
+    dr.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"], inp["S0"],
+                 out=o, S_T=S_T)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(S_T).all()
+    print(f"{name}: |o|max={o.abs().max().item():.3g} |S_T|max={S_T.abs().max().item():.3g}", flush=True)
+    for b, h in pairs:
+        sl = {k: _slice(v, b, h) for k, v in inp.items()}
+        ro, rS = recurrence(sl["q"], sl["k"], sl["v"], sl["log_decay"], sl["erase"], sl["write"], sl["S0"])
+        eo = err_o(o[b:b + 1, :, h:h + 1], ro)
+        eS = err_S(S_T[b:b + 1, h:h + 1], rS)
+        print(f"{name} (b={b}, h={h}): err_o={eo:.3e} err_S={eS:.3e}", flush=True)
+        assert eo <= TOL_BF16 and eS <= TOL_BF16, (b, h, eo, eS)
+
+
+def test_prefill_full_size_linearity_all_heads(dr):
+    """With the gates fixed, (S0, V) -> (O, S_T) is linear, so o(2v) = 2 o(v) and S_T likewise
+    on every head of the full bench workload.  The chunk path meets this only to its rounding
+    level: a one-ulp fp32 difference (the matrix cores' accumulation is not exactly
+    scale-equivariant) can flip the fp16 rounding of a state operand, which moves later chunks
+    by one fp16 step (measured: 1e-4 normwise), so the bound is the bf16-path tolerance."""
+    from gated_delta_rule_dr_amd.workloads import generate, workload
+
+    wl = workload("gdn_scalar_bf16_t4k")
+    inp = generate(wl, device="cuda")
+    o1, S1 = dr.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], None, None)
+    o2, S2 = dr.chunk_fwd(inp["q"], inp["k"], inp["v"] * 2, inp["log_decay"], inp["erase"], None, None)
+    torch.cuda.synchronize()
+    eo, eS = err_o(o2 / 2, o1), err_S(S2 / 2, S1)
+    print(f"linearity: err_o={eo:.3e} err_S={eS:.3e}", flush=True)
+    assert eo <= TOL_BF16 and eS <= TOL_BF16
+
+
+def test_decode_full_size_sampled_pairs(dr):
+    from gated_delta_rule_dr_amd.workloads import generate_decode, workload
+
+    wl = workload("decode_kda_n256_h32")
+    steps = 16
+    inp = generate_decode(wl, steps=steps, device="cuda")
+    pairs = [(0, 0), (100, 17), (255, 31)]
+    S = inp["S0"].clone()
+    refS = {pr: inp["S0"][pr[0]:pr[0] + 1, pr[1]:pr[1] + 1].double().cpu().numpy() for pr in pairs}
+    o = torch.empty((wl.B, wl.H, wl.dv), device="cuda")
+    for s in range(steps):
+        g = lambda key: None if inp[key] is None else inp[key][s]
+        dr.decode_step(g("q"), g("k"), g("v"), g("log_decay"), g("erase"), g("write"), S=S, o=o)
+        torch.cuda.synchronize()
+        for n, h in pairs:
+            cut = lambda x: None if x is None else x[n:n + 1, h:h + 1].cpu()
+            ro, refS[(n, h)] = oracle_decode(cut(g("q")), cut(g("k")), cut(g("v")), cut(g("log_decay")),
+                                             cut(g("erase")), cut(g("write")), refS[(n, h)])
+            eo = err_o(o[n:n + 1, h:h + 1][:, None], ro[:, None])
+            assert eo <= TOL_F32, (s, n, h, eo)
+    for n, h in pairs:
+        eS = err_S(S[n:n + 1, h:h + 1], refS[(n, h)])
+        print(f"decode (n={n}, h={h}) after {steps} steps: err_S={eS:.3e}", flush=True)
+        assert eS <= TOL_F32
+    assert torch.isfinite(S).all()
