@@ -65,9 +65,11 @@ def test_prefill_full_size_sampled_heads(dr, name, pairs):
 def test_prefill_full_size_linearity_all_heads(dr):
     """With the gates fixed, (S0, V) -> (O, S_T) is linear, so o(2v) = 2 o(v) and S_T likewise
     on every head of the full bench workload.  The chunk path meets this only to its rounding
-    level: a one-ulp fp32 difference (the matrix cores' accumulation is not exactly
-    scale-equivariant) can flip the fp16 rounding of a state operand, which moves later chunks
-    by one fp16 step (measured: 1e-4 normwise), so the bound is the bf16-path tolerance."""
+    level: fp16 operands that fall in the subnormal range round on a fixed absolute grid, so
+    doubling them does not double their rounding (the matrix cores and normal-range
+    conversions do scale exactly); the resulting one-ulp differences can flip the fp16
+    rounding of a state operand in a later chunk, which moves that chunk by one fp16 step
+    (measured: 1e-4 normwise), so the bound is the bf16-path tolerance."""
     from gated_delta_rule_dr_amd.workloads import generate, workload
 
     wl = workload("gdn_scalar_bf16_t4k")
