@@ -233,9 +233,11 @@ __device__ __forceinline__ void vm_wait_all() {
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
 }
 
+// Per-channel decay with symmetric gates: held to two waves per SIMD (its input prefetch would
+// otherwise take the registers of the second resident workgroup).
 template <bool DCH, bool GEN>
-__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, char* __restrict__ ws, int nchunks,
-                                                              int64_t nblk) {
+__global__ __launch_bounds__(kThreads, (DCH && !GEN) ? 2 : 1) void chunk_prep_kernel(Problem p, char* __restrict__ ws,
+                                                                                     int nchunks, int64_t nblk) {
   using PK = Packet<DCH, GEN>;
   constexpr int NM = PK::nmat;
   __shared__ __attribute__((aligned(16))) _Float16 KP[C * KS];                 // K+
