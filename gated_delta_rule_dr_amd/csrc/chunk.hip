@@ -408,7 +408,10 @@ __global__ __launch_bounds__(kThreads, (DCH && !GEN) ? 2 : 1) void chunk_prep_ke
     //   0: A for the solve (symmetric: beta_t A_kk; general: A_ku), strict, fp32 to LDS
     //   1: A_qk (lower), 2: A_kk (strict), 3: A_qu (lower), fp16 to the workspace
     constexpr int NG = 10 * NM;
-#pragma unroll
+    // not unrolled for the per-channel symmetric variant: unrolled, its fragment loads are
+    // hoisted and the registers spill under the two-workgroup bound
+    constexpr int kGramUnroll = (DCH && !GEN) ? 1 : (NG + 3) / 4;
+#pragma unroll kGramUnroll
     for (int n = 0; n < (NG + 3) / 4; ++n) {
       const int idx = wave + 4 * n;
       if (idx < NG) {
