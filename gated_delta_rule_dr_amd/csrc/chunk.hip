@@ -233,10 +233,10 @@ __device__ __forceinline__ void vm_wait_all() {
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
 }
 
-// Per-channel decay with symmetric gates: held to two waves per SIMD (its input prefetch would
+// Per-channel decay or general gates: held to two waves per SIMD (the input prefetch would
 // otherwise take the registers of the second resident workgroup).
 template <bool DCH, bool GEN>
-__global__ __launch_bounds__(kThreads, (DCH && !GEN) ? 2 : 1) void chunk_prep_kernel(Problem p, char* __restrict__ ws,
+__global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_kernel(Problem p, char* __restrict__ ws,
                                                                                      int nchunks, int64_t nblk) {
   using PK = Packet<DCH, GEN>;
   constexpr int NM = PK::nmat;
@@ -244,10 +244,14 @@ __global__ __launch_bounds__(kThreads, (DCH && !GEN) ? 2 : 1) void chunk_prep_ke
   __shared__ __attribute__((aligned(16))) _Float16 KM[C * KS];                 // K-
   __shared__ __attribute__((aligned(16))) _Float16 QP[C * KS];                 // Q+
   __shared__ __attribute__((aligned(16))) _Float16 UM[GEN ? C * KS : 8];       // U- (general)
-  __shared__ __attribute__((aligned(16))) float AF[C * AFS];
+  // fp32 matrix of the solve.  With general gates it takes the place of Q+ (same size), whose
+  // last reader runs before it is written: that keeps two workgroups per compute unit.
+  __shared__ __attribute__((aligned(16))) float AFA[GEN ? 4 : C * AFS];
   __shared__ __attribute__((aligned(16))) _Float16 TH[C * CS];
   __shared__ float GB[C];
   __shared__ float GSC[4 * D];
+  static_assert(C * KS * 2 == C * AFS * 4, "the solve matrix must fit in the Q+ tile");
+  float* const AF = GEN ? reinterpret_cast<float*>(QP) : AFA;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, lg = lane >> 4;
@@ -262,25 +266,42 @@ __global__ __launch_bounds__(kThreads, (DCH && !GEN) ? 2 : 1) void chunk_prep_ke
   // Inputs of one chunk in registers: thread (token quad tg, channel octet d8) holds tokens
   // 4 tg + r, channels 8 d8 .. + 7; threads < 64 hold token tid's per-head gates.  Tokens past
   // the end load token T - 1 (zeroed where they are used), so every load is unconditional.
+  // Per-channel decay with general gates does not prefetch the per-channel erase gates (their
+  // registers would spill under the two-workgroup bound); it loads them as the chunk starts,
+  // ahead of their first use after the prefix sums.
+  constexpr bool kPrefetchErr = GEN && !DCH;
   struct In {
     uint4 kr[4], qr[4];
     float ldr[DCH ? 4 : 1][DCH ? 8 : 1];
-    float err[GEN ? 4 : 1][GEN ? 8 : 1];
+    float err[kPrefetchErr ? 4 : 1][kPrefetchErr ? 8 : 1];
     float lds, gb;
   };
-  auto load_in = [&](In& I, int64_t blk) {
+  auto tok_of = [&](int64_t blk) {
     const int bh = int(blk / nchunks), c = int(blk - int64_t(bh) * nchunks);
     const int b = bh / H, h = bh - b * H;
-    auto tok = [&](int t) { return (int64_t(b) * T + (t < T ? t : T - 1)) * H + h; };
+    return [=](int t) { return (int64_t(b) * T + (t < T ? t : T - 1)) * H + h; };
+  };
+  auto load_err = [&](float (&e)[4][8], int64_t blk) {
+    const int c = int(blk - (blk / nchunks) * nchunks);
+    const auto tok = tok_of(blk);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t base = tok(c * C + 4 * tg + r) * D + 8 * d8;
+      unpack8(gload_f4(erin, base), gload_f4(erin, base + 4), e[r]);
+    }
+  };
+  auto load_in = [&](In& I, int64_t blk) {
+    const int c = int(blk - (blk / nchunks) * nchunks);
+    const auto tok = tok_of(blk);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t base = tok(c * C + 4 * tg + r) * D + 8 * d8;
       I.kr[r] = gload_u4(kin, base);
       I.qr[r] = gload_u4(qin, base);
       if constexpr (DCH) unpack8(gload_f4(ldin, base), gload_f4(ldin, base + 4), I.ldr[r]);
-      if constexpr (GEN) {
-        if (erase_ch) unpack8(gload_f4(erin, base), gload_f4(erin, base + 4), I.err[r]);
-      }
+    }
+    if constexpr (kPrefetchErr) {
+      if (erase_ch) load_err(I.err, blk);
     }
     if (tid < C) {
       const int64_t ti = tok(c * C + tid);
@@ -299,21 +320,29 @@ __global__ __launch_bounds__(kThreads, (DCH && !GEN) ? 2 : 1) void chunk_prep_ke
     *reinterpret_cast<uint4*>(wsc + swz<8>(t, c0 + 8)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0 + 8);
   };
 
+  // Per-channel decay with general gates keeps no chunk in flight (its registers would spill);
+  // the second resident workgroup covers its load latency instead.
+  constexpr bool kPrefetch = !(DCH && GEN);
   In I;
   int64_t blk = blockIdx.x;
   const int64_t gstride = gridDim.x;
-  load_in(I, blk);
+  if constexpr (kPrefetch) load_in(I, blk);
   for (int64_t prev = -1; blk < nblk; prev = blk, blk += gstride) {
     const int c = int(blk - (blk / nchunks) * nchunks);
     char* pk = ws + blk * PK::bytes;  // this chunk's packet
     _Float16* wsc = reinterpret_cast<_Float16*>(pk + PK::mat);
     float* gv = reinterpret_cast<float*>(pk + PK::gate);
+    if constexpr (!kPrefetch) load_in(I, blk);
     vm_wait_all();  // this chunk's inputs (loaded one chunk ago) and the older stores
 
     // ---- inputs, masked past the last token --------------------------------------------
     uint4 kr[4], qr[4];
     float ldr[DCH ? 4 : 1][DCH ? 8 : 1];
     float err[GEN ? 4 : 1][GEN ? 8 : 1];
+    float en[GEN && !kPrefetchErr ? 4 : 1][GEN && !kPrefetchErr ? 8 : 1];
+    if constexpr (GEN && !kPrefetchErr) {
+      if (erase_ch) load_err(en, blk);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool ok = c * C + 4 * tg + r < T;
@@ -326,7 +355,7 @@ __global__ __launch_bounds__(kThreads, (DCH && !GEN) ? 2 : 1) void chunk_prep_ke
       }
       if constexpr (GEN) {
 #pragma unroll
-        for (int ch = 0; ch < 8; ++ch) err[r][ch] = (ok && erase_ch) ? I.err[r][ch] : 0.f;
+        for (int ch = 0; ch < 8; ++ch) err[r][ch] = (ok && erase_ch) ? (kPrefetchErr ? I.err[r][ch] : en[r][ch]) : 0.f;
       }
     }
     float lds = 0.f;
@@ -375,7 +404,7 @@ __global__ __launch_bounds__(kThreads, (DCH && !GEN) ? 2 : 1) void chunk_prep_ke
     }
 
     // per-channel decay: the registers are free, fetch the next chunk's inputs right away
-    if constexpr (!PK::kScal) {
+    if constexpr (!PK::kScal && kPrefetch) {
       if (blk + gstride < nblk) load_in(I, blk + gstride);
     }
 
@@ -407,41 +436,44 @@ __global__ __launch_bounds__(kThreads, (DCH && !GEN) ? 2 : 1) void chunk_prep_ke
     // Gram tiles, transposed: lane gets A[t = 16 I + l16][i = 16 J + 4 lg + r].
     //   0: A for the solve (symmetric: beta_t A_kk; general: A_ku), strict, fp32 to LDS
     //   1: A_qk (lower), 2: A_kk (strict), 3: A_qu (lower), fp16 to the workspace
-    constexpr int NG = 10 * NM;
-    // not unrolled for the per-channel symmetric variant: unrolled, its fragment loads are
-    // hoisted and the registers spill under the two-workgroup bound
-    constexpr int kGramUnroll = (DCH && !GEN) ? 1 : (NG + 3) / 4;
-#pragma unroll kGramUnroll
-    for (int n = 0; n < (NG + 3) / 4; ++n) {
-      const int idx = wave + 4 * n;
-      if (idx < NG) {
-        const int which = idx / 10;
-        int I0, J0;
-        tile_ij(idx - 10 * which, I0, J0);
-        const _Float16* Ab = (which == 3 || (GEN && which == 0)) ? UM : KM;
-        const _Float16* Bb = (which == 1 || which == 3) ? QP : KP;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto gram_tile = [&](int idx) {
+      const int which = idx / 10;
+      int I0, J0;
+      tile_ij(idx - 10 * which, I0, J0);
+      const _Float16* Ab = (which == 3 || (GEN && which == 0)) ? UM : KM;
+      const _Float16* Bb = (which == 1 || which == 3) ? QP : KP;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          acc = mfma16x16x32(frag(Ab, KS, 16 * J0, 32 * ks, lane), frag(Bb, KS, 16 * I0, 32 * ks, lane), acc);
-        const int t = 16 * I0 + l16;
-        const int i0 = 16 * J0 + 4 * lg;
-        if (which == 0) {
-          const float sc = GEN ? 1.f : GB[t];
-          float4 v;
-          v.x = (i0 + 0 < t) ? sc * acc[0] : 0.f;
-          v.y = (i0 + 1 < t) ? sc * acc[1] : 0.f;
-          v.z = (i0 + 2 < t) ? sc * acc[2] : 0.f;
-          v.w = (i0 + 3 < t) ? sc * acc[3] : 0.f;
-          *reinterpret_cast<float4*>(AF + t * AFS + i0) = v;
-        } else {
-          const bool strict = which == 2;
-          half4v hv;
+      for (int ks = 0; ks < 4; ++ks)
+        acc = mfma16x16x32(frag(Ab, KS, 16 * J0, 32 * ks, lane), frag(Bb, KS, 16 * I0, 32 * ks, lane), acc);
+      const int t = 16 * I0 + l16;
+      const int i0 = 16 * J0 + 4 * lg;
+      if (which == 0) {
+        const float sc = GEN ? 1.f : GB[t];
+        float4 v;
+        v.x = (i0 + 0 < t) ? sc * acc[0] : 0.f;
+        v.y = (i0 + 1 < t) ? sc * acc[1] : 0.f;
+        v.z = (i0 + 2 < t) ? sc * acc[2] : 0.f;
+        v.w = (i0 + 3 < t) ? sc * acc[3] : 0.f;
+        *reinterpret_cast<float4*>(AF + t * AFS + i0) = v;
+      } else {
+        const bool strict = which == 2;
+        half4v hv;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) hv[r] = (_Float16)((strict ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f);
-          *reinterpret_cast<half4v*>(wsc + which * (C * C) + swz<8>(t, i0)) = hv;
-        }
+        for (int r = 0; r < 4; ++r) hv[r] = (_Float16)((strict ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f);
+        *reinterpret_cast<half4v*>(wsc + which * (C * C) + swz<8>(t, i0)) = hv;
       }
+    };
+    constexpr int NG = 10 * NM;
+    // with general gates the solve matrix (tiles 0..9) overwrites Q+ and comes after the rest
+    constexpr int G0 = GEN ? 10 : 0;
+    // not unrolled with a per-channel decay: unrolled, the fragment loads are
+    // hoisted and the registers spill under the two-workgroup bound
+    constexpr int kGramUnroll = DCH ? 1 : (NG - G0 + 3) / 4;
+#pragma unroll kGramUnroll
+    for (int n = 0; n < (NG - G0 + 3) / 4; ++n) {
+      const int idx = G0 + wave + 4 * n;
+      if (idx < NG) gram_tile(idx);
     }
     // upper-triangular 16 x 16 tiles of the workspace matrices after T are zero
     for (int n = wave; n < 6 * (NM - 1); n += 4) {
@@ -476,6 +508,15 @@ __global__ __launch_bounds__(kThreads, (DCH && !GEN) ? 2 : 1) void chunk_prep_ke
       }
     }
     lds_barrier();
+    if constexpr (GEN) {
+      // A_ku into the solve matrix, now that Q+ has been read for the last time
+#pragma unroll
+      for (int n = 0; n < 3; ++n) {
+        const int idx = wave + 4 * n;
+        if (idx < 10) gram_tile(idx);
+      }
+      lds_barrier();
+    }
     // scalar decay: fetch the next chunk's inputs only now, in flight during the solve, which
     // keeps them out of the Gram stage's registers (measured faster for this variant)
     if constexpr (PK::kScal) {
@@ -1358,14 +1399,13 @@ hipError_t launch_variant(const Problem& p, void* workspace, hipStream_t stream)
   const int nchunks = (p.T + C - 1) / C;
   char* ws = static_cast<char*>(workspace);
   const int64_t nblk = int64_t(p.B) * p.H * nchunks;
-  // Persistent: as many workgroups as fit at once (two per compute unit; one with general
-  // gates, whose tiles need more LDS), each walking every grid-th chunk with its next chunk's
-  // inputs in flight.
+  // Persistent: as many workgroups as fit at once (two per compute unit), each walking every
+  // grid-th chunk with its next chunk's inputs in flight.
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipErrorInvalidDevice;
-  const int64_t resident = int64_t(ncu) * (GEN ? 1 : 2);
+  const int64_t resident = int64_t(ncu) * 2;
   const int64_t grid = nblk < resident ? nblk : resident;
   hipLaunchKernelGGL((chunk_prep_kernel<DCH, GEN>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p, ws, nchunks,
                      nblk);
