@@ -233,6 +233,14 @@ __device__ __forceinline__ void vm_wait_all() {
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
 }
 
+// Wait until at most N of this wave's vector-memory operations are outstanding.  Loads complete
+// in issue order, so this waits for every load issued before the last N loads.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | (0x7 << 4) | (0xf << 8) | ((N >> 4) << 14));
+}
+
 // Per-channel decay or general gates: held to two waves per SIMD (the input prefetch would
 // otherwise take the registers of the second resident workgroup).
 template <bool DCH, bool GEN>
@@ -1070,12 +1078,28 @@ __device__ __forceinline__ half8 frag_s(const _Float16* base, int row0, int k0, 
 
 // A-operand fragment of the transpose of a swizzled [token][128] tile: rows are channels
 // d0 + (lane % 16), contraction over tokens t0 + 8 (lane / 16) + 0..7.
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): lane 16 g + 4 a + b receives as element j
+// (0..3) the 16-bit element b of the 8 bytes at the address that lane 16 g + a + 4 j supplies.
+typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) fp16x4 lds_half4;
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4;
+__device__ __forceinline__ half4v ld_tr16(const _Float16* p) {
+  return __builtin_bit_cast(half4v, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_half4*)p));
+}
+__device__ __forceinline__ short4v ld_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
+}
+
+// frag_s of the transposed tile: A[row = d][k = t] = base[t][d] (base swizzled, 16 units per
+// row).  Lane 16 g + m supplies row t0 + 8 g + m / 4 (and 4 rows on), columns d0 + 4 (m % 4)
+// .. + 3, so lane 16 g + l16 receives base[t0 + 8 g + 0..7][d0 + l16].
 __device__ __forceinline__ half8 frag_ts(const _Float16* base, int d0, int t0, int lane) {
-  const int d = d0 + (lane & 15), t = t0 + 8 * (lane >> 4);
-  half8 a;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = base[swz<16>(t + i, d)];
-  return a;
+  const int m = lane & 15;
+  const int t = t0 + 8 * (lane >> 4) + (m >> 2), d = d0 + 4 * (m & 3);
+  const half4v lo = ld_tr16(base + swz<16>(t, d));
+  const half4v hi = ld_tr16(base + swz<16>(t + 4, d));
+  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 template <bool DCH, int DVS>
@@ -1084,15 +1108,21 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   constexpr bool SCAL = !DCH;
   constexpr int NCT = DVS / 16;  // 16-column tiles of the value slice
   constexpr int VU = DVS / 8;    // 16-byte units per value-slice row
-  // Two buffer sets of copy targets, one array each: reading one set never waits for the
-  // copies into the other.  Set layout (bytes): K+ (scalar decay: k) [64][128], Q+ (q)
-  // [64][128], K-^T [128][64] (per-channel decay), T [64][64], A_qk [64][64], gate vector
-  // [512] f32, v slice [64][DVS] (bf16).
-  constexpr int o_kp = 0, o_qp = o_kp + C * D * 2, o_km = o_qp + C * D * 2;
-  constexpr int o_th = o_km + (SCAL ? 0 : D * C * 2), o_aq = o_th + C * C * 2, o_gv = o_aq + C * C * 2;
-  constexpr int o_vs = o_gv + PK::ngate * 4, set_bytes = o_vs + C * DVS * 2;
-  __shared__ __attribute__((aligned(16))) char BS0[set_bytes];
-  __shared__ __attribute__((aligned(16))) char BS1[set_bytes];
+  // Two buffer sets of copy targets, each split into one array per copy batch: the compiler
+  // tracks copies into LDS per array, so reading one array never waits for the copies into
+  // another.  Batch 1 (bytes): K+ (scalar decay: k) [64][128], Q+ (q) [64][128], gate vector
+  // [512] f32, v slice [64][DVS] (bf16); batch 2: T [64][64], A_qk [64][64]; batch 3: K-^T
+  // [128][64] (per-channel decay).
+  constexpr int o_kp = 0, o_qp = o_kp + C * D * 2, o_gv = o_qp + C * D * 2;
+  constexpr int o_vs = o_gv + PK::ngate * 4, b1_bytes = o_vs + C * DVS * 2;
+  constexpr int o_th = 0, o_aq = o_th + C * C * 2, b2_bytes = o_aq + C * C * 2;
+  constexpr int b3_bytes = SCAL ? 16 : D * C * 2;
+  __shared__ __attribute__((aligned(16))) char B1S0[b1_bytes];
+  __shared__ __attribute__((aligned(16))) char B1S1[b1_bytes];
+  __shared__ __attribute__((aligned(16))) char B2S0[b2_bytes];
+  __shared__ __attribute__((aligned(16))) char B2S1[b2_bytes];
+  __shared__ __attribute__((aligned(16))) char B3S0[b3_bytes];
+  __shared__ __attribute__((aligned(16))) char B3S1[b3_bytes];
   // Written by the workgroup itself.
   __shared__ __attribute__((aligned(16))) _Float16 ST[DVS * KS];  // S~^T
   __shared__ __attribute__((aligned(16))) _Float16 RT[DVS * CS];  // R^T
@@ -1111,15 +1141,16 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   };
   auto set_of = [&](auto one) {
     constexpr bool B1 = decltype(one)::value;
-    char* base = B1 ? BS1 : BS0;
+    char* b1 = B1 ? B1S1 : B1S0;
+    char* b2 = B1 ? B2S1 : B2S0;
     Set x;
-    x.kp = reinterpret_cast<_Float16*>(base + o_kp);
-    x.qp = reinterpret_cast<_Float16*>(base + o_qp);
-    x.km = reinterpret_cast<_Float16*>(base + o_km);
-    x.th = reinterpret_cast<_Float16*>(base + o_th);
-    x.aq = reinterpret_cast<_Float16*>(base + o_aq);
-    x.gv = reinterpret_cast<float*>(base + o_gv);
-    x.vs = reinterpret_cast<uint16_t*>(base + o_vs);
+    x.kp = reinterpret_cast<_Float16*>(b1 + o_kp);
+    x.qp = reinterpret_cast<_Float16*>(b1 + o_qp);
+    x.gv = reinterpret_cast<float*>(b1 + o_gv);
+    x.vs = reinterpret_cast<uint16_t*>(b1 + o_vs);
+    x.th = reinterpret_cast<_Float16*>(b2 + o_th);
+    x.aq = reinterpret_cast<_Float16*>(b2 + o_aq);
+    x.km = reinterpret_cast<_Float16*>(B1 ? B3S1 : B3S0);
     return x;
   };
 
@@ -1158,10 +1189,13 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   struct Fac {  // scalar decay: element 0 only
     float em[4], fc[4], fcm[4];
   };
-  // Issued in batches (the key/query tiles; matrices, gates and values one stage later; K-^T
-  // one more stage later) so that the vector-memory queue drains between them instead of
-  // stalling every wave on one burst.
-  auto fetch_kq = [&](const Set& X, int c) {
+  // Issued in three batches, each as early as its buffers are free and each waited for just
+  // before its first reader: (1) key/query tiles, gate vector, values and factors, read from
+  // the start of the chunk; (2) T and A_qk, read from the D stage on; (3) K-^T (per-channel
+  // decay), read by the state update.  Every copy of batches 2 and 3 is issued by every lane
+  // (past the last chunk it repeats the last chunk into the idle set), so the number of loads
+  // a wave issues after each batch is known and a partial vmcnt wait suffices.
+  auto fetch1 = [&](const Set& X, Fac& F, int c) {
     const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
     const int ub = 16 * tid;     // this lane's byte within a 8 KB block
     const int wb = 1024 * wave;  // this wave's LDS byte within a 8 KB block
@@ -1170,28 +1204,11 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       dma16(pk + PK::kp + ub + 8192 * i, reinterpret_cast<char*>(X.kp) + wb + 8192 * i);
       dma16(pk + PK::qp + ub + 8192 * i, reinterpret_cast<char*>(X.qp) + wb + 8192 * i);
     }
-  };
-  auto fetch_km = [&](const Set& X, int c) {
-    if constexpr (!SCAL) {
-      const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        dma16(pk + PK::kmt + 16 * tid + 8192 * i, reinterpret_cast<char*>(X.km) + 1024 * wave + 8192 * i);
-    }
-  };
-  auto fetch = [&](const Set& X, Fac& F, int c, bool copy) {
-    const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
-    const int ub = 16 * tid;     // this lane's byte within a 8 KB block
-    const int wb = 1024 * wave;  // this wave's LDS byte within a 8 KB block
-    if (copy) {
-    dma16(pk + PK::mat + ub, reinterpret_cast<char*>(X.th) + wb);
-    dma16(pk + PK::mat + C * C * 2 + ub, reinterpret_cast<char*>(X.aq) + wb);
     if (wave < PK::ngate * 4 / 1024) dma16(pk + PK::gate + ub, reinterpret_cast<char*>(X.gv) + wb);
     if (tid < C * VU) {
       const bool ok = c * C + vt < T;
       const int64_t e = ok ? v_off + c * tstride : v_last;
       dma16(vin + 2 * e, reinterpret_cast<char*>(X.vs) + wb);
-    }
     }
     // the factors are loaded unconditionally (a conditional load would need a register copy,
     // and with it an immediate wait)
@@ -1210,6 +1227,21 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       F.fcm[0] = cc.x; F.fcm[1] = cc.y; F.fcm[2] = cc.z; F.fcm[3] = cc.w;
     }
   };
+  // copies per lane of batches 2 and 3, and a lower bound for batch 1
+  constexpr int kB1min = 4, kB2 = 2, kB3 = SCAL ? 0 : 2;
+  auto fetch2 = [&](const Set& X, int c) {
+    const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
+    dma16(pk + PK::mat + 16 * tid, reinterpret_cast<char*>(X.th) + 1024 * wave);
+    dma16(pk + PK::mat + C * C * 2 + 16 * tid, reinterpret_cast<char*>(X.aq) + 1024 * wave);
+  };
+  auto fetch3 = [&](const Set& X, int c) {
+    if constexpr (!SCAL) {
+      const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        dma16(pk + PK::kmt + 16 * tid + 8192 * i, reinterpret_cast<char*>(X.km) + 1024 * wave + 8192 * i);
+    }
+  };
 
   const int xrow = 16 * (wave & 3);
   const bool xq_wave = wave >= 4;
@@ -1225,7 +1257,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   auto step = [&](int c, auto one) {
     constexpr bool B1 = decltype(one)::value;
     const Set X = set_of(Flag<B1>()), Y = set_of(Flag<!B1>());
-    vm_wait_all();  // this chunk's copies (issued one chunk ago) and the previous stores
+    const int cn = c + 1 < nchunks ? c + 1 : c;  // chunk whose copies this step issues
+    vm_wait<kB2 + kB3>();  // batch 1 of this chunk and the stores of the one before
     if (c > 0 && xq_wave) store_out(c - 1, false);
     float em[4], fC[4], fCm[4];
 #pragma unroll
@@ -1242,8 +1275,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(em[r] * S[ct][r]);
       *reinterpret_cast<half4v*>(ST + (16 * ct + l16) * KS + 16 * wave + 4 * lg) = hv;
     }
-    lds_barrier();  // every wave's copies of this chunk have landed; S~^T is complete
-    if (c + 1 < nchunks) fetch_kq(Y, c + 1);
+    lds_barrier();  // every wave's batch 1 of this chunk has landed; S~^T is complete
+    fetch1(Y, F, cn);
 
     // ---- X = [K+; Q+] S~: waves 0-3 X_K rows [16 w, +16); waves 4-7 X_Q rows, transposed --
     f32x4 XR[NCT];
@@ -1281,18 +1314,21 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
           half4v hv;
           const float4 bt = *reinterpret_cast<const float4*>(X.gv + GV_BETA + xrow + 4 * lg);
           const float beta[4] = {bt.x, bt.y, bt.z, bt.w};
+          // v[xrow + 4 lg + r][16 ct + l16], r = 0..3, in one transposing read: lane 16 g + m
+          // supplies row xrow + 4 g + m / 4, columns 16 ct + 4 (m % 4) .. + 3
+          const short4v vr = ld_tr16(X.vs + (xrow + 4 * lg + (l16 >> 2)) * DVS + 16 * ct + 4 * (l16 & 3));
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int t = xrow + 4 * lg + r;
-            const float vv = bf16_to_f32(X.vs[t * DVS + 16 * ct + l16]);
+            const float vv = bf16_to_f32(uint16_t(vr[r]));
             hv[r] = (_Float16)(beta[r] * (vv - acc[r]));
           }
           *reinterpret_cast<half4v*>(RT + (16 * ct + l16) * CS + xrow + 4 * lg) = hv;
         }
       }
     }
+    vm_wait<kB3 + kB1min>();  // batch 2 of this chunk
     lds_barrier();
-    fetch(Y, F, c + 1 < nchunks ? c + 1 : c, c + 1 < nchunks);
+    fetch2(Y, cn);
 
     // ---- D: delta = T R, stored transposed ---------------------------------------------
 #pragma unroll
@@ -1317,8 +1353,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
         *reinterpret_cast<half4v*>(DT2 + (16 * ct + l16) * CS + 16 * i + 4 * lg) = hv;
       }
     }
+    if constexpr (!SCAL) vm_wait<kB1min + kB2>();  // batch 3 of this chunk
     lds_barrier();
-    if (c + 1 < nchunks) fetch_km(Y, c + 1);
+    fetch3(Y, cn);
 
     // ---- O: chunk output rows [16 (w - 4), +16), waves 4-7 (stored with the next chunk) -----
     if (xq_wave) {
@@ -1354,9 +1391,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     lds_barrier();
   };
 
-  fetch_kq(set_of(Flag<false>()), 0);
-  fetch(set_of(Flag<false>()), F, 0, true);
-  fetch_km(set_of(Flag<false>()), 0);
+  fetch1(set_of(Flag<false>()), F, 0);
+  fetch2(set_of(Flag<false>()), 0);
+  fetch3(set_of(Flag<false>()), 0);
   int c = 0;
   for (; c + 1 < nchunks; c += 2) {
     step(c, Flag<false>());
