@@ -1312,48 +1312,60 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       // an index, not a choice between two pointers: LDS reads keep their array's alias scope
       // only through address arithmetic, and without it every read waits for the copies
       const _Float16* Xa = X.kp + (xq_wave ? (o_qp - o_kp) / 2 : 0);
-      half8 af[4];
+      // Every LDS operand of the stage is read, by every wave, before the first product, so
+      // that the reads' latencies overlap instead of adding up.
+      half8 af[4], bsv[NCT][4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) af[ks] = frag_s<16>(Xa, xrow, 32 * ks, lane);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) bsv[ct][ks] = frag_s<16>(ST, 16 * ct, 32 * ks, lane);
+      // gates of rows xrow + 4 lg + r (X_K's layout) and of row xrow + l16 (X_Q^T's layout);
+      // four consecutive floats in one read: a single address keeps the read's alias scope
+      // (per-element addresses would lose it and then wait for the copies)
+      const float4 bt = *reinterpret_cast<const float4*>(X.gv + GV_BETA + xrow + 4 * lg);
+      float4 fk = make_float4(1.f, 1.f, 1.f, 1.f);
+      float fq = 1.f;
+      if constexpr (SCAL) {
+        fk = *reinterpret_cast<const float4*>(X.gv + GV_FP + xrow + 4 * lg);
+        fq = X.gv[GV_FP + xrow + l16];
+      }
+      // v[xrow + 4 lg + r][16 ct + l16], r = 0..3, in one transposing read per column tile:
+      // lane 16 g + m supplies row xrow + 4 g + m / 4, columns 16 ct + 4 (m % 4) .. + 3
+      short4v vr[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int vr_row = xrow + 4 * lg + (l16 >> 2), vr_unit = 2 * ct + ((l16 & 3) >> 1);
+        vr[ct] = ld_tr16(X.vs + vr_row * DVS + 8 * (vr_unit ^ vs_key(vr_row)) + 4 * (l16 & 1));
+      }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const half8 bs = frag_s<16>(ST, 16 * ct, 32 * ks, lane);
           // the wave-dependent operand order is a choice of operands for one product: two
           // products behind a branch gave wrong results in one register allocation
-          const half8 opa = xq_wave ? bs : af[ks], opb = xq_wave ? af[ks] : bs;
+          const half8 opa = xq_wave ? bsv[ct][ks] : af[ks], opb = xq_wave ? af[ks] : bsv[ct][ks];
           acc = mfma16x16x32(opa, opb, acc);
         }
         if constexpr (SCAL) {
           // rows of X_K are tokens xrow + 4 lg + r; X_Q^T has token xrow + l16 as its column
-          if (xq_wave) {
-            const float f = X.gv[GV_FP + xrow + l16];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= f;
-          } else {
-            // four consecutive floats in one read: a single address keeps the read's alias
-            // scope (per-element addresses would lose it and then wait for the copies)
-            const float4 f = *reinterpret_cast<const float4*>(X.gv + GV_FP + xrow + 4 * lg);
-            acc[0] *= f.x; acc[1] *= f.y; acc[2] *= f.z; acc[3] *= f.w;
-          }
+          acc[0] *= xq_wave ? fq : fk.x;
+          acc[1] *= xq_wave ? fq : fk.y;
+          acc[2] *= xq_wave ? fq : fk.z;
+          acc[3] *= xq_wave ? fq : fk.w;
         }
         XR[ct] = acc;
-        if (!xq_wave) {
-          // R = Diag(beta) (V - X_K), stored transposed
-          half4v hv;
-          const float4 bt = *reinterpret_cast<const float4*>(X.gv + GV_BETA + xrow + 4 * lg);
-          const float beta[4] = {bt.x, bt.y, bt.z, bt.w};
-          // v[xrow + 4 lg + r][16 ct + l16], r = 0..3, in one transposing read: lane 16 g + m
-          // supplies row xrow + 4 g + m / 4, columns 16 ct + 4 (m % 4) .. + 3
-          const int vr_row = xrow + 4 * lg + (l16 >> 2), vr_unit = 2 * ct + ((l16 & 3) >> 1);
-          const short4v vr = ld_tr16(X.vs + vr_row * DVS + 8 * (vr_unit ^ vs_key(vr_row)) + 4 * (l16 & 1));
+      }
+      if (!xq_wave) {
+        // R = Diag(beta) (V - X_K), stored transposed
+        const float beta[4] = {bt.x, bt.y, bt.z, bt.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float vv = bf16_to_f32(uint16_t(vr[r]));
-            hv[r] = (_Float16)(beta[r] * (vv - acc[r]));
-          }
+        for (int ct = 0; ct < NCT; ++ct) {
+          half4v hv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(beta[r] * (bf16_to_f32(uint16_t(vr[ct][r])) - XR[ct][r]));
           *reinterpret_cast<half4v*>(RT + swz<8>(16 * ct + l16, xrow + 4 * lg)) = hv;
         }
       }
@@ -1366,11 +1378,17 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
 #pragma unroll
     for (int n = wave; n < 4 * NCT; n += kScanWaves) {
       const int i = n & 3, ct = n >> 2;
+      // T is lower triangular with zero upper tiles in the packet, so the products run over
+      // both halves unconditionally (no branch around the reads)
+      half8 ta[2], rb[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        ta[ks] = frag_s<8>(X.th, 16 * i, 32 * ks, lane);
+        rb[ks] = frag_s<8>(RT, 16 * ct, 32 * ks, lane);
+      }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        if (ks <= (i >> 1))
-          acc = mfma16x16x32(frag_s<8>(X.th, 16 * i, 32 * ks, lane), frag_s<8>(RT, 16 * ct, 32 * ks, lane), acc);
+      for (int ks = 0; ks < 2; ++ks) acc = mfma16x16x32(ta[ks], rb[ks], acc);
       half4v hv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) hv[r] = (_Float16)acc[r];
@@ -1392,13 +1410,19 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     // ---- O: chunk output rows [16 (w - 4), +16), waves 4-7 (stored with the next chunk) -----
     if (xq_wave) {
       const int i = wave & 3;
+      // A_qk has zero upper tiles in the packet: both halves, no branch
+      half8 qa[2], db[NCT][2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        qa[ks] = frag_s<8>(X.aq, 16 * i, 32 * ks, lane);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) db[ct][ks] = frag_s<8>(DT, 16 * ct, 32 * ks, lane);
+      }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         f32x4 acc = XR[ct];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          if (ks <= (i >> 1))
-            acc = mfma16x16x32(frag_s<8>(DT, 16 * ct, 32 * ks, lane), frag_s<8>(X.aq, 16 * i, 32 * ks, lane), acc);
+        for (int ks = 0; ks < 2; ++ks) acc = mfma16x16x32(db[ct][ks], qa[ks], acc);
         OA[ct] = acc;
       }
     }
@@ -1408,13 +1432,17 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       f32x4 acc[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      half8 ak[2], dk[NCT][2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const half8 ak = SCAL ? frag_ts(X.kp, 16 * wave, 32 * ks, lane) : frag_s<8>(X.km, 16 * wave, 32 * ks, lane);
+        ak[ks] = SCAL ? frag_ts(X.kp, 16 * wave, 32 * ks, lane) : frag_s<8>(X.km, 16 * wave, 32 * ks, lane);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          acc[ct] = mfma16x16x32(ak, frag_s<8>(SCAL ? DT2 : DT, 16 * ct, 32 * ks, lane), acc[ct]);
+        for (int ct = 0; ct < NCT; ++ct) dk[ct][ks] = frag_s<8>(SCAL ? DT2 : DT, 16 * ct, 32 * ks, lane);
       }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[ct] = mfma16x16x32(ak[ks], dk[ct][ks], acc[ct]);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
