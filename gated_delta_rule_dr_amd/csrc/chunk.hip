@@ -1448,7 +1448,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[ct][r] = fmaf(fC[r], S[ct][r], fCm[r] * acc[ct][r]);
     }
-    lds_barrier();
+    // No barrier here: the next step's first LDS write (S~^T) targets a tile last read before
+    // this step's second barrier, and its copies go out only after its own first barrier.
   };
 
   fetch1(set_of(Flag<false>()), F, 0);
