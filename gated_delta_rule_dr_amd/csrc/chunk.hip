@@ -405,6 +405,16 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
         float kf[8], qf[8], kp[8], km[8], qp[8];
         bf16x8_to_f32(kr[r], kf);
         bf16x8_to_f32(qr[r], qf);
+        if constexpr (PK::kScal) {
+          // scalar decay: plain k and q, in LDS for the Gram products (which take the decay per
+          // element, e^{g_t - g_i}) and in the packet for the scan
+          const half8 hk = cvt8(kf), hq = cvt8(qf);
+          *reinterpret_cast<half8*>(KP + t * KS + 8 * d8) = hk;
+          *reinterpret_cast<half8*>(QP + t * KS + 8 * d8) = hq;
+          *reinterpret_cast<half8*>(pk + PK::kp + 2 * swz<16>(t, 8 * d8)) = hk;
+          *reinterpret_cast<half8*>(pk + PK::qp + 2 * swz<16>(t, 8 * d8)) = hq;
+          continue;
+        }
 #pragma unroll
         for (int ch = 0; ch < 8; ++ch) {
           const float gg = DCH ? g[r][ch] : g[r][0];
@@ -421,11 +431,6 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
 #pragma unroll
           for (int ch = 0; ch < 8; ++ch) um[ch] = (erase_ch ? err[r][ch] : GB[t]) * km[ch];
           *reinterpret_cast<half8*>(UM + t * KS + 8 * d8) = cvt8(um);
-        }
-        if constexpr (PK::kScal) {
-          // the scan of a scalar decay takes the plain k and q
-          *reinterpret_cast<half8*>(pk + PK::kp + 2 * swz<16>(t, 8 * d8)) = cvt8(kf);
-          *reinterpret_cast<half8*>(pk + PK::qp + 2 * swz<16>(t, 8 * d8)) = cvt8(qf);
         }
       }
     }
@@ -467,7 +472,7 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
       const int which = idx / 10;
       int I0, J0;
       tile_ij(idx - 10 * which, I0, J0);
-      const _Float16* Ab = (which == 3 || (GEN && which == 0)) ? UM : KM;
+      const _Float16* Ab = (which == 3 || (GEN && which == 0)) ? UM : PK::kScal ? KP : KM;
       const _Float16* Bb = (which == 1 || which == 3) ? QP : KP;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -475,6 +480,16 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
         acc = mfma16x16x32(frag(Ab, KS, 16 * J0, 32 * ks, lane), frag(Bb, KS, 16 * I0, 32 * ks, lane), acc);
       const int t = 16 * I0 + l16;
       const int i0 = 16 * J0 + 4 * lg;
+      if constexpr (PK::kScal) {
+        // the decay between token i and token t >= i: e^{g_t - g_i} <= 1 (entries above the
+        // diagonal are zeroed below)
+        const float gt = GSC[t];
+        const float4 gi = *reinterpret_cast<const float4*>(GSC + i0);
+        acc[0] *= __expf(fminf(gt - gi.x, 0.f));
+        acc[1] *= __expf(fminf(gt - gi.y, 0.f));
+        acc[2] *= __expf(fminf(gt - gi.z, 0.f));
+        acc[3] *= __expf(fminf(gt - gi.w, 0.f));
+      }
       if (which == 0) {
         const float sc = GEN ? 1.f : GB[t];
         float4 v;
