@@ -620,26 +620,31 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
 constexpr int kScanWaves = 8;
 constexpr int kScanThreads = 64 * kScanWaves;
 
-// SCAL (scalar decay, symmetric gates): KP / QP hold the plain k and q.
+// Fragment (as frag()) of a swizzled tile with U 16-byte units per row.
+template <int U>
+__device__ __forceinline__ half8 frag_s(const _Float16* base, int row0, int k0, int lane) {
+  return *reinterpret_cast<const half8*>(base + swz<U>(row0 + (lane & 15), k0 + 8 * (lane >> 4)));
+}
+
+// LDS layout of the register-staged scan (general gates).
 template <bool GEN, bool SCAL, int DVS>
 struct ScanLayout {
-  static constexpr int kp = 0;                                // K+ / k   [64][KS] half
-  static constexpr int qp = kp + C * KS * 2;                  // Q+ / q   [64][KS]
-  static constexpr int kmt = qp + C * KS * 2;                 // K-^T     [128][CS] (not SCAL)
-  static constexpr int umt = kmt + (SCAL ? 0 : D * CS * 2);   // U-^T     [128][CS] (general)
-  static constexpr int st = umt + (GEN ? D * CS * 2 : 0);     // S~^T     [DVS][KS]
-  static constexpr int th = st + DVS * KS * 2;                // T        [64][CS]
-  static constexpr int aq = th + C * CS * 2;                  // A_qk     [64][CS]
-  static constexpr int akk = aq + C * CS * 2;                 // A_kk     [64][CS]  (general)
-  static constexpr int aqu = akk + (GEN ? C * CS * 2 : 0);    // A_qu     [64][CS]  (general)
-  static constexpr int rt = aqu + (GEN ? C * CS * 2 : 0);     // R^T / Y^T [DVS][CS]
-  static constexpr int dt = rt + DVS * CS * 2;                // delta^T / (-M)^T [DVS][CS]
-  static constexpr int dt2 = dt + DVS * CS * 2;               // SCAL: (Diag(e^{gm-g}) delta)^T
-  static constexpr int vt = dt2 + (SCAL ? DVS * CS * 2 : 0);  // V [64][DVS+8] or Vt^T [DVS][CS]
-  static constexpr int vstride = GEN ? CS : DVS + 8;
-  static constexpr int vbytes = GEN ? DVS * CS * 2 : C * (DVS + 8) * 2;
-  static constexpr int gv = vt + vbytes;                      // gate vector [512] f32
-  static constexpr int total = gv + (GEN ? 0 : 512 * 4);
+  static_assert(GEN && !SCAL, "the register-staged scan serves general gates");
+  // Every tile in the packet's swizzled layout (see swz_key), so units copy straight across and
+  // fragment reads are conflict-free.
+  static constexpr int kp = 0;                 // K+       [64][128] half
+  static constexpr int qp = kp + C * D * 2;    // Q+       [64][128]
+  static constexpr int kmt = qp + C * D * 2;   // K-^T     [128][64]
+  static constexpr int umt = kmt + D * C * 2;  // U-^T     [128][64]
+  static constexpr int st = umt + D * C * 2;   // S~^T     [DVS][128]
+  static constexpr int th = st + DVS * D * 2;  // T        [64][64]
+  static constexpr int aq = th + C * C * 2;    // A_qk     [64][64]
+  static constexpr int akk = aq + C * C * 2;   // A_kk     [64][64]
+  static constexpr int aqu = akk + C * C * 2;  // A_qu     [64][64]
+  static constexpr int rt = aqu + C * C * 2;   // Y^T      [DVS][64]
+  static constexpr int dt = rt + DVS * C * 2;  // (-M)^T   [DVS][64]
+  static constexpr int vt = dt + DVS * C * 2;  // Vt^T     [DVS][64]
+  static constexpr int total = vt + DVS * C * 2;
 };
 
 // Value-slice words per thread: DVS/8 bf16 values.
@@ -684,14 +689,12 @@ template <bool DCH, bool GEN, bool WCH, int DVS>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, const char* __restrict__ ws) {
   static_assert(GEN, "symmetric gates use chunk_scan_sym_kernel");
   using PK = Packet<DCH, GEN>;
-  constexpr bool SCAL = PK::kScal;
-  using L = ScanLayout<GEN, SCAL, DVS>;
+  using L = ScanLayout<GEN, false, DVS>;
   constexpr int NM = PK::nmat;
   constexpr int NCT = DVS / 16;   // 16-column tiles of the value slice
   constexpr int VPT = DVS / 8;    // value columns per thread in the V load
-  constexpr int NTU = SCAL ? 4 : (GEN ? 8 : 6);    // 16-byte operand-tile units per thread
-  constexpr bool GVL = !GEN;                       // gate vector kept in LDS (beta, e^{+-(g-gm)})
-  constexpr int PF = SCAL ? 2 : 1;                 // chunks of prefetch in flight
+  constexpr int NTU = 8;  // 16-byte operand-tile units per thread (K+, Q+, K-^T, U-^T)
+  constexpr int PF = 1;   // chunks of prefetch in flight
   __shared__ __attribute__((aligned(16))) char smem[L::total];
   _Float16* KP = reinterpret_cast<_Float16*>(smem + L::kp);
   _Float16* QP = reinterpret_cast<_Float16*>(smem + L::qp);
@@ -704,9 +707,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   _Float16* AQU = reinterpret_cast<_Float16*>(smem + L::aqu);
   _Float16* RT = reinterpret_cast<_Float16*>(smem + L::rt);
   _Float16* DT = reinterpret_cast<_Float16*>(smem + L::dt);
-  _Float16* DT2 = reinterpret_cast<_Float16*>(smem + L::dt2);
   _Float16* VT = reinterpret_cast<_Float16*>(smem + L::vt);
-  float* GV = reinterpret_cast<float*>(smem + L::gv);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -717,8 +718,6 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   const int T = p.T, H = p.H;
   const int nchunks = (T + C - 1) / C;
   const int nfull = T / C;  // chunks with C tokens
-  const gptr<const uint16_t> kin = opaque_gptr(static_cast<const uint16_t*>(p.k));
-  const gptr<const uint16_t> qin = opaque_gptr(static_cast<const uint16_t*>(p.q));
   const gptr<const uint16_t> vin = opaque_gptr(static_cast<const uint16_t*>(p.v));
   const gptr<const float> wrin = opaque_gptr(p.write);
   const gptr<const char> pbase = opaque_gptr(ws) + int64_t(bh) * nchunks * PK::bytes;
@@ -734,31 +733,24 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       S[ct][r] = p.S0 ? p.S0[(int64_t(bh) * D + d) * D + j0 + 16 * ct + l16] : 0.f;
     }
 
-  // Load mapping.  Scalar-decay k / q: thread = (token pair tg, channel octet d8), tokens
-  // 2 tg + r, channels 8 d8 .. 8 d8 + 7.  Packet tiles: 16-byte units tid and tid + 512.
-  // Value slice: token tid / 8, columns VPT (tid % 8) .. + VPT - 1.  Matrices: row tid / 8,
-  // columns 8 (tid % 8) .. + 7.
-  const int d8 = tid & 15, tg = tid >> 4;
+  // Load mapping.  Packet tiles: 16-byte units tid and tid + 512; matrices: unit tid.  Value
+  // slice: token tid / 8, columns VPT (tid % 8) .. + VPT - 1.
   const int vtok = tid >> 3, vcol = (tid & 7) * VPT;
   auto tok = [&](int t) { return (int64_t(b) * T + t) * H + h; };
   // Per-thread element offsets at chunk 0; chunk c adds c * tstride (tokens are H * D apart).
   const int64_t tstride = int64_t(C) * H * D;
-  const int64_t kq_off = tok(2 * tg) * D + 8 * d8;
   const int64_t v_off = tok(vtok) * D + j0 + vcol;
   const int64_t w_off = tok(vtok);
   const int64_t o_off = tok(16 * (wave & 3) + l16) * D + j0 + 4 * lg;
   // Tokens past the end load token T - 1 instead (the values are zeroed where they are used), so
   // that every load is issued unconditionally and the wait counts stay exact.
-  const int64_t kq_last = tok(T - 1) * D + 8 * d8;
   const int64_t v_last = tok(T - 1) * D + j0 + vcol;
   const int64_t w_last = tok(T - 1);
 
   struct Pref {
     uint4 mr[NM];             // this thread's 16 bytes of T, A_qk (, A_kk, A_qu)
-    uint4 tl[NTU];            // k, q (scalar decay) or K+, Q+, K-^T (, U-^T) units
-    float gv;                 // gate-vector element tid
-    float4 sc[SCAL ? 1 : 3];  // per-channel e^{gm}, e^{gC}, e^{gC-gm} of this thread's 4 rows
-    float sc3[3];             // scalar decay: e^{gm}, e^{gC}, e^{gC-gm}
+    uint4 tl[NTU];            // K+, Q+, K-^T, U-^T units
+    float4 sc[3];             // per-channel e^{gm}, e^{gC}, e^{gC-gm} of this thread's 4 rows
     VSlice<DVS> vr;
     float wr[GEN ? VPT : 1];  // write gates of the value slice (per channel) or of token vtok
   };
@@ -767,39 +759,24 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   // vector-memory path stays busy without stalling every wave at one point.
   auto load_a = [&](Pref& P, int c) {
     const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
-    if constexpr (SCAL) {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const bool ok = c * C + 2 * tg + r < T;
-        const int64_t base = ok ? kq_off + c * tstride + r * (int64_t(H) * D) : kq_last;
-        P.tl[r] = gload_u4(kin, base);
-        P.tl[2 + r] = gload_u4(qin, base);
-      }
-#pragma unroll
-      for (int i = 0; i < 3; ++i) P.sc3[i] = *(gptr<const float>)(pk + PK::gate + 4 * (GV_SC + i));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        P.tl[i] = ldb16(pk, PK::kp + 16 * (tid + kScanThreads * i));
-        P.tl[2 + i] = ldb16(pk, PK::qp + 16 * (tid + kScanThreads * i));
-      }
-      const int d0 = 16 * wave + 4 * lg;
-      P.sc[0] = ldf16(pk, PK::gate + 4 * (GV_EM + d0));
-      P.sc[1] = ldf16(pk, PK::gate + 4 * (GV_FC + d0));
-      P.sc[2] = ldf16(pk, PK::gate + 4 * (GV_FCM + d0));
+    for (int i = 0; i < 2; ++i) {
+      P.tl[i] = ldb16(pk, PK::kp + 16 * (tid + kScanThreads * i));
+      P.tl[2 + i] = ldb16(pk, PK::qp + 16 * (tid + kScanThreads * i));
     }
-    if constexpr (GVL) P.gv = *(gptr<const float>)(pk + PK::gate + 4 * tid);
+    const int d0 = 16 * wave + 4 * lg;
+    P.sc[0] = ldf16(pk, PK::gate + 4 * (GV_EM + d0));
+    P.sc[1] = ldf16(pk, PK::gate + 4 * (GV_FC + d0));
+    P.sc[2] = ldf16(pk, PK::gate + 4 * (GV_FCM + d0));
   };
   auto load_b = [&](Pref& P, int c) {
     const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
 #pragma unroll
     for (int m = 0; m < NM; ++m) P.mr[m] = ldb16(pk, PK::mat + m * (C * C * 2) + 16 * tid);
-    if constexpr (!SCAL) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        P.tl[4 + i] = ldb16(pk, PK::kmt + 16 * (tid + kScanThreads * i));
-        if constexpr (GEN) P.tl[6 + i] = ldb16(pk, PK::umt + 16 * (tid + kScanThreads * i));
-      }
+    for (int i = 0; i < 2; ++i) {
+      P.tl[4 + i] = ldb16(pk, PK::kmt + 16 * (tid + kScanThreads * i));
+      P.tl[6 + i] = ldb16(pk, PK::umt + 16 * (tid + kScanThreads * i));
     }
   };
   auto load_c = [&](Pref& P, int c) {
@@ -831,56 +808,29 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   auto step = [&](auto tail, int c, Pref& P) {
     constexpr bool TAIL = decltype(tail)::value;
     // ---- L: the chunk's packet, value slice and S~^T into LDS ------------------------------
-    if constexpr (SCAL) {
+    // the LDS tiles keep the packet's layout: 16-byte units copy straight across
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int t = 2 * tg + r;
-        const bool ok = c * C + t < T;
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        float kf[8], qf[8];
-        bf16x8_to_f32(ok ? P.tl[r] : z, kf);
-        bf16x8_to_f32(ok ? P.tl[2 + r] : z, qf);
-        *reinterpret_cast<half8*>(KP + t * KS + 8 * d8) = cvt8(kf);
-        *reinterpret_cast<half8*>(QP + t * KS + 8 * d8) = cvt8(qf);
-      }
-    } else {
-      // packet units are swizzled (see swz_key); LDS rows are padded instead
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int u = tid + kScanThreads * i;
-        const int t = u >> 4, ct = ((u & 15) ^ swz_key<16>(t)) * 8;
-        const int d = u >> 3, dt = ((u & 7) ^ swz_key<8>(d)) * 8;
-        *reinterpret_cast<uint4*>(KP + t * KS + ct) = P.tl[i];
-        *reinterpret_cast<uint4*>(QP + t * KS + ct) = P.tl[2 + i];
-        *reinterpret_cast<uint4*>(KMT + d * CS + dt) = P.tl[4 + i];
-        if constexpr (GEN) *reinterpret_cast<uint4*>(UMT + d * CS + dt) = P.tl[6 + i];
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + kScanThreads * i;
+      *reinterpret_cast<uint4*>(KP + 8 * u) = P.tl[i];
+      *reinterpret_cast<uint4*>(QP + 8 * u) = P.tl[2 + i];
+      *reinterpret_cast<uint4*>(KMT + 8 * u) = P.tl[4 + i];
+      *reinterpret_cast<uint4*>(UMT + 8 * u) = P.tl[6 + i];
     }
-    {
-      const int mc = ((tid & 7) ^ swz_key<8>(vtok)) * 8;
-      *reinterpret_cast<uint4*>(TH + vtok * CS + mc) = P.mr[0];
-      *reinterpret_cast<uint4*>(AQ + vtok * CS + mc) = P.mr[1];
-      if constexpr (GEN) {
-        *reinterpret_cast<uint4*>(AKK + vtok * CS + mc) = P.mr[2 % NM];
-        *reinterpret_cast<uint4*>(AQU + vtok * CS + mc) = P.mr[3 % NM];
-      }
-    }
-    if constexpr (GVL) GV[tid] = P.gv;
+    *reinterpret_cast<uint4*>(TH + 8 * tid) = P.mr[0];
+    *reinterpret_cast<uint4*>(AQ + 8 * tid) = P.mr[1];
+    *reinterpret_cast<uint4*>(AKK + 8 * tid) = P.mr[2];
+    *reinterpret_cast<uint4*>(AQU + 8 * tid) = P.mr[3];
     {
       float vf[VPT];
       vslice_f32<DVS>(P.vr, vf);
       const bool vok = c * C + vtok < T;
 #pragma unroll
       for (int i = 0; i < VPT; ++i) vf[i] = vok ? vf[i] : 0.f;
-      if constexpr (GEN) {
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-          const float w = WCH ? P.wr[i] : P.wr[0];
-          VT[(vcol + i) * CS + vtok] = (_Float16)(w * vf[i]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) VT[vtok * L::vstride + vcol + i] = (_Float16)vf[i];
+      for (int i = 0; i < VPT; ++i) {
+        const float w = WCH ? P.wr[i] : P.wr[0];
+        VT[swz<8>(vcol + i, vtok)] = (_Float16)(w * vf[i]);
       }
     }
     // S~^T = (Diag(e^{gm}) S)^T; the end-of-chunk factors of this wave's rows stay in registers.
@@ -889,22 +839,16 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       float em[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if constexpr (SCAL) {
-          em[r] = P.sc3[0];
-          fC[r] = P.sc3[1];
-          fCm[r] = P.sc3[2];
-        } else {
-          em[r] = (&P.sc[0].x)[r];
-          fC[r] = (&P.sc[1].x)[r];
-          fCm[r] = (&P.sc[2].x)[r];
-        }
+        em[r] = (&P.sc[0].x)[r];
+        fC[r] = (&P.sc[1].x)[r];
+        fCm[r] = (&P.sc[2].x)[r];
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         half4v hv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(em[r] * S[ct][r]);
-        *reinterpret_cast<half4v*>(ST + (16 * ct + l16) * KS + 16 * wave + 4 * lg) = hv;
+        *reinterpret_cast<half4v*>(ST + swz<16>(16 * ct + l16, 16 * wave + 4 * lg)) = hv;
       }
     }
     lds_barrier();
@@ -921,7 +865,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       const _Float16* Xa = xq_wave ? QP : KP;
       half8 af[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) af[ks] = frag(Xa, KS, xrow, 32 * ks, lane);
+      for (int ks = 0; ks < 4; ++ks) af[ks] = frag_s<16>(Xa, xrow, 32 * ks, lane);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -929,80 +873,59 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
         // the output tile it seeds can be stored as 16-byte rows of o.
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const half8 bs = frag(ST, KS, 16 * ct, 32 * ks, lane);
+          const half8 bs = frag_s<16>(ST, 16 * ct, 32 * ks, lane);
           // the wave-dependent operand order is a choice of operands for one product: two
           // products behind a branch gave wrong results in one register allocation
           const half8 opa = xq_wave ? bs : af[ks], opb = xq_wave ? af[ks] : bs;
           acc = mfma16x16x32(opa, opb, acc);
         }
-        if constexpr (SCAL) {
-          // rows of X_K are tokens xrow + 4 lg + r; X_Q^T has token xrow + l16 as its column
-          if (xq_wave) {
-            const float f = GV[GV_FP + xrow + l16];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= f;
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= GV[GV_FP + xrow + 4 * lg + r];
-          }
-        }
         XR[ct] = acc;
-        if constexpr (!GEN) {
-          if (!xq_wave) {
-            // R = Diag(beta) (V - X_K), stored transposed
-            half4v hv;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int t = xrow + 4 * lg + r;
-              const float vv = (float)VT[t * L::vstride + 16 * ct + l16];
-              hv[r] = (_Float16)(GV[GV_BETA + t] * (vv - acc[r]));
-            }
-            *reinterpret_cast<half4v*>(RT + (16 * ct + l16) * CS + xrow + 4 * lg) = hv;
-          }
-        }
       }
     }
     lds_barrier();
 
-    if constexpr (GEN) {
-      // Y = X_K + A_kk Vt, stored transposed (B operand of M = T Y)
-      if (!xq_wave) {
+    // Y = X_K + A_kk Vt, stored transposed (B operand of M = T Y); A_kk has zero upper tiles,
+    // so both halves of the product run unconditionally
+    if (!xq_wave) {
+      half8 ka[2], vb[NCT][2];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          f32x4 y = XR[ct];
+      for (int ks = 0; ks < 2; ++ks) {
+        ka[ks] = frag_s<8>(AKK, xrow, 32 * ks, lane);
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            if (ks <= (wave >> 1))
-              y = mfma16x16x32(frag(AKK, CS, xrow, 32 * ks, lane), frag(VT, CS, 16 * ct, 32 * ks, lane), y);
-          half4v hv;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) hv[r] = (_Float16)y[r];
-          *reinterpret_cast<half4v*>(RT + (16 * ct + l16) * CS + xrow + 4 * lg) = hv;
-        }
+        for (int ct = 0; ct < NCT; ++ct) vb[ct][ks] = frag_s<8>(VT, 16 * ct, 32 * ks, lane);
       }
-      lds_barrier();
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        f32x4 y = XR[ct];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) y = mfma16x16x32(ka[ks], vb[ct][ks], y);
+        half4v hv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hv[r] = (_Float16)y[r];
+        *reinterpret_cast<half4v*>(RT + swz<8>(16 * ct + l16, xrow + 4 * lg)) = hv;
+      }
     }
+    lds_barrier();
 
     load_b(P, cn);
     // ---- D: delta = T R (symmetric) or -M = -(T Y) (general), stored transposed ---------
 #pragma unroll
     for (int n = wave; n < 4 * NCT; n += kScanWaves) {
       const int i = n & 3, ct = n >> 2;
+      // T has zero upper tiles: both halves, no branch
+      half8 ta[2], yb[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        ta[ks] = frag_s<8>(TH, 16 * i, 32 * ks, lane);
+        yb[ks] = frag_s<8>(RT, 16 * ct, 32 * ks, lane);
+      }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        if (ks <= (i >> 1))
-          acc = mfma16x16x32(frag(TH, CS, 16 * i, 32 * ks, lane), frag(RT, CS, 16 * ct, 32 * ks, lane), acc);
+      for (int ks = 0; ks < 2; ++ks) acc = mfma16x16x32(ta[ks], yb[ks], acc);
       half4v hv;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(GEN ? -acc[r] : acc[r]);
-      *reinterpret_cast<half4v*>(DT + (16 * ct + l16) * CS + 16 * i + 4 * lg) = hv;
-      if constexpr (SCAL) {
-        // K-^T delta = k^T (Diag(e^{gm - g}) delta): the state update takes the scaled copy
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(acc[r] * GV[GV_FM + 16 * i + 4 * lg + r]);
-        *reinterpret_cast<half4v*>(DT2 + (16 * ct + l16) * CS + 16 * i + 4 * lg) = hv;
-      }
+      for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(-acc[r]);
+      *reinterpret_cast<half4v*>(DT + swz<8>(16 * ct + l16, 16 * i + 4 * lg)) = hv;
     }
     lds_barrier();
 
@@ -1012,20 +935,26 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       // O^T tile: lane holds O[t = 16 i + l16][j = 16 ct + 4 lg + 0..3]
       const int i = wave & 3;
       const int t = c * C + 16 * i + l16;
+      // A_qk and A_qu have zero upper tiles: both halves, no branch
+      half8 bq[2], bu[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bq[ks] = frag_s<8>(AQ, 16 * i, 32 * ks, lane);
+        bu[ks] = frag_s<8>(AQU, 16 * i, 32 * ks, lane);
+      }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         f32x4 acc = XR[ct];
+        half8 va[2], da[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          if (ks <= (i >> 1)) {
-            const half8 bq = frag(AQ, CS, 16 * i, 32 * ks, lane);
-            if constexpr (GEN) {
-              acc = mfma16x16x32(frag(VT, CS, 16 * ct, 32 * ks, lane), bq, acc);
-              acc = mfma16x16x32(frag(DT, CS, 16 * ct, 32 * ks, lane), frag(AQU, CS, 16 * i, 32 * ks, lane), acc);
-            } else {
-              acc = mfma16x16x32(frag(DT, CS, 16 * ct, 32 * ks, lane), bq, acc);
-            }
-          }
+          va[ks] = frag_s<8>(VT, 16 * ct, 32 * ks, lane);
+          da[ks] = frag_s<8>(DT, 16 * ct, 32 * ks, lane);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          acc = mfma16x16x32(va[ks], bq[ks], acc);
+          acc = mfma16x16x32(da[ks], bu[ks], acc);
         }
         if (!TAIL || t < T) store_o4(p.o, o_off + c * tstride + 16 * ct, acc, p.o_bf16);
       }
@@ -1036,26 +965,24 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       f32x4 acc[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      half8 ak[2], au[2], bv[NCT][2], bd[NCT][2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        half8 ak, au;
-        if constexpr (SCAL) {
-          ak = frag_t(KP, 16 * wave, 32 * ks, lane);
-        } else {
-          ak = frag(KMT, CS, 16 * wave, 32 * ks, lane);
-          if constexpr (GEN) au = frag(UMT, CS, 16 * wave, 32 * ks, lane);
-        }
+        ak[ks] = frag_s<8>(KMT, 16 * wave, 32 * ks, lane);
+        au[ks] = frag_s<8>(UMT, 16 * wave, 32 * ks, lane);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-          const half8 bd = frag(SCAL ? DT2 : DT, CS, 16 * ct, 32 * ks, lane);
-          if constexpr (GEN) {
-            acc[ct] = mfma16x16x32(ak, frag(VT, CS, 16 * ct, 32 * ks, lane), acc[ct]);
-            acc[ct] = mfma16x16x32(au, bd, acc[ct]);
-          } else {
-            acc[ct] = mfma16x16x32(ak, bd, acc[ct]);
-          }
+          bv[ct][ks] = frag_s<8>(VT, 16 * ct, 32 * ks, lane);
+          bd[ct][ks] = frag_s<8>(DT, 16 * ct, 32 * ks, lane);
         }
       }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          acc[ct] = mfma16x16x32(ak[ks], bv[ct][ks], acc[ct]);
+          acc[ct] = mfma16x16x32(au[ks], bd[ct][ks], acc[ct]);
+        }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -1069,26 +996,11 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
     load_b(P, c);
     load_c(P, c);
   };
-  Pref PA, PB;
+  Pref PA;
   load(PA, 0);
-  if constexpr (PF == 2) {
-    // keep the prologue's loads in chunk order: the loop's wait counts assume it
-    asm volatile("" ::: "memory");
-    load(PB, nchunks > 1 ? 1 : 0);
-    asm volatile("" ::: "memory");
-    // both halves unconditional inside the loop, so the wait counts at its head are exact
-    int c = 0;
-    for (; c + 1 < nfull; c += 2) {
-      step(Flag<false>(), c, PA);
-      step(Flag<false>(), c + 1, PB);
-    }
-    if (c < nchunks) step(Flag<true>(), c, PA);
-    if (c + 1 < nchunks) step(Flag<true>(), c + 1, PB);
-  } else {
-    int c = 0;
-    for (; c < nfull; ++c) step(Flag<false>(), c, PA);
-    if (c < nchunks) step(Flag<true>(), c, PA);
-  }
+  int c = 0;
+  for (; c < nfull; ++c) step(Flag<false>(), c, PA);
+  if (c < nchunks) step(Flag<true>(), c, PA);
 
   if (p.S_T) {
 #pragma unroll
@@ -1101,20 +1013,13 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   }
 }
 
+
 // ------------------------------------------------------------------------------------------
 // Scan, symmetric gates (one per-head erase/write gate): the chunks of one (b, h, value slice)
 // in order, eight waves per workgroup.  The packet tiles of chunk c + 1 are copied global ->
 // LDS by the load-to-LDS path (no registers, no VALU) into the second of two buffer sets while
 // chunk c is computed from the first; each chunk starts with one wait for its own copies.
 // ------------------------------------------------------------------------------------------
-// Fragment (as frag()) of a swizzled tile with U 16-byte units per row.
-template <int U>
-__device__ __forceinline__ half8 frag_s(const _Float16* base, int row0, int k0, int lane) {
-  return *reinterpret_cast<const half8*>(base + swz<U>(row0 + (lane & 15), k0 + 8 * (lane >> 4)));
-}
-
-// A-operand fragment of the transpose of a swizzled [token][128] tile: rows are channels
-// d0 + (lane % 16), contraction over tokens t0 + 8 (lane / 16) + 0..7.
 // gfx950 transposing LDS read (ds_read_b64_tr_b16): lane 16 g + 4 a + b receives as element j
 // (0..3) the 16-bit element b of the 8 bytes at the address that lane 16 g + a + 4 j supplies.
 typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
