@@ -882,7 +882,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
         XR[ct] = acc;
       }
     }
-    lds_barrier();
+    // (no barrier: the X stage writes no LDS, and Y reads only tiles stored before the last one)
 
     // Y = X_K + A_kk Vt, stored transposed (B operand of M = T Y); A_kk has zero upper tiles,
     // so both halves of the product run unconditionally
