@@ -198,12 +198,15 @@ struct Packet {
   static constexpr bool kScal = !DCH && !GEN;
   static constexpr int nmat = GEN ? 4 : 2;
   static constexpr int mat = 0;
-  static constexpr int kp = mat + nmat * C * C * 2;
+  // bytes per matrix: symmetric gates store the six nonzero 16 x 32 blocks of their lower-
+  // triangular matrices (see tri_pos), general gates the whole swizzled 64 x 64 tile
+  static constexpr int matb = GEN ? C * C * 2 : 6 * 1024;
+  static constexpr int kp = mat + nmat * matb;
   static constexpr int qp = kp + C * D * 2;
   static constexpr int kmt = qp + C * D * 2;
   static constexpr int umt = kmt + (kScal ? 0 : D * C * 2);
   static constexpr int gate = umt + (GEN ? D * C * 2 : 0);
-  static constexpr int ngate = 512;  // floats
+  static constexpr int ngate = kScal ? 256 : 512;  // floats
   static constexpr int bytes = gate + ngate * 4;
 };
 
@@ -232,6 +235,19 @@ template <int U>
 __device__ __forceinline__ int swz(int r, int col) {
   return (r * U + ((col >> 3) ^ swz_key<U>(r))) * 8 + (col & 7);
 }
+
+// Lower-triangular 64 x 64 fp16 matrices (T, A_qk) of the symmetric-gate packet: only the six
+// 16 x 32 blocks (row tile I, column half H) that hold nonzeros are stored, 1 KB each, in the
+// order (0,0) (1,0) (2,0) (2,1) (3,0) (3,1); within a block, 16 rows of four 16-byte units with
+// unit u of row r at u ^ ((r >> 2) & 3), which makes fragment reads (16 rows at one unit per
+// cycle) conflict-free.  The scan keeps all eight blocks in LDS (block 2 I + H), the two upper
+// ones zero.
+__device__ __forceinline__ int tri_blk(int I, int H) { return I < 2 ? I : 2 * I - 2 + H; }
+__device__ __forceinline__ int tri_in(int r, int col) {  // half offset of (r % 16, col % 32) in a block
+  return ((r & 15) * 4 + (((col >> 3) & 3) ^ ((r >> 2) & 3))) * 8 + (col & 7);
+}
+// half offset of element (t, col) in the six-block packet layout (the block must be stored)
+__device__ __forceinline__ int tri_pos(int t, int col) { return tri_blk(t >> 4, col >> 5) * 512 + tri_in(t, col); }
 
 // gate-vector slots (floats)
 constexpr int GV_BETA = 0;                            // [64]
@@ -343,8 +359,13 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
   auto write_t = [&](int64_t blk) {
     _Float16* wsc = reinterpret_cast<_Float16*>(ws + blk * PK::bytes + PK::mat);
     const int t = tid >> 2, c0 = (tid & 3) * 16;
-    *reinterpret_cast<uint4*>(wsc + swz<8>(t, c0)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0);
-    *reinterpret_cast<uint4*>(wsc + swz<8>(t, c0 + 8)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0 + 8);
+    if constexpr (GEN) {
+      *reinterpret_cast<uint4*>(wsc + swz<8>(t, c0)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0);
+      *reinterpret_cast<uint4*>(wsc + swz<8>(t, c0 + 8)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0 + 8);
+    } else if (c0 < 32 || t >= 32) {  // the blocks that hold nonzeros
+      *reinterpret_cast<uint4*>(wsc + tri_pos(t, c0)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0);
+      *reinterpret_cast<uint4*>(wsc + tri_pos(t, c0 + 8)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0 + 8);
+    }
   };
 
   // Per-channel decay with general gates keeps no chunk in flight (its registers would spill);
@@ -503,7 +524,8 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
         half4v hv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) hv[r] = (_Float16)((strict ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f);
-        *reinterpret_cast<half4v*>(wsc + which * (C * C) + swz<8>(t, i0)) = hv;
+        if constexpr (GEN) *reinterpret_cast<half4v*>(wsc + which * (C * C) + swz<8>(t, i0)) = hv;
+        else *reinterpret_cast<half4v*>(wsc + which * (PK::matb / 2) + tri_pos(t, i0)) = hv;
       }
     };
     constexpr int NG = 10 * NM;
@@ -517,13 +539,19 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
       const int idx = G0 + wave + 4 * n;
       if (idx < NG) gram_tile(idx);
     }
-    // upper-triangular 16 x 16 tiles of the workspace matrices after T are zero
-    for (int n = wave; n < 6 * (NM - 1); n += 4) {
-      const int m = 1 + n / 6, u = n % 6;
-      const int I0 = u < 3 ? 0 : u < 5 ? 1 : 2;           // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-      const int J0 = u < 3 ? 1 + u : u < 5 ? u - 1 : 3;
-      const half4v z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
-      *reinterpret_cast<half4v*>(wsc + m * (C * C) + swz<8>(16 * I0 + l16, 16 * J0 + 4 * lg)) = z;
+    // upper-triangular 16 x 16 tiles of the workspace matrices after T are zero (symmetric
+    // gates store only the two, (0,1) and (2,3), that share a block with nonzeros)
+    const half4v z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+    if constexpr (GEN) {
+      for (int n = wave; n < 6 * (NM - 1); n += 4) {
+        const int m = 1 + n / 6, u = n % 6;
+        const int I0 = u < 3 ? 0 : u < 5 ? 1 : 2;           // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+        const int J0 = u < 3 ? 1 + u : u < 5 ? u - 1 : 3;
+        *reinterpret_cast<half4v*>(wsc + m * (C * C) + swz<8>(16 * I0 + l16, 16 * J0 + 4 * lg)) = z;
+      }
+    } else if (wave < 2) {
+      const int I0 = 2 * wave, J0 = I0 + 1;
+      *reinterpret_cast<half4v*>(wsc + PK::matb / 2 + tri_pos(16 * I0 + l16, 16 * J0 + 4 * lg)) = z;
     }
     // operand tiles for the scan (per-channel decay or general gates): K+, Q+ row-major;
     // K-, U- transposed ([channel][token]); all swizzled
@@ -624,6 +652,12 @@ constexpr int kScanThreads = 64 * kScanWaves;
 template <int U>
 __device__ __forceinline__ half8 frag_s(const _Float16* base, int row0, int k0, int lane) {
   return *reinterpret_cast<const half8*>(base + swz<U>(row0 + (lane & 15), k0 + 8 * (lane >> 4)));
+}
+
+// Fragment (as frag()) of rows 16 I .. + 15, columns 32 H .. + 31 of a lower-triangular matrix
+// held in LDS as eight 16 x 32 blocks (block 2 I + H, layout as tri_in).
+__device__ __forceinline__ half8 frag_tri(const _Float16* base, int I, int H, int lane) {
+  return *reinterpret_cast<const half8*>(base + (2 * I + H) * 512 + tri_in(lane & 15, 8 * (lane >> 4)));
 }
 
 // LDS layout of the register-staged scan (general gates).
@@ -1053,8 +1087,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   // Two buffer sets of copy targets, each split into one array per copy batch: the compiler
   // tracks copies into LDS per array, so reading one array never waits for the copies into
   // another.  Batch 1 (bytes): K+ (scalar decay: k) [64][128], Q+ (q) [64][128], gate vector
-  // [512] f32, v slice [64][DVS] (bf16); batch 2: T [64][64], A_qk [64][64]; batch 3: K-^T
-  // [128][64] (per-channel decay).
+  // [ngate] f32, v slice [64][DVS] (bf16); batch 2: T [64][64], A_qk [64][64] (eight 16 x 32
+  // blocks each, see tri_pos); batch 3: K-^T [128][64] (per-channel decay).
   constexpr int o_kp = 0, o_qp = o_kp + C * D * 2, o_gv = o_qp + C * D * 2;
   constexpr int o_vs = o_gv + PK::ngate * 4, b1_bytes = o_vs + C * DVS * 2;
   constexpr int o_th = 0, o_aq = o_th + C * C * 2, b2_bytes = o_aq + C * C * 2;
@@ -1121,13 +1155,22 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
 
   auto tok = [&](int t) { return (int64_t(b) * T + t) * H + h; };
   const int64_t tstride = int64_t(C) * H * D;  // elements between chunk c and c + 1
-  // value-slice unit of this thread (threads < 64 VU): token tid / VU, columns 8 (tid % VU) ..
-  // The slice sits in LDS row-major with 16-byte unit u of row r at u ^ vs_key(r), so that the
-  // transposing reads (8 rows per 32 lanes) are conflict-free (with 64-byte rows, rows r and
-  // r + 4 share banks otherwise); this thread's copy lands at unit tid % VU of row vt, so it
-  // fetches the unit stored there.
+  // Besides two K+ and two Q+ copies, every wave issues one more 1 KB copy of batch 1, so that
+  // all waves issue the same number and the partial waits are exact: wave w < ngv copies gate
+  // block w, the next nvs waves the value slice, the rest gate block 0 again (same bytes, same
+  // place).
+  constexpr int ngv = PK::ngate * 4 / 1024, nvs = C * VU / 64;
+  static_assert(ngv + nvs <= kScanWaves, "one extra copy per wave");
+  const bool x_vs = wave >= ngv && wave < ngv + nvs;
+  const int x_off = x_vs ? o_vs + 1024 * (wave - ngv) : o_gv + 1024 * (wave < ngv ? wave : 0);
+  // value-slice unit of this thread (waves ngv .. ngv + nvs - 1): unit vu = 64 (wave - ngv) +
+  // lane, token vu / VU, columns 8 (vu % VU) ..  The slice sits in LDS row-major with 16-byte
+  // unit u of row r at u ^ vs_key(r), so that the transposing reads (8 rows per 32 lanes) are
+  // conflict-free (with 64-byte rows, rows r and r + 4 share banks otherwise); this thread's
+  // copy lands at unit vu % VU of row vt, so it fetches the unit stored there.
   auto vs_key = [](int r) { return VU == 4 ? ((r >> 2) & 1) << 1 : 0; };
-  const int vt = tid / VU, vc = 8 * ((tid % VU) ^ vs_key(vt));
+  const int vu = (64 * (wave - ngv) + lane) & (C * VU - 1);
+  const int vt = vu / VU, vc = 8 * ((vu % VU) ^ vs_key(vt));
   const int64_t v_off = tok(vt) * D + j0 + vc;
   const int64_t v_last = tok(T - 1) * D + j0 + vc;  // stands in for tokens past the end
   const int64_t o_off = tok(16 * (wave & 3) + l16) * D + j0 + 4 * lg;
@@ -1140,23 +1183,24 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   // Issued in three batches, each as early as its buffers are free and each waited for just
   // before its first reader: (1) key/query tiles, gate vector, values and factors, read from
   // the start of the chunk; (2) T and A_qk, read from the D stage on; (3) K-^T (per-channel
-  // decay), read by the state update.  Every copy of batches 2 and 3 is issued by every lane
-  // (past the last chunk it repeats the last chunk into the idle set), so the number of loads
-  // a wave issues after each batch is known and a partial vmcnt wait suffices.
+  // decay), read by the state update.  Every wave issues the same number of loads in each
+  // batch that a wait has to look past (past the last chunk the copies repeat the last chunk
+  // into the idle set), so the number of loads a wave issues after each batch is known and a
+  // partial vmcnt wait suffices.
   auto fetch1 = [&](const Set& X, Fac& F, int c) {
     const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
-    const int ub = 16 * tid;     // this lane's byte within a 8 KB block
-    const int wb = 1024 * wave;  // this wave's LDS byte within a 8 KB block
+    const int ub = 16 * tid;     // this lane's byte within an 8 KB block
+    const int wb = 1024 * wave;  // this wave's LDS byte within an 8 KB block
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       dma16(pk + PK::kp + ub + 8192 * i, reinterpret_cast<char*>(X.kp) + wb + 8192 * i);
       dma16(pk + PK::qp + ub + 8192 * i, reinterpret_cast<char*>(X.qp) + wb + 8192 * i);
     }
-    if (wave < PK::ngate * 4 / 1024) dma16(pk + PK::gate + ub, reinterpret_cast<char*>(X.gv) + wb);
-    if (tid < C * VU) {
+    {
       const bool ok = c * C + vt < T;
       const int64_t e = ok ? v_off + c * tstride : v_last;
-      dma16(vin + 2 * e, reinterpret_cast<char*>(X.vs) + wb);
+      const gptr<const char> src = x_vs ? vin + 2 * e : pk + PK::gate + (x_off - o_gv) + 16 * lane;
+      dma16(src, reinterpret_cast<char*>(X.kp) + x_off);
     }
     // the factors are loaded unconditionally (a conditional load would need a register copy,
     // and with it an immediate wait)
@@ -1175,12 +1219,22 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       F.fcm[0] = cc.x; F.fcm[1] = cc.y; F.fcm[2] = cc.z; F.fcm[3] = cc.w;
     }
   };
-  // copies per lane of batches 2 and 3, and a lower bound for batch 1
-  constexpr int kB1min = 4, kB2 = 2, kB3 = SCAL ? 0 : 2;
+  // loads per lane of batches 1 (five copies and the factor loads) and 3; batch 2 (below) has
+  // a lower bound for the scalar decay, whose only wait past it is for batch 1 of the same chunk
+  constexpr int kB1 = 5 + (SCAL ? 1 : 3), kB2min = SCAL ? 1 : 2, kB3 = SCAL ? 0 : 2;
+  // The twelve stored blocks of T and A_qk, 1 KB each: copy s (s = wave, and s = 8 + wave % 4
+  // on waves 0-3, and with a per-channel decay also on waves 4-7, which repeat a copy so that
+  // the count is exact for the wait on batch 3) takes stored block s % 6 of matrix s / 6 to LDS
+  // block 2 I + H.
   auto fetch2 = [&](const Set& X, int c) {
     const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
-    dma16(pk + PK::mat + 16 * tid, reinterpret_cast<char*>(X.th) + 1024 * wave);
-    dma16(pk + PK::mat + C * C * 2 + 16 * tid, reinterpret_cast<char*>(X.aq) + 1024 * wave);
+    auto copy = [&](int sl) {
+      const int m = sl >= 6 ? 1 : 0, k = sl - 6 * m;
+      const int lb = k < 2 ? 2 * k : k + 2;
+      dma16(pk + PK::mat + 1024 * sl + 16 * lane, reinterpret_cast<char*>(X.th) + 8192 * m + 1024 * lb);
+    };
+    copy(wave);
+    if (!SCAL || wave < 4) copy(8 + (wave & 3));
   };
   auto fetch3 = [&](const Set& X, int c) {
     if constexpr (!SCAL) {
@@ -1206,7 +1260,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     constexpr bool B1 = decltype(one)::value;
     const Set X = set_of(Flag<B1>()), Y = set_of(Flag<!B1>());
     const int cn = c + 1 < nchunks ? c + 1 : c;  // chunk whose copies this step issues
-    vm_wait<kB2 + kB3>();  // batch 1 of this chunk and the stores of the one before
+    vm_wait<kB2min + kB3>();  // batch 1 of this chunk and the stores of the one before
     if (c > 0 && xq_wave) store_out(c - 1, false);
     float em[4], fC[4], fCm[4];
 #pragma unroll
@@ -1290,7 +1344,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
         }
       }
     }
-    vm_wait<kB3 + kB1min>();  // batch 2 of this chunk
+    vm_wait<kB3 + kB1>();  // batch 2 of this chunk
     lds_barrier();
     fetch2(Y, cn);
 
@@ -1303,7 +1357,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       half8 ta[2], rb[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        ta[ks] = frag_s<8>(X.th, 16 * i, 32 * ks, lane);
+        ta[ks] = frag_tri(X.th, i, ks, lane);
         rb[ks] = frag_s<8>(RT, 16 * ct, 32 * ks, lane);
       }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1323,7 +1377,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
         *reinterpret_cast<half4v*>(DT2 + swz<8>(16 * ct + l16, 16 * i + 4 * lg)) = hv;
       }
     }
-    if constexpr (!SCAL) vm_wait<kB1min + kB2>();  // batch 3 of this chunk
+    if constexpr (!SCAL) vm_wait<kB1 + kB2min>();  // batch 3 of this chunk
     lds_barrier();
     fetch3(Y, cn);
 
@@ -1334,7 +1388,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       half8 qa[2], db[NCT][2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        qa[ks] = frag_s<8>(X.aq, 16 * i, 32 * ks, lane);
+        qa[ks] = frag_tri(X.aq, i, ks, lane);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) db[ct][ks] = frag_s<8>(DT, 16 * ct, 32 * ks, lane);
       }
@@ -1372,6 +1426,14 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     // this step's second barrier, and its copies go out only after its own first barrier.
   };
 
+  // The upper blocks (0,1) and (1,1) of T and A_qk, in both buffer sets, are zero and never
+  // copied; written before the first copy, so that no write waits for one.
+  if (tid < 256) {
+    const int zb = o_th + 8192 * ((tid >> 6) & 1) + 1024 * (1 + 2 * (tid >> 7)) + 16 * lane;
+    const uint4 zz = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(B2S0 + zb) = zz;
+    *reinterpret_cast<uint4*>(B2S1 + zb) = zz;
+  }
   fetch1(set_of(Flag<false>()), F, 0);
   fetch2(set_of(Flag<false>()), 0);
   fetch3(set_of(Flag<false>()), 0);
