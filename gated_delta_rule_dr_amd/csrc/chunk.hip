@@ -1187,21 +1187,24 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   // batch that a wait has to look past (past the last chunk the copies repeat the last chunk
   // into the idle set), so the number of loads a wave issues after each batch is known and a
   // partial vmcnt wait suffices.
-  auto fetch1 = [&](const Set& X, Fac& F, int c) {
+  // part 0: the K+ copies and the extra copy, right after the first barrier; part 1: the Q+
+  // copies and the factors, after the X stage's products (spreading the copies over the stage
+  // measured faster than issuing them together); part 2: all of it
+  auto fetch1 = [&](const Set& X, Fac& F, int c, int part) {
     const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
     const int ub = 16 * tid;     // this lane's byte within an 8 KB block
     const int wb = 1024 * wave;  // this wave's LDS byte within an 8 KB block
+    if (part != 1) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      dma16(pk + PK::kp + ub + 8192 * i, reinterpret_cast<char*>(X.kp) + wb + 8192 * i);
-      dma16(pk + PK::qp + ub + 8192 * i, reinterpret_cast<char*>(X.qp) + wb + 8192 * i);
-    }
-    {
+      for (int i = 0; i < 2; ++i) dma16(pk + PK::kp + ub + 8192 * i, reinterpret_cast<char*>(X.kp) + wb + 8192 * i);
       const bool ok = c * C + vt < T;
       const int64_t e = ok ? v_off + c * tstride : v_last;
       const gptr<const char> src = x_vs ? vin + 2 * e : pk + PK::gate + (x_off - o_gv) + 16 * lane;
       dma16(src, reinterpret_cast<char*>(X.kp) + x_off);
     }
+    if (part == 0) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(pk + PK::qp + ub + 8192 * i, reinterpret_cast<char*>(X.qp) + wb + 8192 * i);
     // the factors are loaded unconditionally (a conditional load would need a register copy,
     // and with it an immediate wait)
     const gptr<const float> gv = (gptr<const float>)(pk + PK::gate);
@@ -1278,7 +1281,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       *reinterpret_cast<half4v*>(ST + swz<16>(16 * ct + l16, 16 * wave + 4 * lg)) = hv;
     }
     lds_barrier();  // every wave's batch 1 of this chunk has landed; S~^T is complete
-    fetch1(Y, F, cn);
+    fetch1(Y, F, cn, 0);
 
     // ---- X = [K+; Q+] S~: waves 0-3 X_K rows [16 w, +16); waves 4-7 X_Q rows, transposed --
     f32x4 XR[NCT];
@@ -1332,6 +1335,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
         }
         XR[ct] = acc;
       }
+      __builtin_amdgcn_sched_barrier(0);  // keeps the second part after the products
+      fetch1(Y, F, cn, 1);
       if (!xq_wave) {
         // R = Diag(beta) (V - X_K), stored transposed
         const float beta[4] = {bt.x, bt.y, bt.z, bt.w};
@@ -1434,7 +1439,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     *reinterpret_cast<uint4*>(B2S0 + zb) = zz;
     *reinterpret_cast<uint4*>(B2S1 + zb) = zz;
   }
-  fetch1(set_of(Flag<false>()), F, 0);
+  fetch1(set_of(Flag<false>()), F, 0, 2);
   fetch2(set_of(Flag<false>()), 0);
   fetch3(set_of(Flag<false>()), 0);
   int c = 0;
