@@ -1086,13 +1086,16 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   constexpr int VU = DVS / 8;    // 16-byte units per value-slice row
   // Two buffer sets of copy targets, each split into one array per copy batch: the compiler
   // tracks copies into LDS per array, so reading one array never waits for the copies into
-  // another.  Batch 1 (bytes): K+ (scalar decay: k) [64][128], Q+ (q) [64][128], gate vector
-  // [ngate] f32, v slice [64][DVS] (bf16); batch 2: T [64][64], A_qk [64][64] (eight 16 x 32
-  // blocks each, see tri_pos); batch 3: K-^T [128][64] (per-channel decay).
-  constexpr int o_kp = 0, o_qp = o_kp + C * D * 2, o_gv = o_qp + C * D * 2;
+  // another.  Batch 1a (bytes): K+ (scalar decay: k) [64][128]; batch 1b: Q+ (q) [64][128],
+  // gate vector [ngate] f32, v slice [64][DVS] (bf16); batch 2: T [64][64], A_qk [64][64]
+  // (eight 16 x 32 blocks each, see tri_pos); batch 3: K-^T [128][64] (per-channel decay).
+  constexpr int b1a_bytes = C * D * 2;
+  constexpr int o_qp = 0, o_gv = o_qp + C * D * 2;
   constexpr int o_vs = o_gv + PK::ngate * 4, b1_bytes = o_vs + C * DVS * 2;
   constexpr int o_th = 0, o_aq = o_th + C * C * 2, b2_bytes = o_aq + C * C * 2;
   constexpr int b3_bytes = SCAL ? 16 : D * C * 2;
+  __shared__ __attribute__((aligned(16))) char B1aS0[b1a_bytes];
+  __shared__ __attribute__((aligned(16))) char B1aS1[b1a_bytes];
   __shared__ __attribute__((aligned(16))) char B1S0[b1_bytes];
   __shared__ __attribute__((aligned(16))) char B1S1[b1_bytes];
   __shared__ __attribute__((aligned(16))) char B2S0[b2_bytes];
@@ -1121,7 +1124,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     char* b1 = B1 ? B1S1 : B1S0;
     char* b2 = B1 ? B2S1 : B2S0;
     Set x;
-    x.kp = reinterpret_cast<_Float16*>(b1 + o_kp);
+    x.kp = reinterpret_cast<_Float16*>(B1 ? B1aS1 : B1aS0);
     x.qp = reinterpret_cast<_Float16*>(b1 + o_qp);
     x.gv = reinterpret_cast<float*>(b1 + o_gv);
     x.vs = reinterpret_cast<uint16_t*>(b1 + o_vs);
@@ -1173,7 +1176,11 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   const int vt = vu / VU, vc = 8 * ((vu % VU) ^ vs_key(vt));
   const int64_t v_off = tok(vt) * D + j0 + vc;
   const int64_t v_last = tok(T - 1) * D + j0 + vc;  // stands in for tokens past the end
-  const int64_t o_off = tok(16 * (wave & 3) + l16) * D + j0 + 4 * lg;
+  // Work split of the X and O stages.  With two value tiles (NCT == 2) wave w takes token rows
+  // 16 (w % 4) and value tile w / 4 of both X_K (for R) and X_Q (for O), so every wave does the
+  // same work; with one (NCT == 1) waves 0-3 take the X_K rows and waves 4-7 the X_Q rows.
+  const int xct = NCT == 2 ? wave >> 2 : 0;
+  const int64_t o_off = tok(16 * (wave & 3) + l16) * D + j0 + 16 * xct + 4 * lg;
 
   // Copies of chunk c's packet and value slice into buffer set X, plus the per-row decay
   // factors of this thread's state rows into registers.
@@ -1187,24 +1194,34 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   // batch that a wait has to look past (past the last chunk the copies repeat the last chunk
   // into the idle set), so the number of loads a wave issues after each batch is known and a
   // partial vmcnt wait suffices.
-  // part 0: the K+ copies and the extra copy, right after the first barrier; part 1: the Q+
-  // copies and the factors, after the X stage's products (spreading the copies over the stage
-  // measured faster than issuing them together); part 2: all of it
-  auto fetch1 = [&](const Set& X, Fac& F, int c, int part) {
+  // Batch 1 goes out in parts: the K+ tile (read by the state update to the end of the chunk)
+  // and the factors one chunk ahead, after the first barrier; the Q+ tile and the extra copy,
+  // whose buffers are last read before the third barrier, with a per-head decay two chunks
+  // ahead, right after that barrier, into the set of the chunk being processed; with a
+  // per-channel decay the extra copy goes with K+ and the Q+ tile after the X stage's products
+  // (each measured faster for its variant).
+  constexpr bool kEarly = SCAL;
+  auto fetch_q = [&](const Set& X, int c) {
     const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
-    const int ub = 16 * tid;     // this lane's byte within an 8 KB block
-    const int wb = 1024 * wave;  // this wave's LDS byte within an 8 KB block
-    if (part != 1) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) dma16(pk + PK::kp + ub + 8192 * i, reinterpret_cast<char*>(X.kp) + wb + 8192 * i);
-      const bool ok = c * C + vt < T;
-      const int64_t e = ok ? v_off + c * tstride : v_last;
-      const gptr<const char> src = x_vs ? vin + 2 * e : pk + PK::gate + (x_off - o_gv) + 16 * lane;
-      dma16(src, reinterpret_cast<char*>(X.kp) + x_off);
-    }
-    if (part == 0) return;
+    for (int i = 0; i < 2; ++i)
+      dma16(pk + PK::qp + 16 * tid + 8192 * i, reinterpret_cast<char*>(X.qp) + 1024 * wave + 8192 * i);
+  };
+  auto fetch_x = [&](const Set& X, int c) {
+    const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
+    const bool ok = c * C + vt < T;
+    const int64_t e = ok ? v_off + c * tstride : v_last;
+    const gptr<const char> src = x_vs ? vin + 2 * e : pk + PK::gate + (x_off - o_gv) + 16 * lane;
+    dma16(src, reinterpret_cast<char*>(X.qp) + x_off);
+  };
+  auto fetch_k = [&](const Set& X, int c) {
+    const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(pk + PK::qp + ub + 8192 * i, reinterpret_cast<char*>(X.qp) + wb + 8192 * i);
+    for (int i = 0; i < 2; ++i)
+      dma16(pk + PK::kp + 16 * tid + 8192 * i, reinterpret_cast<char*>(X.kp) + 1024 * wave + 8192 * i);
+  };
+  auto load_f = [&](Fac& F, int c) {
+    const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
     // the factors are loaded unconditionally (a conditional load would need a register copy,
     // and with it an immediate wait)
     const gptr<const float> gv = (gptr<const float>)(pk + PK::gate);
@@ -1222,9 +1239,24 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       F.fcm[0] = cc.x; F.fcm[1] = cc.y; F.fcm[2] = cc.z; F.fcm[3] = cc.w;
     }
   };
-  // loads per lane of batches 1 (five copies and the factor loads) and 3; batch 2 (below) has
-  // a lower bound for the scalar decay, whose only wait past it is for batch 1 of the same chunk
-  constexpr int kB1 = 5 + (SCAL ? 1 : 3), kB2min = SCAL ? 1 : 2, kB3 = SCAL ? 0 : 2;
+  // the two parts of batch 1, each issued in one place: 1a after the first barrier (K+ with,
+  // for a per-head decay, the factor loads; for a per-channel decay, the extra copy), 1b after
+  // the third barrier (per-head decay: Q+ and the extra copy, two chunks ahead) or after the X
+  // stage's products (per-channel decay: Q+ and the factor loads)
+  auto fetch1a = [&](const Set& X, Fac& F, int c) {
+    fetch_k(X, c);
+    if constexpr (kEarly) load_f(F, c);
+    else fetch_x(X, c);
+  };
+  auto fetch1b = [&](const Set& X, Fac& F, int c) {
+    fetch_q(X, c);
+    if constexpr (kEarly) fetch_x(X, c);
+    else load_f(F, c);
+  };
+  // loads per lane of batches 1a, 1b and 3; batch 2 (below) has a lower bound for the scalar
+  // decay, whose only wait past it is for batch 1a of the same chunk
+  constexpr int kF = SCAL ? 1 : 3;
+  constexpr int kB1a = kEarly ? 2 + kF : 3, kB1b = kEarly ? 3 : 2 + kF, kB2min = SCAL ? 1 : 2, kB3 = SCAL ? 0 : 2;
   // The twelve stored blocks of T and A_qk, 1 KB each: copy s (s = wave, and s = 8 + wave % 4
   // on waves 0-3, and with a per-channel decay also on waves 4-7, which repeat a copy so that
   // the count is exact for the wait on batch 3) takes stored block s % 6 of matrix s / 6 to LDS
@@ -1250,12 +1282,13 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
 
   const int xrow = 16 * (wave & 3);
   const bool xq_wave = wave >= 4;
-  f32x4 OA[NCT];  // output tile of the previous chunk (waves 4-7), stored one chunk later
+  // output tile of the previous chunk (every wave with NCT == 2, waves 4-7 otherwise), stored
+  // one chunk later
+  f32x4 OA;
+  const bool o_wave = NCT == 2 || xq_wave;
   auto store_out = [&](int c, bool masked) {
     const int t = c * C + xrow + l16;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-      if (!masked || t < T) store_o4(p.o, o_off + c * tstride + 16 * ct, OA[ct], p.o_bf16);
+    if (!masked || t < T) store_o4(p.o, o_off + c * tstride, OA, p.o_bf16);
   };
 
   Fac F;
@@ -1263,8 +1296,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     constexpr bool B1 = decltype(one)::value;
     const Set X = set_of(Flag<B1>()), Y = set_of(Flag<!B1>());
     const int cn = c + 1 < nchunks ? c + 1 : c;  // chunk whose copies this step issues
-    vm_wait<kB2min + kB3>();  // batch 1 of this chunk and the stores of the one before
-    if (c > 0 && xq_wave) store_out(c - 1, false);
+    vm_wait<kB2min + kB3 + (kEarly ? kB1b : 0)>();  // batch 1 of this chunk, older stores
+    if (c > 0 && o_wave) store_out(c - 1, false);
     float em[4], fC[4], fCm[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1281,19 +1314,67 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       *reinterpret_cast<half4v*>(ST + swz<16>(16 * ct + l16, 16 * wave + 4 * lg)) = hv;
     }
     lds_barrier();  // every wave's batch 1 of this chunk has landed; S~^T is complete
-    fetch1(Y, F, cn, 0);
+    fetch1a(Y, F, cn);
 
-    // ---- X = [K+; Q+] S~: waves 0-3 X_K rows [16 w, +16); waves 4-7 X_Q rows, transposed --
-    f32x4 XR[NCT];
-    {
-      // an index, not a choice between two pointers: LDS reads keep their array's alias scope
-      // only through address arithmetic, and without it every read waits for the copies
-      const _Float16* Xa = X.kp + (xq_wave ? (o_qp - o_kp) / 2 : 0);
+    // ---- X = [K+; Q+] S~ ------------------------------------------------------------------
+    f32x4 XQ;  // X_Q^T tile of this wave's O rows (scaled), the start of O
+    if constexpr (NCT == 2) {
+      // Every LDS operand of the stage is read before the first product, so that the reads'
+      // latencies overlap instead of adding up.  One S~ fragment set serves both products (A
+      // and B fragments share their lane layout).
+      half8 kf[4], qf[4], sf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        kf[ks] = frag_s<16>(X.kp, xrow, 32 * ks, lane);
+        qf[ks] = frag_s<16>(X.qp, xrow, 32 * ks, lane);
+        sf[ks] = frag_s<16>(ST, 16 * xct, 32 * ks, lane);
+      }
+      // gates of rows xrow + 4 lg + r (X_K's layout) and of row xrow + l16 (X_Q^T's layout);
+      // four consecutive floats in one read: a single address keeps the read's alias scope
+      const float4 bt = *reinterpret_cast<const float4*>(X.gv + GV_BETA + xrow + 4 * lg);
+      float4 fk = make_float4(1.f, 1.f, 1.f, 1.f);
+      float fq = 1.f;
+      if constexpr (SCAL) {
+        fk = *reinterpret_cast<const float4*>(X.gv + GV_FP + xrow + 4 * lg);
+        fq = X.gv[GV_FP + xrow + l16];
+      }
+      // v[xrow + 4 lg + r][16 xct + l16], r = 0..3, in one transposing read: lane 16 g + m
+      // supplies row xrow + 4 g + m / 4, columns 16 xct + 4 (m % 4) .. + 3
+      const int vr_row = xrow + 4 * lg + (l16 >> 2), vr_unit = 2 * xct + ((l16 & 3) >> 1);
+      const short4v vr = ld_tr16(X.vs + vr_row * DVS + 8 * (vr_unit ^ vs_key(vr_row)) + 4 * (l16 & 1));
+      f32x4 xk = {0.f, 0.f, 0.f, 0.f}, xq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        xk = mfma16x16x32(kf[ks], sf[ks], xk);  // rows: tokens xrow + 4 lg + r
+        xq = mfma16x16x32(sf[ks], qf[ks], xq);  // transposed: token xrow + l16 is the column
+      }
+      if constexpr (!kEarly) {
+        __builtin_amdgcn_sched_barrier(0);  // keeps the copies after the products
+        fetch1b(Y, F, cn);
+      }
+
+      const float beta[4] = {bt.x, bt.y, bt.z, bt.w}, fkr[4] = {fk.x, fk.y, fk.z, fk.w};
+      half4v hv;  // R = Diag(beta) (V - X_K), stored transposed
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = SCAL ? xk[r] * fkr[r] : xk[r];
+        hv[r] = (_Float16)(beta[r] * (bf16_to_f32(uint16_t(vr[r])) - x));
+        XQ[r] = SCAL ? xq[r] * fq : xq[r];
+      }
+      *reinterpret_cast<half4v*>(RT + swz<8>(16 * xct + l16, xrow + 4 * lg)) = hv;
+    } else {
+      f32x4 XR[NCT];
       // Every LDS operand of the stage is read, by every wave, before the first product, so
       // that the reads' latencies overlap instead of adding up.
       half8 af[4], bsv[NCT][4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) af[ks] = frag_s<16>(Xa, xrow, 32 * ks, lane);
+      for (int ks = 0; ks < 4; ++ks) {
+        // two reads and a choice of values, not a choice of pointers: LDS reads keep their
+        // array's alias scope only through address arithmetic on one array, and without it every
+        // read waits for the copies
+        const half8 fk8 = frag_s<16>(X.kp, xrow, 32 * ks, lane), fq8 = frag_s<16>(X.qp, xrow, 32 * ks, lane);
+        af[ks] = xq_wave ? fq8 : fk8;
+      }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -1335,8 +1416,11 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
         }
         XR[ct] = acc;
       }
-      __builtin_amdgcn_sched_barrier(0);  // keeps the second part after the products
-      fetch1(Y, F, cn, 1);
+      if constexpr (!kEarly) {
+        __builtin_amdgcn_sched_barrier(0);  // keeps the copies after the products
+        fetch1b(Y, F, cn);
+      }
+
       if (!xq_wave) {
         // R = Diag(beta) (V - X_K), stored transposed
         const float beta[4] = {bt.x, bt.y, bt.z, bt.w};
@@ -1348,8 +1432,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
           *reinterpret_cast<half4v*>(RT + swz<8>(16 * ct + l16, xrow + 4 * lg)) = hv;
         }
       }
+      XQ = XR[0];
     }
-    vm_wait<kB3 + kB1>();  // batch 2 of this chunk
+    vm_wait<kB3 + kB1b + kB1a>();  // batch 2 of this chunk
     lds_barrier();
     fetch2(Y, cn);
 
@@ -1382,28 +1467,25 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
         *reinterpret_cast<half4v*>(DT2 + swz<8>(16 * ct + l16, 16 * i + 4 * lg)) = hv;
       }
     }
-    if constexpr (!SCAL) vm_wait<kB1 + kB2min>();  // batch 3 of this chunk
+    if constexpr (!SCAL) vm_wait<kB1b + kB1a + kB2min>();  // batch 3 of this chunk
     lds_barrier();
     fetch3(Y, cn);
+    if constexpr (kEarly) fetch1b(X, F, c + 2 < nchunks ? c + 2 : nchunks - 1);  // c + 2 uses set X
 
-    // ---- O: chunk output rows [16 (w - 4), +16), waves 4-7 (stored with the next chunk) -----
-    if (xq_wave) {
+    // ---- O: rows xrow .. + 15, value tile xct (stored with the next chunk) -----------------
+    if (o_wave) {
       const int i = wave & 3;
       // A_qk has zero upper tiles in the packet: both halves, no branch
-      half8 qa[2], db[NCT][2];
+      half8 qa[2], db[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         qa[ks] = frag_tri(X.aq, i, ks, lane);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) db[ct][ks] = frag_s<8>(DT, 16 * ct, 32 * ks, lane);
+        db[ks] = frag_s<8>(DT, 16 * xct, 32 * ks, lane);
       }
+      f32x4 acc = XQ;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        f32x4 acc = XR[ct];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) acc = mfma16x16x32(db[ct][ks], qa[ks], acc);
-        OA[ct] = acc;
-      }
+      for (int ks = 0; ks < 2; ++ks) acc = mfma16x16x32(db[ks], qa[ks], acc);
+      OA = acc;
     }
 
     // ---- S: state update for this wave's rows ---------------------------------------------
@@ -1439,9 +1521,12 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     *reinterpret_cast<uint4*>(B2S0 + zb) = zz;
     *reinterpret_cast<uint4*>(B2S1 + zb) = zz;
   }
-  fetch1(set_of(Flag<false>()), F, 0, 2);
+  if constexpr (kEarly) fetch1b(set_of(Flag<false>()), F, 0);
+  fetch1a(set_of(Flag<false>()), F, 0);
+  if constexpr (!kEarly) fetch1b(set_of(Flag<false>()), F, 0);
   fetch2(set_of(Flag<false>()), 0);
   fetch3(set_of(Flag<false>()), 0);
+  if constexpr (kEarly) fetch1b(set_of(Flag<true>()), F, nchunks > 1 ? 1 : 0);
   int c = 0;
   for (; c + 1 < nchunks; c += 2) {
     step(c, Flag<false>());
@@ -1449,7 +1534,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   }
   if (c < nchunks) step(c, Flag<false>());
   vm_wait_all();
-  if (xq_wave) store_out(nchunks - 1, true);
+  if (o_wave) store_out(nchunks - 1, true);
 
   if (p.S_T) {
 #pragma unroll
