@@ -1290,6 +1290,24 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     const int t = c * C + xrow + l16;
     if (!masked || t < T) store_o4(p.o, o_off + c * tstride, OA, p.o_bf16);
   };
+  // With a per-head decay at 32-column slices the O tiles go out through LDS, so that each
+  // store writes whole 128-byte rows (eight lanes per token) instead of two 64-byte halves from
+  // two waves: the o stores cost the chunk less (a probe without them ran 12% faster).  Staged
+  // O: [64 tokens][32 columns] fp32, 16-byte unit u of row t at u ^ (t % 8).  Wave w stores
+  // tokens 8 w .. + 7; lane l token 8 w + l / 8, columns 4 (l % 8) .. + 3.
+  constexpr bool kStage = SCAL && NCT == 2;
+  __shared__ __attribute__((aligned(16))) float OS[kStage ? C * DVS : 4];
+  const int s_t = 8 * wave + (lane >> 3), s_u = lane & 7;
+  const int64_t s_off = tok(s_t) * D + j0 + 4 * s_u;
+  // The row pieces are read from LDS after the first barrier and stored one chunk later, at the
+  // start of the next step like the direct stores (a store issued after the chunk's factor loads
+  // makes the compiler wait for all loads at the top of every chunk), alternating two registers
+  // so that a piece is not overwritten right after its store.
+  f32x4 SV[2];
+  auto read_staged = [&](int k) { SV[k] = *reinterpret_cast<const f32x4*>(OS + s_t * DVS + 4 * (s_u ^ (s_t & 7))); };
+  auto store_staged = [&](int k, int c, bool masked) {
+    if (!masked || c * C + s_t < T) store_o4(p.o, s_off + c * tstride, SV[k], p.o_bf16);
+  };
 
   Fac F;
   auto step = [&](int c, auto one) {
@@ -1297,7 +1315,11 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     const Set X = set_of(Flag<B1>()), Y = set_of(Flag<!B1>());
     const int cn = c + 1 < nchunks ? c + 1 : c;  // chunk whose copies this step issues
     vm_wait<kB2min + kB3 + (kEarly ? kB1b : 0)>();  // batch 1 of this chunk, older stores
-    if (c > 0 && o_wave) store_out(c - 1, false);
+    if constexpr (!kStage) {
+      if (c > 0 && o_wave) store_out(c - 1, false);
+    } else {
+      if (c > 1) store_staged(B1 ? 1 : 0, c - 2, false);  // read into SV[c % 2] two steps ago
+    }
     float em[4], fC[4], fCm[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1314,6 +1336,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       *reinterpret_cast<half4v*>(ST + swz<16>(16 * ct + l16, 16 * wave + 4 * lg)) = hv;
     }
     lds_barrier();  // every wave's batch 1 of this chunk has landed; S~^T is complete
+    if constexpr (kStage) {
+      if (c > 0) read_staged(B1 ? 0 : 1);  // chunk c - 1 into SV[(c - 1) % 2]
+    }
     fetch1a(Y, F, cn);
 
     // ---- X = [K+; Q+] S~ ------------------------------------------------------------------
@@ -1486,6 +1511,10 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) acc = mfma16x16x32(db[ks], qa[ks], acc);
       OA = acc;
+      if constexpr (kStage) {
+        const int t = xrow + l16, u = 4 * xct + lg;
+        *reinterpret_cast<f32x4*>(OS + t * DVS + 4 * (u ^ (t & 7))) = acc;
+      }
     }
 
     // ---- S: state update for this wave's rows ---------------------------------------------
@@ -1534,7 +1563,15 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   }
   if (c < nchunks) step(c, Flag<false>());
   vm_wait_all();
-  if (o_wave) store_out(nchunks - 1, true);
+  if constexpr (kStage) {
+    // chunk nchunks - 2 was read in the last step; chunk nchunks - 1 is still in LDS
+    if (nchunks > 1) store_staged(nchunks & 1, nchunks - 2, false);
+    lds_barrier();
+    read_staged((nchunks - 1) & 1);
+    store_staged((nchunks - 1) & 1, nchunks - 1, true);
+  } else {
+    if (o_wave) store_out(nchunks - 1, true);
+  }
 
   if (p.S_T) {
 #pragma unroll
