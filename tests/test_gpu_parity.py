@@ -101,6 +101,28 @@ def test_chunk_path_slice_widths(dr, B, H, T, variant):
     assert eo <= TOL_BF16 and eS <= TOL_BF16, (eo, eS)
 
 
+@pytest.mark.parametrize("T", [50, 150, 257])
+@pytest.mark.parametrize("variant", ["scalar", "kda"])
+def test_chunk_path_wide_slices_chunk_counts(dr, T, variant):
+    # 32-column slices (B*H >= 64) over one, three and five chunks: the copies issued one and two
+    # chunks ahead, the first steps and the last, and (per-head decay) the o rows staged in LDS
+    inp = _case(1, T, 64, 128, 128, "bf16", variant, T % 2 == 1, 31 + T)
+    o, S = _run(dr, inp)
+    ro, rS = _oracle(inp)
+    eo, eS = err_o(o, ro), err_S(S, rS)
+    print(f"chunk {variant} H=64 T={T}: err_o={eo:.3e} err_S={eS:.3e}")
+    assert eo <= TOL_BF16 and eS <= TOL_BF16, (eo, eS)
+
+
+def test_bf16_output_wide_slices(dr):
+    # the staged o rows (per-head decay, 32-column slices) written as bf16
+    inp = _case(1, 130, 64, 128, 128, "bf16", "scalar", True, 41)
+    o, S = _run(dr, inp, o_dtype=torch.bfloat16)
+    ro, rS = _oracle(inp)
+    assert o.dtype == torch.bfloat16
+    assert err_o(o.float(), ro) <= TOL_BF16 + 2 ** -8 and err_S(S, rS) <= TOL_BF16
+
+
 def test_chunk_matches_token_kernel(dr):
     # the two GPU paths agree with each other as well as with the oracle
     inp = _case(1, 257, 4, 128, 128, "bf16", "decoupled", True, 23)
