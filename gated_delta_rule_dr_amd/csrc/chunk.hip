@@ -198,9 +198,8 @@ struct Packet {
   static constexpr bool kScal = !DCH && !GEN;
   static constexpr int nmat = GEN ? 4 : 2;
   static constexpr int mat = 0;
-  // bytes per matrix: symmetric gates store the six nonzero 16 x 32 blocks of their lower-
-  // triangular matrices (see tri_pos), general gates the whole swizzled 64 x 64 tile
-  static constexpr int matb = GEN ? C * C * 2 : 6 * 1024;
+  // bytes per matrix: the six nonzero 16 x 32 blocks of the lower-triangular matrices (tri_pos)
+  static constexpr int matb = 6 * 1024;
   static constexpr int kp = mat + nmat * matb;
   static constexpr int qp = kp + C * D * 2;
   static constexpr int kmt = qp + C * D * 2;
@@ -359,10 +358,7 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
   auto write_t = [&](int64_t blk) {
     _Float16* wsc = reinterpret_cast<_Float16*>(ws + blk * PK::bytes + PK::mat);
     const int t = tid >> 2, c0 = (tid & 3) * 16;
-    if constexpr (GEN) {
-      *reinterpret_cast<uint4*>(wsc + swz<8>(t, c0)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0);
-      *reinterpret_cast<uint4*>(wsc + swz<8>(t, c0 + 8)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0 + 8);
-    } else if (c0 < 32 || t >= 32) {  // the blocks that hold nonzeros
+    if (c0 < 32 || t >= 32) {  // the blocks that hold nonzeros
       *reinterpret_cast<uint4*>(wsc + tri_pos(t, c0)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0);
       *reinterpret_cast<uint4*>(wsc + tri_pos(t, c0 + 8)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0 + 8);
     }
@@ -524,8 +520,7 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
         half4v hv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) hv[r] = (_Float16)((strict ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f);
-        if constexpr (GEN) *reinterpret_cast<half4v*>(wsc + which * (C * C) + swz<8>(t, i0)) = hv;
-        else *reinterpret_cast<half4v*>(wsc + which * (PK::matb / 2) + tri_pos(t, i0)) = hv;
+        *reinterpret_cast<half4v*>(wsc + which * (PK::matb / 2) + tri_pos(t, i0)) = hv;
       }
     };
     constexpr int NG = 10 * NM;
@@ -539,19 +534,12 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
       const int idx = G0 + wave + 4 * n;
       if (idx < NG) gram_tile(idx);
     }
-    // upper-triangular 16 x 16 tiles of the workspace matrices after T are zero (symmetric
-    // gates store only the two, (0,1) and (2,3), that share a block with nonzeros)
-    const half4v z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
-    if constexpr (GEN) {
-      for (int n = wave; n < 6 * (NM - 1); n += 4) {
-        const int m = 1 + n / 6, u = n % 6;
-        const int I0 = u < 3 ? 0 : u < 5 ? 1 : 2;           // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-        const int J0 = u < 3 ? 1 + u : u < 5 ? u - 1 : 3;
-        *reinterpret_cast<half4v*>(wsc + m * (C * C) + swz<8>(16 * I0 + l16, 16 * J0 + 4 * lg)) = z;
-      }
-    } else if (wave < 2) {
-      const int I0 = 2 * wave, J0 = I0 + 1;
-      *reinterpret_cast<half4v*>(wsc + PK::matb / 2 + tri_pos(16 * I0 + l16, 16 * J0 + 4 * lg)) = z;
+    // the upper-triangular 16 x 16 tiles (0,1) and (2,3) of the workspace matrices after T share
+    // a stored block with nonzeros and are zero (T's come from TH)
+    for (int n = wave; n < 2 * (NM - 1); n += 4) {
+      const half4v z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+      const int m = 1 + n / 2, I0 = 2 * (n % 2), J0 = I0 + 1;
+      *reinterpret_cast<half4v*>(wsc + m * (PK::matb / 2) + tri_pos(16 * I0 + l16, 16 * J0 + 4 * lg)) = z;
     }
     // operand tiles for the scan (per-channel decay or general gates): K+, Q+ row-major;
     // K-, U- transposed ([channel][token]); all swizzled
@@ -664,13 +652,14 @@ __device__ __forceinline__ half8 frag_tri(const _Float16* base, int I, int H, in
 template <bool GEN, bool SCAL, int DVS>
 struct ScanLayout {
   static_assert(GEN && !SCAL, "the register-staged scan serves general gates");
-  // Every tile in the packet's swizzled layout (see swz_key), so units copy straight across and
-  // fragment reads are conflict-free.
+  // Every tile in the packet's layout (swizzled, see swz_key; the matrices as 16 x 32 blocks, see
+  // tri_pos), so units copy straight across and fragment reads are conflict-free.
   static constexpr int kp = 0;                 // K+       [64][128] half
   static constexpr int qp = kp + C * D * 2;    // Q+       [64][128]
   static constexpr int kmt = qp + C * D * 2;   // K-^T     [128][64]
   static constexpr int umt = kmt + D * C * 2;  // U-^T     [128][64]
   static constexpr int st = umt + D * C * 2;   // S~^T     [DVS][128]
+  // the four lower-triangular matrices: eight 16 x 32 blocks each (see tri_pos), contiguous
   static constexpr int th = st + DVS * D * 2;  // T        [64][64]
   static constexpr int aq = th + C * C * 2;    // A_qk     [64][64]
   static constexpr int akk = aq + C * C * 2;   // A_kk     [64][64]
@@ -782,7 +771,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   const int64_t w_last = tok(T - 1);
 
   struct Pref {
-    uint4 mr[NM];             // this thread's 16 bytes of T, A_qk (, A_kk, A_qu)
+    uint4 mr[NM * 3 / 4];     // this thread's units of the stored blocks of T, A_qk, A_kk, A_qu
     uint4 tl[NTU];            // K+, Q+, K-^T, U-^T units
     float4 sc[3];             // per-channel e^{gm}, e^{gC}, e^{gC-gm} of this thread's 4 rows
     VSlice<DVS> vr;
@@ -806,7 +795,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   auto load_b = [&](Pref& P, int c) {
     const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
 #pragma unroll
-    for (int m = 0; m < NM; ++m) P.mr[m] = ldb16(pk, PK::mat + m * (C * C * 2) + 16 * tid);
+    for (int j = 0; j < NM * 3 / 4; ++j) P.mr[j] = ldb16(pk, PK::mat + 16 * (tid + kScanThreads * j));
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       P.tl[4 + i] = ldb16(pk, PK::kmt + 16 * (tid + kScanThreads * i));
@@ -851,10 +840,13 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       *reinterpret_cast<uint4*>(KMT + 8 * u) = P.tl[4 + i];
       *reinterpret_cast<uint4*>(UMT + 8 * u) = P.tl[6 + i];
     }
-    *reinterpret_cast<uint4*>(TH + 8 * tid) = P.mr[0];
-    *reinterpret_cast<uint4*>(AQ + 8 * tid) = P.mr[1];
-    *reinterpret_cast<uint4*>(AKK + 8 * tid) = P.mr[2];
-    *reinterpret_cast<uint4*>(AQU + 8 * tid) = P.mr[3];
+    // stored block k of matrix m (1 KB each, see tri_pos) to LDS block 2 I + H of that matrix
+#pragma unroll
+    for (int j = 0; j < NM * 3 / 4; ++j) {
+      const int u = tid + kScanThreads * j, m = u / 384, k = (u % 384) / 64;
+      const int lb = k < 2 ? 2 * k : k + 2;
+      *reinterpret_cast<uint4*>(TH + 4096 * m + 512 * lb + 8 * (u % 64)) = P.mr[j];
+    }
     {
       float vf[VPT];
       vslice_f32<DVS>(P.vr, vf);
@@ -924,7 +916,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       half8 ka[2], vb[NCT][2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        ka[ks] = frag_s<8>(AKK, xrow, 32 * ks, lane);
+        ka[ks] = frag_tri(AKK, xrow / 16, ks, lane);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) vb[ct][ks] = frag_s<8>(VT, 16 * ct, 32 * ks, lane);
       }
@@ -950,7 +942,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       half8 ta[2], yb[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        ta[ks] = frag_s<8>(TH, 16 * i, 32 * ks, lane);
+        ta[ks] = frag_tri(TH, i, ks, lane);
         yb[ks] = frag_s<8>(RT, 16 * ct, 32 * ks, lane);
       }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -973,8 +965,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       half8 bq[2], bu[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        bq[ks] = frag_s<8>(AQ, 16 * i, 32 * ks, lane);
-        bu[ks] = frag_s<8>(AQU, 16 * i, 32 * ks, lane);
+        bq[ks] = frag_tri(AQ, i, ks, lane);
+        bu[ks] = frag_tri(AQU, i, ks, lane);
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -1030,6 +1022,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
     load_b(P, c);
     load_c(P, c);
   };
+  // the upper blocks (0,1) and (1,1) of the four matrices are zero and never copied
+  *reinterpret_cast<uint4*>(TH + 4096 * (tid >> 7) + 512 * (1 + 2 * ((tid >> 6) & 1)) + 8 * lane) =
+      make_uint4(0, 0, 0, 0);
   Pref PA;
   load(PA, 0);
   int c = 0;

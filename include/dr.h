@@ -93,12 +93,12 @@ const char* dr_status_str(int status);
 /* Bytes of device workspace dr_chunk_fwd needs for `desc` (0 when none), or 0 for an invalid
  * descriptor.  The matrix-core path stores, per 64-token chunk of every (b, h), one packet of
  * the chunk's state-independent factors: the triangular-solve factor and the in-chunk
- * decay-weighted Gram matrices (fp16 64 x 64; with one per-head erase/write gate only their six
- * nonzero 16 x 32 blocks), the gate factors, and the fp16 key/query tiles (decayed, plus the
- * transposed decayed keys, unless the decay is per head with one per-head gate for erase and
- * write).  That is B * H * ceil(T / 64) * P bytes with P = 46080 (per-head decay, one per-head
- * erase/write gate), 63488 (per-channel decay, one per-head erase/write gate) or 100352
- * (otherwise); the token-by-token path needs none.  The caller allocates it
+ * decay-weighted Gram matrices (lower-triangular fp16 64 x 64, only their six nonzero 16 x 32
+ * blocks), the gate factors, and the fp16 key/query tiles (decayed, plus the transposed decayed
+ * keys, unless the decay is per head with one per-head gate for erase and write).  That is
+ * B * H * ceil(T / 64) * P bytes with P = 46080 (per-head decay, one per-head erase/write gate),
+ * 63488 (per-channel decay, one per-head erase/write gate) or 92160 (otherwise); the
+ * token-by-token path needs none.  The caller allocates it
  * (any device memory, 16-byte aligned, not overlapping the other arguments) and may reuse it
  * once the call's work has finished. */
 size_t dr_chunk_fwd_workspace_bytes(const dr_desc* desc);

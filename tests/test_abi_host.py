@@ -124,12 +124,12 @@ def test_aliasing():
 
 def test_workspace_query_and_errors():
     L = _abi.lib()
-    # matrix-core path: one packet per chunk of every (b, h) -- fp16 64 x 64 matrices (2 or 4;
-    # with symmetric gates only their six nonzero 16 x 32 blocks), fp16 operand tiles, fp32
-    # gate vector (256 floats for a per-head decay with symmetric gates, else 512)
+    # matrix-core path: one packet per chunk of every (b, h) -- the six nonzero 16 x 32 blocks of
+    # each lower-triangular fp16 64 x 64 matrix (2 or 4), fp16 operand tiles, fp32 gate vector
+    # (256 floats for a per-head decay with symmetric gates, else 512)
     scal = 2 * 6 * 16 * 32 * 2 + 2 * 64 * 128 * 2 + 256 * 4
     kda = 2 * 6 * 16 * 32 * 2 + 3 * 64 * 128 * 2 + 512 * 4
-    gen = 4 * 64 * 64 * 2 + 4 * 64 * 128 * 2 + 512 * 4
+    gen = 4 * 6 * 16 * 32 * 2 + 4 * 64 * 128 * 2 + 512 * 4
     assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc())) == 2 * 4 * 2 * scal
     assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(T=64))) == 2 * 4 * 1 * scal
     ch = _good_desc(decay_kind=_abi.DR_GATE_CHANNEL)
