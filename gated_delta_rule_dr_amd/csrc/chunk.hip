@@ -68,16 +68,6 @@ __device__ __forceinline__ half8 frag(const _Float16* base, int stride, int row0
   return *reinterpret_cast<const half8*>(base + (row0 + (lane & 15)) * stride + k0 + 8 * (lane >> 4));
 }
 
-// A-operand fragment of the transposed tile: rows are channels d (contiguous in the row-major
-// [t][d] tile), contraction over tokens t.
-__device__ __forceinline__ half8 frag_t(const _Float16* base, int d0, int t0, int lane) {
-  half8 a;
-  const _Float16* p = base + (t0 + 8 * (lane >> 4)) * KS + d0 + (lane & 15);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = p[i * KS];
-  return a;
-}
-
 __device__ __forceinline__ f32x4 mfma16(half4v a, half4v b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
@@ -97,14 +87,6 @@ __device__ __forceinline__ void bf16x8_to_f32(uint4 u, float* f) {
 }
 
 __device__ __forceinline__ float clamped_exp(float x) { return __expf(fminf(x, kExpClamp)); }
-
-__device__ __forceinline__ float4 ld4(const float* p, bool ok) {
-  return ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
-__device__ __forceinline__ float4 gld4(gptr<const float> p, int64_t i, bool ok) {
-  return ok ? gload_f4(p, i) : make_float4(0.f, 0.f, 0.f, 0.f);
-}
 
 __device__ __forceinline__ void unpack8(float4 a, float4 b, float* f) {
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
@@ -319,7 +301,7 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
     float lds, gb;
   };
   auto tok_of = [&](int64_t blk) {
-    const int bh = int(blk / nchunks), c = int(blk - int64_t(bh) * nchunks);
+    const int bh = int(blk / nchunks);
     const int b = bh / H, h = bh - b * H;
     return [=](int t) { return (int64_t(b) * T + (t < T ? t : T - 1)) * H + h; };
   };
