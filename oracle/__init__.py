@@ -8,8 +8,10 @@ Parity pins (see ``tests/test_oracle_pins.py``): brute-force causal linear atten
 gated-linear-attention closed form, exact memory with unit keys, the per-step key-readback
 identity, a hand-worked 2x2 example, the explicit matrix forms of the scalar, KDA and
 FG2-GDN updates, the gradient-step reading of the delta rule, linearity, state resume, the
-norm bound and the dk = dv = 1 closed form.  No function here is "parity unpinned".
+norm bound and the dk = dv = 1 closed form; for packed sequences, equality with the dense
+batch at equal lengths, isolation between sequences, empty sequences, split invariance (the
+prefill-to-decode handoff) and the one-token closed form.  No function here is "parity unpinned".
 """
-from .recurrence import as_f64, decode_step, recurrence
+from .recurrence import as_f64, decode_step, recurrence, recurrence_varlen
 
-__all__ = ["recurrence", "decode_step", "as_f64"]
+__all__ = ["recurrence", "recurrence_varlen", "decode_step", "as_f64"]

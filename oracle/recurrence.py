@@ -41,7 +41,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["recurrence", "decode_step", "as_f64"]
+__all__ = ["recurrence", "recurrence_varlen", "decode_step", "as_f64"]
 
 
 def as_f64(x):
@@ -138,3 +138,56 @@ def decode_step(q, k, v, log_decay, erase, write, S):
 
     o, S_new = recurrence(tok(q), tok(k), tok(v), tok(log_decay), tok(erase), tok(write), S)
     return o[:, 0], S_new
+
+
+def recurrence_varlen(q, k, v, log_decay, erase, write=None, S0=None, cu_seqlens=None):
+    """The recurrence over a packed batch of independent sequences of different lengths.
+
+    Each sequence keeps its own fixed-size state, started from its own initial state, and no
+    state crosses from one sequence to the next: linear attention replaces the growing cache
+    of each sequence by one fixed-size memory, which is what lets a server hold one state per
+    conversation and decode it in constant memory ("Gated DeltaNet-2: decoupling erase and
+    write in linear attention", sections "The attention bottleneck" and "Why this matters";
+    "KronLSTM ...", section "The problem").  Packing the sequences one after another on the
+    token axis, delimited by offsets, is a layout convention that the pages do not describe.
+
+    Args:
+      q, k: [1, T, H, dk] and v: [1, T, H, dv], the sequences concatenated on the token axis;
+        gates [1, T, H] or [1, T, H, d] likewise (``write=None``: the erase gate).
+      cu_seqlens: N + 1 offsets, cu_seqlens[0] == 0, nondecreasing, cu_seqlens[N] == T;
+        sequence n holds tokens cu_seqlens[n] .. cu_seqlens[n + 1] - 1 (it may be empty).
+      S0: [N, H, dk, dv] initial states, or ``None`` for zeros.
+
+    Returns:
+      (o [1, T, H, dv], S_T [N, H, dk, dv]) as float64; an empty sequence has S_T[n] = S0[n].
+    """
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    log_decay, erase, write, S0 = as_f64(log_decay), as_f64(erase), as_f64(write), as_f64(S0)
+    cu = np.asarray(cu_seqlens if not hasattr(cu_seqlens, "detach") else cu_seqlens.cpu().numpy())
+    cu = cu.astype(np.int64)
+    if q.ndim != 4 or q.shape[0] != 1:
+        raise ValueError("packed inputs have a leading batch dimension of 1")
+    _, T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = len(cu) - 1
+    if N < 0 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must start at 0, end at T and never decrease")
+    if S0 is not None and S0.shape != (N, H, dk, dv):
+        raise ValueError(f"S0 must be [N,H,dk,dv]={N, H, dk, dv}, got {S0.shape}")
+
+    def part(x, lo, hi):
+        return None if x is None else x[:, lo:hi]
+
+    o = np.zeros((1, T, H, dv))
+    S_T = np.empty((N, H, dk, dv))
+    for n in range(N):
+        lo, hi = int(cu[n]), int(cu[n + 1])
+        s0 = None if S0 is None else S0[n : n + 1]
+        if hi == lo:
+            S_T[n] = 0.0 if S0 is None else S0[n]
+            continue
+        o_n, S_n = recurrence(part(q, lo, hi), part(k, lo, hi), part(v, lo, hi),
+                              part(log_decay, lo, hi), part(erase, lo, hi), part(write, lo, hi), s0)
+        o[:, lo:hi] = o_n
+        S_T[n] = S_n[0]
+    return o, S_T

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from chunk_model import chunk_forward
-from oracle import decode_step, recurrence
+from oracle import decode_step, recurrence, recurrence_varlen
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -351,3 +351,114 @@ def test_pins_catch_planted_mistakes():
     _, S = recurrence(wrap(q), wrap(k), wrap(v), wrap(np.log(a)), wrap(beta), None, None)
     assert np.allclose(S[0, 0], S_true, atol=1e-12)
     assert not np.allclose(S[0, 0], S_wrong_order, atol=1e-6)
+
+
+# ---- packed sequences of different lengths -------------------------------------------------
+# Each sequence is its own recurrence from its own initial state ("Gated DeltaNet-2 ...", the
+# attention bottleneck: one fixed-size state per sequence, constant-memory decoding).
+
+
+def _packed(seed, lens, H=2, dk=5, dv=4, decay="channel", erase="channel", write="channel", s0=True):
+    q, k, v, ld, e, w, _ = _inputs(seed, B=1, T=int(sum(lens)), H=H, dk=dk, dv=dv, decay=decay,
+                                   erase=erase, write=write, s0=False)
+    S0 = _rng(seed + 1000).standard_normal((len(lens), H, dk, dv)) if s0 else None
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return q, k, v, ld, e, w, S0, cu
+
+
+# V1 -- equal lengths: the packed batch is the dense batch [N, L] reshaped.
+@pytest.mark.parametrize("write", ["channel", None])
+def test_varlen_equal_lengths_is_dense_batch(write):
+    N, L = 3, 7
+    q, k, v, ld, e, w, S0, cu = _packed(21, [L] * N, erase="channel" if write else "head", write=write)
+    o, S = recurrence_varlen(q, k, v, ld, e, w, S0, cu)
+    dense = lambda x: None if x is None else x.reshape((N, L) + x.shape[2:])
+    od, Sd = recurrence(dense(q), dense(k), dense(v), dense(ld), dense(e), dense(w), S0)
+    assert np.allclose(o.reshape(od.shape), od, rtol=0, atol=1e-13)
+    assert np.allclose(S, Sd, rtol=0, atol=1e-13)
+
+
+# V2 -- isolation: changing every input of one sequence leaves the others' outputs and states
+# exactly as they were, and that sequence alone equals the single-sequence recurrence.
+def test_varlen_sequences_are_isolated():
+    lens = [4, 9, 1, 6]
+    q, k, v, ld, e, w, S0, cu = _packed(22, lens)
+    o, S = recurrence_varlen(q, k, v, ld, e, w, S0, cu)
+    lo, hi = cu[1], cu[2]
+    q2, v2 = q.copy(), v.copy()
+    q2[:, lo:hi] += 1.0
+    v2[:, lo:hi] *= -3.0
+    S02 = S0.copy()
+    S02[1] += 5.0
+    o2, S2 = recurrence_varlen(q2, k, v2, ld, e, w, S02, cu)
+    keep = np.ones(q.shape[1], bool)
+    keep[lo:hi] = False
+    assert np.array_equal(o2[:, keep], o[:, keep])
+    assert np.array_equal(S2[[0, 2, 3]], S[[0, 2, 3]])
+    assert not np.allclose(o2[:, lo:hi], o[:, lo:hi])
+    cut = lambda x: x[:, lo:hi]
+    o1, S1 = recurrence(cut(q2), cut(k), cut(v2), cut(ld), cut(e), cut(w), S02[1:2])
+    assert np.array_equal(o2[:, lo:hi], o1) and np.array_equal(S2[1], S1[0])
+
+
+# V3 -- empty sequences (at the start, in the middle, at the end) pass their initial state
+# through unchanged (zeros without one) and do not shift their neighbours' tokens.
+@pytest.mark.parametrize("s0", [True, False])
+def test_varlen_empty_sequences(s0):
+    lens = [0, 5, 0, 0, 3, 0]
+    q, k, v, ld, e, w, S0, cu = _packed(23, lens, s0=s0)
+    o, S = recurrence_varlen(q, k, v, ld, e, w, S0, cu)
+    for n in (0, 2, 3, 5):
+        assert np.array_equal(S[n], S0[n] if s0 else np.zeros_like(S[n]))
+    nz = [1, 4]
+    o_ref, S_ref = recurrence_varlen(q, k, v, ld, e, w, None if S0 is None else S0[nz],
+                                     np.array([0, 5, 8], np.int32))
+    assert np.array_equal(o, o_ref) and np.array_equal(S[nz], S_ref)
+
+
+# V4 -- split invariance, the prefill-to-decode handoff: one sequence cut into two packed
+# sequences, the second started from the first one's final state, gives the uncut outputs;
+# decode steps continued from a packed prefill's states equal the longer prefill.
+def test_varlen_split_and_decode_handoff():
+    q, k, v, ld, e, w, S0, _ = _packed(24, [10], H=2)
+    o, S = recurrence_varlen(q, k, v, ld, e, w, S0, np.array([0, 10], np.int32))
+    oa, Sa = recurrence_varlen(q[:, :6], k[:, :6], v[:, :6], ld[:, :6], e[:, :6], w[:, :6], S0,
+                               np.array([0, 6], np.int32))
+    ob, Sb = recurrence_varlen(q[:, 6:], k[:, 6:], v[:, 6:], ld[:, 6:], e[:, 6:], w[:, 6:], Sa,
+                               np.array([0, 4], np.int32))
+    assert np.array_equal(np.concatenate([oa, ob], axis=1), o) and np.array_equal(Sb, S)
+    # two sequences: prefill 4 and 7 tokens, then decode 3 more of each
+    lens, extra = [4, 7], 3
+    qs, ks, vs, lds, es, ws, S0s, _ = _packed(25, [sum(lens) + 2 * extra], H=2)
+    S0s = _rng(26).standard_normal((2, 2, 5, 4))
+    seqs = [(0, 4 + extra), (4 + extra, 4 + extra + 7 + extra)]
+    take = lambda x, lo, hi: x[:, lo:hi]
+    pre = np.concatenate([np.arange(lo, lo + L) for (lo, _), L in zip(seqs, lens)])
+    cu = np.array([0, lens[0], sum(lens)], np.int32)
+    _, Sp = recurrence_varlen(*(x[:, pre] for x in (qs, ks, vs, lds, es, ws)), S0s, cu)
+    for j in range(extra):
+        idx = [lo + L + j for (lo, _), L in zip(seqs, lens)]
+        od, Sp = decode_step(*(x[0, idx] for x in (qs, ks, vs, lds, es, ws)), Sp)
+        for n, (lo, hi) in enumerate(seqs):
+            o_full, _ = recurrence(*(take(x, lo, lo + lens[n] + j + 1) for x in (qs, ks, vs, lds, es, ws)),
+                                   S0s[n:n + 1])
+            assert np.allclose(od[n], o_full[0, -1], rtol=0, atol=1e-12)
+
+
+# V5 -- one-token sequences from a zero state, closed form: S = k (w * v)^T and
+# o = (q . k) (w * v), each from its own token only.
+def test_varlen_one_token_closed_form():
+    lens = [1, 1, 1]
+    q, k, v, ld, e, w, _, cu = _packed(27, lens, s0=False)
+    o, S = recurrence_varlen(q, k, v, ld, e, w, None, cu)
+    for n in range(3):
+        kn, qn, vw = k[0, n], q[0, n], w[0, n] * v[0, n]  # [H, d]
+        assert np.allclose(S[n], kn[:, :, None] * vw[:, None, :], rtol=0, atol=1e-14)
+        assert np.allclose(o[0, n], np.sum(qn * kn, -1)[:, None] * vw, rtol=0, atol=1e-14)
+
+
+def test_varlen_rejects_bad_offsets():
+    q, k, v, ld, e, w, S0, cu = _packed(28, [3, 2])
+    for bad in ([0, 3], [1, 3, 5], [0, 4, 3]):
+        with pytest.raises(ValueError):
+            recurrence_varlen(q, k, v, ld, e, w, None, np.array(bad, np.int32))
