@@ -1,7 +1,8 @@
 """Gated delta-rule recurrence on MI355X (gfx950): Python binding of libdr.
 
-``chunk_fwd`` is the prefill / training forward and ``decode_step`` the single-token update;
-both call the C ABI (include/dr.h) on torch's current HIP stream.  Tensors must live on the
+``chunk_fwd`` is the prefill / training forward, ``chunk_fwd_varlen`` the same over a packed
+batch of sequences of different lengths, and ``decode_step`` the single-token update; all call
+the C ABI (include/dr.h) on torch's current HIP stream.  Tensors must live on the
 GPU and be contiguous; the functions only check and marshal arguments, allocate outputs with
 torch and pass raw device pointers.  No step of the recurrence runs in Python, and there is
 no CPU fallback: without the built library every call raises.
@@ -19,7 +20,8 @@ import torch
 
 from . import _abi
 
-__all__ = ["chunk_fwd", "decode_step", "workspace_bytes", "abi_version", "DrError"]
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "decode_step", "workspace_bytes", "varlen_workspace_bytes",
+           "abi_version", "DrError"]
 
 DrError = _abi.DrError
 
@@ -118,6 +120,63 @@ def chunk_fwd(q, k, v, log_decay, erase, write=None, S0=None, *, chunk=64,
         _ptr(write), _ptr(S0), _ptr(out), _ptr(S_T), _ptr(ws), ws_n, _stream(),
     )
     _abi.check("dr_chunk_fwd", st)
+    return out, S_T
+
+
+def varlen_workspace_bytes(desc, nseq) -> int:
+    return int(_abi.lib().dr_chunk_fwd_varlen_workspace_bytes(ctypes.byref(desc), int(nseq)))
+
+
+def chunk_fwd_varlen(q, k, v, log_decay, erase, write=None, S0=None, *, cu_seqlens, chunk=64,
+                     o_dtype=torch.float32, out=None, S_T=None, return_state=True, workspace=None):
+    """Chunked forward over N packed sequences of different lengths, each from its own state.
+
+    q, k: [1, T, H, dk]; v: [1, T, H, dv] with the sequences one after another on the token
+    axis; gates [1, T, H] or [1, T, H, d]; cu_seqlens: int32 [N + 1] on the GPU (sequence n is
+    tokens cu_seqlens[n] .. cu_seqlens[n + 1] - 1); S0: None or [N, H, dk, dv] fp32.
+    Returns (o [1, T, H, dv], S_T [N, H, dk, dv] or None); S_T is the state layout of
+    ``decode_step``.  ``workspace`` may supply a uint8 buffer of at least
+    ``varlen_workspace_bytes`` bytes."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, (torch.float32, torch.bfloat16), dev)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if q.dim() != 4 or q.shape[0] != 1 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [1, T, H, dk] and v [1, T, H, dv]")
+    _check_tensor("cu_seqlens", cu_seqlens, (torch.int32,), dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-d int32 tensor of N + 1 offsets")
+    N = cu_seqlens.numel() - 1
+    _, T, H, dk = q.shape
+    dv = v.shape[3]
+    for name, t in (("log_decay", log_decay), ("erase", erase), ("write", write), ("S0", S0)):
+        if t is not None:
+            _check_tensor(name, t, (torch.float32,), dev)
+    if S0 is not None and tuple(S0.shape) != (N, H, dk, dv):
+        raise ValueError(f"S0 must be [N, H, dk, dv] = {(N, H, dk, dv)}")
+    desc = _desc(1, T, H, dk, dv, chunk, q.dtype, o_dtype, log_decay, erase, write, (1, T, H))
+    if out is None:
+        out = torch.empty((1, T, H, dv), dtype=o_dtype, device=dev)
+    else:
+        _check_tensor("out", out, (o_dtype,), dev)
+    if S_T is None and return_state:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _check_tensor("S_T", S_T, (torch.float32,), dev)
+        if tuple(S_T.shape) != (N, H, dk, dv):
+            raise ValueError(f"S_T must be [N, H, dk, dv] = {(N, H, dk, dv)}")
+    ws_n = varlen_workspace_bytes(desc, N) if N > 0 and T > 0 else 0
+    if workspace is None:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    elif workspace.numel() < ws_n:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, {ws_n} needed")
+    st = _abi.lib().dr_chunk_fwd_varlen(
+        ctypes.byref(desc), _ptr(cu_seqlens), N, _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay),
+        _ptr(erase), _ptr(write), _ptr(S0), _ptr(out), _ptr(S_T), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream(),
+    )
+    _abi.check("dr_chunk_fwd_varlen", st)
     return out, S_T
 
 

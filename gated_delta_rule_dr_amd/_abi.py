@@ -30,6 +30,8 @@ EXPORTS = (
     "dr_status_str",
     "dr_chunk_fwd_workspace_bytes",
     "dr_chunk_fwd",
+    "dr_chunk_fwd_varlen_workspace_bytes",
+    "dr_chunk_fwd_varlen",
     "dr_decode_step",
 )
 
@@ -72,6 +74,10 @@ def lib() -> ctypes.CDLL:
     L.dr_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(DrDesc)]
     L.dr_chunk_fwd.restype = ctypes.c_int
     L.dr_chunk_fwd.argtypes = [ctypes.POINTER(DrDesc)] + [vp] * 10 + [sz, vp]
+    L.dr_chunk_fwd_varlen_workspace_bytes.restype = sz
+    L.dr_chunk_fwd_varlen_workspace_bytes.argtypes = [ctypes.POINTER(DrDesc), ctypes.c_int32]
+    L.dr_chunk_fwd_varlen.restype = ctypes.c_int
+    L.dr_chunk_fwd_varlen.argtypes = [ctypes.POINTER(DrDesc), vp, ctypes.c_int32] + [vp] * 10 + [sz, vp]
     L.dr_decode_step.restype = ctypes.c_int
     L.dr_decode_step.argtypes = [ctypes.POINTER(DrDesc)] + [vp] * 9
     _lib = L

@@ -257,11 +257,56 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 0xf) | (0x7 << 4) | (0xf << 8) | ((N >> 4) << 14));
 }
 
+// One chunk of prep work: the row of its first token on the token axis ([B * T] for a dense
+// batch, the packed axis otherwise), its tokens (1 .. C), its head and its packet index.
+struct ChunkRef {
+  int64_t tok0;
+  int tlen, h;
+  int64_t pkt;
+};
+
+// The sequence of a scan workgroup (bh = sequence * H + h): the row of its first token, its
+// tokens and chunks, and the packet index of its first chunk for head h.  A dense batch stores
+// the packets of (b, h) one after another; packed sequences take their place from the table.
+struct SeqRef {
+  int64_t tok0;
+  int len, nch;
+  int64_t pkt0;
+};
+__device__ __forceinline__ SeqRef seq_ref(const Problem& p, int bh, int h) {
+  SeqRef r;
+  if (p.seqs) {
+    const int4 e = p.seqs[bh / p.H];
+    r.tok0 = e.x;
+    r.len = e.y;
+    r.nch = e.w;
+    r.pkt0 = int64_t(e.z) + int64_t(h) * e.w;
+  } else {
+    r.nch = (p.T + C - 1) / C;
+    r.tok0 = int64_t(bh / p.H) * p.T;
+    r.len = p.T;
+    r.pkt0 = int64_t(bh) * r.nch;
+  }
+  return r;
+}
+
+// A sequence without tokens: S_T = S0 (zeros without S0) on this workgroup's value columns.
+__device__ void pass_state(const Problem& p, int bh, int j0, int ncols) {
+  if (!p.S_T) return;
+  for (int i = threadIdx.x; i < D * ncols; i += blockDim.x) {
+    const int d = i / ncols, j = j0 + i % ncols;
+    const int64_t x = (int64_t(bh) * D + d) * D + j;
+    p.S_T[x] = p.S0 ? p.S0[x] : 0.f;
+  }
+}
+
 // Per-channel decay or general gates: held to two waves per SIMD (the input prefetch would
 // otherwise take the registers of the second resident workgroup).
 template <bool DCH, bool GEN>
 __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_kernel(Problem p, char* __restrict__ ws,
                                                                                      int nchunks, int64_t nblk) {
+  // Packed sequences: the work items are (chunk, head) pairs over the chunk table.
+  if (p.chunks) nblk = int64_t(p.H) * *p.nchunks_total;
   using PK = Packet<DCH, GEN>;
   constexpr int NM = PK::nmat;
   __shared__ __attribute__((aligned(16))) _Float16 KP[C * KS];                 // K+
@@ -300,35 +345,53 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
     float err[kPrefetchErr ? 4 : 1][kPrefetchErr ? 8 : 1];
     float lds, gb;
   };
-  auto tok_of = [&](int64_t blk) {
-    const int bh = int(blk / nchunks);
-    const int b = bh / H, h = bh - b * H;
-    return [=](int t) { return (int64_t(b) * T + (t < T ? t : T - 1)) * H + h; };
+  // Work item blk: a dense batch walks (b, h, chunk) with packet index blk; packed sequences
+  // walk (chunk, head) over the chunk table.
+  auto chunk_ref = [&](int64_t blk) {
+    ChunkRef r;
+    if (p.chunks) {
+      const int64_t g = blk / H;
+      r.h = int(blk - g * H);
+      const int4 e = p.chunks[g];
+      r.tok0 = e.x;
+      r.tlen = e.y;
+      r.pkt = int64_t(e.z) + int64_t(r.h) * e.w;
+    } else {
+      const int bh = int(blk / nchunks), c = int(blk - int64_t(bh) * nchunks);
+      const int b = bh / H;
+      r.h = bh - b * H;
+      r.tok0 = int64_t(b) * T + int64_t(c) * C;
+      r.tlen = T - c * C < C ? T - c * C : C;
+      r.pkt = blk;
+    }
+    return r;
   };
-  auto load_err = [&](float (&e)[4][8], int64_t blk) {
-    const int c = int(blk - (blk / nchunks) * nchunks);
-    const auto tok = tok_of(blk);
+  auto tok_of = [&](const ChunkRef& cr) {
+    return [=](int t) { return (cr.tok0 + (t < cr.tlen ? t : cr.tlen - 1)) * H + cr.h; };
+  };
+  auto load_err = [&](float (&e)[4][8], const ChunkRef& cr) {
+    const auto tok = tok_of(cr);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t base = tok(c * C + 4 * tg + r) * D + 8 * d8;
+      const int64_t base = tok(4 * tg + r) * D + 8 * d8;
       unpack8(gload_f4(erin, base), gload_f4(erin, base + 4), e[r]);
     }
   };
   auto load_in = [&](In& I, int64_t blk) {
-    const int c = int(blk - (blk / nchunks) * nchunks);
-    const auto tok = tok_of(blk);
+    const ChunkRef cr = chunk_ref(blk);
+    const auto tok = tok_of(cr);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t base = tok(c * C + 4 * tg + r) * D + 8 * d8;
+      const int64_t base = tok(4 * tg + r) * D + 8 * d8;
       I.kr[r] = gload_u4(kin, base);
       I.qr[r] = gload_u4(qin, base);
       if constexpr (DCH) unpack8(gload_f4(ldin, base), gload_f4(ldin, base + 4), I.ldr[r]);
     }
     if constexpr (kPrefetchErr) {
-      if (erase_ch) load_err(I.err, blk);
+      if (erase_ch) load_err(I.err, cr);
     }
     if (tid < C) {
-      const int64_t ti = tok(c * C + tid);
+      const int64_t ti = tok(tid);
       if constexpr (!DCH) I.lds = ldin[ti];
       if (!erase_ch) I.gb = erin[ti];
     }
@@ -337,8 +400,8 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
   // One chunk: prefix sums, operand tiles, gates, Gram matrices, triangular solve.  The solve
   // factor T stays in TH and is written out by the next chunk (or after the last), so that the
   // next chunk's wait for its inputs does not also wait for these stores.
-  auto write_t = [&](int64_t blk) {
-    _Float16* wsc = reinterpret_cast<_Float16*>(ws + blk * PK::bytes + PK::mat);
+  auto write_t = [&](int64_t pkt) {
+    _Float16* wsc = reinterpret_cast<_Float16*>(ws + pkt * PK::bytes + PK::mat);
     const int t = tid >> 2, c0 = (tid & 3) * 16;
     if (c0 < 32 || t >= 32) {  // the blocks that hold nonzeros
       *reinterpret_cast<uint4*>(wsc + tri_pos(t, c0)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0);
@@ -352,10 +415,12 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
   In I;
   int64_t blk = blockIdx.x;
   const int64_t gstride = gridDim.x;
-  if constexpr (kPrefetch) load_in(I, blk);
-  for (int64_t prev = -1; blk < nblk; prev = blk, blk += gstride) {
-    const int c = int(blk - (blk / nchunks) * nchunks);
-    char* pk = ws + blk * PK::bytes;  // this chunk's packet
+  if constexpr (kPrefetch) {
+    if (blk < nblk) load_in(I, blk);
+  }
+  for (int64_t prev = -1; blk < nblk; blk += gstride) {
+    const ChunkRef cr = chunk_ref(blk);
+    char* pk = ws + cr.pkt * PK::bytes;  // this chunk's packet
     _Float16* wsc = reinterpret_cast<_Float16*>(pk + PK::mat);
     float* gv = reinterpret_cast<float*>(pk + PK::gate);
     if constexpr (!kPrefetch) load_in(I, blk);
@@ -367,11 +432,11 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
     float err[GEN ? 4 : 1][GEN ? 8 : 1];
     float en[GEN && !kPrefetchErr ? 4 : 1][GEN && !kPrefetchErr ? 8 : 1];
     if constexpr (GEN && !kPrefetchErr) {
-      if (erase_ch) load_err(en, blk);
+      if (erase_ch) load_err(en, cr);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool ok = c * C + 4 * tg + r < T;
+      const bool ok = 4 * tg + r < cr.tlen;
       const uint4 z = make_uint4(0, 0, 0, 0);
       kr[r] = ok ? I.kr[r] : z;
       qr[r] = ok ? I.qr[r] : z;
@@ -386,7 +451,7 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
     }
     float lds = 0.f;
     if (tid < C) {
-      const bool ok = c * C + tid < T;
+      const bool ok = tid < cr.tlen;
       if constexpr (!DCH) lds = ok ? I.lds : 0.f;
       GB[tid] = (ok && !erase_ch) ? I.gb : 0.f;
     }
@@ -608,7 +673,8 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
       }
       lds_barrier();
     }
-    if (blk + gstride >= nblk) write_t(blk);  // this workgroup's last chunk
+    if (blk + gstride >= nblk) write_t(cr.pkt);  // this workgroup's last chunk
+    prev = cr.pkt;
   }
 }
 
@@ -718,14 +784,19 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int bh = blockIdx.x;
-  const int b = bh / p.H, h = bh - b * p.H;
+  const int H = p.H, h = bh % H;
   const int j0 = blockIdx.y * DVS;
-  const int T = p.T, H = p.H;
-  const int nchunks = (T + C - 1) / C;
+  const SeqRef sq = seq_ref(p, bh, h);
+  const int T = sq.len;  // this sequence's tokens
+  const int nchunks = sq.nch;
+  if (nchunks == 0) {
+    pass_state(p, bh, j0, DVS);
+    return;
+  }
   const int nfull = T / C;  // chunks with C tokens
   const gptr<const uint16_t> vin = opaque_gptr(static_cast<const uint16_t*>(p.v));
   const gptr<const float> wrin = opaque_gptr(p.write);
-  const gptr<const char> pbase = opaque_gptr(ws) + int64_t(bh) * nchunks * PK::bytes;
+  const gptr<const char> pbase = opaque_gptr(ws) + sq.pkt0 * PK::bytes;
 
   // State: wave w owns rows [16 w, 16 w + 16) x the DVS columns as NCT accumulator tiles
   // (lane: column 16 ct + l16, rows 16 w + 4 lg + r).
@@ -741,7 +812,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   // Load mapping.  Packet tiles: 16-byte units tid and tid + 512; matrices: unit tid.  Value
   // slice: token tid / 8, columns VPT (tid % 8) .. + VPT - 1.
   const int vtok = tid >> 3, vcol = (tid & 7) * VPT;
-  auto tok = [&](int t) { return (int64_t(b) * T + t) * H + h; };
+  auto tok = [&](int t) { return (sq.tok0 + t) * H + h; };
   // Per-thread element offsets at chunk 0; chunk c adds c * tstride (tokens are H * D apart).
   const int64_t tstride = int64_t(C) * H * D;
   const int64_t v_off = tok(vtok) * D + j0 + vcol;
@@ -1115,11 +1186,16 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int bh = blockIdx.x;
-  const int b = bh / p.H, h = bh - b * p.H;
+  const int H = p.H, h = bh % H;
   const int j0 = blockIdx.y * DVS;
-  const int T = p.T, H = p.H;
-  const int nchunks = (T + C - 1) / C;
-  const gptr<const char> pbase = opaque_gptr(ws) + int64_t(bh) * nchunks * PK::bytes;
+  const SeqRef sq = seq_ref(p, bh, h);
+  const int T = sq.len;  // this sequence's tokens
+  const int nchunks = sq.nch;
+  if (nchunks == 0) {
+    pass_state(p, bh, j0, DVS);
+    return;
+  }
+  const gptr<const char> pbase = opaque_gptr(ws) + sq.pkt0 * PK::bytes;
   const gptr<const char> vin = opaque_gptr(static_cast<const char*>(p.v));
 
   // State: wave w owns rows [16 w, 16 w + 16) x the DVS columns as NCT accumulator tiles
@@ -1133,7 +1209,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       S[ct][r] = p.S0 ? p.S0[(int64_t(bh) * D + d) * D + j0 + 16 * ct + l16] : 0.f;
     }
 
-  auto tok = [&](int t) { return (int64_t(b) * T + t) * H + h; };
+  auto tok = [&](int t) { return (sq.tok0 + t) * H + h; };
   const int64_t tstride = int64_t(C) * H * D;  // elements between chunk c and c + 1
   // Besides two K+ and two Q+ copies, every wave issues one more 1 KB copy of batch 1, so that
   // all waves issue the same number and the partial waits are exact: wave w < ngv copies gate
@@ -1582,7 +1658,9 @@ template <bool DCH, bool GEN>
 hipError_t launch_variant(const Problem& p, void* workspace, hipStream_t stream) {
   const int nchunks = (p.T + C - 1) / C;
   char* ws = static_cast<char*>(workspace);
-  const int64_t nblk = int64_t(p.B) * p.H * nchunks;
+  // packed sequences: the grid is sized for the most chunks their lengths allow; the kernel
+  // reads the actual count from the table
+  const int64_t nblk = p.chunks ? int64_t(p.H) * varlen_max_chunks(p.B, p.T) : int64_t(p.B) * p.H * nchunks;
   // Persistent: as many workgroups as fit at once (two per compute unit), each walking every
   // grid-th chunk with its next chunk's inputs in flight.
   int dev = 0, ncu = 0;
@@ -1605,14 +1683,40 @@ hipError_t launch_variant(const Problem& p, void* workspace, hipStream_t stream)
   }
 }
 
+int64_t packet_bytes(bool symmetric, bool decay_channel) {
+  return !symmetric ? Packet<true, true>::bytes : decay_channel ? Packet<true, false>::bytes : Packet<false, false>::bytes;
+}
+
+int64_t round256(int64_t n) { return (n + 255) / 256 * 256; }
+
 }  // namespace
 
 size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric, bool decay_channel) {
   const int64_t nchunks = (int64_t(T) + C - 1) / C;
-  const int64_t per = !symmetric      ? Packet<true, true>::bytes
-                      : decay_channel ? Packet<true, false>::bytes
-                                      : Packet<false, false>::bytes;
-  return size_t(int64_t(B) * H * nchunks * per);
+  return size_t(int64_t(B) * H * nchunks * packet_bytes(symmetric, decay_channel));
+}
+
+// Packed sequences: packets of at most varlen_max_chunks chunks per head, then the chunk
+// table, the sequence table and the chunk count.
+size_t chunk128_varlen_workspace_bytes(int nseq, int T, int H, bool symmetric, bool decay_channel) {
+  const int64_t maxc = varlen_max_chunks(nseq, T);
+  return size_t(int64_t(H) * maxc * packet_bytes(symmetric, decay_channel) + round256(maxc * 16) +
+                round256(int64_t(nseq) * 16) + 256);
+}
+
+hipError_t launch_chunk128_varlen(Problem p, const int* cu, void* workspace, hipStream_t stream) {
+  const int64_t maxc = varlen_max_chunks(p.B, p.T);
+  char* ws = static_cast<char*>(workspace);
+  char* tables = ws + int64_t(p.H) * maxc * packet_bytes(p.symmetric, p.decay_channel);
+  int4* chunks = reinterpret_cast<int4*>(tables);
+  int4* seqs = reinterpret_cast<int4*>(tables + round256(maxc * 16));
+  int* total = reinterpret_cast<int*>(tables + round256(maxc * 16) + round256(int64_t(p.B) * 16));
+  hipError_t e = launch_varlen_setup(cu, p.B, p.T, p.H, C, seqs, chunks, total, stream);
+  if (e != hipSuccess) return e;
+  p.seqs = seqs;
+  p.chunks = chunks;
+  p.nchunks_total = total;
+  return launch_chunk128(p, workspace, stream);
 }
 
 hipError_t launch_chunk128(const Problem& p, void* workspace, hipStream_t stream) {

@@ -41,6 +41,8 @@ struct Extents {
 // Element counts are bounded so that every index the kernels form fits in int64 and every
 // per-(b,h) offset fits in int32 arithmetic where the kernels use it.
 constexpr uint64_t kMaxElems = uint64_t(1) << 40;
+// Sequences of one packed batch.
+constexpr int32_t kMaxSeqs = int32_t(1) << 30;
 
 int check_desc(const dr_desc* d, bool decode, Extents* ex) {
   if (d == nullptr) return DR_E_NULL;
@@ -193,6 +195,73 @@ int dr_chunk_fwd(const dr_desc* d, const void* q, const void* k, const void* v,
   dr::Problem p = make_problem(d, q, k, v, log_decay, erase, write, S0, o, S_T);
   if (uses_chunk128(d)) return launched(dr::launch_chunk128(p, workspace, s));
   return launched(dr::launch_recurrent(p, s));
+}
+
+size_t dr_chunk_fwd_varlen_workspace_bytes(const dr_desc* desc, int32_t nseq) {
+  Extents ex;
+  if (check_desc(desc, false, &ex) != DR_OK || desc->B != 1 || nseq <= 0 || nseq > kMaxSeqs) return 0;
+  if (uses_chunk128(desc))
+    return dr::chunk128_varlen_workspace_bytes(nseq, desc->T, desc->H, is_symmetric(desc),
+                                               desc->decay_kind == DR_GATE_CHANNEL);
+  return dr::recurrent_varlen_workspace_bytes(nseq);
+}
+
+int dr_chunk_fwd_varlen(const dr_desc* d, const int32_t* cu_seqlens, int32_t nseq, const void* q,
+                        const void* k, const void* v, const float* log_decay, const float* erase,
+                        const float* write, const float* S0, void* o, float* S_T, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  Extents ex;
+  int st = check_desc(d, false, &ex);
+  if (st != DR_OK) return st;
+  if (d->B != 1 || nseq < 0 || nseq > kMaxSeqs) return DR_E_SHAPE;
+  // the states are [nseq, H, dk, dv]
+  const uint64_t state_elems = uint64_t(nseq) * uint64_t(d->H) * uint64_t(d->dk) * uint64_t(d->dv);
+  if (state_elems > kMaxElems) return DR_E_SHAPE;
+  ex.state = state_elems * 4;
+  const uint64_t cu_bytes = (uint64_t(nseq) + 1) * 4;
+  if (cu_seqlens == nullptr) {
+    if (nseq > 0) return DR_E_NULL;
+  } else if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) {
+    return DR_E_ALIGN;
+  }
+  const bool need_write = !d->write_is_erase;
+  if ((st = check_ptr(q, ex.qk, true)) || (st = check_ptr(k, ex.qk, true)) ||
+      (st = check_ptr(v, ex.v, true)) || (st = check_ptr(log_decay, ex.decay, true)) ||
+      (st = check_ptr(erase, ex.erase, true)) ||
+      (st = check_ptr(need_write ? write : nullptr, ex.write, need_write)) ||
+      (st = check_ptr(S0, ex.state, false)) || (st = check_ptr(o, ex.o, true)) ||
+      (st = check_ptr(S_T, ex.state, false)) || (st = check_ptr(workspace, workspace_bytes, false)))
+    return st;
+  const bool work = nseq > 0 && d->T > 0;
+  if (work && workspace_bytes < dr_chunk_fwd_varlen_workspace_bytes(d, nseq)) return DR_E_WORKSPACE;
+  if (work && workspace == nullptr) return DR_E_WORKSPACE;
+
+  const Range rin[] = {range_of(q, ex.qk),         range_of(k, ex.qk),
+                       range_of(v, ex.v),          range_of(log_decay, ex.decay),
+                       range_of(erase, ex.erase),  range_of(need_write ? write : nullptr, ex.write),
+                       range_of(S0, ex.state),     range_of(cu_seqlens, cu_bytes)};
+  const Range ro = range_of(o, ex.o), rs = range_of(S_T, ex.state);
+  for (const Range& r : rin)
+    if (overlaps(ro, r)) return DR_E_ALIAS;
+  if (overlaps(ro, rs)) return DR_E_ALIAS;
+  for (int i = 0; i < 8; ++i)
+    if (i != 6 && overlaps(rs, rin[i])) return DR_E_ALIAS;
+  if (S0 != nullptr && S_T != nullptr && S0 != S_T && overlaps(rs, rin[6])) return DR_E_ALIAS;
+  const Range rw = range_of(workspace, workspace_bytes);
+  for (const Range& r : rin)
+    if (overlaps(rw, r)) return DR_E_ALIAS;
+  if (overlaps(rw, ro) || overlaps(rw, rs)) return DR_E_ALIAS;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (nseq == 0) return DR_OK;
+  if (d->T == 0) {
+    if (S_T == nullptr || S_T == S0) return DR_OK;
+    return launched(dr::launch_state_copy(S0, S_T, int64_t(ex.state / 4), s));
+  }
+  dr::Problem p = make_problem(d, q, k, v, log_decay, erase, write, S0, o, S_T);
+  p.B = nseq;
+  if (uses_chunk128(d)) return launched(dr::launch_chunk128_varlen(p, cu_seqlens, workspace, s));
+  return launched(dr::launch_recurrent_varlen(p, cu_seqlens, workspace, s));
 }
 
 int dr_decode_step(const dr_desc* d, const void* q, const void* k, const void* v,

@@ -26,7 +26,23 @@ struct Problem {
   const float* S0;     // may be null (zeros)
   void* o;
   float* S_T;          // may be null (skip)
+  // Packed sequences of different lengths: B is then the number of sequences and T the
+  // packed token count, and the kernels take each sequence's tokens from these tables (in the
+  // workspace, written by launch_varlen_setup).  Null for a dense [B, T] batch.
+  const int4* seqs = nullptr;          // [B] {first token, tokens, H * chunks before, chunks}
+  const int4* chunks = nullptr;        // [chunks] {first token, tokens, packet of head 0, chunks
+                                       //  of its sequence}; the packet of head h adds h * chunks
+  const int* nchunks_total = nullptr;  // number of entries in `chunks`
 };
+
+// Sequence tables of a packed batch (one workgroup): from nseq + 1 device offsets `cu` over T
+// packed tokens, clamped into [0, T] and made nondecreasing, writes seqs[nseq], chunks[] (when
+// not null; at most varlen_max_chunks entries) and *total, for chunks of `chunk` tokens.
+hipError_t launch_varlen_setup(const int* cu, int nseq, int T, int H, int chunk, int4* seqs, int4* chunks,
+                               int* total, hipStream_t stream);
+
+// Upper bound on the chunks of nseq sequences with T tokens in all: sum ceil(len / 64).
+inline int64_t varlen_max_chunks(int64_t nseq, int64_t T) { return (T + 63 * nseq) / 64; }
 
 // fp32 token-by-token recurrence: any supported dk/dv/dtypes.  Reads S0 before writing S_T
 // element by element in the same thread, so S0 == S_T is safe.
@@ -40,6 +56,16 @@ hipError_t launch_decode128(const Problem& p, hipStream_t stream);
 // state-independent factors per chunk of every (b, h).
 size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric, bool decay_channel);
 hipError_t launch_chunk128(const Problem& p, void* workspace, hipStream_t stream);
+
+// The same over p.B packed sequences delimited by the device offsets `cu` (p.B + 1 of them):
+// the workspace holds the packets of at most varlen_max_chunks(p.B, p.T) chunks per head,
+// then the sequence tables.
+size_t chunk128_varlen_workspace_bytes(int nseq, int T, int H, bool symmetric, bool decay_channel);
+hipError_t launch_chunk128_varlen(Problem p, const int* cu, void* workspace, hipStream_t stream);
+
+// The token-by-token kernel over packed sequences: the workspace holds the sequence table.
+size_t recurrent_varlen_workspace_bytes(int nseq);
+hipError_t launch_recurrent_varlen(Problem p, const int* cu, void* workspace, hipStream_t stream);
 
 // S_T = S0 (copy) or zeros when S0 is null: n floats.
 hipError_t launch_state_copy(const float* S0, float* S_T, int64_t n, hipStream_t stream);

@@ -6,7 +6,8 @@
 // the key side, write on the value side, channel decay from KDA; "FG2-GDN ...", section 2,
 // update rule).  It serves the fp32 workloads, widths the matrix-core path does not cover,
 // chunk == 1, and decode steps of other widths (in place: every state element is read and
-// written by the same lane).
+// written by the same lane).  Over packed sequences of different lengths each workgroup takes
+// its sequence's first token and length from the sequence table.
 //
 // Mapping: one wave per (b, h, group of 16 value columns).  Lane = column c (16) x row group
 // (4); each lane keeps dk/4 rows of its column in registers, so the two reductions over dk per
@@ -86,8 +87,16 @@ __global__ __launch_bounds__(64) void recurrent_kernel(Problem p) {
 #pragma unroll
   for (int r = 0; r < RPL; ++r) s[r] = p.S0 ? p.S0[sbase + int64_t(row0 + r) * dv] : 0.f;
 
-  for (int t = 0; t < p.T; ++t) {
-    const int64_t tok = (int64_t(b) * p.T + t) * p.H + h;
+  // Token rows of sequence b: a dense batch row, or a packed sequence from the table.
+  int64_t tok0 = int64_t(b) * p.T;
+  int len = p.T;
+  if (p.seqs) {
+    const int4 e = p.seqs[b];
+    tok0 = e.x;
+    len = e.y;
+  }
+  for (int t = 0; t < len; ++t) {
+    const int64_t tok = (tok0 + t) * p.H + h;
     float kr[RPL], qr[RPL], ar[RPL], er[RPL];
     load_rows<RPL>(p.k, tok * DK + row0, bf, kr);
     load_rows<RPL>(p.q, tok * DK + row0, bf, qr);
@@ -149,6 +158,20 @@ hipError_t launch_recurrent(const Problem& p, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+size_t recurrent_varlen_workspace_bytes(int nseq) {
+  return size_t((int64_t(nseq) * 16 + 255) / 256 * 256 + 256);
+}
+
+hipError_t launch_recurrent_varlen(Problem p, const int* cu, void* workspace, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  int4* seqs = reinterpret_cast<int4*>(ws);
+  int* total = reinterpret_cast<int*>(ws + (int64_t(p.B) * 16 + 255) / 256 * 256);
+  hipError_t e = launch_varlen_setup(cu, p.B, p.T, p.H, 64, seqs, nullptr, total, stream);
+  if (e != hipSuccess) return e;
+  p.seqs = seqs;
+  return launch_recurrent(p, stream);
 }
 
 hipError_t launch_state_copy(const float* S0, float* S_T, int64_t n, hipStream_t stream) {

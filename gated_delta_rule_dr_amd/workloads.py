@@ -13,6 +13,10 @@ Recipe (numbers, dtypes and draw order), per workload:
            "softplus"   log a = -softplus(N(mu, sd)).   sd is a standard deviation.
   * erase / write gates: sigmoid(N(0, 1)).
   * S0 ~ N(0, s0_std) when s0_std > 0, else no initial state (zeros).
+  * packed workloads (seq_median > 0): B == 1 and the T tokens are split into sequences whose
+    lengths are drawn first, from their own generator seeded with seed + 7919, as
+    round(exp(log(seq_median) + N(0, 1))) clipped to [1, seq_max], until they cover T (the last
+    one is cut to fit); cu_seqlens are their offsets and S0 is [N, H, dk, dv].
   * gates and S0 are computed in fp64 and rounded to fp32 (round to nearest even); q, k, v are
     rounded to bf16 (round to nearest even) for the bf16 workloads.
 On the CPU the generator is torch's CPU generator; ``device="cuda"`` draws on the GPU with
@@ -22,11 +26,12 @@ multi-GiB workloads can be built in seconds.
 from __future__ import annotations
 
 import dataclasses
+import math
 from dataclasses import dataclass
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "generate", "generate_decode", "workload"]
+__all__ = ["Workload", "WORKLOADS", "generate", "generate_decode", "seq_lengths", "workload"]
 
 
 @dataclass(frozen=True)
@@ -48,6 +53,8 @@ class Workload:
     seed: int
     chunk: int = 64
     steps: int = 0  # decode workloads: number of single-token steps
+    seq_median: int = 0  # packed workloads: median sequence length (0: a dense [B, T] batch)
+    seq_max: int = 0  # packed workloads: longest sequence
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -74,6 +81,10 @@ WORKLOADS = {
         # decoupled per-channel erase / write (Gated DeltaNet-2, FG2-GDN+) long-context prefill
         Workload("gdn2_decoupled_bf16_t64k", 1, 65536, 32, 128, 128, "bf16", "softplus", True,
                  -4.0, 1.5, True, "channel", 0.0, 4),
+        # serving prefill: scalar-gate Gated DeltaNet over 16384 packed tokens of sequences of
+        # mixed lengths (median 512, at most 4096), 16 heads
+        Workload("gdn_scalar_bf16_varlen_t16k", 1, 16384, 16, 128, 128, "bf16", "softplus", False,
+                 -4.0, 1.0, False, "erase", 0.0, 6, seq_median=512, seq_max=4096),
         # single-token decode, 256 sequences x 32 heads, resident fp32 state
         Workload("decode_kda_n256_h32", 256, 1, 32, 128, 128, "bf16", "softplus", True, -4.0,
                  1.5, False, "erase", 0.01, 5, steps=1000),
@@ -114,9 +125,23 @@ def _unit_rows(x):
     return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
 
 
+def seq_lengths(wl: Workload) -> list[int]:
+    """Sequence lengths of a packed workload (see the recipe above); they sum to wl.T."""
+    gen = torch.Generator()
+    gen.manual_seed(wl.seed + 7919)
+    lens, total = [], 0
+    while total < wl.T:
+        x = float(torch.randn((), generator=gen, dtype=torch.float64))
+        n = min(max(round(math.exp(math.log(wl.seq_median) + x)), 1), wl.seq_max, wl.T - total)
+        lens.append(n)
+        total += n
+    return lens
+
+
 def generate(wl: Workload, device="cpu"):
     """Inputs for one prefill call: dict with q, k, v, log_decay, erase, write (or None), S0
-    (or None), all in the [B, T, H, d] layout the library takes."""
+    (or None), all in the [B, T, H, d] layout the library takes; packed workloads add
+    cu_seqlens (int32 [N + 1], on ``device``) and take S0 as [N, H, dk, dv]."""
     gen = torch.Generator(device=device)
     gen.manual_seed(wl.seed)
     lead = (wl.B, wl.T, wl.H)
@@ -126,10 +151,20 @@ def generate(wl: Workload, device="cpu"):
     log_decay = _log_decay(gen, wl, lead, device)
     erase = _sigmoid_gate(gen, lead + ((wl.dk,) if wl.erase_channel else ()), device)
     write = _sigmoid_gate(gen, lead + (wl.dv,), device) if wl.write == "channel" else None
+    nstate = wl.B
+    extra = {}
+    if wl.seq_median > 0:
+        if wl.B != 1:
+            raise ValueError("packed workloads have B == 1")
+        lens = seq_lengths(wl)
+        nstate = len(lens)
+        cu = torch.zeros(nstate + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
+        extra["cu_seqlens"] = cu.to(device)
     S0 = None
     if wl.s0_std > 0:
-        S0 = (wl.s0_std * _normal(gen, (wl.B, wl.H, wl.dk, wl.dv), device)).to(torch.float32)
-    return dict(q=q, k=k, v=v, log_decay=log_decay, erase=erase, write=write, S0=S0)
+        S0 = (wl.s0_std * _normal(gen, (nstate, wl.H, wl.dk, wl.dv), device)).to(torch.float32)
+    return dict(q=q, k=k, v=v, log_decay=log_decay, erase=erase, write=write, S0=S0, **extra)
 
 
 def generate_decode(wl: Workload, steps: int | None = None, device="cpu"):

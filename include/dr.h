@@ -123,6 +123,41 @@ int dr_chunk_fwd(const dr_desc* desc, const void* q, const void* k, const void* 
                  const float* S0, void* o, float* S_T, void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/* Packed batches of sequences of different lengths (serving prefill).  The nseq sequences lie
+ * one after another on the token axis of the dr_chunk_fwd layouts with B = 1 (desc->B must be
+ * 1 and desc->T is the packed token count): sequence n holds tokens cu_seqlens[n] ..
+ * cu_seqlens[n + 1] - 1.  Each sequence is an independent recurrence with its own state, as
+ * a server holds one fixed-size state per conversation ("Gated DeltaNet-2: decoupling erase
+ * and write in linear attention", sections "The attention bottleneck" and "Why this matters":
+ * constant-size state, constant-memory decoding); the packed layout is this library's own
+ * convention (those sections describe none).
+ *
+ *   cu_seqlens  nseq + 1 int32 offsets in device memory, 4-byte aligned, read on the device
+ *               (so the call cannot check them).  Valid offsets start at 0, never decrease and
+ *               end at desc->T.  The kernels clamp every offset into [0, T] and take the
+ *               running maximum, so no access leaves the arrays whatever they hold: the
+ *               results for invalid offsets are those of the offsets so corrected, and tokens
+ *               outside every sequence leave o untouched.
+ *   S0, S_T     [nseq, H, dk, dv] fp32 (S0 NULL = zeros, S_T NULL = skip; S0 may equal S_T).
+ *               An empty sequence writes S_T[n] = S0[n] (zeros without S0).  S_T is the state
+ *               layout of dr_decode_step with B = nseq, so decoding continues from it directly.
+ *   workspace   at least dr_chunk_fwd_varlen_workspace_bytes(desc, nseq) bytes.
+ * The paths are those of dr_chunk_fwd.  nseq == 0 or T == 0 enqueues at most the S_T copy.
+ * Errors as dr_chunk_fwd; nseq < 0 or > 2^30 is DR_E_SHAPE, a NULL cu_seqlens with nseq > 0
+ * DR_E_NULL, a cu_seqlens not 4-byte aligned DR_E_ALIGN, and cu_seqlens overlapping an
+ * output or the workspace DR_E_ALIAS. */
+
+/* Workspace bytes of dr_chunk_fwd_varlen (0 for an invalid descriptor or nseq).  The
+ * matrix-core path keeps the packets of dr_chunk_fwd for at most floor((T + 63 nseq) / 64)
+ * chunks per head (P bytes each, P as above), plus 16 bytes per chunk and per sequence of
+ * tables and 256 bytes; the token-by-token path needs the tables of the sequences only. */
+size_t dr_chunk_fwd_varlen_workspace_bytes(const dr_desc* desc, int32_t nseq);
+
+int dr_chunk_fwd_varlen(const dr_desc* desc, const int32_t* cu_seqlens, int32_t nseq, const void* q,
+                        const void* k, const void* v, const float* log_decay, const float* erase,
+                        const float* write, const float* S0, void* o, float* S_T, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /* One decode token for B independent sequences (desc->T must be 1): reads q, k, v, gates in
  * the [B, 1, H, d] layouts above, updates S [B, H, dk, dv] in place and writes o [B, 1, H, dv].
  * The state streams through once (read once, written once).  o must not overlap any input

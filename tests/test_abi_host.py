@@ -161,3 +161,64 @@ def test_descriptor_layout():
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
     fields = re.findall(r"(\w+)\s*[,;]", body)
     assert fields == [f[0] for f in _abi.DrDesc._fields_]
+
+
+# ---- packed sequences of different lengths ---------------------------------------------------
+P_CU = 2 * 1024 * GB  # fake device address of the offsets (4-byte aligned)
+
+
+def _vfwd(desc, nseq=3, **over):
+    ptr = dict(P)
+    ptr.update(over)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return _abi.lib().dr_chunk_fwd_varlen(ctypes.byref(desc) if desc is not None else None,
+                                          vp(ptr.get("cu", P_CU)), nseq,
+                                          vp(ptr["q"]), vp(ptr["k"]), vp(ptr["v"]), vp(ptr["ld"]), vp(ptr["e"]),
+                                          vp(ptr["w"]), vp(ptr["S0"]), vp(ptr["o"]), vp(ptr["ST"]),
+                                          vp(ptr["ws"]), ptr.get("wsn", 1 << 30), None)
+
+
+def test_varlen_workspace_query():
+    L = _abi.lib()
+    scal = 2 * 6 * 16 * 32 * 2 + 2 * 64 * 128 * 2 + 256 * 4
+    gen = 4 * 6 * 16 * 32 * 2 + 4 * 64 * 128 * 2 + 512 * 4
+    r256 = lambda n: (n + 255) // 256 * 256
+    # T = 1000 packed tokens in 5 sequences: at most (1000 + 63 * 5) // 64 = 20 chunks per head
+    d = _good_desc(B=1, T=1000)
+    maxc = (1000 + 63 * 5) // 64
+    tables = r256(16 * maxc) + r256(16 * 5) + 256
+    assert L.dr_chunk_fwd_varlen_workspace_bytes(ctypes.byref(d), 5) == 4 * maxc * scal + tables
+    g = _good_desc(B=1, T=1000, write_is_erase=0)
+    assert L.dr_chunk_fwd_varlen_workspace_bytes(ctypes.byref(g), 5) == 4 * maxc * gen + tables
+    # the token path keeps only the sequence table
+    t = _good_desc(B=1, T=1000, chunk=1)
+    assert L.dr_chunk_fwd_varlen_workspace_bytes(ctypes.byref(t), 5) == r256(16 * 5) + 256
+    # invalid: B != 1, no sequences, too many
+    assert L.dr_chunk_fwd_varlen_workspace_bytes(ctypes.byref(_good_desc(B=2)), 5) == 0
+    assert L.dr_chunk_fwd_varlen_workspace_bytes(ctypes.byref(d), 0) == 0
+    assert L.dr_chunk_fwd_varlen_workspace_bytes(ctypes.byref(d), -1) == 0
+    assert L.dr_chunk_fwd_varlen_workspace_bytes(None, 5) == 0
+
+
+def test_varlen_argument_errors():
+    d = _good_desc(B=1, T=1000)
+    assert _vfwd(None) == _abi.DR_E_NULL
+    assert _vfwd(_good_desc(B=2)) == _abi.DR_E_SHAPE
+    assert _vfwd(d, nseq=-1) == _abi.DR_E_SHAPE
+    assert _vfwd(d, nseq=2**30 + 1) == _abi.DR_E_SHAPE
+    assert _vfwd(d, cu=None) == _abi.DR_E_NULL
+    assert _vfwd(d, cu=P_CU + 2) == _abi.DR_E_ALIGN
+    for name in ("q", "k", "v", "ld", "e", "o"):
+        assert _vfwd(d, **{name: None}) == _abi.DR_E_NULL, name
+    # the states are [nseq, H, dk, dv]: S_T overlapping S0 partially, o or the offsets
+    assert _vfwd(d, ST=P["S0"] + 4096) == _abi.DR_E_ALIAS
+    assert _vfwd(d, o=P_CU) == _abi.DR_E_ALIAS
+    assert _vfwd(d, ST=P_CU - 16) == _abi.DR_E_ALIAS
+    assert _vfwd(d, ws=P_CU - 4096, wsn=1 << 30) == _abi.DR_E_ALIAS
+    need = _abi.lib().dr_chunk_fwd_varlen_workspace_bytes(ctypes.byref(d), 3)
+    assert _vfwd(d, wsn=need - 1) == _abi.DR_E_WORKSPACE
+    assert _vfwd(d, ws=None, wsn=0) == _abi.DR_E_WORKSPACE
+    # the per-sequence state is the extent that is checked: an S_T right after S0's 3 states is fine
+    # to validate but one inside them is not
+    state = 3 * 4 * 128 * 128 * 4
+    assert _vfwd(d, ST=P["S0"] + state - 16) == _abi.DR_E_ALIAS

@@ -1,0 +1,183 @@
+"""GPU parity of packed variable-length batches (dr_chunk_fwd_varlen) against the fp64 oracle.
+
+Each packed sequence is an independent recurrence from its own initial state; the oracle runs
+them one by one (oracle.recurrence_varlen).  Tolerances as for the dense batch: 3e-3 normwise
+for the bf16 matrix-core chunk path, 1e-5 for the fp32 token-by-token kernel."""
+import numpy as np
+import pytest
+import torch
+
+from metrics import err_S, err_o
+from oracle import recurrence, recurrence_varlen
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 3e-3
+
+
+@pytest.fixture(scope="module")
+def dr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_dr_amd as m
+
+    m.abi_version()  # raises if libdr.so is missing
+    return m
+
+
+def _packed(lens, H, variant, dtype="bf16", d=128, s0=True, seed=0):
+    """Seeded packed inputs: the dense recipe drawn over [1, sum(lens), H, d], S0 [N, H, d, d]."""
+    from gated_delta_rule_dr_amd.workloads import Workload, generate
+
+    T = int(sum(lens))
+    wl = Workload("case", 1, T, H, d, d, dtype, "softplus", variant != "scalar", -4.0, 1.5,
+                  variant == "decoupled", "channel" if variant == "decoupled" else "erase", 0.0, seed)
+    inp = generate(wl)
+    if s0:
+        g = torch.Generator().manual_seed(seed + 1)
+        inp["S0"] = (0.05 * torch.randn((len(lens), H, d, d), generator=g, dtype=torch.float64)).float()
+    inp["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    return inp
+
+
+def _run(dr, inp, chunk=64, cu=None, out=None):
+    dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    o, S = dr.chunk_fwd_varlen(dev["q"], dev["k"], dev["v"], dev["log_decay"], dev["erase"], dev["write"],
+                               dev["S0"], cu_seqlens=dev["cu_seqlens"] if cu is None else cu.cuda(),
+                               chunk=chunk, out=out)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def _oracle(inp, cu=None):
+    return recurrence_varlen(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"],
+                             inp["S0"], inp["cu_seqlens"] if cu is None else cu)
+
+
+def _errs_per_sequence(o, S, ro, rS, cu):
+    """Largest normwise error over the sequences (outputs of empty sequences have no rows)."""
+    o = o.double().cpu().numpy()
+    S = S.double().cpu().numpy()
+    eo, eS = 0.0, 0.0
+    for n in range(len(cu) - 1):
+        lo, hi = int(cu[n]), int(cu[n + 1])
+        if hi > lo:
+            eo = max(eo, err_o(o[:, lo:hi], ro[:, lo:hi]))
+        eS = max(eS, err_S(S[n:n + 1], rS[n:n + 1]))
+    return eo, eS
+
+
+LENS = {
+    "ragged": [1, 63, 64, 65, 200],
+    "empties": [0, 130, 0, 7, 0],
+    "one": [300],
+    "short_many": [5] * 20 + [129],
+}
+
+
+@pytest.mark.parametrize("H", [2, 16])
+@pytest.mark.parametrize("mix", list(LENS))
+@pytest.mark.parametrize("variant", ["scalar", "kda", "decoupled"])
+def test_varlen_chunk_path_matches_oracle(dr, H, mix, variant):
+    # H = 2 runs 16-column value slices for most mixes, H = 16 32-column ones (N * H >= 64)
+    lens = LENS[mix]
+    inp = _packed(lens, H, variant, seed=len(lens) + H)
+    o, S = _run(dr, inp)
+    ro, rS = _oracle(inp)
+    eo, eS = _errs_per_sequence(o, S, ro, rS, inp["cu_seqlens"].numpy())
+    print(f"varlen {variant} {mix} H={H}: err_o={eo:.3e} err_S={eS:.3e}")
+    assert eo <= TOL_BF16 and eS <= TOL_BF16, (eo, eS)
+    # an empty sequence passes its state through exactly
+    cu = inp["cu_seqlens"].numpy()
+    for n in range(len(lens)):
+        if cu[n + 1] == cu[n]:
+            assert torch.equal(S[n].cpu(), inp["S0"][n])
+
+
+@pytest.mark.parametrize("variant", ["scalar", "decoupled"])
+@pytest.mark.parametrize("dtype,d", [("f32", 32), ("bf16", 64), ("bf16", 128)])
+def test_varlen_token_path_matches_oracle(dr, variant, dtype, d):
+    lens = [0, 17, 1, 40, 0, 9]
+    inp = _packed(lens, 3, variant, dtype=dtype, d=d, seed=d)
+    o, S = _run(dr, inp, chunk=1)
+    ro, rS = _oracle(inp)
+    eo, eS = _errs_per_sequence(o, S, ro, rS, inp["cu_seqlens"].numpy())
+    assert eo <= TOL_F32 and eS <= TOL_F32, (eo, eS)
+
+
+@pytest.mark.parametrize("variant", ["scalar", "kda", "decoupled"])
+def test_varlen_equal_lengths_equal_dense_batch(dr, variant):
+    # the same chunks through the same kernels: bit-identical to the dense [N, L] batch
+    N, L, H = 3, 150, 4
+    inp = _packed([L] * N, H, variant, seed=5)
+    o, S = _run(dr, inp)
+    dense = {k: (None if v is None else v.reshape((N, L) + tuple(v.shape[2:])).cuda())
+             for k, v in inp.items() if k not in ("cu_seqlens", "S0")}
+    od, Sd = dr.chunk_fwd(dense["q"], dense["k"], dense["v"], dense["log_decay"], dense["erase"],
+                          dense["write"], inp["S0"].cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(o.reshape(od.shape), od) and torch.equal(S, Sd)
+
+
+def test_varlen_decode_handoff(dr):
+    # prefill three sequences packed, then decode four more tokens of each from the returned
+    # states: every decode output equals the oracle over the sequence's whole token run
+    H, lens, extra = 4, [70, 1, 129], 4
+    full = _packed([sum(lens) + extra * len(lens)], H, "kda", seed=9, s0=False)
+    g = torch.Generator().manual_seed(10)
+    S0 = (0.05 * torch.randn((len(lens), H, 128, 128), generator=g, dtype=torch.float64)).float()
+    starts = np.concatenate([[0], np.cumsum([L + extra for L in lens])])
+    pre = np.concatenate([np.arange(starts[n], starts[n] + L) for n, L in enumerate(lens)])
+    keys = ("q", "k", "v", "log_decay", "erase")
+    inp = {k: full[k][:, pre].contiguous() for k in keys}
+    inp["write"], inp["S0"] = None, S0
+    inp["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    _, S = _run(dr, inp)
+    for j in range(extra):
+        idx = [starts[n] + L + j for n, L in enumerate(lens)]
+        step = {k: full[k][0, idx].contiguous().cuda() for k in keys}
+        o = dr.decode_step(step["q"], step["k"], step["v"], step["log_decay"], step["erase"], S=S)
+        torch.cuda.synchronize()
+        for n, L in enumerate(lens):
+            run = slice(starts[n], starts[n] + L + j + 1)
+            ro, _ = recurrence(*(full[k][:, run] for k in keys), None, S0[n:n + 1])
+            e = err_o(o[n:n + 1, None].double().cpu().numpy(), ro[:, -1:])
+            assert e <= TOL_BF16, (n, j, e)
+
+
+def test_varlen_offsets_are_clamped(dr):
+    # offsets outside [0, T] or decreasing are clamped and replaced by their running maximum;
+    # tokens before the first offset are in no sequence and their outputs stay untouched
+    H, T = 2, 200
+    inp = _packed([T], H, "scalar", seed=11)
+    inp["S0"] = inp["S0"].expand(4, -1, -1, -1).contiguous()
+    bad = torch.tensor([10, 60, 30, 400, 150], dtype=torch.int32)
+    fixed = np.array([10, 60, 60, 200, 200])
+    out = torch.full((1, T, H, 128), 7.0, device="cuda")
+    o, S = _run(dr, inp, cu=bad, out=out)
+    sub = {k: (v[:, 10:] if k not in ("S0", "cu_seqlens") and v is not None else v) for k, v in inp.items()}
+    ro, rS = _oracle(sub, cu=fixed - 10)
+    eo, eS = _errs_per_sequence(o[:, 10:], S, ro, rS, fixed - 10)
+    assert eo <= TOL_BF16 and eS <= TOL_BF16, (eo, eS)
+    assert bool((o[:, :10] == 7.0).all())
+
+
+def test_varlen_many_sequences(dr):
+    # more sequences than one workgroup of the table set-up covers at once (1024)
+    rng = np.random.default_rng(12)
+    lens = rng.integers(0, 9, size=1500)
+    inp = _packed(list(lens), 1, "scalar", seed=13)
+    o, S = _run(dr, inp)
+    ro, rS = _oracle(inp)
+    eo, eS = _errs_per_sequence(o, S, ro, rS, inp["cu_seqlens"].numpy())
+    assert eo <= TOL_BF16 and eS <= TOL_BF16, (eo, eS)
+
+
+def test_varlen_no_tokens(dr):
+    inp = _packed([0, 0, 0], 2, "scalar", seed=14)
+    o, S = _run(dr, inp)
+    assert torch.equal(S.cpu(), inp["S0"])
+    inp0 = dict(inp, S0=None, cu_seqlens=torch.zeros(1, dtype=torch.int32))
+    o, S = _run(dr, inp0)
+    assert o.shape == (1, 0, 2, 128) and S.shape == (0, 2, 128, 128)

@@ -1,7 +1,7 @@
 """Seeded input generators: shapes, dtypes, value ranges and determinism (CPU only)."""
 import torch
 
-from gated_delta_rule_dr_amd.workloads import WORKLOADS, generate, generate_decode, workload
+from gated_delta_rule_dr_amd.workloads import WORKLOADS, generate, generate_decode, seq_lengths, workload
 
 
 def test_shapes_dtypes_and_ranges_small():
@@ -28,6 +28,7 @@ def test_shapes_dtypes_and_ranges_small():
         norms = torch.linalg.vector_norm(d["k"].double(), dim=-1)
         assert float((norms - 1).abs().max()) < 1e-2  # unit keys up to the storage rounding
         assert d["S0"] is None
+        assert ("cu_seqlens" in d) == (wl.seq_median > 0)
 
 
 def test_seeded_and_deterministic():
@@ -44,3 +45,18 @@ def test_decay_distribution_matches_recipe():
     wl = workload("gdn_scalar_f32_d32", T=4096, H=8)
     alpha = torch.exp(generate(wl)["log_decay"].double())
     assert 0.90 < float(alpha.mean()) < 0.95
+
+
+def test_packed_lengths_recipe():
+    wl = workload("gdn_scalar_bf16_varlen_t16k")
+    lens = seq_lengths(wl)
+    assert sum(lens) == wl.T and min(lens) >= 1 and max(lens) <= wl.seq_max
+    assert lens == seq_lengths(wl)  # seeded
+    assert 10 <= len(lens) <= 200
+    small = wl.replace(T=3000, H=2, s0_std=0.1)
+    d = generate(small)
+    cu = d["cu_seqlens"]
+    assert cu.dtype == torch.int32 and int(cu[0]) == 0 and int(cu[-1]) == 3000
+    assert bool((cu[1:] >= cu[:-1]).all())
+    assert d["q"].shape == (1, 3000, 2, 128)
+    assert d["S0"].shape == (cu.numel() - 1, 2, 128, 128)
