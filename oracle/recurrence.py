@@ -149,7 +149,7 @@ def recurrence_varlen(q, k, v, log_decay, erase, write=None, S0=None, cu_seqlens
     conversation and decode it in constant memory ("Gated DeltaNet-2: decoupling erase and
     write in linear attention", sections "The attention bottleneck" and "Why this matters";
     "KronLSTM ...", section "The problem").  Packing the sequences one after another on the
-    token axis, delimited by offsets, is a layout convention that the pages do not describe.
+    token axis, delimited by offsets, is a layout convention that those sections do not describe.
 
     Args:
       q, k: [1, T, H, dk] and v: [1, T, H, dv], the sequences concatenated on the token axis;
