@@ -43,16 +43,25 @@ DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_dr_amd", "csrc", "decode.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+def n_states(wl) -> int:
+    """States of one forward: one per batch row, or one per sequence of a packed workload."""
+    if wl.seq_median > 0:
+        from gated_delta_rule_dr_amd.workloads import seq_lengths
+
+        return len(seq_lengths(wl))
+    return wl.B
+
+
 def algorithmic_bytes(wl) -> int:
     """Compulsory HBM bytes of one forward: q, k, v in their storage type, every gate once, the
-    fp32 output, S0 when given and S_T."""
+    fp32 output, S0 when given and S_T (one state per batch row or packed sequence)."""
     th = wl.B * wl.T * wl.H
     qkv = 2 if wl.qkv_dtype == "bf16" else 4
     per_tok = qkv * (2 * wl.dk + wl.dv) + 4 * wl.dv
     per_tok += 4 * (wl.dk if wl.decay_channel else 1)
     per_tok += 4 * (wl.dk if wl.erase_channel else 1)
     per_tok += 4 * wl.dv if wl.write == "channel" else 0
-    state = wl.B * wl.H * wl.dk * wl.dv * 4
+    state = n_states(wl) * wl.H * wl.dk * wl.dv * 4
     return th * per_tok + state * (2 if wl.s0_std > 0 else 1)
 
 
@@ -98,13 +107,18 @@ def counter_traffic(kernel: str, workload: str, src: str):
 def time_prefill(dr, torch, wl, steps, warmup):
     from gated_delta_rule_dr_amd.workloads import generate
 
-    sets = [generate(wl, device="cuda"), generate(wl.replace(seed=wl.seed + 1000), device="cuda")]
+    # the second set keeps the first one's sequence lengths (they are drawn from wl.seed)
+    sets = [generate(wl, device="cuda"), generate(wl, device="cuda", value_seed=wl.seed + 1000)]
     o = torch.empty((wl.B, wl.T, wl.H, wl.dv), device="cuda")
-    S_T = torch.empty((wl.B, wl.H, wl.dk, wl.dv), device="cuda")
+    S_T = torch.empty((n_states(wl), wl.H, wl.dk, wl.dv), device="cuda")
 
     def step(i):
         x = sets[i % 2]
-        dr.chunk_fwd(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"], x["S0"], out=o, S_T=S_T)
+        if "cu_seqlens" in x:
+            dr.chunk_fwd_varlen(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"], x["S0"],
+                                cu_seqlens=x["cu_seqlens"], out=o, S_T=S_T)
+        else:
+            dr.chunk_fwd(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"], x["S0"], out=o, S_T=S_T)
 
     for i in range(warmup):
         step(i)
@@ -175,7 +189,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--all", action="store_true", help="also time the KDA and decoupled prefill workloads")
+    ap.add_argument("--all", action="store_true",
+                    help="also time the KDA, decoupled and packed-sequence prefill workloads")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="also run one plain elementwise copy of this many MiB (a known-size "
                          "reference for HBM byte counters)")
@@ -235,7 +250,7 @@ def main():
     }
     if args.all:
         extra = {}
-        for name in ("kda_channel_bf16_t16k", "gdn2_decoupled_bf16_t64k"):
+        for name in ("kda_channel_bf16_t16k", "gdn2_decoupled_bf16_t64k", "gdn_scalar_bf16_varlen_t16k"):
             w2 = workload(name)
             s2, _ = time_prefill(dr, torch, w2, max(3, args.steps // 10), 2)
             extra[name] = {"tokens_per_s": w2.token_heads / s2, "ms": s2 * 1e3,

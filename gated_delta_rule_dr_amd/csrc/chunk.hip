@@ -290,6 +290,24 @@ __device__ __forceinline__ SeqRef seq_ref(const Problem& p, int bh, int h) {
   return r;
 }
 
+// The (sequence * H + head, value slice) of a scan workgroup.  A dense batch maps blockIdx
+// directly; packed sequences take the sequences longest first (the workgroups start in the
+// order of their linear index), all heads and slices of one sequence together.
+struct WgRef {
+  int bh, slice;
+};
+__device__ __forceinline__ WgRef wg_ref(const Problem& p) {
+  WgRef r{int(blockIdx.x), int(blockIdx.y)};
+  if (p.order) {
+    const int per = p.H * int(gridDim.y);
+    const int w = int(blockIdx.x) + int(gridDim.x) * int(blockIdx.y);
+    const int rank = w / per, rem = w - rank * per;
+    r.slice = rem / p.H;
+    r.bh = p.order[rank] * p.H + (rem - r.slice * p.H);
+  }
+  return r;
+}
+
 // A sequence without tokens: S_T = S0 (zeros without S0) on this workgroup's value columns.
 __device__ void pass_state(const Problem& p, int bh, int j0, int ncols) {
   if (!p.S_T) return;
@@ -346,20 +364,23 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
     float lds, gb;
   };
   // Work item blk: a dense batch walks (b, h, chunk) with packet index blk; packed sequences
-  // walk (chunk, head) over the chunk table.
+  // walk (chunk, head) over the chunk table.  Work items number fewer than 2^31 (one packet
+  // each, and the packets fit in device memory), so the index arithmetic is 32-bit.
   auto chunk_ref = [&](int64_t blk) {
     ChunkRef r;
+    const uint32_t ub = uint32_t(blk);
     if (p.chunks) {
-      const int64_t g = blk / H;
-      r.h = int(blk - g * H);
+      const uint32_t g = ub / uint32_t(H);
+      r.h = int(ub - g * uint32_t(H));
       const int4 e = p.chunks[g];
       r.tok0 = e.x;
       r.tlen = e.y;
       r.pkt = int64_t(e.z) + int64_t(r.h) * e.w;
     } else {
-      const int bh = int(blk / nchunks), c = int(blk - int64_t(bh) * nchunks);
-      const int b = bh / H;
-      r.h = bh - b * H;
+      const uint32_t bh = ub / uint32_t(nchunks);
+      const int c = int(ub - bh * uint32_t(nchunks));
+      const int b = int(bh / uint32_t(H));
+      r.h = int(bh) - b * H;
       r.tok0 = int64_t(b) * T + int64_t(c) * C;
       r.tlen = T - c * C < C ? T - c * C : C;
       r.pkt = blk;
@@ -783,9 +804,10 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int bh = blockIdx.x;
-  const int H = p.H, h = bh % H;
-  const int j0 = blockIdx.y * DVS;
+  const int H = p.H;
+  const WgRef wg = wg_ref(p);
+  const int bh = wg.bh, h = bh % H;
+  const int j0 = wg.slice * DVS;
   const SeqRef sq = seq_ref(p, bh, h);
   const int T = sq.len;  // this sequence's tokens
   const int nchunks = sq.nch;
@@ -1185,9 +1207,10 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int bh = blockIdx.x;
-  const int H = p.H, h = bh % H;
-  const int j0 = blockIdx.y * DVS;
+  const int H = p.H;
+  const WgRef wg = wg_ref(p);
+  const int bh = wg.bh, h = bh % H;
+  const int j0 = wg.slice * DVS;
   const SeqRef sq = seq_ref(p, bh, h);
   const int T = sq.len;  // this sequence's tokens
   const int nchunks = sq.nch;
@@ -1697,11 +1720,11 @@ size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric, bool decay_
 }
 
 // Packed sequences: packets of at most varlen_max_chunks chunks per head, then the chunk
-// table, the sequence table and the chunk count.
+// table, the sequence table, the sequence order and the chunk count.
 size_t chunk128_varlen_workspace_bytes(int nseq, int T, int H, bool symmetric, bool decay_channel) {
   const int64_t maxc = varlen_max_chunks(nseq, T);
   return size_t(int64_t(H) * maxc * packet_bytes(symmetric, decay_channel) + round256(maxc * 16) +
-                round256(int64_t(nseq) * 16) + 256);
+                round256(int64_t(nseq) * 16) + round256(int64_t(nseq) * 4) + 256);
 }
 
 hipError_t launch_chunk128_varlen(Problem p, const int* cu, void* workspace, hipStream_t stream) {
@@ -1710,12 +1733,14 @@ hipError_t launch_chunk128_varlen(Problem p, const int* cu, void* workspace, hip
   char* tables = ws + int64_t(p.H) * maxc * packet_bytes(p.symmetric, p.decay_channel);
   int4* chunks = reinterpret_cast<int4*>(tables);
   int4* seqs = reinterpret_cast<int4*>(tables + round256(maxc * 16));
-  int* total = reinterpret_cast<int*>(tables + round256(maxc * 16) + round256(int64_t(p.B) * 16));
-  hipError_t e = launch_varlen_setup(cu, p.B, p.T, p.H, C, seqs, chunks, total, stream);
+  int* order = reinterpret_cast<int*>(tables + round256(maxc * 16) + round256(int64_t(p.B) * 16));
+  int* total = order + round256(int64_t(p.B) * 4) / 4;
+  hipError_t e = launch_varlen_setup(cu, p.B, p.T, p.H, C, seqs, chunks, total, order, stream);
   if (e != hipSuccess) return e;
   p.seqs = seqs;
   p.chunks = chunks;
   p.nchunks_total = total;
+  p.order = order;
   return launch_chunk128(p, workspace, stream);
 }
 

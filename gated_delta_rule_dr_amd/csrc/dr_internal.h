@@ -33,13 +33,15 @@ struct Problem {
   const int4* chunks = nullptr;        // [chunks] {first token, tokens, packet of head 0, chunks
                                        //  of its sequence}; the packet of head h adds h * chunks
   const int* nchunks_total = nullptr;  // number of entries in `chunks`
+  const int* order = nullptr;          // [B] sequences, longest first (scan workgroup order)
 };
 
 // Sequence tables of a packed batch (one workgroup): from nseq + 1 device offsets `cu` over T
 // packed tokens, clamped into [0, T] and made nondecreasing, writes seqs[nseq], chunks[] (when
-// not null; at most varlen_max_chunks entries) and *total, for chunks of `chunk` tokens.
+// not null; at most varlen_max_chunks entries), *total, for chunks of `chunk` tokens, and
+// (when not null) order[nseq], the sequences longest first.
 hipError_t launch_varlen_setup(const int* cu, int nseq, int T, int H, int chunk, int4* seqs, int4* chunks,
-                               int* total, hipStream_t stream);
+                               int* total, int* order, hipStream_t stream);
 
 // Upper bound on the chunks of nseq sequences with T tokens in all: sum ceil(len / 64).
 inline int64_t varlen_max_chunks(int64_t nseq, int64_t T) { return (T + 63 * nseq) / 64; }

@@ -168,7 +168,7 @@ hipError_t launch_recurrent_varlen(Problem p, const int* cu, void* workspace, hi
   char* ws = static_cast<char*>(workspace);
   int4* seqs = reinterpret_cast<int4*>(ws);
   int* total = reinterpret_cast<int*>(ws + (int64_t(p.B) * 16 + 255) / 256 * 256);
-  hipError_t e = launch_varlen_setup(cu, p.B, p.T, p.H, 64, seqs, nullptr, total, stream);
+  hipError_t e = launch_varlen_setup(cu, p.B, p.T, p.H, 64, seqs, nullptr, total, nullptr, stream);
   if (e != hipSuccess) return e;
   p.seqs = seqs;
   return launch_recurrent(p, stream);

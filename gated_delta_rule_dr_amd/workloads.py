@@ -138,12 +138,13 @@ def seq_lengths(wl: Workload) -> list[int]:
     return lens
 
 
-def generate(wl: Workload, device="cpu"):
+def generate(wl: Workload, device="cpu", value_seed=None):
     """Inputs for one prefill call: dict with q, k, v, log_decay, erase, write (or None), S0
     (or None), all in the [B, T, H, d] layout the library takes; packed workloads add
-    cu_seqlens (int32 [N + 1], on ``device``) and take S0 as [N, H, dk, dv]."""
+    cu_seqlens (int32 [N + 1], on ``device``) and take S0 as [N, H, dk, dv].  ``value_seed``
+    (default wl.seed) seeds the values only; packed sequence lengths always follow wl.seed."""
     gen = torch.Generator(device=device)
-    gen.manual_seed(wl.seed)
+    gen.manual_seed(wl.seed if value_seed is None else value_seed)
     lead = (wl.B, wl.T, wl.H)
     q = _qkv_round(_normal(gen, lead + (wl.dk,), device), wl.qkv_dtype)
     k = _qkv_round(_unit_rows(_normal(gen, lead + (wl.dk,), device)), wl.qkv_dtype)

@@ -149,8 +149,9 @@ int dr_chunk_fwd(const dr_desc* desc, const void* q, const void* k, const void* 
 
 /* Workspace bytes of dr_chunk_fwd_varlen (0 for an invalid descriptor or nseq).  The
  * matrix-core path keeps the packets of dr_chunk_fwd for at most floor((T + 63 nseq) / 64)
- * chunks per head (P bytes each, P as above), plus 16 bytes per chunk and per sequence of
- * tables and 256 bytes; the token-by-token path needs the tables of the sequences only. */
+ * chunks per head (P bytes each, P as above), plus tables of 16 bytes per chunk and 20 bytes
+ * per sequence (each table rounded up to 256 bytes) and 256 bytes; the token-by-token path
+ * needs the 16-byte sequence table and 256 bytes only. */
 size_t dr_chunk_fwd_varlen_workspace_bytes(const dr_desc* desc, int32_t nseq);
 
 int dr_chunk_fwd_varlen(const dr_desc* desc, const int32_t* cu_seqlens, int32_t nseq, const void* q,

@@ -186,7 +186,7 @@ def test_varlen_workspace_query():
     # T = 1000 packed tokens in 5 sequences: at most (1000 + 63 * 5) // 64 = 20 chunks per head
     d = _good_desc(B=1, T=1000)
     maxc = (1000 + 63 * 5) // 64
-    tables = r256(16 * maxc) + r256(16 * 5) + 256
+    tables = r256(16 * maxc) + r256(16 * 5) + r256(4 * 5) + 256
     assert L.dr_chunk_fwd_varlen_workspace_bytes(ctypes.byref(d), 5) == 4 * maxc * scal + tables
     g = _good_desc(B=1, T=1000, write_is_erase=0)
     assert L.dr_chunk_fwd_varlen_workspace_bytes(ctypes.byref(g), 5) == 4 * maxc * gen + tables

@@ -5,7 +5,8 @@ generator); the fp64 oracle then recomputes a few sampled (b, h) pairs -- first,
 inside -- from the very same input values, over the whole sequence, and o and S_T of those
 pairs must agree to the bf16-path tolerance; every head is checked for finiteness.  The decode
 workload runs its full 256 x 32 heads for a number of steps and samples (n, h) pairs the same
-way.  A linearity identity covers every head of the bench workload."""
+way, and the packed serving workload samples (sequence, head) pairs.  A linearity identity
+covers every head of the bench workload."""
 import pytest
 import torch
 
@@ -60,6 +61,35 @@ def test_prefill_full_size_sampled_heads(dr, name, pairs):
         eS = err_S(S_T[b:b + 1, h:h + 1], rS)
         print(f"{name} (b={b}, h={h}): err_o={eo:.3e} err_S={eS:.3e}", flush=True)
         assert eo <= TOL_BF16 and eS <= TOL_BF16, (b, h, eo, eS)
+
+
+def test_packed_full_size_sampled_sequences(dr):
+    """The packed serving workload at full size, as bench.py times it: sampled (sequence, head)
+    pairs -- the first sequence, the longest and the last -- against the oracle over each
+    whole sequence."""
+    from gated_delta_rule_dr_amd.workloads import generate, seq_lengths, workload
+
+    wl = workload("gdn_scalar_bf16_varlen_t16k")
+    inp = generate(wl, device="cuda")
+    lens = seq_lengths(wl)
+    N = len(lens)
+    o = torch.empty((1, wl.T, wl.H, wl.dv), device="cuda")
+    S_T = torch.empty((N, wl.H, wl.dk, wl.dv), device="cuda")
+    dr.chunk_fwd_varlen(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"], inp["S0"],
+                        cu_seqlens=inp["cu_seqlens"], out=o, S_T=S_T)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(S_T).all()
+    cu = inp["cu_seqlens"].cpu().tolist()
+    longest = max(range(N), key=lambda n: lens[n])
+    for n, h in [(0, 0), (longest, 7), (N - 1, wl.H - 1)]:
+        lo, hi = cu[n], cu[n + 1]
+        sl = {k: (None if v is None else v[:, lo:hi, h:h + 1].cpu())
+              for k, v in inp.items() if k not in ("cu_seqlens", "S0")}
+        ro, rS = recurrence(sl["q"], sl["k"], sl["v"], sl["log_decay"], sl["erase"], sl["write"], None)
+        eo = err_o(o[:, lo:hi, h:h + 1], ro)
+        eS = err_S(S_T[n:n + 1, h:h + 1], rS)
+        print(f"packed (sequence {n} of {hi - lo} tokens, h={h}): err_o={eo:.3e} err_S={eS:.3e}", flush=True)
+        assert eo <= TOL_BF16 and eS <= TOL_BF16, (n, h, eo, eS)
 
 
 def test_prefill_full_size_linearity_all_heads(dr):
