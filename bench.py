@@ -75,6 +75,13 @@ def algorithmic_flops(wl) -> float:
     return wl.B * wl.H * (wl.T / C) * per_chunk
 
 
+def gate_desc(wl) -> str:
+    decay = "per channel" if wl.decay_channel else "per head"
+    if wl.write == "channel":
+        return f"fp32 decay {decay}, erase {'per channel' if wl.erase_channel else 'per head'}, write per channel"
+    return f"fp32 decay {decay}, one per-head erase/write gate" if wl.decay_channel else "fp32 per head"
+
+
 def decode_bytes(wl) -> int:
     """Per decode step: the fp32 state read and written once, q/k/v, gates and the output."""
     n = wl.B * wl.H
@@ -167,13 +174,17 @@ def cpu_baseline(wl, tokens):
     from threadpoolctl import threadpool_limits
 
     from gated_delta_rule_dr_amd.workloads import generate
-    from oracle import recurrence
+    from oracle import recurrence, recurrence_varlen
 
     sample = wl.replace(T=tokens)
     inp = generate(sample)
+    args = (inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"], inp["S0"])
     with threadpool_limits(1):
         t0 = time.perf_counter()
-        recurrence(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"], inp["S0"])
+        if "cu_seqlens" in inp:  # packed: the first `tokens` tokens, cut into the recipe's lengths
+            recurrence_varlen(*args, inp["cu_seqlens"])
+        else:
+            recurrence(*args)
         sec = time.perf_counter() - t0
     return dict(value=sample.token_heads / sec, unit="tokens/s", cores=1, kind="oracle",
                 sample=f"{sample.B}x{sample.H} heads x first {tokens} tokens of {wl.name} "
@@ -191,6 +202,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--all", action="store_true",
                     help="also time the KDA, decoupled and packed-sequence prefill workloads")
+    ap.add_argument("--workload", default=PREFILL,
+                    help="prefill workload of the main line (default: the bench workload %(default)s)")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="also run one plain elementwise copy of this many MiB (a known-size "
                          "reference for HBM byte counters)")
@@ -218,13 +231,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    wl = workload(PREFILL)
+    wl = workload(args.workload)
+    if wl.steps:
+        print(f"{wl.name} is a decode workload; --workload takes a prefill one", file=sys.stderr)
+        sys.exit(2)
     sec, wall = time_prefill(dr, torch, wl, args.steps, args.warmup)
     tok_s = wl.token_heads / sec
     nbytes = algorithmic_bytes(wl)
     flops = algorithmic_flops(wl)
     achieved = nbytes / sec / 1e9
-    traffic = counter_traffic("chunk_fwd", PREFILL, CHUNK_SRC)
+    traffic = counter_traffic("chunk_fwd", wl.name, CHUNK_SRC)
     line = {
         "metric": METRIC,
         "value": tok_s,
@@ -238,11 +254,14 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16 matrix operands, fp32 accumulate and state (bf16 inputs)",
         "data": "synthetic (seeded; two alternating input sets)",
-        "config": {"workload": PREFILL, "B": wl.B, "H": wl.H, "T": wl.T, "dk": wl.dk, "dv": wl.dv,
-                   "chunk": wl.chunk, "qkv": "bf16", "gates": "fp32 per head", "o": "fp32"},
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "dk": wl.dk, "dv": wl.dv,
+                   "chunk": wl.chunk, "qkv": wl.qkv_dtype, "gates": gate_desc(wl), "o": "fp32",
+                   **({"sequences": n_states(wl)} if wl.seq_median else {})},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "dr_chunk_fwd = chunk_prep_kernel + chunk_scan_sym_kernel (one call)",
+                     "kernel": ("dr_chunk_fwd_varlen = varlen_setup_kernel + chunk_prep_kernel + scan (one call)"
+                                if wl.seq_median else
+                                "dr_chunk_fwd = chunk_prep_kernel + chunk_scan_sym_kernel (one call)"),
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": {"achieved_tflops": flops / sec / 1e12, "peak_tflops": MFMA_PEAK_TFLOPS,
                  "frac": flops / sec / 1e12 / MFMA_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops},
