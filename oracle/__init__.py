@@ -10,8 +10,10 @@ identity, a hand-worked 2x2 example, the explicit matrix forms of the scalar, KD
 FG2-GDN updates, the gradient-step reading of the delta rule, linearity, state resume, the
 norm bound and the dk = dv = 1 closed form; for packed sequences, equality with the dense
 batch at equal lengths, isolation between sequences, empty sequences, split invariance (the
-prefill-to-decode handoff) and the one-token closed form.  No function here is "parity unpinned".
+prefill-to-decode handoff) and the one-token closed form; for FG2's per-channel rate, its
+explicit matrix form, the KDA form at a channel-constant rate, and the gradient-step reading
+with a diagonal learning-rate matrix.  No function here is "parity unpinned".
 """
-from .recurrence import as_f64, decode_step, recurrence, recurrence_varlen
+from .recurrence import as_f64, decode_step, recurrence, recurrence_fg2, recurrence_varlen
 
-__all__ = ["recurrence", "recurrence_varlen", "decode_step", "as_f64"]
+__all__ = ["recurrence", "recurrence_fg2", "recurrence_varlen", "decode_step", "as_f64"]

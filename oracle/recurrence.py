@@ -41,7 +41,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["recurrence", "recurrence_varlen", "decode_step", "as_f64"]
+__all__ = ["recurrence", "recurrence_fg2", "recurrence_varlen", "decode_step", "as_f64"]
 
 
 def as_f64(x):
@@ -122,6 +122,32 @@ def recurrence(q, k, v, log_decay, erase, write=None, S0=None, return_states=Fal
     if return_states:
         return o, S, states
     return o, S
+
+
+def recurrence_fg2(q, k, v, log_decay, beta, S0=None):
+    """FG2-GDN's update with a per-channel learning rate, token by token in fp64.
+
+    The rate beta_t in R^dk is absorbed symmetrically into the key and the value, which keeps
+    the rank-1 Householder form of the update ("FG2-GDN: Enhancing Long-Context Gated Delta
+    Networks with Doubly Fine-Grained Control", section 2, FG2-GDN update rule):
+
+        k~_t = sqrt(beta_t) * k_t,   v~_t = sqrt(beta_t) * v_t
+        S_t  = (I - k~_t k~_t^T) Diag(a_t) S_{t-1} + k~_t v~_t^T,      o_t = S_t^T q_t
+
+    The rate multiplies value channels, so it needs dk == dv.  The query is not scaled (the
+    update rule scales only k and v).  With the scaled pair this is the general recurrence with
+    unit erase and write gates, which is how it is evaluated here.
+
+    Args: q, k, v [B, T, H, d]; log_decay [B, T, H] or [B, T, H, d]; beta [B, T, H, d] > 0;
+    S0 [B, H, d, d] or None.  Returns (o [B, T, H, d], S_T [B, H, d, d]) as float64.
+    """
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    beta = as_f64(beta)
+    if k.shape[-1] != v.shape[-1] or beta.shape != k.shape:
+        raise ValueError("the per-channel rate needs dk == dv and beta shaped like k")
+    r = np.sqrt(beta)
+    ones = np.ones(k.shape[:3])
+    return recurrence(q, r * k, r * v, log_decay, ones, None, S0)
 
 
 def decode_step(q, k, v, log_decay, erase, write, S):

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from chunk_model import chunk_forward
-from oracle import decode_step, recurrence, recurrence_varlen
+from oracle import decode_step, recurrence, recurrence_fg2, recurrence_varlen
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -462,3 +462,62 @@ def test_varlen_rejects_bad_offsets():
     for bad in ([0, 3], [1, 3, 5], [0, 4, 3]):
         with pytest.raises(ValueError):
             recurrence_varlen(q, k, v, ld, e, w, None, np.array(bad, np.int32))
+
+
+# ---- FG2-GDN's per-channel rate, absorbed as sqrt(beta) into key and value -------------------
+# ("FG2-GDN ...", section 2, FG2-GDN update rule)
+
+
+# F1 -- the explicit form (I - k~ k~^T) Diag(a) S + k~ v~^T as dense matrix products, channel and
+# scalar decay.
+@pytest.mark.parametrize("decay", ["channel", "head"])
+def test_fg2_explicit_matrix_form(decay):
+    r = _rng(41)
+    T, d = 17, 6
+    q, k, v = r.standard_normal((T, d)), _unit(r.standard_normal((T, d))), r.standard_normal((T, d))
+    la = -np.log1p(np.exp(r.normal(-2, 1, (T, d) if decay == "channel" else (T,))))
+    beta = _sig(r.standard_normal((T, d)))
+    S0 = r.standard_normal((d, d))
+    I = np.eye(d)
+    S = S0.copy()
+    o_ref = np.empty((T, d))
+    for t in range(T):
+        kt, vt = np.sqrt(beta[t]) * k[t], np.sqrt(beta[t]) * v[t]
+        A = np.diag(np.exp(la[t]) * np.ones(d))
+        S = (I - np.outer(kt, kt)) @ A @ S + np.outer(kt, vt)
+        o_ref[t] = S.T @ q[t]
+    wrap = lambda x: x[None, :, None]
+    o, S_out = recurrence_fg2(wrap(q), wrap(k), wrap(v), wrap(la), wrap(beta), S0[None, None])
+    assert np.allclose(o[0, :, 0], o_ref, rtol=0, atol=1e-12 * np.abs(o_ref).max())
+    assert np.allclose(S_out[0, 0], S, rtol=0, atol=1e-12 * np.abs(S).max())
+
+
+# F2 -- a rate that is the same on every channel is KDA's scalar beta: sqrt(b) k sqrt(b) k^T =
+# b k k^T and sqrt(b) k sqrt(b) v^T = b k v^T.
+def test_fg2_constant_rate_is_kda():
+    q, k, v, ld, e, _, S0 = _inputs(42, B=2, T=15, H=2, dk=5, dv=5, decay="channel", erase="head", write=None)
+    beta = np.repeat(e[..., None], 5, axis=-1)
+    o1, S1 = recurrence_fg2(q, k, v, ld, beta, S0)
+    o2, S2 = recurrence(q, k, v, ld, e, None, S0)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-12) and np.allclose(S1, S2, rtol=0, atol=1e-12)
+    # and a rate that differs between channels does not reduce to any scalar one
+    beta2 = beta.copy()
+    beta2[..., 0] *= 0.5
+    o3, _ = recurrence_fg2(q, k, v, ld, beta2, S0)
+    assert not np.allclose(o3, o2, atol=1e-6)
+
+
+# F3 -- the online-learning reading: with no decay, one step is the gradient step
+# S <- S - k~ (k~^T S - v~^T) on 1/2 ||S^T k~ - v~||^2 (a diagonal learning-rate matrix on the
+# original pair), so the new state reads back k~^T S_new = (1 - ||k~||^2) k~^T S + ||k~||^2 v~^T.
+def test_fg2_readback_identity():
+    r = _rng(43)
+    d = 7
+    q, k, v = r.standard_normal(d), _unit(r.standard_normal(d)), r.standard_normal(d)
+    beta = _sig(r.standard_normal(d))
+    S0 = r.standard_normal((d, d))
+    wrap = lambda x: x[None, None, None]
+    _, S = recurrence_fg2(wrap(q), wrap(k), wrap(v), wrap(np.zeros(d)), wrap(beta), S0[None, None])
+    kt, vt = np.sqrt(beta) * k, np.sqrt(beta) * v
+    n2 = kt @ kt
+    assert np.allclose(kt @ S[0, 0], (1 - n2) * (kt @ S0) + n2 * vt, rtol=0, atol=1e-12)
