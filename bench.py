@@ -69,7 +69,7 @@ def algorithmic_flops(wl) -> float:
     """Matrix flops of the chunk form per chunk of C = 64 (fixed for counting):
     symmetric gates 10 C^2 d + 6 C d^2 + C^3 / 3, separate erase/write 16 C^2 d + 8 C d^2 + C^3 / 3."""
     C, d = 64, wl.dk
-    general = wl.erase_channel or wl.write == "channel"
+    general = (wl.erase_channel and not wl.rate_sqrt) or wl.write == "channel"
     per_chunk = (16 * C * C * d + 8 * C * d * d) if general else (10 * C * C * d + 6 * C * d * d)
     per_chunk += C ** 3 / 3
     return wl.B * wl.H * (wl.T / C) * per_chunk
@@ -77,6 +77,8 @@ def algorithmic_flops(wl) -> float:
 
 def gate_desc(wl) -> str:
     decay = "per channel" if wl.decay_channel else "per head"
+    if wl.rate_sqrt:
+        return f"fp32 decay {decay}, FG2 per-channel rate (sqrt into k and v)"
     if wl.write == "channel":
         return f"fp32 decay {decay}, erase {'per channel' if wl.erase_channel else 'per head'}, write per channel"
     return f"fp32 decay {decay}, one per-head erase/write gate" if wl.decay_channel else "fp32 per head"
@@ -123,9 +125,10 @@ def time_prefill(dr, torch, wl, steps, warmup):
         x = sets[i % 2]
         if "cu_seqlens" in x:
             dr.chunk_fwd_varlen(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"], x["S0"],
-                                cu_seqlens=x["cu_seqlens"], out=o, S_T=S_T)
+                                cu_seqlens=x["cu_seqlens"], out=o, S_T=S_T, fg2=wl.rate_sqrt)
         else:
-            dr.chunk_fwd(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"], x["S0"], out=o, S_T=S_T)
+            dr.chunk_fwd(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"], x["S0"], out=o, S_T=S_T,
+                         fg2=wl.rate_sqrt)
 
     for i in range(warmup):
         step(i)
@@ -174,7 +177,7 @@ def cpu_baseline(wl, tokens):
     from threadpoolctl import threadpool_limits
 
     from gated_delta_rule_dr_amd.workloads import generate
-    from oracle import recurrence, recurrence_varlen
+    from oracle import recurrence, recurrence_fg2, recurrence_varlen
 
     sample = wl.replace(T=tokens)
     inp = generate(sample)
@@ -183,6 +186,8 @@ def cpu_baseline(wl, tokens):
         t0 = time.perf_counter()
         if "cu_seqlens" in inp:  # packed: the first `tokens` tokens, cut into the recipe's lengths
             recurrence_varlen(*args, inp["cu_seqlens"])
+        elif wl.rate_sqrt:
+            recurrence_fg2(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["S0"])
         else:
             recurrence(*args)
         sec = time.perf_counter() - t0
@@ -201,7 +206,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--all", action="store_true",
-                    help="also time the KDA, decoupled and packed-sequence prefill workloads")
+                    help="also time the KDA, FG2, decoupled and packed-sequence prefill workloads")
     ap.add_argument("--workload", default=PREFILL,
                     help="prefill workload of the main line (default: the bench workload %(default)s)")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -269,7 +274,8 @@ def main():
     }
     if args.all:
         extra = {}
-        for name in ("kda_channel_bf16_t16k", "gdn2_decoupled_bf16_t64k", "gdn_scalar_bf16_varlen_t16k"):
+        for name in ("kda_channel_bf16_t16k", "fg2_channel_bf16_t16k", "gdn2_decoupled_bf16_t64k",
+                     "gdn_scalar_bf16_varlen_t16k"):
             w2 = workload(name)
             s2, _ = time_prefill(dr, torch, w2, max(3, args.steps // 10), 2)
             extra[name] = {"tokens_per_s": w2.token_heads / s2, "ms": s2 * 1e3,

@@ -10,7 +10,10 @@ no CPU fallback: without the built library every call raises.
 The operation (per batch b and head h, state S of dk x dv in fp32):
     S' = Diag(a_t) S,   S = S' - (e_t * k_t)(k_t^T S') + k_t (w_t * v_t)^T,   o_t = S^T q_t
 with a_t = exp(log_decay_t).  Gates are per head ([B, T, H]) or per channel ([B, T, H, d]);
-``write=None`` means the write gate is the erase gate.
+``write=None`` means the write gate is the erase gate.  ``fg2=True`` reads ``erase`` as
+FG2-GDN's per-channel learning rate beta [.., dk] (dk == dv, ``write=None``), absorbed as
+k~ = sqrt(beta) k and v~ = sqrt(beta) v with unit erase and write gates:
+    S = (I - k~ k~^T) Diag(a_t) S + k~ v~^T.
 """
 from __future__ import annotations
 
@@ -65,13 +68,17 @@ def _gate_kind(name, g, lead, d):
     raise ValueError(f"{name} must have shape {lead} or {lead + (d,)}, got {tuple(g.shape)}")
 
 
-def _desc(B, T, H, dk, dv, chunk, qkv_dtype, o_dtype, log_decay, erase, write, lead):
+def _desc(B, T, H, dk, dv, chunk, qkv_dtype, o_dtype, log_decay, erase, write, lead, fg2=False):
     d = _abi.DrDesc()
     d.B, d.T, d.H, d.dk, d.dv, d.chunk = B, T, H, dk, dv, chunk
     d.qkv_dtype = _dtype_code(qkv_dtype)
     d.o_dtype = _dtype_code(o_dtype)
     d.decay_kind = _gate_kind("log_decay", log_decay, lead, dk)
     d.erase_kind = _gate_kind("erase", erase, lead, dk)
+    if fg2:
+        if d.erase_kind != _abi.DR_GATE_CHANNEL or write is not None:
+            raise ValueError("fg2: erase is the per-channel rate beta [.., dk] and write must be None")
+        d.erase_kind = _abi.DR_GATE_RATE_SQRT
     if write is None:
         d.write_is_erase, d.write_kind = 1, d.erase_kind
     else:
@@ -84,7 +91,7 @@ def workspace_bytes(desc) -> int:
 
 
 def chunk_fwd(q, k, v, log_decay, erase, write=None, S0=None, *, chunk=64,
-              o_dtype=torch.float32, out=None, S_T=None, return_state=True):
+              o_dtype=torch.float32, out=None, S_T=None, return_state=True, fg2=False):
     """Chunked forward over T tokens.
 
     q, k: [B, T, H, dk]; v: [B, T, H, dv] (bf16 or fp32, same dtype); log_decay, erase:
@@ -104,7 +111,7 @@ def chunk_fwd(q, k, v, log_decay, erase, write=None, S0=None, *, chunk=64,
     for name, t in (("log_decay", log_decay), ("erase", erase), ("write", write), ("S0", S0)):
         if t is not None:
             _check_tensor(name, t, (torch.float32,), dev)
-    desc = _desc(B, T, H, dk, dv, chunk, q.dtype, o_dtype, log_decay, erase, write, (B, T, H))
+    desc = _desc(B, T, H, dk, dv, chunk, q.dtype, o_dtype, log_decay, erase, write, (B, T, H), fg2)
     if out is None:
         out = torch.empty((B, T, H, dv), dtype=o_dtype, device=dev)
     else:
@@ -128,7 +135,8 @@ def varlen_workspace_bytes(desc, nseq) -> int:
 
 
 def chunk_fwd_varlen(q, k, v, log_decay, erase, write=None, S0=None, *, cu_seqlens, chunk=64,
-                     o_dtype=torch.float32, out=None, S_T=None, return_state=True, workspace=None):
+                     o_dtype=torch.float32, out=None, S_T=None, return_state=True, workspace=None,
+                     fg2=False):
     """Chunked forward over N packed sequences of different lengths, each from its own state.
 
     q, k: [1, T, H, dk]; v: [1, T, H, dv] with the sequences one after another on the token
@@ -155,7 +163,7 @@ def chunk_fwd_varlen(q, k, v, log_decay, erase, write=None, S0=None, *, cu_seqle
             _check_tensor(name, t, (torch.float32,), dev)
     if S0 is not None and tuple(S0.shape) != (N, H, dk, dv):
         raise ValueError(f"S0 must be [N, H, dk, dv] = {(N, H, dk, dv)}")
-    desc = _desc(1, T, H, dk, dv, chunk, q.dtype, o_dtype, log_decay, erase, write, (1, T, H))
+    desc = _desc(1, T, H, dk, dv, chunk, q.dtype, o_dtype, log_decay, erase, write, (1, T, H), fg2)
     if out is None:
         out = torch.empty((1, T, H, dv), dtype=o_dtype, device=dev)
     else:
@@ -180,7 +188,7 @@ def chunk_fwd_varlen(q, k, v, log_decay, erase, write=None, S0=None, *, cu_seqle
     return out, S_T
 
 
-def decode_step(q, k, v, log_decay, erase, write=None, *, S, o=None, o_dtype=torch.float32):
+def decode_step(q, k, v, log_decay, erase, write=None, *, S, o=None, o_dtype=torch.float32, fg2=False):
     """One decode token for N sequences: q, k [N, H, dk]; v [N, H, dv]; gates [N, H] or
     [N, H, d]; S [N, H, dk, dv] fp32 updated in place.  Returns o [N, H, dv]."""
     dev = S.device
@@ -198,7 +206,7 @@ def decode_step(q, k, v, log_decay, erase, write=None, *, S, o=None, o_dtype=tor
     for name, t in (("log_decay", log_decay), ("erase", erase), ("write", write)):
         if t is not None:
             _check_tensor(name, t, (torch.float32,), dev)
-    desc = _desc(N, 1, H, dk, dv, 0, q.dtype, o_dtype, log_decay, erase, write, (N, H))
+    desc = _desc(N, 1, H, dk, dv, 0, q.dtype, o_dtype, log_decay, erase, write, (N, H), fg2)
     if o is None:
         o = torch.empty((N, H, dv), dtype=o_dtype, device=dev)
     else:

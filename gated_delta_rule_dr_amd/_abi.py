@@ -24,6 +24,7 @@ DR_F32 = 0
 DR_BF16 = 1
 DR_GATE_HEAD = 0
 DR_GATE_CHANNEL = 1
+DR_GATE_RATE_SQRT = 2
 
 EXPORTS = (
     "dr_abi_version",

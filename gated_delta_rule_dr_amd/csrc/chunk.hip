@@ -174,8 +174,10 @@ __device__ __forceinline__ float chunk_gend(const float* GSC, int d) {
 // Every fp16 row is a run of 16-byte units (16 per 128-wide row, 8 per 64-wide row) stored
 // XOR-swizzled, unit u of row r at position u ^ swz_key<U>(r), so that the scan can copy a tile
 // into LDS as is and still read matrix-core fragments without bank conflicts.
+// With FG2's per-channel rate (VP) the packet also carries the scaled values v~ = sqrt(beta) v
+// as fp16 [64][128], row-major (the scan copies its value slice from there).
 // ------------------------------------------------------------------------------------------
-template <bool DCH, bool GEN>
+template <bool DCH, bool GEN, bool VP = false>
 struct Packet {
   static constexpr bool kScal = !DCH && !GEN;
   static constexpr int nmat = GEN ? 4 : 2;
@@ -188,7 +190,8 @@ struct Packet {
   static constexpr int umt = kmt + (kScal ? 0 : D * C * 2);
   static constexpr int gate = umt + (GEN ? D * C * 2 : 0);
   static constexpr int ngate = kScal ? 256 : 512;  // floats
-  static constexpr int bytes = gate + ngate * 4;
+  static constexpr int vt = gate + ngate * 4;
+  static constexpr int bytes = vt + (VP ? C * D * 2 : 0);
 };
 
 // XOR key of row r in a tile with U 16-byte units per row.  Measured on gfx950 (bank-conflict
@@ -319,13 +322,17 @@ __device__ void pass_state(const Problem& p, int bh, int j0, int ncols) {
 }
 
 // Per-channel decay or general gates: held to two waves per SIMD (the input prefetch would
-// otherwise take the registers of the second resident workgroup).
-template <bool DCH, bool GEN>
+// otherwise take the registers of the second resident workgroup).  FG2: the erase array holds
+// FG2-GDN's per-channel rate beta ("FG2-GDN ...", section 2, update rule), absorbed here as
+// k~ = sqrt(beta) k (every tile and Gram product takes k~) and v~ = sqrt(beta) v (into the
+// packet), with the unit gate in place of the per-token erase/write gate.
+template <bool DCH, bool GEN, bool FG2 = false>
 __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_kernel(Problem p, char* __restrict__ ws,
                                                                                      int nchunks, int64_t nblk) {
+  static_assert(!(FG2 && GEN), "the per-channel rate keeps the symmetric gates");
   // Packed sequences: the work items are (chunk, head) pairs over the chunk table.
   if (p.chunks) nblk = int64_t(p.H) * *p.nchunks_total;
-  using PK = Packet<DCH, GEN>;
+  using PK = Packet<DCH, GEN, FG2>;
   constexpr int NM = PK::nmat;
   __shared__ __attribute__((aligned(16))) _Float16 KP[C * KS];                 // K+
   __shared__ __attribute__((aligned(16))) _Float16 KM[C * KS];                 // K-
@@ -414,7 +421,7 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
     if (tid < C) {
       const int64_t ti = tok(tid);
       if constexpr (!DCH) I.lds = ldin[ti];
-      if (!erase_ch) I.gb = erin[ti];
+      if (!erase_ch && !FG2) I.gb = erin[ti];
     }
   };
 
@@ -430,9 +437,9 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
     }
   };
 
-  // Per-channel decay with general gates keeps no chunk in flight (its registers would spill);
-  // the second resident workgroup covers its load latency instead.
-  constexpr bool kPrefetch = !(DCH && GEN);
+  // Per-channel decay with general gates or with FG2's rate keeps no chunk in flight (its
+  // registers would spill); the second resident workgroup covers its load latency instead.
+  constexpr bool kPrefetch = !(DCH && GEN) && !(DCH && FG2);
   In I;
   int64_t blk = blockIdx.x;
   const int64_t gstride = gridDim.x;
@@ -445,6 +452,16 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
     _Float16* wsc = reinterpret_cast<_Float16*>(pk + PK::mat);
     float* gv = reinterpret_cast<float*>(pk + PK::gate);
     if constexpr (!kPrefetch) load_in(I, blk);
+    // FG2: this thread's rates and values, issued with the chunk's other inputs
+    float rt[FG2 ? 4 : 1][FG2 ? 8 : 1];
+    uint4 vr[FG2 ? 4 : 1];
+    if constexpr (FG2) {
+      const gptr<const uint16_t> vin = opaque_gptr(static_cast<const uint16_t*>(p.v));
+      load_err(rt, cr);
+      const auto tok = tok_of(cr);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vr[r] = gload_u4(vin, tok(4 * tg + r) * D + 8 * d8);
+    }
     vm_wait_all();  // this chunk's inputs (loaded one chunk ago) and the older stores
 
     // ---- inputs, masked past the last token --------------------------------------------
@@ -470,11 +487,31 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
         for (int ch = 0; ch < 8; ++ch) err[r][ch] = (ok && erase_ch) ? (kPrefetchErr ? I.err[r][ch] : en[r][ch]) : 0.f;
       }
     }
+    // FG2: k~ = sqrt(beta) k replaces k (held as fp16 from here on) and v~ = sqrt(beta) v goes
+    // to the packet, right away, so that neither the rates nor the values stay in registers.
+    // Rows past the end are zero.
+    if constexpr (FG2) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = 4 * tg + r < cr.tlen;
+        float kf[8], vf[8];
+        bf16x8_to_f32(kr[r], kf);
+        bf16x8_to_f32(vr[r], vf);
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) {
+          const float s = ok ? sqrtf(rt[r][ch]) : 0.f;
+          kf[ch] *= s;
+          vf[ch] *= s;
+        }
+        kr[r] = __builtin_bit_cast(uint4, cvt8(kf));
+        *reinterpret_cast<half8*>(pk + PK::vt + 2 * ((4 * tg + r) * D + 8 * d8)) = cvt8(vf);
+      }
+    }
     float lds = 0.f;
     if (tid < C) {
       const bool ok = tid < cr.tlen;
       if constexpr (!DCH) lds = ok ? I.lds : 0.f;
-      GB[tid] = (ok && !erase_ch) ? I.gb : 0.f;
+      GB[tid] = (ok && !erase_ch) ? (FG2 ? 1.f : I.gb) : 0.f;
     }
 
     float g[4][DCH ? 8 : 1];
@@ -488,7 +525,13 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * tg + r;
         float kf[8], qf[8], kp[8], km[8], qp[8];
-        bf16x8_to_f32(kr[r], kf);
+        if constexpr (FG2) {  // k~, fp16
+          const half8 h = __builtin_bit_cast(half8, kr[r]);
+#pragma unroll
+          for (int ch = 0; ch < 8; ++ch) kf[ch] = float(h[ch]);
+        } else {
+          bf16x8_to_f32(kr[r], kf);
+        }
         bf16x8_to_f32(qr[r], qf);
         if constexpr (PK::kScal) {
           // scalar decay: plain k and q, in LDS for the Gram products (which take the decay per
@@ -1148,9 +1191,11 @@ __device__ __forceinline__ half8 frag_ts(const _Float16* base, int d0, int t0, i
   return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-template <bool DCH, int DVS>
+// FG2: the values are FG2's v~ = sqrt(beta) v, fp16 in the packet, instead of the bf16 input.
+template <bool DCH, int DVS, bool FG2 = false>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p, const char* __restrict__ ws) {
-  using PK = Packet<DCH, false>;
+  using PK = Packet<DCH, false, FG2>;
+  auto vval = [](uint16_t u) { return FG2 ? float(__builtin_bit_cast(_Float16, u)) : bf16_to_f32(u); };
   constexpr bool SCAL = !DCH;
   constexpr int NCT = DVS / 16;  // 16-column tiles of the value slice
   constexpr int VU = DVS / 8;    // 16-byte units per value-slice row
@@ -1287,7 +1332,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
     const bool ok = c * C + vt < T;
     const int64_t e = ok ? v_off + c * tstride : v_last;
-    const gptr<const char> src = x_vs ? vin + 2 * e : pk + PK::gate + (x_off - o_gv) + 16 * lane;
+    const gptr<const char> src = !x_vs ? pk + PK::gate + (x_off - o_gv) + 16 * lane
+                                 : FG2  ? pk + PK::vt + 2 * (vt * D + j0 + vc)
+                                        : vin + 2 * e;
     dma16(src, reinterpret_cast<char*>(X.qp) + x_off);
   };
   auto fetch_k = [&](const Set& X, int c) {
@@ -1459,7 +1506,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float x = SCAL ? xk[r] * fkr[r] : xk[r];
-        hv[r] = (_Float16)(beta[r] * (bf16_to_f32(uint16_t(vr[r])) - x));
+        hv[r] = (_Float16)(beta[r] * (vval(uint16_t(vr[r])) - x));
         XQ[r] = SCAL ? xq[r] * fq : xq[r];
       }
       *reinterpret_cast<half4v*>(RT + swz<8>(16 * xct + l16, xrow + 4 * lg)) = hv;
@@ -1529,7 +1576,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
         for (int ct = 0; ct < NCT; ++ct) {
           half4v hv;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(beta[r] * (bf16_to_f32(uint16_t(vr[ct][r])) - XR[ct][r]));
+          for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(beta[r] * (vval(uint16_t(vr[ct][r])) - XR[ct][r]));
           *reinterpret_cast<half4v*>(RT + swz<8>(16 * ct + l16, xrow + 4 * lg)) = hv;
         }
       }
@@ -1660,10 +1707,10 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   }
 }
 
-template <bool DCH, int DVS>
+template <bool DCH, int DVS, bool FG2>
 hipError_t launch_scan_sym(const Problem& p, const char* ws, hipStream_t stream) {
   dim3 grid(unsigned(p.B * p.H), unsigned(D / DVS));
-  hipLaunchKernelGGL((chunk_scan_sym_kernel<DCH, DVS>), grid, dim3(kScanThreads), 0, stream, p, ws);
+  hipLaunchKernelGGL((chunk_scan_sym_kernel<DCH, DVS, FG2>), grid, dim3(kScanThreads), 0, stream, p, ws);
   return hipGetLastError();
 }
 
@@ -1677,7 +1724,7 @@ hipError_t launch_scan_gen(const Problem& p, const char* ws, hipStream_t stream)
   return hipGetLastError();
 }
 
-template <bool DCH, bool GEN>
+template <bool DCH, bool GEN, bool FG2 = false>
 hipError_t launch_variant(const Problem& p, void* workspace, hipStream_t stream) {
   const int nchunks = (p.T + C - 1) / C;
   char* ws = static_cast<char*>(workspace);
@@ -1692,7 +1739,7 @@ hipError_t launch_variant(const Problem& p, void* workspace, hipStream_t stream)
     return hipErrorInvalidDevice;
   const int64_t resident = int64_t(ncu) * 2;
   const int64_t grid = nblk < resident ? nblk : resident;
-  hipLaunchKernelGGL((chunk_prep_kernel<DCH, GEN>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p, ws, nchunks,
+  hipLaunchKernelGGL((chunk_prep_kernel<DCH, GEN, FG2>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p, ws, nchunks,
                      nblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1702,11 +1749,12 @@ hipError_t launch_variant(const Problem& p, void* workspace, hipStream_t stream)
   if constexpr (GEN) {
     return bh >= 64 ? launch_scan_gen<DCH, 32>(p, ws, stream) : launch_scan_gen<DCH, 16>(p, ws, stream);
   } else {
-    return bh >= 64 ? launch_scan_sym<DCH, 32>(p, ws, stream) : launch_scan_sym<DCH, 16>(p, ws, stream);
+    return bh >= 64 ? launch_scan_sym<DCH, 32, FG2>(p, ws, stream) : launch_scan_sym<DCH, 16, FG2>(p, ws, stream);
   }
 }
 
-int64_t packet_bytes(bool symmetric, bool decay_channel) {
+int64_t packet_bytes(bool symmetric, bool decay_channel, bool rate_sqrt) {
+  if (rate_sqrt) return decay_channel ? Packet<true, false, true>::bytes : Packet<false, false, true>::bytes;
   return !symmetric ? Packet<true, true>::bytes : decay_channel ? Packet<true, false>::bytes : Packet<false, false>::bytes;
 }
 
@@ -1714,23 +1762,23 @@ int64_t round256(int64_t n) { return (n + 255) / 256 * 256; }
 
 }  // namespace
 
-size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric, bool decay_channel) {
+size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric, bool decay_channel, bool rate_sqrt) {
   const int64_t nchunks = (int64_t(T) + C - 1) / C;
-  return size_t(int64_t(B) * H * nchunks * packet_bytes(symmetric, decay_channel));
+  return size_t(int64_t(B) * H * nchunks * packet_bytes(symmetric, decay_channel, rate_sqrt));
 }
 
 // Packed sequences: packets of at most varlen_max_chunks chunks per head, then the chunk
 // table, the sequence table, the sequence order and the chunk count.
-size_t chunk128_varlen_workspace_bytes(int nseq, int T, int H, bool symmetric, bool decay_channel) {
+size_t chunk128_varlen_workspace_bytes(int nseq, int T, int H, bool symmetric, bool decay_channel, bool rate_sqrt) {
   const int64_t maxc = varlen_max_chunks(nseq, T);
-  return size_t(int64_t(H) * maxc * packet_bytes(symmetric, decay_channel) + round256(maxc * 16) +
+  return size_t(int64_t(H) * maxc * packet_bytes(symmetric, decay_channel, rate_sqrt) + round256(maxc * 16) +
                 round256(int64_t(nseq) * 16) + round256(int64_t(nseq) * 4) + 256);
 }
 
 hipError_t launch_chunk128_varlen(Problem p, const int* cu, void* workspace, hipStream_t stream) {
   const int64_t maxc = varlen_max_chunks(p.B, p.T);
   char* ws = static_cast<char*>(workspace);
-  char* tables = ws + int64_t(p.H) * maxc * packet_bytes(p.symmetric, p.decay_channel);
+  char* tables = ws + int64_t(p.H) * maxc * packet_bytes(p.symmetric, p.decay_channel, p.rate_sqrt);
   int4* chunks = reinterpret_cast<int4*>(tables);
   int4* seqs = reinterpret_cast<int4*>(tables + round256(maxc * 16));
   int* order = reinterpret_cast<int*>(tables + round256(maxc * 16) + round256(int64_t(p.B) * 16));
@@ -1745,6 +1793,9 @@ hipError_t launch_chunk128_varlen(Problem p, const int* cu, void* workspace, hip
 }
 
 hipError_t launch_chunk128(const Problem& p, void* workspace, hipStream_t stream) {
+  if (p.rate_sqrt)  // FG2's per-channel rate keeps the symmetric gates
+    return p.decay_channel ? launch_variant<true, false, true>(p, workspace, stream)
+                           : launch_variant<false, false, true>(p, workspace, stream);
   const bool symmetric = p.symmetric;
   if (p.decay_channel)
     return symmetric ? launch_variant<true, false>(p, workspace, stream)

@@ -4,7 +4,8 @@
 // Constant-memory decode is the point of the fixed-size state ("Gated DeltaNet-2 ...", the
 // attention bottleneck: decoding uses constant memory; "KronLSTM ...", The problem).  The step
 // is the general one:  S' = Diag(a) S,  S_new = S' - (e*k) m^T + k (w*v)^T with m = S'^T k,
-// o = S_new^T q.  Expanding the read of the new state avoids a second pass over S:
+// o = S_new^T q (FG2's per-channel rate beta scales k and v by sqrt(beta) instead, with unit
+// erase and write gates).  Expanding the read of the new state avoids a second pass over S:
 //   o = S'^T q - m (u . q) + (w*v) (k . q),   u = e * k,
 // so both column reductions over dk (m = S'^T k and p = S'^T q) come from one read of S.
 //
@@ -45,15 +46,22 @@ __global__ __launch_bounds__(kThreads) void decode128_kernel(Problem p) {
   if (tid < D) {
     const int i = tid;
     const int64_t o = nh * D + i;
-    const float kk = load_qkv(p.k, o, kBf16);
+    float kk = load_qkv(p.k, o, kBf16);
+    float e = kEraseCh ? p.erase[o] : p.erase[nh];
+    if (kEraseCh && p.rate_sqrt) {  // FG2's rate: k~ = sqrt(beta) k, unit erase
+      kk *= sqrtf(e);
+      e = 1.f;
+    }
     s_k[i] = kk;
     s_q[i] = load_qkv(p.q, o, kBf16);
     s_a[i] = expf(kDecayCh ? p.log_decay[o] : p.log_decay[nh]);
-    s_u[i] = (kEraseCh ? p.erase[o] : p.erase[nh]) * kk;
+    s_u[i] = e * kk;
   } else {
     const int j = tid - D;
     const int64_t o = nh * D + j;
-    s_wv[j] = (kWriteCh ? p.write[o] : p.write[nh]) * load_qkv(p.v, o, kBf16);
+    float w = kWriteCh ? p.write[o] : p.write[nh];
+    if (kWriteCh && p.rate_sqrt) w = sqrtf(w);  // v~ = sqrt(beta) v, unit write
+    s_wv[j] = w * load_qkv(p.v, o, kBf16);
   }
   __syncthreads();
 

@@ -51,11 +51,13 @@ int check_desc(const dr_desc* d, bool decode, Extents* ex) {
   if (d->qkv_dtype != DR_F32 && d->qkv_dtype != DR_BF16) return DR_E_DTYPE;
   if (d->o_dtype != DR_F32 && d->o_dtype != DR_BF16) return DR_E_DTYPE;
   auto kind_ok = [](int k) { return k == DR_GATE_HEAD || k == DR_GATE_CHANNEL; };
-  if (!kind_ok(d->decay_kind) || !kind_ok(d->erase_kind)) return DR_E_DTYPE;
+  const bool rate = d->erase_kind == DR_GATE_RATE_SQRT;
+  if (!kind_ok(d->decay_kind) || !(kind_ok(d->erase_kind) || rate)) return DR_E_DTYPE;
   if (!d->write_is_erase && !kind_ok(d->write_kind)) return DR_E_DTYPE;
+  if (rate && !d->write_is_erase) return DR_E_DTYPE;
   if (!supported_width(d->dk) || !supported_width(d->dv)) return DR_E_UNSUPPORTED;
   if (!decode && d->chunk != 0 && d->chunk != 1 && d->chunk != 64) return DR_E_UNSUPPORTED;
-  if (d->write_is_erase && d->erase_kind == DR_GATE_CHANNEL && d->dk != d->dv) return DR_E_SHAPE;
+  if (d->write_is_erase && d->erase_kind != DR_GATE_HEAD && d->dk != d->dv) return DR_E_SHAPE;
 
   const uint64_t B = uint64_t(d->B), T = uint64_t(d->T), H = uint64_t(d->H);
   const uint64_t dk = uint64_t(d->dk), dv = uint64_t(d->dv);
@@ -69,7 +71,7 @@ int check_desc(const dr_desc* d, bool decode, Extents* ex) {
   ex->v = bth * dv * qkv_sz;
   ex->o = bth * dv * o_sz;
   ex->decay = bth * (d->decay_kind == DR_GATE_CHANNEL ? dk : 1) * 4;
-  ex->erase = bth * (d->erase_kind == DR_GATE_CHANNEL ? dk : 1) * 4;
+  ex->erase = bth * (d->erase_kind != DR_GATE_HEAD ? dk : 1) * 4;
   if (d->write_is_erase)
     ex->write = 0;
   else
@@ -100,7 +102,8 @@ dr::Problem make_problem(const dr_desc* d, const void* q, const void* k, const v
   p.qkv_bf16 = d->qkv_dtype == DR_BF16;
   p.o_bf16 = d->o_dtype == DR_BF16;
   p.decay_channel = d->decay_kind == DR_GATE_CHANNEL;
-  p.erase_channel = d->erase_kind == DR_GATE_CHANNEL;
+  p.erase_channel = d->erase_kind != DR_GATE_HEAD;
+  p.rate_sqrt = d->erase_kind == DR_GATE_RATE_SQRT;
   p.write_channel = d->write_is_erase ? p.erase_channel : (d->write_kind == DR_GATE_CHANNEL);
   p.q = q;
   p.k = k;
@@ -151,7 +154,8 @@ size_t dr_chunk_fwd_workspace_bytes(const dr_desc* desc) {
   if (check_desc(desc, false, &ex) != DR_OK) return 0;
   if (!uses_chunk128(desc)) return 0;
   return dr::chunk128_workspace_bytes(desc->B, desc->T, desc->H, is_symmetric(desc),
-                                      desc->decay_kind == DR_GATE_CHANNEL);
+                                      desc->decay_kind == DR_GATE_CHANNEL,
+                                      desc->erase_kind == DR_GATE_RATE_SQRT);
 }
 
 int dr_chunk_fwd(const dr_desc* d, const void* q, const void* k, const void* v,
@@ -202,7 +206,8 @@ size_t dr_chunk_fwd_varlen_workspace_bytes(const dr_desc* desc, int32_t nseq) {
   if (check_desc(desc, false, &ex) != DR_OK || desc->B != 1 || nseq <= 0 || nseq > kMaxSeqs) return 0;
   if (uses_chunk128(desc))
     return dr::chunk128_varlen_workspace_bytes(nseq, desc->T, desc->H, is_symmetric(desc),
-                                               desc->decay_kind == DR_GATE_CHANNEL);
+                                               desc->decay_kind == DR_GATE_CHANNEL,
+                                               desc->erase_kind == DR_GATE_RATE_SQRT);
   return dr::recurrent_varlen_workspace_bytes(nseq);
 }
 

@@ -17,6 +17,8 @@ struct Problem {
   int erase_channel;   // erase is [B,T,H,dk]
   int write_channel;   // write is [B,T,H,dv]
   int symmetric;       // one per-head gate is both erase and write (write is erase)
+  int rate_sqrt;       // erase is a per-channel rate beta absorbed as sqrt(beta) into k and v
+                       // (the update then erases and writes with the unit gate); write is erase
   const void* q;
   const void* k;
   const void* v;
@@ -54,15 +56,15 @@ hipError_t launch_recurrent(const Problem& p, hipStream_t stream);
 hipError_t launch_decode128(const Problem& p, hipStream_t stream);
 
 // MFMA chunked forward, bf16 q/k/v, dk == dv == 128, chunk 64.  `workspace` holds at least
-// chunk128_workspace_bytes(B, T, H, symmetric, decay_channel) bytes: one packet of
+// chunk128_workspace_bytes(B, T, H, symmetric, decay_channel, rate_sqrt) bytes: one packet of
 // state-independent factors per chunk of every (b, h).
-size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric, bool decay_channel);
+size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric, bool decay_channel, bool rate_sqrt);
 hipError_t launch_chunk128(const Problem& p, void* workspace, hipStream_t stream);
 
 // The same over p.B packed sequences delimited by the device offsets `cu` (p.B + 1 of them):
 // the workspace holds the packets of at most varlen_max_chunks(p.B, p.T) chunks per head,
 // then the sequence tables.
-size_t chunk128_varlen_workspace_bytes(int nseq, int T, int H, bool symmetric, bool decay_channel);
+size_t chunk128_varlen_workspace_bytes(int nseq, int T, int H, bool symmetric, bool decay_channel, bool rate_sqrt);
 hipError_t launch_chunk128_varlen(Problem p, const int* cu, void* workspace, hipStream_t stream);
 
 // The token-by-token kernel over packed sequences: the workspace holds the sequence table.

@@ -6,7 +6,8 @@
 // the key side, write on the value side, channel decay from KDA; "FG2-GDN ...", section 2,
 // update rule).  It serves the fp32 workloads, widths the matrix-core path does not cover,
 // chunk == 1, and decode steps of other widths (in place: every state element is read and
-// written by the same lane).  Over packed sequences of different lengths each workgroup takes
+// written by the same lane).  FG2's per-channel rate beta ("FG2-GDN ...", section 2, update
+// rule) scales k and v by sqrt(beta) as they are loaded and leaves unit erase and write gates.  Over packed sequences of different lengths each workgroup takes
 // its sequence's first token and length from the sequence table.
 //
 // Mapping: one wave per (b, h, group of 16 value columns).  Lane = column c (16) x row group
@@ -115,7 +116,16 @@ __global__ __launch_bounds__(64) void recurrent_kernel(Problem p) {
       for (int r = 0; r < RPL; ++r) er[r] = e;
     }
     const float vj = load_qkv(p.v, tok * dv + j, bf);
-    const float wj = p.write_channel ? p.write[tok * dv + j] : p.write[tok];
+    float wj = p.write_channel ? p.write[tok * dv + j] : p.write[tok];
+    if (p.rate_sqrt) {
+      // FG2's per-channel rate: key and value scaled by sqrt(beta), unit erase and write
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        kr[r] *= sqrtf(er[r]);
+        er[r] = 1.f;
+      }
+      wj = sqrtf(wj);
+    }
 
     float m = 0.f;
 #pragma unroll

@@ -55,6 +55,7 @@ class Workload:
     steps: int = 0  # decode workloads: number of single-token steps
     seq_median: int = 0  # packed workloads: median sequence length (0: a dense [B, T] batch)
     seq_max: int = 0  # packed workloads: longest sequence
+    rate_sqrt: bool = False  # the per-channel erase gate is FG2-GDN's rate beta (sqrt into k and v)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -81,6 +82,10 @@ WORKLOADS = {
         # decoupled per-channel erase / write (Gated DeltaNet-2, FG2-GDN+) long-context prefill
         Workload("gdn2_decoupled_bf16_t64k", 1, 65536, 32, 128, 128, "bf16", "softplus", True,
                  -4.0, 1.5, True, "channel", 0.0, 4),
+        # FG2-GDN prefill at the KDA workload's shape: channel decay and a per-channel rate
+        # beta = sigmoid(N(0, 1)) absorbed as sqrt(beta) into k and v
+        Workload("fg2_channel_bf16_t16k", 2, 16384, 32, 128, 128, "bf16", "softplus", True, -4.0,
+                 1.5, True, "erase", 0.0, 7, rate_sqrt=True),
         # serving prefill: scalar-gate Gated DeltaNet over 16384 packed tokens of sequences of
         # mixed lengths (median 512, at most 4096), 16 heads
         Workload("gdn_scalar_bf16_varlen_t16k", 1, 16384, 16, 128, 128, "bf16", "softplus", False,

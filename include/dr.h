@@ -65,8 +65,15 @@ typedef enum {
 typedef enum { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
 
 typedef enum {
-  DR_GATE_HEAD = 0,    /* one fp32 value per (b, t, h): [B, T, H] */
-  DR_GATE_CHANNEL = 1  /* one fp32 value per channel: [B, T, H, dk] (decay, erase) or dv (write) */
+  DR_GATE_HEAD = 0,     /* one fp32 value per (b, t, h): [B, T, H] */
+  DR_GATE_CHANNEL = 1,  /* one fp32 value per channel: [B, T, H, dk] (decay, erase) or dv (write) */
+  DR_GATE_RATE_SQRT = 2 /* erase only: FG2-GDN's per-channel learning rate beta [B, T, H, dk],
+                           absorbed symmetrically into key and value, k~ = sqrt(beta) * k and
+                           v~ = sqrt(beta) * v, after which the update erases and writes with the
+                           unit gate: S_t = (I - k~ k~^T) Diag(a_t) S_{t-1} + k~ v~^T ("FG2-GDN
+                           ...", section 2, FG2-GDN update rule).  Needs write_is_erase != 0
+                           (DR_E_DTYPE otherwise) and dk == dv (DR_E_SHAPE otherwise); q is not
+                           scaled. */
 } dr_gate_kind;
 
 /* Problem descriptor.  All fields are 32-bit integers so the struct has one layout on every
@@ -97,7 +104,9 @@ const char* dr_status_str(int status);
  * blocks), the gate factors, and the fp16 key/query tiles (decayed, plus the transposed decayed
  * keys, unless the decay is per head with one per-head gate for erase and write).  That is
  * B * H * ceil(T / 64) * P bytes with P = 46080 (per-head decay, one per-head erase/write gate),
- * 63488 (per-channel decay, one per-head erase/write gate) or 92160 (otherwise); the
+ * 63488 (per-channel decay, one per-head erase/write gate), 62464 (per-head decay,
+ * DR_GATE_RATE_SQRT) or 79872 (per-channel decay, DR_GATE_RATE_SQRT; these two add the scaled
+ * values v~ as fp16 [64][128]) or 92160 (otherwise); the
  * token-by-token path needs none.  The caller allocates it
  * (any device memory, 16-byte aligned, not overlapping the other arguments) and may reuse it
  * once the call's work has finished. */

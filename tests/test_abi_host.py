@@ -222,3 +222,28 @@ def test_varlen_argument_errors():
     # to validate but one inside them is not
     state = 3 * 4 * 128 * 128 * 4
     assert _vfwd(d, ST=P["S0"] + state - 16) == _abi.DR_E_ALIAS
+
+
+# ---- FG2's per-channel rate (erase kind DR_GATE_RATE_SQRT) ----------------------------------------
+def test_rate_sqrt_kind():
+    L = _abi.lib()
+    R = _abi.DR_GATE_RATE_SQRT
+    # symmetric packets plus the scaled values v~ as fp16 [64][128]
+    scal = 2 * 6 * 16 * 32 * 2 + 2 * 64 * 128 * 2 + 256 * 4 + 64 * 128 * 2
+    kda = 2 * 6 * 16 * 32 * 2 + 3 * 64 * 128 * 2 + 512 * 4 + 64 * 128 * 2
+    assert (scal, kda) == (62464, 79872)
+    d = _good_desc(erase_kind=R)
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(d)) == 2 * 4 * 2 * scal
+    dc = _good_desc(erase_kind=R, decay_kind=_abi.DR_GATE_CHANNEL)
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(dc)) == 2 * 4 * 2 * kda
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(erase_kind=R, chunk=1))) == 0
+    # the rate is read per channel of dk: passes validation of the extents (fake pointers fail later)
+    assert _fwd(_good_desc(erase_kind=R), e=P["e"] + 8) == _abi.DR_E_ALIGN
+    # needs write == erase and dk == dv; only the erase gate takes this kind
+    assert _fwd(_good_desc(erase_kind=R, write_is_erase=0)) == _abi.DR_E_DTYPE
+    assert _fwd(_good_desc(erase_kind=R, dk=64)) == _abi.DR_E_SHAPE
+    assert _fwd(_good_desc(decay_kind=R)) == _abi.DR_E_DTYPE
+    assert _fwd(_good_desc(write_is_erase=0, write_kind=R)) == _abi.DR_E_DTYPE
+    # a per-channel extent: the rate array overlapping o by one channel row is an alias
+    rate_bytes = 2 * 100 * 4 * 128 * 4
+    assert _fwd(_good_desc(erase_kind=R), o=P["e"] + rate_bytes - 512) == _abi.DR_E_ALIAS

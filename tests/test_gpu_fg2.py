@@ -1,0 +1,124 @@
+"""GPU parity of FG2-GDN's per-channel rate (erase kind DR_GATE_RATE_SQRT) against the fp64 oracle.
+
+The rate beta in R^dk is absorbed as sqrt(beta) into key and value inside the kernels
+("FG2-GDN ...", section 2, FG2-GDN update rule); the oracle is oracle.recurrence_fg2.
+Tolerances as elsewhere: 3e-3 normwise for the bf16 matrix-core chunk path, 1e-5 for the fp32
+token-by-token kernel and the decode step."""
+import numpy as np
+import pytest
+import torch
+
+from metrics import err_S, err_o
+from oracle import recurrence_fg2
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 3e-3
+
+
+@pytest.fixture(scope="module")
+def dr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_dr_amd as m
+
+    m.abi_version()
+    return m
+
+
+def _case(B, T, H, d, dtype, decay_channel, s0, seed):
+    from gated_delta_rule_dr_amd.workloads import Workload, generate
+
+    wl = Workload("case", B, T, H, d, d, dtype, "softplus", decay_channel, -4.0, 1.5, True, "erase",
+                  0.05 if s0 else 0.0, seed, rate_sqrt=True)
+    return generate(wl)
+
+
+def _run(dr, inp, chunk=64):
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    o, S = dr.chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], None, d["S0"], chunk=chunk, fg2=True)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def _oracle(inp):
+    return recurrence_fg2(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["S0"])
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
+@pytest.mark.parametrize("decay_channel", [True, False])
+def test_fg2_chunk_path(dr, T, decay_channel):
+    inp = _case(1, T, 2, 128, "bf16", decay_channel, T % 2 == 1, 50 + T)
+    o, S = _run(dr, inp)
+    ro, rS = _oracle(inp)
+    eo, eS = err_o(o, ro), err_S(S, rS)
+    print(f"fg2 chunk decay_channel={decay_channel} T={T}: err_o={eo:.3e} err_S={eS:.3e}")
+    assert eo <= TOL_BF16 and eS <= TOL_BF16, (eo, eS)
+
+
+@pytest.mark.parametrize("B,H,T", [(1, 64, 150), (2, 3, 300)])
+@pytest.mark.parametrize("decay_channel", [True, False])
+def test_fg2_chunk_path_slice_widths(dr, B, H, T, decay_channel):
+    # B*H >= 64 runs 32-column value slices, fewer 16-column ones
+    inp = _case(B, T, H, 128, "bf16", decay_channel, True, 60 + T + H)
+    o, S = _run(dr, inp)
+    ro, rS = _oracle(inp)
+    eo, eS = err_o(o, ro), err_S(S, rS)
+    print(f"fg2 chunk decay_channel={decay_channel} B={B} H={H} T={T}: err_o={eo:.3e} err_S={eS:.3e}")
+    assert eo <= TOL_BF16 and eS <= TOL_BF16, (eo, eS)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 32), ("bf16", 64), ("bf16", 128)])
+def test_fg2_token_path(dr, dtype, d):
+    inp = _case(2, 37, 3, d, dtype, True, True, 70 + d)
+    o, S = _run(dr, inp, chunk=1)
+    ro, rS = _oracle(inp)
+    eo, eS = err_o(o, ro), err_S(S, rS)
+    assert eo <= TOL_F32 and eS <= TOL_F32, (eo, eS)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fg2_decode_steps(dr, d):
+    # decode steps continue a state exactly as the recurrence does (128: the streaming decode
+    # kernel; 64: the token kernel in place)
+    inp = _case(4, 5, 3, d, "bf16", True, True, 80 + d)
+    S = inp["S0"].clone().cuda()
+    for t in range(5):
+        g = lambda key: inp[key][:, t].contiguous().cuda()
+        o = dr.decode_step(g("q"), g("k"), g("v"), g("log_decay"), g("erase"), S=S, fg2=True)
+        torch.cuda.synchronize()
+        cut = lambda key: inp[key][:, :t + 1]
+        ro, rS = recurrence_fg2(cut("q"), cut("k"), cut("v"), cut("log_decay"), cut("erase"), inp["S0"])
+        assert err_o(o[:, None], ro[:, -1:]) <= TOL_F32
+    assert err_S(S, rS) <= TOL_F32
+
+
+def test_fg2_packed_sequences(dr):
+    lens = [0, 70, 1, 129]
+    inp = _case(1, sum(lens), 4, 128, "bf16", True, False, 90)
+    g = torch.Generator().manual_seed(91)
+    S0 = (0.05 * torch.randn((len(lens), 4, 128, 128), generator=g, dtype=torch.float64)).float()
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    o, S = dr.chunk_fwd_varlen(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], None, S0.cuda(),
+                               cu_seqlens=torch.tensor(cu, dtype=torch.int32, device="cuda"), fg2=True)
+    torch.cuda.synchronize()
+    for n in range(len(lens)):
+        lo, hi = int(cu[n]), int(cu[n + 1])
+        if hi == lo:
+            assert torch.equal(S[n].cpu(), S0[n])
+            continue
+        cut = lambda key: inp[key][:, lo:hi]
+        ro, rS = recurrence_fg2(cut("q"), cut("k"), cut("v"), cut("log_decay"), cut("erase"), S0[n:n + 1])
+        eo, eS = err_o(o[:, lo:hi], ro), err_S(S[n:n + 1], rS)
+        assert eo <= TOL_BF16 and eS <= TOL_BF16, (n, eo, eS)
+
+
+def test_fg2_rejects_mismatched_gates(dr):
+    inp = _case(1, 10, 2, 128, "bf16", True, False, 92)
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    with pytest.raises(ValueError):  # a per-head gate is no per-channel rate
+        dr.chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"][..., 0].contiguous(), fg2=True)
+    with pytest.raises(ValueError):  # FG2's rate is the write gate too
+        dr.chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["erase"], fg2=True)

@@ -12,7 +12,7 @@ import torch
 
 from metrics import err_S, err_o
 from oracle import decode_step as oracle_decode
-from oracle import recurrence
+from oracle import recurrence, recurrence_fg2
 
 pytestmark = pytest.mark.gpu
 
@@ -40,6 +40,7 @@ def _slice(x, b, h):
 @pytest.mark.parametrize("name,pairs", [
     ("gdn_scalar_bf16_t4k", [(0, 0), (1, 7), (3, 15)]),
     ("kda_channel_bf16_t16k", [(0, 0), (1, 31)]),
+    ("fg2_channel_bf16_t16k", [(0, 0), (1, 31)]),
     ("gdn2_decoupled_bf16_t64k", [(0, 0), (0, 31)]),
 ])
 def test_prefill_full_size_sampled_heads(dr, name, pairs):
@@ -50,13 +51,16 @@ def test_prefill_full_size_sampled_heads(dr, name, pairs):
     o = torch.empty((wl.B, wl.T, wl.H, wl.dv), device="cuda")
     S_T = torch.empty((wl.B, wl.H, wl.dk, wl.dv), device="cuda")
     dr.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"], inp["S0"],
-                 out=o, S_T=S_T)
+                 out=o, S_T=S_T, fg2=wl.rate_sqrt)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(S_T).all()
     print(f"{name}: |o|max={o.abs().max().item():.3g} |S_T|max={S_T.abs().max().item():.3g}", flush=True)
     for b, h in pairs:
         sl = {k: _slice(v, b, h) for k, v in inp.items()}
-        ro, rS = recurrence(sl["q"], sl["k"], sl["v"], sl["log_decay"], sl["erase"], sl["write"], sl["S0"])
+        if wl.rate_sqrt:
+            ro, rS = recurrence_fg2(sl["q"], sl["k"], sl["v"], sl["log_decay"], sl["erase"], sl["S0"])
+        else:
+            ro, rS = recurrence(sl["q"], sl["k"], sl["v"], sl["log_decay"], sl["erase"], sl["write"], sl["S0"])
         eo = err_o(o[b:b + 1, :, h:h + 1], ro)
         eS = err_S(S_T[b:b + 1, h:h + 1], rS)
         print(f"{name} (b={b}, h={h}): err_o={eo:.3e} err_S={eS:.3e}", flush=True)
