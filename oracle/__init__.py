@@ -12,8 +12,10 @@ norm bound and the dk = dv = 1 closed form; for packed sequences, equality with 
 batch at equal lengths, isolation between sequences, empty sequences, split invariance (the
 prefill-to-decode handoff) and the one-token closed form; for FG2's per-channel rate, its
 explicit matrix form, the KDA form at a channel-constant rate, and the gradient-step reading
-with a diagonal learning-rate matrix.  No function here is "parity unpinned".
+with a diagonal learning-rate matrix; for the gradients (recurrence_bwd), central finite
+differences of the forward along random directions and torch autograd through a separately
+written torch forward.  No function here is "parity unpinned".
 """
-from .recurrence import as_f64, decode_step, recurrence, recurrence_fg2, recurrence_varlen
+from .recurrence import as_f64, decode_step, recurrence, recurrence_bwd, recurrence_fg2, recurrence_varlen
 
-__all__ = ["recurrence", "recurrence_fg2", "recurrence_varlen", "decode_step", "as_f64"]
+__all__ = ["recurrence", "recurrence_bwd", "recurrence_fg2", "recurrence_varlen", "decode_step", "as_f64"]

@@ -41,7 +41,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["recurrence", "recurrence_fg2", "recurrence_varlen", "decode_step", "as_f64"]
+__all__ = ["recurrence", "recurrence_bwd", "recurrence_fg2", "recurrence_varlen", "decode_step", "as_f64"]
 
 
 def as_f64(x):
@@ -122,6 +122,100 @@ def recurrence(q, k, v, log_decay, erase, write=None, S0=None, return_states=Fal
     if return_states:
         return o, S, states
     return o, S
+
+
+def recurrence_bwd(q, k, v, log_decay, erase, write=None, S0=None, dO=None, dS_T=None):
+    """Gradients of the recurrence, by the adjoint of the token loop, in fp64.
+
+    The forward pass of training is the recurrence itself (the chunked form is how it is
+    evaluated fast, "FG2-GDN ...", sections 2-3: chunk-parallel training through the WY form);
+    its gradients are those of the scalar objective L = sum(o * dO) + sum(S_T * dS_T).  Walking
+    the tokens backwards with the state's adjoint G = dL/dS_t (starting from dS_T), one token
+    t of the forward step
+
+        S' = Diag(a) S_{t-1},  m = S'^T k,  u = e * k,  v~ = w * v,
+        S_t = S' - u m^T + k v~^T,  o_t = S_t^T q_t
+
+    contributes, in reverse order:
+        G    += q dO_t^T                       dq_t = S_t dO_t
+        dm    = -G^T u                         du   = -G m          dv~ = G^T k
+        dk_t  = G v~ + S' dm + e * du          de_t = k * du        (summed over channels
+        dw_t  = v * dv~                        dv_t = w * dv~        for a per-head gate)
+        G'    = G + k dm^T                     d(log a_t) = a * rowsum(G' * S_{t-1})
+        G     = Diag(a) G'                     (the adjoint of S_{t-1});  dS0 = G at the end.
+    With ``write=None`` the gate is shared, so its gradient is de + dw.
+
+    Args: as ``recurrence``, plus dO [B, T, H, dv] and dS_T [B, H, dk, dv] (None: zero).
+    Returns a dict of float64 arrays: dq, dk, dv, dlog_decay, derase, dwrite (None when
+    ``write`` is None), dS0, each shaped like its input (dS0 like S0, or [B, H, dk, dv]).
+    """
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    log_decay, erase, write, S0 = as_f64(log_decay), as_f64(erase), as_f64(write), as_f64(S0)
+    dO, dS_T = as_f64(dO), as_f64(dS_T)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    shared = write is None
+    if shared:
+        write = erase
+        if write.ndim == 4 and dk != dv:
+            raise ValueError("write=None with a per-channel erase gate needs dk == dv")
+    a = np.exp(_gate(log_decay, B, T, H, dk, "log_decay"))  # [B,H,T,dk|1]
+    e = _gate(erase, B, T, H, dk, "erase")
+    w = _gate(write, B, T, H, dv, "write")
+    qh, kh, vh = (np.transpose(x, (0, 2, 1, 3)) for x in (q, k, v))
+    dOh = np.transpose(dO, (0, 2, 1, 3))
+
+    # forward, keeping S_{t-1} of every token
+    S = np.zeros((B, H, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64, copy=True)
+    prev = np.empty((T, B, H, dk, dv))
+    for t in range(T):
+        prev[t] = S
+        kt = kh[:, :, t]
+        Sp = a[:, :, t][..., :, None] * S
+        m = np.einsum("bhi,bhij->bhj", kt, Sp)
+        S = Sp - (e[:, :, t] * kt)[..., :, None] * m[..., None, :] + kt[..., :, None] * (w[:, :, t] * vh[:, :, t])[..., None, :]
+
+    G = np.zeros((B, H, dk, dv)) if dS_T is None else np.array(dS_T, dtype=np.float64, copy=True)
+    gq, gk, gv = np.zeros_like(qh), np.zeros_like(kh), np.zeros_like(vh)
+    ga = np.zeros(a.shape[:3] + (dk,))
+    ge = np.zeros(e.shape[:3] + (dk,))
+    gw = np.zeros(w.shape[:3] + (dv,))
+    for t in reversed(range(T)):
+        kt, qt, vt, dot = kh[:, :, t], qh[:, :, t], vh[:, :, t], dOh[:, :, t]
+        at = a[:, :, t] * np.ones(dk)
+        et = e[:, :, t] * np.ones(dk)
+        wt = w[:, :, t] * np.ones(dv)
+        Sm1 = prev[t]
+        Sp = at[..., :, None] * Sm1
+        m = np.einsum("bhi,bhij->bhj", kt, Sp)
+        u = et * kt
+        vw = wt * vt
+        St = Sp - u[..., :, None] * m[..., None, :] + kt[..., :, None] * vw[..., None, :]
+        G = G + qt[..., :, None] * dot[..., None, :]
+        gq[:, :, t] = np.einsum("bhij,bhj->bhi", St, dot)
+        dm = -np.einsum("bhij,bhi->bhj", G, u)
+        du = -np.einsum("bhij,bhj->bhi", G, m)
+        dvw = np.einsum("bhij,bhi->bhj", G, kt)
+        gk[:, :, t] = np.einsum("bhij,bhj->bhi", G, vw) + np.einsum("bhij,bhj->bhi", Sp, dm) + et * du
+        ge[:, :, t] = kt * du
+        gw[:, :, t] = vt * dvw
+        gv[:, :, t] = wt * dvw
+        Gp = G + kt[..., :, None] * dm[..., None, :]
+        ga[:, :, t] = at * np.sum(Gp * Sm1, axis=-1)
+        G = at[..., :, None] * Gp
+
+    def back(x, like):  # [B,H,T,d] -> the input's layout, summed over channels for a per-head gate
+        x = np.transpose(x, (0, 2, 1, 3))
+        return x.sum(-1) if like.ndim == 3 else x
+
+    out = dict(dq=np.transpose(gq, (0, 2, 1, 3)), dk=np.transpose(gk, (0, 2, 1, 3)),
+               dv=np.transpose(gv, (0, 2, 1, 3)), dlog_decay=back(ga, log_decay), dS0=G)
+    de, dw = back(ge, erase), back(gw, write)
+    if shared:
+        out["derase"], out["dwrite"] = de + dw, None
+    else:
+        out["derase"], out["dwrite"] = de, dw
+    return out
 
 
 def recurrence_fg2(q, k, v, log_decay, beta, S0=None):

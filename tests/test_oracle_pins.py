@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from chunk_model import chunk_forward
-from oracle import decode_step, recurrence, recurrence_fg2, recurrence_varlen
+from oracle import decode_step, recurrence, recurrence_bwd, recurrence_fg2, recurrence_varlen
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -521,3 +521,98 @@ def test_fg2_readback_identity():
     kt, vt = np.sqrt(beta) * k, np.sqrt(beta) * v
     n2 = kt @ kt
     assert np.allclose(kt @ S[0, 0], (1 - n2) * (kt @ S0) + n2 * vt, rtol=0, atol=1e-12)
+
+
+# ---- gradients (recurrence_bwd) -------------------------------------------------------------
+
+
+def _bwd_case(seed, decay, erase, write, B=2, T=9, H=2, dk=4, dv=3):
+    q, k, v, ld, e, w, S0 = _inputs(seed, B=B, T=T, H=H, dk=dk, dv=dv, decay=decay, erase=erase, write=write)
+    r = _rng(seed + 500)
+    dO = r.standard_normal(q.shape[:3] + (dv,))
+    dST = r.standard_normal(S0.shape)
+    return dict(q=q, k=k, v=v, log_decay=ld, erase=e, write=w, S0=S0), dO, dST
+
+
+def _loss(x, dO, dST):
+    o, S = recurrence(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"], x["S0"])
+    return float(np.sum(o * dO) + np.sum(S * dST))
+
+
+GRAD_KEY = dict(q="dq", k="dk", v="dv", log_decay="dlog_decay", erase="derase", write="dwrite", S0="dS0")
+BWD_VARIANTS = [("head", "head", None), ("channel", "head", None), ("channel", "channel", "channel"),
+                ("head", "channel", "head"), ("channel", "channel", None)]
+
+
+# G1 -- central finite differences of the forward along a random direction of every input
+# agree with the adjoint's directional derivative <grad, d>.
+@pytest.mark.parametrize("decay,erase,write", BWD_VARIANTS)
+def test_bwd_matches_finite_differences(decay, erase, write):
+    dv = 4 if (erase == "channel" and write is None) else 3
+    x, dO, dST = _bwd_case(51, decay, erase, write, dv=dv)
+    g = recurrence_bwd(**x, dO=dO, dS_T=dST)
+    r = _rng(52)
+    h = 1e-6
+    for name, val in x.items():
+        if val is None:
+            continue
+        d = r.standard_normal(val.shape)
+        xp, xm = dict(x), dict(x)
+        xp[name], xm[name] = val + h * d, val - h * d
+        fd = (_loss(xp, dO, dST) - _loss(xm, dO, dST)) / (2 * h)
+        an = float(np.sum(g[GRAD_KEY[name]] * d))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+# G2 -- torch autograd through a torch forward written here with plain tensor ops (float64)
+# gives the same gradients to rounding.
+@pytest.mark.parametrize("decay,erase,write", BWD_VARIANTS)
+def test_bwd_matches_autograd(decay, erase, write):
+    import torch
+
+    dv = 4 if (erase == "channel" and write is None) else 3
+    x, dO, dST = _bwd_case(53, decay, erase, write, dv=dv)
+    g = recurrence_bwd(**x, dO=dO, dS_T=dST)
+    tx = {n: (None if val is None else torch.tensor(val, dtype=torch.float64, requires_grad=True)) for n, val in x.items()}
+    q, k, v, S = tx["q"], tx["k"], tx["v"], tx["S0"]
+    a = torch.exp(tx["log_decay"])
+    e = tx["erase"]
+    w = tx["write"] if tx["write"] is not None else tx["erase"]
+    outs = []
+    for t in range(q.shape[1]):
+        at = a[:, t] if a.dim() == 4 else a[:, t, :, None]
+        et = e[:, t] if e.dim() == 4 else e[:, t, :, None]
+        wt = w[:, t] if w.dim() == 4 else w[:, t, :, None]
+        kt, vt, qt = k[:, t], v[:, t], q[:, t]
+        Sp = at[..., :, None] * S
+        m = torch.einsum("bhi,bhij->bhj", kt, Sp)
+        S = Sp - torch.einsum("bhi,bhj->bhij", et * kt, m) + torch.einsum("bhi,bhj->bhij", kt, wt * vt)
+        outs.append(torch.einsum("bhij,bhi->bhj", S, qt))
+    o = torch.stack(outs, 1)
+    L = (o * torch.tensor(dO)).sum() + (S * torch.tensor(dST)).sum()
+    names = [n for n in tx if tx[n] is not None]
+    grads = torch.autograd.grad(L, [tx[n] for n in names])
+    for n, gr in zip(names, grads):
+        ref = gr.numpy()
+        got = g[GRAD_KEY[n]]  # a shared erase/write gate: autograd sums both uses, as the adjoint does
+        assert np.allclose(got, ref, rtol=0, atol=1e-12 * max(1.0, np.abs(ref).max())), n
+
+
+# G3 -- with no erase and no decay the recurrence is causal linear attention, whose gradient in
+# q is closed-form: dq_t = S0 dO_t + sum_{s <= t} k_s (w_s v_s . dO_t).
+def test_bwd_linear_attention_closed_form():
+    x, dO, dST = _bwd_case(54, "head", "head", "head")
+    x["erase"] = np.zeros_like(x["erase"])
+    x["log_decay"] = np.zeros_like(x["log_decay"])
+    g = recurrence_bwd(**x, dO=dO, dS_T=dST)
+    q, k, v, w, S0 = x["q"], x["k"], x["v"], x["write"], x["S0"]
+    B, T, H, _ = q.shape
+    ref = np.empty_like(q)
+    for b in range(B):
+        for h in range(H):
+            for t in range(T):
+                acc = S0[b, h] @ dO[b, t, h]
+                for s in range(t + 1):
+                    acc = acc + k[b, s, h] * (w[b, s, h] * v[b, s, h] @ dO[b, t, h])
+                ref[b, t, h] = acc
+    assert np.allclose(g["dq"], ref, rtol=0, atol=1e-12)
