@@ -23,8 +23,8 @@ import torch
 
 from . import _abi
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "decode_step", "workspace_bytes", "varlen_workspace_bytes",
-           "abi_version", "DrError"]
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "decode_step", "workspace_bytes",
+           "varlen_workspace_bytes", "abi_version", "DrError"]
 
 DrError = _abi.DrError
 
@@ -186,6 +186,46 @@ def chunk_fwd_varlen(q, k, v, log_decay, erase, write=None, S0=None, *, cu_seqle
     )
     _abi.check("dr_chunk_fwd_varlen", st)
     return out, S_T
+
+
+def chunk_bwd(q, k, v, log_decay, erase, write=None, S0=None, *, dO, dS_T=None, need_dS0=True):
+    """Gradients of sum(o * dO) + sum(S_T * dS_T) with respect to q, k, v, the gates and S0.
+
+    Inputs as ``chunk_fwd``; dO [B, T, H, dv] and dS_T [B, H, dk, dv] are fp32 (dS_T None:
+    zero).  Returns a dict of fp32 tensors dq, dk, dv, dlog_decay, derase, dwrite (None when
+    ``write`` is None: derase then holds the shared gate's whole gradient) and dS0 (None
+    unless ``need_dS0``), each in its input's layout."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, (torch.float32, torch.bfloat16), dev)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B, T, H, dk] and v [B, T, H, dv]")
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    for name, t in (("log_decay", log_decay), ("erase", erase), ("write", write), ("S0", S0), ("dO", dO),
+                    ("dS_T", dS_T)):
+        if t is not None:
+            _check_tensor(name, t, (torch.float32,), dev)
+    if tuple(dO.shape) != (B, T, H, dv):
+        raise ValueError(f"dO must be [B, T, H, dv] = {(B, T, H, dv)}")
+    desc = _desc(B, T, H, dk, dv, 0, q.dtype, torch.float32, log_decay, erase, write, (B, T, H))
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty((B, T, H, dk), **f32), dk=torch.empty((B, T, H, dk), **f32),
+               dv=torch.empty((B, T, H, dv), **f32), dlog_decay=torch.empty(log_decay.shape, **f32),
+               derase=torch.empty(erase.shape, **f32),
+               dwrite=None if write is None else torch.empty(write.shape, **f32),
+               dS0=torch.empty((B, H, dk, dv), **f32) if need_dS0 else None)
+    ws_n = int(_abi.lib().dr_chunk_bwd_workspace_bytes(ctypes.byref(desc)))
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    st = _abi.lib().dr_chunk_bwd(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(erase), _ptr(write), _ptr(S0),
+        _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_decay"]),
+        _ptr(out["derase"]), _ptr(out["dwrite"]), _ptr(out["dS0"]), _ptr(ws), ws_n, _stream(),
+    )
+    _abi.check("dr_chunk_bwd", st)
+    return out
 
 
 def decode_step(q, k, v, log_decay, erase, write=None, *, S, o=None, o_dtype=torch.float32, fg2=False):

@@ -46,6 +46,46 @@ __device__ __forceinline__ void store_o4(void* p, int64_t i, f32x4 x, bool bf16)
   }
 }
 
+// Loads n = RPL contiguous q/k elements starting at element `i` into `out` (vector loads:
+// the ABI guarantees 16-byte aligned bases, and i is a multiple of RPL >= 4).
+template <int RPL>
+__device__ __forceinline__ void load_rows(const void* base, int64_t i, bool bf16, float* out) {
+  if (bf16) {
+    const uint2* p = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + i);
+#pragma unroll
+    for (int r = 0; r < RPL / 4; ++r) {
+      uint2 x = p[r];
+      out[4 * r + 0] = __uint_as_float(x.x << 16);
+      out[4 * r + 1] = __uint_as_float(x.x & 0xffff0000u);
+      out[4 * r + 2] = __uint_as_float(x.y << 16);
+      out[4 * r + 3] = __uint_as_float(x.y & 0xffff0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + i);
+#pragma unroll
+    for (int r = 0; r < RPL / 4; ++r) {
+      float4 x = p[r];
+      out[4 * r + 0] = x.x;
+      out[4 * r + 1] = x.y;
+      out[4 * r + 2] = x.z;
+      out[4 * r + 3] = x.w;
+    }
+  }
+}
+
+template <int RPL>
+__device__ __forceinline__ void load_f32_rows(const float* base, int64_t i, float* out) {
+  const float4* p = reinterpret_cast<const float4*>(base + i);
+#pragma unroll
+  for (int r = 0; r < RPL / 4; ++r) {
+    float4 x = p[r];
+    out[4 * r + 0] = x.x;
+    out[4 * r + 1] = x.y;
+    out[4 * r + 2] = x.z;
+    out[4 * r + 3] = x.w;
+  }
+}
+
 // 16x16x32 fp16 matrix-core product with fp32 accumulation (CDNA4).
 // Lane l supplies A[row = l % 16][k = 8 * (l / 16) + 0..7] and B[k = 8 * (l / 16) + 0..7]
 // [col = l % 16]; it receives D[row = 4 * (l / 16) + 0..3][col = l % 16].

@@ -71,6 +71,23 @@ hipError_t launch_chunk128_varlen(Problem p, const int* cu, void* workspace, hip
 size_t recurrent_varlen_workspace_bytes(int nseq);
 hipError_t launch_recurrent_varlen(Problem p, const int* cu, void* workspace, hipStream_t stream);
 
+// Gradients of the recurrence (fp32 adjoint of the token loop; any supported width).  The
+// outputs are fp32 in their inputs' layouts; dwrite is null when the write gate is the erase
+// gate (derase then takes both parts); dS_T and dS0 may be null.
+struct BwdArgs {
+  const float* dO;    // [B, T, H, dv]
+  const float* dS_T;  // [B, H, dk, dv] or null (zero)
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dlog_decay;
+  float* derase;
+  float* dwrite;
+  float* dS0;
+};
+size_t bwd_workspace_bytes(const Problem& p);
+hipError_t launch_bwd(const Problem& p, const BwdArgs& g, void* workspace, hipStream_t stream);
+
 // S_T = S0 (copy) or zeros when S0 is null: n floats.
 hipError_t launch_state_copy(const float* S0, float* S_T, int64_t n, hipStream_t stream);
 

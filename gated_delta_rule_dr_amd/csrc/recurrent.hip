@@ -23,46 +23,6 @@ namespace {
 constexpr int kCols = 16;
 constexpr int kGroups = 4;
 
-// Loads n = RPL contiguous q/k elements starting at element `i` into `out` (vector loads:
-// the ABI guarantees 16-byte aligned bases, and i is a multiple of RPL >= 4).
-template <int RPL>
-__device__ __forceinline__ void load_rows(const void* base, int64_t i, bool bf16, float* out) {
-  if (bf16) {
-    const uint2* p = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + i);
-#pragma unroll
-    for (int r = 0; r < RPL / 4; ++r) {
-      uint2 x = p[r];
-      out[4 * r + 0] = __uint_as_float(x.x << 16);
-      out[4 * r + 1] = __uint_as_float(x.x & 0xffff0000u);
-      out[4 * r + 2] = __uint_as_float(x.y << 16);
-      out[4 * r + 3] = __uint_as_float(x.y & 0xffff0000u);
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + i);
-#pragma unroll
-    for (int r = 0; r < RPL / 4; ++r) {
-      float4 x = p[r];
-      out[4 * r + 0] = x.x;
-      out[4 * r + 1] = x.y;
-      out[4 * r + 2] = x.z;
-      out[4 * r + 3] = x.w;
-    }
-  }
-}
-
-template <int RPL>
-__device__ __forceinline__ void load_f32_rows(const float* base, int64_t i, float* out) {
-  const float4* p = reinterpret_cast<const float4*>(base + i);
-#pragma unroll
-  for (int r = 0; r < RPL / 4; ++r) {
-    float4 x = p[r];
-    out[4 * r + 0] = x.x;
-    out[4 * r + 1] = x.y;
-    out[4 * r + 2] = x.z;
-    out[4 * r + 3] = x.w;
-  }
-}
-
 __device__ __forceinline__ float group_sum(float x) {
   // Sum over the 4 lanes that share a column: lanes c, c+16, c+32, c+48.
   x += __shfl_xor(x, 16);

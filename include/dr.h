@@ -168,6 +168,32 @@ int dr_chunk_fwd_varlen(const dr_desc* desc, const int32_t* cu_seqlens, int32_t 
                         const float* write, const float* S0, void* o, float* S_T, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* Gradients for training: of L = sum(o * dO) + sum(S_T * dS_T) with respect to every input of
+ * dr_chunk_fwd, by the adjoint of the token loop (the forward pass of training is the
+ * recurrence; "FG2-GDN ...", sections 2-3, chunk-parallel training of the update).  The kernels
+ * run the forward again (state checkpoints every 64 tokens), then walk the tokens backwards in
+ * fp32; desc->chunk is ignored.
+ *
+ *   dO     [B, T, H, dv] fp32 (required).       dS_T  [B, H, dk, dv] fp32, or NULL for zero.
+ *   dq, dk [B, T, H, dk] fp32; dv [B, T, H, dv] fp32 (all required).
+ *   dlog_decay, derase, dwrite: fp32 in the layouts of log_decay, erase and write (a per-head
+ *          gate gets the sum over its channels).  With write_is_erase the one gate's gradient
+ *          (both uses) goes to derase and dwrite is ignored.
+ *   dS0    [B, H, dk, dv] fp32, or NULL to skip.
+ *   workspace: at least dr_chunk_bwd_workspace_bytes(desc) bytes: the checkpoints and each
+ *          wave's chunk of states (128 KB per chunk per (b, h) at dk = dv = 128), one chunk's
+ *          states per (b, h, 16 value columns), and per-row partial sums for each group of 16
+ *          value columns (64 dv / 16 dk bytes per token and head).
+ * Outputs must not overlap one another, any input or the workspace.  T == 0 writes dS0 = dS_T
+ * (zeros without it).  DR_GATE_RATE_SQRT is DR_E_UNSUPPORTED here.  Errors as dr_chunk_fwd. */
+size_t dr_chunk_bwd_workspace_bytes(const dr_desc* desc);
+
+int dr_chunk_bwd(const dr_desc* desc, const void* q, const void* k, const void* v,
+                 const float* log_decay, const float* erase, const float* write, const float* S0,
+                 const float* dO, const float* dS_T, float* dq, float* dk, float* dv,
+                 float* dlog_decay, float* derase, float* dwrite, float* dS0, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
 /* One decode token for B independent sequences (desc->T must be 1): reads q, k, v, gates in
  * the [B, 1, H, d] layouts above, updates S [B, H, dk, dv] in place and writes o [B, 1, H, dv].
  * The state streams through once (read once, written once).  o must not overlap any input

@@ -247,3 +247,35 @@ def test_rate_sqrt_kind():
     # a per-channel extent: the rate array overlapping o by one channel row is an alias
     rate_bytes = 2 * 100 * 4 * 128 * 4
     assert _fwd(_good_desc(erase_kind=R), o=P["e"] + rate_bytes - 512) == _abi.DR_E_ALIAS
+
+
+# ---- gradients ---------------------------------------------------------------------------------
+PG = {name: (20 + i) * 64 * GB for i, name in enumerate(["dO", "dST", "dq", "dk", "dv", "dla", "de", "dw", "dS0"])}
+
+
+def _bwd(desc, **over):
+    ptr = dict(P)
+    ptr.update(PG)
+    ptr.update(over)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    names = ["q", "k", "v", "ld", "e", "w", "S0", "dO", "dST", "dq", "dk", "dv", "dla", "de", "dw", "dS0", "ws"]
+    return _abi.lib().dr_chunk_bwd(ctypes.byref(desc), *[vp(ptr[n]) for n in names], ptr.get("wsn", 1 << 40), None)
+
+
+def test_bwd_workspace_and_errors():
+    L = _abi.lib()
+    d = _good_desc(B=2, T=100, H=4, dk=128, dv=128)
+    waves, nck, bth = 2 * 4 * 8, 2, 2 * 100 * 4
+    need = 4 * (waves * nck * 128 * 16 + waves * 64 * 128 * 16 + 4 * 8 * bth * 128 + bth * 128)
+    assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(d)) == need
+    assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(_good_desc(T=0))) == 0
+    assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(_good_desc(erase_kind=_abi.DR_GATE_RATE_SQRT))) == 0
+    assert _bwd(_good_desc(erase_kind=_abi.DR_GATE_RATE_SQRT)) == _abi.DR_E_UNSUPPORTED
+    for name in ("dO", "dq", "dk", "dv", "dla", "de"):
+        assert _bwd(d, **{name: None}) == _abi.DR_E_NULL, name
+    assert _bwd(_good_desc(write_is_erase=0), dw=None) == _abi.DR_E_NULL
+    assert _bwd(d, dq=PG["dq"] + 8) == _abi.DR_E_ALIGN
+    assert _bwd(d, dk=PG["dq"] + 4096) == _abi.DR_E_ALIAS  # two outputs overlap
+    assert _bwd(d, dv=P["v"]) == _abi.DR_E_ALIAS  # output on an input
+    assert _bwd(d, ws=PG["dO"], wsn=need) == _abi.DR_E_ALIAS
+    assert _bwd(d, wsn=need - 1) == _abi.DR_E_WORKSPACE
