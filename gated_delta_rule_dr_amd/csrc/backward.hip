@@ -41,12 +41,62 @@ __device__ __forceinline__ float group_sum(float x) {  // over the 4 lanes of on
   return x;
 }
 
-__device__ __forceinline__ float column_sum(float x) {  // over the 16 lanes of one row group
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
+// x of the lane that the DPP control CTRL selects within this lane's row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 16 lanes of one row group (one DPP row), left in every one of them: swap lanes
+// 1 apart and 2 apart within each quad (quad permutations [1,0,3,2] and [2,3,0,1]), then mirror
+// within each half-row and within the row.  These run on the vector ALU; a cross-lane shuffle
+// would take a round trip through the LDS crossbar for every value.
+__device__ __forceinline__ float column_sum(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
   return x;
+}
+
+// Reduce-scatter of N values per lane over the 16 lanes of a row group: four DPP pairings
+// (row mirror, half-row mirror, quad swaps 2 and 1 apart); at each one a lane keeps the half of
+// its values that its lane bit selects, adds the partner's copy of that half, and sends the
+// other half.  Afterwards lane c holds the full sums of rows rs_row<N>(c) .. + rs_count<N> - 1
+// in v[0 ..]; with N < 16 some pairings find a single value left and just add the partner's,
+// so several lanes hold the same rows (rs_owner<N> marks one of them).
+template <int CTRL, int BIT, int N>
+__device__ __forceinline__ void rs_stage(float* v, int c) {
+  if constexpr (N > 1) {
+    constexpr int H = N / 2;
+    const bool low = ((c >> BIT) & 1) == 0;
+#pragma unroll
+    for (int m = 0; m < H; ++m) {
+      const float keep = low ? v[m] : v[m + H];
+      const float send = low ? v[m + H] : v[m];
+      v[m] = keep + dpp<CTRL>(send);
+    }
+  } else {
+    v[0] += dpp<CTRL>(v[0]);
+  }
+}
+template <int N>
+__device__ __forceinline__ void row_scatter_sum(float* v, int c) {
+  rs_stage<0x140, 3, N>(v, c);
+  rs_stage<0x141, 2, (N > 1 ? N / 2 : 1)>(v, c);
+  rs_stage<0x4E, 1, (N > 2 ? N / 4 : 1)>(v, c);
+  rs_stage<0xB1, 0, (N > 4 ? N / 8 : 1)>(v, c);
+}
+template <int N>
+__device__ __forceinline__ int rs_row(int c) {
+  return (N > 1 ? (N / 2) * ((c >> 3) & 1) : 0) + (N > 2 ? (N / 4) * ((c >> 2) & 1) : 0) +
+         (N > 4 ? (N / 8) * ((c >> 1) & 1) : 0) + (N > 8 ? (N / 16) * (c & 1) : 0);
+}
+template <int N>
+constexpr int rs_count = N >= 16 ? N / 16 : 1;
+template <int N>
+__device__ __forceinline__ bool rs_owner(int c) {
+  return (N > 8 || (c & 1) == 0) && (N > 4 || (c & 2) == 0) && (N > 2 || (c & 4) == 0) && (N > 1 || (c & 8) == 0);
 }
 
 // Workspace layout of the backward (offsets in floats).
@@ -132,14 +182,18 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
   const int64_t sbase = int64_t(bh) * DK * dv + j;
 #pragma unroll
   for (int r = 0; r < RPL; ++r) s[r] = p.S0 ? p.S0[sbase + int64_t(row0 + r) * dv] : 0.f;
+  // Every loop loads the next token's inputs before working on the current one, so that one
+  // token's computation covers the next one's load latency.
+  Tok x, nx;
+  if (T > 0) load_tok(nx, token(0));
   for (int t = 0; t < T; ++t) {
+    x = nx;
+    if (t + 1 < T) load_tok(nx, token(t + 1));
     if (t % CK == 0) {
       float* dst = ck + int64_t(t / CK) * DK * kCols;
 #pragma unroll
       for (int r = 0; r < RPL; ++r) dst[at(r)] = s[r];
     }
-    Tok x;
-    load_tok(x, token(t));
     step(s, x);
   }
 
@@ -154,56 +208,80 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
     const float* src = ck + ci * DK * kCols;
 #pragma unroll
     for (int r = 0; r < RPL; ++r) s[r] = src[at(r)];
+    load_tok(nx, token(t0));
     for (int t = t0; t < t1; ++t) {  // S_{t-1} of every token of the chunk
+      x = nx;
+      if (t + 1 < t1) load_tok(nx, token(t + 1));
       float* dst = st + int64_t(t - t0) * DK * kCols;
 #pragma unroll
       for (int r = 0; r < RPL; ++r) dst[at(r)] = s[r];
-      Tok x;
-      load_tok(x, token(t));
       step(s, x);
     }
-    for (int t = t1 - 1; t >= t0; --t) {
+    // the adjoint walk: token t's inputs, q, dO and S_{t-1}, loaded one token ahead
+    float nq[RPL], nsp[RPL], ndO;
+    auto load_back = [&](int t) {
       const int64_t tok = token(t);
-      Tok x;
-      load_tok(x, tok);
-      float qr[RPL], sp[RPL];
-      load_rows<RPL>(p.q, tok * DK + row0, bf, qr);
+      load_tok(nx, tok);
+      load_rows<RPL>(p.q, tok * DK + row0, bf, nq);
       const float* prv = st + int64_t(t - t0) * DK * kCols;
 #pragma unroll
-      for (int r = 0; r < RPL; ++r) sp[r] = prv[at(r)];
-      const float dO = g.dO[tok * dv + j];
+      for (int r = 0; r < RPL; ++r) nsp[r] = prv[at(r)];
+      ndO = g.dO[tok * dv + j];
+    };
+    load_back(t1 - 1);
+    for (int t = t1 - 1; t >= t0; --t) {
+      const int64_t tok = token(t);
+      float qr[RPL], sp[RPL];
+      x = nx;
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        qr[r] = nq[r];
+        sp[r] = nsp[r];
+      }
+      const float dO = ndO;
+      if (t > t0) load_back(t - 1);
       float m = 0.f;
 #pragma unroll
       for (int r = 0; r < RPL; ++r) m = fmaf(x.k[r], x.a[r] * sp[r], m);
       m = group_sum(m);
       const float vw = x.w * x.v;
-      // row parts, summed over this wave's 16 columns; lane c stores rows r = c (mod 16)
-      float* pbase = parts + (int64_t(slice) * L.bth + tok) * DK + row0;
-      auto put = [&](int r, int which, float val) {
-        const float sum = column_sum(val);
-        if ((r & (kCols - 1)) == c) pbase[which * pstride + r] = sum;
+      // row parts, summed over this wave's 16 columns (reduce-scatter: lane c stores rows
+      // rs_row(c) ..)
+      float* pbase = parts + (int64_t(slice) * L.bth + tok) * DK + row0 + rs_row<RPL>(c);
+      const bool owner = rs_owner<RPL>(c);
+      auto put = [&](float* part, int which) {
+        row_scatter_sum<RPL>(part, c);
+        if (owner) {
+#pragma unroll
+          for (int i = 0; i < rs_count<RPL>; ++i) pbase[which * pstride + i] = part[i];
+        }
       };
       float dm = 0.f, dvw = 0.f;
+      float pa[RPL], pb[RPL];
 #pragma unroll
       for (int r = 0; r < RPL; ++r) {
         const float Sp = x.a[r] * sp[r];
         const float St = fmaf(-x.e[r] * x.k[r], m, fmaf(x.k[r], vw, Sp));
         G[r] = fmaf(qr[r], dO, G[r]);
-        put(r, 0, St * dO);    // dq
-        put(r, 1, -G[r] * m);  // du
+        pa[r] = St * dO;    // dq
+        pb[r] = -G[r] * m;  // du
         dm = fmaf(-G[r] * x.e[r], x.k[r], dm);
         dvw = fmaf(G[r], x.k[r], dvw);
       }
+      put(pa, 0);
+      put(pb, 1);
       dm = group_sum(dm);
       dvw = group_sum(dvw);
 #pragma unroll
       for (int r = 0; r < RPL; ++r) {
         const float Sp = x.a[r] * sp[r];
-        put(r, 2, fmaf(G[r], vw, Sp * dm));  // dk, less the erase part
+        pa[r] = fmaf(G[r], vw, Sp * dm);  // dk, less the erase part
         const float Gp = fmaf(x.k[r], dm, G[r]);
-        put(r, 3, Gp * sp[r]);  // d(log a) / a
+        pb[r] = Gp * sp[r];  // d(log a) / a
         G[r] = x.a[r] * Gp;
       }
+      put(pa, 2);
+      put(pb, 3);
       if (grp == 0) {
         g.dv[tok * dv + j] = x.w * dvw;
         ws[L.tmp_dw + tok * dv + j] = x.v * dvw;
