@@ -35,10 +35,17 @@ constexpr int kCols = 16;   // value columns per wave
 constexpr int kGroups = 4;  // row groups per wave
 constexpr int CK = 64;      // tokens per checkpoint
 
-__device__ __forceinline__ float group_sum(float x) {  // over the 4 lanes of one column
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+// Sum over the 4 lanes of one column (lanes c, c + 16, c + 32, c + 48), in every one of them,
+// with the gfx950 row swaps: swapping rows 1 <-> 0 and 3 <-> 2 of a value with itself and adding
+// both results gives each lane the sum of its pair of rows; the half-wave swap then adds the
+// other pair.  Both lanes of a pair add in the same order, so all four hold the same sum.
+__device__ __forceinline__ float group_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned w = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // x of the lane that the DPP control CTRL selects within this lane's row of 16 lanes.
@@ -134,7 +141,23 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
   const int64_t wave_id = int64_t(bh) * L.nslice + slice;
   float* ck = ws + L.ckpt + wave_id * L.nck * DK * kCols;
   float* st = ws + L.states + wave_id * CK * DK * kCols;
-  auto at = [&](int r) { return (row0 + r) * kCols + c; };  // this lane's element of a state slice
+  // A state slice in the scratch area is stored lane-major (lane l's RPL values contiguous), so
+  // that a lane saves or restores its part with RPL / 4 16-byte accesses.
+  auto save = [&](float* dst, const float (&v)[RPL]) {
+#pragma unroll
+    for (int i = 0; i < RPL; i += 4)
+      *reinterpret_cast<f32x4*>(dst + lane * RPL + i) = f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]};
+  };
+  auto restore = [&](const float* src, float (&v)[RPL]) {
+#pragma unroll
+    for (int i = 0; i < RPL; i += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src + lane * RPL + i);
+      v[i] = x[0];
+      v[i + 1] = x[1];
+      v[i + 2] = x[2];
+      v[i + 3] = x[3];
+    }
+  };
 
   struct Tok {
     float k[RPL], a[RPL], e[RPL];
@@ -190,9 +213,7 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
     x = nx;
     if (t + 1 < T) load_tok(nx, token(t + 1));
     if (t % CK == 0) {
-      float* dst = ck + int64_t(t / CK) * DK * kCols;
-#pragma unroll
-      for (int r = 0; r < RPL; ++r) dst[at(r)] = s[r];
+      save(ck + int64_t(t / CK) * DK * kCols, s);
     }
     step(s, x);
   }
@@ -205,16 +226,12 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
   const int64_t pstride = L.nslice * L.bth * DK;  // between the four row-part arrays
   for (int64_t ci = L.nck - 1; ci >= 0; --ci) {
     const int t0 = int(ci * CK), t1 = t0 + CK < T ? t0 + CK : T;
-    const float* src = ck + ci * DK * kCols;
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) s[r] = src[at(r)];
+    restore(ck + ci * DK * kCols, s);
     load_tok(nx, token(t0));
     for (int t = t0; t < t1; ++t) {  // S_{t-1} of every token of the chunk
       x = nx;
       if (t + 1 < t1) load_tok(nx, token(t + 1));
-      float* dst = st + int64_t(t - t0) * DK * kCols;
-#pragma unroll
-      for (int r = 0; r < RPL; ++r) dst[at(r)] = s[r];
+      save(st + int64_t(t - t0) * DK * kCols, s);
       step(s, x);
     }
     // the adjoint walk: token t's inputs, q, dO and S_{t-1}, loaded one token ahead
@@ -223,9 +240,7 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
       const int64_t tok = token(t);
       load_tok(nx, tok);
       load_rows<RPL>(p.q, tok * DK + row0, bf, nq);
-      const float* prv = st + int64_t(t - t0) * DK * kCols;
-#pragma unroll
-      for (int r = 0; r < RPL; ++r) nsp[r] = prv[at(r)];
+      restore(st + int64_t(t - t0) * DK * kCols, nsp);
       ndO = g.dO[tok * dv + j];
     };
     load_back(t1 - 1);
