@@ -84,6 +84,40 @@ def gate_desc(wl) -> str:
     return f"fp32 decay {decay}, one per-head erase/write gate" if wl.decay_channel else "fp32 per head"
 
 
+def backward_bytes(wl) -> int:
+    """Compulsory HBM bytes of one gradient call: the forward's inputs, dO (fp32), and the fp32
+    gradients of q, k, v and every gate (S0 / dS_T / dS0 when the forward has an S0)."""
+    th = wl.B * wl.T * wl.H
+    qkv = 2 if wl.qkv_dtype == "bf16" else 4
+    gates = 4 * ((wl.dk if wl.decay_channel else 1) + (wl.dk if wl.erase_channel else 1)
+                 + (wl.dv if wl.write == "channel" else 0))
+    per_tok = qkv * (2 * wl.dk + wl.dv) + 4 * wl.dv + 4 * (2 * wl.dk + wl.dv) + 2 * gates
+    state = wl.B * wl.H * wl.dk * wl.dv * 4
+    return th * per_tok + (3 * state if wl.s0_std > 0 else state)
+
+
+def time_backward(dr, torch, wl, steps, warmup):
+    from gated_delta_rule_dr_amd.workloads import generate
+
+    x = generate(wl, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(wl.seed + 77)
+    dO = torch.randn((wl.B, wl.T, wl.H, wl.dv), generator=g, device="cuda")
+    dST = torch.randn((wl.B, wl.H, wl.dk, wl.dv), generator=g, device="cuda")
+    call = lambda: dr.chunk_bwd(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"], x["S0"],
+                                dO=dO, dS_T=dST)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / steps
+
+
 def decode_bytes(wl) -> int:
     """Per decode step: the fp32 state read and written once, q/k/v, gates and the output."""
     n = wl.B * wl.H
@@ -207,6 +241,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--all", action="store_true",
                     help="also time the KDA, FG2, decoupled and packed-sequence prefill workloads")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the gradient call (dr_chunk_bwd) on the main workload")
     ap.add_argument("--workload", default=PREFILL,
                     help="prefill workload of the main line (default: the bench workload %(default)s)")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -283,6 +319,15 @@ def main():
                            "mfma_frac": algorithmic_flops(w2) / s2 / 1e12 / MFMA_PEAK_TFLOPS}
             torch.cuda.empty_cache()
         line["other_prefill"] = extra
+    if args.backward:
+        bsteps = max(2, args.steps // 10)
+        bsec = time_backward(dr, torch, wl, bsteps, 1)
+        bbytes = backward_bytes(wl)
+        line["backward"] = {"workload": wl.name, "calls": bsteps, "ms": bsec * 1e3,
+                            "tokens_per_s": wl.token_heads / bsec, "hbm_frac": bbytes / bsec / 1e9 / HBM_PEAK_GBS,
+                            "bytes_per_call": bbytes,
+                            "kernel": "dr_chunk_bwd = bwd_token_kernel + bwd_reduce_kernel (fp32 token adjoint)"}
+        torch.cuda.empty_cache()
     if not args.no_decode:
         dwl = workload(DECODE)
         dsec = time_decode(dr, torch, dwl, args.decode_steps)
