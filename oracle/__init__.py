@@ -16,6 +16,8 @@ with a diagonal learning-rate matrix; for the gradients (recurrence_bwd), centra
 differences of the forward along random directions and torch autograd through a separately
 written torch forward.  No function here is "parity unpinned".
 """
-from .recurrence import as_f64, decode_step, recurrence, recurrence_bwd, recurrence_fg2, recurrence_varlen
+from .recurrence import (as_f64, decode_step, recurrence, recurrence_bwd, recurrence_fg2, recurrence_fg2_bwd,
+                         recurrence_varlen)
 
-__all__ = ["recurrence", "recurrence_bwd", "recurrence_fg2", "recurrence_varlen", "decode_step", "as_f64"]
+__all__ = ["recurrence", "recurrence_bwd", "recurrence_fg2", "recurrence_fg2_bwd", "recurrence_varlen",
+           "decode_step", "as_f64"]

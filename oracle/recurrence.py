@@ -41,7 +41,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["recurrence", "recurrence_bwd", "recurrence_fg2", "recurrence_varlen", "decode_step", "as_f64"]
+__all__ = ["recurrence", "recurrence_bwd", "recurrence_fg2", "recurrence_fg2_bwd", "recurrence_varlen", "decode_step",
+           "as_f64"]
 
 
 def as_f64(x):
@@ -242,6 +243,18 @@ def recurrence_fg2(q, k, v, log_decay, beta, S0=None):
     r = np.sqrt(beta)
     ones = np.ones(k.shape[:3])
     return recurrence(q, r * k, r * v, log_decay, ones, None, S0)
+
+
+def recurrence_fg2_bwd(q, k, v, log_decay, beta, S0=None, dO=None, dS_T=None):
+    """Gradients of FG2-GDN's rate form (``recurrence_fg2``), in fp64: the adjoint of the
+    recurrence on the scaled pair (k~, v~) = (sqrt(beta) k, sqrt(beta) v) with unit gates, then
+    the chain rule through the scaling: dk = sqrt(beta) dk~, dv = sqrt(beta) dv~ and
+    dbeta = (k dk~ + v dv~) / (2 sqrt(beta)).  Returns dq, dk, dv, dlog_decay, dbeta, dS0."""
+    q, k, v, beta = as_f64(q), as_f64(k), as_f64(v), as_f64(beta)
+    r = np.sqrt(beta)
+    g = recurrence_bwd(q, r * k, r * v, log_decay, np.ones(k.shape[:3]), None, S0, dO, dS_T)
+    return dict(dq=g["dq"], dk=r * g["dk"], dv=r * g["dv"], dlog_decay=g["dlog_decay"],
+                dbeta=(k * g["dk"] + v * g["dv"]) / (2 * r), dS0=g["dS0"])
 
 
 def decode_step(q, k, v, log_decay, erase, write, S):

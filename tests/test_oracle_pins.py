@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from chunk_model import chunk_forward
-from oracle import decode_step, recurrence, recurrence_bwd, recurrence_fg2, recurrence_varlen
+from oracle import decode_step, recurrence, recurrence_bwd, recurrence_fg2, recurrence_fg2_bwd, recurrence_varlen
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -616,3 +616,31 @@ def test_bwd_linear_attention_closed_form():
                     acc = acc + k[b, s, h] * (w[b, s, h] * v[b, s, h] @ dO[b, t, h])
                 ref[b, t, h] = acc
     assert np.allclose(g["dq"], ref, rtol=0, atol=1e-12)
+
+
+# G4 -- FG2's rate form: central finite differences of recurrence_fg2 along random directions
+# of q, k, v, the decay, the rate and S0 agree with recurrence_fg2_bwd.
+@pytest.mark.parametrize("decay", ["channel", "head"])
+def test_fg2_bwd_matches_finite_differences(decay):
+    r = _rng(61)
+    B, T, H, d = 2, 8, 2, 4
+    x = dict(q=r.standard_normal((B, T, H, d)), k=_unit(r.standard_normal((B, T, H, d))),
+             v=r.standard_normal((B, T, H, d)),
+             log_decay=-np.log1p(np.exp(r.normal(-2, 1, (B, T, H, d) if decay == "channel" else (B, T, H)))),
+             beta=_sig(r.standard_normal((B, T, H, d))), S0=r.standard_normal((B, H, d, d)))
+    dO, dST = r.standard_normal((B, T, H, d)), r.standard_normal((B, H, d, d))
+    g = recurrence_fg2_bwd(**x, dO=dO, dS_T=dST)
+    key = dict(q="dq", k="dk", v="dv", log_decay="dlog_decay", beta="dbeta", S0="dS0")
+
+    def loss(y):
+        o, S = recurrence_fg2(**y)
+        return float(np.sum(o * dO) + np.sum(S * dST))
+
+    h = 1e-6
+    for name, val in x.items():
+        dirn = r.standard_normal(val.shape)
+        yp, ym = dict(x), dict(x)
+        yp[name], ym[name] = val + h * dirn, val - h * dirn
+        fd = (loss(yp) - loss(ym)) / (2 * h)
+        an = float(np.sum(g[key[name]] * dirn))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
