@@ -188,13 +188,14 @@ def chunk_fwd_varlen(q, k, v, log_decay, erase, write=None, S0=None, *, cu_seqle
     return out, S_T
 
 
-def chunk_bwd(q, k, v, log_decay, erase, write=None, S0=None, *, dO, dS_T=None, need_dS0=True):
+def chunk_bwd(q, k, v, log_decay, erase, write=None, S0=None, *, dO, dS_T=None, need_dS0=True, fg2=False):
     """Gradients of sum(o * dO) + sum(S_T * dS_T) with respect to q, k, v, the gates and S0.
 
     Inputs as ``chunk_fwd``; dO [B, T, H, dv] and dS_T [B, H, dk, dv] are fp32 (dS_T None:
     zero).  Returns a dict of fp32 tensors dq, dk, dv, dlog_decay, derase, dwrite (None when
     ``write`` is None: derase then holds the shared gate's whole gradient) and dS0 (None
-    unless ``need_dS0``), each in its input's layout."""
+    unless ``need_dS0``), each in its input's layout.  ``fg2=True``: ``erase`` is FG2's rate
+    beta, and derase its gradient."""
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(name, t, (torch.float32, torch.bfloat16), dev)
@@ -210,7 +211,7 @@ def chunk_bwd(q, k, v, log_decay, erase, write=None, S0=None, *, dO, dS_T=None, 
             _check_tensor(name, t, (torch.float32,), dev)
     if tuple(dO.shape) != (B, T, H, dv):
         raise ValueError(f"dO must be [B, T, H, dv] = {(B, T, H, dv)}")
-    desc = _desc(B, T, H, dk, dv, 0, q.dtype, torch.float32, log_decay, erase, write, (B, T, H))
+    desc = _desc(B, T, H, dk, dv, 0, q.dtype, torch.float32, log_decay, erase, write, (B, T, H), fg2)
     f32 = dict(dtype=torch.float32, device=dev)
     out = dict(dq=torch.empty((B, T, H, dk), **f32), dk=torch.empty((B, T, H, dk), **f32),
                dv=torch.empty((B, T, H, dv), **f32), dlog_decay=torch.empty(log_decay.shape, **f32),

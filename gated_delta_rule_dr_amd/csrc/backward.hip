@@ -184,6 +184,14 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
     }
     x.v = load_qkv(p.v, tok * dv + j, bf);
     x.w = p.write_channel ? p.write[tok * dv + j] : p.write[tok];
+    if (p.rate_sqrt) {  // FG2's rate: the scaled key sqrt(beta) k with a unit erase, v~ = sqrt(beta) v
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        x.k[r] *= sqrtf(x.e[r]);
+        x.e[r] = 1.f;
+      }
+      x.w = sqrtf(x.w);
+    }
   };
   // one forward token: s <- S_t from s = S_{t-1}
   auto step = [&](float (&s)[RPL], const Tok& x) {
@@ -344,11 +352,23 @@ __global__ __launch_bounds__(128) void bwd_reduce_kernel(Problem p, BwdArgs g, c
     const float e = p.erase_channel ? p.erase[tok * dk + i] : p.erase[tok];
     const float a = expf(p.decay_channel ? p.log_decay[tok * dk + i] : p.log_decay[tok]);
     g.dq[tok * dk + i] = sq;
-    g.dk[tok * dk + i] = fmaf(e, sdu, skw);
-    de = k * sdu;
     dla = a * sda;
+    if (p.rate_sqrt) {
+      // FG2's rate: the parts are for the scaled key k~ = sqrt(beta) k with a unit erase, so
+      // dk~ = skw + sdu; dk = sqrt(beta) dk~, and beta's gradient gathers k dk~ and (below)
+      // v dv~, each over 2 sqrt(beta)
+      const float rt = sqrtf(e), dkt = skw + sdu;
+      g.dk[tok * dk + i] = rt * dkt;
+      de = k * dkt / (2.f * rt);
+    } else {
+      g.dk[tok * dk + i] = fmaf(e, sdu, skw);
+      de = k * sdu;
+    }
   }
-  if (i < dv) dwv = ws[L.tmp_dw + tok * dv + i];
+  if (i < dv) {
+    dwv = ws[L.tmp_dw + tok * dv + i];
+    if (p.rate_sqrt) dwv /= 2.f * sqrtf(p.erase[tok * dk + i]);  // v dv~ / (2 sqrt(beta)); dk == dv
+  }
   // decay
   if (p.decay_channel) {
     if (i < dk) g.dlog_decay[tok * dk + i] = dla;

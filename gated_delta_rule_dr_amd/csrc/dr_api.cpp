@@ -271,7 +271,7 @@ int dr_chunk_fwd_varlen(const dr_desc* d, const int32_t* cu_seqlens, int32_t nse
 
 size_t dr_chunk_bwd_workspace_bytes(const dr_desc* desc) {
   Extents ex;
-  if (check_desc(desc, false, &ex) != DR_OK || desc->erase_kind == DR_GATE_RATE_SQRT || desc->T == 0) return 0;
+  if (check_desc(desc, false, &ex) != DR_OK || desc->T == 0) return 0;
   dr::Problem p = make_problem(desc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                nullptr);
   return dr::bwd_workspace_bytes(p);
@@ -284,7 +284,6 @@ int dr_chunk_bwd(const dr_desc* d, const void* q, const void* k, const void* v, 
   Extents ex;
   int st = check_desc(d, false, &ex);
   if (st != DR_OK) return st;
-  if (d->erase_kind == DR_GATE_RATE_SQRT) return DR_E_UNSUPPORTED;
   const bool need_write = !d->write_is_erase;
   if (!need_write) dwrite = nullptr;
   const uint64_t bth = uint64_t(d->B) * uint64_t(d->T) * uint64_t(d->H);

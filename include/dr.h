@@ -185,7 +185,8 @@ int dr_chunk_fwd_varlen(const dr_desc* desc, const int32_t* cu_seqlens, int32_t 
  *          states per (b, h, 16 value columns), and per-row partial sums for each group of 16
  *          value columns (64 dv / 16 dk bytes per token and head).
  * Outputs must not overlap one another, any input or the workspace.  T == 0 writes dS0 = dS_T
- * (zeros without it).  DR_GATE_RATE_SQRT is DR_E_UNSUPPORTED here.  Errors as dr_chunk_fwd. */
+ * (zeros without it).  With DR_GATE_RATE_SQRT, derase is the gradient of the rate beta (through
+ * both sqrt(beta) k and sqrt(beta) v).  Errors as dr_chunk_fwd. */
 size_t dr_chunk_bwd_workspace_bytes(const dr_desc* desc);
 
 int dr_chunk_bwd(const dr_desc* desc, const void* q, const void* k, const void* v,

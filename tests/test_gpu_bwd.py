@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import recurrence_bwd
+from oracle import recurrence_bwd, recurrence_fg2_bwd
 
 pytestmark = pytest.mark.gpu
 
@@ -105,3 +105,24 @@ def test_bwd_deterministic(dr):
     for key in a:
         if a[key] is not None:
             assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("decay_channel", [True, False])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_fg2_rate(dr, decay_channel, d):
+    from gated_delta_rule_dr_amd.workloads import Workload, generate
+
+    wl = Workload("case", 1, 90, 2, d, d, "bf16", "softplus", decay_channel, -4.0, 1.5, True, "erase", 0.05, 500 + d,
+                  rate_sqrt=True)
+    inp = generate(wl)
+    g = torch.Generator().manual_seed(501)
+    dO = torch.randn((1, 90, 2, d), generator=g, dtype=torch.float64).float()
+    dST = torch.randn((1, 2, d, d), generator=g, dtype=torch.float64).float()
+    x = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    out = dr.chunk_bwd(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], None, x["S0"], dO=dO.cuda(),
+                       dS_T=dST.cuda(), fg2=True)
+    torch.cuda.synchronize()
+    ref = recurrence_fg2_bwd(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["S0"], dO, dST)
+    errs = {key: _err(out[key], ref[key]) for key in ("dq", "dk", "dv", "dlog_decay", "dS0")}
+    errs["dbeta"] = _err(out["derase"], ref["dbeta"])
+    assert max(errs.values()) <= TOL, errs
