@@ -118,6 +118,31 @@ def time_backward(dr, torch, wl, steps, warmup):
     return e0.elapsed_time(e1) / 1e3 / steps
 
 
+def cpu_baseline_backward(wl, tokens):
+    """The fp64 adjoint oracle on the first `tokens` tokens of every (b, h) of the workload."""
+    from threadpoolctl import threadpool_limits
+
+    from gated_delta_rule_dr_amd.workloads import generate
+    from oracle import recurrence_bwd
+
+    sample = wl.replace(T=tokens)
+    inp = generate(sample)
+    dO = _dO_sample(sample)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        recurrence_bwd(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"], inp["S0"], dO=dO)
+        sec = time.perf_counter() - t0
+    return dict(value=sample.token_heads / sec, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{sample.B}x{sample.H} heads x first {tokens} tokens of {wl.name} "
+                       f"({sample.token_heads} token-heads, {sec:.1f} s, fp64 numpy, 1 thread)")
+
+
+def _dO_sample(wl):
+    import numpy as np
+
+    return np.random.default_rng(wl.seed + 77).standard_normal((wl.B, wl.T, wl.H, wl.dv))
+
+
 def decode_bytes(wl) -> int:
     """Per decode step: the fp32 state read and written once, q/k/v, gates and the output."""
     n = wl.B * wl.H
@@ -327,6 +352,8 @@ def main():
                             "tokens_per_s": wl.token_heads / bsec, "hbm_frac": bbytes / bsec / 1e9 / HBM_PEAK_GBS,
                             "bytes_per_call": bbytes,
                             "kernel": "dr_chunk_bwd = bwd_token_kernel + bwd_reduce_kernel (fp32 token adjoint)"}
+        if not args.no_cpu:
+            line["backward"]["cpu_baseline"] = cpu_baseline_backward(wl, max(64, args.cpu_tokens // 16))
         torch.cuda.empty_cache()
     if not args.no_decode:
         dwl = workload(DECODE)
