@@ -188,14 +188,16 @@ def chunk_fwd_varlen(q, k, v, log_decay, erase, write=None, S0=None, *, cu_seqle
     return out, S_T
 
 
-def chunk_bwd(q, k, v, log_decay, erase, write=None, S0=None, *, dO, dS_T=None, need_dS0=True, fg2=False):
+def chunk_bwd(q, k, v, log_decay, erase, write=None, S0=None, *, dO, dS_T=None, need_dS0=True, fg2=False,
+              cu_seqlens=None):
     """Gradients of sum(o * dO) + sum(S_T * dS_T) with respect to q, k, v, the gates and S0.
 
-    Inputs as ``chunk_fwd``; dO [B, T, H, dv] and dS_T [B, H, dk, dv] are fp32 (dS_T None:
-    zero).  Returns a dict of fp32 tensors dq, dk, dv, dlog_decay, derase, dwrite (None when
-    ``write`` is None: derase then holds the shared gate's whole gradient) and dS0 (None
-    unless ``need_dS0``), each in its input's layout.  ``fg2=True``: ``erase`` is FG2's rate
-    beta, and derase its gradient."""
+    Inputs as ``chunk_fwd`` (or, with ``cu_seqlens``, as ``chunk_fwd_varlen``: [1, T, ...] packed
+    sequences with states [N, H, dk, dv]); dO [B, T, H, dv] and dS_T are fp32 (dS_T None: zero).
+    Returns a dict of fp32 tensors dq, dk, dv, dlog_decay, derase, dwrite (None when ``write``
+    is None: derase then holds the shared gate's whole gradient) and dS0 (None unless
+    ``need_dS0``), each in its input's layout.  ``fg2=True``: ``erase`` is FG2's rate beta, and
+    derase its gradient."""
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(name, t, (torch.float32, torch.bfloat16), dev)
@@ -211,21 +213,33 @@ def chunk_bwd(q, k, v, log_decay, erase, write=None, S0=None, *, dO, dS_T=None, 
             _check_tensor(name, t, (torch.float32,), dev)
     if tuple(dO.shape) != (B, T, H, dv):
         raise ValueError(f"dO must be [B, T, H, dv] = {(B, T, H, dv)}")
+    nstate = B
+    if cu_seqlens is not None:
+        _check_tensor("cu_seqlens", cu_seqlens, (torch.int32,), dev)
+        if B != 1 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("packed sequences: q is [1, T, H, dk] and cu_seqlens holds N + 1 offsets")
+        nstate = cu_seqlens.numel() - 1
     desc = _desc(B, T, H, dk, dv, 0, q.dtype, torch.float32, log_decay, erase, write, (B, T, H), fg2)
     f32 = dict(dtype=torch.float32, device=dev)
     out = dict(dq=torch.empty((B, T, H, dk), **f32), dk=torch.empty((B, T, H, dk), **f32),
                dv=torch.empty((B, T, H, dv), **f32), dlog_decay=torch.empty(log_decay.shape, **f32),
                derase=torch.empty(erase.shape, **f32),
                dwrite=None if write is None else torch.empty(write.shape, **f32),
-               dS0=torch.empty((B, H, dk, dv), **f32) if need_dS0 else None)
-    ws_n = int(_abi.lib().dr_chunk_bwd_workspace_bytes(ctypes.byref(desc)))
+               dS0=torch.empty((nstate, H, dk, dv), **f32) if need_dS0 else None)
+    L = _abi.lib()
+    if cu_seqlens is None:
+        ws_n = int(L.dr_chunk_bwd_workspace_bytes(ctypes.byref(desc)))
+    else:
+        ws_n = int(L.dr_chunk_bwd_varlen_workspace_bytes(ctypes.byref(desc), nstate)) if nstate and T else 0
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
-    st = _abi.lib().dr_chunk_bwd(
-        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(erase), _ptr(write), _ptr(S0),
-        _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_decay"]),
-        _ptr(out["derase"]), _ptr(out["dwrite"]), _ptr(out["dS0"]), _ptr(ws), ws_n, _stream(),
-    )
-    _abi.check("dr_chunk_bwd", st)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(erase), _ptr(write), _ptr(S0), _ptr(dO), _ptr(dS_T),
+            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_decay"]), _ptr(out["derase"]),
+            _ptr(out["dwrite"]), _ptr(out["dS0"]), _ptr(ws), ws_n, _stream())
+    if cu_seqlens is None:
+        _abi.check("dr_chunk_bwd", L.dr_chunk_bwd(ctypes.byref(desc), *args))
+    else:
+        _abi.check("dr_chunk_bwd_varlen",
+                   L.dr_chunk_bwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), nstate, *args))
     return out
 
 

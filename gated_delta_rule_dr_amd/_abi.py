@@ -35,6 +35,8 @@ EXPORTS = (
     "dr_chunk_fwd_varlen",
     "dr_chunk_bwd_workspace_bytes",
     "dr_chunk_bwd",
+    "dr_chunk_bwd_varlen_workspace_bytes",
+    "dr_chunk_bwd_varlen",
     "dr_decode_step",
 )
 
@@ -85,6 +87,10 @@ def lib() -> ctypes.CDLL:
     L.dr_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(DrDesc)]
     L.dr_chunk_bwd.restype = ctypes.c_int
     L.dr_chunk_bwd.argtypes = [ctypes.POINTER(DrDesc)] + [vp] * 17 + [sz, vp]
+    L.dr_chunk_bwd_varlen_workspace_bytes.restype = sz
+    L.dr_chunk_bwd_varlen_workspace_bytes.argtypes = [ctypes.POINTER(DrDesc), ctypes.c_int32]
+    L.dr_chunk_bwd_varlen.restype = ctypes.c_int
+    L.dr_chunk_bwd_varlen.argtypes = [ctypes.POINTER(DrDesc), vp, ctypes.c_int32] + [vp] * 17 + [sz, vp]
     L.dr_decode_step.restype = ctypes.c_int
     L.dr_decode_step.argtypes = [ctypes.POINTER(DrDesc)] + [vp] * 9
     _lib = L

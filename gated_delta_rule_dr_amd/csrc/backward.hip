@@ -106,17 +106,21 @@ __device__ __forceinline__ bool rs_owner(int c) {
   return (N > 8 || (c & 1) == 0) && (N > 4 || (c & 2) == 0) && (N > 2 || (c & 4) == 0) && (N > 1 || (c & 8) == 0);
 }
 
-// Workspace layout of the backward (offsets in floats).
+// Workspace layout of the backward (offsets in floats).  Packed sequences (p.B of them over p.T
+// tokens, one token row each): the checkpoints of sequence n, head h and column group s start at
+// chunk nslice * H * (chunks before n) + (h * nslice + s) * (chunks of n), at most
+// nslice * H * varlen_max_chunks chunks in all.
 struct BwdLayout {
   int64_t nslice, nck, bth;
   int64_t ckpt, states, parts, tmp_dw, total;
-  __host__ __device__ BwdLayout(const Problem& p) {
+  __host__ __device__ BwdLayout(const Problem& p, bool packed) {
     nslice = p.dv / kCols;
     nck = (int64_t(p.T) + CK - 1) / CK;
-    bth = int64_t(p.B) * p.T * p.H;
+    bth = packed ? int64_t(p.T) * p.H : int64_t(p.B) * p.T * p.H;
     const int64_t waves = int64_t(p.B) * p.H * nslice;
-    ckpt = 0;                                             // [waves][nck][dk][16]
-    states = ckpt + waves * nck * p.dk * kCols;           // [waves][CK][dk][16]
+    const int64_t nckpt = packed ? nslice * p.H * varlen_max_chunks(p.B, p.T) : waves * nck;
+    ckpt = 0;                                             // [nckpt][dk][16]
+    states = ckpt + nckpt * p.dk * kCols;                 // [waves][CK][dk][16]
     parts = states + waves * CK * p.dk * kCols;           // [4][nslice][bth][dk]
     tmp_dw = parts + 4 * nslice * bth * p.dk;             // [bth][dv]: v * dv~
     total = tmp_dw + bth * p.dv;
@@ -136,10 +140,20 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
   const int j = slice * kCols + c;
   const int row0 = grp * RPL;
   const bool bf = p.qkv_bf16;
-  const int T = p.T;
-  const BwdLayout L(p);
+  const BwdLayout L(p, p.seqs != nullptr);
   const int64_t wave_id = int64_t(bh) * L.nslice + slice;
+  // this wave's sequence: a dense batch row, or a packed sequence from the table
+  int64_t tok_base = int64_t(b) * p.T;
+  int T = p.T;
+  int64_t nck = L.nck;
   float* ck = ws + L.ckpt + wave_id * L.nck * DK * kCols;
+  if (p.seqs) {
+    const int4 e = p.seqs[b];  // {first token, tokens, H * chunks before, chunks}
+    tok_base = e.x;
+    T = e.y;
+    nck = e.w;
+    ck = ws + L.ckpt + (L.nslice * e.z + int64_t(h * L.nslice + slice) * e.w) * DK * kCols;
+  }
   float* st = ws + L.states + wave_id * CK * DK * kCols;
   // A state slice in the scratch area is stored lane-major (lane l's RPL values contiguous), so
   // that a lane saves or restores its part with RPL / 4 16-byte accesses.
@@ -206,7 +220,7 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
 #pragma unroll
     for (int r = 0; r < RPL; ++r) s[r] = fmaf(-x.e[r] * x.k[r], m, fmaf(x.k[r], wv, s[r]));
   };
-  auto token = [&](int t) { return (int64_t(b) * T + t) * p.H + h; };
+  auto token = [&](int t) { return (tok_base + t) * p.H + h; };
 
   // ---- pass 1: forward, checkpoint every CK tokens -------------------------------------------
   float s[RPL];
@@ -232,7 +246,7 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
   for (int r = 0; r < RPL; ++r) G[r] = g.dS_T ? g.dS_T[sbase + int64_t(row0 + r) * dv] : 0.f;
   float* parts = ws + L.parts;
   const int64_t pstride = L.nslice * L.bth * DK;  // between the four row-part arrays
-  for (int64_t ci = L.nck - 1; ci >= 0; --ci) {
+  for (int64_t ci = nck - 1; ci >= 0; --ci) {
     const int t0 = int(ci * CK), t1 = t0 + CK < T ? t0 + CK : T;
     restore(ck + ci * DK * kCols, s);
     load_tok(nx, token(t0));
@@ -332,7 +346,7 @@ __device__ float block_sum128(float x, float* red) {
 // One workgroup of 128 threads per token (b, t, h); thread i < dk is row i, i < dv column i.
 __global__ __launch_bounds__(128) void bwd_reduce_kernel(Problem p, BwdArgs g, const float* __restrict__ ws) {
   __shared__ float red[2];
-  const BwdLayout L(p);
+  const BwdLayout L(p, p.seqs != nullptr);
   const int64_t tok = blockIdx.x;
   const int i = threadIdx.x;
   const int dk = p.dk, dv = p.dv;
@@ -396,7 +410,24 @@ __global__ __launch_bounds__(128) void bwd_reduce_kernel(Problem p, BwdArgs g, c
 
 }  // namespace
 
-size_t bwd_workspace_bytes(const Problem& p) { return size_t(BwdLayout(p).total) * 4; }
+size_t bwd_workspace_bytes(const Problem& p) { return size_t(BwdLayout(p, false).total) * 4; }
+
+// Packed sequences: the sequence table and the chunk count first, then the layout above.
+static int64_t bwd_tables_bytes(int nseq) { return (int64_t(nseq) * 16 + 255) / 256 * 256 + 256; }
+
+size_t bwd_varlen_workspace_bytes(const Problem& p) {
+  return size_t(bwd_tables_bytes(p.B) + BwdLayout(p, true).total * 4);
+}
+
+hipError_t launch_bwd_varlen(Problem p, const int* cu, const BwdArgs& g, void* workspace, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  int4* seqs = reinterpret_cast<int4*>(ws);
+  int* total = reinterpret_cast<int*>(ws + (int64_t(p.B) * 16 + 255) / 256 * 256);
+  hipError_t e = launch_varlen_setup(cu, p.B, p.T, p.H, CK, seqs, nullptr, total, nullptr, stream);
+  if (e != hipSuccess) return e;
+  p.seqs = seqs;
+  return launch_bwd(p, g, ws + bwd_tables_bytes(p.B), stream);
+}
 
 hipError_t launch_bwd(const Problem& p, const BwdArgs& g, void* workspace, hipStream_t stream) {
   float* ws = static_cast<float*>(workspace);
@@ -410,7 +441,7 @@ hipError_t launch_bwd(const Problem& p, const BwdArgs& g, void* workspace, hipSt
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t bth = int64_t(p.B) * p.T * p.H;
+  const int64_t bth = BwdLayout(p, p.seqs != nullptr).bth;
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(unsigned(bth)), dim3(128), 0, stream, p, g, ws);
   return hipGetLastError();
 }

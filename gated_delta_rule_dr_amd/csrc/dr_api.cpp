@@ -128,6 +128,15 @@ int launched(hipError_t launch_err) {
   return hipGetLastError() == hipSuccess ? DR_OK : DR_E_HIP;
 }
 
+
+// Validation and launch of the gradient call, dense (packed == false) or over nseq packed
+// sequences delimited by cu_seqlens (packed == true: desc->B == 1, states [nseq, H, dk, dv]).
+int chunk_bwd_common(const dr_desc* d, const int32_t* cu_seqlens, int32_t nseq, bool packed, const void* q,
+                     const void* k, const void* v, const float* log_decay, const float* erase, const float* write,
+                     const float* S0, const float* dO, const float* dS_T, float* dq, float* dk, float* dv,
+                     float* dlog_decay, float* derase, float* dwrite, float* dS0, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -281,52 +290,27 @@ int dr_chunk_bwd(const dr_desc* d, const void* q, const void* k, const void* v, 
                  const float* erase, const float* write, const float* S0, const float* dO,
                  const float* dS_T, float* dq, float* dk, float* dv, float* dlog_decay, float* derase,
                  float* dwrite, float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_bwd_common(d, nullptr, 0, false, q, k, v, log_decay, erase, write, S0, dO, dS_T, dq, dk, dv,
+                          dlog_decay, derase, dwrite, dS0, workspace, workspace_bytes, stream);
+}
+
+size_t dr_chunk_bwd_varlen_workspace_bytes(const dr_desc* desc, int32_t nseq) {
   Extents ex;
-  int st = check_desc(d, false, &ex);
-  if (st != DR_OK) return st;
-  const bool need_write = !d->write_is_erase;
-  if (!need_write) dwrite = nullptr;
-  const uint64_t bth = uint64_t(d->B) * uint64_t(d->T) * uint64_t(d->H);
-  const uint64_t g_qk = bth * uint64_t(d->dk) * 4, g_v = bth * uint64_t(d->dv) * 4;
-  const uint64_t g_decay = ex.decay, g_erase = ex.erase, g_write = ex.write;
-  if ((st = check_ptr(q, ex.qk, true)) || (st = check_ptr(k, ex.qk, true)) ||
-      (st = check_ptr(v, ex.v, true)) || (st = check_ptr(log_decay, ex.decay, true)) ||
-      (st = check_ptr(erase, ex.erase, true)) ||
-      (st = check_ptr(need_write ? write : nullptr, ex.write, need_write)) ||
-      (st = check_ptr(S0, ex.state, false)) || (st = check_ptr(dO, g_v, true)) ||
-      (st = check_ptr(dS_T, ex.state, false)) || (st = check_ptr(dq, g_qk, true)) ||
-      (st = check_ptr(dk, g_qk, true)) || (st = check_ptr(dv, g_v, true)) ||
-      (st = check_ptr(dlog_decay, g_decay, true)) || (st = check_ptr(derase, g_erase, true)) ||
-      (st = check_ptr(dwrite, g_write, need_write)) || (st = check_ptr(dS0, ex.state, false)) ||
-      (st = check_ptr(workspace, workspace_bytes, false)))
-    return st;
-  if (workspace_bytes < dr_chunk_bwd_workspace_bytes(d)) return DR_E_WORKSPACE;
-  if (d->T > 0 && workspace == nullptr) return DR_E_WORKSPACE;
+  if (check_desc(desc, false, &ex) != DR_OK || desc->B != 1 || nseq <= 0 || nseq > kMaxSeqs || desc->T == 0)
+    return 0;
+  dr::Problem p = make_problem(desc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                               nullptr);
+  p.B = nseq;
+  return dr::bwd_varlen_workspace_bytes(p);
+}
 
-  const Range rin[] = {range_of(q, ex.qk),        range_of(k, ex.qk),         range_of(v, ex.v),
-                       range_of(log_decay, ex.decay), range_of(erase, ex.erase),
-                       range_of(need_write ? write : nullptr, ex.write), range_of(S0, ex.state),
-                       range_of(dO, g_v),         range_of(dS_T, ex.state)};
-  const Range rout[] = {range_of(dq, g_qk),         range_of(dk, g_qk),         range_of(dv, g_v),
-                        range_of(dlog_decay, g_decay), range_of(derase, g_erase),
-                        range_of(dwrite, g_write),  range_of(dS0, ex.state),
-                        range_of(workspace, workspace_bytes)};
-  const int nout = 8;
-  for (int i = 0; i < nout; ++i) {
-    for (const Range& r : rin)
-      if (overlaps(rout[i], r)) return DR_E_ALIAS;
-    for (int j2 = i + 1; j2 < nout; ++j2)
-      if (overlaps(rout[i], rout[j2])) return DR_E_ALIAS;
-  }
-
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (d->T == 0) {
-    if (dS0 == nullptr) return DR_OK;
-    return launched(dr::launch_state_copy(dS_T, dS0, int64_t(ex.state / 4), s));
-  }
-  dr::Problem p = make_problem(d, q, k, v, log_decay, erase, write, S0, nullptr, nullptr);
-  dr::BwdArgs g{dO, dS_T, dq, dk, dv, dlog_decay, derase, dwrite, dS0};
-  return launched(dr::launch_bwd(p, g, workspace, s));
+int dr_chunk_bwd_varlen(const dr_desc* d, const int32_t* cu_seqlens, int32_t nseq, const void* q, const void* k,
+                        const void* v, const float* log_decay, const float* erase, const float* write,
+                        const float* S0, const float* dO, const float* dS_T, float* dq, float* dk, float* dv,
+                        float* dlog_decay, float* derase, float* dwrite, float* dS0, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return chunk_bwd_common(d, cu_seqlens, nseq, true, q, k, v, log_decay, erase, write, S0, dO, dS_T, dq, dk, dv,
+                          dlog_decay, derase, dwrite, dS0, workspace, workspace_bytes, stream);
 }
 
 int dr_decode_step(const dr_desc* d, const void* q, const void* k, const void* v,
@@ -357,3 +341,80 @@ int dr_decode_step(const dr_desc* d, const void* q, const void* k, const void* v
 }
 
 }  // extern "C"
+
+namespace {
+
+int chunk_bwd_common(const dr_desc* d, const int32_t* cu_seqlens, int32_t nseq, bool packed, const void* q,
+                     const void* k, const void* v, const float* log_decay, const float* erase, const float* write,
+                     const float* S0, const float* dO, const float* dS_T, float* dq, float* dk, float* dv,
+                     float* dlog_decay, float* derase, float* dwrite, float* dS0, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  Extents ex;
+  int st = check_desc(d, false, &ex);
+  if (st != DR_OK) return st;
+  uint64_t cu_bytes = 0;
+  if (packed) {
+    if (d->B != 1 || nseq < 0 || nseq > kMaxSeqs) return DR_E_SHAPE;
+    const uint64_t state_elems = uint64_t(nseq) * uint64_t(d->H) * uint64_t(d->dk) * uint64_t(d->dv);
+    if (state_elems > kMaxElems) return DR_E_SHAPE;
+    ex.state = state_elems * 4;
+    cu_bytes = (uint64_t(nseq) + 1) * 4;
+    if (cu_seqlens == nullptr) {
+      if (nseq > 0) return DR_E_NULL;
+    } else if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) {
+      return DR_E_ALIGN;
+    }
+  }
+  const bool need_write = !d->write_is_erase;
+  if (!need_write) dwrite = nullptr;
+  const uint64_t bth = uint64_t(d->B) * uint64_t(d->T) * uint64_t(d->H);
+  const uint64_t g_qk = bth * uint64_t(d->dk) * 4, g_v = bth * uint64_t(d->dv) * 4;
+  const uint64_t g_decay = ex.decay, g_erase = ex.erase, g_write = ex.write;
+  if ((st = check_ptr(q, ex.qk, true)) || (st = check_ptr(k, ex.qk, true)) ||
+      (st = check_ptr(v, ex.v, true)) || (st = check_ptr(log_decay, ex.decay, true)) ||
+      (st = check_ptr(erase, ex.erase, true)) ||
+      (st = check_ptr(need_write ? write : nullptr, ex.write, need_write)) ||
+      (st = check_ptr(S0, ex.state, false)) || (st = check_ptr(dO, g_v, true)) ||
+      (st = check_ptr(dS_T, ex.state, false)) || (st = check_ptr(dq, g_qk, true)) ||
+      (st = check_ptr(dk, g_qk, true)) || (st = check_ptr(dv, g_v, true)) ||
+      (st = check_ptr(dlog_decay, g_decay, true)) || (st = check_ptr(derase, g_erase, true)) ||
+      (st = check_ptr(dwrite, g_write, need_write)) || (st = check_ptr(dS0, ex.state, false)) ||
+      (st = check_ptr(workspace, workspace_bytes, false)))
+    return st;
+  const bool work = d->T > 0 && (!packed || nseq > 0);
+  const size_t need = !work ? 0 : packed ? dr_chunk_bwd_varlen_workspace_bytes(d, nseq) : dr_chunk_bwd_workspace_bytes(d);
+  if (workspace_bytes < need) return DR_E_WORKSPACE;
+  if (work && workspace == nullptr) return DR_E_WORKSPACE;
+
+  const Range rin[] = {range_of(q, ex.qk),        range_of(k, ex.qk),         range_of(v, ex.v),
+                       range_of(log_decay, ex.decay), range_of(erase, ex.erase),
+                       range_of(need_write ? write : nullptr, ex.write), range_of(S0, ex.state),
+                       range_of(dO, g_v),         range_of(dS_T, ex.state),   range_of(cu_seqlens, cu_bytes)};
+  const Range rout[] = {range_of(dq, g_qk),         range_of(dk, g_qk),         range_of(dv, g_v),
+                        range_of(dlog_decay, g_decay), range_of(derase, g_erase),
+                        range_of(dwrite, g_write),  range_of(dS0, ex.state),
+                        range_of(workspace, workspace_bytes)};
+  const int nout = 8;
+  for (int i = 0; i < nout; ++i) {
+    for (const Range& r : rin)
+      if (overlaps(rout[i], r)) return DR_E_ALIAS;
+    for (int j2 = i + 1; j2 < nout; ++j2)
+      if (overlaps(rout[i], rout[j2])) return DR_E_ALIAS;
+  }
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (packed && nseq == 0) return DR_OK;
+  if (d->T == 0) {
+    if (dS0 == nullptr) return DR_OK;
+    return launched(dr::launch_state_copy(dS_T, dS0, int64_t(ex.state / 4), s));
+  }
+  dr::Problem p = make_problem(d, q, k, v, log_decay, erase, write, S0, nullptr, nullptr);
+  dr::BwdArgs g{dO, dS_T, dq, dk, dv, dlog_decay, derase, dwrite, dS0};
+  if (packed) {
+    p.B = nseq;
+    return launched(dr::launch_bwd_varlen(p, cu_seqlens, g, workspace, s));
+  }
+  return launched(dr::launch_bwd(p, g, workspace, s));
+}
+
+}  // namespace

@@ -46,7 +46,7 @@ hipError_t launch_varlen_setup(const int* cu, int nseq, int T, int H, int chunk,
                                int* total, int* order, hipStream_t stream);
 
 // Upper bound on the chunks of nseq sequences with T tokens in all: sum ceil(len / 64).
-inline int64_t varlen_max_chunks(int64_t nseq, int64_t T) { return (T + 63 * nseq) / 64; }
+__host__ __device__ inline int64_t varlen_max_chunks(int64_t nseq, int64_t T) { return (T + 63 * nseq) / 64; }
 
 // fp32 token-by-token recurrence: any supported dk/dv/dtypes.  Reads S0 before writing S_T
 // element by element in the same thread, so S0 == S_T is safe.
@@ -87,6 +87,9 @@ struct BwdArgs {
 };
 size_t bwd_workspace_bytes(const Problem& p);
 hipError_t launch_bwd(const Problem& p, const BwdArgs& g, void* workspace, hipStream_t stream);
+// The same over p.B packed sequences delimited by the device offsets `cu` (p.T packed tokens).
+size_t bwd_varlen_workspace_bytes(const Problem& p);
+hipError_t launch_bwd_varlen(Problem p, const int* cu, const BwdArgs& g, void* workspace, hipStream_t stream);
 
 // S_T = S0 (copy) or zeros when S0 is null: n floats.
 hipError_t launch_state_copy(const float* S0, float* S_T, int64_t n, hipStream_t stream);

@@ -195,6 +195,20 @@ int dr_chunk_bwd(const dr_desc* desc, const void* q, const void* k, const void* 
                  float* dlog_decay, float* derase, float* dwrite, float* dS0, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/* Gradients over a packed batch of nseq sequences (the layouts and offsets of
+ * dr_chunk_fwd_varlen; desc->B must be 1): every gradient as dr_chunk_bwd, with S0, dS_T and dS0
+ * [nseq, H, dk, dv].  The offsets are clamped as for dr_chunk_fwd_varlen; gradient rows of
+ * tokens in no sequence (possible only with invalid offsets) are left unspecified.  Errors as
+ * dr_chunk_bwd plus those of the offsets as in dr_chunk_fwd_varlen. */
+size_t dr_chunk_bwd_varlen_workspace_bytes(const dr_desc* desc, int32_t nseq);
+
+int dr_chunk_bwd_varlen(const dr_desc* desc, const int32_t* cu_seqlens, int32_t nseq, const void* q,
+                        const void* k, const void* v, const float* log_decay, const float* erase,
+                        const float* write, const float* S0, const float* dO, const float* dS_T,
+                        float* dq, float* dk, float* dv, float* dlog_decay, float* derase,
+                        float* dwrite, float* dS0, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 /* One decode token for B independent sequences (desc->T must be 1): reads q, k, v, gates in
  * the [B, 1, H, d] layouts above, updates S [B, H, dk, dv] in place and writes o [B, 1, H, dv].
  * The state streams through once (read once, written once).  o must not overlap any input

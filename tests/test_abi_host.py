@@ -278,3 +278,32 @@ def test_bwd_workspace_and_errors():
     assert _bwd(d, dv=P["v"]) == _abi.DR_E_ALIAS  # output on an input
     assert _bwd(d, ws=PG["dO"], wsn=need) == _abi.DR_E_ALIAS
     assert _bwd(d, wsn=need - 1) == _abi.DR_E_WORKSPACE
+
+
+
+def test_bwd_varlen_workspace_and_errors():
+    L = _abi.lib()
+    d = _good_desc(B=1, T=1000, H=4, dk=128, dv=128)
+    nseq = 5
+    maxc = (1000 + 63 * nseq) // 64
+    nslice, waves, bth = 8, nseq * 4 * 8, 1000 * 4
+    tables = (16 * nseq + 255) // 256 * 256 + 256
+    layout = 4 * (nslice * 4 * maxc * 128 * 16 + waves * 64 * 128 * 16 + 4 * nslice * bth * 128 + bth * 128)
+    assert L.dr_chunk_bwd_varlen_workspace_bytes(ctypes.byref(d), nseq) == tables + layout
+    assert L.dr_chunk_bwd_varlen_workspace_bytes(ctypes.byref(_good_desc(B=2)), nseq) == 0
+    assert L.dr_chunk_bwd_varlen_workspace_bytes(ctypes.byref(d), 0) == 0
+    ptr = dict(P)
+    ptr.update(PG)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    names = ["q", "k", "v", "ld", "e", "w", "S0", "dO", "dST", "dq", "dk", "dv", "dla", "de", "dw", "dS0", "ws"]
+
+    def call(desc, cu=P_CU, n=nseq, **over):
+        pp = dict(ptr)
+        pp.update(over)
+        return L.dr_chunk_bwd_varlen(ctypes.byref(desc), vp(cu), n, *[vp(pp[x]) for x in names], 1 << 40, None)
+
+    assert call(_good_desc(B=2)) == _abi.DR_E_SHAPE
+    assert call(d, cu=None) == _abi.DR_E_NULL
+    assert call(d, cu=P_CU + 2) == _abi.DR_E_ALIGN
+    assert call(d, dq=P_CU) == _abi.DR_E_ALIAS  # an output on the offsets
+    assert call(d, n=-1) == _abi.DR_E_SHAPE

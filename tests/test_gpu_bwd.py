@@ -126,3 +126,32 @@ def test_bwd_fg2_rate(dr, decay_channel, d):
     errs = {key: _err(out[key], ref[key]) for key in ("dq", "dk", "dv", "dlog_decay", "dS0")}
     errs["dbeta"] = _err(out["derase"], ref["dbeta"])
     assert max(errs.values()) <= TOL, errs
+
+
+@pytest.mark.parametrize("variant", ["scalar", "decoupled"])
+def test_bwd_packed_sequences(dr, variant):
+    # packed sequences (one empty, ragged lengths): each sequence's gradients equal the dense
+    # adjoint over its own tokens from its own state
+    lens = [70, 0, 1, 129, 64]
+    inp, dO, _ = _case(1, sum(lens), 2, 128, 128, "bf16", variant, False, 600)
+    g = torch.Generator().manual_seed(601)
+    N = len(lens)
+    S0 = (0.05 * torch.randn((N, 2, 128, 128), generator=g, dtype=torch.float64)).float()
+    dST = torch.randn((N, 2, 128, 128), generator=g, dtype=torch.float64).float()
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    out = dr.chunk_bwd(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"], S0.cuda(), dO=dO.cuda(),
+                       dS_T=dST.cuda(), cu_seqlens=torch.tensor(cu, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    for n in range(N):
+        lo, hi = int(cu[n]), int(cu[n + 1])
+        if hi == lo:
+            assert torch.equal(out["dS0"][n].cpu(), dST[n])
+            continue
+        cut = lambda key: None if inp[key] is None else inp[key][:, lo:hi]
+        ref = recurrence_bwd(cut("q"), cut("k"), cut("v"), cut("log_decay"), cut("erase"), cut("write"), S0[n:n + 1],
+                             dO=dO[:, lo:hi], dS_T=dST[n:n + 1])
+        for key in ("dq", "dk", "dv", "dlog_decay", "derase", "dwrite"):
+            if ref[key] is not None:
+                assert _err(out[key][:, lo:hi], ref[key]) <= TOL, (n, key)
+        assert _err(out["dS0"][n:n + 1], ref["dS0"]) <= TOL, n
