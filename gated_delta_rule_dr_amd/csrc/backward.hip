@@ -11,14 +11,14 @@
 //     G' = G + k dm^T;  d(log a) = a * rowsum(G' * S_{t-1});  G = Diag(a) G'
 // and dS0 is G after token 0.
 //
-// Kernel 1, one wave per (b, h, group of 16 value columns), with the token kernel's mapping
-// (lane = column (16) x row group (4), dk / 4 rows of one column per lane):
+// Kernel 1, one wave per (b, h, group of 8 value columns; 16 where dk = 16): lane = column x
+// row group (8 x 8, or 16 x 4), dk / 8 (dk / 4) rows of one column per lane:
 //   pass 1 runs the forward and stores the state at the start of every 64-token chunk;
 //   pass 2 takes the chunks backwards: it recomputes the chunk's states from its checkpoint
 //   into a scratch area of its own, then walks the chunk's tokens backwards through the adjoint
-//   above.  Column sums (m, dm, dv~) are lane sums plus two cross-lane steps; row sums (the
-//   per-row parts of dq, du, dk and d(log a), summed over this wave's 16 columns) are reduced
-//   over the 16 column lanes and stored per column group.
+//   above.  Column sums (m, dm, dv~) are lane sums plus cross-lane steps; row sums (the per-row
+//   parts of dq, du, dk and d(log a), summed over this wave's columns) are reduced over the
+//   column lanes and stored per column group.
 // Kernel 2 sums the column groups' row parts, applies the per-row factors (e, k, a) and forms
 // the gate gradients (summed over channels for a per-head gate; the erase and write parts added
 // for a shared gate).
@@ -31,15 +31,26 @@
 namespace dr {
 namespace {
 
-constexpr int kCols = 16;   // value columns per wave
-constexpr int kGroups = 4;  // row groups per wave
-constexpr int CK = 64;      // tokens per checkpoint
+constexpr int CK = 64;  // tokens per checkpoint
 
-// Sum over the 4 lanes of one column (lanes c, c + 16, c + 32, c + 48), in every one of them,
-// with the gfx950 row swaps: swapping rows 1 <-> 0 and 3 <-> 2 of a value with itself and adding
-// both results gives each lane the sum of its pair of rows; the half-wave swap then adds the
-// other pair.  Both lanes of a pair add in the same order, so all four hold the same sum.
+// Value columns per wave: 8 (row groups of 8 lanes, dk / 8 rows per lane) where dk >= 32, else
+// 16 (dk / 4 rows per lane; a lane holds at least four rows either way).
+__host__ __device__ constexpr int cols_for(int dk) { return dk >= 32 ? 8 : 16; }
+
+// x of the lane that the DPP control CTRL selects within this lane's row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the lanes of one column (lanes c + COLS i), in every one of them: with 8 columns a
+// row rotation by 8 first adds the other half-row; then the gfx950 row swaps: swapping rows
+// 1 <-> 0 and 3 <-> 2 of a value with itself and adding both results gives each lane the sum of
+// its pair of rows, and the half-wave swap adds the other pair.  Paired lanes add in the same
+// order, so every lane of the column holds the same sum.
+template <int COLS>
 __device__ __forceinline__ float group_sum(float x) {
+  if constexpr (COLS == 8) x += dpp<0x128>(x);  // row rotate by 8: the other half-row
   const unsigned u = __float_as_uint(x);
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -48,30 +59,12 @@ __device__ __forceinline__ float group_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// x of the lane that the DPP control CTRL selects within this lane's row of 16 lanes.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
-// Sum over the 16 lanes of one row group (one DPP row), left in every one of them: swap lanes
-// 1 apart and 2 apart within each quad (quad permutations [1,0,3,2] and [2,3,0,1]), then mirror
-// within each half-row and within the row.  These run on the vector ALU; a cross-lane shuffle
-// would take a round trip through the LDS crossbar for every value.
-__device__ __forceinline__ float column_sum(float x) {
-  x += dpp<0xB1>(x);
-  x += dpp<0x4E>(x);
-  x += dpp<0x141>(x);
-  x += dpp<0x140>(x);
-  return x;
-}
-
-// Reduce-scatter of N values per lane over the 16 lanes of a row group: four DPP pairings
-// (row mirror, half-row mirror, quad swaps 2 and 1 apart); at each one a lane keeps the half of
-// its values that its lane bit selects, adds the partner's copy of that half, and sends the
-// other half.  Afterwards lane c holds the full sums of rows rs_row<N>(c) .. + rs_count<N> - 1
-// in v[0 ..]; with N < 16 some pairings find a single value left and just add the partner's,
-// so several lanes hold the same rows (rs_owner<N> marks one of them).
+// Reduce-scatter of N values per lane over the COLS lanes of a row group: DPP pairings (row
+// mirror for 16 columns, then half-row mirror, quad swaps 2 and 1 apart); at each one a lane
+// keeps the half of its values that its lane bit selects, adds the partner's copy of that half,
+// and sends the other half.  Afterwards lane c holds the full sums of rows rs_row(c) .. +
+// rs_count - 1 in v[0 ..]; when fewer values than lanes remain, a pairing finds a single value
+// and just adds the partner's, so several lanes hold the same rows (rs_owner marks one).
 template <int CTRL, int BIT, int N>
 __device__ __forceinline__ void rs_stage(float* v, int c) {
   if constexpr (N > 1) {
@@ -87,23 +80,36 @@ __device__ __forceinline__ void rs_stage(float* v, int c) {
     v[0] += dpp<CTRL>(v[0]);
   }
 }
-template <int N>
+template <int COLS, int N>
 __device__ __forceinline__ void row_scatter_sum(float* v, int c) {
-  rs_stage<0x140, 3, N>(v, c);
-  rs_stage<0x141, 2, (N > 1 ? N / 2 : 1)>(v, c);
-  rs_stage<0x4E, 1, (N > 2 ? N / 4 : 1)>(v, c);
-  rs_stage<0xB1, 0, (N > 4 ? N / 8 : 1)>(v, c);
+  if constexpr (COLS == 16) {
+    rs_stage<0x140, 3, N>(v, c);
+    rs_stage<0x141, 2, (N > 1 ? N / 2 : 1)>(v, c);
+    rs_stage<0x4E, 1, (N > 2 ? N / 4 : 1)>(v, c);
+    rs_stage<0xB1, 0, (N > 4 ? N / 8 : 1)>(v, c);
+  } else {
+    rs_stage<0x141, 2, N>(v, c);
+    rs_stage<0x4E, 1, (N > 1 ? N / 2 : 1)>(v, c);
+    rs_stage<0xB1, 0, (N > 2 ? N / 4 : 1)>(v, c);
+  }
 }
-template <int N>
+template <int COLS, int N>
 __device__ __forceinline__ int rs_row(int c) {
-  return (N > 1 ? (N / 2) * ((c >> 3) & 1) : 0) + (N > 2 ? (N / 4) * ((c >> 2) & 1) : 0) +
-         (N > 4 ? (N / 8) * ((c >> 1) & 1) : 0) + (N > 8 ? (N / 16) * (c & 1) : 0);
+  if constexpr (COLS == 16)
+    return (N > 1 ? (N / 2) * ((c >> 3) & 1) : 0) + (N > 2 ? (N / 4) * ((c >> 2) & 1) : 0) +
+           (N > 4 ? (N / 8) * ((c >> 1) & 1) : 0) + (N > 8 ? (N / 16) * (c & 1) : 0);
+  else
+    return (N > 1 ? (N / 2) * ((c >> 2) & 1) : 0) + (N > 2 ? (N / 4) * ((c >> 1) & 1) : 0) +
+           (N > 4 ? (N / 8) * (c & 1) : 0);
 }
-template <int N>
-constexpr int rs_count = N >= 16 ? N / 16 : 1;
-template <int N>
+template <int COLS, int N>
+constexpr int rs_count = N >= COLS ? N / COLS : 1;
+template <int COLS, int N>
 __device__ __forceinline__ bool rs_owner(int c) {
-  return (N > 8 || (c & 1) == 0) && (N > 4 || (c & 2) == 0) && (N > 2 || (c & 4) == 0) && (N > 1 || (c & 8) == 0);
+  if constexpr (COLS == 16)
+    return (N > 8 || (c & 1) == 0) && (N > 4 || (c & 2) == 0) && (N > 2 || (c & 4) == 0) && (N > 1 || (c & 8) == 0);
+  else
+    return (N > 4 || (c & 1) == 0) && (N > 2 || (c & 2) == 0) && (N > 1 || (c & 4) == 0);
 }
 
 // Workspace layout of the backward (offsets in floats).  Packed sequences (p.B of them over p.T
@@ -114,14 +120,15 @@ struct BwdLayout {
   int64_t nslice, nck, bth;
   int64_t ckpt, states, parts, tmp_dw, total;
   __host__ __device__ BwdLayout(const Problem& p, bool packed) {
-    nslice = p.dv / kCols;
+    nslice = p.dv / cols_for(p.dk);
     nck = (int64_t(p.T) + CK - 1) / CK;
     bth = packed ? int64_t(p.T) * p.H : int64_t(p.B) * p.T * p.H;
     const int64_t waves = int64_t(p.B) * p.H * nslice;
     const int64_t nckpt = packed ? nslice * p.H * varlen_max_chunks(p.B, p.T) : waves * nck;
-    ckpt = 0;                                             // [nckpt][dk][16]
-    states = ckpt + nckpt * p.dk * kCols;                 // [waves][CK][dk][16]
-    parts = states + waves * CK * p.dk * kCols;           // [4][nslice][bth][dk]
+    const int cols = cols_for(p.dk);
+    ckpt = 0;                                             // [nckpt][dk][cols]
+    states = ckpt + nckpt * p.dk * cols;                  // [waves][CK][dk][cols]
+    parts = states + waves * CK * p.dk * cols;            // [4][nslice][bth][dk]
     tmp_dw = parts + 4 * nslice * bth * p.dk;             // [bth][dv]: v * dv~
     total = tmp_dw + bth * p.dv;
   }
@@ -129,10 +136,11 @@ struct BwdLayout {
 
 template <int DK>
 __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, float* __restrict__ ws) {
-  constexpr int RPL = DK / kGroups;
+  constexpr int kCols = cols_for(DK);
+  constexpr int RPL = DK * kCols / 64;  // rows per lane
   const int lane = threadIdx.x;
   const int c = lane & (kCols - 1);
-  const int grp = lane >> 4;
+  const int grp = lane / kCols;
   const int bh = blockIdx.x;
   const int b = bh / p.H, h = bh - b * p.H;
   const int dv = p.dv;
@@ -215,7 +223,7 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
       s[r] *= x.a[r];
       m = fmaf(x.k[r], s[r], m);
     }
-    m = group_sum(m);
+    m = group_sum<kCols>(m);
     const float wv = x.w * x.v;
 #pragma unroll
     for (int r = 0; r < RPL; ++r) s[r] = fmaf(-x.e[r] * x.k[r], m, fmaf(x.k[r], wv, s[r]));
@@ -280,17 +288,17 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
       float m = 0.f;
 #pragma unroll
       for (int r = 0; r < RPL; ++r) m = fmaf(x.k[r], x.a[r] * sp[r], m);
-      m = group_sum(m);
+      m = group_sum<kCols>(m);
       const float vw = x.w * x.v;
       // row parts, summed over this wave's 16 columns (reduce-scatter: lane c stores rows
       // rs_row(c) ..)
-      float* pbase = parts + (int64_t(slice) * L.bth + tok) * DK + row0 + rs_row<RPL>(c);
-      const bool owner = rs_owner<RPL>(c);
+      float* pbase = parts + (int64_t(slice) * L.bth + tok) * DK + row0 + rs_row<kCols, RPL>(c);
+      const bool owner = rs_owner<kCols, RPL>(c);
       auto put = [&](float* part, int which) {
-        row_scatter_sum<RPL>(part, c);
+        row_scatter_sum<kCols, RPL>(part, c);
         if (owner) {
 #pragma unroll
-          for (int i = 0; i < rs_count<RPL>; ++i) pbase[which * pstride + i] = part[i];
+          for (int i = 0; i < rs_count<kCols, RPL>; ++i) pbase[which * pstride + i] = part[i];
         }
       };
       float dm = 0.f, dvw = 0.f;
@@ -307,8 +315,8 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
       }
       put(pa, 0);
       put(pb, 1);
-      dm = group_sum(dm);
-      dvw = group_sum(dvw);
+      dm = group_sum<kCols>(dm);
+      dvw = group_sum<kCols>(dvw);
 #pragma unroll
       for (int r = 0; r < RPL; ++r) {
         const float Sp = x.a[r] * sp[r];
@@ -431,7 +439,7 @@ hipError_t launch_bwd_varlen(Problem p, const int* cu, const BwdArgs& g, void* w
 
 hipError_t launch_bwd(const Problem& p, const BwdArgs& g, void* workspace, hipStream_t stream) {
   float* ws = static_cast<float*>(workspace);
-  dim3 grid(unsigned(p.B * p.H), unsigned(p.dv / kCols));
+  dim3 grid(unsigned(p.B * p.H), unsigned(p.dv / cols_for(p.dk)));
   switch (p.dk) {
     case 16: hipLaunchKernelGGL(bwd_token_kernel<16>, grid, dim3(64), 0, stream, p, g, ws); break;
     case 32: hipLaunchKernelGGL(bwd_token_kernel<32>, grid, dim3(64), 0, stream, p, g, ws); break;

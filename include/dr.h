@@ -180,10 +180,10 @@ int dr_chunk_fwd_varlen(const dr_desc* desc, const int32_t* cu_seqlens, int32_t 
  *          gate gets the sum over its channels).  With write_is_erase the one gate's gradient
  *          (both uses) goes to derase and dwrite is ignored.
  *   dS0    [B, H, dk, dv] fp32, or NULL to skip.
- *   workspace: at least dr_chunk_bwd_workspace_bytes(desc) bytes: the checkpoints and each
- *          wave's chunk of states (128 KB per chunk per (b, h) at dk = dv = 128), one chunk's
- *          states per (b, h, 16 value columns), and per-row partial sums for each group of 16
- *          value columns (64 dv / 16 dk bytes per token and head).
+ *   workspace: at least dr_chunk_bwd_workspace_bytes(desc) bytes: a state checkpoint every 64
+ *          tokens and one chunk of states per (b, h, group of 8 value columns; 16 where
+ *          dk = 16), and four fp32 partial sums per row for each group (at dk = dv = 128,
+ *          32 KB per token and head: 8.6 GB for B 4, H 16, T 4096).
  * Outputs must not overlap one another, any input or the workspace.  T == 0 writes dS0 = dS_T
  * (zeros without it).  With DR_GATE_RATE_SQRT, derase is the gradient of the rate beta (through
  * both sqrt(beta) k and sqrt(beta) v).  Errors as dr_chunk_fwd. */
