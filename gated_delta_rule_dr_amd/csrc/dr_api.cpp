@@ -151,7 +151,7 @@ const char* dr_status_str(int status) {
     case DR_E_DTYPE: return "unknown dtype or gate kind";
     case DR_E_ALIGN: return "pointer not 16-byte aligned";
     case DR_E_ALIAS: return "an output overlaps an input";
-    case DR_E_UNSUPPORTED: return "combination not supported by this build";
+    case DR_E_UNSUPPORTED: return "combination not supported by this library";
     case DR_E_WORKSPACE: return "workspace missing or too small";
     case DR_E_HIP: return "HIP launch failed";
     default: return "unknown status";

@@ -57,7 +57,7 @@ typedef enum {
   DR_E_DTYPE = -3,       /* unknown dtype or gate-kind code */
   DR_E_ALIGN = -4,       /* a pointer is not 16-byte aligned */
   DR_E_ALIAS = -5,       /* an output overlaps an input (other than the allowed S0 == S_T) */
-  DR_E_UNSUPPORTED = -6, /* a valid combination this build does not implement */
+  DR_E_UNSUPPORTED = -6, /* a valid combination this library does not implement */
   DR_E_WORKSPACE = -7,   /* workspace missing or smaller than dr_chunk_fwd_workspace_bytes */
   DR_E_HIP = -8          /* a HIP launch failed */
 } dr_status;
