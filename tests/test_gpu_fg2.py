@@ -122,3 +122,14 @@ def test_fg2_rejects_mismatched_gates(dr):
         dr.chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"][..., 0].contiguous(), fg2=True)
     with pytest.raises(ValueError):  # FG2's rate is the write gate too
         dr.chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["erase"], fg2=True)
+
+
+def test_fg2_bf16_output_wide_slices(dr):
+    inp = _case(1, 150, 64, 128, "bf16", True, True, 93)
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    o, S = dr.chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], None, d["S0"], fg2=True,
+                        o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ro, rS = _oracle(inp)
+    eo, eS = err_o(o.float(), ro), err_S(S, rS)
+    assert o.dtype == torch.bfloat16 and eo <= TOL_BF16 + 2.0 ** -8 and eS <= TOL_BF16, (eo, eS)

@@ -181,3 +181,19 @@ def test_varlen_no_tokens(dr):
     inp0 = dict(inp, S0=None, cu_seqlens=torch.zeros(1, dtype=torch.int32))
     o, S = _run(dr, inp0)
     assert o.shape == (1, 0, 2, 128) and S.shape == (0, 2, 128, 128)
+
+
+def test_varlen_bf16_output_and_determinism(dr):
+    # bf16 o through the packed path (32-column slices, staged o rows), and two identical calls
+    lens = [130, 3, 64, 257]
+    inp = _packed(lens, 16, "scalar", seed=15)
+    dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    call = lambda: dr.chunk_fwd_varlen(dev["q"], dev["k"], dev["v"], dev["log_decay"], dev["erase"], None,
+                                       dev["S0"], cu_seqlens=dev["cu_seqlens"], o_dtype=torch.bfloat16)
+    o1, S1 = call()
+    o2, S2 = call()
+    torch.cuda.synchronize()
+    assert o1.dtype == torch.bfloat16 and torch.equal(o1, o2) and torch.equal(S1, S2)
+    ro, rS = _oracle(inp)
+    eo, eS = _errs_per_sequence(o1.float(), S1, ro, rS, inp["cu_seqlens"].numpy())
+    assert eo <= TOL_BF16 + 2.0 ** -8 and eS <= TOL_BF16, (eo, eS)
