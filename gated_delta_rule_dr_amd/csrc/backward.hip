@@ -19,11 +19,13 @@
 //   above.  Column sums (m, dm, dv~) are lane sums plus cross-lane steps; row sums (the per-row
 //   parts of dq, du, dk and d(log a), summed over this wave's columns) are reduced over the
 //   column lanes and stored per column group.
-// Kernel 2 sums the column groups' row parts, applies the per-row factors (e, k, a) and forms
+// Up to four column groups of one (b, h) share a workgroup and sum their row parts in LDS before
+// storing them, so one row part per workgroup reaches memory.
+// Kernel 2 sums the workgroups' row parts, applies the per-row factors (e, k, a) and forms
 // the gate gradients (summed over channels for a per-head gate; the erase and write parts added
 // for a shared gate).
-// Every state value is read and written by the lane that owns it, so neither pass needs a
-// barrier; the two kernels are ordered by the stream.
+// Every state value is read and written by the lane that owns it; the only barrier is the one
+// per token before the LDS sum.  The two kernels are ordered by the stream.
 
 #include "dr_device.h"
 #include "dr_internal.h"
@@ -118,9 +120,13 @@ __device__ __forceinline__ bool rs_owner(int c) {
 // nslice * H * varlen_max_chunks chunks in all.
 struct BwdLayout {
   int64_t nslice, nck, bth;
+  int wpg;          // column groups (waves) per workgroup: their row parts are summed in LDS
+  int64_t ngroups;  // workgroups per (b, h): one stored row part each
   int64_t ckpt, states, parts, tmp_dw, total;
   __host__ __device__ BwdLayout(const Problem& p, bool packed) {
     nslice = p.dv / cols_for(p.dk);
+    wpg = nslice >= 4 ? 4 : int(nslice);
+    ngroups = nslice / wpg;
     nck = (int64_t(p.T) + CK - 1) / CK;
     bth = packed ? int64_t(p.T) * p.H : int64_t(p.B) * p.T * p.H;
     const int64_t waves = int64_t(p.B) * p.H * nslice;
@@ -128,23 +134,25 @@ struct BwdLayout {
     const int cols = cols_for(p.dk);
     ckpt = 0;                                             // [nckpt][dk][cols]
     states = ckpt + nckpt * p.dk * cols;                  // [waves][CK][dk][cols]
-    parts = states + waves * CK * p.dk * cols;            // [4][nslice][bth][dk]
-    tmp_dw = parts + 4 * nslice * bth * p.dk;             // [bth][dv]: v * dv~
+    parts = states + waves * CK * p.dk * cols;            // [4][ngroups][bth][dk]
+    tmp_dw = parts + 4 * ngroups * bth * p.dk;            // [bth][dv]: v * dv~
     total = tmp_dw + bth * p.dv;
   }
 };
 
 template <int DK>
-__global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, float* __restrict__ ws) {
+__global__ __launch_bounds__(256) void bwd_token_kernel(Problem p, BwdArgs g, float* __restrict__ ws) {
   constexpr int kCols = cols_for(DK);
   constexpr int RPL = DK * kCols / 64;  // rows per lane
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int c = lane & (kCols - 1);
   const int grp = lane / kCols;
   const int bh = blockIdx.x;
   const int b = bh / p.H, h = bh - b * p.H;
   const int dv = p.dv;
-  const int slice = blockIdx.y;
+  const int nw = blockDim.x >> 6;  // column groups in this workgroup
+  const int slice = blockIdx.y * nw + wave;
   const int j = slice * kCols + c;
   const int row0 = grp * RPL;
   const bool bf = p.qkv_bf16;
@@ -253,7 +261,9 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
 #pragma unroll
   for (int r = 0; r < RPL; ++r) G[r] = g.dS_T ? g.dS_T[sbase + int64_t(row0 + r) * dv] : 0.f;
   float* parts = ws + L.parts;
-  const int64_t pstride = L.nslice * L.bth * DK;  // between the four row-part arrays
+  const int64_t pstride = L.ngroups * L.bth * DK;  // between the four row-part arrays
+  // the workgroup's column groups' row parts of one token, alternating between two buffers
+  __shared__ float red[2][4][4][DK];
   for (int64_t ci = nck - 1; ci >= 0; --ci) {
     const int t0 = int(ci * CK), t1 = t0 + CK < T ? t0 + CK : T;
     restore(ck + ci * DK * kCols, s);
@@ -290,15 +300,16 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
       for (int r = 0; r < RPL; ++r) m = fmaf(x.k[r], x.a[r] * sp[r], m);
       m = group_sum<kCols>(m);
       const float vw = x.w * x.v;
-      // row parts, summed over this wave's 16 columns (reduce-scatter: lane c stores rows
-      // rs_row(c) ..)
-      float* pbase = parts + (int64_t(slice) * L.bth + tok) * DK + row0 + rs_row<kCols, RPL>(c);
+      // row parts, summed over this wave's columns (reduce-scatter: lane c holds rows
+      // rs_row(c) ..), then over the workgroup's column groups through LDS
+      const int buf = t & 1;
+      const int prow = row0 + rs_row<kCols, RPL>(c);
       const bool owner = rs_owner<kCols, RPL>(c);
       auto put = [&](float* part, int which) {
         row_scatter_sum<kCols, RPL>(part, c);
         if (owner) {
 #pragma unroll
-          for (int i = 0; i < rs_count<kCols, RPL>; ++i) pbase[which * pstride + i] = part[i];
+          for (int i = 0; i < rs_count<kCols, RPL>; ++i) red[buf][wave][which][prow + i] = part[i];
         }
       };
       float dm = 0.f, dvw = 0.f;
@@ -327,6 +338,15 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(Problem p, BwdArgs g, flo
       }
       put(pa, 2);
       put(pb, 3);
+      // Every wave of the workgroup walks the same tokens, so all meet here; a buffer is written
+      // again two tokens later, after the next token's barrier, which every reader has passed.
+      lds_barrier();
+      for (int i = threadIdx.x; i < 4 * DK; i += blockDim.x) {
+        const int which = i / DK, row = i - which * DK;
+        float sum = 0.f;
+        for (int w = 0; w < nw; ++w) sum += red[buf][w][which][row];
+        parts[which * pstride + (int64_t(blockIdx.y) * L.bth + tok) * DK + row] = sum;
+      }
       if (grp == 0) {
         g.dv[tok * dv + j] = x.w * dvw;
         ws[L.tmp_dw + tok * dv + j] = x.v * dvw;
@@ -359,11 +379,11 @@ __global__ __launch_bounds__(128) void bwd_reduce_kernel(Problem p, BwdArgs g, c
   const int i = threadIdx.x;
   const int dk = p.dk, dv = p.dv;
   const float* parts = ws + L.parts;
-  const int64_t pstride = L.nslice * L.bth * dk;
+  const int64_t pstride = L.ngroups * L.bth * dk;
   float sq = 0.f, sdu = 0.f, skw = 0.f, sda = 0.f;
   float de = 0.f, dla = 0.f, dwv = 0.f;
   if (i < dk) {
-    for (int64_t s = 0; s < L.nslice; ++s) {
+    for (int64_t s = 0; s < L.ngroups; ++s) {
       const float* pb = parts + (s * L.bth + tok) * dk + i;
       sq += pb[0];
       sdu += pb[pstride];
@@ -439,12 +459,14 @@ hipError_t launch_bwd_varlen(Problem p, const int* cu, const BwdArgs& g, void* w
 
 hipError_t launch_bwd(const Problem& p, const BwdArgs& g, void* workspace, hipStream_t stream) {
   float* ws = static_cast<float*>(workspace);
-  dim3 grid(unsigned(p.B * p.H), unsigned(p.dv / cols_for(p.dk)));
+  const BwdLayout L(p, p.seqs != nullptr);
+  dim3 grid(unsigned(p.B * p.H), unsigned(L.ngroups));
+  const dim3 block(unsigned(64 * L.wpg));
   switch (p.dk) {
-    case 16: hipLaunchKernelGGL(bwd_token_kernel<16>, grid, dim3(64), 0, stream, p, g, ws); break;
-    case 32: hipLaunchKernelGGL(bwd_token_kernel<32>, grid, dim3(64), 0, stream, p, g, ws); break;
-    case 64: hipLaunchKernelGGL(bwd_token_kernel<64>, grid, dim3(64), 0, stream, p, g, ws); break;
-    case 128: hipLaunchKernelGGL(bwd_token_kernel<128>, grid, dim3(64), 0, stream, p, g, ws); break;
+    case 16: hipLaunchKernelGGL(bwd_token_kernel<16>, grid, block, 0, stream, p, g, ws); break;
+    case 32: hipLaunchKernelGGL(bwd_token_kernel<32>, grid, block, 0, stream, p, g, ws); break;
+    case 64: hipLaunchKernelGGL(bwd_token_kernel<64>, grid, block, 0, stream, p, g, ws); break;
+    case 128: hipLaunchKernelGGL(bwd_token_kernel<128>, grid, block, 0, stream, p, g, ws); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
