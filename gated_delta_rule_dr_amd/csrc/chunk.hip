@@ -28,8 +28,14 @@
 // (b, h, value slice) in order, carrying the fp32 state in registers; per chunk it copies the
 // packet into LDS and runs only the state-dependent products, so no exponential, prefix sum
 // or format conversion is repeated by the value slices of a head.  With a scalar decay the
-// packet holds no operand tiles: the scan stages the plain k and q and applies the per-token
-// factors e^{+-(g_t - gm)} to product rows instead.
+// packet holds no decayed tiles: it carries the plain k and q, and the scan applies the
+// per-token factors e^{+-(g_t - gm)} to product rows instead.
+//
+// FG2-GDN's per-channel rate beta runs the symmetric kernels on the scaled pair
+// (sqrt(beta) k, sqrt(beta) v) with a unit gate: the prep scales k as it loads it and writes the
+// scaled values into the packet, from where the scan copies its value slice.  Packed sequences
+// of different lengths run the same kernels over tables of their chunks (prep) and sequences
+// (scan), written into the workspace by a set-up kernel.
 //
 // Products use v_mfma_f32_16x16x32_f16 (fp16 operands, fp32 accumulation).  Gram tiles are
 // computed transposed (A^T = K- Q+^T) so that each lane owns four consecutive columns of one
