@@ -35,9 +35,9 @@ namespace {
 
 constexpr int CK = 64;  // tokens per checkpoint
 
-// Value columns per wave: 8 (row groups of 8 lanes, dk / 8 rows per lane) where dk >= 32, else
-// 16 (dk / 4 rows per lane; a lane holds at least four rows either way).
-__host__ __device__ constexpr int cols_for(int dk) { return dk >= 32 ? 8 : 16; }
+// Value columns per wave: the fewest that leave a lane at least four rows (dk * cols / 64 >= 4),
+// and at least 4 -- more, narrower waves run side by side on a SIMD.
+__host__ __device__ constexpr int cols_for(int dk) { return dk >= 64 ? 4 : dk == 32 ? 8 : 16; }
 
 // x of the lane that the DPP control CTRL selects within this lane's row of 16 lanes.
 template <int CTRL>
@@ -45,14 +45,16 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 
-// Sum over the lanes of one column (lanes c + COLS i), in every one of them: with 8 columns a
-// row rotation by 8 first adds the other half-row; then the gfx950 row swaps: swapping rows
+// Sum over the lanes of one column (lanes c + COLS i), in every one of them: within a row of 16
+// lanes, rotations by 4 (4 columns) and by 8 add the lanes of the same column; then the gfx950
+// row swaps: swapping rows
 // 1 <-> 0 and 3 <-> 2 of a value with itself and adding both results gives each lane the sum of
 // its pair of rows, and the half-wave swap adds the other pair.  Paired lanes add in the same
 // order, so every lane of the column holds the same sum.
 template <int COLS>
 __device__ __forceinline__ float group_sum(float x) {
-  if constexpr (COLS == 8) x += dpp<0x128>(x);  // row rotate by 8: the other half-row
+  if constexpr (COLS == 4) x += dpp<0x124>(x);  // row rotate by 4: lanes 4 apart
+  if constexpr (COLS <= 8) x += dpp<0x128>(x);  // row rotate by 8: the other half-row
   const unsigned u = __float_as_uint(x);
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -89,10 +91,13 @@ __device__ __forceinline__ void row_scatter_sum(float* v, int c) {
     rs_stage<0x141, 2, (N > 1 ? N / 2 : 1)>(v, c);
     rs_stage<0x4E, 1, (N > 2 ? N / 4 : 1)>(v, c);
     rs_stage<0xB1, 0, (N > 4 ? N / 8 : 1)>(v, c);
-  } else {
+  } else if constexpr (COLS == 8) {
     rs_stage<0x141, 2, N>(v, c);
     rs_stage<0x4E, 1, (N > 1 ? N / 2 : 1)>(v, c);
     rs_stage<0xB1, 0, (N > 2 ? N / 4 : 1)>(v, c);
+  } else {
+    rs_stage<0x4E, 1, N>(v, c);
+    rs_stage<0xB1, 0, (N > 1 ? N / 2 : 1)>(v, c);
   }
 }
 template <int COLS, int N>
@@ -100,9 +105,11 @@ __device__ __forceinline__ int rs_row(int c) {
   if constexpr (COLS == 16)
     return (N > 1 ? (N / 2) * ((c >> 3) & 1) : 0) + (N > 2 ? (N / 4) * ((c >> 2) & 1) : 0) +
            (N > 4 ? (N / 8) * ((c >> 1) & 1) : 0) + (N > 8 ? (N / 16) * (c & 1) : 0);
-  else
+  else if constexpr (COLS == 8)
     return (N > 1 ? (N / 2) * ((c >> 2) & 1) : 0) + (N > 2 ? (N / 4) * ((c >> 1) & 1) : 0) +
            (N > 4 ? (N / 8) * (c & 1) : 0);
+  else
+    return (N > 1 ? (N / 2) * ((c >> 1) & 1) : 0) + (N > 2 ? (N / 4) * (c & 1) : 0);
 }
 template <int COLS, int N>
 constexpr int rs_count = N >= COLS ? N / COLS : 1;
@@ -110,8 +117,10 @@ template <int COLS, int N>
 __device__ __forceinline__ bool rs_owner(int c) {
   if constexpr (COLS == 16)
     return (N > 8 || (c & 1) == 0) && (N > 4 || (c & 2) == 0) && (N > 2 || (c & 4) == 0) && (N > 1 || (c & 8) == 0);
-  else
+  else if constexpr (COLS == 8)
     return (N > 4 || (c & 1) == 0) && (N > 2 || (c & 2) == 0) && (N > 1 || (c & 4) == 0);
+  else
+    return (N > 2 || (c & 1) == 0) && (N > 1 || (c & 2) == 0);
 }
 
 // Workspace layout of the backward (offsets in floats).  Packed sequences (p.B of them over p.T
@@ -124,14 +133,16 @@ struct BwdLayout {
   int64_t ngroups;  // workgroups per (b, h): one stored row part each
   int64_t ckpt, states, parts, tmp_dw, total;
   __host__ __device__ BwdLayout(const Problem& p, bool packed) {
-    nslice = p.dv / cols_for(p.dk);
-    wpg = nslice >= 4 ? 4 : int(nslice);
+    const int cols = cols_for(p.dk);
+    nslice = p.dv / cols;
+    // waves per workgroup: 32 value columns (at most 8 waves), so a workgroup stores one row part
+    // per 32 columns whatever the wave width
+    wpg = int(32 / cols) < nslice ? int(32 / cols) : int(nslice);
     ngroups = nslice / wpg;
     nck = (int64_t(p.T) + CK - 1) / CK;
     bth = packed ? int64_t(p.T) * p.H : int64_t(p.B) * p.T * p.H;
     const int64_t waves = int64_t(p.B) * p.H * nslice;
     const int64_t nckpt = packed ? nslice * p.H * varlen_max_chunks(p.B, p.T) : waves * nck;
-    const int cols = cols_for(p.dk);
     ckpt = 0;                                             // [nckpt][dk][cols]
     states = ckpt + nckpt * p.dk * cols;                  // [waves][CK][dk][cols]
     parts = states + waves * CK * p.dk * cols;            // [4][ngroups][bth][dk]
@@ -141,7 +152,7 @@ struct BwdLayout {
 };
 
 template <int DK>
-__global__ __launch_bounds__(256) void bwd_token_kernel(Problem p, BwdArgs g, float* __restrict__ ws) {
+__global__ __launch_bounds__(512) void bwd_token_kernel(Problem p, BwdArgs g, float* __restrict__ ws) {
   constexpr int kCols = cols_for(DK);
   constexpr int RPL = DK * kCols / 64;  // rows per lane
   const int lane = threadIdx.x & 63;
@@ -263,7 +274,7 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(Problem p, BwdArgs g, fl
   float* parts = ws + L.parts;
   const int64_t pstride = L.ngroups * L.bth * DK;  // between the four row-part arrays
   // the workgroup's column groups' row parts of one token, alternating between two buffers
-  __shared__ float red[2][4][4][DK];
+  __shared__ float red[2][8][4][DK];
   for (int64_t ci = nck - 1; ci >= 0; --ci) {
     const int t0 = int(ci * CK), t1 = t0 + CK < T ? t0 + CK : T;
     restore(ck + ci * DK * kCols, s);
