@@ -11,16 +11,16 @@
 //     G' = G + k dm^T;  d(log a) = a * rowsum(G' * S_{t-1});  G = Diag(a) G'
 // and dS0 is G after token 0.
 //
-// Kernel 1, one wave per (b, h, group of 8 value columns; 16 where dk = 16): lane = column x
-// row group (8 x 8, or 16 x 4), dk / 8 (dk / 4) rows of one column per lane:
+// Kernel 1, one wave per (b, h, group of 4 value columns; 8 where dk = 32, 16 where dk = 16):
+// lane = column x row group, dk * columns / 64 rows of one column per lane:
 //   pass 1 runs the forward and stores the state at the start of every 64-token chunk;
 //   pass 2 takes the chunks backwards: it recomputes the chunk's states from its checkpoint
 //   into a scratch area of its own, then walks the chunk's tokens backwards through the adjoint
 //   above.  Column sums (m, dm, dv~) are lane sums plus cross-lane steps; row sums (the per-row
 //   parts of dq, du, dk and d(log a), summed over this wave's columns) are reduced over the
 //   column lanes and stored per column group.
-// Up to four column groups of one (b, h) share a workgroup and sum their row parts in LDS before
-// storing them, so one row part per workgroup reaches memory.
+// The column groups of 32 value columns of one (b, h) share a workgroup and sum their row parts
+// in LDS before storing them, so one row part per workgroup reaches memory.
 // Kernel 2 sums the workgroups' row parts, applies the per-row factors (e, k, a) and forms
 // the gate gradients (summed over channels for a per-head gate; the erase and write parts added
 // for a shared gate).
