@@ -11,8 +11,8 @@
 //     G' = G + k dm^T;  d(log a) = a * rowsum(G' * S_{t-1});  G = Diag(a) G'
 // and dS0 is G after token 0.
 //
-// Kernel 1, one wave per (b, h, group of 4 value columns; 8 where dk = 32, 16 where dk = 16):
-// lane = column x row group, dk * columns / 64 rows of one column per lane:
+// Kernel 1, one wave per (b, h, group of 256 / dk value columns): lane = column x row group,
+// four rows of one column per lane:
 //   pass 1 runs the forward and stores the state at the start of every 64-token chunk;
 //   pass 2 takes the chunks backwards: it recomputes the chunk's states from its checkpoint
 //   into a scratch area of its own, then walks the chunk's tokens backwards through the adjoint
@@ -35,9 +35,9 @@ namespace {
 
 constexpr int CK = 64;  // tokens per checkpoint
 
-// Value columns per wave: the fewest that leave a lane at least four rows (dk * cols / 64 >= 4),
-// and at least 4 -- more, narrower waves run side by side on a SIMD.
-__host__ __device__ constexpr int cols_for(int dk) { return dk >= 64 ? 4 : dk == 32 ? 8 : 16; }
+// Value columns per wave: the fewest that leave a lane four rows (dk * cols / 64 == 4): more,
+// narrower waves run side by side on a SIMD.
+__host__ __device__ constexpr int cols_for(int dk) { return 256 / dk; }
 
 // x of the lane that the DPP control CTRL selects within this lane's row of 16 lanes.
 template <int CTRL>
@@ -53,7 +53,8 @@ __device__ __forceinline__ float dpp(float x) {
 // order, so every lane of the column holds the same sum.
 template <int COLS>
 __device__ __forceinline__ float group_sum(float x) {
-  if constexpr (COLS == 4) x += dpp<0x124>(x);  // row rotate by 4: lanes 4 apart
+  if constexpr (COLS == 2) x += dpp<0x122>(x);  // row rotate by 2: lanes 2 apart
+  if constexpr (COLS <= 4) x += dpp<0x124>(x);  // row rotate by 4: lanes 4 apart
   if constexpr (COLS <= 8) x += dpp<0x128>(x);  // row rotate by 8: the other half-row
   const unsigned u = __float_as_uint(x);
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
@@ -95,9 +96,11 @@ __device__ __forceinline__ void row_scatter_sum(float* v, int c) {
     rs_stage<0x141, 2, N>(v, c);
     rs_stage<0x4E, 1, (N > 1 ? N / 2 : 1)>(v, c);
     rs_stage<0xB1, 0, (N > 2 ? N / 4 : 1)>(v, c);
-  } else {
+  } else if constexpr (COLS == 4) {
     rs_stage<0x4E, 1, N>(v, c);
     rs_stage<0xB1, 0, (N > 1 ? N / 2 : 1)>(v, c);
+  } else {
+    rs_stage<0xB1, 0, N>(v, c);
   }
 }
 template <int COLS, int N>
@@ -108,8 +111,10 @@ __device__ __forceinline__ int rs_row(int c) {
   else if constexpr (COLS == 8)
     return (N > 1 ? (N / 2) * ((c >> 2) & 1) : 0) + (N > 2 ? (N / 4) * ((c >> 1) & 1) : 0) +
            (N > 4 ? (N / 8) * (c & 1) : 0);
-  else
+  else if constexpr (COLS == 4)
     return (N > 1 ? (N / 2) * ((c >> 1) & 1) : 0) + (N > 2 ? (N / 4) * (c & 1) : 0);
+  else
+    return N > 1 ? (N / 2) * (c & 1) : 0;
 }
 template <int COLS, int N>
 constexpr int rs_count = N >= COLS ? N / COLS : 1;
@@ -119,8 +124,10 @@ __device__ __forceinline__ bool rs_owner(int c) {
     return (N > 8 || (c & 1) == 0) && (N > 4 || (c & 2) == 0) && (N > 2 || (c & 4) == 0) && (N > 1 || (c & 8) == 0);
   else if constexpr (COLS == 8)
     return (N > 4 || (c & 1) == 0) && (N > 2 || (c & 2) == 0) && (N > 1 || (c & 4) == 0);
-  else
+  else if constexpr (COLS == 4)
     return (N > 2 || (c & 1) == 0) && (N > 1 || (c & 2) == 0);
+  else
+    return N > 1 || (c & 1) == 0;
 }
 
 // Workspace layout of the backward (offsets in floats).  Packed sequences (p.B of them over p.T
@@ -135,8 +142,8 @@ struct BwdLayout {
   __host__ __device__ BwdLayout(const Problem& p, bool packed) {
     const int cols = cols_for(p.dk);
     nslice = p.dv / cols;
-    // waves per workgroup: 32 value columns (at most 8 waves), so a workgroup stores one row part
-    // per 32 columns whatever the wave width
+    // waves per workgroup: 32 value columns (at most 16 waves), so a workgroup stores one row
+    // part per 32 columns whatever the wave width
     wpg = int(32 / cols) < nslice ? int(32 / cols) : int(nslice);
     ngroups = nslice / wpg;
     nck = (int64_t(p.T) + CK - 1) / CK;
@@ -152,7 +159,7 @@ struct BwdLayout {
 };
 
 template <int DK>
-__global__ __launch_bounds__(512) void bwd_token_kernel(Problem p, BwdArgs g, float* __restrict__ ws) {
+__global__ __launch_bounds__(1024) void bwd_token_kernel(Problem p, BwdArgs g, float* __restrict__ ws) {
   constexpr int kCols = cols_for(DK);
   constexpr int RPL = DK * kCols / 64;  // rows per lane
   const int lane = threadIdx.x & 63;
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(512) void bwd_token_kernel(Problem p, BwdArgs g, fl
   float* parts = ws + L.parts;
   const int64_t pstride = L.ngroups * L.bth * DK;  // between the four row-part arrays
   // the workgroup's column groups' row parts of one token, alternating between two buffers
-  __shared__ float red[2][8][4][DK];
+  __shared__ float red[2][16][4][DK];
   for (int64_t ci = nck - 1; ci >= 0; --ci) {
     const int t0 = int(ci * CK), t1 = t0 + CK < T ? t0 + CK : T;
     restore(ck + ci * DK * kCols, s);

@@ -265,10 +265,10 @@ def _bwd(desc, **over):
 def test_bwd_workspace_and_errors():
     L = _abi.lib()
     d = _good_desc(B=2, T=100, H=4, dk=128, dv=128)
-    # one wave per (b, h, 4 value columns) at dk >= 64: 32 column groups
-    waves, nck, bth = 2 * 4 * 32, 2, 2 * 100 * 4
-    # row parts: one per workgroup of eight column groups (32 columns)
-    need = 4 * (waves * nck * 128 * 4 + waves * 64 * 128 * 4 + 4 * 4 * bth * 128 + bth * 128)
+    # one wave per (b, h, 256 / dk = 2 value columns): 64 column groups
+    waves, nck, bth = 2 * 4 * 64, 2, 2 * 100 * 4
+    # row parts: one per workgroup of 32 columns
+    need = 4 * (waves * nck * 128 * 2 + waves * 64 * 128 * 2 + 4 * 4 * bth * 128 + bth * 128)
     assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(d)) == need
     assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(_good_desc(T=0))) == 0
     assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(_good_desc(erase_kind=_abi.DR_GATE_RATE_SQRT))) > 0
@@ -288,9 +288,9 @@ def test_bwd_varlen_workspace_and_errors():
     d = _good_desc(B=1, T=1000, H=4, dk=128, dv=128)
     nseq = 5
     maxc = (1000 + 63 * nseq) // 64
-    nslice, waves, bth = 32, nseq * 4 * 32, 1000 * 4
+    nslice, waves, bth = 64, nseq * 4 * 64, 1000 * 4
     tables = (16 * nseq + 255) // 256 * 256 + 256
-    layout = 4 * (nslice * 4 * maxc * 128 * 4 + waves * 64 * 128 * 4 + 4 * (nslice // 8) * bth * 128 + bth * 128)
+    layout = 4 * (nslice * 4 * maxc * 128 * 2 + waves * 64 * 128 * 2 + 4 * (nslice // 16) * bth * 128 + bth * 128)
     assert L.dr_chunk_bwd_varlen_workspace_bytes(ctypes.byref(d), nseq) == tables + layout
     assert L.dr_chunk_bwd_varlen_workspace_bytes(ctypes.byref(_good_desc(B=2)), nseq) == 0
     assert L.dr_chunk_bwd_varlen_workspace_bytes(ctypes.byref(d), 0) == 0
