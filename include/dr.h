@@ -181,8 +181,8 @@ int dr_chunk_fwd_varlen(const dr_desc* desc, const int32_t* cu_seqlens, int32_t 
  *          (both uses) goes to derase and dwrite is ignored.
  *   dS0    [B, H, dk, dv] fp32, or NULL to skip.
  *   workspace: at least dr_chunk_bwd_workspace_bytes(desc) bytes: a state checkpoint every 64
- *          tokens and one chunk of states per (b, h, group of 4 value columns; 8 where
- *          dk = 32, 16 where dk = 16), and four fp32 partial sums per row for every 32 value
+ *          tokens and one chunk of states per (b, h, group of 256 / dk value columns), and
+ *          four fp32 partial sums per row for every 32 value
  *          columns (at dk = dv = 128, 8 KB per token and head: 2.1 GB for B 4, H 16, T 4096).
  * Outputs must not overlap one another, any input or the workspace.  T == 0 writes dS0 = dS_T
  * (zeros without it).  With DR_GATE_RATE_SQRT, derase is the gradient of the rate beta (through
