@@ -82,3 +82,239 @@ def chunk_forward(q, k, v, log_decay, erase, write=None, S0=None, chunk=64, symm
             o[sl] = Qp @ S + A_qk @ Vt - A_qu @ M
             S = np.exp(gC)[:, None] * S + Kend.T @ Vt - Uend.T @ M
     return o, S
+
+
+# ------------------------------------------------------------------------------------------
+# Kernel-faithful emulation of the matrix-core chunk path.
+#
+# The chunk form above is exact in any arithmetic with unbounded range; the HIP kernels run its
+# products on fp16 matrix operands (fp32 accumulation, fp32 state), so every decay factor that
+# multiplies an operand must stay inside fp16's range, and the way each factor e^{g_t - g_i} is
+# split between the two operands of a product (its reference point) decides whether the
+# method stays exact for every valid decay a in (0, 1).  `kernel_emulation` reproduces the
+# roundings and the referencing of one scheme in fp64:
+#
+#   scheme="safe"      every factor that is not immediately followed by its exact inverse is
+#                      e^{x} with x <= 0: the state is referenced at the chunk start (rows
+#                      q_t e^{g_t}, k_t e^{g_t}; state update k_i e^{g_C - g_i}), the
+#                      off-diagonal 16 x 16 blocks of the Gram matrices at their block
+#                      boundary, and the diagonal blocks either at the block's log-midpoint
+#                      (when its decay is at most 12 nats on every channel, so both factors lie
+#                      within e^{+-6}) or, beyond that, by levels: pairs split at the boundary of
+#                      the halves of 16-, 8-, 4- and 2-token segments, plus the diagonal.
+#   scheme="midpoint"  the referencing of the first kernel version: every operand taken
+#                      relative to the chunk's midpoint, with exponents clamped at 11 and the
+#                      state scaled by e^{g_mid} into fp16 -- exact only while half a chunk's
+#                      log-decay stays above -11.
+#
+# fp16 rounding is applied wherever the kernel stores or feeds an fp16 matrix operand; sums
+# are kept in fp64 (the kernel accumulates in fp32, which is far finer than fp16 operands).
+# ------------------------------------------------------------------------------------------
+_BLK = 16
+_FAST_SPAN = 12.0  # largest per-channel log-decay over a 16-token block for the midpoint split
+_FP16_SAFE = 32768.0
+
+
+def _h(x):
+    """Round to fp16 (round to nearest even; overflow gives inf, as the conversion does)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, np.float64).astype(np.float16).astype(np.float64)
+
+
+def _diag_block(rows, cols, gl, D):
+    """Diagonal 16 x 16 block of the Gram matrices, A[x][y][t, i] = sum_d rows[x][t, d] cols[y][i, d]
+    e^{gl[t, d] - gl[i, d]} for i <= t (lower triangle, diagonal included; the caller masks).
+
+    rows: dict name -> [16, d] row operands (k, q); cols: dict name -> [16, d] column operands
+    (k, u); gl: [16, d] in-block inclusive prefix of the log-decay; D: [d] block total."""
+    n = gl.shape[0]
+    lower = np.tril(np.ones((n, n)))
+    out = {}
+    half = D / 2
+    ops_r = {x: _h(r * np.exp(gl - half)) for x, r in rows.items()}
+    ops_c = {y: _h(c * np.exp(half - gl)) for y, c in cols.items()}
+    fast = bool(np.all(D >= -_FAST_SPAN))
+    for dct in (ops_r, ops_c):
+        for a in dct.values():
+            fast = fast and bool(np.all(np.isfinite(a)) and np.all(np.abs(a) <= _FP16_SAFE))
+    if fast:
+        for x in rows:
+            for y in cols:
+                out[x, y] = (ops_r[x] @ ops_c[y].T) * lower
+        return out, True
+    # levels: segments of s tokens, rows in the second half, columns in the first, both
+    # referenced at the last token of the first half (every factor e^{x}, x <= 0)
+    p = np.arange(n)
+    for x in rows:
+        for y in cols:
+            out[x, y] = np.zeros((n, n))
+    s = n
+    while s >= 2:
+        hs = s // 2
+        seg, pos = p // s, p % s
+        ref = seg * s + hs - 1
+        is_row = pos >= hs
+        f = np.where(is_row[:, None], np.exp(gl - gl[ref]), np.exp(gl[ref] - gl))
+        same = (seg[:, None] == seg[None, :]) & is_row[:, None] & ~is_row[None, :]
+        for x, r in rows.items():
+            ro = _h(np.where(is_row[:, None], r * f, 0.0))
+            for y, c in cols.items():
+                co = _h(np.where(is_row[:, None], 0.0, c * f))
+                out[x, y] += np.where(same, ro @ co.T, 0.0)
+        s = hs
+    eye = np.eye(n, dtype=bool)
+    for x, r in rows.items():
+        for y, c in cols.items():
+            out[x, y] += np.where(eye, _h(r) @ _h(c).T, 0.0)
+    return out, False
+
+
+def _gram_safe(rows, cols, gl, D):
+    """Lower-triangular C x C Gram matrices with block-boundary referencing (see above).
+    rows/cols: dict name -> [C, d]; gl: [C, d] in-block prefixes; D: [nblk, d] block totals.
+    Returns (dict (x, y) -> [C, C] with the diagonal included, list of fast flags per block)."""
+    C = gl.shape[0]
+    nb = (C + _BLK - 1) // _BLK
+    A = {(x, y): np.zeros((C, C)) for x in rows for y in cols}
+    fast = []
+    # column operands referenced at the end of their own block: k_i e^{D_J - gl_i} <= 1
+    cend = {y: _h(c * np.exp(D[np.arange(C) // _BLK] - gl)) for y, c in cols.items()}
+    for I in range(nb):
+        ti = slice(_BLK * I, min(_BLK * (I + 1), C))
+        rop = {x: _h(r[ti] * np.exp(gl[ti])) for x, r in rows.items()}  # e^{g_t - g_{b_I}}
+        for J in range(I):
+            tj = slice(_BLK * J, _BLK * (J + 1))
+            # the decay of the blocks strictly between J and I, applied in fp16 to the
+            # stored column fragment
+            F = _h(np.exp(D[J + 1:I].sum(axis=0))) if I > J + 1 else None
+            for y in cols:
+                co = cend[y][tj] if F is None else _h(cend[y][tj] * F)
+                for x in rows:
+                    A[x, y][ti, tj] = rop[x] @ co.T
+        blk, ok = _diag_block({x: r[ti] for x, r in rows.items()}, {y: c[ti] for y, c in cols.items()},
+                              gl[ti], D[I])
+        fast.append(ok)
+        for key, val in blk.items():
+            A[key][ti, ti] = val
+    return A, fast
+
+
+def _tri(x, strict):
+    return np.tril(x, -1 if strict else 0)
+
+
+def kernel_emulation(q, k, v, log_decay, erase, write=None, S0=None, scheme="safe", fg2=False,
+                     return_flags=False):
+    """Emulate the matrix-core chunk path for one (b, h); arguments as ``chunk_forward`` plus
+    ``fg2`` (erase is then FG2-GDN's per-channel rate beta, taken as sqrt(beta) into k and v with
+    unit gates).  Returns (o [T, dv], S_T) in fp64, or with ``return_flags`` also the list of
+    per-block fast-path flags of the safe scheme."""
+    C = 64
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    T, dk = k.shape
+    dv = v.shape[1]
+    la = np.asarray(log_decay, np.float64)
+    dch = la.ndim == 2
+    la = np.broadcast_to(la[:, None] if la.ndim == 1 else la, (T, dk))
+    e_in = np.asarray(erase, np.float64)
+    if fg2:
+        sq = np.sqrt(e_in)
+        k = k * sq
+        v = _h(v * sq)  # the prep writes v~ into the packet in fp16
+        e = np.ones((T, dk))
+        w = np.ones((T, dv))
+        symmetric, beta = True, np.ones(T)
+    else:
+        symmetric = e_in.ndim == 1 and write is None
+        e = np.broadcast_to(e_in[:, None] if e_in.ndim == 1 else e_in, (T, dk))
+        w_in = e_in if write is None else np.asarray(write, np.float64)
+        w = np.broadcast_to(w_in[:, None] if w_in.ndim == 1 else w_in, (T, dv))
+        beta = e_in if symmetric else None
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, np.float64)
+    o = np.zeros((T, dv))
+    flags = []
+    scalar_path = symmetric and not dch  # plain k, q tiles with per-row / per-element factors
+    for c0 in range(0, T, C):
+        n = min(C, T - c0)
+        sl = slice(c0, c0 + n)
+        pad = lambda x: np.concatenate([x, np.zeros((C - n,) + x.shape[1:])]) if n < C else x
+        kc, qc, vc = pad(k[sl]), pad(q[sl]), pad(v[sl])
+        lac, ec, wc = pad(la[sl]), pad(e[sl]), pad(w[sl])
+        g = np.cumsum(lac, axis=0)
+        gC = g[-1]
+        gm = g[31]
+        if symmetric:
+            bc = pad(np.asarray(beta, np.float64)[sl])
+        if scheme == "safe":
+            blocks = np.arange(C) // _BLK
+            D = np.stack([lac[_BLK * b:_BLK * (b + 1)].sum(axis=0) for b in range(C // _BLK)])
+            gb = np.concatenate([np.zeros((1, dk)), np.cumsum(D, axis=0)[:-1]])
+            gl = g - gb[blocks]
+        if scalar_path:
+            # plain fp16 k, q; Gram products take e^{g_t - g_i} <= 1 per element in fp32
+            kh, qh = _h(kc), _h(qc)
+            gs = g[:, 0]
+            dec = np.exp(np.minimum(gs[:, None] - gs[None, :], 0.0))
+            A_kk = _tri((kh @ kh.T) * dec, True)
+            A_qk = _tri((qh @ kh.T) * dec, False)
+            if scheme == "safe":
+                St, fp, fm, fcm = _h(S), np.exp(gs), np.exp(gC[0] - gs), 1.0
+            else:
+                St = _h(np.exp(gm[0]) * S)
+                fp = np.exp(np.minimum(gs - gm[0], 11.0))
+                fm = np.exp(np.minimum(gm[0] - gs, 11.0))
+                fcm = np.exp(min(gC[0] - gm[0], 11.0))
+            Tm = _h(np.linalg.inv(np.eye(C) + bc[:, None] * A_kk))
+            Aq = _h(A_qk)
+            XK = (kh @ St) * fp[:, None]
+            XQ = (qh @ St) * fp[:, None]
+            R = _h(bc[:, None] * (vc - XK))
+            delta = Tm @ R
+            dh = _h(delta)
+            O = XQ + Aq @ dh
+            S = np.exp(gC[0]) * S + fcm * (kh.T @ _h(delta * fm[:, None]))
+            o[sl] = O[:n]
+            continue
+        u = ec * kc
+        rows = {"k": kc, "q": qc}
+        cols = {"k": kc} if symmetric else {"k": kc, "u": u}
+        if scheme == "safe":
+            A, fl = _gram_safe(rows, cols, gl, D)
+            flags.extend(fl)
+            Kp, Qp = _h(kc * np.exp(g)), _h(qc * np.exp(g))
+            Kend = _h(kc * np.exp(gC - g))
+            Uend = _h(u * np.exp(gC - g))
+            St = _h(S)
+            fcm = 1.0
+        else:
+            fpm = np.exp(np.minimum(g - gm, 11.0))
+            fmm = np.exp(np.minimum(gm - g, 11.0))
+            Kp, Qp = _h(kc * fpm), _h(qc * fpm)
+            Km, Um = _h(kc * fmm), _h(u * fmm)
+            A = {("k", "k"): Kp @ Km.T, ("q", "k"): Qp @ Km.T, ("k", "u"): Kp @ Um.T, ("q", "u"): Qp @ Um.T}
+            St = _h(np.exp(gm)[:, None] * S)
+            Kend, Uend = Km, Um
+            fcm = np.exp(np.minimum(gC - gm, 11.0))[:, None]
+        XK = Kp @ St
+        XQ = Qp @ St
+        if symmetric:
+            Tm = _h(np.linalg.inv(np.eye(C) + bc[:, None] * _tri(A["k", "k"], True)))
+            Aq = _h(_tri(A["q", "k"], False))
+            R = _h(bc[:, None] * (vc - XK))
+            dh = _h(Tm @ R)
+            O = XQ + Aq @ dh
+            S = np.exp(gC)[:, None] * S + fcm * (Kend.T @ dh)
+        else:
+            Tm = _h(np.linalg.inv(np.eye(C) + _tri(A["k", "u"], True)))
+            Akk = _h(_tri(A["k", "k"], True))
+            Aqk = _h(_tri(A["q", "k"], False))
+            Aqu = _h(_tri(A["q", "u"], False))
+            Vt = _h(wc * vc)
+            Y = _h(XK + Akk @ Vt)
+            Mh = _h(Tm @ Y)
+            O = XQ + Aqk @ Vt - Aqu @ Mh
+            S = np.exp(gC)[:, None] * S + fcm * (Kend.T @ Vt - Uend.T @ Mh)
+        o[sl] = O[:n]
+    if return_flags:
+        return o, S, flags
+    return o, S
