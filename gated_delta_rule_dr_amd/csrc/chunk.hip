@@ -8,28 +8,36 @@
 // in-chunk states are rebuilt from the chunk's boundary state ("Linearized 2-Simplicial
 // Attention", method: architecture and implementation).
 //
-// Per chunk, with incoming state S, chunk-local cumulative log-decay g_t (per channel) and a
-// per-channel reference gm (g at the chunk midpoint):
-//   K+ = k e^{g - gm}, Q+ = q e^{g - gm}, K- = k e^{gm - g}, U- = (e * k) e^{gm - g}
-//   A_kk = strict_lower(K+ K-^T)  A_ku = strict_lower(K+ U-^T)  A_qk = lower(Q+ K-^T)
-//   A_qu = lower(Q+ U-^T)          X_K = K+ S~,  X_Q = Q+ S~,  S~ = Diag(e^{gm}) S
+// Per chunk, with incoming state S and chunk-local cumulative log-decay g_t (per channel, or
+// one per head):
+//   K+ = k e^{g}, Q+ = q e^{g}, K^end = k e^{g_C - g}, U^end = (e * k) e^{g_C - g}
+//   A_kk = strict_lower(k_t . k_i e^{g_t - g_i})  A_ku = strict_lower(k_t . u_i e^{g_t - g_i})
+//   A_qk = lower(q_t . k_i e^{g_t - g_i})          A_qu = lower(q_t . u_i e^{g_t - g_i})
+//   X_K = K+ S,  X_Q = Q+ S
 // symmetric gates (one beta for erase and write):
 //   T = (I + Diag(beta) A_kk)^{-1},  delta = T Diag(beta) (V - X_K)
-//   O = X_Q + A_qk delta,            S <- Diag(e^{g_C}) S + Diag(e^{g_C - gm}) K-^T delta
+//   O = X_Q + A_qk delta,            S <- Diag(e^{g_C}) S + K^end^T delta
 // general gates (erase e, write w; Vt = w * v):
 //   T = (I + A_ku)^{-1},  M = T (X_K + A_kk Vt)
-//   O = X_Q + A_qk Vt - A_qu M,  S <- Diag(e^{g_C}) S + Diag(e^{g_C - gm}) (K-^T Vt - U-^T M)
+//   O = X_Q + A_qk Vt - A_qu M,  S <- Diag(e^{g_C}) S + K^end^T Vt - U^end^T M
 //
-// Two kernels.  chunk_prep_kernel runs one workgroup per chunk (all chunks of all heads in
-// parallel) and writes everything that does not depend on the state into a per-chunk packet
-// in the caller's workspace: T (the only factor that needs a serial algorithm), the Gram
-// matrices, the gate factors and, unless the decay is one scalar per token, the decayed fp16
-// operand tiles K+, Q+, K-^T (and U-^T).  chunk_scan_kernel then walks the chunks of one
-// (b, h, value slice) in order, carrying the fp32 state in registers; per chunk it copies the
-// packet into LDS and runs only the state-dependent products, so no exponential, prefix sum
-// or format conversion is repeated by the value slices of a head.  With a scalar decay the
-// packet holds no decayed tiles: it carries the plain k and q, and the scan applies the
-// per-token factors e^{+-(g_t - gm)} to product rows instead.
+// Range.  The method allows any decay a in (0, 1) ("Gated DeltaNet-2", gate table; "FG2-GDN",
+// section 2, update rule), so no factor that scales an fp16 operand may grow with the decay:
+// every one is e^{x} with x <= 0 -- the scan's tiles are referenced at the chunk start, the
+// Gram matrices' off-diagonal 16-token blocks at their block boundaries -- except for the
+// diagonal blocks' midpoint split, which is taken only where it stays within e^{+-6}.  A
+// factor then underflows only where the term it scales is negligible.
+//
+// Two kernels.  The prep (one workgroup per chunk, all chunks of all heads in parallel) writes
+// everything that does not depend on the state into a per-chunk packet in the caller's
+// workspace: T (the only factor that needs a serial algorithm), the Gram matrices, the gate
+// factors and, unless the decay is one scalar per token, the decayed fp16 operand tiles K+, Q+,
+// K^end (and U^end).  The scan then walks the chunks of one (b, h, value slice) in order,
+// carrying the fp32 state in registers; per chunk it copies the packet into LDS and runs only
+// the state-dependent products, so no exponential, prefix sum or format conversion is repeated
+// by the value slices of a head.  With a scalar decay the packet holds no decayed tiles: it
+// carries the plain k and q, and the scan applies the per-token factors e^{g_t} and
+// e^{g_C - g_t} to product rows instead.
 //
 // FG2-GDN's per-channel rate beta runs the symmetric kernels on the scaled pair
 // (sqrt(beta) k, sqrt(beta) v) with a unit gate: the prep scales k as it loads it and writes the
@@ -38,12 +46,8 @@
 // (scan), written into the workspace by a set-up kernel.
 //
 // Products use v_mfma_f32_16x16x32_f16 (fp16 operands, fp32 accumulation).  Gram tiles are
-// computed transposed (A^T = K- Q+^T) so that each lane owns four consecutive columns of one
-// row of A and stores them with one vector write.
-//
-// Range: the midpoint reference keeps every fp16 operand within e^{+-(half-chunk decay)}.  The
-// exponents are clamped at 11 (e^11 < 65504), so a per-channel log-decay sum below -11 over half
-// a chunk loses accuracy (the token-by-token path has no such limit).
+// computed transposed (A^T = K Q^T) so that each lane owns four consecutive columns of one row
+// of A and stores them with one vector write.
 
 #include "dr_device.h"
 #include "dr_internal.h"
@@ -60,7 +64,6 @@ constexpr int KS = 136;    // row stride (halves) of [64][128] tiles: 16-byte pa
 constexpr int CS = 72;     // row stride (halves) of [*][64] tiles
 constexpr int AFS = 68;    // row stride (floats) of the fp32 64 x 64 matrix (16-byte rows)
 constexpr int kThreads = 256;
-constexpr float kExpClamp = 11.f;
 
 // Lower-triangular 16x16 tile (I, J), I >= J, enumerated row by row.
 __device__ __forceinline__ void tile_ij(int idx, int& I, int& J) {
@@ -92,8 +95,6 @@ __device__ __forceinline__ void bf16x8_to_f32(uint4 u, float* f) {
   f[6] = __uint_as_float(u.w << 16); f[7] = __uint_as_float(u.w & 0xffff0000u);
 }
 
-__device__ __forceinline__ float clamped_exp(float x) { return __expf(fminf(x, kExpClamp)); }
-
 __device__ __forceinline__ void unpack8(float4 a, float4 b, float* f) {
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
@@ -108,80 +109,19 @@ __device__ __forceinline__ float4 ldf16(gptr<const char> base, int64_t off) {
   return make_float4(x.x, x.y, x.z, x.w);
 }
 
-// Chunk-local inclusive prefix sums of the log-decay.  Thread (token quad tg, channel octet
-// d8) holds its 4 x 8 (per channel) or 4 (per head: wave 0 lane t holds token t) log-decays;
-// on return g[r][ch] (per head: g[r][0]) is the cumulative log-decay of its tokens and GSC holds
-// per-wave totals (per channel, [4][128]) or the 64 per-token prefixes (per head).
-template <bool DCH>
-__device__ __forceinline__ void chunk_cumsum(const float (&ldr)[DCH ? 4 : 1][DCH ? 8 : 1], float lds,
-                                             float (&g)[4][DCH ? 8 : 1], float* GSC, int tid) {
-  const int lane = tid & 63, wave = tid >> 6, lg = lane >> 4, d8 = tid & 15, tg = tid >> 4;
-  if constexpr (DCH) {
-    float ex[8];
-#pragma unroll
-    for (int ch = 0; ch < 8; ++ch) {
-      float acc = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        acc += ldr[r][ch];
-        g[r][ch] = acc;
-      }
-      // inclusive scan of the quad totals over the 4 token quads of this wave (lanes 16 apart)
-      float x = acc, y;
-      y = __shfl_up(x, 16);
-      if (lg >= 1) x += y;
-      y = __shfl_up(x, 32);
-      if (lg >= 2) x += y;
-      ex[ch] = x - acc;
-      if (lg == 3) GSC[wave * D + 8 * d8 + ch] = x;
-    }
-    lds_barrier();
-#pragma unroll
-    for (int ch = 0; ch < 8; ++ch) {
-      float pre = ex[ch];
-      for (int w = 0; w < wave; ++w) pre += GSC[w * D + 8 * d8 + ch];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) g[r][ch] += pre;
-    }
-  } else {
-    if (wave == 0) {
-      float x = lds;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-      }
-      GSC[lane] = x;
-    }
-    lds_barrier();
-#pragma unroll
-    for (int r = 0; r < 4; ++r) g[r][0] = GSC[4 * tg + r];
-  }
-}
-
-template <bool DCH>
-__device__ __forceinline__ float chunk_gmid(const float* GSC, int d) {
-  return DCH ? GSC[d] + GSC[D + d] : GSC[31];
-}
-
-template <bool DCH>
-__device__ __forceinline__ float chunk_gend(const float* GSC, int d) {
-  return DCH ? GSC[d] + GSC[D + d] + GSC[2 * D + d] + GSC[3 * D + d] : GSC[63];
-}
-
 // ------------------------------------------------------------------------------------------
 // Per-chunk packet in the workspace (byte offsets).  Matrices are fp16 64 x 64 with zero upper
 // triangles, in the order T, A_qk (, A_kk, A_qu for general gates); tiles are fp16; the gate
 // vector is fp32 [512].
 //   scalar decay, symmetric gates: matrices, k [64][128], q [64][128] (plain), gates
-//     {beta[64], e^{g-gm}[64], e^{gm-g}[64], e^{gm}, e^{gC}, e^{gC-gm}}
-//   otherwise: matrices, K+ [64][128], Q+ [64][128], K-^T [128][64] (, U-^T [128][64]),
-//     gates {beta[64] (symmetric gates), e^{gm}[128], e^{gC}[128], e^{gC-gm}[128]}
-// Every fp16 row is a run of 16-byte units (16 per 128-wide row, 8 per 64-wide row) stored
-// XOR-swizzled, unit u of row r at position u ^ swz_key<U>(r), so that the scan can copy a tile
-// into LDS as is and still read matrix-core fragments without bank conflicts.
-// With FG2's per-channel rate (VP) the packet also carries the scaled values v~ = sqrt(beta) v
-// as fp16 [64][128], row-major (the scan copies its value slice from there).
+//     {beta[64], e^{g}[64], e^{g_C - g}[64], 1, e^{g_C}, 1}
+//   otherwise: matrices, K+ [64][128], Q+ [64][128], K^end [64][128] (, U^end [64][128]), gates
+//     {beta[64] (symmetric gates), 1[128], e^{g_C}[128], 1[128]}
+// Every fp16 row is a run of 16-byte units (16 per 128-wide row) stored XOR-swizzled, unit u of
+// row r at position u ^ swz_key<16>(r), so that the scan can copy a tile into LDS as is and
+// still read matrix-core fragments (and, from K^end, transposed fragments) without bank
+// conflicts.  With FG2's per-channel rate (VP) the packet also carries the scaled values
+// v~ = sqrt(beta) v as fp16 [64][128], row-major (the scan copies its value slice from there).
 // ------------------------------------------------------------------------------------------
 template <bool DCH, bool GEN, bool VP = false>
 struct Packet {
@@ -224,6 +164,12 @@ __device__ __forceinline__ int swz_key(int r) {
 template <int U>
 __device__ __forceinline__ int swz(int r, int col) {
   return (r * U + ((col >> 3) ^ swz_key<U>(r))) * 8 + (col & 7);
+}
+
+// Fragment (as frag()) of a swizzled tile with U 16-byte units per row.
+template <int U>
+__device__ __forceinline__ half8 frag_s(const _Float16* base, int row0, int k0, int lane) {
+  return *reinterpret_cast<const half8*>(base + swz<U>(row0 + (lane & 15), k0 + 8 * (lane >> 4)));
 }
 
 // Lower-triangular 64 x 64 fp16 matrices (T, A_qk) of the symmetric-gate packet: only the six
@@ -327,377 +273,47 @@ __device__ void pass_state(const Problem& p, int bh, int j0, int ncols) {
   }
 }
 
-// Per-channel decay or general gates: held to two waves per SIMD (the input prefetch would
-// otherwise take the registers of the second resident workgroup).  FG2: the erase array holds
-// FG2-GDN's per-channel rate beta ("FG2-GDN ...", section 2, update rule), absorbed here as
-// k~ = sqrt(beta) k (every tile and Gram product takes k~) and v~ = sqrt(beta) v (into the
-// packet), with the unit gate in place of the per-token erase/write gate.
-template <bool DCH, bool GEN, bool FG2 = false>
-__global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_kernel(Problem p, char* __restrict__ ws,
-                                                                                     int nchunks, int64_t nblk) {
-  static_assert(!(FG2 && GEN), "the per-channel rate keeps the symmetric gates");
-  // Packed sequences: the work items are (chunk, head) pairs over the chunk table.
-  if (p.chunks) nblk = int64_t(p.H) * *p.nchunks_total;
-  using PK = Packet<DCH, GEN, FG2>;
-  constexpr int NM = PK::nmat;
-  __shared__ __attribute__((aligned(16))) _Float16 KP[C * KS];                 // K+
-  __shared__ __attribute__((aligned(16))) _Float16 KM[C * KS];                 // K-
-  __shared__ __attribute__((aligned(16))) _Float16 QP[C * KS];                 // Q+
-  __shared__ __attribute__((aligned(16))) _Float16 UM[GEN ? C * KS : 8];       // U- (general)
-  // fp32 matrix of the solve.  With general gates it takes the place of Q+ (same size), whose
-  // last reader runs before it is written: that keeps two workgroups per compute unit.
-  __shared__ __attribute__((aligned(16))) float AFA[GEN ? 4 : C * AFS];
-  __shared__ __attribute__((aligned(16))) _Float16 TH[C * CS];
-  __shared__ float GB[C];
-  __shared__ float GSC[4 * D];
-  static_assert(C * KS * 2 == C * AFS * 4, "the solve matrix must fit in the Q+ tile");
-  float* const AF = GEN ? reinterpret_cast<float*>(QP) : AFA;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, lg = lane >> 4;
-  const int d8 = tid & 15, tg = tid >> 4;
-  const int T = p.T, H = p.H;
-  const gptr<const uint16_t> kin = opaque_gptr(static_cast<const uint16_t*>(p.k));
-  const gptr<const uint16_t> qin = opaque_gptr(static_cast<const uint16_t*>(p.q));
-  const gptr<const float> ldin = opaque_gptr(p.log_decay);
-  const gptr<const float> erin = opaque_gptr(p.erase);
-  const bool erase_ch = GEN && p.erase_channel;
-
-  // Inputs of one chunk in registers: thread (token quad tg, channel octet d8) holds tokens
-  // 4 tg + r, channels 8 d8 .. + 7; threads < 64 hold token tid's per-head gates.  Tokens past
-  // the end load token T - 1 (zeroed where they are used), so every load is unconditional.
-  // Per-channel decay with general gates does not prefetch the per-channel erase gates (their
-  // registers would spill under the two-workgroup bound); it loads them as the chunk starts,
-  // ahead of their first use after the prefix sums.
-  constexpr bool kPrefetchErr = GEN && !DCH;
-  struct In {
-    uint4 kr[4], qr[4];
-    float ldr[DCH ? 4 : 1][DCH ? 8 : 1];
-    float err[kPrefetchErr ? 4 : 1][kPrefetchErr ? 8 : 1];
-    float lds, gb;
-  };
-  // Work item blk: a dense batch walks (b, h, chunk) with packet index blk; packed sequences
-  // walk (chunk, head) over the chunk table.  Work items number fewer than 2^31 (one packet
-  // each, and the packets fit in device memory), so the index arithmetic is 32-bit.
-  auto chunk_ref = [&](int64_t blk) {
-    ChunkRef r;
-    const uint32_t ub = uint32_t(blk);
-    if (p.chunks) {
-      const uint32_t g = ub / uint32_t(H);
-      r.h = int(ub - g * uint32_t(H));
-      const int4 e = p.chunks[g];
-      r.tok0 = e.x;
-      r.tlen = e.y;
-      r.pkt = int64_t(e.z) + int64_t(r.h) * e.w;
-    } else {
-      const uint32_t bh = ub / uint32_t(nchunks);
-      const int c = int(ub - bh * uint32_t(nchunks));
-      const int b = int(bh / uint32_t(H));
-      r.h = int(bh) - b * H;
-      r.tok0 = int64_t(b) * T + int64_t(c) * C;
-      r.tlen = T - c * C < C ? T - c * C : C;
-      r.pkt = blk;
-    }
-    return r;
-  };
-  auto tok_of = [&](const ChunkRef& cr) {
-    return [=](int t) { return (cr.tok0 + (t < cr.tlen ? t : cr.tlen - 1)) * H + cr.h; };
-  };
-  auto load_err = [&](float (&e)[4][8], const ChunkRef& cr) {
-    const auto tok = tok_of(cr);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t base = tok(4 * tg + r) * D + 8 * d8;
-      unpack8(gload_f4(erin, base), gload_f4(erin, base + 4), e[r]);
-    }
-  };
-  auto load_in = [&](In& I, int64_t blk) {
-    const ChunkRef cr = chunk_ref(blk);
-    const auto tok = tok_of(cr);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t base = tok(4 * tg + r) * D + 8 * d8;
-      I.kr[r] = gload_u4(kin, base);
-      I.qr[r] = gload_u4(qin, base);
-      if constexpr (DCH) unpack8(gload_f4(ldin, base), gload_f4(ldin, base + 4), I.ldr[r]);
-    }
-    if constexpr (kPrefetchErr) {
-      if (erase_ch) load_err(I.err, cr);
-    }
-    if (tid < C) {
-      const int64_t ti = tok(tid);
-      if constexpr (!DCH) I.lds = ldin[ti];
-      if (!erase_ch && !FG2) I.gb = erin[ti];
-    }
-  };
-
-  // One chunk: prefix sums, operand tiles, gates, Gram matrices, triangular solve.  The solve
-  // factor T stays in TH and is written out by the next chunk (or after the last), so that the
-  // next chunk's wait for its inputs does not also wait for these stores.
-  auto write_t = [&](int64_t pkt) {
-    _Float16* wsc = reinterpret_cast<_Float16*>(ws + pkt * PK::bytes + PK::mat);
-    const int t = tid >> 2, c0 = (tid & 3) * 16;
-    if (c0 < 32 || t >= 32) {  // the blocks that hold nonzeros
-      *reinterpret_cast<uint4*>(wsc + tri_pos(t, c0)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0);
-      *reinterpret_cast<uint4*>(wsc + tri_pos(t, c0 + 8)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0 + 8);
-    }
-  };
-
-  // Per-channel decay with general gates or with FG2's rate keeps no chunk in flight (its
-  // registers would spill); the second resident workgroup covers its load latency instead.
-  constexpr bool kPrefetch = !(DCH && GEN) && !(DCH && FG2);
-  In I;
-  int64_t blk = blockIdx.x;
-  const int64_t gstride = gridDim.x;
-  if constexpr (kPrefetch) {
-    if (blk < nblk) load_in(I, blk);
+// One chunk of prep work, from its work-item index: a dense batch walks (b, h, chunk) with
+// packet index blk; packed sequences walk (chunk, head) over the chunk table.  Work items number
+// fewer than 2^31 (one packet each, and the packets fit in device memory), so the index
+// arithmetic is 32-bit.
+__device__ __forceinline__ ChunkRef chunk_ref_of(const Problem& p, int64_t blk, int nchunks) {
+  ChunkRef r;
+  const uint32_t ub = uint32_t(blk);
+  if (p.chunks) {
+    const uint32_t g = ub / uint32_t(p.H);
+    r.h = int(ub - g * uint32_t(p.H));
+    const int4 e = p.chunks[g];
+    r.tok0 = e.x;
+    r.tlen = e.y;
+    r.pkt = int64_t(e.z) + int64_t(r.h) * e.w;
+  } else {
+    const uint32_t bh = ub / uint32_t(nchunks);
+    const int c = int(ub - bh * uint32_t(nchunks));
+    const int b = int(bh / uint32_t(p.H));
+    r.h = int(bh) - b * p.H;
+    r.tok0 = int64_t(b) * p.T + int64_t(c) * C;
+    r.tlen = p.T - c * C < C ? p.T - c * C : C;
+    r.pkt = blk;
   }
-  for (int64_t prev = -1; blk < nblk; blk += gstride) {
-    const ChunkRef cr = chunk_ref(blk);
-    char* pk = ws + cr.pkt * PK::bytes;  // this chunk's packet
-    _Float16* wsc = reinterpret_cast<_Float16*>(pk + PK::mat);
-    float* gv = reinterpret_cast<float*>(pk + PK::gate);
-    if constexpr (!kPrefetch) load_in(I, blk);
-    // FG2: this thread's rates and values, issued with the chunk's other inputs
-    float rt[FG2 ? 4 : 1][FG2 ? 8 : 1];
-    uint4 vr[FG2 ? 4 : 1];
-    if constexpr (FG2) {
-      const gptr<const uint16_t> vin = opaque_gptr(static_cast<const uint16_t*>(p.v));
-      load_err(rt, cr);
-      const auto tok = tok_of(cr);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vr[r] = gload_u4(vin, tok(4 * tg + r) * D + 8 * d8);
-    }
-    vm_wait_all();  // this chunk's inputs (loaded one chunk ago) and the older stores
+  return r;
+}
 
-    // ---- inputs, masked past the last token --------------------------------------------
-    uint4 kr[4], qr[4];
-    float ldr[DCH ? 4 : 1][DCH ? 8 : 1];
-    float err[GEN ? 4 : 1][GEN ? 8 : 1];
-    float en[GEN && !kPrefetchErr ? 4 : 1][GEN && !kPrefetchErr ? 8 : 1];
-    if constexpr (GEN && !kPrefetchErr) {
-      if (erase_ch) load_err(en, cr);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool ok = 4 * tg + r < cr.tlen;
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      kr[r] = ok ? I.kr[r] : z;
-      qr[r] = ok ? I.qr[r] : z;
-      if constexpr (DCH) {
-#pragma unroll
-        for (int ch = 0; ch < 8; ++ch) ldr[r][ch] = ok ? I.ldr[r][ch] : 0.f;
-      }
-      if constexpr (GEN) {
-#pragma unroll
-        for (int ch = 0; ch < 8; ++ch) err[r][ch] = (ok && erase_ch) ? (kPrefetchErr ? I.err[r][ch] : en[r][ch]) : 0.f;
-      }
-    }
-    // FG2: k~ = sqrt(beta) k replaces k (held as fp16 from here on) and v~ = sqrt(beta) v goes
-    // to the packet, right away, so that neither the rates nor the values stay in registers.
-    // Rows past the end are zero.
-    if constexpr (FG2) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = 4 * tg + r < cr.tlen;
-        float kf[8], vf[8];
-        bf16x8_to_f32(kr[r], kf);
-        bf16x8_to_f32(vr[r], vf);
-#pragma unroll
-        for (int ch = 0; ch < 8; ++ch) {
-          const float s = ok ? sqrtf(rt[r][ch]) : 0.f;
-          kf[ch] *= s;
-          vf[ch] *= s;
-        }
-        kr[r] = __builtin_bit_cast(uint4, cvt8(kf));
-        *reinterpret_cast<half8*>(pk + PK::vt + 2 * ((4 * tg + r) * D + 8 * d8)) = cvt8(vf);
-      }
-    }
-    float lds = 0.f;
-    if (tid < C) {
-      const bool ok = tid < cr.tlen;
-      if constexpr (!DCH) lds = ok ? I.lds : 0.f;
-      GB[tid] = (ok && !erase_ch) ? (FG2 ? 1.f : I.gb) : 0.f;
-    }
+// The solve factor T (fp16 in LDS, row stride CS, zero upper triangle) into the six stored
+// 16 x 32 blocks of the packet's first matrix.
+__device__ __forceinline__ void write_tri_t(char* mat, const _Float16* TH, int tid) {
+  _Float16* wsc = reinterpret_cast<_Float16*>(mat);
+  const int t = tid >> 2, c0 = (tid & 3) * 16;
+  if (c0 < 32 || t >= 32) {  // the blocks that hold nonzeros
+    *reinterpret_cast<uint4*>(wsc + tri_pos(t, c0)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0);
+    *reinterpret_cast<uint4*>(wsc + tri_pos(t, c0 + 8)) = *reinterpret_cast<const uint4*>(TH + t * CS + c0 + 8);
+  }
+}
 
-    float g[4][DCH ? 8 : 1];
-    chunk_cumsum<DCH>(ldr, lds, g, GSC, tid);
-
-    {
-      float gm[8];
-#pragma unroll
-      for (int ch = 0; ch < 8; ++ch) gm[ch] = chunk_gmid<DCH>(GSC, 8 * d8 + ch);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * tg + r;
-        float kf[8], qf[8], kp[8], km[8], qp[8];
-        if constexpr (FG2) {  // k~, fp16
-          const half8 h = __builtin_bit_cast(half8, kr[r]);
-#pragma unroll
-          for (int ch = 0; ch < 8; ++ch) kf[ch] = float(h[ch]);
-        } else {
-          bf16x8_to_f32(kr[r], kf);
-        }
-        bf16x8_to_f32(qr[r], qf);
-        if constexpr (PK::kScal) {
-          // scalar decay: plain k and q, in LDS for the Gram products (which take the decay per
-          // element, e^{g_t - g_i}) and in the packet for the scan
-          const half8 hk = cvt8(kf), hq = cvt8(qf);
-          *reinterpret_cast<half8*>(KP + t * KS + 8 * d8) = hk;
-          *reinterpret_cast<half8*>(QP + t * KS + 8 * d8) = hq;
-          *reinterpret_cast<half8*>(pk + PK::kp + 2 * swz<16>(t, 8 * d8)) = hk;
-          *reinterpret_cast<half8*>(pk + PK::qp + 2 * swz<16>(t, 8 * d8)) = hq;
-          continue;
-        }
-#pragma unroll
-        for (int ch = 0; ch < 8; ++ch) {
-          const float gg = DCH ? g[r][ch] : g[r][0];
-          const float fp = clamped_exp(gg - gm[ch]), fm = clamped_exp(gm[ch] - gg);
-          kp[ch] = kf[ch] * fp;
-          qp[ch] = qf[ch] * fp;
-          km[ch] = kf[ch] * fm;
-        }
-        *reinterpret_cast<half8*>(KP + t * KS + 8 * d8) = cvt8(kp);
-        *reinterpret_cast<half8*>(QP + t * KS + 8 * d8) = cvt8(qp);
-        *reinterpret_cast<half8*>(KM + t * KS + 8 * d8) = cvt8(km);
-        if constexpr (GEN) {
-          float um[8];
-#pragma unroll
-          for (int ch = 0; ch < 8; ++ch) um[ch] = (erase_ch ? err[r][ch] : GB[t]) * km[ch];
-          *reinterpret_cast<half8*>(UM + t * KS + 8 * d8) = cvt8(um);
-        }
-      }
-    }
-
-    // per-channel decay: the registers are free, fetch the next chunk's inputs right away
-    if constexpr (!PK::kScal && kPrefetch) {
-      if (blk + gstride < nblk) load_in(I, blk + gstride);
-    }
-
-    // gate vector
-    if constexpr (PK::kScal) {
-      if (tid < C) {
-        const float x = GSC[tid] - GSC[31];
-        gv[GV_BETA + tid] = GB[tid];
-        gv[GV_FP + tid] = clamped_exp(x);
-        gv[GV_FM + tid] = clamped_exp(-x);
-      } else if (tid == C) {
-        const float gmid = GSC[31], gend = GSC[63];
-        *reinterpret_cast<float4*>(gv + GV_SC) =
-            make_float4(clamped_exp(gmid), expf(gend), clamped_exp(gend - gmid), 0.f);
-      }
-    } else {
-      if (tid < C) gv[GV_BETA + tid] = GB[tid];
-      if (tid < D) {
-        const float gmid = chunk_gmid<DCH>(GSC, tid), gend = chunk_gend<DCH>(GSC, tid);
-        gv[GV_EM + tid] = clamped_exp(gmid);
-        gv[GV_FC + tid] = expf(gend);
-        gv[GV_FCM + tid] = clamped_exp(gend - gmid);
-      }
-    }
-    if (prev >= 0) write_t(prev);  // the previous chunk's T, still in TH
-    lds_barrier();
-    for (int i = tid; i < C * CS; i += kThreads) TH[i] = (_Float16)0.f;
-
-    // Gram tiles, transposed: lane gets A[t = 16 I + l16][i = 16 J + 4 lg + r].
-    //   0: A for the solve (symmetric: beta_t A_kk; general: A_ku), strict, fp32 to LDS
-    //   1: A_qk (lower), 2: A_kk (strict), 3: A_qu (lower), fp16 to the workspace
-    auto gram_tile = [&](int idx) {
-      const int which = idx / 10;
-      int I0, J0;
-      tile_ij(idx - 10 * which, I0, J0);
-      const _Float16* Ab = (which == 3 || (GEN && which == 0)) ? UM : PK::kScal ? KP : KM;
-      const _Float16* Bb = (which == 1 || which == 3) ? QP : KP;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        acc = mfma16x16x32(frag(Ab, KS, 16 * J0, 32 * ks, lane), frag(Bb, KS, 16 * I0, 32 * ks, lane), acc);
-      const int t = 16 * I0 + l16;
-      const int i0 = 16 * J0 + 4 * lg;
-      if constexpr (PK::kScal) {
-        // the decay between token i and token t >= i: e^{g_t - g_i} <= 1 (entries above the
-        // diagonal are zeroed below)
-        const float gt = GSC[t];
-        const float4 gi = *reinterpret_cast<const float4*>(GSC + i0);
-        acc[0] *= __expf(fminf(gt - gi.x, 0.f));
-        acc[1] *= __expf(fminf(gt - gi.y, 0.f));
-        acc[2] *= __expf(fminf(gt - gi.z, 0.f));
-        acc[3] *= __expf(fminf(gt - gi.w, 0.f));
-      }
-      if (which == 0) {
-        const float sc = GEN ? 1.f : GB[t];
-        float4 v;
-        v.x = (i0 + 0 < t) ? sc * acc[0] : 0.f;
-        v.y = (i0 + 1 < t) ? sc * acc[1] : 0.f;
-        v.z = (i0 + 2 < t) ? sc * acc[2] : 0.f;
-        v.w = (i0 + 3 < t) ? sc * acc[3] : 0.f;
-        *reinterpret_cast<float4*>(AF + t * AFS + i0) = v;
-      } else {
-        const bool strict = which == 2;
-        half4v hv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hv[r] = (_Float16)((strict ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f);
-        *reinterpret_cast<half4v*>(wsc + which * (PK::matb / 2) + tri_pos(t, i0)) = hv;
-      }
-    };
-    constexpr int NG = 10 * NM;
-    // with general gates the solve matrix (tiles 0..9) overwrites Q+ and comes after the rest
-    constexpr int G0 = GEN ? 10 : 0;
-    // not unrolled with a per-channel decay: unrolled, the fragment loads are
-    // hoisted and the registers spill under the two-workgroup bound
-    constexpr int kGramUnroll = DCH ? 1 : (NG - G0 + 3) / 4;
-#pragma unroll kGramUnroll
-    for (int n = 0; n < (NG - G0 + 3) / 4; ++n) {
-      const int idx = G0 + wave + 4 * n;
-      if (idx < NG) gram_tile(idx);
-    }
-    // the upper-triangular 16 x 16 tiles (0,1) and (2,3) of the workspace matrices after T share
-    // a stored block with nonzeros and are zero (T's come from TH)
-    for (int n = wave; n < 2 * (NM - 1); n += 4) {
-      const half4v z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
-      const int m = 1 + n / 2, I0 = 2 * (n % 2), J0 = I0 + 1;
-      *reinterpret_cast<half4v*>(wsc + m * (PK::matb / 2) + tri_pos(16 * I0 + l16, 16 * J0 + 4 * lg)) = z;
-    }
-    // operand tiles for the scan (per-channel decay or general gates): K+, Q+ row-major;
-    // K-, U- transposed ([channel][token]); all swizzled
-    if constexpr (!PK::kScal) {
-#pragma unroll
-      for (int i = 0; i < C * D / 8 / kThreads; ++i) {
-        const int u = tid + kThreads * i;
-        const int t = u >> 4, c8 = ((u & 15) ^ swz_key<16>(t)) * 8;  // stored unit u & 15 holds column c8
-        *reinterpret_cast<uint4*>(pk + PK::kp + 16 * u) = *reinterpret_cast<const uint4*>(KP + t * KS + c8);
-        *reinterpret_cast<uint4*>(pk + PK::qp + 16 * u) = *reinterpret_cast<const uint4*>(QP + t * KS + c8);
-      }
-#pragma unroll
-      for (int i = 0; i < C * D / 8 / kThreads; ++i) {
-        const int d = tid & (D - 1), t0 = 8 * ((tid >> 7) + 2 * i);
-        half8 x;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = KM[(t0 + j) * KS + d];
-        *reinterpret_cast<half8*>(pk + PK::kmt + 2 * swz<8>(d, t0)) = x;
-        if constexpr (GEN) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = UM[(t0 + j) * KS + d];
-          *reinterpret_cast<half8*>(pk + PK::umt + 2 * swz<8>(d, t0)) = x;
-        }
-      }
-    }
-    lds_barrier();
-    if constexpr (GEN) {
-      // A_ku into the solve matrix, now that Q+ has been read for the last time
-#pragma unroll
-      for (int n = 0; n < 3; ++n) {
-        const int idx = wave + 4 * n;
-        if (idx < 10) gram_tile(idx);
-      }
-      lds_barrier();
-    }
-    // scalar decay: fetch the next chunk's inputs only now, in flight during the solve, which
-    // keeps them out of the Gram stage's registers (measured faster for this variant)
-    if constexpr (PK::kScal) {
-      if (blk + gstride < nblk) load_in(I, blk + gstride);
-    }
-
+// T = (I + A)^{-1} for the strictly lower-triangular fp32 A in AF (row stride AFS), into TH
+// (fp16, zero upper triangle, which the caller has cleared).  Ends with a barrier.
+__device__ __forceinline__ void solve_t(const float* AF, _Float16* TH, int tid) {
+  const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, lg = lane >> 4;
     // Diagonal 16x16 blocks: fp32 forward substitution, one lane per (block, column).
     if (wave == 0) {
       const int bl = lg, col = l16;
@@ -743,7 +359,719 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
       }
       lds_barrier();
     }
+}
+
+template <int N>
+struct IntTag {
+  static constexpr int value = N;
+};
+
+// ------------------------------------------------------------------------------------------
+// Prep, per-head decay with one per-head erase/write gate (scalar-gate Gated DeltaNet; FG2's
+// rate with a per-head decay).  Persistent: each workgroup walks every grid-th chunk with the
+// next chunk's inputs in flight.  The decay is one scalar per token, so the Gram products run on
+// the plain k and q tiles and take the decay between token i and token t >= i per element,
+// e^{g_t - g_i} <= 1, in fp32.  The packet carries plain k and q and the scan's per-token
+// factors relative to the chunk start, e^{g_t} (rows of K S and Q S) and e^{g_C - g_t} (rows of
+// the update's delta), so every factor is at most one whatever the decay.
+// ------------------------------------------------------------------------------------------
+template <bool FG2>
+__global__ __launch_bounds__(kThreads, 1) void chunk_prep_scalar_kernel(Problem p, char* __restrict__ ws,
+                                                                        int nchunks, int64_t nblk) {
+  // Packed sequences: the work items are (chunk, head) pairs over the chunk table.
+  if (p.chunks) nblk = int64_t(p.H) * *p.nchunks_total;
+  using PK = Packet<false, false, FG2>;
+  __shared__ __attribute__((aligned(16))) _Float16 KP[C * KS];  // k
+  __shared__ __attribute__((aligned(16))) _Float16 QP[C * KS];  // q
+  __shared__ __attribute__((aligned(16))) float AF[C * AFS];    // fp32 matrix of the solve
+  __shared__ __attribute__((aligned(16))) _Float16 TH[C * CS];
+  __shared__ float GB[C];
+  __shared__ float GSC[C];  // chunk-local cumulative log-decay per token
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, lg = lane >> 4;
+  const int d8 = tid & 15, tg = tid >> 4;
+  const int H = p.H;
+  const gptr<const uint16_t> kin = opaque_gptr(static_cast<const uint16_t*>(p.k));
+  const gptr<const uint16_t> qin = opaque_gptr(static_cast<const uint16_t*>(p.q));
+  const gptr<const float> ldin = opaque_gptr(p.log_decay);
+  const gptr<const float> erin = opaque_gptr(p.erase);
+
+  // Inputs of one chunk in registers: thread (token quad tg, channel octet d8) holds tokens
+  // 4 tg + r, channels 8 d8 .. + 7; threads < 64 hold token tid's per-head gates.  Tokens past
+  // the end load token T - 1 (zeroed where they are used), so every load is unconditional.
+  struct In {
+    uint4 kr[4], qr[4];
+    float lds, gb;
+  };
+  // Work item blk: a dense batch walks (b, h, chunk) with packet index blk; packed sequences
+  // walk (chunk, head) over the chunk table.  Work items number fewer than 2^31 (one packet
+  // each, and the packets fit in device memory), so the index arithmetic is 32-bit.
+  auto chunk_ref = [&](int64_t blk) { return chunk_ref_of(p, blk, nchunks); };
+  auto tok_of = [&](const ChunkRef& cr) {
+    return [=](int t) { return (cr.tok0 + (t < cr.tlen ? t : cr.tlen - 1)) * H + cr.h; };
+  };
+  auto load_in = [&](In& I, int64_t blk) {
+    const ChunkRef cr = chunk_ref(blk);
+    const auto tok = tok_of(cr);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t base = tok(4 * tg + r) * D + 8 * d8;
+      I.kr[r] = gload_u4(kin, base);
+      I.qr[r] = gload_u4(qin, base);
+    }
+    if (tid < C) {
+      const int64_t ti = tok(tid);
+      I.lds = ldin[ti];
+      if (!FG2) I.gb = erin[ti];
+    }
+  };
+
+  // The solve factor T stays in TH and is written out by the next chunk (or after the last),
+  // so that the next chunk's wait for its inputs does not also wait for these stores.
+  auto write_t = [&](int64_t pkt) { write_tri_t(ws + pkt * PK::bytes + PK::mat, TH, tid); };
+
+  In I;
+  int64_t blk = blockIdx.x;
+  const int64_t gstride = gridDim.x;
+  if (blk < nblk) load_in(I, blk);
+  for (int64_t prev = -1; blk < nblk; blk += gstride) {
+    const ChunkRef cr = chunk_ref(blk);
+    char* pk = ws + cr.pkt * PK::bytes;  // this chunk's packet
+    _Float16* wsc = reinterpret_cast<_Float16*>(pk + PK::mat);
+    float* gv = reinterpret_cast<float*>(pk + PK::gate);
+    // FG2: this thread's rates and values, issued with the chunk's other inputs
+    float rt[FG2 ? 4 : 1][FG2 ? 8 : 1];
+    uint4 vr[FG2 ? 4 : 1];
+    if constexpr (FG2) {
+      const gptr<const uint16_t> vin = opaque_gptr(static_cast<const uint16_t*>(p.v));
+      const auto tok = tok_of(cr);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t base = tok(4 * tg + r) * D + 8 * d8;
+        unpack8(gload_f4(erin, base), gload_f4(erin, base + 4), rt[r]);
+        vr[r] = gload_u4(vin, base);
+      }
+    }
+    vm_wait_all();  // this chunk's inputs (loaded one chunk ago) and the older stores
+
+    uint4 kr[4], qr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = 4 * tg + r < cr.tlen;
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      kr[r] = ok ? I.kr[r] : z;
+      qr[r] = ok ? I.qr[r] : z;
+    }
+    float lds = 0.f;
+    if (tid < C) {
+      const bool ok = tid < cr.tlen;
+      lds = ok ? I.lds : 0.f;
+      GB[tid] = ok ? (FG2 ? 1.f : I.gb) : 0.f;
+    }
+    // chunk-local inclusive prefix sums of the log-decay (wave 0 lane t holds token t)
+    if (wave == 0) {
+      float x = lds;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+      }
+      GSC[lane] = x;
+    }
+    // plain k and q (FG2: k~ = sqrt(beta) k), in LDS for the Gram products and in the packet for
+    // the scan; FG2's v~ = sqrt(beta) v goes straight to the packet.  Rows past the end are zero.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * tg + r;
+      float kf[8], qf[8];
+      bf16x8_to_f32(kr[r], kf);
+      bf16x8_to_f32(qr[r], qf);
+      if constexpr (FG2) {
+        const bool ok = t < cr.tlen;
+        float vf[8];
+        bf16x8_to_f32(vr[r], vf);
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) {
+          const float s = ok ? sqrtf(rt[r][ch]) : 0.f;
+          kf[ch] *= s;
+          vf[ch] *= s;
+        }
+        *reinterpret_cast<half8*>(pk + PK::vt + 2 * (t * D + 8 * d8)) = cvt8(vf);
+      }
+      const half8 hk = cvt8(kf), hq = cvt8(qf);
+      *reinterpret_cast<half8*>(KP + t * KS + 8 * d8) = hk;
+      *reinterpret_cast<half8*>(QP + t * KS + 8 * d8) = hq;
+      *reinterpret_cast<half8*>(pk + PK::kp + 2 * swz<16>(t, 8 * d8)) = hk;
+      *reinterpret_cast<half8*>(pk + PK::qp + 2 * swz<16>(t, 8 * d8)) = hq;
+    }
+    if (prev >= 0) write_t(prev);  // the previous chunk's T, still in TH
+    lds_barrier();
+    // gate vector: beta, and the scan's row factors relative to the chunk start (all <= 1)
+    if (tid < C) {
+      gv[GV_BETA + tid] = GB[tid];
+      gv[GV_FP + tid] = __expf(GSC[tid]);
+      gv[GV_FM + tid] = __expf(GSC[C - 1] - GSC[tid]);
+    } else if (tid == C) {
+      *reinterpret_cast<float4*>(gv + GV_SC) = make_float4(1.f, __expf(GSC[C - 1]), 1.f, 0.f);
+    }
+    for (int i = tid; i < C * CS; i += kThreads) TH[i] = (_Float16)0.f;
+
+    // Gram tiles, transposed: lane gets A[t = 16 I + l16][i = 16 J + 4 lg + r].
+    //   which 0: beta_t A_kk (strict), fp32 to LDS for the solve; 1: A_qk (lower), fp16 to the packet
+    auto gram_tile = [&](int idx) {
+      const int which = idx / 10;
+      int I0, J0;
+      tile_ij(idx - 10 * which, I0, J0);
+      const _Float16* Bb = which == 1 ? QP : KP;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc = mfma16x16x32(frag(KP, KS, 16 * J0, 32 * ks, lane), frag(Bb, KS, 16 * I0, 32 * ks, lane), acc);
+      const int t = 16 * I0 + l16;
+      const int i0 = 16 * J0 + 4 * lg;
+      // the decay between token i and token t >= i: e^{g_t - g_i} <= 1 (entries above the
+      // diagonal are zeroed below)
+      const float gt = GSC[t];
+      const float4 gi = *reinterpret_cast<const float4*>(GSC + i0);
+      acc[0] *= __expf(fminf(gt - gi.x, 0.f));
+      acc[1] *= __expf(fminf(gt - gi.y, 0.f));
+      acc[2] *= __expf(fminf(gt - gi.z, 0.f));
+      acc[3] *= __expf(fminf(gt - gi.w, 0.f));
+      if (which == 0) {
+        const float sc = GB[t];
+        float4 v;
+        v.x = (i0 + 0 < t) ? sc * acc[0] : 0.f;
+        v.y = (i0 + 1 < t) ? sc * acc[1] : 0.f;
+        v.z = (i0 + 2 < t) ? sc * acc[2] : 0.f;
+        v.w = (i0 + 3 < t) ? sc * acc[3] : 0.f;
+        *reinterpret_cast<float4*>(AF + t * AFS + i0) = v;
+      } else {
+        half4v hv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(i0 + r <= t ? acc[r] : 0.f);
+        *reinterpret_cast<half4v*>(wsc + PK::matb / 2 + tri_pos(t, i0)) = hv;
+      }
+    };
+#pragma unroll
+    for (int n = 0; n < 5; ++n) gram_tile(wave + 4 * n);
+    // the upper-triangular 16 x 16 tiles (0,1) and (2,3) of A_qk share a stored block with
+    // nonzeros and are zero (T's come from TH)
+    if (wave < 2) {
+      const half4v z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+      const int I0 = 2 * wave, J0 = I0 + 1;
+      *reinterpret_cast<half4v*>(wsc + PK::matb / 2 + tri_pos(16 * I0 + l16, 16 * J0 + 4 * lg)) = z;
+    }
+    lds_barrier();
+    // fetch the next chunk's inputs only now, in flight during the solve, which keeps them out of
+    // the Gram stage's registers (measured faster)
+    if (blk + gstride < nblk) load_in(I, blk + gstride);
+    solve_t(AF, TH, tid);
     if (blk + gstride >= nblk) write_t(cr.pkt);  // this workgroup's last chunk
+    prev = cr.pkt;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Prep with a per-channel decay or separate erase/write gates (KDA, Gated DeltaNet-2 /
+// FG2-GDN+, FG2's rate with a per-channel decay).  Persistent like the scalar prep; two
+// workgroups per compute unit.
+//
+// Every factor e^{x} that scales a matrix operand has x <= 0 (apart from the bounded midpoint
+// split below), so fp16 operands stay in range for every decay in (0, 1]: a factor underflows
+// only where the term it scales is itself negligible.
+//  - The scan's tiles are referenced at the chunk start: K+ = k e^{g_t}, Q+ = q e^{g_t},
+//    K^end = k e^{g_C - g_t} (and U^end for separate gates), with the state unscaled.
+//  - The Gram matrices are built in 16-token blocks.  Block I's rows are referenced at the token
+//    before the block, x_t e^{gl_t} (gl: the in-block inclusive prefix of the log-decay); the
+//    columns of an earlier block J at the end of their own block, k_i e^{D_J - gl_i} (D_J: the
+//    block's total), times the decay of the blocks strictly between them, e^{D_{J+1} + ...},
+//    applied to the column fragment.
+//  - A diagonal block is split at its log-midpoint, rows x_t e^{gl_t - D/2} and columns
+//    k_i e^{D/2 - gl_i}, when its total decay is at most 12 on every channel (factors within
+//    e^{+-6}) and its inputs are moderate; otherwise by levels: the pairs of the two halves of
+//    16-, 8-, 4- and 2-token segments, each split at the boundary of its halves (factors <= 1),
+//    plus the diagonal t = i with the plain operands.
+//
+// Lanes hold one token each: lane 16 lg + l16 of wave w holds token 16 w + l16 of the chunk and
+// its channels 32 ks + 8 lg + j (ks, j = 0..3, 0..7), exactly the operand fragment layout of
+// v_mfma_f32_16x16x32_f16, so the diagonal block of wave w is formed and multiplied in
+// registers; the off-diagonal blocks read row and column operands written to LDS.
+// ------------------------------------------------------------------------------------------
+constexpr float kFastSpan = 12.f;  // largest per-channel log-decay of a block split at its midpoint
+constexpr float kFastMag = 80.f;   // largest |k|, |q|, |u| there: 80 e^6 < 32768
+
+// Inclusive prefix sum over the 16 lanes of each row (DPP row shifts; lanes without a source
+// add zero).
+template <int N>
+__device__ __forceinline__ float dpp_row_shr(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_prefix(float x) {
+  x += dpp_row_shr<1>(x);
+  x += dpp_row_shr<2>(x);
+  x += dpp_row_shr<4>(x);
+  x += dpp_row_shr<8>(x);
+  return x;
+}
+
+// The value of lane (l & ~(S - 1)) | (S / 2 - 1) of each 16-lane row: the last token of the
+// first half of this lane's S-token segment (ds_swizzle bit mode within 32 lanes).
+template <int S>
+__device__ __forceinline__ float seg_ref(float x) {
+  constexpr int pattern = (0x10 | (0xf & ~(S - 1))) | ((S / 2 - 1) << 5);
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), pattern));
+}
+
+template <bool DCH, bool GEN, bool FG2>
+__global__ __launch_bounds__(kThreads, 2) void chunk_prep_ch_kernel(Problem p, char* __restrict__ ws, int nchunks,
+                                                                    int64_t nblk) {
+  static_assert(DCH || GEN, "a per-head decay with one per-head gate runs chunk_prep_scalar_kernel");
+  static_assert(!(FG2 && GEN), "the per-channel rate keeps the symmetric gates");
+  if (p.chunks) nblk = int64_t(p.H) * *p.nchunks_total;
+  using PK = Packet<DCH, GEN, FG2>;
+  constexpr int NG = DCH ? 32 : 1;  // log-decays per lane
+  // Gram products (row operand, column operand): 0 (k, k), 1 (q, k), 2 (k, u), 3 (q, u).  The
+  // solve takes beta_t A_kk (symmetric gates) or A_ku; the packet holds A_qk (and A_kk, A_qu).
+  constexpr int NP = GEN ? 4 : 2;
+  constexpr int kSolveProd = GEN ? 2 : 0;
+
+  __shared__ __attribute__((aligned(16))) _Float16 KR[C * D];          // row operands k e^{gl}
+  __shared__ __attribute__((aligned(16))) float QRAF[C * AFS];         // row operands q e^{gl}, then AF
+  __shared__ __attribute__((aligned(16))) _Float16 KC[48 * D];         // column operands k e^{D - gl}
+  __shared__ __attribute__((aligned(16))) _Float16 UC[GEN ? 48 * D : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 TH[C * CS];
+  __shared__ __attribute__((aligned(16))) float GSC[4 * D];            // block totals D_w
+  __shared__ __attribute__((aligned(16))) float TW[4 * 3 * D];         // e^{g_b}, e^{g_C - g_e}, e^{-D/2}
+  __shared__ __attribute__((aligned(16))) _Float16 FT[3 * D];          // e^{D_1}, e^{D_2}, e^{D_1 + D_2}
+  __shared__ float GB[C];
+  static_assert(C * D * 2 <= C * AFS * 4, "the solve matrix takes the place of the q row operands");
+  _Float16* const QR = reinterpret_cast<_Float16*>(QRAF);
+  float* const AF = QRAF;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
+  const int tl = 16 * w + l16;  // this lane's token in the chunk
+  const int H = p.H;
+  const gptr<const uint16_t> kin = opaque_gptr(static_cast<const uint16_t*>(p.k));
+  const gptr<const uint16_t> qin = opaque_gptr(static_cast<const uint16_t*>(p.q));
+  const gptr<const float> ldin = opaque_gptr(p.log_decay);
+  const gptr<const float> erin = opaque_gptr(p.erase);
+  const bool erase_ch = GEN && p.erase_channel;
+  // register c = 8 ks + j holds channel 32 ks + 8 lg + j
+
+  auto write_t = [&](int64_t pkt) { write_tri_t(ws + pkt * PK::bytes + PK::mat, TH, tid); };
+
+  for (int64_t blk = blockIdx.x, prev = -1; blk < nblk; blk += gridDim.x) {
+    const ChunkRef cr = chunk_ref_of(p, blk, nchunks);
+    char* pk = ws + cr.pkt * PK::bytes;
+    _Float16* wsc = reinterpret_cast<_Float16*>(pk + PK::mat);
+    float* gv = reinterpret_cast<float*>(pk + PK::gate);
+    const bool ok = tl < cr.tlen;
+    // tokens past the end load token T - 1 and are zeroed here
+    const int64_t ti = (cr.tok0 + (ok ? tl : cr.tlen - 1)) * H + cr.h;
+
+    // ---- inputs ------------------------------------------------------------------------
+    // k and q stay packed (bf16; FG2: k~ as fp16) and are widened where they are used
+    uint4 kr[4], qr[4];
+    float gl[NG], ef[GEN ? 32 : 1], bt = 0.f;
+    bool bad = false;  // this lane's part of the diagonal block's range check
+    {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        kr[ks] = gload_u4(kin, ti * D + 32 * ks + 8 * lg);
+        qr[ks] = gload_u4(qin, ti * D + 32 * ks + 8 * lg);
+      }
+      if constexpr (DCH) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int64_t base = ti * D + 32 * ks + 8 * lg;
+          unpack8(gload_f4(ldin, base), gload_f4(ldin, base + 4), gl + 8 * ks);
+        }
+      } else {
+        gl[0] = ldin[ti];
+      }
+      if constexpr (GEN) {
+        if (erase_ch) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const int64_t base = ti * D + 32 * ks + 8 * lg;
+            unpack8(gload_f4(erin, base), gload_f4(erin, base + 4), ef + 8 * ks);
+          }
+        } else {
+          const float e1 = erin[ti];
+#pragma unroll
+          for (int c = 0; c < 32; ++c) ef[c] = e1;
+        }
+      } else if constexpr (!FG2) {
+        bt = erin[ti];
+      } else {
+        bt = 1.f;
+      }
+      float rt[FG2 ? 32 : 1];
+      uint4 vr[FG2 ? 4 : 1];
+      if constexpr (FG2) {
+        const gptr<const uint16_t> vin = opaque_gptr(static_cast<const uint16_t*>(p.v));
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int64_t base = ti * D + 32 * ks + 8 * lg;
+          unpack8(gload_f4(erin, base), gload_f4(erin, base + 4), rt + 8 * ks);
+          vr[ks] = gload_u4(vin, base);
+        }
+      }
+      const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        kr[ks] = ok ? kr[ks] : z;
+        qr[ks] = ok ? qr[ks] : z;
+      }
+      if constexpr (GEN) {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) ef[c] = ok ? ef[c] : 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < NG; ++c) gl[c] = ok ? gl[c] : 0.f;
+      bt = ok ? bt : 0.f;
+      // inputs the midpoint split takes: |k|, |q| <= kFastMag and erase gates within [0, 1]
+      // (FG2: the rates within [0, 1], so that |k~| <= |k|)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        float kf[8], qf[8];
+        bf16x8_to_f32(kr[ks], kf);
+        bf16x8_to_f32(qr[ks], qf);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          bad |= !(fabsf(kf[j]) <= kFastMag) || !(fabsf(qf[j]) <= kFastMag);
+          if constexpr (GEN) bad |= !(fabsf(ef[8 * ks + j]) <= 1.f);
+          if constexpr (FG2) bad |= !(rt[8 * ks + j] >= 0.f && rt[8 * ks + j] <= 1.f);
+        }
+      }
+      // FG2: k~ = sqrt(beta) k replaces k (fp16 from here on); v~ = sqrt(beta) v goes straight
+      // to the packet
+      if constexpr (FG2) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          float kf[8], vf[8];
+          bf16x8_to_f32(kr[ks], kf);
+          bf16x8_to_f32(vr[ks], vf);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float s = ok ? sqrtf(rt[8 * ks + j]) : 0.f;
+            kf[j] *= s;
+            vf[j] *= s;
+          }
+          kr[ks] = __builtin_bit_cast(uint4, cvt8(kf));
+          *reinterpret_cast<half8*>(pk + PK::vt + 2 * (tl * D + 32 * ks + 8 * lg)) = cvt8(vf);
+        }
+      }
+    }
+    // channels 32 ks + 8 lg + 0..7 of k and q, widened
+    auto kval = [&](int ks, float* f) {
+      if constexpr (FG2) {
+        const half8 h = __builtin_bit_cast(half8, kr[ks]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = float(h[j]);
+      } else {
+        bf16x8_to_f32(kr[ks], f);
+      }
+    };
+    auto qval = [&](int ks, float* f) { bf16x8_to_f32(qr[ks], f); };
+    // eight floats of an LDS table at channel 32 ks + 8 lg
+    auto lds8 = [&](const float* base, int ks, float* f) {
+      unpack8(*reinterpret_cast<const float4*>(base + 32 * ks + 8 * lg),
+              *reinterpret_cast<const float4*>(base + 32 * ks + 8 * lg + 4), f);
+    };
+
+    // ---- in-block prefix sums, block totals --------------------------------------------
+#pragma unroll
+    for (int c = 0; c < NG; ++c) gl[c] = row_prefix(gl[c]);
+    if (l16 == 15) {
+      if constexpr (DCH) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          *reinterpret_cast<float4*>(GSC + w * D + 32 * ks + 8 * lg) =
+              make_float4(gl[8 * ks], gl[8 * ks + 1], gl[8 * ks + 2], gl[8 * ks + 3]);
+          *reinterpret_cast<float4*>(GSC + w * D + 32 * ks + 8 * lg + 4) =
+              make_float4(gl[8 * ks + 4], gl[8 * ks + 5], gl[8 * ks + 6], gl[8 * ks + 7]);
+        }
+      } else if (lg == 0) {
+        GSC[w * D] = gl[0];
+      }
+    }
+    if (lg == 0) GB[tl] = bt;
+    if (prev >= 0) write_t(prev);  // the previous chunk's T, still in TH
+    lds_barrier();
+
+    // ---- per-block factors, gate vector ------------------------------------------------
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int d = lane + 64 * i, dd = DCH ? d : 0;
+      const float D0 = GSC[dd], D1 = GSC[D + dd], D2 = GSC[2 * D + dd], D3 = GSC[3 * D + dd];
+      const float Dw = w == 0 ? D0 : w == 1 ? D1 : w == 2 ? D2 : D3;
+      const float after = (w < 1 ? D1 : 0.f) + (w < 2 ? D2 : 0.f) + (w < 3 ? D3 : 0.f);
+      const float before = (w > 0 ? D0 : 0.f) + (w > 1 ? D1 : 0.f) + (w > 2 ? D2 : 0.f);
+      TW[(3 * w + 0) * D + d] = __expf(before);
+      TW[(3 * w + 1) * D + d] = __expf(after);
+      TW[(3 * w + 2) * D + d] = __expf(-0.5f * Dw);
+      if (w == 0) {
+        FT[d] = (_Float16)__expf(D1);
+        FT[D + d] = (_Float16)__expf(D2);
+        FT[2 * D + d] = (_Float16)__expf(D1 + D2);
+      } else if (w == 1) {
+        gv[GV_EM + d] = 1.f;
+        gv[GV_FC + d] = __expf(D0 + D1 + D2 + D3);
+        gv[GV_FCM + d] = 1.f;
+      } else if (w == 2 && i == 0) {
+        gv[GV_BETA + lane] = GB[lane];
+      }
+    }
+    for (int i = tid; i < C * CS; i += kThreads) TH[i] = (_Float16)0.f;
+    // (the wave reads back only table rows its own lanes wrote above)
+    const float* Dwt = GSC + w * D;  // this wave's block total per channel
+    const float* TB = TW + 3 * w * D;      // e^{g before the block}
+    const float* TA = TW + (3 * w + 1) * D;  // e^{g_C - g at the block's end}
+    const float* TM = TW + (3 * w + 2) * D;  // e^{-D/2}
+
+    // The diagonal block takes the midpoint split when every channel's block decay is at most
+    // kFastSpan and the inputs are moderate (checked as they load); NaN takes the level split
+    // and propagates.
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if constexpr (DCH) {
+        float dw[8];
+        lds8(Dwt, ks, dw);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bad |= !(dw[j] >= -kFastSpan);
+      } else {
+        bad |= !(Dwt[0] >= -kFastSpan);
+      }
+    }
+    const bool fast = __ballot(bad) == 0;
+
+    // ---- operand tiles: scan tiles to the packet, Gram operands to LDS, diagonal block ----
+    f32x4 dacc[NP];
+#pragma unroll
+    for (int n = 0; n < NP; ++n) dacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float kf[8], qf[8], dw[8], tb[8], ta[8], tm[8];
+      kval(ks, kf);
+      qval(ks, qf);
+      if constexpr (DCH) {
+        lds8(Dwt, ks, dw);
+        lds8(TB, ks, tb);
+        lds8(TA, ks, ta);
+        lds8(TM, ks, tm);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          dw[j] = Dwt[0];
+          tb[j] = TB[0];
+          ta[j] = TA[0];
+          tm[j] = TM[0];
+        }
+      }
+      float kp8[8], qp8[8], ke8[8], ue8[8], kr8[8], qr8[8], kc8[8], uc8[8];
+      float rk8[8], rq8[8], ck8[8], cu8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float g = gl[DCH ? 8 * ks + j : 0];
+        const float eg = __expf(g), edg = __expf(dw[j] - g);  // both <= 1
+        const float u = GEN ? ef[GEN ? 8 * ks + j : 0] * kf[j] : 0.f;
+        const float ep = eg * tb[j], ee = edg * ta[j];         // e^{g_t}, e^{g_C - g_t}
+        kp8[j] = kf[j] * ep;
+        qp8[j] = qf[j] * ep;
+        ke8[j] = kf[j] * ee;
+        ue8[j] = u * ee;
+        kr8[j] = kf[j] * eg;
+        qr8[j] = qf[j] * eg;
+        kc8[j] = kf[j] * edg;
+        uc8[j] = u * edg;
+        rk8[j] = kr8[j] * tm[j];
+        rq8[j] = qr8[j] * tm[j];
+        ck8[j] = kc8[j] * tm[j];
+        cu8[j] = uc8[j] * tm[j];
+      }
+      const int po = 2 * swz<16>(tl, 32 * ks + 8 * lg);  // byte offset in a packet tile
+      *reinterpret_cast<half8*>(pk + PK::kp + po) = cvt8(kp8);
+      *reinterpret_cast<half8*>(pk + PK::qp + po) = cvt8(qp8);
+      *reinterpret_cast<half8*>(pk + PK::kmt + po) = cvt8(ke8);
+      if constexpr (GEN) *reinterpret_cast<half8*>(pk + PK::umt + po) = cvt8(ue8);
+      const int lo = swz<16>(tl, 32 * ks + 8 * lg);  // half offset in an LDS tile
+      *reinterpret_cast<half8*>(KR + lo) = cvt8(kr8);
+      *reinterpret_cast<half8*>(QR + lo) = cvt8(qr8);
+      if (w < 3) {
+        *reinterpret_cast<half8*>(KC + lo) = cvt8(kc8);
+        if constexpr (GEN) *reinterpret_cast<half8*>(UC + lo) = cvt8(uc8);
+      }
+      if (fast) {
+        // lane: A[row = i (this token)][k = 8 lg + j] and B[k][col = t (this token)]
+        const half8 rk = cvt8(rk8), rq = cvt8(rq8), ck = cvt8(ck8);
+        dacc[0] = mfma16x16x32(ck, rk, dacc[0]);
+        dacc[1] = mfma16x16x32(ck, rq, dacc[1]);
+        if constexpr (GEN) {
+          const half8 cu = cvt8(cu8);
+          dacc[2] = mfma16x16x32(cu, rk, dacc[2]);
+          dacc[3] = mfma16x16x32(cu, rq, dacc[3]);
+        }
+      }
+    }
+    // lane (lg, l16) holds the diagonal block's A[t = l16][i = 4 lg + r] (block-local)
+    if (!fast) {
+      auto level = [&](auto seg) {
+        constexpr int S = decltype(seg)::value;
+        const bool is_row = (l16 & (S - 1)) >= S / 2;
+        f32x4 lacc[NP];
+#pragma unroll
+        for (int n = 0; n < NP; ++n) lacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          float kf[8], qf[8], rk8[8], rq8[8], ck8[8], cu8[8];
+          kval(ks, kf);
+          qval(ks, qf);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float g = gl[DCH ? 8 * ks + j : 0];
+            const float gr = seg_ref<S>(g);
+            const float f = __expf(is_row ? g - gr : gr - g);  // <= 1
+            const float kx = kf[j] * f;
+            rk8[j] = is_row ? kx : 0.f;
+            rq8[j] = is_row ? qf[j] * f : 0.f;
+            ck8[j] = is_row ? 0.f : kx;
+            cu8[j] = (is_row || !GEN) ? 0.f : ef[GEN ? 8 * ks + j : 0] * kx;
+          }
+          const half8 rk = cvt8(rk8), rq = cvt8(rq8), ck = cvt8(ck8);
+          lacc[0] = mfma16x16x32(ck, rk, lacc[0]);
+          lacc[1] = mfma16x16x32(ck, rq, lacc[1]);
+          if constexpr (GEN) {
+            const half8 cu = cvt8(cu8);
+            lacc[2] = mfma16x16x32(cu, rk, lacc[2]);
+            lacc[3] = mfma16x16x32(cu, rq, lacc[3]);
+          }
+        }
+        // keep the pairs of one segment (rows and columns of other segments meet here too)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool same = (l16 / S) == ((4 * lg + r) / S);
+#pragma unroll
+          for (int n = 0; n < NP; ++n) dacc[n][r] += same ? lacc[n][r] : 0.f;
+        }
+      };
+      // (one level at a time: interleaved, their operands would not fit in registers)
+      level(IntTag<16>());
+      __builtin_amdgcn_sched_barrier(0);
+      level(IntTag<8>());
+      __builtin_amdgcn_sched_barrier(0);
+      level(IntTag<4>());
+      __builtin_amdgcn_sched_barrier(0);
+      level(IntTag<2>());
+      __builtin_amdgcn_sched_barrier(0);
+      // the diagonal t = i with the plain operands
+      f32x4 lacc[NP];
+#pragma unroll
+      for (int n = 0; n < NP; ++n) lacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        float kf[8], qf[8], u8[8];
+        kval(ks, kf);
+        qval(ks, qf);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) u8[j] = GEN ? ef[GEN ? 8 * ks + j : 0] * kf[j] : 0.f;
+        const half8 hk = cvt8(kf), hq = cvt8(qf);
+        lacc[0] = mfma16x16x32(hk, hk, lacc[0]);
+        lacc[1] = mfma16x16x32(hk, hq, lacc[1]);
+        if constexpr (GEN) {
+          const half8 hu = cvt8(u8);
+          lacc[2] = mfma16x16x32(hu, hk, lacc[2]);
+          lacc[3] = mfma16x16x32(hu, hq, lacc[3]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int n = 0; n < NP; ++n) dacc[n][r] += (l16 == 4 * lg + r) ? lacc[n][r] : 0.f;
+    }
+    lds_barrier();  // row and column operands, FT, TH cleared
+
+    // ---- Gram tiles ----------------------------------------------------------------------
+    // Off-diagonal tile n = 0..5: (I, J) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2), transposed:
+    // lane gets A[t = 16 I + l16][i = 16 J + 4 lg + r].
+    auto off_tile = [&](int n, int prod) {
+      const int I = n < 1 ? 1 : n < 3 ? 2 : 3;
+      const int J = n - (I * (I - 1)) / 2;
+      const _Float16* rowb = (prod & 1) ? QR : KR;
+      const _Float16* colb = (prod & 2) ? UC : KC;
+      const int fi = (I == 2 && J == 0) ? 0 : (I == 3 && J == 1) ? 1 : 2;  // e^{D between}
+      const bool far = J < I - 1;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        half8 a = frag_s<16>(colb, 16 * J, 32 * ks, lane);
+        if (far) a = a * *reinterpret_cast<const half8*>(FT + fi * D + 32 * ks + 8 * lg);
+        acc = mfma16x16x32(a, frag_s<16>(rowb, 16 * I, 32 * ks, lane), acc);
+      }
+      return acc;
+    };
+    // packet matrix of product n (1: A_qk, 2: A_kk, 3: A_qu); strict: A_kk
+    auto pkt_mat = [&](int prod) { return prod == 1 ? 1 : prod == 0 ? 2 : 3; };
+    auto store_pkt = [&](int prod, int t, int i0, f32x4 acc, bool diag) {
+      const bool strict = prod == 0;
+      half4v hv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hv[r] = (_Float16)((!diag || (strict ? i0 + r < t : i0 + r <= t)) ? acc[r] : 0.f);
+      *reinterpret_cast<half4v*>(wsc + pkt_mat(prod) * (PK::matb / 2) + tri_pos(t, i0)) = hv;
+    };
+    auto store_af = [&](int t, int i0, f32x4 acc, bool diag) {
+      const float sc = GEN ? 1.f : GB[t];
+      float4 v;
+      v.x = (!diag || i0 + 0 < t) ? sc * acc[0] : 0.f;
+      v.y = (!diag || i0 + 1 < t) ? sc * acc[1] : 0.f;
+      v.z = (!diag || i0 + 2 < t) ? sc * acc[2] : 0.f;
+      v.w = (!diag || i0 + 3 < t) ? sc * acc[3] : 0.f;
+      *reinterpret_cast<float4*>(AF + t * AFS + i0) = v;
+    };
+    // phase A: the packet's products (they read the q row operands, which the solve matrix
+    // overwrites in phase B)
+    {
+      constexpr int NA = GEN ? 18 : 6;  // (tile, product) pairs
+#pragma unroll
+      for (int m = 0; m < (NA + 3) / 4; ++m) {
+        const int x = w + 4 * m;
+        if (x < NA) {
+          const int n = x % 6, a = x / 6;
+          const int prod = GEN ? (a == 0 ? 0 : a == 1 ? 1 : 3) : 1;
+          const int I = n < 1 ? 1 : n < 3 ? 2 : 3;
+          const int J = n - (I * (I - 1)) / 2;
+          store_pkt(prod, 16 * I + l16, 16 * J + 4 * lg, off_tile(n, prod), false);
+        }
+      }
+      const int t = tl, i0 = 16 * w + 4 * lg;
+      store_pkt(1, t, i0, dacc[1], true);
+      if constexpr (GEN) {
+        store_pkt(0, t, i0, dacc[0], true);
+        store_pkt(3, t, i0, dacc[3], true);
+      }
+      // the upper-triangular 16 x 16 tiles (0,1) and (2,3) of the packet matrices after T share
+      // a stored block with nonzeros and are zero
+      for (int n = w; n < 2 * (PK::nmat - 1); n += 4) {
+        const half4v z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+        const int m = 1 + n / 2, I0 = 2 * (n % 2), J0 = I0 + 1;
+        *reinterpret_cast<half4v*>(wsc + m * (PK::matb / 2) + tri_pos(16 * I0 + l16, 16 * J0 + 4 * lg)) = z;
+      }
+    }
+    lds_barrier();
+    // phase B: the solve matrix, fp32, over the q row operands
+    {
+      for (int n = w; n < 6; n += 4) {
+        const int I = n < 1 ? 1 : n < 3 ? 2 : 3;
+        const int J = n - (I * (I - 1)) / 2;
+        store_af(16 * I + l16, 16 * J + 4 * lg, off_tile(n, kSolveProd), false);
+      }
+      store_af(tl, 16 * w + 4 * lg, dacc[kSolveProd], true);
+    }
+    lds_barrier();
+    solve_t(AF, TH, tid);
+    if (blk + gridDim.x >= nblk) write_t(cr.pkt);  // this workgroup's last chunk
     prev = cr.pkt;
   }
 }
@@ -754,16 +1082,34 @@ __global__ __launch_bounds__(kThreads, (DCH || GEN) ? 2 : 1) void chunk_prep_ker
 constexpr int kScanWaves = 8;
 constexpr int kScanThreads = 64 * kScanWaves;
 
-// Fragment (as frag()) of a swizzled tile with U 16-byte units per row.
-template <int U>
-__device__ __forceinline__ half8 frag_s(const _Float16* base, int row0, int k0, int lane) {
-  return *reinterpret_cast<const half8*>(base + swz<U>(row0 + (lane & 15), k0 + 8 * (lane >> 4)));
-}
-
 // Fragment (as frag()) of rows 16 I .. + 15, columns 32 H .. + 31 of a lower-triangular matrix
 // held in LDS as eight 16 x 32 blocks (block 2 I + H, layout as tri_in).
 __device__ __forceinline__ half8 frag_tri(const _Float16* base, int I, int H, int lane) {
   return *reinterpret_cast<const half8*>(base + (2 * I + H) * 512 + tri_in(lane & 15, 8 * (lane >> 4)));
+}
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): lane 16 g + 4 a + b receives as element j
+// (0..3) the 16-bit element b of the 8 bytes at the address that lane 16 g + a + 4 j supplies.
+typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) fp16x4 lds_half4;
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4;
+__device__ __forceinline__ half4v ld_tr16(const _Float16* p) {
+  return __builtin_bit_cast(half4v, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_half4*)p));
+}
+__device__ __forceinline__ short4v ld_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
+}
+
+// frag_s of the transposed tile: A[row = d][k = t] = base[t][d] (base swizzled, 16 units per
+// row).  Lane 16 g + m supplies row t0 + 8 g + m / 4 (and 4 rows on), columns d0 + 4 (m % 4)
+// .. + 3, so lane 16 g + l16 receives base[t0 + 8 g + 0..7][d0 + l16].
+__device__ __forceinline__ half8 frag_ts(const _Float16* base, int d0, int t0, int lane) {
+  const int m = lane & 15;
+  const int t = t0 + 8 * (lane >> 4) + (m >> 2), d = d0 + 4 * (m & 3);
+  const half4v lo = ld_tr16(base + swz<16>(t, d));
+  const half4v hi = ld_tr16(base + swz<16>(t + 4, d));
+  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 // LDS layout of the register-staged scan (general gates).
@@ -774,8 +1120,8 @@ struct ScanLayout {
   // tri_pos), so units copy straight across and fragment reads are conflict-free.
   static constexpr int kp = 0;                 // K+       [64][128] half
   static constexpr int qp = kp + C * D * 2;    // Q+       [64][128]
-  static constexpr int kmt = qp + C * D * 2;   // K-^T     [128][64]
-  static constexpr int umt = kmt + D * C * 2;  // U-^T     [128][64]
+  static constexpr int kmt = qp + C * D * 2;   // K^end    [64][128]
+  static constexpr int umt = kmt + D * C * 2;  // U^end    [64][128]
   static constexpr int st = umt + D * C * 2;   // S~^T     [DVS][128]
   // the four lower-triangular matrices: eight 16 x 32 blocks each (see tri_pos), contiguous
   static constexpr int th = st + DVS * D * 2;  // T        [64][64]
@@ -834,7 +1180,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   constexpr int NM = PK::nmat;
   constexpr int NCT = DVS / 16;   // 16-column tiles of the value slice
   constexpr int VPT = DVS / 8;    // value columns per thread in the V load
-  constexpr int NTU = 8;  // 16-byte operand-tile units per thread (K+, Q+, K-^T, U-^T)
+  constexpr int NTU = 8;  // 16-byte operand-tile units per thread (K+, Q+, K^end, U^end)
   constexpr int PF = 1;   // chunks of prefetch in flight
   __shared__ __attribute__((aligned(16))) char smem[L::total];
   _Float16* KP = reinterpret_cast<_Float16*>(smem + L::kp);
@@ -896,8 +1242,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
 
   struct Pref {
     uint4 mr[NM * 3 / 4];     // this thread's units of the stored blocks of T, A_qk, A_kk, A_qu
-    uint4 tl[NTU];            // K+, Q+, K-^T, U-^T units
-    float4 sc[3];             // per-channel e^{gm}, e^{gC}, e^{gC-gm} of this thread's 4 rows
+    uint4 tl[NTU];            // K+, Q+, K^end, U^end units
+    float4 sc[3];             // per-channel state factors (1, e^{g_C}, 1) of this thread's 4 rows
     VSlice<DVS> vr;
     float wr[GEN ? VPT : 1];  // write gates of the value slice (per channel) or of token vtok
   };
@@ -983,7 +1329,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
         VT[swz<8>(vcol + i, vtok)] = (_Float16)(w * vf[i]);
       }
     }
-    // S~^T = (Diag(e^{gm}) S)^T; the end-of-chunk factors of this wave's rows stay in registers.
+    // S~^T = (Diag(em) S)^T (em = 1: the tiles are referenced at the chunk start); the end-of-chunk
+    // factors of this wave's rows stay in registers.
     float fC[4], fCm[4];
     {
       float em[4];
@@ -1118,8 +1465,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
       half8 ak[2], au[2], bv[NCT][2], bd[NCT][2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        ak[ks] = frag_s<8>(KMT, 16 * wave, 32 * ks, lane);
-        au[ks] = frag_s<8>(UMT, 16 * wave, 32 * ks, lane);
+        ak[ks] = frag_ts(KMT, 16 * wave, 32 * ks, lane);
+        au[ks] = frag_ts(UMT, 16 * wave, 32 * ks, lane);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           bv[ct][ks] = frag_s<8>(VT, 16 * ct, 32 * ks, lane);
@@ -1173,30 +1520,6 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
 // LDS by the load-to-LDS path (no registers, no VALU) into the second of two buffer sets while
 // chunk c is computed from the first; each chunk starts with one wait for its own copies.
 // ------------------------------------------------------------------------------------------
-// gfx950 transposing LDS read (ds_read_b64_tr_b16): lane 16 g + 4 a + b receives as element j
-// (0..3) the 16-bit element b of the 8 bytes at the address that lane 16 g + a + 4 j supplies.
-typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
-typedef __attribute__((address_space(3))) fp16x4 lds_half4;
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) short4v lds_short4;
-__device__ __forceinline__ half4v ld_tr16(const _Float16* p) {
-  return __builtin_bit_cast(half4v, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_half4*)p));
-}
-__device__ __forceinline__ short4v ld_tr16(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
-}
-
-// frag_s of the transposed tile: A[row = d][k = t] = base[t][d] (base swizzled, 16 units per
-// row).  Lane 16 g + m supplies row t0 + 8 g + m / 4 (and 4 rows on), columns d0 + 4 (m % 4)
-// .. + 3, so lane 16 g + l16 receives base[t0 + 8 g + 0..7][d0 + l16].
-__device__ __forceinline__ half8 frag_ts(const _Float16* base, int d0, int t0, int lane) {
-  const int m = lane & 15;
-  const int t = t0 + 8 * (lane >> 4) + (m >> 2), d = d0 + 4 * (m & 3);
-  const half4v lo = ld_tr16(base + swz<16>(t, d));
-  const half4v hi = ld_tr16(base + swz<16>(t + 4, d));
-  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
 // FG2: the values are FG2's v~ = sqrt(beta) v, fp16 in the packet, instead of the bf16 input.
 template <bool DCH, int DVS, bool FG2 = false>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p, const char* __restrict__ ws) {
@@ -1209,7 +1532,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   // tracks copies into LDS per array, so reading one array never waits for the copies into
   // another.  Batch 1a (bytes): K+ (scalar decay: k) [64][128]; batch 1b: Q+ (q) [64][128],
   // gate vector [ngate] f32, v slice [64][DVS] (bf16); batch 2: T [64][64], A_qk [64][64]
-  // (eight 16 x 32 blocks each, see tri_pos); batch 3: K-^T [128][64] (per-channel decay).
+  // (eight 16 x 32 blocks each, see tri_pos); batch 3: K^end [64][128] (per-channel decay).
   constexpr int b1a_bytes = C * D * 2;
   constexpr int o_qp = 0, o_gv = o_qp + C * D * 2;
   constexpr int o_vs = o_gv + PK::ngate * 4, b1_bytes = o_vs + C * DVS * 2;
@@ -1228,7 +1551,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   __shared__ __attribute__((aligned(16))) _Float16 ST[DVS * D];  // S~^T
   __shared__ __attribute__((aligned(16))) _Float16 RT[DVS * C];  // R^T
   __shared__ __attribute__((aligned(16))) _Float16 DT[DVS * C];  // delta^T
-  __shared__ __attribute__((aligned(16))) _Float16 DT2[SCAL ? DVS * C : 8];  // (Diag(e^{gm-g}) delta)^T
+  __shared__ __attribute__((aligned(16))) _Float16 DT2[SCAL ? DVS * C : 8];  // (Diag(e^{g_C - g}) delta)^T
 
   // Buffer set 0 or 1 (a compile-time choice, so that every access names its array).
   struct Set {
@@ -1316,7 +1639,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   };
   // Issued in three batches, each as early as its buffers are free and each waited for just
   // before its first reader: (1) key/query tiles, gate vector, values and factors, read from
-  // the start of the chunk; (2) T and A_qk, read from the D stage on; (3) K-^T (per-channel
+  // the start of the chunk; (2) T and A_qk, read from the D stage on; (3) K^end (per-channel
   // decay), read by the state update.  Every wave issues the same number of loads in each
   // batch that a wait has to look past (past the last chunk the copies repeat the last chunk
   // into the idle set), so the number of loads a wave issues after each batch is known and a
@@ -1456,7 +1779,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       fC[r] = F.fc[SCAL ? 0 : r];
       fCm[r] = F.fcm[SCAL ? 0 : r];
     }
-    // S~^T = (Diag(e^{gm}) S)^T
+    // S~^T = (Diag(em) S)^T, em = 1 (chunk-start reference)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       half4v hv;
@@ -1612,7 +1935,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       for (int r = 0; r < 4; ++r) hv[r] = (_Float16)acc[r];
       *reinterpret_cast<half4v*>(DT + swz<8>(16 * ct + l16, 16 * i + 4 * lg)) = hv;
       if constexpr (SCAL) {
-        // K-^T delta = k^T (Diag(e^{gm - g}) delta): the state update takes the scaled copy
+        // K^end^T delta = k^T (Diag(e^{g_C - g}) delta): the state update takes the scaled copy
         const float4 fm = *reinterpret_cast<const float4*>(X.gv + GV_FM + 16 * i + 4 * lg);
         hv[0] = (_Float16)(acc[0] * fm.x);
         hv[1] = (_Float16)(acc[1] * fm.y);
@@ -1654,7 +1977,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
       half8 ak[2], dk[NCT][2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        ak[ks] = SCAL ? frag_ts(X.kp, 16 * wave, 32 * ks, lane) : frag_s<8>(X.km, 16 * wave, 32 * ks, lane);
+        ak[ks] = frag_ts(SCAL ? X.kp : X.km, 16 * wave, 32 * ks, lane);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) dk[ct][ks] = frag_s<8>(SCAL ? DT2 : DT, 16 * ct, 32 * ks, lane);
       }
@@ -1745,8 +2068,12 @@ hipError_t launch_variant(const Problem& p, void* workspace, hipStream_t stream)
     return hipErrorInvalidDevice;
   const int64_t resident = int64_t(ncu) * 2;
   const int64_t grid = nblk < resident ? nblk : resident;
-  hipLaunchKernelGGL((chunk_prep_kernel<DCH, GEN, FG2>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p, ws, nchunks,
-                     nblk);
+  if constexpr (!DCH && !GEN)
+    hipLaunchKernelGGL((chunk_prep_scalar_kernel<FG2>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p, ws, nchunks,
+                       nblk);
+  else
+    hipLaunchKernelGGL((chunk_prep_ch_kernel<DCH, GEN, FG2>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p, ws,
+                       nchunks, nblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Fill the 256 compute units with (b, h, value-slice) workgroups while keeping the slices
