@@ -95,6 +95,11 @@ __device__ __forceinline__ void bf16x8_to_f32(uint4 u, float* f) {
   f[6] = __uint_as_float(u.w << 16); f[7] = __uint_as_float(u.w & 0xffff0000u);
 }
 
+// v when ok, else zero
+__device__ __forceinline__ uint4 mask4(bool ok, uint4 v) {
+  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+
 __device__ __forceinline__ void unpack8(float4 a, float4 b, float* f) {
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
@@ -643,7 +648,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_ch_kernel(Problem p, c
   __shared__ __attribute__((aligned(16))) _Float16 TH[C * CS];
   __shared__ __attribute__((aligned(16))) float GSC[4 * D];            // block totals D_w
   __shared__ __attribute__((aligned(16))) float TW[4 * 3 * D];         // e^{g_b}, e^{g_C - g_e}, e^{-D/2}
-  __shared__ __attribute__((aligned(16))) _Float16 FT[3 * D];          // e^{D_1}, e^{D_2}, e^{D_1 + D_2}
+  __shared__ __attribute__((aligned(16))) _Float16 FT[4 * D];          // e^{D_1}, e^{D_2}, e^{D_1 + D_2}, 1
   __shared__ float GB[C];
   static_assert(C * D * 2 <= C * AFS * 4, "the solve matrix takes the place of the q row operands");
   _Float16* const QR = reinterpret_cast<_Float16*>(QRAF);
@@ -655,114 +660,101 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_ch_kernel(Problem p, c
   const int H = p.H;
   const gptr<const uint16_t> kin = opaque_gptr(static_cast<const uint16_t*>(p.k));
   const gptr<const uint16_t> qin = opaque_gptr(static_cast<const uint16_t*>(p.q));
+  const gptr<const uint16_t> vin = opaque_gptr(static_cast<const uint16_t*>(p.v));
   const gptr<const float> ldin = opaque_gptr(p.log_decay);
   const gptr<const float> erin = opaque_gptr(p.erase);
   const bool erase_ch = GEN && p.erase_channel;
-  // register c = 8 ks + j holds channel 32 ks + 8 lg + j
+
+  // One chunk's inputs for this lane's token (register c = 8 ks + j holds channel
+  // 32 ks + 8 lg + j).  Tokens past the end load token T - 1 (zeroed where they are used), so
+  // every load is unconditional.  No chunk is kept in flight: its registers would spill, and the
+  // second resident workgroup covers the load latency (measured: prefetching the next chunk
+  // during this chunk's Gram tiles and solve was 8-40% slower).
+  constexpr bool ECH = GEN;  // erase gates held per channel (a per-head gate is repeated)
+  struct In {
+    uint4 kr[4], qr[4];
+    float la[NG];
+    float er[ECH ? 32 : 1];
+    float bt;  // symmetric gates: the per-head erase/write gate
+    float rt[FG2 ? 32 : 1];
+    uint4 vr[FG2 ? 4 : 1];
+  };
+  auto load_in = [&](In& I, int64_t b) {
+    const ChunkRef cr = chunk_ref_of(p, b, nchunks);
+    const int64_t ti = (cr.tok0 + (tl < cr.tlen ? tl : cr.tlen - 1)) * H + cr.h;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int64_t base = ti * D + 32 * ks + 8 * lg;
+      I.kr[ks] = gload_u4(kin, base);
+      I.qr[ks] = gload_u4(qin, base);
+      if constexpr (DCH) unpack8(gload_f4(ldin, base), gload_f4(ldin, base + 4), I.la + 8 * ks);
+      if constexpr (FG2) {
+        unpack8(gload_f4(erin, base), gload_f4(erin, base + 4), I.rt + 8 * ks);
+        I.vr[ks] = gload_u4(vin, base);
+      }
+    }
+    if constexpr (!DCH) I.la[0] = ldin[ti];
+    if constexpr (GEN) {
+      if (erase_ch) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int64_t base = ti * D + 32 * ks + 8 * lg;
+          unpack8(gload_f4(erin, base), gload_f4(erin, base + 4), I.er + 8 * ks);
+        }
+      } else {
+        const float e1 = erin[ti];
+#pragma unroll
+        for (int c = 0; c < 32; ++c) I.er[c] = e1;
+      }
+    }
+    I.bt = (GEN || FG2) ? 1.f : erin[ti];
+  };
 
   auto write_t = [&](int64_t pkt) { write_tri_t(ws + pkt * PK::bytes + PK::mat, TH, tid); };
 
+  In I;
   for (int64_t blk = blockIdx.x, prev = -1; blk < nblk; blk += gridDim.x) {
     const ChunkRef cr = chunk_ref_of(p, blk, nchunks);
     char* pk = ws + cr.pkt * PK::bytes;
     _Float16* wsc = reinterpret_cast<_Float16*>(pk + PK::mat);
     float* gv = reinterpret_cast<float*>(pk + PK::gate);
     const bool ok = tl < cr.tlen;
-    // tokens past the end load token T - 1 and are zeroed here
-    const int64_t ti = (cr.tok0 + (ok ? tl : cr.tlen - 1)) * H + cr.h;
+    load_in(I, blk);
 
-    // ---- inputs ------------------------------------------------------------------------
-    // k and q stay packed (bf16; FG2: k~ as fp16) and are widened where they are used
+    // ---- this chunk's inputs, masked past the last token ---------------------------------
+    // k and q stay packed (bf16; FG2: k~ as fp16) and are widened where they are used.  (Vectors
+    // are selected component by component: a select of whole vectors becomes a select of their
+    // addresses in scratch memory.)
     uint4 kr[4], qr[4];
-    float gl[NG], ef[GEN ? 32 : 1], bt = 0.f;
-    bool bad = false;  // this lane's part of the diagonal block's range check
-    {
+    float gl[NG], ef[GEN ? 32 : 1];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      kr[ks] = mask4(ok, I.kr[ks]);
+      qr[ks] = mask4(ok, I.qr[ks]);
+    }
+#pragma unroll
+    for (int c = 0; c < NG; ++c) gl[c] = ok ? I.la[c] : 0.f;
+    if constexpr (GEN) {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) ef[c] = ok ? I.er[c] : 0.f;
+    }
+    const float bt = ok ? I.bt : 0.f;
+    // FG2: k~ = sqrt(beta) k replaces k (fp16 from here on); v~ = sqrt(beta) v goes straight to
+    // the packet
+    if constexpr (FG2) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        kr[ks] = gload_u4(kin, ti * D + 32 * ks + 8 * lg);
-        qr[ks] = gload_u4(qin, ti * D + 32 * ks + 8 * lg);
-      }
-      if constexpr (DCH) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int64_t base = ti * D + 32 * ks + 8 * lg;
-          unpack8(gload_f4(ldin, base), gload_f4(ldin, base + 4), gl + 8 * ks);
-        }
-      } else {
-        gl[0] = ldin[ti];
-      }
-      if constexpr (GEN) {
-        if (erase_ch) {
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const int64_t base = ti * D + 32 * ks + 8 * lg;
-            unpack8(gload_f4(erin, base), gload_f4(erin, base + 4), ef + 8 * ks);
-          }
-        } else {
-          const float e1 = erin[ti];
-#pragma unroll
-          for (int c = 0; c < 32; ++c) ef[c] = e1;
-        }
-      } else if constexpr (!FG2) {
-        bt = erin[ti];
-      } else {
-        bt = 1.f;
-      }
-      float rt[FG2 ? 32 : 1];
-      uint4 vr[FG2 ? 4 : 1];
-      if constexpr (FG2) {
-        const gptr<const uint16_t> vin = opaque_gptr(static_cast<const uint16_t*>(p.v));
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int64_t base = ti * D + 32 * ks + 8 * lg;
-          unpack8(gload_f4(erin, base), gload_f4(erin, base + 4), rt + 8 * ks);
-          vr[ks] = gload_u4(vin, base);
-        }
-      }
-      const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        kr[ks] = ok ? kr[ks] : z;
-        qr[ks] = ok ? qr[ks] : z;
-      }
-      if constexpr (GEN) {
-#pragma unroll
-        for (int c = 0; c < 32; ++c) ef[c] = ok ? ef[c] : 0.f;
-      }
-#pragma unroll
-      for (int c = 0; c < NG; ++c) gl[c] = ok ? gl[c] : 0.f;
-      bt = ok ? bt : 0.f;
-      // inputs the midpoint split takes: |k|, |q| <= kFastMag and erase gates within [0, 1]
-      // (FG2: the rates within [0, 1], so that |k~| <= |k|)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        float kf[8], qf[8];
+        float kf[8], vf[8];
         bf16x8_to_f32(kr[ks], kf);
-        bf16x8_to_f32(qr[ks], qf);
+        bf16x8_to_f32(I.vr[ks], vf);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          bad |= !(fabsf(kf[j]) <= kFastMag) || !(fabsf(qf[j]) <= kFastMag);
-          if constexpr (GEN) bad |= !(fabsf(ef[8 * ks + j]) <= 1.f);
-          if constexpr (FG2) bad |= !(rt[8 * ks + j] >= 0.f && rt[8 * ks + j] <= 1.f);
+          const float s = ok ? sqrtf(I.rt[8 * ks + j]) : 0.f;
+          kf[j] *= s;
+          vf[j] *= s;
         }
-      }
-      // FG2: k~ = sqrt(beta) k replaces k (fp16 from here on); v~ = sqrt(beta) v goes straight
-      // to the packet
-      if constexpr (FG2) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          float kf[8], vf[8];
-          bf16x8_to_f32(kr[ks], kf);
-          bf16x8_to_f32(vr[ks], vf);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float s = ok ? sqrtf(rt[8 * ks + j]) : 0.f;
-            kf[j] *= s;
-            vf[j] *= s;
-          }
-          kr[ks] = __builtin_bit_cast(uint4, cvt8(kf));
-          *reinterpret_cast<half8*>(pk + PK::vt + 2 * (tl * D + 32 * ks + 8 * lg)) = cvt8(vf);
-        }
+        kr[ks] = __builtin_bit_cast(uint4, cvt8(kf));
+        *reinterpret_cast<half8*>(pk + PK::vt + 2 * (tl * D + 32 * ks + 8 * lg)) = cvt8(vf);
       }
     }
     // channels 32 ks + 8 lg + 0..7 of k and q, widened
@@ -817,6 +809,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_ch_kernel(Problem p, c
         FT[d] = (_Float16)__expf(D1);
         FT[D + d] = (_Float16)__expf(D2);
         FT[2 * D + d] = (_Float16)__expf(D1 + D2);
+        FT[3 * D + d] = (_Float16)1.f;
       } else if (w == 1) {
         gv[GV_EM + d] = 1.f;
         gv[GV_FC + d] = __expf(D0 + D1 + D2 + D3);
@@ -827,34 +820,23 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_ch_kernel(Problem p, c
     }
     for (int i = tid; i < C * CS; i += kThreads) TH[i] = (_Float16)0.f;
     // (the wave reads back only table rows its own lanes wrote above)
-    const float* Dwt = GSC + w * D;  // this wave's block total per channel
-    const float* TB = TW + 3 * w * D;      // e^{g before the block}
-    const float* TA = TW + (3 * w + 1) * D;  // e^{g_C - g at the block's end}
-    const float* TM = TW + (3 * w + 2) * D;  // e^{-D/2}
+    const float* Dwt = GSC + w * D;            // this wave's block total per channel
+    const float* TB = TW + 3 * w * D;          // e^{g before the block}
+    const float* TA = TW + (3 * w + 1) * D;    // e^{g_C - g at the block's end}
+    const float* TM = TW + (3 * w + 2) * D;    // e^{-D/2}
 
-    // The diagonal block takes the midpoint split when every channel's block decay is at most
-    // kFastSpan and the inputs are moderate (checked as they load); NaN takes the level split
-    // and propagates.
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if constexpr (DCH) {
-        float dw[8];
-        lds8(Dwt, ks, dw);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) bad |= !(dw[j] >= -kFastSpan);
-      } else {
-        bad |= !(Dwt[0] >= -kFastSpan);
-      }
-    }
-    const bool fast = __ballot(bad) == 0;
-
-    // ---- operand tiles: scan tiles to the packet, Gram operands to LDS, diagonal block ----
+    // ---- operand tiles and the diagonal block, 32 channels at a time -----------------------
+    // The diagonal block's contraction over channels splits into independent 32-channel slices,
+    // so each slice takes the midpoint split when its block decay is at most kFastSpan on every
+    // channel and its inputs are moderate, and the level split otherwise (NaN takes the level
+    // split, and propagates).  Lane (lg, l16) accumulates the block's A[t = l16][i = 4 lg + r]
+    // (block-local) of each product.
     f32x4 dacc[NP];
 #pragma unroll
     for (int n = 0; n < NP; ++n) dacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      float kf[8], qf[8], dw[8], tb[8], ta[8], tm[8];
+      float kf[8], qf[8], uf[8], dw[8], tb[8], ta[8], tm[8];
       kval(ks, kf);
       qval(ks, qf);
       if constexpr (DCH) {
@@ -871,143 +853,125 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_ch_kernel(Problem p, c
           tm[j] = TM[0];
         }
       }
-      float kp8[8], qp8[8], ke8[8], ue8[8], kr8[8], qr8[8], kc8[8], uc8[8];
-      float rk8[8], rq8[8], ck8[8], cu8[8];
+      bool bad = false;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uf[j] = GEN ? ef[GEN ? 8 * ks + j : 0] * kf[j] : 0.f;
+        bad |= !(dw[j] >= -kFastSpan);
+        bad |= !(fabsf(kf[j]) <= kFastMag) || !(fabsf(qf[j]) <= kFastMag);
+        if constexpr (GEN) bad |= !(fabsf(uf[j]) <= kFastMag);
+      }
+      const bool fast = __ballot(bad) == 0;
+      float eg[8], edg[8];  // e^{gl} and e^{D - gl}, both <= 1
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float g = gl[DCH ? 8 * ks + j : 0];
-        const float eg = __expf(g), edg = __expf(dw[j] - g);  // both <= 1
-        const float u = GEN ? ef[GEN ? 8 * ks + j : 0] * kf[j] : 0.f;
-        const float ep = eg * tb[j], ee = edg * ta[j];         // e^{g_t}, e^{g_C - g_t}
-        kp8[j] = kf[j] * ep;
-        qp8[j] = qf[j] * ep;
-        ke8[j] = kf[j] * ee;
-        ue8[j] = u * ee;
-        kr8[j] = kf[j] * eg;
-        qr8[j] = qf[j] * eg;
-        kc8[j] = kf[j] * edg;
-        uc8[j] = u * edg;
-        rk8[j] = kr8[j] * tm[j];
-        rq8[j] = qr8[j] * tm[j];
-        ck8[j] = kc8[j] * tm[j];
-        cu8[j] = uc8[j] * tm[j];
+        eg[j] = __expf(g);
+        edg[j] = __expf(dw[j] - g);
       }
+      // each tile formed, converted and stored in turn (kept apart, the eight would not fit in
+      // registers): scan tiles k e^{g_t}, q e^{g_t}, k e^{g_C - g_t} (, u e^{g_C - g_t}) to the
+      // packet; Gram operands k e^{gl}, q e^{gl}, k e^{D - gl} (, u e^{D - gl}) to LDS
+      auto put = [&](auto&& f, void* dst) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = f(j);
+        *reinterpret_cast<half8*>(dst) = cvt8(x);
+      };
       const int po = 2 * swz<16>(tl, 32 * ks + 8 * lg);  // byte offset in a packet tile
-      *reinterpret_cast<half8*>(pk + PK::kp + po) = cvt8(kp8);
-      *reinterpret_cast<half8*>(pk + PK::qp + po) = cvt8(qp8);
-      *reinterpret_cast<half8*>(pk + PK::kmt + po) = cvt8(ke8);
-      if constexpr (GEN) *reinterpret_cast<half8*>(pk + PK::umt + po) = cvt8(ue8);
-      const int lo = swz<16>(tl, 32 * ks + 8 * lg);  // half offset in an LDS tile
-      *reinterpret_cast<half8*>(KR + lo) = cvt8(kr8);
-      *reinterpret_cast<half8*>(QR + lo) = cvt8(qr8);
+      const int lo = swz<16>(tl, 32 * ks + 8 * lg);      // half offset in an LDS tile
+      put([&](int j) { return kf[j] * (eg[j] * tb[j]); }, pk + PK::kp + po);
+      put([&](int j) { return qf[j] * (eg[j] * tb[j]); }, pk + PK::qp + po);
+      put([&](int j) { return kf[j] * (edg[j] * ta[j]); }, pk + PK::kmt + po);
+      if constexpr (GEN) put([&](int j) { return uf[j] * (edg[j] * ta[j]); }, pk + PK::umt + po);
+      put([&](int j) { return kf[j] * eg[j]; }, KR + lo);
+      put([&](int j) { return qf[j] * eg[j]; }, QR + lo);
       if (w < 3) {
-        *reinterpret_cast<half8*>(KC + lo) = cvt8(kc8);
-        if constexpr (GEN) *reinterpret_cast<half8*>(UC + lo) = cvt8(uc8);
+        put([&](int j) { return kf[j] * edg[j]; }, KC + lo);
+        if constexpr (GEN) put([&](int j) { return uf[j] * edg[j]; }, UC + lo);
       }
-      if (fast) {
-        // lane: A[row = i (this token)][k = 8 lg + j] and B[k][col = t (this token)]
-        const half8 rk = cvt8(rk8), rq = cvt8(rq8), ck = cvt8(ck8);
-        dacc[0] = mfma16x16x32(ck, rk, dacc[0]);
-        dacc[1] = mfma16x16x32(ck, rq, dacc[1]);
+      // lane: A[row = i (this token)][k = 8 lg + j] and B[k][col = t (this token)]
+      auto products = [&](const half8& rk, const half8& rq, const half8& ck, const half8& cu, f32x4 (&acc)[NP]) {
+        acc[0] = mfma16x16x32(ck, rk, acc[0]);
+        acc[1] = mfma16x16x32(ck, rq, acc[1]);
         if constexpr (GEN) {
-          const half8 cu = cvt8(cu8);
-          dacc[2] = mfma16x16x32(cu, rk, dacc[2]);
-          dacc[3] = mfma16x16x32(cu, rq, dacc[3]);
+          acc[2] = mfma16x16x32(cu, rk, acc[2]);
+          acc[3] = mfma16x16x32(cu, rq, acc[3]);
         }
-      }
-    }
-    // lane (lg, l16) holds the diagonal block's A[t = l16][i = 4 lg + r] (block-local)
-    if (!fast) {
-      auto level = [&](auto seg) {
-        constexpr int S = decltype(seg)::value;
-        const bool is_row = (l16 & (S - 1)) >= S / 2;
-        f32x4 lacc[NP];
+      };
+      if (fast) {
+        float rk8[8], rq8[8], ck8[8], cu8[8];
 #pragma unroll
-        for (int n = 0; n < NP; ++n) lacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          float kf[8], qf[8], rk8[8], rq8[8], ck8[8], cu8[8];
-          kval(ks, kf);
-          qval(ks, qf);
+        for (int j = 0; j < 8; ++j) {
+          const float er = eg[j] * tm[j], ec = edg[j] * tm[j];  // e^{gl - D/2}, e^{D/2 - gl}
+          rk8[j] = kf[j] * er;
+          rq8[j] = qf[j] * er;
+          ck8[j] = kf[j] * ec;
+          cu8[j] = uf[j] * ec;
+        }
+        products(cvt8(rk8), cvt8(rq8), cvt8(ck8), cvt8(cu8), dacc);
+      } else {
+        // levels: segments of S tokens, rows in the second half, columns in the first, both
+        // referenced at the last token of the first half (factors <= 1); the pairs of other
+        // segments that also meet in a product are masked out
+        auto level = [&](auto seg) {
+          constexpr int S = decltype(seg)::value;
+          const bool is_row = (l16 & (S - 1)) >= S / 2;
+          float rk8[8], rq8[8], ck8[8], cu8[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float g = gl[DCH ? 8 * ks + j : 0];
             const float gr = seg_ref<S>(g);
-            const float f = __expf(is_row ? g - gr : gr - g);  // <= 1
-            const float kx = kf[j] * f;
-            rk8[j] = is_row ? kx : 0.f;
+            const float f = __expf(is_row ? g - gr : gr - g);
+            rk8[j] = is_row ? kf[j] * f : 0.f;
             rq8[j] = is_row ? qf[j] * f : 0.f;
-            ck8[j] = is_row ? 0.f : kx;
-            cu8[j] = (is_row || !GEN) ? 0.f : ef[GEN ? 8 * ks + j : 0] * kx;
+            ck8[j] = is_row ? 0.f : kf[j] * f;
+            cu8[j] = is_row ? 0.f : uf[j] * f;
           }
-          const half8 rk = cvt8(rk8), rq = cvt8(rq8), ck = cvt8(ck8);
-          lacc[0] = mfma16x16x32(ck, rk, lacc[0]);
-          lacc[1] = mfma16x16x32(ck, rq, lacc[1]);
-          if constexpr (GEN) {
-            const half8 cu = cvt8(cu8);
-            lacc[2] = mfma16x16x32(cu, rk, lacc[2]);
-            lacc[3] = mfma16x16x32(cu, rq, lacc[3]);
+          f32x4 lacc[NP];
+#pragma unroll
+          for (int n = 0; n < NP; ++n) lacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+          products(cvt8(rk8), cvt8(rq8), cvt8(ck8), cvt8(cu8), lacc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool same = (l16 / S) == ((4 * lg + r) / S);
+#pragma unroll
+            for (int n = 0; n < NP; ++n) dacc[n][r] += same ? lacc[n][r] : 0.f;
           }
-        }
-        // keep the pairs of one segment (rows and columns of other segments meet here too)
+        };
+        level(IntTag<16>());
+        level(IntTag<8>());
+        level(IntTag<4>());
+        level(IntTag<2>());
+        // the diagonal t = i with the plain operands
+        f32x4 lacc[NP];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool same = (l16 / S) == ((4 * lg + r) / S);
+        for (int n = 0; n < NP; ++n) lacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const half8 hk = cvt8(kf);
+        products(hk, cvt8(qf), hk, cvt8(uf), lacc);
 #pragma unroll
-          for (int n = 0; n < NP; ++n) dacc[n][r] += same ? lacc[n][r] : 0.f;
-        }
-      };
-      // (one level at a time: interleaved, their operands would not fit in registers)
-      level(IntTag<16>());
-      __builtin_amdgcn_sched_barrier(0);
-      level(IntTag<8>());
-      __builtin_amdgcn_sched_barrier(0);
-      level(IntTag<4>());
-      __builtin_amdgcn_sched_barrier(0);
-      level(IntTag<2>());
-      __builtin_amdgcn_sched_barrier(0);
-      // the diagonal t = i with the plain operands
-      f32x4 lacc[NP];
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int n = 0; n < NP; ++n) lacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        float kf[8], qf[8], u8[8];
-        kval(ks, kf);
-        qval(ks, qf);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) u8[j] = GEN ? ef[GEN ? 8 * ks + j : 0] * kf[j] : 0.f;
-        const half8 hk = cvt8(kf), hq = cvt8(qf);
-        lacc[0] = mfma16x16x32(hk, hk, lacc[0]);
-        lacc[1] = mfma16x16x32(hk, hq, lacc[1]);
-        if constexpr (GEN) {
-          const half8 hu = cvt8(u8);
-          lacc[2] = mfma16x16x32(hu, hk, lacc[2]);
-          lacc[3] = mfma16x16x32(hu, hq, lacc[3]);
-        }
+          for (int n = 0; n < NP; ++n) dacc[n][r] += (l16 == 4 * lg + r) ? lacc[n][r] : 0.f;
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int n = 0; n < NP; ++n) dacc[n][r] += (l16 == 4 * lg + r) ? lacc[n][r] : 0.f;
     }
     lds_barrier();  // row and column operands, FT, TH cleared
 
     // ---- Gram tiles ----------------------------------------------------------------------
     // Off-diagonal tile n = 0..5: (I, J) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2), transposed:
-    // lane gets A[t = 16 I + l16][i = 16 J + 4 lg + r].
+    // lane gets A[t = 16 I + l16][i = 16 J + 4 lg + r].  The column fragments of the tiles two or
+    // three blocks apart are scaled by the decay of the blocks between (FT rows 0..2; row 3 is one).
     auto off_tile = [&](int n, int prod) {
       const int I = n < 1 ? 1 : n < 3 ? 2 : 3;
       const int J = n - (I * (I - 1)) / 2;
       const _Float16* rowb = (prod & 1) ? QR : KR;
       const _Float16* colb = (prod & 2) ? UC : KC;
-      const int fi = (I == 2 && J == 0) ? 0 : (I == 3 && J == 1) ? 1 : 2;  // e^{D between}
-      const bool far = J < I - 1;
+      const int fi = n == 1 ? 0 : n == 4 ? 1 : n == 3 ? 2 : 3;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        half8 a = frag_s<16>(colb, 16 * J, 32 * ks, lane);
-        if (far) a = a * *reinterpret_cast<const half8*>(FT + fi * D + 32 * ks + 8 * lg);
+        const half8 a = frag_s<16>(colb, 16 * J, 32 * ks, lane) *
+                        *reinterpret_cast<const half8*>(FT + fi * D + 32 * ks + 8 * lg);
         acc = mfma16x16x32(a, frag_s<16>(rowb, 16 * I, 32 * ks, lane), acc);
       }
       return acc;
@@ -1034,7 +998,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_ch_kernel(Problem p, c
     // overwrites in phase B)
     {
       constexpr int NA = GEN ? 18 : 6;  // (tile, product) pairs
-#pragma unroll
+      // (rolled: unrolled, the fragment reads of all of a wave's tiles are hoisted together and
+      // spill)
+#pragma unroll 1
       for (int m = 0; m < (NA + 3) / 4; ++m) {
         const int x = w + 4 * m;
         if (x < NA) {
@@ -1061,14 +1027,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_ch_kernel(Problem p, c
     }
     lds_barrier();
     // phase B: the solve matrix, fp32, over the q row operands
-    {
-      for (int n = w; n < 6; n += 4) {
-        const int I = n < 1 ? 1 : n < 3 ? 2 : 3;
-        const int J = n - (I * (I - 1)) / 2;
-        store_af(16 * I + l16, 16 * J + 4 * lg, off_tile(n, kSolveProd), false);
-      }
-      store_af(tl, 16 * w + 4 * lg, dacc[kSolveProd], true);
+    for (int n = w; n < 6; n += 4) {
+      const int I = n < 1 ? 1 : n < 3 ? 2 : 3;
+      const int J = n - (I * (I - 1)) / 2;
+      store_af(16 * I + l16, 16 * J + 4 * lg, off_tile(n, kSolveProd), false);
     }
+    store_af(tl, 16 * w + 4 * lg, dacc[kSolveProd], true);
     lds_barrier();
     solve_t(AF, TH, tid);
     if (blk + gridDim.x >= nblk) write_t(cr.pkt);  // this workgroup's last chunk
