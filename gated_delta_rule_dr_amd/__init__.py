@@ -23,7 +23,7 @@ import torch
 
 from . import _abi
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "decode_step", "workspace_bytes",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_fwd_varlen", "chunk_bwd", "decode_step", "workspace_bytes",
            "varlen_workspace_bytes", "abi_version", "DrError"]
 
 DrError = _abi.DrError
@@ -128,6 +128,42 @@ def chunk_fwd(q, k, v, log_decay, erase, write=None, S0=None, *, chunk=64,
     )
     _abi.check("dr_chunk_fwd", st)
     return out, S_T
+
+
+def chunk_fwd_noalloc(q, k, v, log_decay, erase, write=None, S0=None, *, out, S_T=None, chunk=64, fg2=False):
+    """``chunk_fwd`` through the allocation-free entry point: the caller passes the outputs
+    (``out`` [B, T, H, dv], optional ``S_T``) and the library's fixed device scratch serves as
+    the workspace, so the call allocates nothing (usable under graph capture).  Calls that may
+    overlap on one device race on that scratch.  Raises DrError (DR_E_SCRATCH) when the problem
+    needs more than ``noalloc_max_bytes()``.  Returns (out, S_T)."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, (torch.float32, torch.bfloat16), dev)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B, T, H, dk] and v [B, T, H, dv]")
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    for name, t in (("log_decay", log_decay), ("erase", erase), ("write", write), ("S0", S0)):
+        if t is not None:
+            _check_tensor(name, t, (torch.float32,), dev)
+    _check_tensor("out", out, (torch.float32, torch.bfloat16), dev)
+    if tuple(out.shape) != (B, T, H, dv):
+        raise ValueError(f"out must be [B, T, H, dv] = {(B, T, H, dv)}")
+    if S_T is not None:
+        _check_tensor("S_T", S_T, (torch.float32,), dev)
+    desc = _desc(B, T, H, dk, dv, chunk, q.dtype, out.dtype, log_decay, erase, write, (B, T, H), fg2)
+    st = _abi.lib().dr_chunk_fwd_noalloc(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(erase), _ptr(write), _ptr(S0),
+        _ptr(out), _ptr(S_T), _stream(),
+    )
+    _abi.check("dr_chunk_fwd_noalloc", st)
+    return out, S_T
+
+
+def noalloc_max_bytes() -> int:
+    return int(_abi.lib().dr_chunk_fwd_noalloc_max_bytes())
 
 
 def varlen_workspace_bytes(desc, nseq) -> int:

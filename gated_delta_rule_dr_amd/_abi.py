@@ -19,6 +19,7 @@ DR_E_ALIAS = -5
 DR_E_UNSUPPORTED = -6
 DR_E_WORKSPACE = -7
 DR_E_HIP = -8
+DR_E_SCRATCH = -9
 
 DR_F32 = 0
 DR_BF16 = 1
@@ -31,6 +32,8 @@ EXPORTS = (
     "dr_status_str",
     "dr_chunk_fwd_workspace_bytes",
     "dr_chunk_fwd",
+    "dr_chunk_fwd_noalloc_max_bytes",
+    "dr_chunk_fwd_noalloc",
     "dr_chunk_fwd_varlen_workspace_bytes",
     "dr_chunk_fwd_varlen",
     "dr_chunk_bwd_workspace_bytes",
@@ -79,6 +82,10 @@ def lib() -> ctypes.CDLL:
     L.dr_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(DrDesc)]
     L.dr_chunk_fwd.restype = ctypes.c_int
     L.dr_chunk_fwd.argtypes = [ctypes.POINTER(DrDesc)] + [vp] * 10 + [sz, vp]
+    L.dr_chunk_fwd_noalloc_max_bytes.restype = sz
+    L.dr_chunk_fwd_noalloc_max_bytes.argtypes = []
+    L.dr_chunk_fwd_noalloc.restype = ctypes.c_int
+    L.dr_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(DrDesc)] + [vp] * 10
     L.dr_chunk_fwd_varlen_workspace_bytes.restype = sz
     L.dr_chunk_fwd_varlen_workspace_bytes.argtypes = [ctypes.POINTER(DrDesc), ctypes.c_int32]
     L.dr_chunk_fwd_varlen.restype = ctypes.c_int

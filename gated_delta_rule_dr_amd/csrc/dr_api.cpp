@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/dr.h"
 #include "dr_internal.h"
 
@@ -129,6 +131,87 @@ int launched(hipError_t launch_err) {
 }
 
 
+size_t chunk_fwd_workspace(const dr_desc* desc);
+
+// Validation of a dense forward call.  check_ws: the caller passes the workspace (it must be
+// large enough and must not overlap the other arrays); otherwise the library supplies it.
+int check_chunk_fwd(const dr_desc* d, const void* q, const void* k, const void* v, const float* log_decay,
+                    const float* erase, const float* write, const float* S0, const void* o, const float* S_T,
+                    const void* workspace, size_t workspace_bytes, bool check_ws, Extents* exo) {
+  Extents& ex = *exo;
+  int st = check_desc(d, false, &ex);
+  if (st != DR_OK) return st;
+  const bool need_write = !d->write_is_erase;
+  if ((st = check_ptr(q, ex.qk, true)) || (st = check_ptr(k, ex.qk, true)) ||
+      (st = check_ptr(v, ex.v, true)) || (st = check_ptr(log_decay, ex.decay, true)) ||
+      (st = check_ptr(erase, ex.erase, true)) ||
+      (st = check_ptr(need_write ? write : nullptr, ex.write, need_write)) ||
+      (st = check_ptr(S0, ex.state, false)) || (st = check_ptr(o, ex.o, true)) ||
+      (st = check_ptr(S_T, ex.state, false)) || (st = check_ptr(workspace, workspace_bytes, false)))
+    return st;
+  if (check_ws && workspace_bytes < chunk_fwd_workspace(d)) return DR_E_WORKSPACE;
+
+  const Range rin[] = {range_of(q, ex.qk),         range_of(k, ex.qk),
+                       range_of(v, ex.v),          range_of(log_decay, ex.decay),
+                       range_of(erase, ex.erase),  range_of(need_write ? write : nullptr, ex.write),
+                       range_of(S0, ex.state)};
+  const Range ro = range_of(o, ex.o), rs = range_of(S_T, ex.state);
+  for (const Range& r : rin)
+    if (overlaps(ro, r)) return DR_E_ALIAS;
+  if (overlaps(ro, rs)) return DR_E_ALIAS;
+  for (int i = 0; i < 6; ++i)
+    if (overlaps(rs, rin[i])) return DR_E_ALIAS;
+  if (S0 != nullptr && S_T != nullptr && S0 != S_T && overlaps(rs, rin[6])) return DR_E_ALIAS;
+  if (check_ws) {
+    const Range rw = range_of(workspace, workspace_bytes);
+    for (const Range& r : rin)
+      if (overlaps(rw, r)) return DR_E_ALIAS;
+    if (overlaps(rw, ro) || overlaps(rw, rs)) return DR_E_ALIAS;
+  }
+  return DR_OK;
+}
+
+// Launch of a validated dense forward call.
+int launch_chunk_fwd(const dr_desc* d, const void* q, const void* k, const void* v, const float* log_decay,
+                     const float* erase, const float* write, const float* S0, void* o, float* S_T, void* workspace,
+                     const Extents& ex, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (d->T == 0) {
+    if (S_T == nullptr || S_T == S0) return DR_OK;
+    return launched(dr::launch_state_copy(S0, S_T, int64_t(ex.state / 4), s));
+  }
+  dr::Problem p = make_problem(d, q, k, v, log_decay, erase, write, S0, o, S_T);
+  if (uses_chunk128(d)) return launched(dr::launch_chunk128(p, workspace, s));
+  return launched(dr::launch_recurrent(p, s));
+}
+
+// ---- the fixed scratch of dr_chunk_fwd_noalloc -------------------------------------------
+// A file-scope device array (each device that loads the library holds its own copy until the
+// process ends).  Host code never uses the array's name as an address: it is a host-side
+// stand-in.  The device address is resolved once per device, with that device current, by
+// hipGetSymbolAddress, and only that address reaches kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// This device's scratch address (the current device).
+int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DR_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return DR_E_UNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = ptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return DR_E_HIP;
+  *out = g_scratch_ptr[dev];
+  return DR_OK;
+}
+
 // Validation and launch of the gradient call, dense (packed == false) or over nseq packed
 // sequences delimited by cu_seqlens (packed == true: desc->B == 1, states [nseq, H, dk, dv]).
 int chunk_bwd_common(const dr_desc* d, const int32_t* cu_seqlens, int32_t nseq, bool packed, const void* q,
@@ -154,11 +237,17 @@ const char* dr_status_str(int status) {
     case DR_E_UNSUPPORTED: return "combination not supported by this library";
     case DR_E_WORKSPACE: return "workspace missing or too small";
     case DR_E_HIP: return "HIP launch failed";
+    case DR_E_SCRATCH: return "the problem needs more than the fixed scratch of dr_chunk_fwd_noalloc";
     default: return "unknown status";
   }
 }
 
-size_t dr_chunk_fwd_workspace_bytes(const dr_desc* desc) {
+size_t dr_chunk_fwd_workspace_bytes(const dr_desc* desc) { return chunk_fwd_workspace(desc); }
+
+}  // extern "C"
+
+namespace {
+size_t chunk_fwd_workspace(const dr_desc* desc) {
   Extents ex;
   if (check_desc(desc, false, &ex) != DR_OK) return 0;
   if (!uses_chunk128(desc)) return 0;
@@ -166,48 +255,34 @@ size_t dr_chunk_fwd_workspace_bytes(const dr_desc* desc) {
                                       desc->decay_kind == DR_GATE_CHANNEL,
                                       desc->erase_kind == DR_GATE_RATE_SQRT);
 }
+}  // namespace
+
+extern "C" {
 
 int dr_chunk_fwd(const dr_desc* d, const void* q, const void* k, const void* v,
                  const float* log_decay, const float* erase, const float* write,
                  const float* S0, void* o, float* S_T, void* workspace, size_t workspace_bytes,
                  void* stream) {
   Extents ex;
-  int st = check_desc(d, false, &ex);
+  const int st = check_chunk_fwd(d, q, k, v, log_decay, erase, write, S0, o, S_T, workspace, workspace_bytes,
+                                 true, &ex);
   if (st != DR_OK) return st;
-  const bool need_write = !d->write_is_erase;
-  if ((st = check_ptr(q, ex.qk, true)) || (st = check_ptr(k, ex.qk, true)) ||
-      (st = check_ptr(v, ex.v, true)) || (st = check_ptr(log_decay, ex.decay, true)) ||
-      (st = check_ptr(erase, ex.erase, true)) ||
-      (st = check_ptr(need_write ? write : nullptr, ex.write, need_write)) ||
-      (st = check_ptr(S0, ex.state, false)) || (st = check_ptr(o, ex.o, true)) ||
-      (st = check_ptr(S_T, ex.state, false)) || (st = check_ptr(workspace, workspace_bytes, false)))
-    return st;
-  if (workspace_bytes < dr_chunk_fwd_workspace_bytes(d)) return DR_E_WORKSPACE;
+  return launch_chunk_fwd(d, q, k, v, log_decay, erase, write, S0, o, S_T, workspace, ex, stream);
+}
 
-  const Range rin[] = {range_of(q, ex.qk),         range_of(k, ex.qk),
-                       range_of(v, ex.v),          range_of(log_decay, ex.decay),
-                       range_of(erase, ex.erase),  range_of(need_write ? write : nullptr, ex.write),
-                       range_of(S0, ex.state)};
-  const Range ro = range_of(o, ex.o), rs = range_of(S_T, ex.state);
-  for (const Range& r : rin)
-    if (overlaps(ro, r)) return DR_E_ALIAS;
-  if (overlaps(ro, rs)) return DR_E_ALIAS;
-  for (int i = 0; i < 6; ++i)
-    if (overlaps(rs, rin[i])) return DR_E_ALIAS;
-  if (S0 != nullptr && S_T != nullptr && S0 != S_T && overlaps(rs, rin[6])) return DR_E_ALIAS;
-  const Range rw = range_of(workspace, workspace_bytes);
-  for (const Range& r : rin)
-    if (overlaps(rw, r)) return DR_E_ALIAS;
-  if (overlaps(rw, ro) || overlaps(rw, rs)) return DR_E_ALIAS;
+size_t dr_chunk_fwd_noalloc_max_bytes(void) { return kScratchBytes; }
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (d->T == 0) {
-    if (S_T == nullptr || S_T == S0) return DR_OK;
-    return launched(dr::launch_state_copy(S0, S_T, int64_t(ex.state / 4), s));
-  }
-  dr::Problem p = make_problem(d, q, k, v, log_decay, erase, write, S0, o, S_T);
-  if (uses_chunk128(d)) return launched(dr::launch_chunk128(p, workspace, s));
-  return launched(dr::launch_recurrent(p, s));
+int dr_chunk_fwd_noalloc(const dr_desc* d, const void* q, const void* k, const void* v,
+                         const float* log_decay, const float* erase, const float* write,
+                         const float* S0, void* o, float* S_T, void* stream) {
+  Extents ex;
+  int st = check_chunk_fwd(d, q, k, v, log_decay, erase, write, S0, o, S_T, nullptr, 0, false, &ex);
+  if (st != DR_OK) return st;
+  const size_t need = dr_chunk_fwd_workspace_bytes(d);
+  if (need > kScratchBytes) return DR_E_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_ptr(&ws)) != DR_OK) return st;
+  return launch_chunk_fwd(d, q, k, v, log_decay, erase, write, S0, o, S_T, ws, ex, stream);
 }
 
 size_t dr_chunk_fwd_varlen_workspace_bytes(const dr_desc* desc, int32_t nseq) {

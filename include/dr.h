@@ -29,8 +29,16 @@
  *
  * Ownership and threading.  Every pointer is a device pointer that the caller allocated and
  * keeps alive until the enqueued work has finished.  The library allocates nothing, never
- * synchronises, keeps no mutable global state and enqueues all work on `stream` (a
- * hipStream_t; NULL = the default stream), so calls on distinct streams may run concurrently.
+ * synchronises and enqueues all work on `stream` (a hipStream_t; NULL = the default stream),
+ * so calls on distinct streams may run concurrently.  Its only global state is the fixed
+ * scratch of dr_chunk_fwd_noalloc (a device array per device, and that array's address,
+ * resolved once per device).
+ *
+ * Range.  The matrix-core path multiplies fp16 operands: q, k, v and the fp32 state enter its
+ * products as fp16, so entries of q, k, v or S of magnitude 65504 or more (and values formed
+ * from them, such as beta (v - S^T k)) overflow there.  Decay factors never do: every one is
+ * at most one, or bounded by e^6 where the inputs are checked to be moderate, for any decay in
+ * (0, 1].  The token-by-token path (fp32) has no such limit.
  *
  * Errors.  Argument errors are detected synchronously, before anything is enqueued, and the
  * call returns a negative dr_status with no device work issued.  A failed launch returns
@@ -59,7 +67,9 @@ typedef enum {
   DR_E_ALIAS = -5,       /* an output overlaps an input (other than the allowed S0 == S_T) */
   DR_E_UNSUPPORTED = -6, /* a valid combination this library does not implement */
   DR_E_WORKSPACE = -7,   /* workspace missing or smaller than dr_chunk_fwd_workspace_bytes */
-  DR_E_HIP = -8          /* a HIP launch failed */
+  DR_E_HIP = -8,         /* a HIP launch failed */
+  DR_E_SCRATCH = -9      /* dr_chunk_fwd_noalloc: the problem needs more workspace than its fixed
+                            scratch holds (dr_chunk_fwd_noalloc_max_bytes) */
 } dr_status;
 
 typedef enum { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
@@ -101,8 +111,9 @@ const char* dr_status_str(int status);
  * descriptor.  The matrix-core path stores, per 64-token chunk of every (b, h), one packet of
  * the chunk's state-independent factors: the triangular-solve factor and the in-chunk
  * decay-weighted Gram matrices (lower-triangular fp16 64 x 64, only their six nonzero 16 x 32
- * blocks), the gate factors, and the fp16 key/query tiles (decayed, plus the transposed decayed
- * keys, unless the decay is per head with one per-head gate for erase and write).  That is
+ * blocks), the gate factors, and the fp16 key/query tiles (decayed from the chunk start, plus
+ * the keys decayed to the chunk end, unless the decay is per head with one per-head gate for
+ * erase and write).  That is
  * B * H * ceil(T / 64) * P bytes with P = 46080 (per-head decay, one per-head erase/write gate),
  * 63488 (per-channel decay, one per-head erase/write gate), 62464 (per-head decay,
  * DR_GATE_RATE_SQRT) or 79872 (per-channel decay, DR_GATE_RATE_SQRT; these two add the scaled
@@ -131,6 +142,25 @@ int dr_chunk_fwd(const dr_desc* desc, const void* q, const void* k, const void* 
                  const float* log_decay, const float* erase, const float* write,
                  const float* S0, void* o, float* S_T, void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/* Allocation-free forward, for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same operation, paths,
+ * arguments and errors as dr_chunk_fwd without the workspace arguments: the workspace is a
+ * fixed device array inside the library (dr_chunk_fwd_noalloc_max_bytes() = 64 MiB), one per
+ * device, allocated when the library's device code is loaded on that device and held until the
+ * process ends; the call itself allocates nothing.  A problem whose dr_chunk_fwd_workspace_bytes
+ * exceeds it returns DR_E_SCRATCH before any device work (about 700 to 1,450 chunks of 64 tokens
+ * across all (b, h), by gate kind: e.g. H = 32 heads of up to 1,400 tokens with separate
+ * erase/write gates).  All calls on one device share its array: calls that may overlap in time
+ * on one device (different streams, or different host threads without ordering) race and must
+ * be serialised by the caller.  Nothing in the array needs clearing between calls (each call
+ * writes every byte it reads).  The first call on a device resolves the array's device
+ * address (hipGetSymbolAddress); a failure there returns DR_E_HIP. */
+size_t dr_chunk_fwd_noalloc_max_bytes(void);
+
+int dr_chunk_fwd_noalloc(const dr_desc* desc, const void* q, const void* k, const void* v,
+                         const float* log_decay, const float* erase, const float* write,
+                         const float* S0, void* o, float* S_T, void* stream);
 
 /* Packed batches of sequences of different lengths (serving prefill).  The nseq sequences lie
  * one after another on the token axis of the dr_chunk_fwd layouts with B = 1 (desc->B must be

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 def test_version_and_status_strings():
     L = _abi.lib()
     assert L.dr_abi_version() == 1
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert _abi.status_str(code)
     assert _abi.status_str(-99) == "unknown status"
     assert _abi.status_str(0) == "ok"
@@ -309,3 +309,30 @@ def test_bwd_varlen_workspace_and_errors():
     assert call(d, cu=P_CU + 2) == _abi.DR_E_ALIGN
     assert call(d, dq=P_CU) == _abi.DR_E_ALIAS  # an output on the offsets
     assert call(d, n=-1) == _abi.DR_E_SHAPE
+
+
+def _fwd_noalloc(desc, **over):
+    ptr = dict(P)
+    ptr.update(over)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return _abi.lib().dr_chunk_fwd_noalloc(ctypes.byref(desc) if desc is not None else None,
+                                           vp(ptr["q"]), vp(ptr["k"]), vp(ptr["v"]), vp(ptr["ld"]), vp(ptr["e"]),
+                                           vp(ptr["w"]), vp(ptr["S0"]), vp(ptr["o"]), vp(ptr["ST"]), None)
+
+
+def test_noalloc_validates_before_any_device_work():
+    # the allocation-free forward checks every argument as dr_chunk_fwd does, and refuses a
+    # problem beyond its fixed scratch, all before it touches the device
+    L = _abi.lib()
+    assert L.dr_chunk_fwd_noalloc_max_bytes() == 64 << 20
+    assert _abi.status_str(_abi.DR_E_SCRATCH) != "unknown status"
+    assert _fwd_noalloc(None) == _abi.DR_E_NULL
+    assert _fwd_noalloc(_good_desc(), q=None) == _abi.DR_E_NULL
+    assert _fwd_noalloc(_good_desc(), o=P["q"]) == _abi.DR_E_ALIAS
+    assert _fwd_noalloc(_good_desc(qkv_dtype=7)) == _abi.DR_E_DTYPE
+    assert _fwd_noalloc(_good_desc(), k=P["k"] + 8) == _abi.DR_E_ALIGN
+    # 2 x 4 heads x 100 tokens fit; 64 heads x 1,600 tokens of separate gates do not
+    big = _good_desc(B=1, T=1600, H=64, decay_kind=_abi.DR_GATE_CHANNEL, erase_kind=_abi.DR_GATE_CHANNEL,
+                     write_kind=_abi.DR_GATE_CHANNEL, write_is_erase=0)
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(big)) > 64 << 20
+    assert _fwd_noalloc(big) == _abi.DR_E_SCRATCH
