@@ -1,25 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark of the gated delta-rule hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--all]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-decode]
+                    [--no-extra] [--backward]
 
-One step is one chunked forward (dr_chunk_fwd) over the scalar-gate Gated DeltaNet prefill
-batch B=4, H=16, T=4096, dk=dv=128, bf16 q/k/v, fp32 gates and state, chunk 64.  W untimed
-warm-up steps run first; K steps are then timed between two device synchronisations with HIP
-events on the stream the kernels are launched on.  Two independently drawn input sets
-alternate so that the 194 MiB batch is not served from the 256 MB last-level cache.
+One step is one chunked forward (dr_chunk_fwd) over the main prefill workload, by default the
+long-context one: decoupled per-channel erase and write gates with a per-channel decay
+(Gated DeltaNet-2 / FG2-GDN+), B=1, H=32, T=65536, dk=dv=128, bf16 q/k/v, fp32 gates, output and
+state, chunk 64.  W untimed warm-up steps run first; K steps are then timed between two device
+synchronisations with HIP events on the stream the kernels are launched on.  Two independently
+drawn input sets alternate so that the batch is not served from the 256 MB last-level cache.
 
 The single JSON line printed at the end carries:
-  value        prefill tokens/s (B*H*T per second of kernel time)
-  roofline     one forward call (its two kernels: the chunk-parallel prep and the chunk scan)
-               against HBM bandwidth: algorithmic bytes per call (compulsory input/output
-               bytes) / average call duration, peak 8 TB/s, plus the counter-measured HBM
-               traffic of both kernels when a counter summary for the current kernel source is
-               committed under profiles/
-  mfma         algorithmic matrix flops / time against the 2.5 PFLOP/s dense fp16/bf16 peak
-  decode       1000 single-token steps for 256 sequences x 32 heads (steps/s, GB/s, fraction
-               of HBM peak)
-  cpu_baseline the fp64 oracle on a bounded sample of the same workload, one thread
+  value         prefill tokens/s of the main workload (B*H*T per second of kernel time)
+  roofline      one forward call (its two kernels: the chunk-parallel prep and the chunk scan)
+                against HBM bandwidth: algorithmic bytes per call (compulsory input/output bytes)
+                / average call duration, peak 8 TB/s, plus the counter-measured HBM traffic of both
+                kernels when a counter summary for the current kernel source is committed under
+                profiles/
+  mfma          algorithmic matrix flops / time against the 2.5 PFLOP/s dense fp16/bf16 peak
+  other_prefill the other prefill workloads timed the same way in the same run: scalar-gate
+                Gated DeltaNet B=4 H=16 T=4096, KDA B=2 H=32 T=16384, FG2's rate at the KDA shape,
+                and the packed serving prefill (16k tokens in 20 sequences)
+  decode        1000 single-token steps for 256 sequences x 32 heads (steps/s, GB/s, fraction of
+                HBM peak)
+  cpu_baseline  the fp64 oracle on the first --cpu-tokens tokens of every head of the main
+                workload, the heads sharded over one worker process per host core (at most 16)
 """
 from __future__ import annotations
 
@@ -36,7 +42,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16
 METRIC = "prefill tokens/s (B·H·T/s) + MFMA % peak; decode steps/s + HBM GB/s % peak"
-PREFILL = "gdn_scalar_bf16_t4k"
+PREFILL = "gdn2_decoupled_bf16_t64k"
+EXTRA_PREFILL = ("gdn_scalar_bf16_t4k", "kda_channel_bf16_t16k", "fg2_channel_bf16_t16k",
+                 "gdn_scalar_bf16_varlen_t16k")
 DECODE = "decode_kda_n256_h32"
 CHUNK_SRC = os.path.join(ROOT, "gated_delta_rule_dr_amd", "csrc", "chunk.hip")
 DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_dr_amd", "csrc", "decode.hip")
@@ -231,28 +239,105 @@ def time_decode(dr, torch, wl, steps):
     return sec / steps
 
 
-def cpu_baseline(wl, tokens):
-    """The fp64 oracle on the first `tokens` tokens of every (b, h) of the workload."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def _oracle_shard(args):
+    """Worker: the oracle on heads h0:h1 of the sample memory-mapped from `folder`; returns its
+    compute interval (wall-clock start and end)."""
+    folder, h0, h1, kind = args
+    import numpy as np
     from threadpoolctl import threadpool_limits
 
-    from gated_delta_rule_dr_amd.workloads import generate
     from oracle import recurrence, recurrence_fg2, recurrence_varlen
 
-    sample = wl.replace(T=tokens)
-    inp = generate(sample)
-    args = (inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"], inp["S0"])
+    def ld(name):
+        path = os.path.join(folder, name + ".npy")
+        if not os.path.exists(path):
+            return None
+        x = np.load(path, mmap_mode="r")
+        return np.ascontiguousarray(x[:, :, h0:h1]) if name != "S0" and name != "cu_seqlens" else x
+
+    x = {n: ld(n) for n in ("q", "k", "v", "log_decay", "erase", "write", "cu_seqlens")}
+    s0 = ld("S0")
+    if s0 is not None:
+        s0 = np.ascontiguousarray(s0[:, h0:h1])
     with threadpool_limits(1):
-        t0 = time.perf_counter()
-        if "cu_seqlens" in inp:  # packed: the first `tokens` tokens, cut into the recipe's lengths
-            recurrence_varlen(*args, inp["cu_seqlens"])
-        elif wl.rate_sqrt:
-            recurrence_fg2(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["S0"])
+        t0 = time.time()
+        if kind == "varlen":
+            recurrence_varlen(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"], s0, x["cu_seqlens"])
+        elif kind == "fg2":
+            recurrence_fg2(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], s0)
         else:
-            recurrence(*args)
-        sec = time.perf_counter() - t0
-    return dict(value=sample.token_heads / sec, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{sample.B}x{sample.H} heads x first {tokens} tokens of {wl.name} "
-                       f"({sample.token_heads} token-heads, {sec:.1f} s, fp64 numpy, 1 thread)")
+            recurrence(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"], s0)
+        t1 = time.time()
+    return t0, t1
+
+
+def cpu_baseline(wl, tokens, max_workers=16):
+    """The fp64 oracle on the first `tokens` tokens of every (b, h) of the workload, the heads
+    sharded over one worker process per host core (spawned; BLAS/OMP threads 1 each)."""
+    import multiprocessing
+    import shutil
+    import tempfile
+
+    import numpy as np
+
+    from gated_delta_rule_dr_amd.workloads import generate
+
+    sample = wl.replace(T=min(tokens, wl.T))
+    inp = generate(sample)
+    workers = max(1, min(len(os.sched_getaffinity(0)), max_workers, wl.H))
+    folder = tempfile.mkdtemp(prefix="dr_oracle_", dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    try:
+        for name, t in inp.items():
+            if t is None:
+                continue
+            a = t.numpy() if t.dtype != __import__("torch").bfloat16 else t.float().numpy()
+            np.save(os.path.join(folder, name + ".npy"), a)
+        del inp
+        kind = "varlen" if wl.seq_median > 0 else "fg2" if wl.rate_sqrt else "dense"
+        bounds = np.linspace(0, wl.H, workers + 1).round().astype(int)
+        jobs = [(folder, int(bounds[i]), int(bounds[i + 1]), kind) for i in range(workers)]
+        ctx = multiprocessing.get_context("spawn")
+        wall0 = time.perf_counter()
+        with ctx.Pool(workers) as pool:
+            spans = pool.map(_oracle_shard, jobs)
+        wall = time.perf_counter() - wall0
+    finally:
+        shutil.rmtree(folder, ignore_errors=True)
+    sec = max(e for _, e in spans) - min(s for s, _ in spans)
+    return dict(value=sample.token_heads / sec, unit="tokens/s", cores=workers, kind="oracle", cpu_model=cpu_model(),
+                sample=f"first {sample.T} tokens of all {wl.B}x{wl.H} heads of {wl.name} ({sample.token_heads} "
+                       f"token-heads), heads sharded over {workers} worker processes: {sec:.1f} s of compute "
+                       f"({wall:.1f} s with process start), fp64 numpy, 1 thread each")
+
+
+def kernel_desc(wl) -> str:
+    """The kernels one forward call of the workload launches."""
+    general = (wl.erase_channel and not wl.rate_sqrt) or wl.write == "channel"
+    prep = "chunk_prep_ch_kernel" if (wl.decay_channel or general) else "chunk_prep_scalar_kernel"
+    scan = "chunk_scan_kernel" if general else "chunk_scan_sym_kernel"
+    if wl.seq_median:
+        return f"dr_chunk_fwd_varlen = varlen_setup_kernel + {prep} + {scan} (one call)"
+    return f"dr_chunk_fwd = {prep} + {scan} (one call)"
+
+
+def prefill_record(wl, sec):
+    return {"tokens_per_s": wl.token_heads / sec, "ms": sec * 1e3,
+            "hbm_frac": algorithmic_bytes(wl) / sec / 1e9 / HBM_PEAK_GBS,
+            "mfma_frac": algorithmic_flops(wl) / sec / 1e12 / MFMA_PEAK_TFLOPS,
+            "algorithmic_bytes_per_launch": algorithmic_bytes(wl), "kernel": kernel_desc(wl)}
 
 
 def main():
@@ -261,15 +346,15 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-tokens", type=int, default=16384,
+                    help="tokens per head of the oracle's sample (default %(default)s)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--all", action="store_true",
-                    help="also time the KDA, FG2, decoupled and packed-sequence prefill workloads")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other prefill workloads")
     ap.add_argument("--backward", action="store_true",
                     help="also time the gradient call (dr_chunk_bwd) on the main workload")
     ap.add_argument("--workload", default=PREFILL,
-                    help="prefill workload of the main line (default: the bench workload %(default)s)")
+                    help="prefill workload of the main line (default: %(default)s)")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="also run one plain elementwise copy of this many MiB (a known-size "
                          "reference for HBM byte counters)")
@@ -302,6 +387,7 @@ def main():
         print(f"{wl.name} is a decode workload; --workload takes a prefill one", file=sys.stderr)
         sys.exit(2)
     sec, wall = time_prefill(dr, torch, wl, args.steps, args.warmup)
+    torch.cuda.empty_cache()
     tok_s = wl.token_heads / sec
     nbytes = algorithmic_bytes(wl)
     flops = algorithmic_flops(wl)
@@ -324,24 +410,20 @@ def main():
                    "chunk": wl.chunk, "qkv": wl.qkv_dtype, "gates": gate_desc(wl), "o": "fp32",
                    **({"sequences": n_states(wl)} if wl.seq_median else {})},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": ("dr_chunk_fwd_varlen = varlen_setup_kernel + chunk_prep_kernel + scan (one call)"
-                                if wl.seq_median else
-                                "dr_chunk_fwd = chunk_prep_kernel + chunk_scan_sym_kernel (one call)"),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kernel_desc(wl),
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": {"achieved_tflops": flops / sec / 1e12, "peak_tflops": MFMA_PEAK_TFLOPS,
                  "frac": flops / sec / 1e12 / MFMA_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops},
         "timed_wall_s": wall,
     }
-    if args.all:
+    if not args.no_extra:
         extra = {}
-        for name in ("kda_channel_bf16_t16k", "fg2_channel_bf16_t16k", "gdn2_decoupled_bf16_t64k",
-                     "gdn_scalar_bf16_varlen_t16k"):
+        for name in EXTRA_PREFILL:
+            if name == wl.name:
+                continue
             w2 = workload(name)
-            s2, _ = time_prefill(dr, torch, w2, max(3, args.steps // 10), 2)
-            extra[name] = {"tokens_per_s": w2.token_heads / s2, "ms": s2 * 1e3,
-                           "hbm_frac": algorithmic_bytes(w2) / s2 / 1e9 / HBM_PEAK_GBS,
-                           "mfma_frac": algorithmic_flops(w2) / s2 / 1e12 / MFMA_PEAK_TFLOPS}
+            s2, _ = time_prefill(dr, torch, w2, max(5, args.steps // 5), 2)
+            extra[name] = prefill_record(w2, s2)
             torch.cuda.empty_cache()
         line["other_prefill"] = extra
     if args.backward:
@@ -353,7 +435,7 @@ def main():
                             "bytes_per_call": bbytes,
                             "kernel": "dr_chunk_bwd = bwd_token_kernel + bwd_reduce_kernel (fp32 token adjoint)"}
         if not args.no_cpu:
-            line["backward"]["cpu_baseline"] = cpu_baseline_backward(wl, max(64, args.cpu_tokens // 16))
+            line["backward"]["cpu_baseline"] = cpu_baseline_backward(wl, max(64, args.cpu_tokens // 64))
         torch.cuda.empty_cache()
     if not args.no_decode:
         dwl = workload(DECODE)
