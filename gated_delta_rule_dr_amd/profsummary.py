@@ -3,8 +3,16 @@
 
     python -m gated_delta_rule_dr_amd.profsummary trace  <kernel_stats.csv> <out.md> "<command>"
     python -m gated_delta_rule_dr_amd.profsummary traffic <fetch_counter_collection.csv> \\
-        <write_counter_collection.csv> <copy_ref_mib> <kernel-substring>[,<kernel-substring>...] \\
+        <write_counter_collection.csv> <copy_ref_mib> <kernel-substring>[;<kernel-substring>...] \\
         <source-file> <algorithmic-bytes-per-call> <out.json> "<fetch command>" "<write command>"
+    python -m gated_delta_rule_dr_amd.profsummary mfma <counter_collection.csv> <kernel_stats.csv> \\
+        <kernel-substring>[;...] <out.md> "<counter command>" "<trace command>"
+
+``mfma`` reports, per kernel, the matrix-core counters of one dispatch (averaged over the
+dispatches profiled): SQ_INSTS_VALU_MFMA_MOPS_F16 (units of 512 flops), SQ_INSTS_MFMA,
+SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES and GRBM_GUI_ACTIVE, with the counted fp16 matrix
+flops divided by the kernel's average duration from a kernel trace of the same command, against
+the 2.5 PFLOP/s dense fp16 peak.
 
 ``traffic`` converts the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch) of the kernels
 one call launches (each named by a substring; one dispatch of each per call) into HBM bytes
@@ -71,7 +79,7 @@ def traffic(fetch_csv, write_csv, copy_mib, patterns, source, alg_bytes, out_jso
     w_fac, w_ref = _copy_ref(wr, "WRITE_SIZE", copy_bytes)
     kernels = {}
     read_b = write_b = 0.0
-    for pattern in patterns.split(","):
+    for pattern in patterns.split(";"):
         f_kib, nf = _kernel_avg(fr, "FETCH_SIZE", pattern)
         w_kib, nw = _kernel_avg(wr, "WRITE_SIZE", pattern)
         kernels[pattern] = {"fetch_size_kib_per_dispatch": f_kib, "write_size_kib_per_dispatch": w_kib,
@@ -99,11 +107,48 @@ def traffic(fetch_csv, write_csv, copy_mib, patterns, source, alg_bytes, out_jso
         f.write("\n")
 
 
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
+                 "GRBM_GUI_ACTIVE")
+
+
+def mfma(counter_csv, stats_csv, patterns, out_md, cmd_counters, cmd_trace):
+    rows = _rows(counter_csv)
+    stats = _rows(stats_csv)
+    lines = [
+        "# Matrix-core counters per dispatch",
+        "",
+        f"Counters: `{cmd_counters}`",
+        "",
+        f"Durations: `{cmd_trace}`",
+        "",
+        "Counted fp16 matrix flops = SQ_INSTS_VALU_MFMA_MOPS_F16 x 512; rate = flops / average duration;",
+        "peak 2.5 PFLOP/s (dense fp16).",
+        "",
+        "| kernel | " + " | ".join(MFMA_COUNTERS) + " | avg duration (us) | counted TFLOP/s | fraction of peak |",
+        "|---|" + "---|" * (len(MFMA_COUNTERS) + 3),
+    ]
+    for pattern in patterns.split(";"):
+        vals = []
+        for c in MFMA_COUNTERS:
+            v, _ = _kernel_avg(rows, c, pattern)
+            vals.append(v)
+        durs = [float(r["AverageNs"]) for r in stats if pattern in r["Name"]]
+        dur_ns = durs[0] if durs else float("nan")
+        flops = vals[0] * 512.0
+        tf = flops / dur_ns / 1e3 if durs else float("nan")
+        lines.append(f"| `{pattern}` | " + " | ".join(f"{v:.4g}" for v in vals) +
+                     f" | {dur_ns / 1e3:.1f} | {tf:.1f} | {tf / 2500.0:.4f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     mode = sys.argv[1]
     if mode == "trace":
         trace(*sys.argv[2:5])
     elif mode == "traffic":
         traffic(*sys.argv[2:12])
+    elif mode == "mfma":
+        mfma(*sys.argv[2:8])
     else:
         raise SystemExit(__doc__)
