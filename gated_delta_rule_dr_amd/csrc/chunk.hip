@@ -1145,7 +1145,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   constexpr int NCT = DVS / 16;   // 16-column tiles of the value slice
   constexpr int VPT = DVS / 8;    // value columns per thread in the V load
   constexpr int NTU = 8;  // 16-byte operand-tile units per thread (K+, Q+, K^end, U^end)
-  constexpr int PF = 1;   // chunks of prefetch in flight
+  constexpr int PF = 2;   // chunks of prefetch in flight (one register set each)
   __shared__ __attribute__((aligned(16))) char smem[L::total];
   _Float16* KP = reinterpret_cast<_Float16*>(smem + L::kp);
   _Float16* QP = reinterpret_cast<_Float16*>(smem + L::qp);
@@ -1460,11 +1460,20 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   // the upper blocks (0,1) and (1,1) of the four matrices are zero and never copied
   *reinterpret_cast<uint4*>(TH + 4096 * (tid >> 7) + 512 * (1 + 2 * ((tid >> 6) & 1)) + 8 * lane) =
       make_uint4(0, 0, 0, 0);
-  Pref PA;
+  // chunk c's inputs sit in set c % 2; each step refills its set with chunk c + 2
+  Pref PA, PB;
   load(PA, 0);
+  load(PB, nchunks > 1 ? 1 : 0);
   int c = 0;
-  for (; c < nfull; ++c) step(Flag<false>(), c, PA);
-  if (c < nchunks) step(Flag<true>(), c, PA);
+  for (; c + 1 < nfull; c += 2) {
+    step(Flag<false>(), c, PA);
+    step(Flag<false>(), c + 1, PB);
+  }
+  if (c < nfull) step(Flag<false>(), c++, PA);
+  if (c < nchunks) {
+    if (c & 1) step(Flag<true>(), c, PB);
+    else step(Flag<true>(), c, PA);
+  }
 
   if (p.S_T) {
 #pragma unroll
