@@ -2,7 +2,7 @@
 """Benchmark of the gated delta-rule hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-decode]
-                    [--no-extra] [--backward]
+                    [--no-extra] [--backward] [--segment-scan P]
 
 One step is one chunked forward (dr_chunk_fwd) over the main prefill workload, by default the
 long-context one: decoupled per-channel erase and write gates with a per-channel decay
@@ -212,6 +212,62 @@ def time_prefill(dr, torch, wl, steps, warmup):
     return e0.elapsed_time(e1) / 1e3 / steps, wall
 
 
+def time_segment_scan(dr, torch, wl, nseg, reps=3):
+    """The segment-parallel alternative to the sequential chunk scan, composed from the library's
+    own packed-sequence call (a measurement for the design record; dr_chunk_fwd does not take
+    this route).  Each head's T tokens split into nseg segments; because the chunk map is affine
+    in (S0, v), one packed call over the first nseg - 1 segments with v = 0 and S0 = I gives the
+    segments' state maps F, a second with S0 = 0 their offsets H; the segments' incoming states
+    S_in[s] = F[s - 1] S_in[s - 1] + H[s - 1] are chained (nseg - 1 small matrix products per
+    head, torch), and a third packed call runs all segments from their true S_in, giving o and
+    S_T.  Returns (segmented ms, single-pass ms, max relative difference of o and S_T)."""
+    from gated_delta_rule_dr_amd.workloads import generate
+
+    assert wl.B == 1 and wl.dk == wl.dv and wl.T % (64 * nseg) == 0, "one sequence, whole-chunk segments"
+    x = generate(wl, device="cuda")
+    T, H, d = wl.T, wl.H, wl.dk
+    seg = T // nseg
+    cu_all = torch.arange(0, T + 1, seg, dtype=torch.int32, device="cuda")
+    cu_maps = cu_all[:nseg].contiguous()
+    Tm = int(cu_maps[-1])
+    head = lambda t: None if t is None else t[:, :Tm].contiguous()
+    qm, km, ldm, em, wm = (head(x[n]) for n in ("q", "k", "log_decay", "erase", "write"))
+    vm, v0 = head(x["v"]), torch.zeros_like(head(x["v"]))
+    eye = torch.eye(d, device="cuda").expand(nseg - 1, H, d, d).contiguous()
+    s0 = torch.zeros((1, H, d, d), device="cuda") if x["S0"] is None else x["S0"]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def segmented():
+        _, F = dr.chunk_fwd_varlen(qm, km, v0, ldm, em, wm, eye, cu_seqlens=cu_maps, fg2=wl.rate_sqrt)
+        _, Hs = dr.chunk_fwd_varlen(qm, km, vm, ldm, em, wm, None, cu_seqlens=cu_maps, fg2=wl.rate_sqrt)
+        S_in = [s0[0]]
+        for s in range(1, nseg):
+            S_in.append(torch.matmul(F[s - 1], S_in[-1]) + Hs[s - 1])
+        return dr.chunk_fwd_varlen(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"],
+                                   torch.stack(S_in), cu_seqlens=cu_all, fg2=wl.rate_sqrt)
+
+    def single():
+        return dr.chunk_fwd(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"], x["S0"], fg2=wl.rate_sqrt)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            e0.record()
+            out = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1)
+            best = t if best is None else min(best, t)
+        return best, out
+
+    t_seg, (o_s, S_s) = timed(segmented)
+    t_one, (o_1, S_1) = timed(single)
+    rel = max(float((o_s - o_1).abs().max() / o_1.abs().max()), float((S_s[-1] - S_1[0]).abs().max() / S_1.abs().max()))
+    return t_seg, t_one, rel
+
+
 def time_decode(dr, torch, wl, steps):
     from gated_delta_rule_dr_amd.workloads import generate_decode
 
@@ -355,6 +411,9 @@ def main():
                     help="also time the gradient call (dr_chunk_bwd) on the main workload")
     ap.add_argument("--workload", default=PREFILL,
                     help="prefill workload of the main line (default: %(default)s)")
+    ap.add_argument("--segment-scan", type=int, default=0, metavar="P",
+                    help="also time the segment-parallel scan alternative with P segments per head on "
+                         "the main workload (composed from dr_chunk_fwd_varlen; design record only)")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="also run one plain elementwise copy of this many MiB (a known-size "
                          "reference for HBM byte counters)")
@@ -426,6 +485,11 @@ def main():
             extra[name] = prefill_record(w2, s2)
             torch.cuda.empty_cache()
         line["other_prefill"] = extra
+    if args.segment_scan:
+        t_seg, t_one, rel = time_segment_scan(dr, torch, wl, args.segment_scan)
+        line["segment_scan"] = {"segments": args.segment_scan, "ms": t_seg, "single_pass_ms": t_one,
+                                "max_rel_diff": rel}
+        torch.cuda.empty_cache()
     if args.backward:
         bsteps = max(2, args.steps // 10)
         bsec = time_backward(dr, torch, wl, bsteps, 1)

@@ -8,6 +8,15 @@
     python -m gated_delta_rule_dr_amd.profsummary mfma <counter_collection.csv> <kernel_stats.csv> \\
         <kernel-substring>[;...] <out.md> "<counter command>" "<trace command>"
 
+    python -m gated_delta_rule_dr_amd.profsummary l2path <out.md> <kernel-substring>[;...] \
+        "<command 1>" <counter_collection 1.csv> ["<command 2>" <counter_collection 2.csv> ...]
+
+``l2path`` tabulates the vector-memory counters of one dispatch per kernel (averaged over the
+dispatches profiled, summed over the device) from any number of counter runs, and derives the
+average L1-miss latency TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum (cycles), the L2 hit
+rate TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum) and the fraction of CU cycles the L1 stalled on
+pending L2 data, TCP_PENDING_STALL_CYCLES_sum / (GRBM_GUI_ACTIVE / 8 XCDs x 256 CUs).
+
 ``mfma`` reports, per kernel, the matrix-core counters of one dispatch (averaged over the
 dispatches profiled): SQ_INSTS_VALU_MFMA_MOPS_F16 (units of 512 flops), SQ_INSTS_MFMA,
 SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES and GRBM_GUI_ACTIVE, with the counted fp16 matrix
@@ -142,6 +151,32 @@ def mfma(counter_csv, stats_csv, patterns, out_md, cmd_counters, cmd_trace):
         f.write("\n".join(lines) + "\n")
 
 
+def l2path(out_md, patterns, *runs):
+    pats = patterns.split(";")
+    cmds, vals = [], {p: {} for p in pats}
+    for cmd, path in zip(runs[0::2], runs[1::2]):
+        cmds.append(cmd)
+        rows = _rows(path)
+        for p in pats:
+            for c in sorted({r["Counter_Name"] for r in rows if p in r["Kernel_Name"]}):
+                vals[p][c] = _kernel_avg(rows, c, p)[0]
+    counters = sorted({c for d in vals.values() for c in d})
+    lines = ["# Vector-memory path counters per dispatch", ""]
+    lines += [f"Run {i + 1}: `{c}`" for i, c in enumerate(cmds)]
+    lines += ["", "| kernel | " + " | ".join(counters) + " | L1-miss latency (cycles) | L2 hit rate | L1 pending-stall fraction |",
+              "|---|" + "---|" * (len(counters) + 3)]
+    for p in pats:
+        d = vals[p]
+        lat = d["TCP_TCC_READ_REQ_LATENCY_sum"] / d["TCP_TCC_READ_REQ_sum"] if "TCP_TCC_READ_REQ_sum" in d else float("nan")
+        hit = d["TCC_HIT_sum"] / (d["TCC_HIT_sum"] + d["TCC_MISS_sum"]) if "TCC_HIT_sum" in d else float("nan")
+        stall = (d["TCP_PENDING_STALL_CYCLES_sum"] / (d["GRBM_GUI_ACTIVE"] / 8 * 256)
+                 if "TCP_PENDING_STALL_CYCLES_sum" in d and "GRBM_GUI_ACTIVE" in d else float("nan"))
+        lines.append(f"| `{p}` | " + " | ".join(f"{d.get(c, float('nan')):.4g}" for c in counters) +
+                     f" | {lat:.0f} | {hit:.3f} | {stall:.3f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     mode = sys.argv[1]
     if mode == "trace":
@@ -150,5 +185,7 @@ if __name__ == "__main__":
         traffic(*sys.argv[2:12])
     elif mode == "mfma":
         mfma(*sys.argv[2:8])
+    elif mode == "l2path":
+        l2path(*sys.argv[2:])
     else:
         raise SystemExit(__doc__)
