@@ -15,6 +15,9 @@ pytestmark = pytest.mark.gpu
 
 TOL_F32 = 1e-5
 TOL_BF16 = 3e-3
+# bf16 o is an optional output format outside the 3e-3 contract (stated for fp32 o): rounding o to
+# bf16 alone costs up to 2^-9 relative, so its cases take the path's bar plus 2^-8
+TOL_BF16_O = TOL_BF16 + 2 ** -8
 
 
 @pytest.fixture(scope="module")
@@ -132,4 +135,4 @@ def test_fg2_bf16_output_wide_slices(dr):
     torch.cuda.synchronize()
     ro, rS = _oracle(inp)
     eo, eS = err_o(o.float(), ro), err_S(S, rS)
-    assert o.dtype == torch.bfloat16 and eo <= TOL_BF16 + 2.0 ** -8 and eS <= TOL_BF16, (eo, eS)
+    assert o.dtype == torch.bfloat16 and eo <= TOL_BF16_O and eS <= TOL_BF16, (eo, eS)

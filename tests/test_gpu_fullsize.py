@@ -5,8 +5,9 @@ generator); the fp64 oracle then recomputes a few sampled (b, h) pairs -- first,
 inside -- from the very same input values, over the whole sequence, and o and S_T of those
 pairs must agree to the bf16-path tolerance; every head is checked for finiteness.  The decode
 workload runs its full 256 x 32 heads for a number of steps and samples (n, h) pairs the same
-way, and the packed serving workload samples (sequence, head) pairs.  A linearity identity
-covers every head of the bench workload."""
+way, and one sequence (all its heads) follows the oracle over all 1,000 steps of the workload;
+the packed serving workload samples (sequence, head) pairs.  A linearity identity covers every
+head of a prefill workload."""
 import pytest
 import torch
 
@@ -114,6 +115,39 @@ def test_prefill_full_size_linearity_all_heads(dr):
     eo, eS = err_o(o2 / 2, o1), err_S(S2 / 2, S1)
     print(f"linearity: err_o={eo:.3e} err_S={eS:.3e}", flush=True)
     assert eo <= TOL_BF16 and eS <= TOL_BF16
+
+
+def test_decode_all_steps_one_sequence(dr):
+    # the decode workload's full length: all 1,000 steps on all 256 x 32 heads, as bench.py runs
+    # them; sequence 137 (all 32 heads) follows the oracle's token steps from the same inputs, o
+    # at every step and S after the last
+    from gated_delta_rule_dr_amd.workloads import generate_decode, workload
+
+    wl = workload("decode_kda_n256_h32")
+    n = 137
+    inp = generate_decode(wl, steps=wl.steps, device="cuda")
+    S = inp["S0"].clone()
+    o = torch.empty((wl.B, wl.H, wl.dv), device="cuda")
+    o_seq = torch.empty((wl.steps, wl.H, wl.dv), device="cuda")
+    for s in range(wl.steps):
+        g = lambda key: None if inp[key] is None else inp[key][s]
+        dr.decode_step(g("q"), g("k"), g("v"), g("log_decay"), g("erase"), g("write"), S=S, o=o)
+        o_seq[s].copy_(o[n])
+    torch.cuda.synchronize()
+    cut = lambda key: None if inp[key] is None else inp[key][:, n:n + 1].cpu()
+    seq = {key: cut(key) for key in ("q", "k", "v", "log_decay", "erase", "write")}
+    refS = inp["S0"][n:n + 1].double().cpu().numpy()
+    del inp
+    worst = 0.0
+    o_seq = o_seq.cpu()
+    for s in range(wl.steps):
+        g = lambda key: None if seq[key] is None else seq[key][s]
+        ro, refS = oracle_decode(g("q"), g("k"), g("v"), g("log_decay"), g("erase"), g("write"), refS)
+        worst = max(worst, err_o(o_seq[s][None, None], ro[:, None]))
+    eS = err_S(S[n:n + 1], refS)
+    print(f"decode sequence {n}, {wl.H} heads, {wl.steps} steps: max err_o={worst:.3e} err_S={eS:.3e}", flush=True)
+    assert worst <= TOL_F32 and eS <= TOL_F32
+    assert torch.isfinite(S).all()
 
 
 def test_decode_full_size_sampled_pairs(dr):

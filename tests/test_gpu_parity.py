@@ -1,7 +1,10 @@
 """GPU parity: libdr (through the C ABI) against the fp64 oracle on identical seeded inputs.
 
 Tolerances (normwise per (b, h), tests/metrics.py): 1e-5 where q/k/v are fp32 or where the
-fp32 token-by-token kernel runs, 3e-3 for the bf16 matrix-core chunk path."""
+fp32 token-by-token kernel runs, 3e-3 for the bf16 matrix-core chunk path.  bf16 o is an optional
+output format outside that contract: rounding o to bf16 alone costs up to 2^-9 relative, so those
+cases take TOL_BF16_O = 3e-3 + 2^-8 (chunk path) or 2^-8 (token path), and fp32 o is the format
+the 3e-3 bar is stated for."""
 import numpy as np
 import pytest
 import torch
@@ -14,6 +17,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_F32 = 1e-5
 TOL_BF16 = 3e-3
+TOL_BF16_O = TOL_BF16 + 2 ** -8  # bf16 o: the path's bar plus the output format's own rounding
 
 
 @pytest.fixture(scope="module")
@@ -120,7 +124,7 @@ def test_bf16_output_wide_slices(dr):
     o, S = _run(dr, inp, o_dtype=torch.bfloat16)
     ro, rS = _oracle(inp)
     assert o.dtype == torch.bfloat16
-    assert err_o(o.float(), ro) <= TOL_BF16 + 2 ** -8 and err_S(S, rS) <= TOL_BF16
+    assert err_o(o.float(), ro) <= TOL_BF16_O and err_S(S, rS) <= TOL_BF16
 
 
 def test_chunk_matches_token_kernel(dr):
@@ -158,7 +162,7 @@ def test_bf16_output_chunk_path(dr):
     o, S = _run(dr, inp, o_dtype=torch.bfloat16)
     ro, rS = _oracle(inp)
     assert o.dtype == torch.bfloat16
-    assert err_o(o.float(), ro) <= TOL_BF16 + 2 ** -8 and err_S(S, rS) <= TOL_BF16
+    assert err_o(o.float(), ro) <= TOL_BF16_O and err_S(S, rS) <= TOL_BF16
 
 
 def test_in_place_state_carry(dr):

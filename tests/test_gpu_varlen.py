@@ -14,6 +14,9 @@ pytestmark = pytest.mark.gpu
 
 TOL_F32 = 1e-5
 TOL_BF16 = 3e-3
+# bf16 o is an optional output format outside the 3e-3 contract (stated for fp32 o): rounding o to
+# bf16 alone costs up to 2^-9 relative, so its cases take the path's bar plus 2^-8
+TOL_BF16_O = TOL_BF16 + 2 ** -8
 
 
 @pytest.fixture(scope="module")
@@ -196,4 +199,4 @@ def test_varlen_bf16_output_and_determinism(dr):
     assert o1.dtype == torch.bfloat16 and torch.equal(o1, o2) and torch.equal(S1, S2)
     ro, rS = _oracle(inp)
     eo, eS = _errs_per_sequence(o1.float(), S1, ro, rS, inp["cu_seqlens"].numpy())
-    assert eo <= TOL_BF16 + 2.0 ** -8 and eS <= TOL_BF16, (eo, eS)
+    assert eo <= TOL_BF16_O and eS <= TOL_BF16, (eo, eS)
