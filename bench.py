@@ -104,7 +104,7 @@ def backward_bytes(wl) -> int:
     return th * per_tok + (3 * state if wl.s0_std > 0 else state)
 
 
-def time_backward(dr, torch, wl, steps, warmup):
+def time_backward(dr, torch, wl, steps, warmup, chunk=64):
     from gated_delta_rule_dr_amd.workloads import generate
 
     x = generate(wl, device="cuda")
@@ -112,7 +112,7 @@ def time_backward(dr, torch, wl, steps, warmup):
     dO = torch.randn((wl.B, wl.T, wl.H, wl.dv), generator=g, device="cuda")
     dST = torch.randn((wl.B, wl.H, wl.dk, wl.dv), generator=g, device="cuda")
     call = lambda: dr.chunk_bwd(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"], x["S0"],
-                                dO=dO, dS_T=dST)
+                                dO=dO, dS_T=dST, chunk=chunk)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -494,10 +494,16 @@ def main():
         bsteps = max(2, args.steps // 10)
         bsec = time_backward(dr, torch, wl, bsteps, 1)
         bbytes = backward_bytes(wl)
+        chunked = wl.qkv_dtype == "bf16" and wl.dk == 128 and wl.dv == 128 and not wl.seq_median
         line["backward"] = {"workload": wl.name, "calls": bsteps, "ms": bsec * 1e3,
                             "tokens_per_s": wl.token_heads / bsec, "hbm_frac": bbytes / bsec / 1e9 / HBM_PEAK_GBS,
                             "bytes_per_call": bbytes,
-                            "kernel": "dr_chunk_bwd = bwd_token_kernel + bwd_reduce_kernel (fp32 token adjoint)"}
+                            "kernel": ("dr_chunk_bwd = chunked forward with chunk-start states + adjoint scan + "
+                                       "bwd_chunk_kernel + bwd_reduce_kernel") if chunked else
+                                      "dr_chunk_bwd = bwd_token_kernel + bwd_reduce_kernel (fp32 token adjoint)"}
+        if chunked:
+            tsec = time_backward(dr, torch, wl, 2, 1, chunk=1)
+            line["backward"]["token_adjoint_ms"] = tsec * 1e3
         if not args.no_cpu:
             line["backward"]["cpu_baseline"] = cpu_baseline_backward(wl, max(64, args.cpu_tokens // 64))
         torch.cuda.empty_cache()

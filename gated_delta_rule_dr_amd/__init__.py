@@ -225,7 +225,7 @@ def chunk_fwd_varlen(q, k, v, log_decay, erase, write=None, S0=None, *, cu_seqle
 
 
 def chunk_bwd(q, k, v, log_decay, erase, write=None, S0=None, *, dO, dS_T=None, need_dS0=True, fg2=False,
-              cu_seqlens=None):
+              cu_seqlens=None, chunk=64):
     """Gradients of sum(o * dO) + sum(S_T * dS_T) with respect to q, k, v, the gates and S0.
 
     Inputs as ``chunk_fwd`` (or, with ``cu_seqlens``, as ``chunk_fwd_varlen``: [1, T, ...] packed
@@ -233,7 +233,8 @@ def chunk_bwd(q, k, v, log_decay, erase, write=None, S0=None, *, dO, dS_T=None, 
     Returns a dict of fp32 tensors dq, dk, dv, dlog_decay, derase, dwrite (None when ``write``
     is None: derase then holds the shared gate's whole gradient) and dS0 (None unless
     ``need_dS0``), each in its input's layout.  ``fg2=True``: ``erase`` is FG2's rate beta, and
-    derase its gradient."""
+    derase its gradient.  ``chunk=1`` takes the fp32 token adjoint wherever the chunk path would
+    run (bf16 q/k/v, dk == dv == 128, a dense batch)."""
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(name, t, (torch.float32, torch.bfloat16), dev)
@@ -255,7 +256,7 @@ def chunk_bwd(q, k, v, log_decay, erase, write=None, S0=None, *, dO, dS_T=None, 
         if B != 1 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
             raise ValueError("packed sequences: q is [1, T, H, dk] and cu_seqlens holds N + 1 offsets")
         nstate = cu_seqlens.numel() - 1
-    desc = _desc(B, T, H, dk, dv, 0, q.dtype, torch.float32, log_decay, erase, write, (B, T, H), fg2)
+    desc = _desc(B, T, H, dk, dv, chunk, q.dtype, torch.float32, log_decay, erase, write, (B, T, H), fg2)
     f32 = dict(dtype=torch.float32, device=dev)
     out = dict(dq=torch.empty((B, T, H, dk), **f32), dk=torch.empty((B, T, H, dk), **f32),
                dv=torch.empty((B, T, H, dv), **f32), dlog_decay=torch.empty(log_decay.shape, **f32),

@@ -88,6 +88,13 @@ __device__ __forceinline__ half8 cvt8(const float* x) {
   return h;
 }
 
+__device__ __forceinline__ half4v cvt4(f32x4 a) {
+  half4v h;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) h[r] = (_Float16)a[r];
+  return h;
+}
+
 __device__ __forceinline__ void bf16x8_to_f32(uint4 u, float* f) {
   f[0] = __uint_as_float(u.x << 16); f[1] = __uint_as_float(u.x & 0xffff0000u);
   f[2] = __uint_as_float(u.y << 16); f[3] = __uint_as_float(u.y & 0xffff0000u);
@@ -276,6 +283,17 @@ __device__ void pass_state(const Problem& p, int bh, int j0, int ncols) {
     const int64_t x = (int64_t(bh) * D + d) * D + j;
     p.S_T[x] = p.S0 ? p.S0[x] : 0.f;
   }
+}
+
+// This wave's part of a scan's fp32 state tiles (rows 16 w + 4 lg + r, columns j0 + 16 ct + l16)
+// into the [dk][dv] matrix at dst.
+template <int NCT>
+__device__ __forceinline__ void store_state(float* dst, int j0, const f32x4 (&S)[NCT]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[(16 * wave + 4 * lg + r) * D + j0 + 16 * ct + l16] = S[ct][r];
 }
 
 // One chunk of prep work, from its work-item index: a dense batch walks (b, h, chunk) with
@@ -1136,7 +1154,8 @@ struct Flag {
 // Scan, general gates (separate erase and write gates): the packet (too large for two LDS
 // buffer sets) is staged through registers one or two chunks ahead.  WCH: per-channel write
 // gate.
-template <bool DCH, bool GEN, bool WCH, int DVS>
+// CKPT: also store the state at the start of every chunk (p.ck_S, for the gradients).
+template <bool DCH, bool GEN, bool WCH, int DVS, bool CKPT = false>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, const char* __restrict__ ws) {
   static_assert(GEN, "symmetric gates use chunk_scan_sym_kernel");
   using PK = Packet<DCH, GEN>;
@@ -1264,6 +1283,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   // conservative.
   auto step = [&](auto tail, int c, Pref& P) {
     constexpr bool TAIL = decltype(tail)::value;
+    if constexpr (CKPT) store_state(p.ck_S + (sq.pkt0 + c) * D * D, j0, S);
     // ---- L: the chunk's packet, value slice and S~^T into LDS ------------------------------
     // the LDS tiles keep the packet's layout: 16-byte units copy straight across
 #pragma unroll
@@ -1494,7 +1514,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
 // chunk c is computed from the first; each chunk starts with one wait for its own copies.
 // ------------------------------------------------------------------------------------------
 // FG2: the values are FG2's v~ = sqrt(beta) v, fp16 in the packet, instead of the bf16 input.
-template <bool DCH, int DVS, bool FG2 = false>
+template <bool DCH, int DVS, bool FG2 = false, bool CKPT = false>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p, const char* __restrict__ ws) {
   using PK = Packet<DCH, false, FG2>;
   auto vval = [](uint16_t u) { return FG2 ? float(__builtin_bit_cast(_Float16, u)) : bf16_to_f32(u); };
@@ -1740,6 +1760,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     const Set X = set_of(Flag<B1>()), Y = set_of(Flag<!B1>());
     const int cn = c + 1 < nchunks ? c + 1 : c;  // chunk whose copies this step issues
     vm_wait<kB2min + kB3 + (kEarly ? kB1b : 0)>();  // batch 1 of this chunk, older stores
+    // (checkpoint stores only make the later partial waits stricter: they wait for these too)
+    if constexpr (CKPT) store_state(p.ck_S + (sq.pkt0 + c) * D * D, j0, S);
     if constexpr (!kStage) {
       if (c > 0 && o_wave) store_out(c - 1, false);
     } else {
@@ -2009,20 +2031,260 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Adjoint scan (gradients): the chunks of one (b, h, value slice) from the last, carrying the
+// state's adjoint G = dL/dS at the end of the chunk in fp32 registers like the forward state.
+// Reversing the chunk form above (L = sum(o * dO) + sum(S_T * dS_T)), one chunk maps G to the
+// adjoint at its start,
+//   X1 = W1^T dO + E G~,  Z = -B T^T X1,  G <- Diag(e^{g_C}) G + Q+^T dO + K+^T Z,
+// with W1 = A_qk, E = K^end, B = Diag(beta) for symmetric gates (X1 is delta's adjoint, Z the
+// adjoint of K+ S) and W1 = A_qu, E = U^end, B = I for general gates (X1 = -M's adjoint).  With a
+// per-head decay the packet holds plain k and q: K^end = Diag(e^{g_C - g}) k scales the rows of
+// k G~, and Q+ = Diag(e^{g}) q, K+ = Diag(e^{g}) k put e^{g_t} on dO's and Z's rows.  The
+// adjoint at the end of every chunk goes to p.ck_G (the chunk-parallel adjoint of the token
+// loop starts there), and the one at the start of the sequence is dS0.  Eight waves, register
+// staging one chunk ahead, four barriers per chunk.
+// ------------------------------------------------------------------------------------------
+// frag_ts of a lower-triangular matrix held in LDS as eight 16 x 32 blocks (block 2 I + H, layout
+// as tri_in): lane 16 g + l16 receives A[r0 + 8 g + 0..7][c0 + l16] (c0 % 16 == 0, r0 % 8 == 0).
+__device__ __forceinline__ half8 frag_tri_t(const _Float16* base, int c0, int r0, int lane) {
+  const int m = lane & 15;
+  const int r = r0 + 8 * (lane >> 4) + (m >> 2), c = c0 + 4 * (m & 3);
+  const half4v lo = ld_tr16(base + (2 * (r >> 4) + (c >> 5)) * 512 + tri_in(r, c));
+  const half4v hi = ld_tr16(base + (2 * ((r + 4) >> 4) + (c >> 5)) * 512 + tri_in(r + 4, c));
+  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <bool DCH, bool GEN, bool FG2, int DVS>
+__global__ __launch_bounds__(kScanThreads) void chunk_adjoint_scan_kernel(Problem p, const char* __restrict__ ws,
+                                                                          const float* __restrict__ dO,
+                                                                          const float* __restrict__ dS_T,
+                                                                          float* __restrict__ dS0) {
+  using PK = Packet<DCH, GEN, FG2>;
+  constexpr bool SCAL = !DCH && !GEN;
+  constexpr int NCT = DVS / 16;
+  constexpr int VPT = DVS / 8;       // dO columns per thread in its load
+  constexpr int W1 = GEN ? 3 : 1;    // packet matrix of W1
+  // LDS: operand tiles (the packet's swizzled layout), T and W1 as eight 16 x 32 blocks each,
+  // the gate vector, and the workgroup's own G~^T, dO^T (and Diag(e^g) dO^T), X1^T, Z^T
+  __shared__ __attribute__((aligned(16))) _Float16 QP[C * D];
+  __shared__ __attribute__((aligned(16))) _Float16 KP[C * D];
+  __shared__ __attribute__((aligned(16))) _Float16 EP[SCAL ? 8 : C * D];
+  __shared__ __attribute__((aligned(16))) _Float16 TM[2 * 8 * 512];  // T, then W1
+  __shared__ __attribute__((aligned(16))) float GV[PK::ngate];
+  __shared__ __attribute__((aligned(16))) _Float16 GT[DVS * D];
+  __shared__ __attribute__((aligned(16))) _Float16 DOT[DVS * C];
+  __shared__ __attribute__((aligned(16))) _Float16 DOG[SCAL ? DVS * C : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 X1T[DVS * C];
+  __shared__ __attribute__((aligned(16))) _Float16 ZT[DVS * C];
+  const _Float16* const EE = SCAL ? KP : EP;  // E's rows: K^end (or k, scaled), U^end
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int H = p.H;
+  const WgRef wg = wg_ref(p);
+  const int bh = wg.bh, h = bh % H;
+  const int j0 = wg.slice * DVS;
+  const SeqRef sq = seq_ref(p, bh, h);
+  const int T = sq.len;
+  const int nchunks = sq.nch;
+  const gptr<const char> pbase = opaque_gptr(ws) + sq.pkt0 * PK::bytes;
+  const gptr<const float> dOin = opaque_gptr(dO);
+
+  // G: wave w owns rows [16 w, 16 w + 16) x the DVS columns (lane: column 16 ct + l16, rows
+  // 16 w + 4 lg + r)
+  f32x4 G[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int d = 16 * wave + 4 * lg + r;
+      G[ct][r] = dS_T ? dS_T[(int64_t(bh) * D + d) * D + j0 + 16 * ct + l16] : 0.f;
+    }
+  if (nchunks == 0) {
+    if (dS0) store_state(dS0 + int64_t(bh) * D * D, j0, G);
+    return;
+  }
+  // zero upper blocks (0,1) and (1,1) of both matrices, never copied
+  if (tid < 256) *reinterpret_cast<uint4*>(TM + 4096 * (tid >> 7) + 512 * (1 + 2 * ((tid >> 6) & 1)) + 8 * lane) =
+      make_uint4(0, 0, 0, 0);
+
+  auto tok = [&](int t) { return (sq.tok0 + t) * H + h; };
+  const int vtok = tid >> 3, vcol = (tid & 7) * VPT;  // dO slice: token tid / 8
+  const int64_t tstride = int64_t(C) * H * D;
+  const int64_t d_off = tok(vtok) * D + j0 + vcol, d_last = tok(T - 1) * D + j0 + vcol;
+
+  struct Pref {
+    uint4 tl[SCAL ? 4 : 6];  // Q+, K+ (, E) units tid and tid + 512
+    uint4 mr[2];             // stored blocks of T and W1: units tid, tid + 512 (< 768)
+    float4 gv;               // gate vector floats 4 tid .. (tid < ngate / 4)
+    float dv[VPT];
+  };
+  auto load = [&](Pref& P, int c) {
+    const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      P.tl[i] = ldb16(pk, PK::qp + 16 * (tid + kScanThreads * i));
+      P.tl[2 + i] = ldb16(pk, PK::kp + 16 * (tid + kScanThreads * i));
+      if constexpr (!SCAL) P.tl[4 + i] = ldb16(pk, (GEN ? PK::umt : PK::kmt) + 16 * (tid + kScanThreads * i));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int u = tid + kScanThreads * j, m = u / 384, k = (u % 384) / 64;
+      if (u < 768) P.mr[j] = ldb16(pk, PK::mat + (m ? W1 : 0) * PK::matb + 1024 * k + 16 * (u % 64));
+    }
+    if (tid < PK::ngate / 4) P.gv = ldf16(pk, PK::gate + 16 * tid);
+    const bool ok = c * C + vtok < T;
+    const int64_t e = ok ? d_off + c * tstride : d_last;
+#pragma unroll
+    for (int i = 0; i < VPT; i += 2) {
+      const f32x2 x = *(gptr<const f32x2>)(dOin + e + i);
+      P.dv[i] = ok ? x.x : 0.f;
+      P.dv[i + 1] = ok ? x.y : 0.f;
+    }
+  };
+
+  // scale of the rows of Z (and of E G~ with a per-head decay): the chunk's per-row factors
+  const int zi = 16 * (wave & 3) + 4 * lg;  // rows of this wave's X1 / Z tile
+  const int zct = NCT == 2 ? wave >> 2 : 0;
+  const bool zwave = NCT == 2 || wave < 4;
+
+  auto step = [&](int c, Pref& P) {
+    if (p.ck_G) store_state(p.ck_G + (sq.pkt0 + c) * D * D, j0, G);
+    // ---- L: the chunk's packet, dO^T and G~^T into LDS ------------------------------------
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + kScanThreads * i;
+      *reinterpret_cast<uint4*>(QP + 8 * u) = P.tl[i];
+      *reinterpret_cast<uint4*>(KP + 8 * u) = P.tl[2 + i];
+      if constexpr (!SCAL) *reinterpret_cast<uint4*>(EP + 8 * u) = P.tl[4 + i];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int u = tid + kScanThreads * j, m = u / 384, k = (u % 384) / 64;
+      const int lb = k < 2 ? 2 * k : k + 2;
+      if (u < 768) *reinterpret_cast<uint4*>(TM + 4096 * m + 512 * lb + 8 * (u % 64)) = P.mr[j];
+    }
+    if (tid < PK::ngate / 4) *reinterpret_cast<float4*>(GV + 4 * tid) = P.gv;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) DOT[swz<8>(vcol + i, vtok)] = (_Float16)P.dv[i];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+      *reinterpret_cast<half4v*>(GT + swz<16>(16 * ct + l16, 16 * wave + 4 * lg)) = cvt4(G[ct]);
+    lds_barrier();
+    if constexpr (SCAL) {  // Diag(e^{g}) dO^T for Q+^T dO
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) DOG[swz<8>(vcol + i, vtok)] = (_Float16)(P.dv[i] * GV[GV_FP + vtok]);
+    }
+    const int cn = c > 0 ? c - 1 : 0;
+    load(P, cn);
+
+    // ---- X1 = W1^T dO + E G~, stored transposed --------------------------------------------
+    if (zwave) {
+      const int I = wave & 3;
+      f32x4 xa = {0.f, 0.f, 0.f, 0.f}, xb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        xa = mfma16x16x32(frag_tri_t(TM + 4096, 16 * I, 32 * ks, lane), frag_s<8>(DOT, 16 * zct, 32 * ks, lane), xa);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        xb = mfma16x16x32(frag_s<16>(EE, 16 * I, 32 * ks, lane), frag_s<16>(GT, 16 * zct, 32 * ks, lane), xb);
+      half4v hv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float eb = SCAL ? GV[GV_FM + zi + r] : 1.f;  // K^end = Diag(e^{g_C - g}) k
+        hv[r] = (_Float16)(fmaf(eb, xb[r], xa[r]));
+      }
+      *reinterpret_cast<half4v*>(X1T + swz<8>(16 * zct + l16, zi)) = hv;
+    }
+    lds_barrier();
+    // ---- Z = -B T^T X1 (per-head decay: times Diag(e^{g})), stored transposed ---------------
+    if (zwave) {
+      const int I = wave & 3;
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        z = mfma16x16x32(frag_tri_t(TM, 16 * I, 32 * ks, lane), frag_s<8>(X1T, 16 * zct, 32 * ks, lane), z);
+      half4v hv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float f = GEN ? -1.f : -GV[GV_BETA + zi + r];
+        if constexpr (SCAL) f *= GV[GV_FP + zi + r];
+        hv[r] = (_Float16)(f * z[r]);
+      }
+      *reinterpret_cast<half4v*>(ZT + swz<8>(16 * zct + l16, zi)) = hv;
+    }
+    lds_barrier();
+    // ---- G <- Diag(e^{g_C}) G + Q+^T dO + K+^T Z (this wave's rows) -------------------------
+    {
+      f32x4 acc[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const half8 aq = frag_ts(QP, 16 * wave, 32 * ks, lane), ak = frag_ts(KP, 16 * wave, 32 * ks, lane);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          acc[ct] = mfma16x16x32(aq, frag_s<8>(SCAL ? DOG : DOT, 16 * ct, 32 * ks, lane), acc[ct]);
+          acc[ct] = mfma16x16x32(ak, frag_s<8>(ZT, 16 * ct, 32 * ks, lane), acc[ct]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float fC = SCAL ? GV[GV_SC + 1] : GV[GV_FC + 16 * wave + 4 * lg + r];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) G[ct][r] = fmaf(fC, G[ct][r], acc[ct][r]);
+      }
+    }
+    lds_barrier();
+  };
+
+  Pref PA;
+  load(PA, nchunks - 1);
+  for (int c = nchunks - 1; c >= 0; --c) step(c, PA);
+  if (dS0) store_state(dS0 + int64_t(bh) * D * D, j0, G);
+}
+
+template <bool DCH, bool GEN, bool FG2>
+hipError_t launch_adjoint_scan(const Problem& p, const char* ws, const float* dO, const float* dS_T, float* dS0,
+                               hipStream_t stream) {
+  const int64_t bh = int64_t(p.B) * p.H;
+  if (bh >= 64) {
+    dim3 grid(unsigned(bh), unsigned(D / 32));
+    hipLaunchKernelGGL((chunk_adjoint_scan_kernel<DCH, GEN, FG2, 32>), grid, dim3(kScanThreads), 0, stream, p, ws,
+                       dO, dS_T, dS0);
+  } else {
+    dim3 grid(unsigned(bh), unsigned(D / 16));
+    hipLaunchKernelGGL((chunk_adjoint_scan_kernel<DCH, GEN, FG2, 16>), grid, dim3(kScanThreads), 0, stream, p, ws,
+                       dO, dS_T, dS0);
+  }
+  return hipGetLastError();
+}
+
 template <bool DCH, int DVS, bool FG2>
 hipError_t launch_scan_sym(const Problem& p, const char* ws, hipStream_t stream) {
   dim3 grid(unsigned(p.B * p.H), unsigned(D / DVS));
-  hipLaunchKernelGGL((chunk_scan_sym_kernel<DCH, DVS, FG2>), grid, dim3(kScanThreads), 0, stream, p, ws);
+  if (p.ck_S)
+    hipLaunchKernelGGL((chunk_scan_sym_kernel<DCH, DVS, FG2, true>), grid, dim3(kScanThreads), 0, stream, p, ws);
+  else
+    hipLaunchKernelGGL((chunk_scan_sym_kernel<DCH, DVS, FG2>), grid, dim3(kScanThreads), 0, stream, p, ws);
   return hipGetLastError();
 }
 
 template <bool DCH, int DVS>
 hipError_t launch_scan_gen(const Problem& p, const char* ws, hipStream_t stream) {
   dim3 grid(unsigned(p.B * p.H), unsigned(D / DVS));
-  if (p.write_channel)
+  if (p.ck_S) {
+    if (p.write_channel)
+      hipLaunchKernelGGL((chunk_scan_kernel<DCH, true, true, DVS, true>), grid, dim3(kScanThreads), 0, stream, p, ws);
+    else
+      hipLaunchKernelGGL((chunk_scan_kernel<DCH, true, false, DVS, true>), grid, dim3(kScanThreads), 0, stream, p, ws);
+  } else if (p.write_channel) {
     hipLaunchKernelGGL((chunk_scan_kernel<DCH, true, true, DVS>), grid, dim3(kScanThreads), 0, stream, p, ws);
-  else
+  } else {
     hipLaunchKernelGGL((chunk_scan_kernel<DCH, true, false, DVS>), grid, dim3(kScanThreads), 0, stream, p, ws);
+  }
   return hipGetLastError();
 }
 
@@ -2096,6 +2358,19 @@ hipError_t launch_chunk128_varlen(Problem p, const int* cu, void* workspace, hip
   p.nchunks_total = total;
   p.order = order;
   return launch_chunk128(p, workspace, stream);
+}
+
+hipError_t launch_chunk128_adjoint(const Problem& p, const void* workspace, const float* dO, const float* dS_T,
+                                   float* dS0, hipStream_t stream) {
+  const char* ws = static_cast<const char*>(workspace);
+  if (p.rate_sqrt)
+    return p.decay_channel ? launch_adjoint_scan<true, false, true>(p, ws, dO, dS_T, dS0, stream)
+                           : launch_adjoint_scan<false, false, true>(p, ws, dO, dS_T, dS0, stream);
+  if (p.decay_channel)
+    return p.symmetric ? launch_adjoint_scan<true, false, false>(p, ws, dO, dS_T, dS0, stream)
+                       : launch_adjoint_scan<true, true, false>(p, ws, dO, dS_T, dS0, stream);
+  return p.symmetric ? launch_adjoint_scan<false, false, false>(p, ws, dO, dS_T, dS0, stream)
+                     : launch_adjoint_scan<false, true, false>(p, ws, dO, dS_T, dS0, stream);
 }
 
 hipError_t launch_chunk128(const Problem& p, void* workspace, hipStream_t stream) {

@@ -358,7 +358,7 @@ size_t dr_chunk_bwd_workspace_bytes(const dr_desc* desc) {
   if (check_desc(desc, false, &ex) != DR_OK || desc->T == 0) return 0;
   dr::Problem p = make_problem(desc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                nullptr);
-  return dr::bwd_workspace_bytes(p);
+  return uses_chunk128(desc) ? dr::bwd_chunked_workspace_bytes(p) : dr::bwd_workspace_bytes(p);
 }
 
 int dr_chunk_bwd(const dr_desc* d, const void* q, const void* k, const void* v, const float* log_decay,
@@ -489,6 +489,7 @@ int chunk_bwd_common(const dr_desc* d, const int32_t* cu_seqlens, int32_t nseq, 
     p.B = nseq;
     return launched(dr::launch_bwd_varlen(p, cu_seqlens, g, workspace, s));
   }
+  if (uses_chunk128(d)) return launched(dr::launch_bwd_chunked(p, g, workspace, s));
   return launched(dr::launch_bwd(p, g, workspace, s));
 }
 

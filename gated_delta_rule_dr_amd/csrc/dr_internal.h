@@ -36,6 +36,10 @@ struct Problem {
                                        //  of its sequence}; the packet of head h adds h * chunks
   const int* nchunks_total = nullptr;  // number of entries in `chunks`
   const int* order = nullptr;          // [B] sequences, longest first (scan workgroup order)
+  // Gradients through the chunk path: the state at the start of every chunk (forward scans) and
+  // its adjoint at the end of every chunk (adjoint scan), fp32 [packet][dk][dv]; null otherwise.
+  float* ck_S = nullptr;
+  float* ck_G = nullptr;
 };
 
 // Sequence tables of a packed batch (one workgroup): from nseq + 1 device offsets `cu` over T
@@ -60,6 +64,12 @@ hipError_t launch_decode128(const Problem& p, hipStream_t stream);
 // state-independent factors per chunk of every (b, h).
 size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric, bool decay_channel, bool rate_sqrt);
 hipError_t launch_chunk128(const Problem& p, void* workspace, hipStream_t stream);
+
+// The adjoint scan over the packets that launch_chunk128 left in `workspace` (same problem): the
+// state's adjoint at the end of every chunk into p.ck_G and at the start of the sequence into
+// dS0 (when not null), from dO [B,T,H,dv] and dS_T (null: zero).
+hipError_t launch_chunk128_adjoint(const Problem& p, const void* workspace, const float* dO, const float* dS_T,
+                                   float* dS0, hipStream_t stream);
 
 // The same over p.B packed sequences delimited by the device offsets `cu` (p.B + 1 of them):
 // the workspace holds the packets of at most varlen_max_chunks(p.B, p.T) chunks per head,
@@ -87,6 +97,11 @@ struct BwdArgs {
 };
 size_t bwd_workspace_bytes(const Problem& p);
 hipError_t launch_bwd(const Problem& p, const BwdArgs& g, void* workspace, hipStream_t stream);
+// Gradients through the matrix-core chunk path (bf16 q/k/v, dk == dv == 128, a dense batch): the
+// chunked forward stores the state at every chunk start, the adjoint scan the state's adjoint
+// at every chunk end, and the adjoint of the token loop then runs every chunk in parallel.
+size_t bwd_chunked_workspace_bytes(const Problem& p);
+hipError_t launch_bwd_chunked(const Problem& p, const BwdArgs& g, void* workspace, hipStream_t stream);
 // The same over p.B packed sequences delimited by the device offsets `cu` (p.T packed tokens).
 size_t bwd_varlen_workspace_bytes(const Problem& p);
 hipError_t launch_bwd_varlen(Problem p, const int* cu, const BwdArgs& g, void* workspace, hipStream_t stream);

@@ -318,3 +318,204 @@ def kernel_emulation(q, k, v, log_decay, erase, write=None, S0=None, scheme="saf
     if return_flags:
         return o, S, flags
     return o, S
+
+
+# ------------------------------------------------------------------------------------------
+# Chunk form of the gradients (the matrix-core backward's algebra), fp64.
+#
+# For one chunk, with S its incoming state, G the state's adjoint at its end and dO its output
+# adjoint, the general (non-symmetric) chunk form above gives, by reverse mode through
+#   M = (I + A_ku)^{-1} (K+ S + A_kk Vt),  O = Q+ S + A_qk Vt - A_qu M,
+#   S_C = Diag(e^{g_C}) S + Kend^T Vt - Uend^T M:
+#   Z     = -(I + A_ku)^{-T} (A_qu^T dO + Uend G)       (the adjoint of K+ S + A_kk Vt)
+#   dK+   = Z S^T,  dQ+ = dO S^T,  dKend = Vt G^T,  dUend = -M G^T
+#   dA_kk = strict(Z Vt^T), dA_ku = -strict(Z M^T), dA_qk = lower(dO Vt^T), dA_qu = -lower(dO M^T)
+#   dVt   = A_kk^T Z + A_qk^T dO + Kend G,  dGamma = rowsum(S * G)
+#   S's adjoint at the chunk start: Diag(e^{g_C}) G + Q+^T dO + K+^T Z   (the adjoint scan)
+# and, through the Gram matrices A_xy[t, i] = sum_d x_t,d y_i,d e^{g_t,d - g_i,d}:
+#   dx_t = sum_i dA[t, i] y_i e^{g_t - g_i},  dy_i = sum_t dA[t, i] x_t e^{g_t - g_i},
+#   and the cumulative log-decay g takes x * dx on the row side and -y * dy on the column side.
+# Every decayed operand adds its own share to g's adjoint (K+ = k e^{g}: + K+ * dK+; Kend =
+# k e^{g_C - g}: - Kend * dKend at t and + at C), e^{g_C} adds e^{g_C} dGamma at C, and the
+# log-decay's adjoint is the reverse prefix sum of g's over the chunk.
+# With FG2's rate (u = k~, unit gates, T symmetric) A_ku = A_kk, A_qu = A_qk and Uend = Kend, so
+# their adjoints merge: dA_kk = strict(Z Delta^T), dA_qk = lower(dO Delta^T), dKend = Delta G^T
+# with Delta = Vt - M, and dVt = -Z.
+# ------------------------------------------------------------------------------------------
+def _masked_exp_diff(g, strict):
+    """E[t, i, d] = e^{g_t,d - g_i,d} on the (strict) lower triangle, 0 elsewhere."""
+    C = g.shape[0]
+    mask = np.tril(np.ones((C, C), dtype=bool), -1 if strict else 0)
+    diff = np.where(mask[:, :, None], g[:, None, :] - g[None, :, :], -np.inf)
+    return np.exp(diff)
+
+
+def gram_bwd_exact(dA, x, y, g, strict):
+    """(dx, dy) of A = mask(x_t . y_i e^{g_t - g_i}) for the adjoint dA, element by element."""
+    W = dA[:, :, None] * _masked_exp_diff(g, strict)
+    return np.einsum("tid,id->td", W, y), np.einsum("tid,td->id", W, x)
+
+
+def gram_bwd_blocked(dA, x, y, g, strict, blk=16, rnd=lambda a: a):
+    """The same in the kernel's arrangement: diagonal blk x blk blocks element by element; an
+    off-diagonal block (I, J), J < I, as one product dA_IJ Y~_J (and dA_IJ^T X~_I) of operands
+    referenced inside their own block -- Y~ = y e^{g_r - g} with r the last token of J, X~ =
+    x e^{g - g_s} with s the last token before I -- scaled by e^{g_s - g_r} per channel and by the
+    row factor (e^{g_t - g_s} or e^{g_r - g_i}).  Every factor is e^{x} with x <= 0.  ``rnd``
+    rounds the product operands (fp16 in the kernel)."""
+    C = g.shape[0]
+    nb = C // blk
+    dx, dy = np.zeros_like(x), np.zeros_like(y)
+    for b in range(nb):
+        sl = slice(blk * b, blk * (b + 1))
+        a, c = gram_bwd_exact(dA[sl, sl], x[sl], y[sl], g[sl], strict)
+        dx[sl] += a
+        dy[sl] += c
+    dAr = rnd(dA)
+    for I in range(1, nb):
+        si = slice(blk * I, blk * (I + 1))
+        s = blk * I - 1
+        Xt = rnd(x[si] * np.exp(g[si] - g[s]))
+        for J in range(I):
+            sj = slice(blk * J, blk * (J + 1))
+            r = blk * J + blk - 1
+            F = np.exp(g[s] - g[r])
+            Yt = rnd(y[sj] * np.exp(g[r] - g[sj]))
+            dx[si] += np.exp(g[si] - g[s]) * F * (dAr[si, sj] @ Yt)
+            dy[sj] += np.exp(g[r] - g[sj]) * F * (dAr[si, sj].T @ Xt)
+    return dx, dy
+
+
+def chunk_backward(q, k, v, log_decay, erase, write=None, S0=None, dO=None, dS_T=None, fg2=False,
+                   blocked=False, fp16=False):
+    """Gradients of one (b, h) through the chunk form (chunks of 64, the last one padded with
+    zero inputs and unit decay, as the kernels do), in fp64: the forward stores every chunk's
+    incoming state S and reads M (FG2: Delta = T (Vt - K+ S)), the adjoint scan every chunk's
+    end adjoint G and Z, and each chunk's gradients follow from those alone.  Arguments as
+    ``chunk_forward`` (``fg2``: erase is FG2's per-channel rate); ``blocked`` takes the kernel's
+    block arrangement of the Gram adjoints, ``fp16`` rounds every matrix operand to fp16 where
+    the kernels do.  Returns a dict like ``oracle.recurrence_bwd`` for one (b, h): dq, dk, dv
+    [T, d], dlog_decay, derase, dwrite in their inputs' shapes (dwrite None for a shared gate),
+    dS0."""
+    C = 64
+    rnd = _h if fp16 else (lambda a: a)
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    T, dk = k.shape
+    dv = v.shape[1]
+    la_in = np.asarray(log_decay, np.float64)
+    la = np.broadcast_to(la_in[:, None] if la_in.ndim == 1 else la_in, (T, dk))
+    e_in = np.asarray(erase, np.float64)
+    if fg2:
+        rt = np.sqrt(e_in)
+        kap, vt_all = k * rt, v * rt
+        e = np.ones((T, dk))
+        w = np.ones((T, dv))
+    else:
+        kap = k
+        e = np.broadcast_to(e_in[:, None] if e_in.ndim == 1 else e_in, (T, dk))
+        w_in = e_in if write is None else np.asarray(write, np.float64)
+        w = np.broadcast_to(w_in[:, None] if w_in.ndim == 1 else w_in, (T, dv))
+        vt_all = w * v
+    dO = np.zeros((T, dv)) if dO is None else np.asarray(dO, np.float64)
+    nck = (T + C - 1) // C
+
+    def pad(x, n):
+        return np.concatenate([x, np.zeros((C - n,) + x.shape[1:])]) if n < C else x
+
+    # per-chunk factors, forward
+    chunks = []
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, np.float64)
+    for c in range(nck):
+        c0 = C * c
+        n = min(C, T - c0)
+        sl = slice(c0, c0 + n)
+        x = dict(k=pad(kap[sl], n), q=pad(q[sl], n), u=pad(e[sl] * kap[sl], n), vt=pad(vt_all[sl], n),
+                 la=pad(la[sl], n), dO=pad(dO[sl], n), n=n, sl=sl)
+        g = np.cumsum(x["la"], axis=0)
+        gC = g[-1]
+        Kp, Qp = x["k"] * np.exp(g), x["q"] * np.exp(g)
+        Ke, Ue = x["k"] * np.exp(gC - g), x["u"] * np.exp(gC - g)
+        Akk = _lower(np.einsum("td,id,tid->ti", x["k"], x["k"], _masked_exp_diff(g, True)), True)
+        Aku = _lower(np.einsum("td,id,tid->ti", x["k"], x["u"], _masked_exp_diff(g, True)), True)
+        Aqk = _lower(np.einsum("td,id,tid->ti", x["q"], x["k"], _masked_exp_diff(g, False)), False)
+        Aqu = _lower(np.einsum("td,id,tid->ti", x["q"], x["u"], _masked_exp_diff(g, False)), False)
+        Tm = np.linalg.inv(np.eye(C) + Aku)
+        M = Tm @ (Kp @ S + Akk @ x["vt"])
+        x.update(g=g, gC=gC, Kp=Kp, Qp=Qp, Ke=Ke, Ue=Ue, Akk=Akk, Aku=Aku, Aqk=Aqk, Aqu=Aqu, Tm=Tm, S=S.copy(),
+                 M=M, Delta=x["vt"] - M)
+        chunks.append(x)
+        S = np.exp(gC)[:, None] * S + Ke.T @ x["vt"] - Ue.T @ M
+
+    # adjoint scan: G at every chunk end, and Z
+    G = np.zeros((dk, dv)) if dS_T is None else np.array(dS_T, np.float64)
+    for x in reversed(chunks):
+        x["G"] = G.copy()
+        x["Z"] = -x["Tm"].T @ (x["Aqu"].T @ x["dO"] + x["Ue"] @ G)
+        G = np.exp(x["gC"])[:, None] * G + x["Qp"].T @ x["dO"] + x["Kp"].T @ x["Z"]
+    dS0 = G
+
+    out = {n: np.zeros((T, d)) for n, d in (("dq", dk), ("dk", dk), ("dv", dv), ("dla", dk), ("de", dk), ("dw", dv))}
+    for x in chunks:
+        n, sl = x["n"], x["sl"]
+        S, G, Z, dOc = rnd(x["S"]), rnd(x["G"]), rnd(x["Z"]), rnd(x["dO"])
+        Vt = rnd(x["vt"])
+        Mx = rnd(x["Delta"] if fg2 else x["M"])
+        # the products with the state and its adjoint
+        dKp, dQp = Z @ S.T, dOc @ S.T
+        dGam = np.sum(x["S"] * x["G"], axis=1)
+        if fg2:
+            dKe, dUe = Mx @ G.T, np.zeros((C, dk))
+            dAkk, dAku = _lower(Z @ Mx.T, True), np.zeros((C, C))
+            dAqk, dAqu = _lower(dOc @ Mx.T, False), np.zeros((C, C))
+            dVt = -x["Z"]
+        else:
+            dKe, dUe = Vt @ G.T, -Mx @ G.T
+            dAkk, dAku = _lower(Z @ Vt.T, True), -_lower(Z @ Mx.T, True)
+            dAqk, dAqu = _lower(dOc @ Vt.T, False), -_lower(dOc @ Mx.T, False)
+            dVt = rnd(x["Akk"]).T @ Z + rnd(x["Aqk"]).T @ dOc + rnd(x["Ke"]) @ G
+        # through the Gram matrices
+        gb = gram_bwd_blocked if blocked else (lambda dA, a, b, g, s: gram_bwd_exact(dA, a, b, g, s))
+        kw = dict(rnd=rnd) if blocked else {}
+        g, kk, qq, uu = x["g"], x["k"], x["q"], x["u"]
+        r1, c1 = gb(dAkk, kk, kk, g, True, **kw)
+        r2, c2 = gb(dAku, kk, uu, g, True, **kw)
+        r3, c3 = gb(dAqk, qq, kk, g, False, **kw)
+        r4, c4 = gb(dAqu, qq, uu, g, False, **kw)
+        k_row, q_row, k_col, u_col = r1 + r2, r3 + r4, c1 + c3, c2 + c4
+        eg, egn = np.exp(g), np.exp(x["gC"] - g)
+        dkap = eg * dKp + egn * dKe + k_row + k_col
+        du = egn * dUe + u_col
+        dq = eg * dQp + q_row
+        dg = (kk * eg * dKp + qq * eg * dQp - kk * egn * dKe - uu * egn * dUe
+              + kk * k_row + qq * q_row - kk * k_col - uu * u_col)
+        dg[n - 1] += np.sum(kk * egn * dKe + uu * egn * dUe, axis=0) + np.exp(x["gC"]) * dGam
+        dla = np.cumsum(dg[::-1], axis=0)[::-1]
+        ec = pad(e[sl], n)
+        wc = pad(w[sl], n)
+        vc = pad(v[sl], n)
+        out["dq"][sl] = dq[:n]
+        out["dla"][sl] = dla[:n]
+        if fg2:
+            out["dk"][sl] = dkap[:n]  # k~'s adjoint; scaled below
+            out["dv"][sl] = dVt[:n]
+        else:
+            out["dk"][sl] = (dkap + ec * du)[:n]
+            out["de"][sl] = (kk * du)[:n]
+            out["dv"][sl] = (wc * dVt)[:n]
+            out["dw"][sl] = (vc * dVt)[:n]
+    res = dict(dq=out["dq"], dS0=dS0)
+    res["dlog_decay"] = out["dla"].sum(-1) if la_in.ndim == 1 else out["dla"]
+    if fg2:
+        res["dk"] = rt * out["dk"]
+        res["dv"] = rt * out["dv"]
+        res["dbeta"] = (k * out["dk"] + v * out["dv"]) / (2 * rt)
+        return res
+    res["dk"], res["dv"] = out["dk"], out["dv"]
+    de = out["de"].sum(-1) if e_in.ndim == 1 else out["de"]
+    if write is None:
+        dw = out["dw"].sum(-1) if e_in.ndim == 1 else out["dw"]
+        res["derase"], res["dwrite"] = de + dw, None
+    else:
+        w_nd = np.asarray(write).ndim
+        res["derase"], res["dwrite"] = de, (out["dw"].sum(-1) if w_nd == 1 else out["dw"])
+    return res

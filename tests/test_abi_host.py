@@ -265,10 +265,19 @@ def _bwd(desc, **over):
 def test_bwd_workspace_and_errors():
     L = _abi.lib()
     d = _good_desc(B=2, T=100, H=4, dk=128, dv=128)
-    # one wave per (b, h, 256 / dk = 2 value columns): 64 column groups
     waves, nck, bth = 2 * 4 * 64, 2, 2 * 100 * 4
-    # row parts: one per workgroup of 32 columns
-    need = 4 * (waves * nck * 128 * 2 + waves * 64 * 128 * 2 + 4 * 4 * bth * 128 + bth * 128)
+    # the token path (chunk = 1): one wave per (b, h, 256 / dk = 2 value columns), 64 column
+    # groups; a checkpoint per chunk and one chunk of states per wave; row parts per workgroup of
+    # 32 columns; v * dv~
+    token = 4 * (waves * nck * 128 * 2 + waves * 64 * 128 * 2 + 4 * 4 * bth * 128 + bth * 128)
+    assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(_good_desc(B=2, T=100, H=4, chunk=1))) == token
+    # the chunk path: the forward's packets, a bf16 o buffer, the state at every chunk start and
+    # its adjoint at every chunk end, eight checkpoints per wave of each (b, h, chunk, 32-column)
+    # work item (at most 512 workgroups), then the same row parts and v * dv~
+    r256 = lambda n: (n + 255) // 256 * 256
+    nwork = 2 * 4 * nck * 4
+    need = (r256(2 * 4 * nck * 46080) + r256(bth * 128 * 2) + 2 * r256(2 * 4 * nck * 128 * 128 * 4) +
+            r256(min(nwork, 512) * 16 * 8 * 128 * 2 * 4) + r256(4 * 4 * bth * 128 * 4) + r256(bth * 128 * 4))
     assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(d)) == need
     assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(_good_desc(T=0))) == 0
     assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(_good_desc(erase_kind=_abi.DR_GATE_RATE_SQRT))) > 0

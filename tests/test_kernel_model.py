@@ -148,3 +148,69 @@ def test_large_values():
     ro, rS = _oracle(inp, False)
     o, S, _ = _emulate(inp, "safe", False)
     assert err_o(o, ro) <= TOL_BF16 and err_S(S, rS) <= TOL_BF16
+
+
+# ---- the gradients' chunk form --------------------------------------------------------------
+# The matrix-core backward evaluates the gradients chunk by chunk from each chunk's incoming state
+# and end adjoint (tests/chunk_model.py, ``chunk_backward``).  Its algebra must equal the adjoint
+# of the token loop exactly (fp64, both the element-by-element and the kernels' block arrangement
+# of the Gram adjoints, for every gate form and decay strength), and with fp16 operands where the
+# kernels round it must stay inside the bf16 parity bar.
+BWD_VARIANTS = ["scalar", "kda", "decoupled", "channel_shared", "fg2"]
+BWD_REGIMES = [("softplus", -4.0, 1.5), ("sigmoid", 0.0, 1.5), ("softplus", 2.0, 1.0)]
+
+
+def _bwd_case(variant, decay, mu, sd, T=150, d=32, seed=3):
+    import torch
+
+    from gated_delta_rule_dr_amd.workloads import Workload, generate
+
+    wl = Workload("case", 1, T, 1, d, d, "f32", decay, variant != "scalar", mu, sd,
+                  variant in ("decoupled", "channel_shared", "fg2"), "channel" if variant == "decoupled" else "erase",
+                  0.05, seed, rate_sqrt=variant == "fg2")
+    inp = generate(wl)
+    g = torch.Generator().manual_seed(seed + 1)
+    dO = torch.randn((1, T, 1, d), generator=g, dtype=torch.float64)
+    dST = torch.randn((1, 1, d, d), generator=g, dtype=torch.float64)
+    return inp, dO, dST
+
+
+def _bwd_errors(variant, decay, mu, sd, blocked, fp16):
+    from chunk_model import chunk_backward
+    from oracle import recurrence_bwd, recurrence_fg2_bwd
+
+    inp, dO, dST = _bwd_case(variant, decay, mu, sd)
+    fg2 = variant == "fg2"
+    if fg2:
+        ref = recurrence_fg2_bwd(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["S0"], dO, dST)
+    else:
+        ref = recurrence_bwd(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"], inp["S0"],
+                             dO=dO, dS_T=dST)
+    sel = lambda x: None if x is None else _f(x)[0, :, 0]
+    got = chunk_backward(sel(inp["q"]), sel(inp["k"]), sel(inp["v"]), sel(inp["log_decay"]), sel(inp["erase"]),
+                         sel(inp["write"]), _f(inp["S0"])[0, 0], _f(dO)[0, :, 0], _f(dST)[0, 0], fg2=fg2,
+                         blocked=blocked, fp16=fp16)
+    errs = {}
+    for key, x in got.items():
+        if x is None:
+            assert ref.get(key) is None
+            continue
+        r = ref[key][0, 0] if key == "dS0" else ref[key][0, :, 0]
+        errs[key] = float(np.abs(x - r).max() / max(np.abs(r).max(), 1e-300))
+    return errs
+
+
+@pytest.mark.parametrize("variant", BWD_VARIANTS)
+@pytest.mark.parametrize("decay,mu,sd", BWD_REGIMES)
+def test_chunk_backward_algebra_exact(variant, decay, mu, sd):
+    for blocked in (False, True):
+        errs = _bwd_errors(variant, decay, mu, sd, blocked, False)
+        assert max(errs.values()) <= 1e-12, (blocked, errs)
+
+
+@pytest.mark.parametrize("variant", BWD_VARIANTS)
+def test_chunk_backward_fp16_operands_meet_bar(variant):
+    for decay, mu, sd in BWD_REGIMES:
+        errs = _bwd_errors(variant, decay, mu, sd, True, True)
+        assert max(errs.values()) <= TOL_BF16, (decay, mu, errs)
+
