@@ -498,8 +498,9 @@ def main():
         line["backward"] = {"workload": wl.name, "calls": bsteps, "ms": bsec * 1e3,
                             "tokens_per_s": wl.token_heads / bsec, "hbm_frac": bbytes / bsec / 1e9 / HBM_PEAK_GBS,
                             "bytes_per_call": bbytes,
-                            "kernel": ("dr_chunk_bwd = chunked forward with chunk-start states + adjoint scan + "
-                                       "bwd_chunk_kernel + bwd_reduce_kernel") if chunked else
+                            "kernel": ("dr_chunk_bwd = general-gate chunked forward (stores S, M) + adjoint scan "
+                                       "(stores G, Z) + chunk_grad_state_kernel + chunk_grad_gram_kernel")
+                                      if chunked else
                                       "dr_chunk_bwd = bwd_token_kernel + bwd_reduce_kernel (fp32 token adjoint)"}
         if chunked:
             tsec = time_backward(dr, torch, wl, 2, 1, chunk=1)

@@ -377,218 +377,6 @@ __global__ __launch_bounds__(1024) void bwd_token_kernel(Problem p, BwdArgs g, f
   }
 }
 
-// The adjoint of the token loop, every chunk of a dense batch in parallel (gradients through
-// the chunk path).  Each chunk starts from its state ck_S (stored by the chunked forward) and
-// walks back from the state's adjoint at its end, ck_G (stored by the adjoint scan), so the
-// chunks need nothing from one another.  Work item (b, h, chunk, group of 32 value columns)
-// runs one workgroup of 16 waves with the token kernel's lane layout and per-token arithmetic,
-// row-part sums and outputs; dS0 comes from the adjoint scan.  In-chunk states are rebuilt from
-// eight register checkpoints (every 8 tokens, kept in this workgroup's scratch slot): the
-// forward over the chunk saves them, then each 8-token block is replayed into registers and
-// walked backwards.  Persistent: each workgroup takes every grid-th work item.
-constexpr int kBlk = 8;                 // tokens per replayed block
-constexpr int kBwdChunkGrid = 512;      // most workgroups of the chunk-parallel adjoint
-
-template <int DK>
-__global__ __launch_bounds__(1024) void bwd_chunk_kernel(Problem p, BwdArgs g, const float* __restrict__ ck_S,
-                                                         const float* __restrict__ ck_G, float* __restrict__ scratch,
-                                                         float* __restrict__ parts, float* __restrict__ tmp_dw,
-                                                         int64_t nwork, int64_t ngroups) {
-  constexpr int kCols = cols_for(DK);
-  constexpr int RPL = DK * kCols / 64;  // rows per lane
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int c = lane & (kCols - 1);
-  const int grp = lane / kCols;
-  const int row0 = grp * RPL;
-  const int nw = blockDim.x >> 6;
-  const int dv = p.dv;
-  const bool bf = p.qkv_bf16;
-  const int nck = (p.T + CK - 1) / CK;
-  const int64_t bth = int64_t(p.B) * p.T * p.H;
-  const int64_t pstride = ngroups * bth * DK;
-  // this wave's checkpoints: CK / kBlk states of DK x kCols, lane-major
-  float* my = scratch + (int64_t(blockIdx.x) * nw + wave) * (CK / kBlk) * DK * kCols;
-  auto save = [&](float* dst, const float (&v)[RPL]) {
-#pragma unroll
-    for (int i = 0; i < RPL; i += 4)
-      *reinterpret_cast<f32x4*>(dst + lane * RPL + i) = f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]};
-  };
-  auto restore = [&](const float* src, float (&v)[RPL]) {
-#pragma unroll
-    for (int i = 0; i < RPL; i += 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(src + lane * RPL + i);
-      v[i] = x[0];
-      v[i + 1] = x[1];
-      v[i + 2] = x[2];
-      v[i + 3] = x[3];
-    }
-  };
-  __shared__ float red[2][16][4][DK];
-
-  for (int64_t wi = blockIdx.x; wi < nwork; wi += gridDim.x) {
-    const int gi = int(wi % ngroups);
-    const int64_t rest = wi / ngroups;
-    const int ci = int(rest % nck);
-    const int bh = int(rest / nck);
-    const int b = bh / p.H, h = bh - b * p.H;
-    const int slice = gi * nw + wave;
-    const int j = slice * kCols + c;
-    const int t0 = ci * CK, t1 = t0 + CK < p.T ? t0 + CK : p.T;
-    auto token = [&](int t) { return (int64_t(b) * p.T + t) * p.H + h; };
-
-    struct Tok {
-      float k[RPL], a[RPL], e[RPL];
-      float v, w;
-    };
-    auto load_tok = [&](Tok& x, int64_t tok) {
-      float la[RPL];
-      load_rows<RPL>(p.k, tok * DK + row0, bf, x.k);
-      if (p.decay_channel) {
-        load_f32_rows<RPL>(p.log_decay, tok * DK + row0, la);
-      } else {
-        const float l = p.log_decay[tok];
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) la[r] = l;
-      }
-#pragma unroll
-      for (int r = 0; r < RPL; ++r) x.a[r] = expf(la[r]);
-      if (p.erase_channel) {
-        load_f32_rows<RPL>(p.erase, tok * DK + row0, x.e);
-      } else {
-        const float e = p.erase[tok];
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) x.e[r] = e;
-      }
-      x.v = load_qkv(p.v, tok * dv + j, bf);
-      x.w = p.write_channel ? p.write[tok * dv + j] : p.write[tok];
-      if (p.rate_sqrt) {
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) {
-          x.k[r] *= sqrtf(x.e[r]);
-          x.e[r] = 1.f;
-        }
-        x.w = sqrtf(x.w);
-      }
-    };
-    auto fwd = [&](float (&s)[RPL], const Tok& x) {
-      float m = 0.f;
-#pragma unroll
-      for (int r = 0; r < RPL; ++r) {
-        s[r] *= x.a[r];
-        m = fmaf(x.k[r], s[r], m);
-      }
-      m = group_sum<kCols>(m);
-      const float wv = x.w * x.v;
-#pragma unroll
-      for (int r = 0; r < RPL; ++r) s[r] = fmaf(-x.e[r] * x.k[r], m, fmaf(x.k[r], wv, s[r]));
-    };
-
-    // the chunk's start state and its end adjoint, this wave's columns
-    const int64_t pkt = int64_t(bh) * nck + ci;
-    float s[RPL], G[RPL];
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      s[r] = ck_S[(pkt * DK + row0 + r) * dv + j];
-      G[r] = ck_G[(pkt * DK + row0 + r) * dv + j];
-    }
-    const int nb = (t1 - t0 + kBlk - 1) / kBlk;
-    for (int bi = 0; bi < nb; ++bi) {
-      save(my + bi * DK * kCols, s);
-      const int tb = t0 + kBlk * bi;
-#pragma unroll
-      for (int i = 0; i < kBlk; ++i) {
-        if (tb + i < t1) {
-          Tok x;
-          load_tok(x, token(tb + i));
-          fwd(s, x);
-        }
-      }
-    }
-    for (int bi = nb - 1; bi >= 0; --bi) {
-      const int tb = t0 + kBlk * bi;
-      restore(my + bi * DK * kCols, s);
-      float sp[kBlk][RPL];  // S_{t-1} of the block's tokens
-#pragma unroll
-      for (int i = 0; i < kBlk; ++i) {
-        if (tb + i < t1) {
-#pragma unroll
-          for (int r = 0; r < RPL; ++r) sp[i][r] = s[r];
-          Tok x;
-          load_tok(x, token(tb + i));
-          fwd(s, x);
-        }
-      }
-#pragma unroll
-      for (int i = kBlk - 1; i >= 0; --i) {
-        const int t = tb + i;
-        if (t >= t1) continue;  // uniform over the workgroup
-        const int64_t tok = token(t);
-        Tok x;
-        load_tok(x, tok);
-        float qr[RPL];
-        load_rows<RPL>(p.q, tok * DK + row0, bf, qr);
-        const float dO = g.dO[tok * dv + j];
-        float m = 0.f;
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) m = fmaf(x.k[r], x.a[r] * sp[i][r], m);
-        m = group_sum<kCols>(m);
-        const float vw = x.w * x.v;
-        const int buf = t & 1;
-        const int prow = row0 + rs_row<kCols, RPL>(c);
-        const bool owner = rs_owner<kCols, RPL>(c);
-        auto put = [&](float* part, int which) {
-          row_scatter_sum<kCols, RPL>(part, c);
-          if (owner) {
-#pragma unroll
-            for (int q2 = 0; q2 < rs_count<kCols, RPL>; ++q2) red[buf][wave][which][prow + q2] = part[q2];
-          }
-        };
-        float dm = 0.f, dvw = 0.f;
-        float pa[RPL], pb[RPL];
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) {
-          const float Sp = x.a[r] * sp[i][r];
-          const float St = fmaf(-x.e[r] * x.k[r], m, fmaf(x.k[r], vw, Sp));
-          G[r] = fmaf(qr[r], dO, G[r]);
-          pa[r] = St * dO;    // dq
-          pb[r] = -G[r] * m;  // du
-          dm = fmaf(-G[r] * x.e[r], x.k[r], dm);
-          dvw = fmaf(G[r], x.k[r], dvw);
-        }
-        put(pa, 0);
-        put(pb, 1);
-        dm = group_sum<kCols>(dm);
-        dvw = group_sum<kCols>(dvw);
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) {
-          const float Sp = x.a[r] * sp[i][r];
-          pa[r] = fmaf(G[r], vw, Sp * dm);  // dk, less the erase part
-          const float Gp = fmaf(x.k[r], dm, G[r]);
-          pb[r] = Gp * sp[i][r];  // d(log a) / a
-          G[r] = x.a[r] * Gp;
-        }
-        put(pa, 2);
-        put(pb, 3);
-        lds_barrier();
-        for (int q2 = threadIdx.x; q2 < 4 * DK; q2 += blockDim.x) {
-          const int which = q2 / DK, row = q2 - which * DK;
-          float sum = 0.f;
-          for (int w2 = 0; w2 < nw; ++w2) sum += red[buf][w2][which][row];
-          parts[which * pstride + (int64_t(gi) * bth + tok) * DK + row] = sum;
-        }
-        if (grp == 0) {
-          g.dv[tok * dv + j] = x.w * dvw;
-          tmp_dw[tok * dv + j] = x.v * dvw;
-        }
-      }
-    }
-    // the next work item's first LDS writes use the other buffer only after every wave has
-    // passed its last barrier here
-    lds_barrier();
-  }
-}
-
 // Sum over the workgroup (128 threads).
 __device__ float block_sum128(float x, float* red) {
   const int tid = threadIdx.x;
@@ -688,28 +476,23 @@ hipError_t launch_bwd_varlen(Problem p, const int* cu, const BwdArgs& g, void* w
   return launch_bwd(p, g, ws + bwd_tables_bytes(p.B), stream);
 }
 
-// Chunked gradients: workspace = forward packets | o (bf16, unused) | chunk-start states |
-// chunk-end adjoints | the chunk adjoint's checkpoint slots | row parts | v * dv~.
+// Gradients through the chunk path: workspace = forward packets (general-gate layout, or FG2's
+// symmetric one) | o (bf16, unused) | chunk-start states | chunk-end adjoints (fp32 [dk][dv]
+// per chunk) | M (FG2: delta) and Z (fp16 [C][dv] per chunk) | the chunk gradients' products.
 struct BwdChunkedLayout {
-  int64_t pkt, obuf, ckS, ckG, scr, parts, tmp_dw, total;  // byte offsets
-  int64_t ngroups, nwork;
+  int64_t pkt, obuf, ckS, ckG, ckM, ckZ, work, total;  // byte offsets
   BwdChunkedLayout(const Problem& p) {
-    const int64_t r256 = 256;
-    auto up = [&](int64_t n) { return (n + r256 - 1) / r256 * r256; };
+    auto up = [](int64_t n) { return (n + 255) / 256 * 256; };
     const int64_t nck = (int64_t(p.T) + CK - 1) / CK, bth = int64_t(p.B) * p.T * p.H;
-    const int cols = cols_for(p.dk);
-    const int wpg = 32 / cols;
-    ngroups = (p.dv / cols) / wpg;
-    nwork = int64_t(p.B) * p.H * nck * ngroups;
+    const int64_t chunks = int64_t(p.B) * p.H * nck;
     pkt = 0;
-    obuf = up(int64_t(chunk128_workspace_bytes(p.B, p.T, p.H, p.symmetric, p.decay_channel, p.rate_sqrt)));
+    obuf = up(int64_t(chunk128_workspace_bytes(p.B, p.T, p.H, false, p.decay_channel, p.rate_sqrt)));
     ckS = obuf + up(bth * p.dv * 2);
-    ckG = ckS + up(int64_t(p.B) * p.H * nck * p.dk * p.dv * 4);
-    scr = ckG + up(int64_t(p.B) * p.H * nck * p.dk * p.dv * 4);
-    const int64_t grid = nwork < kBwdChunkGrid ? nwork : kBwdChunkGrid;
-    parts = scr + up(grid * wpg * (CK / kBlk) * p.dk * cols * 4);
-    tmp_dw = parts + up(4 * ngroups * bth * p.dk * 4);
-    total = tmp_dw + up(bth * p.dv * 4);
+    ckG = ckS + up(chunks * p.dk * p.dv * 4);
+    ckM = ckG + up(chunks * p.dk * p.dv * 4);
+    ckZ = ckM + up(chunks * CK * p.dv * 2);
+    work = ckZ + up(chunks * CK * p.dv * 2);
+    total = work + up(int64_t(chunk_grad_work_bytes(p)));
   }
 };
 
@@ -719,38 +502,31 @@ hipError_t launch_bwd_chunked(const Problem& p, const BwdArgs& g, void* workspac
   if (p.dk != 128 || p.dv != 128 || p.seqs) return hipErrorInvalidValue;
   const BwdChunkedLayout L(p);
   char* ws = static_cast<char*>(workspace);
-  // the chunked forward, storing the state at every chunk start (o goes to a bf16 buffer)
+  // One per-head gate for erase and write is the general form with u = beta k, v~ = beta v, so
+  // every gate form but FG2's rate runs the general-gate kernels, whose forward scan yields the
+  // in-chunk reads M that the gradients need.
   Problem pf = p;
+  pf.symmetric = 0;
   pf.o = ws + L.obuf;
   pf.o_bf16 = 1;
   pf.S_T = nullptr;
   pf.ck_S = reinterpret_cast<float*>(ws + L.ckS);
+  pf.ck_M = ws + L.ckM;
   hipError_t e = launch_chunk128(pf, ws + L.pkt, stream);
   if (e != hipSuccess) return e;
-  // the state's adjoint at every chunk end, and dS0
+  // the state's adjoint at every chunk end and Z, and dS0
   Problem pa = pf;
   pa.ck_S = nullptr;
+  pa.ck_M = nullptr;
   pa.ck_G = reinterpret_cast<float*>(ws + L.ckG);
+  pa.ck_Z = ws + L.ckZ;
   e = launch_chunk128_adjoint(pa, ws + L.pkt, g.dO, g.dS_T, g.dS0, stream);
   if (e != hipSuccess) return e;
-  // every chunk's token adjoint in parallel
-  int dev = 0, ncu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return hipErrorInvalidDevice;
-  int64_t grid = int64_t(ncu) * 2;
-  if (grid > kBwdChunkGrid) grid = kBwdChunkGrid;
-  if (grid > L.nwork) grid = L.nwork;
-  float* parts = reinterpret_cast<float*>(ws + L.parts);
-  float* tmp_dw = reinterpret_cast<float*>(ws + L.tmp_dw);
-  hipLaunchKernelGGL(bwd_chunk_kernel<128>, dim3(unsigned(grid)), dim3(64 * (32 / cols_for(128))), 0, stream, p, g,
-                     pf.ck_S, pa.ck_G, reinterpret_cast<float*>(ws + L.scr), parts, tmp_dw, L.nwork, L.ngroups);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t bth = int64_t(p.B) * p.T * p.H;
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(unsigned(bth)), dim3(128), 0, stream, p, g, parts, tmp_dw, L.ngroups,
-                     bth);
-  return hipGetLastError();
+  // every chunk's gradients
+  Problem pg = pf;
+  pg.ck_G = pa.ck_G;
+  pg.ck_Z = pa.ck_Z;
+  return launch_chunk_grad(pg, g, ws + L.pkt, ws + L.work, stream);
 }
 
 hipError_t launch_bwd(const Problem& p, const BwdArgs& g, void* workspace, hipStream_t stream) {

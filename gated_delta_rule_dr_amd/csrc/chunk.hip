@@ -49,179 +49,19 @@
 // computed transposed (A^T = K Q^T) so that each lane owns four consecutive columns of one row
 // of A and stores them with one vector write.
 
+#include "chunk_layout.h"
 #include "dr_device.h"
 #include "dr_internal.h"
 
 namespace dr {
 namespace {
 
-typedef _Float16 half4v __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int C = 64;      // chunk length
-constexpr int D = 128;     // dk == dv
-constexpr int KS = 136;    // row stride (halves) of [64][128] tiles: 16-byte pad
-constexpr int CS = 72;     // row stride (halves) of [*][64] tiles
-constexpr int AFS = 68;    // row stride (floats) of the fp32 64 x 64 matrix (16-byte rows)
-constexpr int kThreads = 256;
-
-// Lower-triangular 16x16 tile (I, J), I >= J, enumerated row by row.
-__device__ __forceinline__ void tile_ij(int idx, int& I, int& J) {
-  I = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3;
-  J = idx - (I * (I + 1)) / 2;
-}
-
-// Operand fragment for v_mfma_f32_16x16x32_f16 from a tile whose rows are the fragment's
-// rows (A operand) or columns (B operand) and whose contraction index is contiguous.
-__device__ __forceinline__ half8 frag(const _Float16* base, int stride, int row0, int k0, int lane) {
-  return *reinterpret_cast<const half8*>(base + (row0 + (lane & 15)) * stride + k0 + 8 * (lane >> 4));
-}
-
-__device__ __forceinline__ f32x4 mfma16(half4v a, half4v b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ half8 cvt8(const float* x) {
-  half8 h;
+// Rows t0 .. t0 + 3 of column j of a per-chunk fp16 [C][D] matrix (packet index pkt) from an
+// accumulator tile's four values.
+__device__ __forceinline__ void store_rows(void* base, int64_t pkt, int t0, int j, f32x4 x) {
+  _Float16* dst = static_cast<_Float16*>(base) + pkt * C * D + int64_t(t0) * D + j;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) h[i] = (_Float16)x[i];
-  return h;
-}
-
-__device__ __forceinline__ half4v cvt4(f32x4 a) {
-  half4v h;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) h[r] = (_Float16)a[r];
-  return h;
-}
-
-__device__ __forceinline__ void bf16x8_to_f32(uint4 u, float* f) {
-  f[0] = __uint_as_float(u.x << 16); f[1] = __uint_as_float(u.x & 0xffff0000u);
-  f[2] = __uint_as_float(u.y << 16); f[3] = __uint_as_float(u.y & 0xffff0000u);
-  f[4] = __uint_as_float(u.z << 16); f[5] = __uint_as_float(u.z & 0xffff0000u);
-  f[6] = __uint_as_float(u.w << 16); f[7] = __uint_as_float(u.w & 0xffff0000u);
-}
-
-// v when ok, else zero
-__device__ __forceinline__ uint4 mask4(bool ok, uint4 v) {
-  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
-}
-
-__device__ __forceinline__ void unpack8(float4 a, float4 b, float* f) {
-  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-}
-
-// 16 bytes at byte offset `off` of a global byte pointer.
-__device__ __forceinline__ uint4 ldb16(gptr<const char> base, int64_t off) {
-  const u32x4 x = *(gptr<const u32x4>)(base + off);
-  return make_uint4(x.x, x.y, x.z, x.w);
-}
-__device__ __forceinline__ float4 ldf16(gptr<const char> base, int64_t off) {
-  const f32x4 x = *(gptr<const f32x4>)(base + off);
-  return make_float4(x.x, x.y, x.z, x.w);
-}
-
-// ------------------------------------------------------------------------------------------
-// Per-chunk packet in the workspace (byte offsets).  Matrices are fp16 64 x 64 with zero upper
-// triangles, in the order T, A_qk (, A_kk, A_qu for general gates); tiles are fp16; the gate
-// vector is fp32 [512].
-//   scalar decay, symmetric gates: matrices, k [64][128], q [64][128] (plain), gates
-//     {beta[64], e^{g}[64], e^{g_C - g}[64], 1, e^{g_C}, 1}
-//   otherwise: matrices, K+ [64][128], Q+ [64][128], K^end [64][128] (, U^end [64][128]), gates
-//     {beta[64] (symmetric gates), 1[128], e^{g_C}[128], 1[128]}
-// Every fp16 row is a run of 16-byte units (16 per 128-wide row) stored XOR-swizzled, unit u of
-// row r at position u ^ swz_key<16>(r), so that the scan can copy a tile into LDS as is and
-// still read matrix-core fragments (and, from K^end, transposed fragments) without bank
-// conflicts.  With FG2's per-channel rate (VP) the packet also carries the scaled values
-// v~ = sqrt(beta) v as fp16 [64][128], row-major (the scan copies its value slice from there).
-// ------------------------------------------------------------------------------------------
-template <bool DCH, bool GEN, bool VP = false>
-struct Packet {
-  static constexpr bool kScal = !DCH && !GEN;
-  static constexpr int nmat = GEN ? 4 : 2;
-  static constexpr int mat = 0;
-  // bytes per matrix: the six nonzero 16 x 32 blocks of the lower-triangular matrices (tri_pos)
-  static constexpr int matb = 6 * 1024;
-  static constexpr int kp = mat + nmat * matb;
-  static constexpr int qp = kp + C * D * 2;
-  static constexpr int kmt = qp + C * D * 2;
-  static constexpr int umt = kmt + (kScal ? 0 : D * C * 2);
-  static constexpr int gate = umt + (GEN ? D * C * 2 : 0);
-  static constexpr int ngate = kScal ? 256 : 512;  // floats
-  static constexpr int vt = gate + ngate * 4;
-  static constexpr int bytes = vt + (VP ? C * D * 2 : 0);
-};
-
-// XOR key of row r in a tile with U 16-byte units per row.  Measured on gfx950 (bank-conflict
-// counters over fixed lane patterns), the LDS behaves as follows:
-//  - ds_read_b128: 16 lanes of equal lane / 16 per cycle, over 16 slots of 16 bytes, slot
-//    ((addr >> 4) ^ (addr >> 10 & 1)) & 15;
-//  - ds_read_b64_tr_b16: 32 lanes of equal lane / 32 per cycle, over the 32 8-byte slots of a
-//    256-byte window;
-//  - ds_write_b64: 16 lanes of equal lane / 16 per cycle, over the 16 8-byte slots of a 128-byte
-//    window.
-// With these keys a fragment read (rows r0 .. r0 + 15, r0 % 16 == 0) of either tile width and
-// the transposing read of a 128-wide tile (rows t0 + 8 g + 0..3, t0 % 32 == 0) are
-// conflict-free; fragment-layout writes of 8 bytes per lane into the tiles are 2-way, the least
-// that 16 rows at one column allow.  For U = 16 the key / 2 is one-to-one on row bits 0, 1, 3
-// (the transposing read), and key ^ (bit 2 of the row, placed at bit 0) on row bits 0..3 (the
-// fragment read, after the address hash).
-template <int U>
-__device__ __forceinline__ int swz_key(int r) {
-  if constexpr (U == 16) return ((r >> 3) & 1) | ((r & 3) << 1) | (r & 8);
-  else return r & 7;
-}
-
-// Half offset of column `col` of row `r` in a swizzled tile with U 16-byte units per row.
-template <int U>
-__device__ __forceinline__ int swz(int r, int col) {
-  return (r * U + ((col >> 3) ^ swz_key<U>(r))) * 8 + (col & 7);
-}
-
-// Fragment (as frag()) of a swizzled tile with U 16-byte units per row.
-template <int U>
-__device__ __forceinline__ half8 frag_s(const _Float16* base, int row0, int k0, int lane) {
-  return *reinterpret_cast<const half8*>(base + swz<U>(row0 + (lane & 15), k0 + 8 * (lane >> 4)));
-}
-
-// Lower-triangular 64 x 64 fp16 matrices (T, A_qk) of the symmetric-gate packet: only the six
-// 16 x 32 blocks (row tile I, column half H) that hold nonzeros are stored, 1 KB each, in the
-// order (0,0) (1,0) (2,0) (2,1) (3,0) (3,1); within a block, 16 rows of four 16-byte units with
-// unit u of row r at u ^ ((r >> 2) & 3), which makes fragment reads (16 rows at one unit per
-// cycle) conflict-free.  The scan keeps all eight blocks in LDS (block 2 I + H), the two upper
-// ones zero.
-__device__ __forceinline__ int tri_blk(int I, int H) { return I < 2 ? I : 2 * I - 2 + H; }
-__device__ __forceinline__ int tri_in(int r, int col) {  // half offset of (r % 16, col % 32) in a block
-  return ((r & 15) * 4 + (((col >> 3) & 3) ^ ((r >> 2) & 3))) * 8 + (col & 7);
-}
-// half offset of element (t, col) in the six-block packet layout (the block must be stored)
-__device__ __forceinline__ int tri_pos(int t, int col) { return tri_blk(t >> 4, col >> 5) * 512 + tri_in(t, col); }
-
-// gate-vector slots (floats)
-constexpr int GV_BETA = 0;                            // [64]
-constexpr int GV_FP = 64, GV_FM = 128, GV_SC = 192;   // scalar decay
-constexpr int GV_EM = 64, GV_FC = 192, GV_FCM = 320;  // per-channel decay, [128] each
-
-typedef __attribute__((address_space(1))) void gvoid;
-typedef __attribute__((address_space(3))) void lvoid;
-
-// Lane l copies the 16 bytes at its global address `src` to LDS byte `lds_wave` + 16 l
-// (`lds_wave` is the same for the whole wave).
-__device__ __forceinline__ void dma16(gptr<const char> src, void* lds_wave) {
-  __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)lds_wave, 16, 0, 0);
-}
-
-// Wait for all of this wave's vector-memory operations (loads, stores, copies to LDS).
-__device__ __forceinline__ void vm_wait_all() {
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
-}
-
-// Wait until at most N of this wave's vector-memory operations are outstanding.  Loads complete
-// in issue order, so this waits for every load issued before the last N loads.
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xf) | (0x7 << 4) | (0xf << 8) | ((N >> 4) << 14));
+  for (int r = 0; r < 4; ++r) dst[r * D] = (_Float16)x[r];
 }
 
 // One chunk of prep work: the row of its first token on the token axis ([B * T] for a dense
@@ -1064,36 +904,6 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_ch_kernel(Problem p, c
 constexpr int kScanWaves = 8;
 constexpr int kScanThreads = 64 * kScanWaves;
 
-// Fragment (as frag()) of rows 16 I .. + 15, columns 32 H .. + 31 of a lower-triangular matrix
-// held in LDS as eight 16 x 32 blocks (block 2 I + H, layout as tri_in).
-__device__ __forceinline__ half8 frag_tri(const _Float16* base, int I, int H, int lane) {
-  return *reinterpret_cast<const half8*>(base + (2 * I + H) * 512 + tri_in(lane & 15, 8 * (lane >> 4)));
-}
-
-// gfx950 transposing LDS read (ds_read_b64_tr_b16): lane 16 g + 4 a + b receives as element j
-// (0..3) the 16-bit element b of the 8 bytes at the address that lane 16 g + a + 4 j supplies.
-typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
-typedef __attribute__((address_space(3))) fp16x4 lds_half4;
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) short4v lds_short4;
-__device__ __forceinline__ half4v ld_tr16(const _Float16* p) {
-  return __builtin_bit_cast(half4v, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_half4*)p));
-}
-__device__ __forceinline__ short4v ld_tr16(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
-}
-
-// frag_s of the transposed tile: A[row = d][k = t] = base[t][d] (base swizzled, 16 units per
-// row).  Lane 16 g + m supplies row t0 + 8 g + m / 4 (and 4 rows on), columns d0 + 4 (m % 4)
-// .. + 3, so lane 16 g + l16 receives base[t0 + 8 g + 0..7][d0 + l16].
-__device__ __forceinline__ half8 frag_ts(const _Float16* base, int d0, int t0, int lane) {
-  const int m = lane & 15;
-  const int t = t0 + 8 * (lane >> 4) + (m >> 2), d = d0 + 4 * (m & 3);
-  const half4v lo = ld_tr16(base + swz<16>(t, d));
-  const half4v hi = ld_tr16(base + swz<16>(t + 4, d));
-  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
 // LDS layout of the register-staged scan (general gates).
 template <bool GEN, bool SCAL, int DVS>
 struct ScanLayout {
@@ -1407,6 +1217,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
 #pragma unroll
       for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(-acc[r]);
       *reinterpret_cast<half4v*>(DT + swz<8>(16 * ct + l16, 16 * i + 4 * lg)) = hv;
+      if constexpr (CKPT) {
+        if (p.ck_M) store_rows(p.ck_M, sq.pkt0 + c, 16 * i + 4 * lg, j0 + 16 * ct + l16, acc);
+      }
     }
     lds_barrier();
 
@@ -1929,6 +1742,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
 #pragma unroll
       for (int r = 0; r < 4; ++r) hv[r] = (_Float16)acc[r];
       *reinterpret_cast<half4v*>(DT + swz<8>(16 * ct + l16, 16 * i + 4 * lg)) = hv;
+      if constexpr (CKPT) {
+        if (p.ck_M) store_rows(p.ck_M, sq.pkt0 + c, 16 * i + 4 * lg, j0 + 16 * ct + l16, acc);
+      }
       if constexpr (SCAL) {
         // K^end^T delta = k^T (Diag(e^{g_C - g}) delta): the state update takes the scaled copy
         const float4 fm = *reinterpret_cast<const float4*>(X.gv + GV_FM + 16 * i + 4 * lg);
@@ -2045,16 +1861,6 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
 // loop starts there), and the one at the start of the sequence is dS0.  Eight waves, register
 // staging one chunk ahead, four barriers per chunk.
 // ------------------------------------------------------------------------------------------
-// frag_ts of a lower-triangular matrix held in LDS as eight 16 x 32 blocks (block 2 I + H, layout
-// as tri_in): lane 16 g + l16 receives A[r0 + 8 g + 0..7][c0 + l16] (c0 % 16 == 0, r0 % 8 == 0).
-__device__ __forceinline__ half8 frag_tri_t(const _Float16* base, int c0, int r0, int lane) {
-  const int m = lane & 15;
-  const int r = r0 + 8 * (lane >> 4) + (m >> 2), c = c0 + 4 * (m & 3);
-  const half4v lo = ld_tr16(base + (2 * (r >> 4) + (c >> 5)) * 512 + tri_in(r, c));
-  const half4v hi = ld_tr16(base + (2 * ((r + 4) >> 4) + (c >> 5)) * 512 + tri_in(r + 4, c));
-  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
 template <bool DCH, bool GEN, bool FG2, int DVS>
 __global__ __launch_bounds__(kScanThreads) void chunk_adjoint_scan_kernel(Problem p, const char* __restrict__ ws,
                                                                           const float* __restrict__ dO,
@@ -2207,13 +2013,16 @@ __global__ __launch_bounds__(kScanThreads) void chunk_adjoint_scan_kernel(Proble
       for (int ks = 0; ks < 2; ++ks)
         z = mfma16x16x32(frag_tri_t(TM, 16 * I, 32 * ks, lane), frag_s<8>(X1T, 16 * zct, 32 * ks, lane), z);
       half4v hv;
+      f32x4 zu;  // Z itself (without the per-head decay's row factor)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float f = GEN ? -1.f : -GV[GV_BETA + zi + r];
+        zu[r] = f * z[r];
         if constexpr (SCAL) f *= GV[GV_FP + zi + r];
         hv[r] = (_Float16)(f * z[r]);
       }
       *reinterpret_cast<half4v*>(ZT + swz<8>(16 * zct + l16, zi)) = hv;
+      if (p.ck_Z) store_rows(p.ck_Z, sq.pkt0 + c, zi, j0 + 16 * zct + l16, zu);
     }
     lds_barrier();
     // ---- G <- Diag(e^{g_C}) G + Q+^T dO + K+^T Z (this wave's rows) -------------------------

@@ -1,0 +1,701 @@
+// Gradients through the matrix-core chunk path, chunk by chunk on the matrix cores.
+//
+// Training runs the chunked forward and needs its gradients ("FG2-GDN ...", sections 2-3: the WY
+// form keeps a chunk of rank-1 updates a set of dense products, which is what makes chunk-parallel
+// training possible; "Linearized 2-Simplicial Attention", method: the backward is a second scan
+// over the chunks).  With general gates (erase e, write w; u = e * k, Vt = w * v) a chunk with
+// incoming state S computes
+//   M = (I + A_ku)^{-1} (K+ S + A_kk Vt),  O = Q+ S + A_qk Vt - A_qu M,
+//   S_C = Diag(e^{g_C}) S + K^end^T Vt - U^end^T M,
+// and for the adjoint G of S_C and dO of O, reverse mode through these products gives
+//   Z     = -(I + A_ku)^{-T} (A_qu^T dO + U^end G)                 (the adjoint scan)
+//   dK+   = Z S^T,   dQ+ = dO S^T,   dK^end = Vt G^T,   dU^end = -M G^T,   dGamma = rowsum(S * G)
+//   dA_kk = strict(Z Vt^T),  dA_ku = -strict(Z M^T),  dA_qk = lower(dO Vt^T),  dA_qu = -lower(dO M^T)
+//   dVt   = A_kk^T Z + A_qk^T dO + K^end G.
+// One scalar gate per head (u = beta k, Vt = beta v) is the same algebra, so those problems run
+// the general-gate forward and adjoint scans here.  With FG2's rate (u = k~, unit gates) A_ku =
+// A_kk, A_qu = A_qk and U^end = K^end, so the adjoints merge: dA_kk = strict(Z Delta^T), dA_qk =
+// lower(dO Delta^T), dK^end = Delta G^T with Delta = Vt - M (the symmetric scan's delta), and
+// dVt = -Z.
+//
+// Kernel 1 (one workgroup of eight waves per chunk): the products above, from the chunk's
+// incoming state (stored by the forward scan), its end adjoint and Z (stored by the adjoint
+// scan), M (forward scan), dO, Vt and the packet's A_kk, A_qk, K^end; fp16 operands, fp32
+// results into the workspace.
+//
+// Kernel 2 (one workgroup of four waves per chunk): the adjoints of the Gram matrices
+// A_xy[t, i] = sum_d x_t,d y_i,d e^{g_t,d - g_i,d}:
+//   dx_t = sum_i dA[t, i] y_i e^{g_t - g_i},   dy_i = sum_t dA[t, i] x_t e^{g_t - g_i},
+// with g's adjoint taking x * dx on the row side and -y * dy on the column side.  An off-diagonal
+// 16-token block (I, J), J < I, is one product dA_IJ Y~_J (and dA_IJ^T X~_I) of operands
+// referenced inside their own block -- Y~ = y e^{g_r - g} with r the last token of J, X~ =
+// x e^{g - g_s} with s the last token before I -- scaled by e^{g_s - g_r} per channel and by the
+// row's own factor, so every factor is e^{x} with x <= 0 (no decay in (0, 1] overflows); the
+// diagonal blocks are summed element by element in fp32 with the exact factor.  Then the chain
+// rule through the decayed operands (K+ = k e^{g}: g takes K+ * dK+, and so on; e^{g_C} and the
+// end-referenced operands add their share at the chunk's last token) and the gates, and the
+// log-decay's adjoint as the reverse prefix sum of g's over the chunk.  Channels are taken 32 at a
+// time (the Gram adjoints are independent per channel); per-head gate gradients are summed over
+// channels in a fixed order, so the results are deterministic.
+
+#include "chunk_layout.h"
+#include "dr_device.h"
+#include "dr_internal.h"
+
+namespace dr {
+namespace {
+
+constexpr int kG1Threads = 512;
+constexpr int kG2Threads = 256;
+constexpr int P1 = 136;  // row stride (halves) of fp16 [*][128] LDS tiles
+constexpr int P2 = 72;   // row stride (halves) of fp16 [*][64] LDS tiles
+constexpr int QC = 32;   // channels per pass of kernel 2
+constexpr int PQ = 36;   // row stride (floats) of its fp32 [64][32] tables
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Kernel-1 results per chunk (fp32): five [C][D] matrices dK+, dQ+, dK^end, dU^end, dVt; four
+// [C][C] matrices dA_kk, dA_ku, dA_qk, dA_qu; dGamma [D].
+constexpr int64_t kGkFloats = 5 * C * D;
+constexpr int64_t kGaFloats = 4 * C * C;
+enum { GK_KP = 0, GK_QP = 1, GK_KE = 2, GK_UE = 3, GK_VT = 4 };
+enum { GA_KK = 0, GA_KU = 1, GA_QK = 2, GA_QU = 3 };
+
+struct GradWork {
+  float* gk;  // [chunks][5][C][D]
+  float* ga;  // [chunks][4][C][C]
+  float* gd;  // [chunks][D]
+};
+
+// A[row][k] = base[k][row] from a row-major tile of row stride `stride` (halves), as frag():
+// lane 16 g + l16 receives base[k0 + 8 g + 0..7][r0 + l16] (r0 % 4 == 0, stride % 4 == 0).
+__device__ __forceinline__ half8 fragT(const _Float16* base, int stride, int r0, int k0, int lane) {
+  const int m = lane & 15;
+  const int k = k0 + 8 * (lane >> 4) + (m >> 2), r = r0 + 4 * (m & 3);
+  const half4v lo = ld_tr16(base + k * stride + r);
+  const half4v hi = ld_tr16(base + (k + 4) * stride + r);
+  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Operands of v_mfma_f32_16x16x16_f16: lane l supplies A[row = l % 16][k = 4 (l / 16) + 0..3].
+__device__ __forceinline__ half4v frag4N(const _Float16* base, int stride, int r0, int k0, int lane) {
+  return *reinterpret_cast<const half4v*>(base + (r0 + (lane & 15)) * stride + k0 + 4 * (lane >> 4));
+}
+// ... and the same of A[row][k] = base[k][row]: lane 16 g + l16 receives base[k0 + 4 g + 0..3][r0 + l16].
+__device__ __forceinline__ half4v frag4T(const _Float16* base, int stride, int r0, int k0, int lane) {
+  const int m = lane & 15;
+  return ld_tr16(base + (k0 + 4 * (lane >> 4) + (m >> 2)) * stride + r0 + 4 * (m & 3));
+}
+
+__device__ __forceinline__ half4v h4(float4 x) {
+  return half4v{(_Float16)x.x, (_Float16)x.y, (_Float16)x.z, (_Float16)x.w};
+}
+
+// ------------------------------------------------------------------------------------------
+// Kernel 1: the products with the state and its adjoint, and the Gram matrices' adjoints.
+// ------------------------------------------------------------------------------------------
+template <bool FG2>
+__global__ __launch_bounds__(kG1Threads) void chunk_grad_state_kernel(Problem p, const char* __restrict__ ws,
+                                                                      const float* __restrict__ dO, GradWork gw) {
+  using PK = Packet<true, true>;
+  __shared__ __attribute__((aligned(16))) _Float16 SG[D * P1];  // S, then G: [d][j]
+  __shared__ __attribute__((aligned(16))) _Float16 ZZ[C * P1];  // Z [t][j]
+  __shared__ __attribute__((aligned(16))) _Float16 MM[C * P1];  // M (FG2: Delta) [t][j]
+  __shared__ __attribute__((aligned(16))) _Float16 DO[C * P1];  // dO [t][j]
+  __shared__ __attribute__((aligned(16))) _Float16 VV[C * P1];  // Vt [t][j]
+  __shared__ __attribute__((aligned(16))) _Float16 AK[FG2 ? 8 : C * P2];  // A_kk [t][i]
+  __shared__ __attribute__((aligned(16))) _Float16 AQ[FG2 ? 8 : C * P2];  // A_qk [t][i]
+  __shared__ __attribute__((aligned(16))) _Float16 KE[FG2 ? 8 : C * P1];  // K^end [t][d]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int64_t pkt = blockIdx.x;
+  const int nck = (p.T + C - 1) / C;
+  const int bh = int(pkt / nck), ci = int(pkt - int64_t(bh) * nck);
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int tlen = p.T - ci * C < C ? p.T - ci * C : C;
+  const int64_t tok0 = (int64_t(b) * p.T + int64_t(ci) * C) * p.H + h;
+  auto tok = [&](int t) { return tok0 + int64_t(t) * p.H; };
+  const float* Sg = p.ck_S + pkt * D * D;
+  const float* Gg = p.ck_G + pkt * D * D;
+  const _Float16* Zg = static_cast<const _Float16*>(p.ck_Z) + pkt * C * D;
+  const _Float16* Mg = static_cast<const _Float16*>(p.ck_M) + pkt * C * D;
+  float* out_k = gw.gk + pkt * kGkFloats;
+  float* out_a = gw.ga + pkt * kGaFloats;
+
+  // ---- loads ----------------------------------------------------------------------------
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {  // S: 4096 float4
+    const int f = tid + kG1Threads * i, d = f >> 5, j = (f & 31) * 4;
+    *reinterpret_cast<half4v*>(SG + d * P1 + j) = h4(*reinterpret_cast<const float4*>(Sg + d * D + j));
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // Z, M: 1024 units of 8 halves each
+    const int u = tid + kG1Threads * i, t = u >> 4, j = (u & 15) * 8;
+    *reinterpret_cast<uint4*>(ZZ + t * P1 + j) = *reinterpret_cast<const uint4*>(Zg + t * D + j);
+    *reinterpret_cast<uint4*>(MM + t * P1 + j) = *reinterpret_cast<const uint4*>(Mg + t * D + j);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // dO: 2048 float4, zero past the last token
+    const int f = tid + kG1Threads * i, t = f >> 5, j = (f & 31) * 4;
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < tlen) x = *reinterpret_cast<const float4*>(dO + tok(t) * D + j);
+    *reinterpret_cast<half4v*>(DO + t * P1 + j) = h4(x);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // Vt = w * v (FG2: sqrt(beta) v): 1024 units of 8 values
+    const int u = tid + kG1Threads * i, t = u >> 4, j = (u & 15) * 8;
+    float vf[8];
+    for (int e = 0; e < 8; ++e) vf[e] = 0.f;
+    if (t < tlen) {
+      const int64_t x = tok(t);
+      bf16x8_to_f32(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) + x * D + j), vf);
+      if (FG2) {
+        for (int e = 0; e < 8; ++e) vf[e] *= sqrtf(p.erase[x * D + j + e]);
+      } else if (p.write_channel) {
+        for (int e = 0; e < 8; ++e) vf[e] *= p.write[x * D + j + e];
+      } else {
+        const float w = p.write[x];
+        for (int e = 0; e < 8; ++e) vf[e] *= w;
+      }
+    }
+    *reinterpret_cast<half8*>(VV + t * P1 + j) = cvt8(vf);
+  }
+  if constexpr (!FG2) {
+    const char* pk = ws + pkt * PK::bytes;
+    // A_kk (packet matrix 2) and A_qk (matrix 1): six stored 16 x 32 blocks of 1 KB each
+    for (int u = tid; u < 768; u += kG1Threads) {
+      const int m = u / 384, k = (u % 384) / 64, w64 = u % 64, r = w64 >> 2;
+      const int lu = (w64 & 3) ^ ((r >> 2) & 3);
+      const int I = k < 2 ? k : 2 + ((k - 2) >> 1), Hh = k < 2 ? 0 : ((k - 2) & 1);
+      const uint4 x = *reinterpret_cast<const uint4*>(pk + PK::mat + (m ? 1 : 2) * PK::matb + 1024 * k + 16 * w64);
+      *reinterpret_cast<uint4*>((m ? AQ : AK) + (16 * I + r) * P2 + 32 * Hh + 8 * lu) = x;
+    }
+    if (tid < 256) {  // the upper blocks that the packet does not store
+      const int m = tid >> 7, r = (tid >> 2) & 31, c8 = 32 + 8 * (tid & 3);
+      *reinterpret_cast<uint4*>((m ? AQ : AK) + r * P2 + c8) = make_uint4(0, 0, 0, 0);
+    }
+    // K^end: swizzled [64][128] tile
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + kG1Threads * i, t = u >> 4, pos = u & 15;
+      *reinterpret_cast<uint4*>(KE + t * P1 + 8 * (pos ^ swz_key<16>(t))) =
+          *reinterpret_cast<const uint4*>(pk + PK::kmt + 16 * u);
+    }
+  }
+  __syncthreads();
+
+  // One 16 x 16 output tile of out[m][n] = sum_k A[m][k] Bm[n][k] over k = 0 .. 32 NK - 1 of two
+  // row-major tiles, computed transposed so that lane holds out[m0 + l16][n0 + 4 lg + 0..3].
+  auto tileNN = [&](const _Float16* A, const _Float16* Bm, int m0, int n0, int NK) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < NK; ++ks)
+      acc = mfma16x16x32(frag(Bm, P1, n0, 32 * ks, lane), frag(A, P1, m0, 32 * ks, lane), acc);
+    return acc;
+  };
+  auto store4 = [&](float* dst, f32x4 x) { *reinterpret_cast<f32x4*>(dst) = x; };
+
+  // ---- products with S, and the Gram adjoints ---------------------------------------------
+  // tasks: 32 dK+ tiles, 32 dQ+ tiles, then 16 tiles of each Gram adjoint (upper ones zero)
+  constexpr int NA = FG2 ? 2 : 4;
+  for (int n = wave; n < 64 + 16 * NA; n += 8) {
+    if (n < 64) {
+      const int q = n >> 5, tm = (n >> 3) & 3, tn = n & 7;
+      const f32x4 acc = tileNN(q ? DO : ZZ, SG, 16 * tm, 16 * tn, 4);
+      store4(out_k + ((q ? GK_QP : GK_KP) * C + 16 * tm + l16) * D + 16 * tn + 4 * lg, acc);
+    } else {
+      const int a = (n - 64) >> 4, tm = ((n - 64) >> 2) & 3, tn = (n - 64) & 3;
+      // FG2: dA_kk = Z Delta^T, dA_qk = dO Delta^T; general: Z Vt^T, -Z M^T, dO Vt^T, -dO M^T
+      const int which = FG2 ? (a ? GA_QK : GA_KK) : a == 0 ? GA_KK : a == 1 ? GA_KU : a == 2 ? GA_QK : GA_QU;
+      const bool rowz = which == GA_KK || which == GA_KU;
+      const bool colm = FG2 || which == GA_KU || which == GA_QU;
+      const float sgn = (!FG2 && colm) ? -1.f : 1.f;
+      const bool strict = which == GA_KK || which == GA_KU;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (tn <= tm) {
+        acc = tileNN(rowz ? ZZ : DO, colm ? MM : VV, 16 * tm, 16 * tn, 4);
+        const int t = 16 * tm + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * tn + 4 * lg + r;
+          acc[r] = (i < t || (!strict && i == t)) ? sgn * acc[r] : 0.f;
+        }
+      }
+      store4(out_a + (which * C + 16 * tm + l16) * C + 16 * tn + 4 * lg, acc);
+    }
+  }
+  // dVt's tiles are kept by their wave across the load of G: wave w owns tiles w, w + 8, ...
+  f32x4 dvt[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) dvt[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (!FG2) {
+    // A_kk^T Z + A_qk^T dO: out[t][j] = sum_i A[i][t] X[i][j], transposed as above
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int n = wave + 8 * k, tm = n >> 3, tn = n & 7;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        acc = mfma16x16x32(fragT(ZZ, P1, 16 * tn, 32 * ks, lane), fragT(AK, P2, 16 * tm, 32 * ks, lane), acc);
+        acc = mfma16x16x32(fragT(DO, P1, 16 * tn, 32 * ks, lane), fragT(AQ, P2, 16 * tm, 32 * ks, lane), acc);
+      }
+      dvt[k] = acc;
+    }
+  }
+  __syncthreads();
+
+  // ---- G, and dGamma = rowsum(S * G) in fp32 -----------------------------------------------
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int f = tid + kG1Threads * i, d = f >> 5, j = (f & 31) * 4;
+    const float4 g4 = *reinterpret_cast<const float4*>(Gg + d * D + j);
+    const float4 s4 = *reinterpret_cast<const float4*>(Sg + d * D + j);
+    *reinterpret_cast<half4v*>(SG + d * P1 + j) = h4(g4);
+    float x = g4.x * s4.x + g4.y * s4.y + g4.z * s4.z + g4.w * s4.w;
+    // the 32 threads of row d are lanes 32 (lane / 32) .. + 31 of one wave
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    if ((lane & 31) == 0) gw.gd[pkt * D + d] = x;
+  }
+  __syncthreads();
+
+  // ---- products with G ------------------------------------------------------------------
+  for (int n = wave; n < (FG2 ? 32 : 64); n += 8) {
+    const int q = n >> 5, tm = (n >> 3) & 3, tn = n & 7;
+    // dK^end = Vt G^T (FG2: Delta G^T); dU^end = -M G^T
+    f32x4 acc = tileNN((q || FG2) ? MM : VV, SG, 16 * tm, 16 * tn, 4);
+    if (q) acc = -acc;
+    store4(out_k + ((q ? GK_UE : GK_KE) * C + 16 * tm + l16) * D + 16 * tn + 4 * lg, acc);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int n = wave + 8 * k, tm = n >> 3, tn = n & 7;
+    f32x4 acc = dvt[k];
+    if constexpr (FG2) {
+      // dVt = -Z
+      const _Float16* z = ZZ + (16 * tm + l16) * P1 + 16 * tn + 4 * lg;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = -float(z[r]);
+    } else {
+      // + K^end G: out[t][j] = sum_d KE[t][d] G[d][j]
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc = mfma16x16x32(fragT(SG, P1, 16 * tn, 32 * ks, lane), frag(KE, P1, 16 * tm, 32 * ks, lane), acc);
+    }
+    store4(out_k + (GK_VT * C + 16 * tm + l16) * D + 16 * tn + 4 * lg, acc);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Kernel 2: the Gram adjoints with their decays, the chain rule, the outputs.
+// ------------------------------------------------------------------------------------------
+template <bool DCH, bool FG2>
+__global__ __launch_bounds__(kG2Threads) void chunk_grad_gram_kernel(Problem p, BwdArgs g, GradWork gw) {
+  constexpr int NA = FG2 ? 2 : 4;  // Gram adjoints held: kk, qk (, ku, qu)
+  __shared__ __attribute__((aligned(16))) _Float16 DA[4][C * P2];  // dA_kk, dA_ku, dA_qk, dA_qu [t][i]
+  __shared__ __attribute__((aligned(16))) float GL[C * PQ];   // g log2(e), this pass's channels
+  __shared__ __attribute__((aligned(16))) float XK[C * PQ];   // k (FG2: k~)
+  __shared__ __attribute__((aligned(16))) float XQ[C * PQ];   // q
+  __shared__ __attribute__((aligned(16))) float XU[FG2 ? 4 : C * PQ];   // u = e * k
+  __shared__ __attribute__((aligned(16))) _Float16 XT[2][QC * P2];  // X~^T of k, q: [c][t]
+  __shared__ __attribute__((aligned(16))) _Float16 YT[2][QC * P2];  // Y~^T of k, u: [c][i]
+  __shared__ __attribute__((aligned(16))) float DG[C * PQ];   // g's adjoint
+  __shared__ __attribute__((aligned(16))) float GN[4 * QC];   // end-referenced shares, per block
+  __shared__ float SUMS[3][C];                                // per-head decay / erase / write sums
+  __shared__ float TOT[8 * QC];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int64_t pkt = blockIdx.x;
+  const int nck = (p.T + C - 1) / C;
+  const int bh = int(pkt / nck), ci = int(pkt - int64_t(bh) * nck);
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int tlen = p.T - ci * C < C ? p.T - ci * C : C;
+  const int64_t tok0 = (int64_t(b) * p.T + int64_t(ci) * C) * p.H + h;
+  auto tok = [&](int t) { return tok0 + int64_t(t) * p.H; };
+  const float* gk = gw.gk + pkt * kGkFloats;
+  const float* ga = gw.ga + pkt * kGaFloats;
+  const bool shared_gate = g.dwrite == nullptr;  // write gate == erase gate
+
+  // the Gram adjoints, fp16
+  for (int f = tid; f < NA * C * C / 4; f += kG2Threads) {
+    const int m = f / (C * C / 4), r = f % (C * C / 4), t = r >> 4, i = (r & 15) * 4;
+    const int src = FG2 ? (m ? GA_QK : GA_KK) : m;
+    const int dst = FG2 ? (m ? GA_QK : GA_KK) : m;
+    *reinterpret_cast<half4v*>(DA[dst] + t * P2 + i) = h4(*reinterpret_cast<const float4*>(ga + (src * C + t) * C + i));
+  }
+  if (tid < C) {
+    SUMS[0][tid] = 0.f;
+    SUMS[1][tid] = 0.f;
+    SUMS[2][tid] = 0.f;
+  }
+
+  const int blk = wave;  // this wave's 16-token block
+  const int t_own = 16 * blk + l16;
+  const bool own_ok = t_own < tlen;
+  for (int qc = 0; qc < D / QC; ++qc) {
+    const int c0 = QC * qc;
+    // ---- g (cumulative log-decay, log2 units), k, q, u of this pass's channels ----------
+    {
+      const int c = tid & 31, seg = tid >> 5;  // tokens 8 seg .. + 7 of channel c
+      float acc = 0.f, gl[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = 8 * seg + e;
+        float la = 0.f;
+        if (t < tlen) la = DCH ? p.log_decay[tok(t) * D + c0 + c] : p.log_decay[tok(t)];
+        acc += la;
+        gl[e] = acc;
+      }
+      TOT[seg * QC + c] = acc;
+      __syncthreads();
+      float base = 0.f;
+      for (int s2 = 0; s2 < seg; ++s2) base += TOT[s2 * QC + c];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) GL[(8 * seg + e) * PQ + c] = (base + gl[e]) * kLog2e;
+    }
+    {
+      const int t = tid >> 2, c8 = (tid & 3) * 8;  // 8 channels of token t
+      float kf[8], qf[8], uf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[e] = qf[e] = uf[e] = 0.f;
+      if (t < tlen) {
+        const int64_t x = tok(t) * D + c0 + c8;
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + x), kf);
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + x), qf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (FG2) {
+            kf[e] *= sqrtf(p.erase[x + e]);
+          } else {
+            uf[e] = kf[e] * (p.erase_channel ? p.erase[x + e] : p.erase[tok(t)]);
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        XK[t * PQ + c8 + e] = kf[e];
+        XQ[t * PQ + c8 + e] = qf[e];
+        if constexpr (!FG2) XU[t * PQ + c8 + e] = uf[e];
+      }
+    }
+    __syncthreads();
+    // ---- operands referenced inside their own block ---------------------------------------
+    {
+      const int c = tid & 31, t8 = (tid >> 5) * 8;
+      half8 xk, xq, yk, yu;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = t8 + e, blk_t = t >> 4;
+        const float gt = GL[t * PQ + c];
+        // X~ = x e^{g - g_s} (s = 16 I - 1, I >= 1); Y~ = y e^{g_r - g} (r = 16 J + 15, J <= 2)
+        const float fx = blk_t >= 1 ? exp2f(gt - GL[(16 * blk_t - 1) * PQ + c]) : 0.f;
+        const float fy = blk_t <= 2 ? exp2f(GL[(16 * blk_t + 15) * PQ + c] - gt) : 0.f;
+        xk[e] = (_Float16)(XK[t * PQ + c] * fx);
+        xq[e] = (_Float16)(XQ[t * PQ + c] * fx);
+        yk[e] = (_Float16)(XK[t * PQ + c] * fy);
+        yu[e] = FG2 ? (_Float16)0.f : (_Float16)(XU[t * PQ + c] * fy);
+      }
+      *reinterpret_cast<half8*>(XT[0] + c * P2 + t8) = xk;
+      *reinterpret_cast<half8*>(XT[1] + c * P2 + t8) = xq;
+      *reinterpret_cast<half8*>(YT[0] + c * P2 + t8) = yk;
+      *reinterpret_cast<half8*>(YT[1] + c * P2 + t8) = yu;
+    }
+    __syncthreads();
+
+    // ---- this wave's block: lane holds token t_own and channels c0 + 16 ct + 4 lg + r -------
+    f32x4 rowK[2], rowQ[2], colK[2], colU[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int cc = 16 * ct;  // channel tile within the pass
+      f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = rk, ck = rk, cu = rk;
+      // row side: blocks J < blk
+      for (int J = 0; J < blk; ++J) {
+        const half4v yk = frag4N(YT[0], P2, cc, 16 * J, lane), yu = frag4N(YT[1], P2, cc, 16 * J, lane);
+        f32x4 ak = mfma16(yk, frag4N(DA[GA_KK], P2, 16 * blk, 16 * J, lane), f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 aq = mfma16(yk, frag4N(DA[GA_QK], P2, 16 * blk, 16 * J, lane), f32x4{0.f, 0.f, 0.f, 0.f});
+        if constexpr (!FG2) {
+          ak = mfma16(yu, frag4N(DA[GA_KU], P2, 16 * blk, 16 * J, lane), ak);
+          aq = mfma16(yu, frag4N(DA[GA_QU], P2, 16 * blk, 16 * J, lane), aq);
+        }
+        const int s = 16 * blk - 1, r = 16 * J + 15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = cc + 4 * lg + e;
+          const float F = s == r ? 1.f : exp2f(GL[s * PQ + c] - GL[r * PQ + c]);
+          rk[e] = fmaf(F, ak[e], rk[e]);
+          rq[e] = fmaf(F, aq[e], rq[e]);
+        }
+      }
+      // column side: blocks I > blk
+      for (int I = blk + 1; I < 4; ++I) {
+        const half4v xk = frag4N(XT[0], P2, cc, 16 * I, lane), xq = frag4N(XT[1], P2, cc, 16 * I, lane);
+        f32x4 ak = mfma16(xk, frag4T(DA[GA_KK], P2, 16 * blk, 16 * I, lane), f32x4{0.f, 0.f, 0.f, 0.f});
+        ak = mfma16(xq, frag4T(DA[GA_QK], P2, 16 * blk, 16 * I, lane), ak);
+        f32x4 au = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (!FG2) {
+          au = mfma16(xk, frag4T(DA[GA_KU], P2, 16 * blk, 16 * I, lane), au);
+          au = mfma16(xq, frag4T(DA[GA_QU], P2, 16 * blk, 16 * I, lane), au);
+        }
+        const int s = 16 * I - 1, r = 16 * blk + 15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = cc + 4 * lg + e;
+          const float F = s == r ? 1.f : exp2f(GL[s * PQ + c] - GL[r * PQ + c]);
+          ck[e] = fmaf(F, ak[e], ck[e]);
+          cu[e] = fmaf(F, au[e], cu[e]);
+        }
+      }
+      // the rows' own factors
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = cc + 4 * lg + e;
+        const float gt = GL[t_own * PQ + c];
+        const float fr = blk > 0 ? exp2f(gt - GL[(16 * blk - 1) * PQ + c]) : 0.f;
+        const float fc = blk < 3 ? exp2f(GL[(16 * blk + 15) * PQ + c] - gt) : 0.f;
+        rk[e] *= fr;
+        rq[e] *= fr;
+        ck[e] *= fc;
+        cu[e] *= fc;
+      }
+      rowK[ct] = rk;
+      rowQ[ct] = rq;
+      colK[ct] = ck;
+      colU[ct] = cu;
+    }
+    // diagonal block, element by element: row side pairs (t_own, i), column side (t, t_own)
+    for (int i2 = 0; i2 < 16; ++i2) {
+      const int o = 16 * blk + i2;
+      const bool row_ok = i2 <= l16, col_ok = i2 >= l16;
+      const float r_kk = float(DA[GA_KK][t_own * P2 + o]), r_qk = float(DA[GA_QK][t_own * P2 + o]);
+      const float c_kk = float(DA[GA_KK][o * P2 + t_own]), c_qk = float(DA[GA_QK][o * P2 + t_own]);
+      float r_ku = 0.f, r_qu = 0.f, c_ku = 0.f, c_qu = 0.f;
+      if constexpr (!FG2) {
+        r_ku = float(DA[GA_KU][t_own * P2 + o]);
+        r_qu = float(DA[GA_QU][t_own * P2 + o]);
+        c_ku = float(DA[GA_KU][o * P2 + t_own]);
+        c_qu = float(DA[GA_QU][o * P2 + t_own]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const f32x4 go = *reinterpret_cast<const f32x4*>(GL + o * PQ + 16 * ct + 4 * lg);
+        const f32x4 gt = *reinterpret_cast<const f32x4*>(GL + t_own * PQ + 16 * ct + 4 * lg);
+        const f32x4 ko = *reinterpret_cast<const f32x4*>(XK + o * PQ + 16 * ct + 4 * lg);
+        const f32x4 qo = *reinterpret_cast<const f32x4*>(XQ + o * PQ + 16 * ct + 4 * lg);
+        f32x4 uo = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (!FG2) uo = *reinterpret_cast<const f32x4*>(XU + o * PQ + 16 * ct + 4 * lg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // e^{g_t - g_o} for o <= t (row side) and e^{g_o - g_t} for o >= t (column side)
+          const float er = row_ok ? exp2f(gt[e] - go[e]) : 0.f;
+          const float ec = col_ok ? exp2f(go[e] - gt[e]) : 0.f;
+          rowK[ct][e] = fmaf(er, fmaf(r_kk, ko[e], r_ku * uo[e]), rowK[ct][e]);
+          rowQ[ct][e] = fmaf(er, fmaf(r_qk, ko[e], r_qu * uo[e]), rowQ[ct][e]);
+          colK[ct][e] = fmaf(ec, fmaf(c_kk, ko[e], c_qk * qo[e]), colK[ct][e]);
+          colU[ct][e] = fmaf(ec, fmaf(c_ku, ko[e], c_qu * qo[e]), colU[ct][e]);
+        }
+      }
+    }
+
+    // ---- chain rule, outputs ------------------------------------------------------------
+    float s_e = 0.f, s_w = 0.f, s_g = 0.f;  // per-head sums over this lane's channels
+    f32x4 gn_part[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int cl = 16 * ct + 4 * lg;  // channel within the pass
+      const int64_t x = tok(own_ok ? t_own : 0) * D + c0 + cl;
+      const f32x4 gt = *reinterpret_cast<const f32x4*>(GL + t_own * PQ + cl);
+      const f32x4 gC = *reinterpret_cast<const f32x4*>(GL + 63 * PQ + cl);
+      const f32x4 kk = *reinterpret_cast<const f32x4*>(XK + t_own * PQ + cl);
+      const f32x4 qq = *reinterpret_cast<const f32x4*>(XQ + t_own * PQ + cl);
+      f32x4 uu = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (!FG2) uu = *reinterpret_cast<const f32x4*>(XU + t_own * PQ + cl);
+      const f32x4 dkp = *reinterpret_cast<const f32x4*>(gk + (GK_KP * C + t_own) * D + c0 + cl);
+      const f32x4 dqp = *reinterpret_cast<const f32x4*>(gk + (GK_QP * C + t_own) * D + c0 + cl);
+      const f32x4 dke = *reinterpret_cast<const f32x4*>(gk + (GK_KE * C + t_own) * D + c0 + cl);
+      f32x4 due = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (!FG2) due = *reinterpret_cast<const f32x4*>(gk + (GK_UE * C + t_own) * D + c0 + cl);
+      const f32x4 dvt = *reinterpret_cast<const f32x4*>(gk + (GK_VT * C + t_own) * D + c0 + cl);
+      f32x4 o_dq, o_dk, o_dv, o_de, gnp, o_dw = {0.f, 0.f, 0.f, 0.f};
+      float vv[4] = {0.f, 0.f, 0.f, 0.f}, ee[4] = {1.f, 1.f, 1.f, 1.f}, ww[4] = {1.f, 1.f, 1.f, 1.f};
+      float rt[4] = {1.f, 1.f, 1.f, 1.f}, kraw[4] = {0.f, 0.f, 0.f, 0.f};
+      if (own_ok) {
+        const uint2 vb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.v) + x);
+        vv[0] = __uint_as_float(vb.x << 16);
+        vv[1] = __uint_as_float(vb.x & 0xffff0000u);
+        vv[2] = __uint_as_float(vb.y << 16);
+        vv[3] = __uint_as_float(vb.y & 0xffff0000u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (FG2) {
+            rt[e] = sqrtf(p.erase[x + e]);
+          } else {
+            ee[e] = p.erase_channel ? p.erase[x + e] : p.erase[tok(t_own)];
+            ww[e] = p.write_channel ? p.write[x + e] : p.write[tok(t_own)];
+          }
+        }
+        if (FG2) {
+          const uint2 kb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.k) + x);
+          kraw[0] = __uint_as_float(kb.x << 16);
+          kraw[1] = __uint_as_float(kb.x & 0xffff0000u);
+          kraw[2] = __uint_as_float(kb.y << 16);
+          kraw[3] = __uint_as_float(kb.y & 0xffff0000u);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float eg = exp2f(gt[e]), egn = exp2f(gC[e] - gt[e]);
+        const float a_kp = eg * dkp[e], a_qp = eg * dqp[e], a_ke = egn * dke[e], a_ue = egn * due[e];
+        const float dkap = a_kp + a_ke + rowK[ct][e] + colK[ct][e];
+        const float du = a_ue + colU[ct][e];
+        o_dq[e] = a_qp + rowQ[ct][e];
+        const float dg = kk[e] * (a_kp - a_ke + rowK[ct][e] - colK[ct][e]) + qq[e] * (a_qp + rowQ[ct][e]) -
+                         uu[e] * (a_ue + colU[ct][e]);
+        gnp[e] = kk[e] * a_ke + uu[e] * a_ue;
+        DG[t_own * PQ + cl + e] = dg;
+        if (FG2) {
+          o_dk[e] = rt[e] * dkap;
+          o_dv[e] = rt[e] * dvt[e];
+          o_de[e] = (kraw[e] * dkap + vv[e] * dvt[e]) / (2.f * rt[e]);
+        } else {
+          o_dk[e] = fmaf(ee[e], du, dkap);
+          o_de[e] = kk[e] * du;
+          o_dv[e] = ww[e] * dvt[e];
+          o_dw[e] = vv[e] * dvt[e];
+          if (shared_gate) o_de[e] += o_dw[e];
+        }
+        s_e += o_de[e];
+        s_w += o_dw[e];
+        s_g += dg;
+      }
+      gn_part[ct] = gnp;
+      if (own_ok) {
+        *reinterpret_cast<f32x4*>(g.dq + x) = o_dq;
+        *reinterpret_cast<f32x4*>(g.dk + x) = o_dk;
+        *reinterpret_cast<f32x4*>(g.dv + x) = o_dv;
+        if (FG2 || p.erase_channel) *reinterpret_cast<f32x4*>(g.derase + x) = o_de;
+        if (!FG2 && !shared_gate && p.write_channel) *reinterpret_cast<f32x4*>(g.dwrite + x) = o_dw;
+      }
+    }
+    // end-referenced shares: sum over the block's 16 tokens (lanes of one lg group), per channel
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = gn_part[ct][e];
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+        if (l16 == 0) GN[blk * QC + 16 * ct + 4 * lg + e] = v;
+      }
+    // per-head gates and decay: sums over this pass's channels (the four lane groups of token t)
+    if (!DCH || !(FG2 || p.erase_channel) || (!FG2 && !shared_gate && !p.write_channel)) {
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        s_e += __shfl_xor(s_e, o);
+        s_w += __shfl_xor(s_w, o);
+        s_g += __shfl_xor(s_g, o);
+      }
+      if (lg == 0) {
+        SUMS[0][t_own] += s_g;
+        SUMS[1][t_own] += s_e;
+        SUMS[2][t_own] += s_w;
+      }
+    }
+    __syncthreads();
+    // ---- the log-decay's adjoint: reverse prefix sum over the chunk, plus the end shares -----
+    if constexpr (DCH) {
+      const int c = tid & 31, seg = tid >> 5;
+      float sfx[8], acc = 0.f;
+#pragma unroll
+      for (int e = 7; e >= 0; --e) {
+        acc += DG[(8 * seg + e) * PQ + c];
+        sfx[e] = acc;
+      }
+      __syncthreads();
+      TOT[seg * QC + c] = acc;
+      __syncthreads();
+      float base = 0.f;
+      for (int s2 = seg + 1; s2 < 8; ++s2) base += TOT[s2 * QC + c];
+      // g_C's share: e^{g_C} dGamma and the end-referenced operands' sum
+      const float gC = GL[63 * PQ + c];
+      const float dgn = exp2f(gC) * gw.gd[pkt * D + c0 + c] + GN[c] + GN[QC + c] + GN[2 * QC + c] + GN[3 * QC + c];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = 8 * seg + e;
+        if (t < tlen) g.dlog_decay[tok(t) * D + c0 + c] = base + sfx[e] + dgn;
+      }
+    } else {
+      if (tid < QC) {
+        const int c = tid;
+        const float dgn = exp2f(GL[63 * PQ + c]) * gw.gd[pkt * D + c0 + c] + GN[c] + GN[QC + c] + GN[2 * QC + c] +
+                          GN[3 * QC + c];
+        TOT[c] = dgn;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        float s = 0.f;
+        for (int c = 0; c < QC; ++c) s += TOT[c];
+        TOT[QC] = s;
+      }
+      __syncthreads();
+      if (tid == 0) SUMS[0][63] += TOT[QC];  // added at the last row: every earlier token's suffix takes it
+    }
+    __syncthreads();
+  }
+
+  // ---- per-head sums ----------------------------------------------------------------------
+  if (tid < C) {
+    const int t = tid;
+    if (!DCH) {
+      float s = 0.f;
+      for (int t2 = C - 1; t2 >= t; --t2) s += SUMS[0][t2];
+      if (t < tlen) g.dlog_decay[tok(t)] = s;
+    }
+    if (t < tlen) {
+      if (!FG2 && !p.erase_channel) g.derase[tok(t)] = SUMS[1][t];
+      if (!FG2 && !shared_gate && !p.write_channel) g.dwrite[tok(t)] = SUMS[2][t];
+    }
+  }
+}
+
+template <bool FG2>
+void launch_state(const Problem& p, const char* ws, const float* dO, GradWork gw, int64_t nchunks,
+                  hipStream_t stream) {
+  hipLaunchKernelGGL((chunk_grad_state_kernel<FG2>), dim3(unsigned(nchunks)), dim3(kG1Threads), 0, stream, p, ws,
+                     dO, gw);
+}
+
+template <bool DCH, bool FG2>
+void launch_gram(const Problem& p, const BwdArgs& g, GradWork gw, int64_t nchunks, hipStream_t stream) {
+  hipLaunchKernelGGL((chunk_grad_gram_kernel<DCH, FG2>), dim3(unsigned(nchunks)), dim3(kG2Threads), 0, stream, p, g,
+                     gw);
+}
+
+}  // namespace
+
+size_t chunk_grad_work_bytes(const Problem& p) {
+  const int64_t nchunks = int64_t(p.B) * p.H * ((int64_t(p.T) + C - 1) / C);
+  return size_t(nchunks * (kGkFloats + kGaFloats + D) * 4);
+}
+
+hipError_t launch_chunk_grad(const Problem& p, const BwdArgs& g, const void* packets, void* work,
+                             hipStream_t stream) {
+  const int64_t nchunks = int64_t(p.B) * p.H * ((int64_t(p.T) + C - 1) / C);
+  if (nchunks == 0) return hipSuccess;
+  float* w = static_cast<float*>(work);
+  GradWork gw{w, w + nchunks * kGkFloats, w + nchunks * (kGkFloats + kGaFloats)};
+  const char* ws = static_cast<const char*>(packets);
+  if (p.rate_sqrt) {
+    launch_state<true>(p, ws, g.dO, gw, nchunks, stream);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    if (p.decay_channel) launch_gram<true, true>(p, g, gw, nchunks, stream);
+    else launch_gram<false, true>(p, g, gw, nchunks, stream);
+  } else {
+    launch_state<false>(p, ws, g.dO, gw, nchunks, stream);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    if (p.decay_channel) launch_gram<true, false>(p, g, gw, nchunks, stream);
+    else launch_gram<false, false>(p, g, gw, nchunks, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dr

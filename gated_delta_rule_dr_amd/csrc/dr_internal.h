@@ -40,6 +40,11 @@ struct Problem {
   // its adjoint at the end of every chunk (adjoint scan), fp32 [packet][dk][dv]; null otherwise.
   float* ck_S = nullptr;
   float* ck_G = nullptr;
+  // ... and, as fp16 [packet][token][dv], the forward's in-chunk reads M (general gates; with
+  // FG2's rate the symmetric scan's delta instead) and the adjoint scan's Z (the adjoint of
+  // K+ S + A_kk Vt); null otherwise.
+  void* ck_M = nullptr;
+  void* ck_Z = nullptr;
 };
 
 // Sequence tables of a packed batch (one workgroup): from nseq + 1 device offsets `cu` over T
@@ -98,10 +103,15 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(const Problem& p);
 hipError_t launch_bwd(const Problem& p, const BwdArgs& g, void* workspace, hipStream_t stream);
 // Gradients through the matrix-core chunk path (bf16 q/k/v, dk == dv == 128, a dense batch): the
-// chunked forward stores the state at every chunk start, the adjoint scan the state's adjoint
-// at every chunk end, and the adjoint of the token loop then runs every chunk in parallel.
+// chunked forward stores every chunk's incoming state and in-chunk reads, the adjoint scan every
+// chunk's end adjoint and Z, and each chunk's gradients then follow on the matrix cores.
 size_t bwd_chunked_workspace_bytes(const Problem& p);
 hipError_t launch_bwd_chunked(const Problem& p, const BwdArgs& g, void* workspace, hipStream_t stream);
+// The per-chunk gradient kernels (p carries ck_S, ck_G, ck_M, ck_Z; `packets` the forward's
+// packets; `work` chunk_grad_work_bytes(p) bytes).
+size_t chunk_grad_work_bytes(const Problem& p);
+hipError_t launch_chunk_grad(const Problem& p, const BwdArgs& g, const void* packets, void* work,
+                             hipStream_t stream);
 // The same over p.B packed sequences delimited by the device offsets `cu` (p.T packed tokens).
 size_t bwd_varlen_workspace_bytes(const Problem& p);
 hipError_t launch_bwd_varlen(Problem p, const int* cu, const BwdArgs& g, void* workspace, hipStream_t stream);
