@@ -112,7 +112,7 @@ def time_backward(dr, torch, wl, steps, warmup, chunk=64):
     dO = torch.randn((wl.B, wl.T, wl.H, wl.dv), generator=g, device="cuda")
     dST = torch.randn((wl.B, wl.H, wl.dk, wl.dv), generator=g, device="cuda")
     call = lambda: dr.chunk_bwd(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], x["write"], x["S0"],
-                                dO=dO, dS_T=dST, chunk=chunk)
+                                dO=dO, dS_T=dST, chunk=chunk, fg2=wl.rate_sqrt)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -131,14 +131,18 @@ def cpu_baseline_backward(wl, tokens):
     from threadpoolctl import threadpool_limits
 
     from gated_delta_rule_dr_amd.workloads import generate
-    from oracle import recurrence_bwd
+    from oracle import recurrence_bwd, recurrence_fg2_bwd
 
     sample = wl.replace(T=tokens)
     inp = generate(sample)
     dO = _dO_sample(sample)
     with threadpool_limits(1):
         t0 = time.perf_counter()
-        recurrence_bwd(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"], inp["S0"], dO=dO)
+        if wl.rate_sqrt:
+            recurrence_fg2_bwd(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["S0"], dO)
+        else:
+            recurrence_bwd(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"], inp["S0"],
+                           dO=dO)
         sec = time.perf_counter() - t0
     return dict(value=sample.token_heads / sec, unit="tokens/s", cores=1, kind="oracle",
                 sample=f"{sample.B}x{sample.H} heads x first {tokens} tokens of {wl.name} "

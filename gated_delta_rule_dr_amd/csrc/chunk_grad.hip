@@ -46,11 +46,9 @@ namespace dr {
 namespace {
 
 constexpr int kG1Threads = 512;
-constexpr int kG2Threads = 256;
+constexpr int kG2Threads = 512;
 constexpr int P1 = 136;  // row stride (halves) of fp16 [*][128] LDS tiles
 constexpr int P2 = 72;   // row stride (halves) of fp16 [*][64] LDS tiles
-constexpr int QC = 32;   // channels per pass of kernel 2
-constexpr int PQ = 36;   // row stride (floats) of its fp32 [64][32] tables
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Kernel-1 results per chunk (fp32): five [C][D] matrices dK+, dQ+, dK^end, dU^end, dVt; four
@@ -290,21 +288,21 @@ __global__ __launch_bounds__(kG1Threads) void chunk_grad_state_kernel(Problem p,
 // ------------------------------------------------------------------------------------------
 template <bool DCH, bool FG2>
 __global__ __launch_bounds__(kG2Threads) void chunk_grad_gram_kernel(Problem p, BwdArgs g, GradWork gw) {
-  constexpr int NA = FG2 ? 2 : 4;  // Gram adjoints held: kk, qk (, ku, qu)
-  __shared__ __attribute__((aligned(16))) _Float16 DA[4][C * P2];  // dA_kk, dA_ku, dA_qk, dA_qu [t][i]
-  __shared__ __attribute__((aligned(16))) float GL[C * PQ];   // g log2(e), this pass's channels
-  __shared__ __attribute__((aligned(16))) float XK[C * PQ];   // k (FG2: k~)
-  __shared__ __attribute__((aligned(16))) float XQ[C * PQ];   // q
-  __shared__ __attribute__((aligned(16))) float XU[FG2 ? 4 : C * PQ];   // u = e * k
-  __shared__ __attribute__((aligned(16))) _Float16 XT[2][QC * P2];  // X~^T of k, q: [c][t]
-  __shared__ __attribute__((aligned(16))) _Float16 YT[2][QC * P2];  // Y~^T of k, u: [c][i]
-  __shared__ __attribute__((aligned(16))) float DG[C * PQ];   // g's adjoint
-  __shared__ __attribute__((aligned(16))) float GN[4 * QC];   // end-referenced shares, per block
-  __shared__ float SUMS[3][C];                                // per-head decay / erase / write sums
-  __shared__ float TOT[8 * QC];
+  constexpr int NA = FG2 ? 2 : 4;      // Gram adjoints held: kk, qk (, ku, qu)
+  constexpr int GS = D + 4;            // row stride (floats) of the per-channel g table
+  __shared__ __attribute__((aligned(16))) _Float16 DA[4][C * P2];      // dA_kk, dA_ku, dA_qk, dA_qu [t][i]
+  __shared__ __attribute__((aligned(16))) float GL[DCH ? C * GS : C];  // g log2(e) [t][c] (or [t])
+  __shared__ __attribute__((aligned(16))) _Float16 XK[C * P1];         // k (FG2: k~) [t][c]
+  __shared__ __attribute__((aligned(16))) _Float16 XQ[C * P1];         // q
+  __shared__ __attribute__((aligned(16))) _Float16 XU[FG2 ? 8 : C * P1];  // u = e * k
+  __shared__ __attribute__((aligned(16))) float BT[4][D];   // per block: g-adjoint totals, then shares
+  __shared__ __attribute__((aligned(16))) float GNS[4][D];  // per block: end-referenced shares
+  __shared__ float RED[3][2][C];                            // per-head sums (decay, erase, write)
+  __shared__ float MISC[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
+  const int blk = wave & 3, hc = wave >> 2;  // this wave's 16 tokens and 64 channels
   const int64_t pkt = blockIdx.x;
   const int nck = (p.T + C - 1) / C;
   const int bh = int(pkt / nck), ci = int(pkt - int64_t(bh) * nck);
@@ -315,345 +313,365 @@ __global__ __launch_bounds__(kG2Threads) void chunk_grad_gram_kernel(Problem p, 
   const float* gk = gw.gk + pkt * kGkFloats;
   const float* ga = gw.ga + pkt * kGaFloats;
   const bool shared_gate = g.dwrite == nullptr;  // write gate == erase gate
+  const int t_own = 16 * blk + l16;
+  const bool own_ok = t_own < tlen;
+  const int64_t x_own = tok(own_ok ? t_own : 0) * D;  // row of this lane's token (token 0 when padded)
 
   // the Gram adjoints, fp16
   for (int f = tid; f < NA * C * C / 4; f += kG2Threads) {
     const int m = f / (C * C / 4), r = f % (C * C / 4), t = r >> 4, i = (r & 15) * 4;
-    const int src = FG2 ? (m ? GA_QK : GA_KK) : m;
-    const int dst = FG2 ? (m ? GA_QK : GA_KK) : m;
-    *reinterpret_cast<half4v*>(DA[dst] + t * P2 + i) = h4(*reinterpret_cast<const float4*>(ga + (src * C + t) * C + i));
+    const int which = FG2 ? (m ? GA_QK : GA_KK) : m;
+    *reinterpret_cast<half4v*>(DA[which] + t * P2 + i) = h4(*reinterpret_cast<const float4*>(ga + (which * C + t) * C + i));
   }
-  if (tid < C) {
-    SUMS[0][tid] = 0.f;
-    SUMS[1][tid] = 0.f;
-    SUMS[2][tid] = 0.f;
+  // k, q, u of every channel, fp16
+  {
+    const int t = tid >> 3, c16 = (tid & 7) * 16;
+    float kf[16], qf[16], uf[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) kf[e] = qf[e] = uf[e] = 0.f;
+    if (t < tlen) {
+      const int64_t x = tok(t) * D + c16;
+      const uint16_t* kp = static_cast<const uint16_t*>(p.k) + x;
+      const uint16_t* qp = static_cast<const uint16_t*>(p.q) + x;
+      bf16x8_to_f32(*reinterpret_cast<const uint4*>(kp), kf);
+      bf16x8_to_f32(*reinterpret_cast<const uint4*>(kp + 8), kf + 8);
+      bf16x8_to_f32(*reinterpret_cast<const uint4*>(qp), qf);
+      bf16x8_to_f32(*reinterpret_cast<const uint4*>(qp + 8), qf + 8);
+      if (FG2 || p.erase_channel) {
+        float ef[16];
+#pragma unroll
+        for (int e = 0; e < 16; e += 4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(p.erase + x + e);
+          ef[e] = v4.x; ef[e + 1] = v4.y; ef[e + 2] = v4.z; ef[e + 3] = v4.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (FG2) kf[e] *= sqrtf(ef[e]);
+          else uf[e] = kf[e] * ef[e];
+        }
+      } else {
+        const float e1 = p.erase[tok(t)];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) uf[e] = kf[e] * e1;
+      }
+    }
+    *reinterpret_cast<half8*>(XK + t * P1 + c16) = cvt8(kf);
+    *reinterpret_cast<half8*>(XK + t * P1 + c16 + 8) = cvt8(kf + 8);
+    *reinterpret_cast<half8*>(XQ + t * P1 + c16) = cvt8(qf);
+    *reinterpret_cast<half8*>(XQ + t * P1 + c16 + 8) = cvt8(qf + 8);
+    if constexpr (!FG2) {
+      *reinterpret_cast<half8*>(XU + t * P1 + c16) = cvt8(uf);
+      *reinterpret_cast<half8*>(XU + t * P1 + c16 + 8) = cvt8(uf + 8);
+    }
   }
-
-  const int blk = wave;  // this wave's 16-token block
-  const int t_own = 16 * blk + l16;
-  const bool own_ok = t_own < tlen;
-  for (int qc = 0; qc < D / QC; ++qc) {
-    const int c0 = QC * qc;
-    // ---- g (cumulative log-decay, log2 units), k, q, u of this pass's channels ----------
-    {
-      const int c = tid & 31, seg = tid >> 5;  // tokens 8 seg .. + 7 of channel c
-      float acc = 0.f, gl[8];
+  // g: the chunk-local inclusive prefix sum of the log-decay, in log2 units
+  if constexpr (DCH) {
+    const int c = tid & 127, seg = tid >> 7;  // tokens 16 seg .. + 15 of channel c
+    float gl[16], acc = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = 8 * seg + e;
-        float la = 0.f;
-        if (t < tlen) la = DCH ? p.log_decay[tok(t) * D + c0 + c] : p.log_decay[tok(t)];
-        acc += la;
-        gl[e] = acc;
-      }
-      TOT[seg * QC + c] = acc;
-      __syncthreads();
-      float base = 0.f;
-      for (int s2 = 0; s2 < seg; ++s2) base += TOT[s2 * QC + c];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) GL[(8 * seg + e) * PQ + c] = (base + gl[e]) * kLog2e;
+    for (int e = 0; e < 16; ++e) {
+      const int t = 16 * seg + e;
+      acc += t < tlen ? p.log_decay[tok(t) * D + c] : 0.f;
+      gl[e] = acc;
     }
-    {
-      const int t = tid >> 2, c8 = (tid & 3) * 8;  // 8 channels of token t
-      float kf[8], qf[8], uf[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kf[e] = qf[e] = uf[e] = 0.f;
-      if (t < tlen) {
-        const int64_t x = tok(t) * D + c0 + c8;
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + x), kf);
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + x), qf);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (FG2) {
-            kf[e] *= sqrtf(p.erase[x + e]);
-          } else {
-            uf[e] = kf[e] * (p.erase_channel ? p.erase[x + e] : p.erase[tok(t)]);
-          }
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        XK[t * PQ + c8 + e] = kf[e];
-        XQ[t * PQ + c8 + e] = qf[e];
-        if constexpr (!FG2) XU[t * PQ + c8 + e] = uf[e];
-      }
-    }
+    BT[seg][c] = acc;
     __syncthreads();
-    // ---- operands referenced inside their own block ---------------------------------------
-    {
-      const int c = tid & 31, t8 = (tid >> 5) * 8;
-      half8 xk, xq, yk, yu;
+    float base = 0.f;
+    for (int s2 = 0; s2 < seg; ++s2) base += BT[s2][c];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = t8 + e, blk_t = t >> 4;
-        const float gt = GL[t * PQ + c];
-        // X~ = x e^{g - g_s} (s = 16 I - 1, I >= 1); Y~ = y e^{g_r - g} (r = 16 J + 15, J <= 2)
-        const float fx = blk_t >= 1 ? exp2f(gt - GL[(16 * blk_t - 1) * PQ + c]) : 0.f;
-        const float fy = blk_t <= 2 ? exp2f(GL[(16 * blk_t + 15) * PQ + c] - gt) : 0.f;
-        xk[e] = (_Float16)(XK[t * PQ + c] * fx);
-        xq[e] = (_Float16)(XQ[t * PQ + c] * fx);
-        yk[e] = (_Float16)(XK[t * PQ + c] * fy);
-        yu[e] = FG2 ? (_Float16)0.f : (_Float16)(XU[t * PQ + c] * fy);
+    for (int e = 0; e < 16; ++e) GL[(16 * seg + e) * GS + c] = (base + gl[e]) * kLog2e;
+  } else {
+    if (wave == 0) {
+      float x = lane < tlen ? p.log_decay[tok(lane)] : 0.f;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(x, o);
+        if (lane >= o) x += y;
       }
-      *reinterpret_cast<half8*>(XT[0] + c * P2 + t8) = xk;
-      *reinterpret_cast<half8*>(XT[1] + c * P2 + t8) = xq;
-      *reinterpret_cast<half8*>(YT[0] + c * P2 + t8) = yk;
-      *reinterpret_cast<half8*>(YT[1] + c * P2 + t8) = yu;
+      GL[lane] = x * kLog2e;
     }
-    __syncthreads();
+  }
+  __syncthreads();
 
-    // ---- this wave's block: lane holds token t_own and channels c0 + 16 ct + 4 lg + r -------
-    f32x4 rowK[2], rowQ[2], colK[2], colU[2];
+  auto gl = [&](int t, int c) { return DCH ? GL[t * GS + c] : GL[t]; };
+  // Operand fragment (rows c0 + l16, contraction over tokens tb + 4 lg + 0..3) of x e^{g_t - g_ref}
+  // (inv = false) or x e^{g_ref - g_t} (inv = true).
+  auto opfrag = [&](const _Float16* X, int c0, int tb, int ref, bool inv) {
+    const int c = c0 + l16;
+    const float gr = gl(ref, c);
+    half4v f;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int cc = 16 * ct;  // channel tile within the pass
-      f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = rk, ck = rk, cu = rk;
-      // row side: blocks J < blk
-      for (int J = 0; J < blk; ++J) {
-        const half4v yk = frag4N(YT[0], P2, cc, 16 * J, lane), yu = frag4N(YT[1], P2, cc, 16 * J, lane);
-        f32x4 ak = mfma16(yk, frag4N(DA[GA_KK], P2, 16 * blk, 16 * J, lane), f32x4{0.f, 0.f, 0.f, 0.f});
-        f32x4 aq = mfma16(yk, frag4N(DA[GA_QK], P2, 16 * blk, 16 * J, lane), f32x4{0.f, 0.f, 0.f, 0.f});
-        if constexpr (!FG2) {
-          ak = mfma16(yu, frag4N(DA[GA_KU], P2, 16 * blk, 16 * J, lane), ak);
-          aq = mfma16(yu, frag4N(DA[GA_QU], P2, 16 * blk, 16 * J, lane), aq);
-        }
-        const int s = 16 * blk - 1, r = 16 * J + 15;
+    for (int j = 0; j < 4; ++j) {
+      const int t = tb + 4 * lg + j;
+      const float d = gl(t, c) - gr;
+      f[j] = (_Float16)(float(X[t * P1 + c]) * exp2f(inv ? -d : d));
+    }
+    return f;
+  };
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  const int m_ref = 16 * blk + 7;  // the diagonal block's reference token
+  constexpr float kSpan = 6.f * kLog2e;
+
+  float s_e = 0.f, s_w = 0.f, s_g = 0.f;  // per-head sums over this lane's channels
+  f32x4 dgv[4], gnv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = cc + 4 * lg + e;
-          const float F = s == r ? 1.f : exp2f(GL[s * PQ + c] - GL[r * PQ + c]);
-          rk[e] = fmaf(F, ak[e], rk[e]);
-          rq[e] = fmaf(F, aq[e], rq[e]);
-        }
+  for (int ct = 0; ct < 4; ++ct) {
+    const int c0 = 64 * hc + 16 * ct;   // channel tile
+    const int cq = c0 + 4 * lg;         // this lane's output channels cq .. + 3
+    // this lane's kernel-1 products and the raw inputs of the chain rule, issued before the
+    // products of this tile
+    f32x4 pk[5];
+#pragma unroll
+    for (int q = 0; q < 5; ++q)
+      pk[q] = (FG2 && q == GK_UE) ? z4 : *reinterpret_cast<const f32x4*>(gk + (q * C + t_own) * D + cq);
+    uint2 vb = make_uint2(0, 0), kb = make_uint2(0, 0);
+    f32x4 e4 = {1.f, 1.f, 1.f, 1.f}, w4 = {1.f, 1.f, 1.f, 1.f};
+    if (own_ok) {
+      vb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.v) + x_own + cq);
+      if (FG2) {
+        kb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.k) + x_own + cq);
+        e4 = *reinterpret_cast<const f32x4*>(p.erase + x_own + cq);
+      } else {
+        if (p.erase_channel) e4 = *reinterpret_cast<const f32x4*>(p.erase + x_own + cq);
+        else e4 = f32x4{1.f, 1.f, 1.f, 1.f} * p.erase[x_own / D];
+        if (p.write_channel) w4 = *reinterpret_cast<const f32x4*>(p.write + x_own + cq);
+        else w4 = f32x4{1.f, 1.f, 1.f, 1.f} * p.write[x_own / D];
       }
-      // column side: blocks I > blk
-      for (int I = blk + 1; I < 4; ++I) {
-        const half4v xk = frag4N(XT[0], P2, cc, 16 * I, lane), xq = frag4N(XT[1], P2, cc, 16 * I, lane);
-        f32x4 ak = mfma16(xk, frag4T(DA[GA_KK], P2, 16 * blk, 16 * I, lane), f32x4{0.f, 0.f, 0.f, 0.f});
-        ak = mfma16(xq, frag4T(DA[GA_QK], P2, 16 * blk, 16 * I, lane), ak);
-        f32x4 au = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (!FG2) {
-          au = mfma16(xk, frag4T(DA[GA_KU], P2, 16 * blk, 16 * I, lane), au);
-          au = mfma16(xq, frag4T(DA[GA_QU], P2, 16 * blk, 16 * I, lane), au);
-        }
-        const int s = 16 * I - 1, r = 16 * blk + 15;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = cc + 4 * lg + e;
-          const float F = s == r ? 1.f : exp2f(GL[s * PQ + c] - GL[r * PQ + c]);
-          ck[e] = fmaf(F, ak[e], ck[e]);
-          cu[e] = fmaf(F, au[e], cu[e]);
-        }
+    }
+
+    // ---- row side (this block's tokens as rows): earlier blocks J, then the diagonal -------
+    f32x4 rk = z4, rq = z4, ck = z4, cu = z4;
+    for (int J = 0; J < blk; ++J) {
+      const int r = 16 * J + 15, s = 16 * blk - 1;
+      const half4v yk = opfrag(XK, c0, 16 * J, r, true);
+      f32x4 tk = mfma16(yk, frag4N(DA[GA_KK], P2, 16 * blk, 16 * J, lane), z4);
+      f32x4 tq = mfma16(yk, frag4N(DA[GA_QK], P2, 16 * blk, 16 * J, lane), z4);
+      if constexpr (!FG2) {
+        const half4v yu = opfrag(XU, c0, 16 * J, r, true);
+        tk = mfma16(yu, frag4N(DA[GA_KU], P2, 16 * blk, 16 * J, lane), tk);
+        tq = mfma16(yu, frag4N(DA[GA_QU], P2, 16 * blk, 16 * J, lane), tq);
       }
-      // the rows' own factors
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int c = cc + 4 * lg + e;
-        const float gt = GL[t_own * PQ + c];
-        const float fr = blk > 0 ? exp2f(gt - GL[(16 * blk - 1) * PQ + c]) : 0.f;
-        const float fc = blk < 3 ? exp2f(GL[(16 * blk + 15) * PQ + c] - gt) : 0.f;
-        rk[e] *= fr;
-        rq[e] *= fr;
-        ck[e] *= fc;
-        cu[e] *= fc;
+        const float F = r == s ? 1.f : exp2f(gl(s, cq + e) - gl(r, cq + e));
+        rk[e] = fmaf(F, tk[e], rk[e]);
+        rq[e] = fmaf(F, tq[e], rq[e]);
       }
-      rowK[ct] = rk;
-      rowQ[ct] = rq;
-      colK[ct] = ck;
-      colU[ct] = cu;
     }
-    // diagonal block, element by element: row side pairs (t_own, i), column side (t, t_own)
-    for (int i2 = 0; i2 < 16; ++i2) {
-      const int o = 16 * blk + i2;
-      const bool row_ok = i2 <= l16, col_ok = i2 >= l16;
-      const float r_kk = float(DA[GA_KK][t_own * P2 + o]), r_qk = float(DA[GA_QK][t_own * P2 + o]);
-      const float c_kk = float(DA[GA_KK][o * P2 + t_own]), c_qk = float(DA[GA_QK][o * P2 + t_own]);
-      float r_ku = 0.f, r_qu = 0.f, c_ku = 0.f, c_qu = 0.f;
+    // ---- column side (this block's tokens as columns): later blocks I ----------------------
+    for (int I = blk + 1; I < 4; ++I) {
+      const int s = 16 * I - 1, r = 16 * blk + 15;
+      const half4v xk = opfrag(XK, c0, 16 * I, s, false), xq = opfrag(XQ, c0, 16 * I, s, false);
+      f32x4 tk = mfma16(xk, frag4T(DA[GA_KK], P2, 16 * blk, 16 * I, lane), z4);
+      tk = mfma16(xq, frag4T(DA[GA_QK], P2, 16 * blk, 16 * I, lane), tk);
+      f32x4 tu = z4;
       if constexpr (!FG2) {
-        r_ku = float(DA[GA_KU][t_own * P2 + o]);
-        r_qu = float(DA[GA_QU][t_own * P2 + o]);
-        c_ku = float(DA[GA_KU][o * P2 + t_own]);
-        c_qu = float(DA[GA_QU][o * P2 + t_own]);
+        tu = mfma16(xk, frag4T(DA[GA_KU], P2, 16 * blk, 16 * I, lane), z4);
+        tu = mfma16(xq, frag4T(DA[GA_QU], P2, 16 * blk, 16 * I, lane), tu);
       }
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const f32x4 go = *reinterpret_cast<const f32x4*>(GL + o * PQ + 16 * ct + 4 * lg);
-        const f32x4 gt = *reinterpret_cast<const f32x4*>(GL + t_own * PQ + 16 * ct + 4 * lg);
-        const f32x4 ko = *reinterpret_cast<const f32x4*>(XK + o * PQ + 16 * ct + 4 * lg);
-        const f32x4 qo = *reinterpret_cast<const f32x4*>(XQ + o * PQ + 16 * ct + 4 * lg);
-        f32x4 uo = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (!FG2) uo = *reinterpret_cast<const f32x4*>(XU + o * PQ + 16 * ct + 4 * lg);
+      for (int e = 0; e < 4; ++e) {
+        const float F = r == s ? 1.f : exp2f(gl(s, cq + e) - gl(r, cq + e));
+        ck[e] = fmaf(F, tk[e], ck[e]);
+        cu[e] = fmaf(F, tu[e], cu[e]);
+      }
+    }
+    // the rows' own factors (to their reference: the token before the block, the block's last)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float gt = gl(t_own, cq + e);
+      const float fr = blk > 0 ? exp2f(gt - gl(16 * blk - 1, cq + e)) : 0.f;
+      const float fc = blk < 3 ? exp2f(gl(16 * blk + 15, cq + e) - gt) : 0.f;
+      rk[e] *= fr;
+      rq[e] *= fr;
+      ck[e] *= fc;
+      cu[e] *= fc;
+    }
+    // ---- the diagonal block: referenced at its 8th token when every factor stays within
+    // e^{+-6} and the operands below 80 (fp16 range), else element by element in fp32 ---------
+    bool ok = true;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float d = gl(t_own, cq + e) - gl(m_ref, cq + e);
+      const float ax = fmaxf(fabsf(float(XK[t_own * P1 + cq + e])), fabsf(float(XQ[t_own * P1 + cq + e])));
+      const float au = FG2 ? 0.f : fabsf(float(XU[t_own * P1 + cq + e]));
+      ok = ok && fabsf(d) <= kSpan && fmaxf(ax, au) <= 80.f;
+    }
+    if (__all(ok)) {
+      const half4v yk = opfrag(XK, c0, 16 * blk, m_ref, true);
+      const half4v xk = opfrag(XK, c0, 16 * blk, m_ref, false), xq = opfrag(XQ, c0, 16 * blk, m_ref, false);
+      f32x4 tk = mfma16(yk, frag4N(DA[GA_KK], P2, 16 * blk, 16 * blk, lane), z4);
+      f32x4 tq = mfma16(yk, frag4N(DA[GA_QK], P2, 16 * blk, 16 * blk, lane), z4);
+      f32x4 sk = mfma16(xk, frag4T(DA[GA_KK], P2, 16 * blk, 16 * blk, lane), z4);
+      sk = mfma16(xq, frag4T(DA[GA_QK], P2, 16 * blk, 16 * blk, lane), sk);
+      f32x4 su = z4;
+      if constexpr (!FG2) {
+        const half4v yu = opfrag(XU, c0, 16 * blk, m_ref, true);
+        tk = mfma16(yu, frag4N(DA[GA_KU], P2, 16 * blk, 16 * blk, lane), tk);
+        tq = mfma16(yu, frag4N(DA[GA_QU], P2, 16 * blk, 16 * blk, lane), tq);
+        su = mfma16(xk, frag4T(DA[GA_KU], P2, 16 * blk, 16 * blk, lane), z4);
+        su = mfma16(xq, frag4T(DA[GA_QU], P2, 16 * blk, 16 * blk, lane), su);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float d = gl(t_own, cq + e) - gl(m_ref, cq + e);
+        const float fr = exp2f(d), fc = exp2f(-d);
+        rk[e] = fmaf(fr, tk[e], rk[e]);
+        rq[e] = fmaf(fr, tq[e], rq[e]);
+        ck[e] = fmaf(fc, sk[e], ck[e]);
+        cu[e] = fmaf(fc, su[e], cu[e]);
+      }
+    } else {
+#pragma unroll 1
+      for (int i2 = 0; i2 < 16; ++i2) {
+        const int o = 16 * blk + i2;
+        const bool row_ok = i2 <= l16, col_ok = i2 >= l16;
+        const float r_kk = float(DA[GA_KK][t_own * P2 + o]), r_qk = float(DA[GA_QK][t_own * P2 + o]);
+        const float c_kk = float(DA[GA_KK][o * P2 + t_own]), c_qk = float(DA[GA_QK][o * P2 + t_own]);
+        float r_ku = 0.f, r_qu = 0.f, c_ku = 0.f, c_qu = 0.f;
+        if constexpr (!FG2) {
+          r_ku = float(DA[GA_KU][t_own * P2 + o]);
+          r_qu = float(DA[GA_QU][t_own * P2 + o]);
+          c_ku = float(DA[GA_KU][o * P2 + t_own]);
+          c_qu = float(DA[GA_QU][o * P2 + t_own]);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // e^{g_t - g_o} for o <= t (row side) and e^{g_o - g_t} for o >= t (column side)
-          const float er = row_ok ? exp2f(gt[e] - go[e]) : 0.f;
-          const float ec = col_ok ? exp2f(go[e] - gt[e]) : 0.f;
-          rowK[ct][e] = fmaf(er, fmaf(r_kk, ko[e], r_ku * uo[e]), rowK[ct][e]);
-          rowQ[ct][e] = fmaf(er, fmaf(r_qk, ko[e], r_qu * uo[e]), rowQ[ct][e]);
-          colK[ct][e] = fmaf(ec, fmaf(c_kk, ko[e], c_qk * qo[e]), colK[ct][e]);
-          colU[ct][e] = fmaf(ec, fmaf(c_ku, ko[e], c_qu * qo[e]), colU[ct][e]);
+          const float go = gl(o, cq + e), gt = gl(t_own, cq + e);
+          const float ko = float(XK[o * P1 + cq + e]), qo = float(XQ[o * P1 + cq + e]);
+          const float uo = FG2 ? 0.f : float(XU[o * P1 + cq + e]);
+          const float er = row_ok ? exp2f(gt - go) : 0.f;
+          const float ec = col_ok ? exp2f(go - gt) : 0.f;
+          rk[e] = fmaf(er, fmaf(r_kk, ko, r_ku * uo), rk[e]);
+          rq[e] = fmaf(er, fmaf(r_qk, ko, r_qu * uo), rq[e]);
+          ck[e] = fmaf(ec, fmaf(c_kk, ko, c_qk * qo), ck[e]);
+          cu[e] = fmaf(ec, fmaf(c_ku, ko, c_qu * qo), cu[e]);
         }
       }
     }
 
     // ---- chain rule, outputs ------------------------------------------------------------
-    float s_e = 0.f, s_w = 0.f, s_g = 0.f;  // per-head sums over this lane's channels
-    f32x4 gn_part[2];
+    const f32x4 dkp = pk[GK_KP], dqp = pk[GK_QP], dke = pk[GK_KE], due = pk[GK_UE], dvt = pk[GK_VT];
+    float vv[4], kraw[4];
+    vv[0] = __uint_as_float(vb.x << 16);
+    vv[1] = __uint_as_float(vb.x & 0xffff0000u);
+    vv[2] = __uint_as_float(vb.y << 16);
+    vv[3] = __uint_as_float(vb.y & 0xffff0000u);
+    kraw[0] = __uint_as_float(kb.x << 16);
+    kraw[1] = __uint_as_float(kb.x & 0xffff0000u);
+    kraw[2] = __uint_as_float(kb.y << 16);
+    kraw[3] = __uint_as_float(kb.y & 0xffff0000u);
+    f32x4 o_dq, o_dk, o_dv, o_de, o_dw = z4, dgt, gnt;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int cl = 16 * ct + 4 * lg;  // channel within the pass
-      const int64_t x = tok(own_ok ? t_own : 0) * D + c0 + cl;
-      const f32x4 gt = *reinterpret_cast<const f32x4*>(GL + t_own * PQ + cl);
-      const f32x4 gC = *reinterpret_cast<const f32x4*>(GL + 63 * PQ + cl);
-      const f32x4 kk = *reinterpret_cast<const f32x4*>(XK + t_own * PQ + cl);
-      const f32x4 qq = *reinterpret_cast<const f32x4*>(XQ + t_own * PQ + cl);
-      f32x4 uu = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (!FG2) uu = *reinterpret_cast<const f32x4*>(XU + t_own * PQ + cl);
-      const f32x4 dkp = *reinterpret_cast<const f32x4*>(gk + (GK_KP * C + t_own) * D + c0 + cl);
-      const f32x4 dqp = *reinterpret_cast<const f32x4*>(gk + (GK_QP * C + t_own) * D + c0 + cl);
-      const f32x4 dke = *reinterpret_cast<const f32x4*>(gk + (GK_KE * C + t_own) * D + c0 + cl);
-      f32x4 due = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (!FG2) due = *reinterpret_cast<const f32x4*>(gk + (GK_UE * C + t_own) * D + c0 + cl);
-      const f32x4 dvt = *reinterpret_cast<const f32x4*>(gk + (GK_VT * C + t_own) * D + c0 + cl);
-      f32x4 o_dq, o_dk, o_dv, o_de, gnp, o_dw = {0.f, 0.f, 0.f, 0.f};
-      float vv[4] = {0.f, 0.f, 0.f, 0.f}, ee[4] = {1.f, 1.f, 1.f, 1.f}, ww[4] = {1.f, 1.f, 1.f, 1.f};
-      float rt[4] = {1.f, 1.f, 1.f, 1.f}, kraw[4] = {0.f, 0.f, 0.f, 0.f};
-      if (own_ok) {
-        const uint2 vb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.v) + x);
-        vv[0] = __uint_as_float(vb.x << 16);
-        vv[1] = __uint_as_float(vb.x & 0xffff0000u);
-        vv[2] = __uint_as_float(vb.y << 16);
-        vv[3] = __uint_as_float(vb.y & 0xffff0000u);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (FG2) {
-            rt[e] = sqrtf(p.erase[x + e]);
-          } else {
-            ee[e] = p.erase_channel ? p.erase[x + e] : p.erase[tok(t_own)];
-            ww[e] = p.write_channel ? p.write[x + e] : p.write[tok(t_own)];
-          }
-        }
-        if (FG2) {
-          const uint2 kb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.k) + x);
-          kraw[0] = __uint_as_float(kb.x << 16);
-          kraw[1] = __uint_as_float(kb.x & 0xffff0000u);
-          kraw[2] = __uint_as_float(kb.y << 16);
-          kraw[3] = __uint_as_float(kb.y & 0xffff0000u);
-        }
+    for (int e = 0; e < 4; ++e) {
+      const int c = cq + e;
+      const float gt = gl(t_own, c);
+      const float eg = exp2f(gt), egn = exp2f(gl(C - 1, c) - gt);
+      const float kk = float(XK[t_own * P1 + c]), qq = float(XQ[t_own * P1 + c]);
+      const float uu = FG2 ? 0.f : float(XU[t_own * P1 + c]);
+      const float a_kp = eg * dkp[e], a_qp = eg * dqp[e], a_ke = egn * dke[e], a_ue = egn * due[e];
+      const float dkap = a_kp + a_ke + rk[e] + ck[e];
+      const float du = a_ue + cu[e];
+      o_dq[e] = a_qp + rq[e];
+      dgt[e] = kk * (a_kp - a_ke + rk[e] - ck[e]) + qq * (a_qp + rq[e]) - uu * (a_ue + cu[e]);
+      gnt[e] = kk * a_ke + uu * a_ue;
+      if (FG2) {
+        const float rt = sqrtf(e4[e]);
+        o_dk[e] = rt * dkap;
+        o_dv[e] = rt * dvt[e];
+        o_de[e] = own_ok ? (kraw[e] * dkap + vv[e] * dvt[e]) / (2.f * rt) : 0.f;
+      } else {
+        // k's adjoint with the erase gate's share (u = e * k); the fp16 table holds k exactly
+        o_dk[e] = fmaf(e4[e], du, dkap);
+        o_de[e] = kk * du;
+        o_dv[e] = w4[e] * dvt[e];
+        o_dw[e] = vv[e] * dvt[e];
+        if (shared_gate) o_de[e] += o_dw[e];
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float eg = exp2f(gt[e]), egn = exp2f(gC[e] - gt[e]);
-        const float a_kp = eg * dkp[e], a_qp = eg * dqp[e], a_ke = egn * dke[e], a_ue = egn * due[e];
-        const float dkap = a_kp + a_ke + rowK[ct][e] + colK[ct][e];
-        const float du = a_ue + colU[ct][e];
-        o_dq[e] = a_qp + rowQ[ct][e];
-        const float dg = kk[e] * (a_kp - a_ke + rowK[ct][e] - colK[ct][e]) + qq[e] * (a_qp + rowQ[ct][e]) -
-                         uu[e] * (a_ue + colU[ct][e]);
-        gnp[e] = kk[e] * a_ke + uu[e] * a_ue;
-        DG[t_own * PQ + cl + e] = dg;
-        if (FG2) {
-          o_dk[e] = rt[e] * dkap;
-          o_dv[e] = rt[e] * dvt[e];
-          o_de[e] = (kraw[e] * dkap + vv[e] * dvt[e]) / (2.f * rt[e]);
-        } else {
-          o_dk[e] = fmaf(ee[e], du, dkap);
-          o_de[e] = kk[e] * du;
-          o_dv[e] = ww[e] * dvt[e];
-          o_dw[e] = vv[e] * dvt[e];
-          if (shared_gate) o_de[e] += o_dw[e];
-        }
-        s_e += o_de[e];
-        s_w += o_dw[e];
-        s_g += dg;
-      }
-      gn_part[ct] = gnp;
-      if (own_ok) {
-        *reinterpret_cast<f32x4*>(g.dq + x) = o_dq;
-        *reinterpret_cast<f32x4*>(g.dk + x) = o_dk;
-        *reinterpret_cast<f32x4*>(g.dv + x) = o_dv;
-        if (FG2 || p.erase_channel) *reinterpret_cast<f32x4*>(g.derase + x) = o_de;
-        if (!FG2 && !shared_gate && p.write_channel) *reinterpret_cast<f32x4*>(g.dwrite + x) = o_dw;
-      }
+      s_e += o_de[e];
+      s_w += o_dw[e];
+      s_g += dgt[e];
     }
-    // end-referenced shares: sum over the block's 16 tokens (lanes of one lg group), per channel
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float v = gn_part[ct][e];
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-        if (l16 == 0) GN[blk * QC + 16 * ct + 4 * lg + e] = v;
-      }
-    // per-head gates and decay: sums over this pass's channels (the four lane groups of token t)
-    if (!DCH || !(FG2 || p.erase_channel) || (!FG2 && !shared_gate && !p.write_channel)) {
-#pragma unroll
-      for (int o = 16; o <= 32; o <<= 1) {
-        s_e += __shfl_xor(s_e, o);
-        s_w += __shfl_xor(s_w, o);
-        s_g += __shfl_xor(s_g, o);
-      }
-      if (lg == 0) {
-        SUMS[0][t_own] += s_g;
-        SUMS[1][t_own] += s_e;
-        SUMS[2][t_own] += s_w;
-      }
+    dgv[ct] = dgt;
+    gnv[ct] = gnt;
+    if (own_ok) {
+      *reinterpret_cast<f32x4*>(g.dq + x_own + cq) = o_dq;
+      *reinterpret_cast<f32x4*>(g.dk + x_own + cq) = o_dk;
+      *reinterpret_cast<f32x4*>(g.dv + x_own + cq) = o_dv;
+      if (FG2 || p.erase_channel) *reinterpret_cast<f32x4*>(g.derase + x_own + cq) = o_de;
+      if (!FG2 && !shared_gate && p.write_channel) *reinterpret_cast<f32x4*>(g.dwrite + x_own + cq) = o_dw;
     }
-    __syncthreads();
-    // ---- the log-decay's adjoint: reverse prefix sum over the chunk, plus the end shares -----
-    if constexpr (DCH) {
-      const int c = tid & 31, seg = tid >> 5;
-      float sfx[8], acc = 0.f;
-#pragma unroll
-      for (int e = 7; e >= 0; --e) {
-        acc += DG[(8 * seg + e) * PQ + c];
-        sfx[e] = acc;
-      }
-      __syncthreads();
-      TOT[seg * QC + c] = acc;
-      __syncthreads();
-      float base = 0.f;
-      for (int s2 = seg + 1; s2 < 8; ++s2) base += TOT[s2 * QC + c];
-      // g_C's share: e^{g_C} dGamma and the end-referenced operands' sum
-      const float gC = GL[63 * PQ + c];
-      const float dgn = exp2f(gC) * gw.gd[pkt * D + c0 + c] + GN[c] + GN[QC + c] + GN[2 * QC + c] + GN[3 * QC + c];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = 8 * seg + e;
-        if (t < tlen) g.dlog_decay[tok(t) * D + c0 + c] = base + sfx[e] + dgn;
-      }
-    } else {
-      if (tid < QC) {
-        const int c = tid;
-        const float dgn = exp2f(GL[63 * PQ + c]) * gw.gd[pkt * D + c0 + c] + GN[c] + GN[QC + c] + GN[2 * QC + c] +
-                          GN[3 * QC + c];
-        TOT[c] = dgn;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        float s = 0.f;
-        for (int c = 0; c < QC; ++c) s += TOT[c];
-        TOT[QC] = s;
-      }
-      __syncthreads();
-      if (tid == 0) SUMS[0][63] += TOT[QC];  // added at the last row: every earlier token's suffix takes it
-    }
-    __syncthreads();
   }
 
-  // ---- per-head sums ----------------------------------------------------------------------
-  if (tid < C) {
-    const int t = tid;
-    if (!DCH) {
-      float s = 0.f;
-      for (int t2 = C - 1; t2 >= t; --t2) s += SUMS[0][t2];
-      if (t < tlen) g.dlog_decay[tok(t)] = s;
+  // ---- g's adjoint: suffix sums within the block (lanes of one lane group are its 16 tokens),
+  // block totals and the end-referenced shares through LDS --------------------------------------
+  __syncthreads();  // BT held the prefix-sum totals
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = dgv[ct][e];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float y = __shfl_down(v, o, 16);
+        if (l16 + o < 16) v += y;
+      }
+      dgv[ct][e] = v;
+      float n = gnv[ct][e];
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) n += __shfl_xor(n, o);
+      const int c = 64 * hc + 16 * ct + 4 * lg + e;
+      if (l16 == 0) {
+        BT[blk][c] = v;
+        GNS[blk][c] = n;
+      }
     }
-    if (t < tlen) {
-      if (!FG2 && !p.erase_channel) g.derase[tok(t)] = SUMS[1][t];
-      if (!FG2 && !shared_gate && !p.write_channel) g.dwrite[tok(t)] = SUMS[2][t];
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    s_e += __shfl_xor(s_e, o);
+    s_w += __shfl_xor(s_w, o);
+    s_g += __shfl_xor(s_g, o);
+  }
+  if (lg == 0) {
+    RED[0][hc][t_own] = s_g;
+    RED[1][hc][t_own] = s_e;
+    RED[2][hc][t_own] = s_w;
+  }
+  __syncthreads();
+  if constexpr (DCH) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int cq = 64 * hc + 16 * ct + 4 * lg;
+      f32x4 out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = cq + e;
+        float later = 0.f;
+        for (int b2 = blk + 1; b2 < 4; ++b2) later += BT[b2][c];
+        const float dgn = exp2f(gl(C - 1, c)) * gw.gd[pkt * D + c] + GNS[0][c] + GNS[1][c] + GNS[2][c] + GNS[3][c];
+        out[e] = dgv[ct][e] + later + dgn;
+      }
+      if (own_ok) *reinterpret_cast<f32x4*>(g.dlog_decay + x_own + cq) = out;
     }
+  } else {
+    // g_C's share summed over channels (waves 0 and 1: one channel per thread)
+    if (wave < 2) {
+      const int c = tid;
+      float n = exp2f(gl(C - 1, c)) * gw.gd[pkt * D + c] + GNS[0][c] + GNS[1][c] + GNS[2][c] + GNS[3][c];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o);
+      if (lane == 0) MISC[wave] = n;
+    }
+    __syncthreads();
+    if (tid < C) {
+      float s = MISC[0] + MISC[1];
+      for (int t2 = C - 1; t2 >= tid; --t2) s += RED[0][0][t2] + RED[0][1][t2];
+      if (tid < tlen) g.dlog_decay[tok(tid)] = s;
+    }
+  }
+  if (tid < tlen) {
+    if (!FG2 && !p.erase_channel) g.derase[tok(tid)] = RED[1][0][tid] + RED[1][1][tid];
+    if (!FG2 && !shared_gate && !p.write_channel) g.dwrite[tok(tid)] = RED[2][0][tid] + RED[2][1][tid];
   }
 }
 
