@@ -477,7 +477,7 @@ hipError_t launch_bwd_varlen(Problem p, const int* cu, const BwdArgs& g, void* w
 }
 
 // Gradients through the chunk path: workspace = forward packets (general-gate layout, or FG2's
-// symmetric one) | o (bf16, unused) | chunk-start states | chunk-end adjoints (fp32 [dk][dv]
+// symmetric one) | o (bf16, unused) | chunk-start states | chunk-end adjoints (fp16 [dk][dv]
 // per chunk) | M (FG2: delta) and Z (fp16 [C][dv] per chunk) | the chunk gradients' products.
 struct BwdChunkedLayout {
   int64_t pkt, obuf, ckS, ckG, ckM, ckZ, work, total;  // byte offsets
@@ -488,8 +488,8 @@ struct BwdChunkedLayout {
     pkt = 0;
     obuf = up(int64_t(chunk128_workspace_bytes(p.B, p.T, p.H, false, p.decay_channel, p.rate_sqrt)));
     ckS = obuf + up(bth * p.dv * 2);
-    ckG = ckS + up(chunks * p.dk * p.dv * 4);
-    ckM = ckG + up(chunks * p.dk * p.dv * 4);
+    ckG = ckS + up(chunks * p.dk * p.dv * 2);
+    ckM = ckG + up(chunks * p.dk * p.dv * 2);
     ckZ = ckM + up(chunks * CK * p.dv * 2);
     work = ckZ + up(chunks * CK * p.dv * 2);
     total = work + up(int64_t(chunk_grad_work_bytes(p)));
@@ -510,7 +510,7 @@ hipError_t launch_bwd_chunked(const Problem& p, const BwdArgs& g, void* workspac
   pf.o = ws + L.obuf;
   pf.o_bf16 = 1;
   pf.S_T = nullptr;
-  pf.ck_S = reinterpret_cast<float*>(ws + L.ckS);
+  pf.ck_S = ws + L.ckS;
   pf.ck_M = ws + L.ckM;
   hipError_t e = launch_chunk128(pf, ws + L.pkt, stream);
   if (e != hipSuccess) return e;
@@ -518,7 +518,7 @@ hipError_t launch_bwd_chunked(const Problem& p, const BwdArgs& g, void* workspac
   Problem pa = pf;
   pa.ck_S = nullptr;
   pa.ck_M = nullptr;
-  pa.ck_G = reinterpret_cast<float*>(ws + L.ckG);
+  pa.ck_G = ws + L.ckG;
   pa.ck_Z = ws + L.ckZ;
   e = launch_chunk128_adjoint(pa, ws + L.pkt, g.dO, g.dS_T, g.dS0, stream);
   if (e != hipSuccess) return e;

@@ -56,6 +56,17 @@
 namespace dr {
 namespace {
 
+// The same as fp16 into the [dk][dv] matrix at dst (a chunk's checkpoint for the gradients).
+template <int NCT>
+__device__ __forceinline__ void store_state_h(void* dst, int j0, const f32x4 (&S)[NCT]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, lg = lane >> 4;
+  _Float16* d = static_cast<_Float16*>(dst);
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d[(16 * wave + 4 * lg + r) * D + j0 + 16 * ct + l16] = (_Float16)S[ct][r];
+}
+
 // Rows t0 .. t0 + 3 of column j of a per-chunk fp16 [C][D] matrix (packet index pkt) from an
 // accumulator tile's four values.
 __device__ __forceinline__ void store_rows(void* base, int64_t pkt, int t0, int j, f32x4 x) {
@@ -1093,7 +1104,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, con
   // conservative.
   auto step = [&](auto tail, int c, Pref& P) {
     constexpr bool TAIL = decltype(tail)::value;
-    if constexpr (CKPT) store_state(p.ck_S + (sq.pkt0 + c) * D * D, j0, S);
+    if constexpr (CKPT) store_state_h(static_cast<_Float16*>(p.ck_S) + (sq.pkt0 + c) * D * D, j0, S);
     // ---- L: the chunk's packet, value slice and S~^T into LDS ------------------------------
     // the LDS tiles keep the packet's layout: 16-byte units copy straight across
 #pragma unroll
@@ -1574,7 +1585,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     const int cn = c + 1 < nchunks ? c + 1 : c;  // chunk whose copies this step issues
     vm_wait<kB2min + kB3 + (kEarly ? kB1b : 0)>();  // batch 1 of this chunk, older stores
     // (checkpoint stores only make the later partial waits stricter: they wait for these too)
-    if constexpr (CKPT) store_state(p.ck_S + (sq.pkt0 + c) * D * D, j0, S);
+    if constexpr (CKPT) store_state_h(static_cast<_Float16*>(p.ck_S) + (sq.pkt0 + c) * D * D, j0, S);
     if constexpr (!kStage) {
       if (c > 0 && o_wave) store_out(c - 1, false);
     } else {
@@ -1957,7 +1968,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_adjoint_scan_kernel(Proble
   const bool zwave = NCT == 2 || wave < 4;
 
   auto step = [&](int c, Pref& P) {
-    if (p.ck_G) store_state(p.ck_G + (sq.pkt0 + c) * D * D, j0, G);
+    if (p.ck_G) store_state_h(static_cast<_Float16*>(p.ck_G) + (sq.pkt0 + c) * D * D, j0, G);
     // ---- L: the chunk's packet, dO^T and G~^T into LDS ------------------------------------
 #pragma unroll
     for (int i = 0; i < 2; ++i) {

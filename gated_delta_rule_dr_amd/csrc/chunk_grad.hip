@@ -51,16 +51,17 @@ constexpr int P1 = 136;  // row stride (halves) of fp16 [*][128] LDS tiles
 constexpr int P2 = 72;   // row stride (halves) of fp16 [*][64] LDS tiles
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Kernel-1 results per chunk (fp32): five [C][D] matrices dK+, dQ+, dK^end, dU^end, dVt; four
-// [C][C] matrices dA_kk, dA_ku, dA_qk, dA_qu; dGamma [D].
+// Kernel-1 results per chunk: five fp32 [C][D] matrices dK+, dQ+, dK^end, dU^end, dVt; four fp16
+// [C][C] matrices dA_kk, dA_ku, dA_qk, dA_qu (kernel 2 multiplies them as fp16 operands);
+// dGamma [D] fp32.
 constexpr int64_t kGkFloats = 5 * C * D;
-constexpr int64_t kGaFloats = 4 * C * C;
+constexpr int64_t kGaHalves = 4 * C * C;
 enum { GK_KP = 0, GK_QP = 1, GK_KE = 2, GK_UE = 3, GK_VT = 4 };
 enum { GA_KK = 0, GA_KU = 1, GA_QK = 2, GA_QU = 3 };
 
 struct GradWork {
   float* gk;  // [chunks][5][C][D]
-  float* ga;  // [chunks][4][C][C]
+  _Float16* ga;  // [chunks][4][C][C]
   float* gd;  // [chunks][D]
 };
 
@@ -113,18 +114,18 @@ __global__ __launch_bounds__(kG1Threads) void chunk_grad_state_kernel(Problem p,
   const int tlen = p.T - ci * C < C ? p.T - ci * C : C;
   const int64_t tok0 = (int64_t(b) * p.T + int64_t(ci) * C) * p.H + h;
   auto tok = [&](int t) { return tok0 + int64_t(t) * p.H; };
-  const float* Sg = p.ck_S + pkt * D * D;
-  const float* Gg = p.ck_G + pkt * D * D;
+  const _Float16* Sg = static_cast<const _Float16*>(p.ck_S) + pkt * D * D;
+  const _Float16* Gg = static_cast<const _Float16*>(p.ck_G) + pkt * D * D;
   const _Float16* Zg = static_cast<const _Float16*>(p.ck_Z) + pkt * C * D;
   const _Float16* Mg = static_cast<const _Float16*>(p.ck_M) + pkt * C * D;
   float* out_k = gw.gk + pkt * kGkFloats;
-  float* out_a = gw.ga + pkt * kGaFloats;
+  _Float16* out_a = gw.ga + pkt * kGaHalves;
 
   // ---- loads ----------------------------------------------------------------------------
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {  // S: 4096 float4
-    const int f = tid + kG1Threads * i, d = f >> 5, j = (f & 31) * 4;
-    *reinterpret_cast<half4v*>(SG + d * P1 + j) = h4(*reinterpret_cast<const float4*>(Sg + d * D + j));
+  for (int i = 0; i < 4; ++i) {  // S: 2048 units of 8 halves
+    const int u = tid + kG1Threads * i, d = u >> 4, j = (u & 15) * 8;
+    *reinterpret_cast<uint4*>(SG + d * P1 + j) = *reinterpret_cast<const uint4*>(Sg + d * D + j);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {  // Z, M: 1024 units of 8 halves each
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(kG1Threads) void chunk_grad_state_kernel(Problem p,
           acc[r] = (i < t || (!strict && i == t)) ? sgn * acc[r] : 0.f;
         }
       }
-      store4(out_a + (which * C + 16 * tm + l16) * C + 16 * tn + 4 * lg, acc);
+      *reinterpret_cast<half4v*>(out_a + (which * C + 16 * tm + l16) * C + 16 * tn + 4 * lg) = cvt4(acc);
     }
   }
   // dVt's tiles are kept by their wave across the load of G: wave w owns tiles w, w + 8, ...
@@ -243,16 +244,23 @@ __global__ __launch_bounds__(kG1Threads) void chunk_grad_state_kernel(Problem p,
 
   // ---- G, and dGamma = rowsum(S * G) in fp32 -----------------------------------------------
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int f = tid + kG1Threads * i, d = f >> 5, j = (f & 31) * 4;
-    const float4 g4 = *reinterpret_cast<const float4*>(Gg + d * D + j);
-    const float4 s4 = *reinterpret_cast<const float4*>(Sg + d * D + j);
-    *reinterpret_cast<half4v*>(SG + d * P1 + j) = h4(g4);
-    float x = g4.x * s4.x + g4.y * s4.y + g4.z * s4.z + g4.w * s4.w;
-    // the 32 threads of row d are lanes 32 (lane / 32) .. + 31 of one wave
+  for (int i = 0; i < 4; ++i) {
+    const int u = tid + kG1Threads * i, d = u >> 4, j = (u & 15) * 8;
+    const half8 g8 = *reinterpret_cast<const half8*>(Gg + d * D + j);
+    const half8 s8 = *reinterpret_cast<const half8*>(SG + d * P1 + j);
+    float x = 0.f;
 #pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-    if ((lane & 31) == 0) gw.gd[pkt * D + d] = x;
+    for (int e = 0; e < 8; ++e) x = fmaf(float(g8[e]), float(s8[e]), x);
+    // the 16 threads of row d are lanes 16 (lane / 16) .. + 15 of one wave
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    if (l16 == 0) gw.gd[pkt * D + d] = x;
+  }
+  __syncthreads();  // every S read above is done
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = tid + kG1Threads * i, d = u >> 4, j = (u & 15) * 8;
+    *reinterpret_cast<uint4*>(SG + d * P1 + j) = *reinterpret_cast<const uint4*>(Gg + d * D + j);
   }
   __syncthreads();
 
@@ -311,7 +319,7 @@ __global__ __launch_bounds__(kG2Threads) void chunk_grad_gram_kernel(Problem p, 
   const int64_t tok0 = (int64_t(b) * p.T + int64_t(ci) * C) * p.H + h;
   auto tok = [&](int t) { return tok0 + int64_t(t) * p.H; };
   const float* gk = gw.gk + pkt * kGkFloats;
-  const float* ga = gw.ga + pkt * kGaFloats;
+  const _Float16* ga = gw.ga + pkt * kGaHalves;
   const bool shared_gate = g.dwrite == nullptr;  // write gate == erase gate
   const int t_own = 16 * blk + l16;
   const bool own_ok = t_own < tlen;
@@ -321,7 +329,7 @@ __global__ __launch_bounds__(kG2Threads) void chunk_grad_gram_kernel(Problem p, 
   for (int f = tid; f < NA * C * C / 4; f += kG2Threads) {
     const int m = f / (C * C / 4), r = f % (C * C / 4), t = r >> 4, i = (r & 15) * 4;
     const int which = FG2 ? (m ? GA_QK : GA_KK) : m;
-    *reinterpret_cast<half4v*>(DA[which] + t * P2 + i) = h4(*reinterpret_cast<const float4*>(ga + (which * C + t) * C + i));
+    *reinterpret_cast<half4v*>(DA[which] + t * P2 + i) = *reinterpret_cast<const half4v*>(ga + (which * C + t) * C + i);
   }
   // k, q, u of every channel, fp16
   {
@@ -692,7 +700,7 @@ void launch_gram(const Problem& p, const BwdArgs& g, GradWork gw, int64_t nchunk
 
 size_t chunk_grad_work_bytes(const Problem& p) {
   const int64_t nchunks = int64_t(p.B) * p.H * ((int64_t(p.T) + C - 1) / C);
-  return size_t(nchunks * (kGkFloats + kGaFloats + D) * 4);
+  return size_t(nchunks * ((kGkFloats + D) * 4 + kGaHalves * 2));
 }
 
 hipError_t launch_chunk_grad(const Problem& p, const BwdArgs& g, const void* packets, void* work,
@@ -700,7 +708,7 @@ hipError_t launch_chunk_grad(const Problem& p, const BwdArgs& g, const void* pac
   const int64_t nchunks = int64_t(p.B) * p.H * ((int64_t(p.T) + C - 1) / C);
   if (nchunks == 0) return hipSuccess;
   float* w = static_cast<float*>(work);
-  GradWork gw{w, w + nchunks * kGkFloats, w + nchunks * (kGkFloats + kGaFloats)};
+  GradWork gw{w, reinterpret_cast<_Float16*>(w + nchunks * (kGkFloats + D)), w + nchunks * kGkFloats};
   const char* ws = static_cast<const char*>(packets);
   if (p.rate_sqrt) {
     launch_state<true>(p, ws, g.dO, gw, nchunks, stream);

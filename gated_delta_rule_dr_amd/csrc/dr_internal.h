@@ -37,9 +37,9 @@ struct Problem {
   const int* nchunks_total = nullptr;  // number of entries in `chunks`
   const int* order = nullptr;          // [B] sequences, longest first (scan workgroup order)
   // Gradients through the chunk path: the state at the start of every chunk (forward scans) and
-  // its adjoint at the end of every chunk (adjoint scan), fp32 [packet][dk][dv]; null otherwise.
-  float* ck_S = nullptr;
-  float* ck_G = nullptr;
+  // its adjoint at the end of every chunk (adjoint scan), fp16 [packet][dk][dv]; null otherwise.
+  void* ck_S = nullptr;
+  void* ck_G = nullptr;
   // ... and, as fp16 [packet][token][dv], the forward's in-chunk reads M (general gates; with
   // FG2's rate the symmetric scan's delta instead) and the adjoint scan's Z (the adjoint of
   // K+ S + A_kk Vt); null otherwise.
