@@ -480,18 +480,20 @@ hipError_t launch_bwd_varlen(Problem p, const int* cu, const BwdArgs& g, void* w
 // symmetric one) | o (bf16, unused) | chunk-start states | chunk-end adjoints (fp16 [dk][dv]
 // per chunk) | M (FG2: delta) and Z (fp16 [C][dv] per chunk) | the chunk gradients' products.
 struct BwdChunkedLayout {
-  int64_t pkt, obuf, ckS, ckG, ckM, ckZ, work, total;  // byte offsets
+  int64_t pkt, obuf, ckS, ckG, ckM, ckZ, ckA, work, total;  // byte offsets
   BwdChunkedLayout(const Problem& p) {
     auto up = [](int64_t n) { return (n + 255) / 256 * 256; };
     const int64_t nck = (int64_t(p.T) + CK - 1) / CK, bth = int64_t(p.B) * p.T * p.H;
     const int64_t chunks = int64_t(p.B) * p.H * nck;
+    const bool one_gate = p.symmetric && !p.rate_sqrt;
     pkt = 0;
-    obuf = up(int64_t(chunk128_workspace_bytes(p.B, p.T, p.H, false, p.decay_channel, p.rate_sqrt)));
+    obuf = up(int64_t(chunk128_workspace_bytes(p.B, p.T, p.H, p.symmetric, p.decay_channel, p.rate_sqrt)));
     ckS = obuf + up(bth * p.dv * 2);
     ckG = ckS + up(chunks * p.dk * p.dv * 2);
     ckM = ckG + up(chunks * p.dk * p.dv * 2);
     ckZ = ckM + up(chunks * CK * p.dv * 2);
-    work = ckZ + up(chunks * CK * p.dv * 2);
+    ckA = ckZ + up(chunks * CK * p.dv * 2);
+    work = ckA + (one_gate ? up(chunks * 6 * 1024) : 0);
     total = work + up(int64_t(chunk_grad_work_bytes(p)));
   }
 };
@@ -502,22 +504,23 @@ hipError_t launch_bwd_chunked(const Problem& p, const BwdArgs& g, void* workspac
   if (p.dk != 128 || p.dv != 128 || p.seqs) return hipErrorInvalidValue;
   const BwdChunkedLayout L(p);
   char* ws = static_cast<char*>(workspace);
-  // One per-head gate for erase and write is the general form with u = beta k, v~ = beta v, so
-  // every gate form but FG2's rate runs the general-gate kernels, whose forward scan yields the
-  // in-chunk reads M that the gradients need.
+  // The forward stores every chunk's incoming state and its in-chunk reads M (general gates) or
+  // delta (one per-head gate, with the prep's A_kk, from which the gradients rebuild M; FG2's
+  // rate, whose adjoints need only delta).
   Problem pf = p;
-  pf.symmetric = 0;
   pf.o = ws + L.obuf;
   pf.o_bf16 = 1;
   pf.S_T = nullptr;
   pf.ck_S = ws + L.ckS;
   pf.ck_M = ws + L.ckM;
+  if (p.symmetric && !p.rate_sqrt) pf.ck_A = ws + L.ckA;
   hipError_t e = launch_chunk128(pf, ws + L.pkt, stream);
   if (e != hipSuccess) return e;
   // the state's adjoint at every chunk end and Z, and dS0
   Problem pa = pf;
   pa.ck_S = nullptr;
   pa.ck_M = nullptr;
+  pa.ck_A = nullptr;
   pa.ck_G = ws + L.ckG;
   pa.ck_Z = ws + L.ckZ;
   e = launch_chunk128_adjoint(pa, ws + L.pkt, g.dO, g.dS_T, g.dS0, stream);

@@ -67,6 +67,9 @@ __device__ __forceinline__ void store_state_h(void* dst, int j0, const f32x4 (&S
     for (int r = 0; r < 4; ++r) d[(16 * wave + 4 * lg + r) * D + j0 + 16 * ct + l16] = (_Float16)S[ct][r];
 }
 
+// Halves per chunk of the one-gate A_kk side buffer (the six stored 16 x 32 blocks).
+constexpr int64_t kAkkHalves = 6 * 512;
+
 // Rows t0 .. t0 + 3 of column j of a per-chunk fp16 [C][D] matrix (packet index pkt) from an
 // accumulator tile's four values.
 __device__ __forceinline__ void store_rows(void* base, int64_t pkt, int t0, int j, f32x4 x) {
@@ -420,6 +423,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_prep_scalar_kernel(Problem 
         v.z = (i0 + 2 < t) ? sc * acc[2] : 0.f;
         v.w = (i0 + 3 < t) ? sc * acc[3] : 0.f;
         *reinterpret_cast<float4*>(AF + t * AFS + i0) = v;
+        if (p.ck_A) {  // A_kk itself, for the gradients
+          half4v hv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(i0 + r < t ? acc[r] : 0.f);
+          *reinterpret_cast<half4v*>(static_cast<_Float16*>(p.ck_A) + cr.pkt * kAkkHalves + tri_pos(t, i0)) = hv;
+        }
       } else {
         half4v hv;
 #pragma unroll
@@ -435,6 +444,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_prep_scalar_kernel(Problem 
       const half4v z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
       const int I0 = 2 * wave, J0 = I0 + 1;
       *reinterpret_cast<half4v*>(wsc + PK::matb / 2 + tri_pos(16 * I0 + l16, 16 * J0 + 4 * lg)) = z;
+      if (p.ck_A)
+        *reinterpret_cast<half4v*>(static_cast<_Float16*>(p.ck_A) + cr.pkt * kAkkHalves +
+                                   tri_pos(16 * I0 + l16, 16 * J0 + 4 * lg)) = z;
     }
     lds_barrier();
     // fetch the next chunk's inputs only now, in flight during the solve, which keeps them out of
@@ -895,13 +907,30 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_ch_kernel(Problem p, c
       }
     }
     lds_barrier();
-    // phase B: the solve matrix, fp32, over the q row operands
+    // phase B: the solve matrix, fp32, over the q row operands (one per-head gate: A_kk also to
+    // the gradients' side buffer when it is given)
+    _Float16* const cka = (!GEN && p.ck_A) ? static_cast<_Float16*>(p.ck_A) + cr.pkt * kAkkHalves : nullptr;
+    auto store_cka = [&](int t, int i0, f32x4 acc, bool diag) {
+      half4v hv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hv[r] = (_Float16)((!diag || i0 + r < t) ? acc[r] : 0.f);
+      *reinterpret_cast<half4v*>(cka + tri_pos(t, i0)) = hv;
+    };
     for (int n = w; n < 6; n += 4) {
       const int I = n < 1 ? 1 : n < 3 ? 2 : 3;
       const int J = n - (I * (I - 1)) / 2;
-      store_af(16 * I + l16, 16 * J + 4 * lg, off_tile(n, kSolveProd), false);
+      const f32x4 a = off_tile(n, kSolveProd);
+      store_af(16 * I + l16, 16 * J + 4 * lg, a, false);
+      if (cka) store_cka(16 * I + l16, 16 * J + 4 * lg, a, false);
     }
     store_af(tl, 16 * w + 4 * lg, dacc[kSolveProd], true);
+    if (cka) {
+      store_cka(tl, 16 * w + 4 * lg, dacc[kSolveProd], true);
+      if (w < 2) {
+        const half4v z = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+        *reinterpret_cast<half4v*>(cka + tri_pos(32 * w + l16, 32 * w + 16 + 4 * lg)) = z;
+      }
+    }
     lds_barrier();
     solve_t(AF, TH, tid);
     if (blk + gridDim.x >= nblk) write_t(cr.pkt);  // this workgroup's last chunk

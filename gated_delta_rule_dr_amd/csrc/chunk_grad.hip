@@ -92,18 +92,26 @@ __device__ __forceinline__ half4v h4(float4 x) {
 // ------------------------------------------------------------------------------------------
 // Kernel 1: the products with the state and its adjoint, and the Gram matrices' adjoints.
 // ------------------------------------------------------------------------------------------
-template <bool FG2>
+// MODE: general gates (the general-gate packet and M from the forward scan); one per-head gate
+// (the symmetric packet, A_kk from the prep's side buffer, delta from the forward scan, and
+// M = K+ S + A_kk delta formed here); FG2's rate (delta only, merged adjoints).
+enum { kModeGen = 0, kModeSym = 1, kModeFg2 = 2 };
+
+template <int MODE, bool DCH>
 __global__ __launch_bounds__(kG1Threads) void chunk_grad_state_kernel(Problem p, const char* __restrict__ ws,
                                                                       const float* __restrict__ dO, GradWork gw) {
-  using PK = Packet<true, true>;
+  constexpr bool FG2 = MODE == kModeFg2, SYM = MODE == kModeSym;
+  constexpr bool SCAL = SYM && !DCH;  // plain k tiles with per-row factors in the packet
+  using PK = Packet<SYM ? DCH : true, !SYM>;
   __shared__ __attribute__((aligned(16))) _Float16 SG[D * P1];  // S, then G: [d][j]
   __shared__ __attribute__((aligned(16))) _Float16 ZZ[C * P1];  // Z [t][j]
-  __shared__ __attribute__((aligned(16))) _Float16 MM[C * P1];  // M (FG2: Delta) [t][j]
+  __shared__ __attribute__((aligned(16))) _Float16 MM[C * P1];  // M (FG2: Delta; one gate: Delta, then M)
   __shared__ __attribute__((aligned(16))) _Float16 DO[C * P1];  // dO [t][j]
   __shared__ __attribute__((aligned(16))) _Float16 VV[C * P1];  // Vt [t][j]
   __shared__ __attribute__((aligned(16))) _Float16 AK[FG2 ? 8 : C * P2];  // A_kk [t][i]
   __shared__ __attribute__((aligned(16))) _Float16 AQ[FG2 ? 8 : C * P2];  // A_qk [t][i]
-  __shared__ __attribute__((aligned(16))) _Float16 KE[FG2 ? 8 : C * P1];  // K^end [t][d]
+  __shared__ __attribute__((aligned(16))) _Float16 KE[FG2 ? 8 : C * P1];  // K^end [t][d] (one gate: K+ first)
+  __shared__ float FAC[SCAL ? 2 * C : 1];  // one gate, per-head decay: e^{g_t}, e^{g_C - g_t}
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -161,27 +169,72 @@ __global__ __launch_bounds__(kG1Threads) void chunk_grad_state_kernel(Problem p,
   }
   if constexpr (!FG2) {
     const char* pk = ws + pkt * PK::bytes;
-    // A_kk (packet matrix 2) and A_qk (matrix 1): six stored 16 x 32 blocks of 1 KB each
+    // A_kk (packet matrix 2; one gate: the prep's side buffer) and A_qk (matrix 1): six stored
+    // 16 x 32 blocks of 1 KB each
+    const char* akk = SYM ? static_cast<const char*>(p.ck_A) + pkt * (6 * 1024) : pk + PK::mat + 2 * PK::matb;
     for (int u = tid; u < 768; u += kG1Threads) {
       const int m = u / 384, k = (u % 384) / 64, w64 = u % 64, r = w64 >> 2;
       const int lu = (w64 & 3) ^ ((r >> 2) & 3);
       const int I = k < 2 ? k : 2 + ((k - 2) >> 1), Hh = k < 2 ? 0 : ((k - 2) & 1);
-      const uint4 x = *reinterpret_cast<const uint4*>(pk + PK::mat + (m ? 1 : 2) * PK::matb + 1024 * k + 16 * w64);
+      const char* src = m ? pk + PK::mat + PK::matb : akk;
+      const uint4 x = *reinterpret_cast<const uint4*>(src + 1024 * k + 16 * w64);
       *reinterpret_cast<uint4*>((m ? AQ : AK) + (16 * I + r) * P2 + 32 * Hh + 8 * lu) = x;
     }
     if (tid < 256) {  // the upper blocks that the packet does not store
       const int m = tid >> 7, r = (tid >> 2) & 31, c8 = 32 + 8 * (tid & 3);
       *reinterpret_cast<uint4*>((m ? AQ : AK) + r * P2 + c8) = make_uint4(0, 0, 0, 0);
     }
-    // K^end: swizzled [64][128] tile
+    // K^end (one gate: K+ first): swizzled [64][128] tile
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int u = tid + kG1Threads * i, t = u >> 4, pos = u & 15;
       *reinterpret_cast<uint4*>(KE + t * P1 + 8 * (pos ^ swz_key<16>(t))) =
-          *reinterpret_cast<const uint4*>(pk + PK::kmt + 16 * u);
+          *reinterpret_cast<const uint4*>(pk + (SYM ? PK::kp : PK::kmt) + 16 * u);
+    }
+    if constexpr (SCAL) {
+      if (tid < C) {
+        const float* gv = reinterpret_cast<const float*>(pk + PK::gate);
+        FAC[tid] = gv[GV_FP + tid];
+        FAC[C + tid] = gv[GV_FM + tid];
+      }
     }
   }
   __syncthreads();
+
+  if constexpr (SYM) {
+    // M = K+ S + A_kk delta (the in-chunk reads), transposed as below; then into MM
+    f32x4 mt[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int n = wave + 8 * k, tm = n >> 3, tn = n & 7;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc = mfma16x16x32(fragT(SG, P1, 16 * tn, 32 * ks, lane), frag(KE, P1, 16 * tm, 32 * ks, lane), acc);
+      if constexpr (SCAL) acc = acc * FAC[16 * tm + l16];  // K+ = Diag(e^{g}) k
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        acc = mfma16x16x32(fragT(MM, P1, 16 * tn, 32 * ks, lane), frag(AK, P2, 16 * tm, 32 * ks, lane), acc);
+      mt[k] = acc;
+    }
+    __syncthreads();  // every read of delta and K+ is done
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int n = wave + 8 * k, tm = n >> 3, tn = n & 7;
+      *reinterpret_cast<half4v*>(MM + (16 * tm + l16) * P1 + 16 * tn + 4 * lg) = cvt4(mt[k]);
+    }
+    // K^end: DCH, the packet's tile; per-head decay, plain k (the row factor goes on the product)
+    if constexpr (DCH) {
+      const char* pk = ws + pkt * PK::bytes;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int u = tid + kG1Threads * i, t = u >> 4, pos = u & 15;
+        *reinterpret_cast<uint4*>(KE + t * P1 + 8 * (pos ^ swz_key<16>(t))) =
+            *reinterpret_cast<const uint4*>(pk + PK::kmt + 16 * u);
+      }
+    }
+    __syncthreads();
+  }
 
   // One 16 x 16 output tile of out[m][n] = sum_k A[m][k] Bm[n][k] over k = 0 .. 32 NK - 1 of two
   // row-major tiles, computed transposed so that lane holds out[m0 + l16][n0 + 4 lg + 0..3].
@@ -283,9 +336,12 @@ __global__ __launch_bounds__(kG1Threads) void chunk_grad_state_kernel(Problem p,
       for (int r = 0; r < 4; ++r) acc[r] = -float(z[r]);
     } else {
       // + K^end G: out[t][j] = sum_d KE[t][d] G[d][j]
+      f32x4 kg = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        acc = mfma16x16x32(fragT(SG, P1, 16 * tn, 32 * ks, lane), frag(KE, P1, 16 * tm, 32 * ks, lane), acc);
+        kg = mfma16x16x32(fragT(SG, P1, 16 * tn, 32 * ks, lane), frag(KE, P1, 16 * tm, 32 * ks, lane), kg);
+      if constexpr (SCAL) kg = kg * FAC[C + 16 * tm + l16];  // K^end = Diag(e^{g_C - g}) k
+      acc += kg;
     }
     store4(out_k + (GK_VT * C + 16 * tm + l16) * D + 16 * tn + 4 * lg, acc);
   }
@@ -683,11 +739,11 @@ __global__ __launch_bounds__(kG2Threads) void chunk_grad_gram_kernel(Problem p, 
   }
 }
 
-template <bool FG2>
+template <int MODE, bool DCH>
 void launch_state(const Problem& p, const char* ws, const float* dO, GradWork gw, int64_t nchunks,
                   hipStream_t stream) {
-  hipLaunchKernelGGL((chunk_grad_state_kernel<FG2>), dim3(unsigned(nchunks)), dim3(kG1Threads), 0, stream, p, ws,
-                     dO, gw);
+  hipLaunchKernelGGL((chunk_grad_state_kernel<MODE, DCH>), dim3(unsigned(nchunks)), dim3(kG1Threads), 0, stream, p,
+                     ws, dO, gw);
 }
 
 template <bool DCH, bool FG2>
@@ -711,12 +767,14 @@ hipError_t launch_chunk_grad(const Problem& p, const BwdArgs& g, const void* pac
   GradWork gw{w, reinterpret_cast<_Float16*>(w + nchunks * (kGkFloats + D)), w + nchunks * kGkFloats};
   const char* ws = static_cast<const char*>(packets);
   if (p.rate_sqrt) {
-    launch_state<true>(p, ws, g.dO, gw, nchunks, stream);
+    launch_state<kModeFg2, false>(p, ws, g.dO, gw, nchunks, stream);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     if (p.decay_channel) launch_gram<true, true>(p, g, gw, nchunks, stream);
     else launch_gram<false, true>(p, g, gw, nchunks, stream);
   } else {
-    launch_state<false>(p, ws, g.dO, gw, nchunks, stream);
+    if (!p.symmetric) launch_state<kModeGen, false>(p, ws, g.dO, gw, nchunks, stream);
+    else if (p.decay_channel) launch_state<kModeSym, true>(p, ws, g.dO, gw, nchunks, stream);
+    else launch_state<kModeSym, false>(p, ws, g.dO, gw, nchunks, stream);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     if (p.decay_channel) launch_gram<true, false>(p, g, gw, nchunks, stream);
     else launch_gram<false, false>(p, g, gw, nchunks, stream);

@@ -45,6 +45,9 @@ struct Problem {
   // K+ S + A_kk Vt); null otherwise.
   void* ck_M = nullptr;
   void* ck_Z = nullptr;
+  // ... and with one per-head gate, the prep's A_kk (fp16, the packet's six-block triangular
+  // layout, 6 KB per chunk), from which the gradients rebuild M; null otherwise.
+  void* ck_A = nullptr;
 };
 
 // Sequence tables of a packed batch (one workgroup): from nseq + 1 device offsets `cu` over T

@@ -271,14 +271,15 @@ def test_bwd_workspace_and_errors():
     # 32 columns; v * dv~
     token = 4 * (waves * nck * 128 * 2 + waves * 64 * 128 * 2 + 4 * 4 * bth * 128 + bth * 128)
     assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(_good_desc(B=2, T=100, H=4, chunk=1))) == token
-    # the chunk path: the forward's packets (general-gate layout, 92,160 B per chunk), a bf16 o
-    # buffer, the state at every chunk start and its adjoint at every chunk end (fp16), the
-    # in-chunk reads M and Z (fp16 [64][128] per chunk), then the gradient kernels' products
-    # (five [64][128] fp32 matrices, dGamma [128] fp32 and four [64][64] fp16 matrices per chunk)
+    # the chunk path (one per-head gate): the forward's packets (46,080 B per chunk), a bf16 o
+    # buffer, the state at every chunk start and its adjoint at every chunk end (fp16), delta and
+    # Z (fp16 [64][128] per chunk), the prep's A_kk (6 KB per chunk), then the gradient kernels'
+    # products (five [64][128] fp32 matrices, dGamma [128] fp32 and four [64][64] fp16 matrices)
     r256 = lambda n: (n + 255) // 256 * 256
     chunks = 2 * 4 * nck
-    need = (r256(chunks * 92160) + r256(bth * 128 * 2) + 2 * r256(chunks * 128 * 128 * 2) +
-            2 * r256(chunks * 64 * 128 * 2) + r256(chunks * ((5 * 64 * 128 + 128) * 4 + 4 * 64 * 64 * 2)))
+    need = (r256(chunks * 46080) + r256(bth * 128 * 2) + 2 * r256(chunks * 128 * 128 * 2) +
+            2 * r256(chunks * 64 * 128 * 2) + r256(chunks * 6 * 1024) +
+            r256(chunks * ((5 * 64 * 128 + 128) * 4 + 4 * 64 * 64 * 2)))
     assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(d)) == need
     assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(_good_desc(T=0))) == 0
     assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(_good_desc(erase_kind=_abi.DR_GATE_RATE_SQRT))) > 0
