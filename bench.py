@@ -2,7 +2,7 @@
 """Benchmark of the gated delta-rule hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-decode]
-                    [--no-extra] [--backward] [--segment-scan P]
+                    [--no-extra] [--backward | --backward-workload NAME | --no-backward] [--segment-scan P]
 
 One step is one chunked forward (dr_chunk_fwd) over the main prefill workload, by default the
 long-context one: decoupled per-channel erase and write gates with a per-channel decay
@@ -24,6 +24,10 @@ The single JSON line printed at the end carries:
                 and the packed serving prefill (16k tokens in 20 sequences)
   decode        1000 single-token steps for 256 sequences x 32 heads (steps/s, GB/s, fraction of
                 HBM peak)
+  backward      one gradient call (dr_chunk_bwd) on the scalar-gate workload (B=4 H=16 T=4096; or
+                --backward-workload, --backward for the main one): ms per call, beside the fp32
+                token-loop adjoint (chunk = 1) on the same inputs, and the fp64 adjoint oracle on a
+                sample
   cpu_baseline  the fp64 oracle on the first --cpu-tokens tokens of every head of the main
                 workload, the heads sharded over one worker process per host core (at most 16)
 """
@@ -412,7 +416,10 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other prefill workloads")
     ap.add_argument("--backward", action="store_true",
-                    help="also time the gradient call (dr_chunk_bwd) on the main workload")
+                    help="time the gradient call (dr_chunk_bwd) on the main workload")
+    ap.add_argument("--backward-workload", default="gdn_scalar_bf16_t4k",
+                    help="workload of the gradient call's timing (default: %(default)s)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the gradient call's timing")
     ap.add_argument("--workload", default=PREFILL,
                     help="prefill workload of the main line (default: %(default)s)")
     ap.add_argument("--segment-scan", type=int, default=0, metavar="P",
@@ -494,23 +501,25 @@ def main():
         line["segment_scan"] = {"segments": args.segment_scan, "ms": t_seg, "single_pass_ms": t_one,
                                 "max_rel_diff": rel}
         torch.cuda.empty_cache()
-    if args.backward:
-        bsteps = max(2, args.steps // 10)
-        bsec = time_backward(dr, torch, wl, bsteps, 1)
-        bbytes = backward_bytes(wl)
-        chunked = wl.qkv_dtype == "bf16" and wl.dk == 128 and wl.dv == 128 and not wl.seq_median
-        line["backward"] = {"workload": wl.name, "calls": bsteps, "ms": bsec * 1e3,
-                            "tokens_per_s": wl.token_heads / bsec, "hbm_frac": bbytes / bsec / 1e9 / HBM_PEAK_GBS,
-                            "bytes_per_call": bbytes,
-                            "kernel": ("dr_chunk_bwd = general-gate chunked forward (stores S, M) + adjoint scan "
+    if not args.no_backward:
+        bwl = wl if args.backward else workload(args.backward_workload)
+        bsteps = max(5, args.steps // 10)
+        bsec = time_backward(dr, torch, bwl, bsteps, 2)
+        bbytes = backward_bytes(bwl)
+        chunked = bwl.qkv_dtype == "bf16" and bwl.dk == 128 and bwl.dv == 128 and not bwl.seq_median
+        line["backward"] = {"workload": bwl.name, "calls": bsteps, "ms": bsec * 1e3,
+                            "tokens_per_s": bwl.token_heads / bsec,
+                            "hbm_frac": bbytes / bsec / 1e9 / HBM_PEAK_GBS, "bytes_per_call": bbytes,
+                            "kernel": ("dr_chunk_bwd = chunked forward (stores S and M or delta) + adjoint scan "
                                        "(stores G, Z) + chunk_grad_state_kernel + chunk_grad_gram_kernel")
                                       if chunked else
                                       "dr_chunk_bwd = bwd_token_kernel + bwd_reduce_kernel (fp32 token adjoint)"}
         if chunked:
-            tsec = time_backward(dr, torch, wl, 2, 1, chunk=1)
+            tsec = time_backward(dr, torch, bwl, 2, 1, chunk=1)
             line["backward"]["token_adjoint_ms"] = tsec * 1e3
+            line["backward"]["speedup_over_token_adjoint"] = tsec / bsec
         if not args.no_cpu:
-            line["backward"]["cpu_baseline"] = cpu_baseline_backward(wl, max(64, args.cpu_tokens // 64))
+            line["backward"]["cpu_baseline"] = cpu_baseline_backward(bwl, max(64, args.cpu_tokens // 64))
         torch.cuda.empty_cache()
     if not args.no_decode:
         dwl = workload(DECODE)

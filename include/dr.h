@@ -199,10 +199,16 @@ int dr_chunk_fwd_varlen(const dr_desc* desc, const int32_t* cu_seqlens, int32_t 
                         size_t workspace_bytes, void* stream);
 
 /* Gradients for training: of L = sum(o * dO) + sum(S_T * dS_T) with respect to every input of
- * dr_chunk_fwd, by the adjoint of the token loop (the forward pass of training is the
- * recurrence; "FG2-GDN ...", sections 2-3, chunk-parallel training of the update).  The kernels
- * run the forward again (state checkpoints every 64 tokens), then walk the tokens backwards in
- * fp32; desc->chunk is ignored.
+ * dr_chunk_fwd ("FG2-GDN ...", sections 2-3: the WY form makes training chunk-parallel;
+ * "Linearized 2-Simplicial Attention", method: the backward is a second scan over the chunks).
+ * Two paths:
+ *   - bf16 q/k/v with dk == dv == 128 and chunk 0 or 64 (the matrix-core path): the chunked
+ *     forward runs again and stores every chunk's incoming state and in-chunk reads, a reverse
+ *     scan over the chunks carries the state's adjoint and stores it at every chunk end, and
+ *     per-chunk kernels form the gradients on the matrix cores (fp16 operands, fp32
+ *     accumulation; the forward's accuracy);
+ *   - everything else, and chunk == 1: the fp32 adjoint of the token loop (state checkpoints
+ *     every 64 tokens, the tokens walked backwards).
  *
  *   dO     [B, T, H, dv] fp32 (required).       dS_T  [B, H, dk, dv] fp32, or NULL for zero.
  *   dq, dk [B, T, H, dk] fp32; dv [B, T, H, dv] fp32 (all required).
@@ -210,10 +216,14 @@ int dr_chunk_fwd_varlen(const dr_desc* desc, const int32_t* cu_seqlens, int32_t 
  *          gate gets the sum over its channels).  With write_is_erase the one gate's gradient
  *          (both uses) goes to derase and dwrite is ignored.
  *   dS0    [B, H, dk, dv] fp32, or NULL to skip.
- *   workspace: at least dr_chunk_bwd_workspace_bytes(desc) bytes: a state checkpoint every 64
- *          tokens and one chunk of states per (b, h, group of 256 / dk value columns), and
- *          four fp32 partial sums per row for every 32 value
- *          columns (at dk = dv = 128, 8 KB per token and head: 2.1 GB for B 4, H 16, T 4096).
+ *   workspace: at least dr_chunk_bwd_workspace_bytes(desc) bytes.  Matrix-core path: the
+ *          forward's packets, a bf16 copy of o, per 64-token chunk the incoming state and its
+ *          adjoint at the chunk end (fp16, 32 KB each), the reads and Z (fp16, 16 KB each), with
+ *          one per-head gate A_kk (6 KB), and the products of the gradient kernels (five fp32
+ *          [64][128], four fp16 [64][64] matrices and 512 B): 433 KB per chunk with general gates.
+ *          Token path: a state checkpoint every 64 tokens and one chunk of states per (b, h,
+ *          group of 256 / dk value columns), and four fp32 partial sums per row for every 32
+ *          value columns (at dk = dv = 128, 8 KB per token and head).
  * Outputs must not overlap one another, any input or the workspace.  T == 0 writes dS0 = dS_T
  * (zeros without it).  With DR_GATE_RATE_SQRT, derase is the gradient of the rate beta (through
  * both sqrt(beta) k and sqrt(beta) v).  Errors as dr_chunk_fwd. */

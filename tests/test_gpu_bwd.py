@@ -204,3 +204,40 @@ def test_bwd_full_shape_sampled_heads(dr):
         errs["dS0"] = _err(out["dS0"][b:b + 1, h:h + 1], ref["dS0"])
         print(f"bwd full shape (b={b}, h={h}): " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
         assert max(errs.values()) <= TOL_CHUNK, (b, h, errs)
+
+
+@pytest.mark.parametrize("variant", ["scalar", "kda", "decoupled", "fg2"])
+@pytest.mark.parametrize("edge", ["no_decay", "no_erase", "full_gates"])
+def test_bwd_chunk_path_edge_gates(dr, variant, edge):
+    # log a = 0; erase = 0 (one gate: no write either, so the reads M come only from the state;
+    # decoupled gates: gated linear attention); erase = write = 1
+    fg2 = variant == "fg2"
+    if fg2 and edge == "no_erase":
+        pytest.skip("FG2's rate is a square root of beta > 0")
+    inp, dO, dST = _case(1, 150, 2, 128, 128, "bf16", "kda" if fg2 else variant, True, 900)
+    if fg2:
+        from gated_delta_rule_dr_amd.workloads import Workload, generate
+
+        wl = Workload("case", 1, 150, 2, 128, 128, "bf16", "softplus", True, -4.0, 1.5, True, "erase", 0.05, 901,
+                      rate_sqrt=True)
+        inp = generate(wl)
+    if edge == "no_decay":
+        inp["log_decay"] = torch.zeros_like(inp["log_decay"])
+    elif edge == "no_erase":
+        inp["erase"] = torch.zeros_like(inp["erase"])
+    else:
+        inp["erase"] = torch.ones_like(inp["erase"])
+        if inp["write"] is not None:
+            inp["write"] = torch.ones_like(inp["write"])
+    if fg2:
+        x = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+        out = dr.chunk_bwd(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], None, x["S0"], dO=dO.cuda(),
+                           dS_T=dST.cuda(), fg2=True)
+        torch.cuda.synchronize()
+        ref = recurrence_fg2_bwd(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["S0"], dO, dST)
+        errs = {key: _err(out[key], ref[key]) for key in ("dq", "dk", "dv", "dlog_decay", "dS0")}
+        errs["dbeta"] = _err(out["derase"], ref["dbeta"])
+    else:
+        errs = _check(dr, inp, dO, dST)
+    print(f"bwd edge {variant} {edge}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert max(errs.values()) <= TOL_CHUNK, errs
