@@ -219,8 +219,7 @@ int dr_chunk_fwd_varlen(const dr_desc* desc, const int32_t* cu_seqlens, int32_t 
  *   workspace: at least dr_chunk_bwd_workspace_bytes(desc) bytes.  Matrix-core path: the
  *          forward's packets, a bf16 copy of o, per 64-token chunk the incoming state and its
  *          adjoint at the chunk end (fp16, 32 KB each), the reads and Z (fp16, 16 KB each), with
- *          one per-head gate A_kk (6 KB), and the products of the gradient kernels (five fp32
- *          [64][128], four fp16 [64][64] matrices and 512 B): 433 KB per chunk with general gates.
+ *          one per-head gate A_kk (6 KB), and 1.6 KB of per-token sums per chunk.
  *          Token path: a state checkpoint every 64 tokens and one chunk of states per (b, h,
  *          group of 256 / dk value columns), and four fp32 partial sums per row for every 32
  *          value columns (at dk = dv = 128, 8 KB per token and head).

@@ -273,13 +273,12 @@ def test_bwd_workspace_and_errors():
     assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(_good_desc(B=2, T=100, H=4, chunk=1))) == token
     # the chunk path (one per-head gate): the forward's packets (46,080 B per chunk), a bf16 o
     # buffer, the state at every chunk start and its adjoint at every chunk end (fp16), delta and
-    # Z (fp16 [64][128] per chunk), the prep's A_kk (6 KB per chunk), then the gradient kernels'
-    # products (five [64][128] fp32 matrices, dGamma [128] fp32 and four [64][64] fp16 matrices)
+    # Z (fp16 [64][128] per chunk), the prep's A_kk (6 KB per chunk), then the per-token sums of
+    # the per-head gates over each half of the channels (2 x (3 x 64 + 4) fp32 per chunk)
     r256 = lambda n: (n + 255) // 256 * 256
     chunks = 2 * 4 * nck
     need = (r256(chunks * 46080) + r256(bth * 128 * 2) + 2 * r256(chunks * 128 * 128 * 2) +
-            2 * r256(chunks * 64 * 128 * 2) + r256(chunks * 6 * 1024) +
-            r256(chunks * ((5 * 64 * 128 + 128) * 4 + 4 * 64 * 64 * 2)))
+            2 * r256(chunks * 64 * 128 * 2) + r256(chunks * 6 * 1024) + r256(chunks * 2 * 196 * 4))
     assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(d)) == need
     assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(_good_desc(T=0))) == 0
     assert L.dr_chunk_bwd_workspace_bytes(ctypes.byref(_good_desc(erase_kind=_abi.DR_GATE_RATE_SQRT))) > 0
