@@ -476,33 +476,40 @@ hipError_t launch_bwd_varlen(Problem p, const int* cu, const BwdArgs& g, void* w
   return launch_bwd(p, g, ws + bwd_tables_bytes(p.B), stream);
 }
 
-// Gradients through the chunk path: workspace = forward packets (general-gate layout, or FG2's
-// symmetric one) | o (bf16, unused) | chunk-start states | chunk-end adjoints (fp16 [dk][dv]
-// per chunk) | M (FG2: delta) and Z (fp16 [C][dv] per chunk) | the chunk gradients' products.
+// Gradients through the chunk path: workspace = the forward's workspace (its packets, in the
+// general-gate or symmetric layout; packed sequences: and the tables) | o (bf16, unused) |
+// chunk-start states | chunk-end adjoints (fp16 [dk][dv] per chunk) | M (one gate, FG2: delta) and
+// Z (fp16 [C][dv] per chunk) | A_kk (one gate) | the per-token sums of the gradient kernels.
 struct BwdChunkedLayout {
   int64_t pkt, obuf, ckS, ckG, ckM, ckZ, ckA, work, total;  // byte offsets
-  BwdChunkedLayout(const Problem& p) {
+  BwdChunkedLayout(const Problem& p, bool packed) {
     auto up = [](int64_t n) { return (n + 255) / 256 * 256; };
-    const int64_t nck = (int64_t(p.T) + CK - 1) / CK, bth = int64_t(p.B) * p.T * p.H;
-    const int64_t chunks = int64_t(p.B) * p.H * nck;
+    const int64_t bth = packed ? int64_t(p.T) * p.H : int64_t(p.B) * p.T * p.H;
+    const int64_t chunks = packed ? int64_t(p.H) * varlen_max_chunks(p.B, p.T)
+                                  : int64_t(p.B) * p.H * ((int64_t(p.T) + CK - 1) / CK);
     const bool one_gate = p.symmetric && !p.rate_sqrt;
     pkt = 0;
-    obuf = up(int64_t(chunk128_workspace_bytes(p.B, p.T, p.H, p.symmetric, p.decay_channel, p.rate_sqrt)));
+    obuf = up(int64_t(packed ? chunk128_varlen_workspace_bytes(p.B, p.T, p.H, p.symmetric, p.decay_channel,
+                                                               p.rate_sqrt)
+                             : chunk128_workspace_bytes(p.B, p.T, p.H, p.symmetric, p.decay_channel, p.rate_sqrt)));
     ckS = obuf + up(bth * p.dv * 2);
     ckG = ckS + up(chunks * p.dk * p.dv * 2);
     ckM = ckG + up(chunks * p.dk * p.dv * 2);
     ckZ = ckM + up(chunks * CK * p.dv * 2);
     ckA = ckZ + up(chunks * CK * p.dv * 2);
     work = ckA + (one_gate ? up(chunks * 6 * 1024) : 0);
-    total = work + up(int64_t(chunk_grad_work_bytes(p)));
+    total = work + up(int64_t(chunk_grad_work_bytes(p, packed)));
   }
 };
 
-size_t bwd_chunked_workspace_bytes(const Problem& p) { return size_t(BwdChunkedLayout(p).total); }
+size_t bwd_chunked_workspace_bytes(const Problem& p) { return size_t(BwdChunkedLayout(p, false).total); }
+size_t bwd_chunked_varlen_workspace_bytes(const Problem& p) { return size_t(BwdChunkedLayout(p, true).total); }
 
-hipError_t launch_bwd_chunked(const Problem& p, const BwdArgs& g, void* workspace, hipStream_t stream) {
-  if (p.dk != 128 || p.dv != 128 || p.seqs) return hipErrorInvalidValue;
-  const BwdChunkedLayout L(p);
+namespace {
+hipError_t bwd_chunked(const Problem& p, const int* cu, const BwdArgs& g, void* workspace, hipStream_t stream) {
+  if (p.dk != 128 || p.dv != 128) return hipErrorInvalidValue;
+  const bool packed = cu != nullptr;
+  const BwdChunkedLayout L(p, packed);
   char* ws = static_cast<char*>(workspace);
   // The forward stores every chunk's incoming state and its in-chunk reads M (general gates) or
   // delta (one per-head gate, with the prep's A_kk, from which the gradients rebuild M; FG2's
@@ -514,8 +521,9 @@ hipError_t launch_bwd_chunked(const Problem& p, const BwdArgs& g, void* workspac
   pf.ck_S = ws + L.ckS;
   pf.ck_M = ws + L.ckM;
   if (p.symmetric && !p.rate_sqrt) pf.ck_A = ws + L.ckA;
-  hipError_t e = launch_chunk128(pf, ws + L.pkt, stream);
+  hipError_t e = packed ? launch_chunk128_varlen(pf, cu, ws + L.pkt, stream) : launch_chunk128(pf, ws + L.pkt, stream);
   if (e != hipSuccess) return e;
+  if (packed) chunk128_varlen_tables(pf, ws + L.pkt);
   // the state's adjoint at every chunk end and Z, and dS0
   Problem pa = pf;
   pa.ck_S = nullptr;
@@ -530,6 +538,17 @@ hipError_t launch_bwd_chunked(const Problem& p, const BwdArgs& g, void* workspac
   pg.ck_G = pa.ck_G;
   pg.ck_Z = pa.ck_Z;
   return launch_chunk_grad(pg, g, ws + L.pkt, ws + L.work, stream);
+}
+}  // namespace
+
+hipError_t launch_bwd_chunked(const Problem& p, const BwdArgs& g, void* workspace, hipStream_t stream) {
+  if (p.seqs) return hipErrorInvalidValue;
+  return bwd_chunked(p, nullptr, g, workspace, stream);
+}
+
+hipError_t launch_bwd_chunked_varlen(const Problem& p, const int* cu, const BwdArgs& g, void* workspace,
+                                     hipStream_t stream) {
+  return bwd_chunked(p, cu, g, workspace, stream);
 }
 
 hipError_t launch_bwd(const Problem& p, const BwdArgs& g, void* workspace, hipStream_t stream) {

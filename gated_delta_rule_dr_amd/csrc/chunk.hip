@@ -78,13 +78,7 @@ __device__ __forceinline__ void store_rows(void* base, int64_t pkt, int t0, int 
   for (int r = 0; r < 4; ++r) dst[r * D] = (_Float16)x[r];
 }
 
-// One chunk of prep work: the row of its first token on the token axis ([B * T] for a dense
-// batch, the packed axis otherwise), its tokens (1 .. C), its head and its packet index.
-struct ChunkRef {
-  int64_t tok0;
-  int tlen, h;
-  int64_t pkt;
-};
+
 
 // The sequence of a scan workgroup (bh = sequence * H + h): the row of its first token, its
 // tokens and chunks, and the packet index of its first chunk for head h.  A dense batch stores
@@ -150,31 +144,6 @@ __device__ __forceinline__ void store_state(float* dst, int j0, const f32x4 (&S)
     for (int r = 0; r < 4; ++r) dst[(16 * wave + 4 * lg + r) * D + j0 + 16 * ct + l16] = S[ct][r];
 }
 
-// One chunk of prep work, from its work-item index: a dense batch walks (b, h, chunk) with
-// packet index blk; packed sequences walk (chunk, head) over the chunk table.  Work items number
-// fewer than 2^31 (one packet each, and the packets fit in device memory), so the index
-// arithmetic is 32-bit.
-__device__ __forceinline__ ChunkRef chunk_ref_of(const Problem& p, int64_t blk, int nchunks) {
-  ChunkRef r;
-  const uint32_t ub = uint32_t(blk);
-  if (p.chunks) {
-    const uint32_t g = ub / uint32_t(p.H);
-    r.h = int(ub - g * uint32_t(p.H));
-    const int4 e = p.chunks[g];
-    r.tok0 = e.x;
-    r.tlen = e.y;
-    r.pkt = int64_t(e.z) + int64_t(r.h) * e.w;
-  } else {
-    const uint32_t bh = ub / uint32_t(nchunks);
-    const int c = int(ub - bh * uint32_t(nchunks));
-    const int b = int(bh / uint32_t(p.H));
-    r.h = int(bh) - b * p.H;
-    r.tok0 = int64_t(b) * p.T + int64_t(c) * C;
-    r.tlen = p.T - c * C < C ? p.T - c * C : C;
-    r.pkt = blk;
-  }
-  return r;
-}
 
 // The solve factor T (fp16 in LDS, row stride CS, zero upper triangle) into the six stored
 // 16 x 32 blocks of the packet's first matrix.
@@ -2192,20 +2161,22 @@ size_t chunk128_varlen_workspace_bytes(int nseq, int T, int H, bool symmetric, b
                 round256(int64_t(nseq) * 16) + round256(int64_t(nseq) * 4) + 256);
 }
 
-hipError_t launch_chunk128_varlen(Problem p, const int* cu, void* workspace, hipStream_t stream) {
+void chunk128_varlen_tables(Problem& p, void* workspace) {
   const int64_t maxc = varlen_max_chunks(p.B, p.T);
-  char* ws = static_cast<char*>(workspace);
-  char* tables = ws + int64_t(p.H) * maxc * packet_bytes(p.symmetric, p.decay_channel, p.rate_sqrt);
-  int4* chunks = reinterpret_cast<int4*>(tables);
-  int4* seqs = reinterpret_cast<int4*>(tables + round256(maxc * 16));
+  char* tables = static_cast<char*>(workspace) +
+                 int64_t(p.H) * maxc * packet_bytes(p.symmetric, p.decay_channel, p.rate_sqrt);
+  p.chunks = reinterpret_cast<int4*>(tables);
+  p.seqs = reinterpret_cast<int4*>(tables + round256(maxc * 16));
   int* order = reinterpret_cast<int*>(tables + round256(maxc * 16) + round256(int64_t(p.B) * 16));
-  int* total = order + round256(int64_t(p.B) * 4) / 4;
-  hipError_t e = launch_varlen_setup(cu, p.B, p.T, p.H, C, seqs, chunks, total, order, stream);
-  if (e != hipSuccess) return e;
-  p.seqs = seqs;
-  p.chunks = chunks;
-  p.nchunks_total = total;
   p.order = order;
+  p.nchunks_total = order + round256(int64_t(p.B) * 4) / 4;
+}
+
+hipError_t launch_chunk128_varlen(Problem p, const int* cu, void* workspace, hipStream_t stream) {
+  chunk128_varlen_tables(p, workspace);
+  hipError_t e = launch_varlen_setup(cu, p.B, p.T, p.H, C, const_cast<int4*>(p.seqs), const_cast<int4*>(p.chunks),
+                                     const_cast<int*>(p.nchunks_total), const_cast<int*>(p.order), stream);
+  if (e != hipSuccess) return e;
   return launch_chunk128(p, workspace, stream);
 }
 

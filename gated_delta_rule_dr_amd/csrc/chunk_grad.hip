@@ -126,14 +126,14 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int blk = wave & 3, pq = wave >> 2;  // this wave's block and channel pair
-  const int64_t pkt = blockIdx.x >> 1;
+  // work item blk = one chunk of one head (packed sequences: from the chunk table)
+  const int64_t item = blockIdx.x >> 1;
+  if (p.chunks && item >= int64_t(p.H) * *p.nchunks_total) return;
+  const ChunkRef cr = chunk_ref_of(p, item, (p.T + C - 1) / C);
+  const int64_t pkt = cr.pkt;
   const int half = blockIdx.x & 1, ch0 = 64 * half;
-  const int nck = (p.T + C - 1) / C;
-  const int bh = int(pkt / nck), ci = int(pkt - int64_t(bh) * nck);
-  const int b = bh / p.H, h = bh - b * p.H;
-  const int tlen = p.T - ci * C < C ? p.T - ci * C : C;
-  const int64_t tok0 = (int64_t(b) * p.T + int64_t(ci) * C) * p.H + h;
-  auto tok = [&](int t) { return tok0 + int64_t(t) * p.H; };
+  const int tlen = cr.tlen;
+  auto tok = [&](int t) { return (cr.tok0 + t) * int64_t(p.H) + cr.h; };
   const _Float16* Sg = static_cast<const _Float16*>(p.ck_S) + pkt * D * D;
   const _Float16* Gg = static_cast<const _Float16*>(p.ck_G) + pkt * D * D;
   const _Float16* Zg = static_cast<const _Float16*>(p.ck_Z) + pkt * C * D;
@@ -669,7 +669,7 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
   // the half's per-token sums (the two channel pairs added in a fixed order)
   if (part) {
     __syncthreads();
-    float* pp = part + (pkt * 2 + half) * kPartFloats;
+    float* pp = part + (item * 2 + half) * kPartFloats;
     if (tid < 3 * C) {
       const int which = tid / C, t = tid - which * C;
       pp[tid] = RED[(which * 2 + 0) * 64 + t] + RED[(which * 2 + 1) * 64 + t];
@@ -684,14 +684,13 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
 // g_C's share.
 __global__ __launch_bounds__(64) void chunk_grad_sums_kernel(Problem p, BwdArgs g, const float* __restrict__ part,
                                                              int want_decay, int want_erase, int want_write) {
-  const int64_t pkt = blockIdx.x;
+  const int64_t blk = blockIdx.x;
   const int lane = threadIdx.x;
-  const int nck = (p.T + C - 1) / C;
-  const int bh = int(pkt / nck), ci = int(pkt - int64_t(bh) * nck);
-  const int b = bh / p.H, h = bh - b * p.H;
-  const int tlen = p.T - ci * C < C ? p.T - ci * C : C;
-  const int64_t tk = (int64_t(b) * p.T + int64_t(ci) * C + lane) * p.H + h;
-  const float* p0 = part + pkt * 2 * kPartFloats;
+  if (p.chunks && blk >= int64_t(p.H) * *p.nchunks_total) return;
+  const ChunkRef cr = chunk_ref_of(p, blk, (p.T + C - 1) / C);
+  const int tlen = cr.tlen;
+  const int64_t tk = (cr.tok0 + lane) * int64_t(p.H) + cr.h;
+  const float* p0 = part + blk * 2 * kPartFloats;
   const float* p1 = p0 + kPartFloats;
   if (want_decay) {
     float x = p0[lane] + p1[lane];
@@ -711,14 +710,18 @@ __global__ __launch_bounds__(64) void chunk_grad_sums_kernel(Problem p, BwdArgs 
 
 }  // namespace
 
-size_t chunk_grad_work_bytes(const Problem& p) {
-  const int64_t nchunks = int64_t(p.B) * p.H * ((int64_t(p.T) + C - 1) / C);
-  return size_t(nchunks * 2 * kPartFloats * 4);
+// Work items: every chunk of every head (packed sequences: as many as their lengths allow).
+static int64_t grad_items(const Problem& p, bool packed) {
+  return packed ? int64_t(p.H) * varlen_max_chunks(p.B, p.T) : int64_t(p.B) * p.H * ((int64_t(p.T) + C - 1) / C);
+}
+
+size_t chunk_grad_work_bytes(const Problem& p, bool packed) {
+  return size_t(grad_items(p, packed) * 2 * kPartFloats * 4);
 }
 
 hipError_t launch_chunk_grad(const Problem& p, const BwdArgs& g, const void* packets, void* work,
                              hipStream_t stream) {
-  const int64_t nchunks = int64_t(p.B) * p.H * ((int64_t(p.T) + C - 1) / C);
+  const int64_t nchunks = grad_items(p, p.chunks != nullptr);
   if (nchunks == 0) return hipSuccess;
   const bool fg2 = p.rate_sqrt;
   const bool want_decay = !p.decay_channel;

@@ -4,6 +4,7 @@
 #pragma once
 
 #include "dr_device.h"
+#include "dr_internal.h"
 
 namespace dr {
 namespace {
@@ -219,6 +220,40 @@ __device__ __forceinline__ half8 frag_tri_t(const _Float16* base, int c0, int r0
   return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+
+// One chunk of prep work: the row of its first token on the token axis ([B * T] for a dense
+// batch, the packed axis otherwise), its tokens (1 .. C), its head and its packet index.
+struct ChunkRef {
+  int64_t tok0;
+  int tlen, h;
+  int64_t pkt;
+};
+
+// One chunk of prep work, from its work-item index: a dense batch walks (b, h, chunk) with
+// packet index blk; packed sequences walk (chunk, head) over the chunk table.  Work items number
+// fewer than 2^31 (one packet each, and the packets fit in device memory), so the index
+// arithmetic is 32-bit.
+__device__ __forceinline__ ChunkRef chunk_ref_of(const Problem& p, int64_t blk, int nchunks) {
+  ChunkRef r;
+  const uint32_t ub = uint32_t(blk);
+  if (p.chunks) {
+    const uint32_t g = ub / uint32_t(p.H);
+    r.h = int(ub - g * uint32_t(p.H));
+    const int4 e = p.chunks[g];
+    r.tok0 = e.x;
+    r.tlen = e.y;
+    r.pkt = int64_t(e.z) + int64_t(r.h) * e.w;
+  } else {
+    const uint32_t bh = ub / uint32_t(nchunks);
+    const int c = int(ub - bh * uint32_t(nchunks));
+    const int b = int(bh / uint32_t(p.H));
+    r.h = int(bh) - b * p.H;
+    r.tok0 = int64_t(b) * p.T + int64_t(c) * C;
+    r.tlen = p.T - c * C < C ? p.T - c * C : C;
+    r.pkt = blk;
+  }
+  return r;
+}
 
 }  // namespace
 }  // namespace dr

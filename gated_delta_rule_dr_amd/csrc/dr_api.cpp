@@ -376,7 +376,7 @@ size_t dr_chunk_bwd_varlen_workspace_bytes(const dr_desc* desc, int32_t nseq) {
   dr::Problem p = make_problem(desc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                nullptr);
   p.B = nseq;
-  return dr::bwd_varlen_workspace_bytes(p);
+  return uses_chunk128(desc) ? dr::bwd_chunked_varlen_workspace_bytes(p) : dr::bwd_varlen_workspace_bytes(p);
 }
 
 int dr_chunk_bwd_varlen(const dr_desc* d, const int32_t* cu_seqlens, int32_t nseq, const void* q, const void* k,
@@ -487,6 +487,7 @@ int chunk_bwd_common(const dr_desc* d, const int32_t* cu_seqlens, int32_t nseq, 
   dr::BwdArgs g{dO, dS_T, dq, dk, dv, dlog_decay, derase, dwrite, dS0};
   if (packed) {
     p.B = nseq;
+    if (uses_chunk128(d)) return launched(dr::launch_bwd_chunked_varlen(p, cu_seqlens, g, workspace, s));
     return launched(dr::launch_bwd_varlen(p, cu_seqlens, g, workspace, s));
   }
   if (uses_chunk128(d)) return launched(dr::launch_bwd_chunked(p, g, workspace, s));

@@ -76,6 +76,9 @@ hipError_t launch_chunk128(const Problem& p, void* workspace, hipStream_t stream
 // The adjoint scan over the packets that launch_chunk128 left in `workspace` (same problem): the
 // state's adjoint at the end of every chunk into p.ck_G and at the start of the sequence into
 // dS0 (when not null), from dO [B,T,H,dv] and dS_T (null: zero).
+// The table pointers (p.seqs, p.chunks, p.nchunks_total, p.order) of a packed batch in the
+// workspace of launch_chunk128_varlen (the tables its setup kernel writes).
+void chunk128_varlen_tables(Problem& p, void* workspace);
 hipError_t launch_chunk128_adjoint(const Problem& p, const void* workspace, const float* dO, const float* dS_T,
                                    float* dS0, hipStream_t stream);
 
@@ -110,9 +113,13 @@ hipError_t launch_bwd(const Problem& p, const BwdArgs& g, void* workspace, hipSt
 // chunk's end adjoint and Z, and each chunk's gradients then follow on the matrix cores.
 size_t bwd_chunked_workspace_bytes(const Problem& p);
 hipError_t launch_bwd_chunked(const Problem& p, const BwdArgs& g, void* workspace, hipStream_t stream);
-// The per-chunk gradient kernels (p carries ck_S, ck_G, ck_M, ck_Z; `packets` the forward's
-// packets; `work` chunk_grad_work_bytes(p) bytes).
-size_t chunk_grad_work_bytes(const Problem& p);
+// The same over p.B packed sequences delimited by the device offsets `cu` (p.T packed tokens).
+size_t bwd_chunked_varlen_workspace_bytes(const Problem& p);
+hipError_t launch_bwd_chunked_varlen(const Problem& p, const int* cu, const BwdArgs& g, void* workspace,
+                                     hipStream_t stream);
+// The per-chunk gradient kernels (p carries ck_S, ck_G, ck_M, ck_Z (and ck_A), and for packed
+// sequences the chunk tables; `packets` the forward's packets; `work` chunk_grad_work_bytes bytes).
+size_t chunk_grad_work_bytes(const Problem& p, bool packed);
 hipError_t launch_chunk_grad(const Problem& p, const BwdArgs& g, const void* packets, void* work,
                              hipStream_t stream);
 // The same over p.B packed sequences delimited by the device offsets `cu` (p.T packed tokens).

@@ -202,7 +202,8 @@ int dr_chunk_fwd_varlen(const dr_desc* desc, const int32_t* cu_seqlens, int32_t 
  * dr_chunk_fwd ("FG2-GDN ...", sections 2-3: the WY form makes training chunk-parallel;
  * "Linearized 2-Simplicial Attention", method: the backward is a second scan over the chunks).
  * Two paths:
- *   - bf16 q/k/v with dk == dv == 128 and chunk 0 or 64 (the matrix-core path): the chunked
+ *   - bf16 q/k/v with dk == dv == 128 and chunk 0 or 64 (the matrix-core path; dense or packed
+ *     with dr_chunk_bwd_varlen): the chunked
  *     forward runs again and stores every chunk's incoming state and in-chunk reads, a reverse
  *     scan over the chunks carries the state's adjoint and stores it at every chunk end, and
  *     per-chunk kernels form the gradients on the matrix cores (fp16 operands, fp32

@@ -299,9 +299,19 @@ def test_bwd_varlen_workspace_and_errors():
     nseq = 5
     maxc = (1000 + 63 * nseq) // 64
     nslice, waves, bth = 64, nseq * 4 * 64, 1000 * 4
+    # the token path (chunk = 1): the sequence table, checkpoints, states, row parts, v * dv~
     tables = (16 * nseq + 255) // 256 * 256 + 256
     layout = 4 * (nslice * 4 * maxc * 128 * 2 + waves * 64 * 128 * 2 + 4 * (nslice // 16) * bth * 128 + bth * 128)
-    assert L.dr_chunk_bwd_varlen_workspace_bytes(ctypes.byref(d), nseq) == tables + layout
+    assert L.dr_chunk_bwd_varlen_workspace_bytes(ctypes.byref(_good_desc(B=1, T=1000, H=4, chunk=1)), nseq) == \
+        tables + layout
+    # the chunk path: the packed forward's workspace (packets of H x maxc chunks, the chunk,
+    # sequence and order tables, the count), then the dense path's buffers for H x maxc chunks
+    r256 = lambda n: (n + 255) // 256 * 256
+    chunks = 4 * maxc
+    fwd = chunks * 46080 + r256(maxc * 16) + r256(nseq * 16) + r256(nseq * 4) + 256
+    need = (r256(fwd) + r256(bth * 128 * 2) + 2 * r256(chunks * 128 * 128 * 2) + 2 * r256(chunks * 64 * 128 * 2) +
+            r256(chunks * 6 * 1024) + r256(chunks * 2 * 196 * 4))
+    assert L.dr_chunk_bwd_varlen_workspace_bytes(ctypes.byref(d), nseq) == need
     assert L.dr_chunk_bwd_varlen_workspace_bytes(ctypes.byref(_good_desc(B=2)), nseq) == 0
     assert L.dr_chunk_bwd_varlen_workspace_bytes(ctypes.byref(d), 0) == 0
     ptr = dict(P)
