@@ -243,3 +243,37 @@ def test_bwd_chunk_path_edge_gates(dr, variant, edge):
         errs = _check(dr, inp, dO, dST)
     print(f"bwd edge {variant} {edge}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert max(errs.values()) <= TOL_CHUNK, errs
+
+
+def test_bwd_packed_fg2_rate(dr):
+    # FG2's rate over packed sequences (one empty): each sequence's gradients against the rate
+    # form's adjoint over its own tokens from its own state
+    from gated_delta_rule_dr_amd.workloads import Workload, generate
+
+    lens = [90, 0, 1, 130]
+    T = sum(lens)
+    wl = Workload("case", 1, T, 2, 128, 128, "bf16", "softplus", True, -4.0, 1.5, True, "erase", 0.0, 610,
+                  rate_sqrt=True)
+    inp = generate(wl)
+    g = torch.Generator().manual_seed(611)
+    N = len(lens)
+    S0 = (0.05 * torch.randn((N, 2, 128, 128), generator=g, dtype=torch.float64)).float()
+    dO = torch.randn((1, T, 2, 128), generator=g, dtype=torch.float64).float()
+    dST = torch.randn((N, 2, 128, 128), generator=g, dtype=torch.float64).float()
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    out = dr.chunk_bwd(x["q"], x["k"], x["v"], x["log_decay"], x["erase"], None, S0.cuda(), dO=dO.cuda(),
+                       dS_T=dST.cuda(), fg2=True, cu_seqlens=torch.tensor(cu, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    for n in range(N):
+        lo, hi = int(cu[n]), int(cu[n + 1])
+        if hi == lo:
+            assert torch.equal(out["dS0"][n].cpu(), dST[n])
+            continue
+        cut = lambda key: inp[key][:, lo:hi]
+        ref = recurrence_fg2_bwd(cut("q"), cut("k"), cut("v"), cut("log_decay"), cut("erase"), S0[n:n + 1],
+                                 dO[:, lo:hi], dST[n:n + 1])
+        for key in ("dq", "dk", "dv", "dlog_decay"):
+            assert _err(out[key][:, lo:hi], ref[key]) <= TOL_CHUNK, (n, key)
+        assert _err(out["derase"][:, lo:hi], ref["dbeta"]) <= TOL_CHUNK, n
+        assert _err(out["dS0"][n:n + 1], ref["dS0"]) <= TOL_CHUNK, n
