@@ -94,7 +94,7 @@ constexpr int kArena = kArenaP12 + 2 * C * 4 + 64 * 4;                          
 
 template <int MODE, bool DCH>
 __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArgs g, const char* __restrict__ ws,
-                                                               float* __restrict__ part) {
+                                                               float* __restrict__ part, int64_t nitems) {
   constexpr bool FG2 = MODE == kModeFg2, SYM = MODE == kModeSym;
   constexpr bool SCAL = SYM && !DCH;
   constexpr int NA = FG2 ? 2 : 4;
@@ -126,12 +126,16 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int blk = wave & 3, pq = wave >> 2;  // this wave's block and channel pair
-  // work item blk = one chunk of one head (packed sequences: from the chunk table)
-  const int64_t item = blockIdx.x >> 1;
-  if (p.chunks && item >= int64_t(p.H) * *p.nchunks_total) return;
+  // Work item = one chunk of one head (packed sequences: from the chunk table).  Workgroups are
+  // dealt to the eight XCDs in turn (linear id mod 8), each with its own L2, so the two halves of
+  // an item take ids 8 apart: the same XCD, one after the other, and the second half finds the
+  // chunk's shared operands in that L2.
+  const uint32_t lid = blockIdx.x;
+  const int64_t item = int64_t((lid >> 4) << 3 | (lid & 7));
+  const int half = (lid >> 3) & 1, ch0 = 64 * half;
+  if (item >= nitems || (p.chunks && item >= int64_t(p.H) * *p.nchunks_total)) return;
   const ChunkRef cr = chunk_ref_of(p, item, (p.T + C - 1) / C);
   const int64_t pkt = cr.pkt;
-  const int half = blockIdx.x & 1, ch0 = 64 * half;
   const int tlen = cr.tlen;
   auto tok = [&](int t) { return (cr.tok0 + t) * int64_t(p.H) + cr.h; };
   const _Float16* Sg = static_cast<const _Float16*>(p.ck_S) + pkt * D * D;
@@ -729,22 +733,22 @@ hipError_t launch_chunk_grad(const Problem& p, const BwdArgs& g, const void* pac
   const bool want_write = !fg2 && g.dwrite != nullptr && !p.write_channel;
   float* part = (want_decay || want_erase || want_write) ? static_cast<float*>(work) : nullptr;
   const char* ws = static_cast<const char*>(packets);
-  const dim3 grid(unsigned(2 * nchunks)), block(kFThreads);
+  const dim3 grid(unsigned((2 * nchunks + 15) / 16 * 16)), block(kFThreads);  // whole groups of 8 x 2
   if (fg2) {
     if (p.decay_channel)
-      hipLaunchKernelGGL((chunk_grad_kernel<kModeFg2, true>), grid, block, 0, stream, p, g, ws, part);
+      hipLaunchKernelGGL((chunk_grad_kernel<kModeFg2, true>), grid, block, 0, stream, p, g, ws, part, nchunks);
     else
-      hipLaunchKernelGGL((chunk_grad_kernel<kModeFg2, false>), grid, block, 0, stream, p, g, ws, part);
+      hipLaunchKernelGGL((chunk_grad_kernel<kModeFg2, false>), grid, block, 0, stream, p, g, ws, part, nchunks);
   } else if (p.symmetric) {
     if (p.decay_channel)
-      hipLaunchKernelGGL((chunk_grad_kernel<kModeSym, true>), grid, block, 0, stream, p, g, ws, part);
+      hipLaunchKernelGGL((chunk_grad_kernel<kModeSym, true>), grid, block, 0, stream, p, g, ws, part, nchunks);
     else
-      hipLaunchKernelGGL((chunk_grad_kernel<kModeSym, false>), grid, block, 0, stream, p, g, ws, part);
+      hipLaunchKernelGGL((chunk_grad_kernel<kModeSym, false>), grid, block, 0, stream, p, g, ws, part, nchunks);
   } else {
     if (p.decay_channel)
-      hipLaunchKernelGGL((chunk_grad_kernel<kModeGen, true>), grid, block, 0, stream, p, g, ws, part);
+      hipLaunchKernelGGL((chunk_grad_kernel<kModeGen, true>), grid, block, 0, stream, p, g, ws, part, nchunks);
     else
-      hipLaunchKernelGGL((chunk_grad_kernel<kModeGen, false>), grid, block, 0, stream, p, g, ws, part);
+      hipLaunchKernelGGL((chunk_grad_kernel<kModeGen, false>), grid, block, 0, stream, p, g, ws, part, nchunks);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !part) return e;
