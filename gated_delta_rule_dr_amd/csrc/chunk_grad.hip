@@ -305,20 +305,11 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
   __syncthreads();
 
   // ---- phase 2: G; dGamma of the half's channels; the products with G ------------------------
-  {
-    const int u = tid, d = ch0 + (u >> 3), j = (u & 7) * 16;  // 64 rows x 8 units of 16 halves
-    float x = 0.f;
-#pragma unroll
-    for (int e2 = 0; e2 < 2; ++e2) {
-      const half8 g8 = *reinterpret_cast<const half8*>(Gg + d * D + j + 8 * e2);
-      const half8 s8 = *reinterpret_cast<const half8*>(SG + d * P1 + j + 8 * e2);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x = fmaf(float(g8[e]), float(s8[e]), x);
-    }
-#pragma unroll
-    for (int o = 4; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-    if ((lane & 7) == 0) DGAM[u >> 3] = x;
-  }
+  // dGamma of the half's channels: this thread's 16 S values of row ch0 + tid / 8 go to registers,
+  // G replaces S in the LDS, then the products
+  const int dg_d = ch0 + (tid >> 3), dg_j = (tid & 7) * 16;
+  const half8 s_a = *reinterpret_cast<const half8*>(SG + dg_d * P1 + dg_j);
+  const half8 s_b = *reinterpret_cast<const half8*>(SG + dg_d * P1 + dg_j + 8);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 2048 / kFThreads; ++i) {
@@ -326,6 +317,19 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
     *reinterpret_cast<uint4*>(SG + d * P1 + j) = *reinterpret_cast<const uint4*>(Gg + d * D + j);
   }
   __syncthreads();
+  {
+    const half8 g_a = *reinterpret_cast<const half8*>(SG + dg_d * P1 + dg_j);
+    const half8 g_b = *reinterpret_cast<const half8*>(SG + dg_d * P1 + dg_j + 8);
+    float x = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x = fmaf(float(g_a[e]), float(s_a[e]), x);
+      x = fmaf(float(g_b[e]), float(s_b[e]), x);
+    }
+#pragma unroll
+    for (int o = 4; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    if ((lane & 7) == 0) DGAM[tid >> 3] = x;
+  }
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int c0 = ch0 + 32 * pq + 16 * ct;
@@ -426,6 +430,27 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
   const int m_ref = 16 * blk + 7;
   constexpr float kSpan = 6.f * kLog2e;
 
+  // the chain rule's raw inputs of this lane's channels, issued before the products
+  uint2 vbs[2], kbs[2];
+  f32x4 e4s[2], w4s[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int64_t xo = x_own + ch0 + 32 * pq + 16 * ct + 4 * lg;
+    vbs[ct] = kbs[ct] = make_uint2(0, 0);
+    e4s[ct] = w4s[ct] = f32x4{1.f, 1.f, 1.f, 1.f};
+    if (own_ok) {
+      vbs[ct] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.v) + xo);
+      if (FG2) {
+        kbs[ct] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.k) + xo);
+        e4s[ct] = *reinterpret_cast<const f32x4*>(p.erase + xo);
+      } else {
+        if (p.erase_channel) e4s[ct] = *reinterpret_cast<const f32x4*>(p.erase + xo);
+        else e4s[ct] = f32x4{1.f, 1.f, 1.f, 1.f} * p.erase[x_own / D];
+        if (p.write_channel) w4s[ct] = *reinterpret_cast<const f32x4*>(p.write + xo);
+        else w4s[ct] = f32x4{1.f, 1.f, 1.f, 1.f} * p.write[x_own / D];
+      }
+    }
+  }
   float s_e = 0.f, s_w = 0.f, s_g = 0.f;
   f32x4 dgv[2], gnv[2];
 #pragma unroll
@@ -549,20 +574,8 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
 
     // ---- chain rule, outputs (global channels ch0 + cq ..) -----------------------------------
     const int64_t xo = x_own + ch0 + cq;
-    uint2 vb = make_uint2(0, 0), kb = make_uint2(0, 0);
-    f32x4 e4 = {1.f, 1.f, 1.f, 1.f}, w4 = {1.f, 1.f, 1.f, 1.f};
-    if (own_ok) {
-      vb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.v) + xo);
-      if (FG2) {
-        kb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.k) + xo);
-        e4 = *reinterpret_cast<const f32x4*>(p.erase + xo);
-      } else {
-        if (p.erase_channel) e4 = *reinterpret_cast<const f32x4*>(p.erase + xo);
-        else e4 = f32x4{1.f, 1.f, 1.f, 1.f} * p.erase[x_own / D];
-        if (p.write_channel) w4 = *reinterpret_cast<const f32x4*>(p.write + xo);
-        else w4 = f32x4{1.f, 1.f, 1.f, 1.f} * p.write[x_own / D];
-      }
-    }
+    const uint2 vb = vbs[ct], kb = kbs[ct];
+    const f32x4 e4 = e4s[ct], w4 = w4s[ct];
     float vv[4], kraw[4];
     vv[0] = __uint_as_float(vb.x << 16);
     vv[1] = __uint_as_float(vb.x & 0xffff0000u);
