@@ -511,7 +511,7 @@ def main():
                             "tokens_per_s": bwl.token_heads / bsec,
                             "hbm_frac": bbytes / bsec / 1e9 / HBM_PEAK_GBS, "bytes_per_call": bbytes,
                             "kernel": ("dr_chunk_bwd = chunked forward (stores S and M or delta) + adjoint scan "
-                                       "(stores G, Z) + chunk_grad_state_kernel + chunk_grad_gram_kernel")
+                                       "(stores G, Z) + chunk_grad_kernel + chunk_grad_sums_kernel")
                                       if chunked else
                                       "dr_chunk_bwd = bwd_token_kernel + bwd_reduce_kernel (fp32 token adjoint)"}
         if chunked:
