@@ -85,6 +85,19 @@ __device__ __forceinline__ half4v h4(float4 x) {
 //     the chain rule and the outputs; per-head gate and decay sums of the half go to `part` and
 //     chunk_grad_sums_kernel adds the two halves.
 // ------------------------------------------------------------------------------------------
+// `x` through an empty asm: a load that is masked where it is used stays where it was issued
+// (the compiler otherwise moves such a load into the branch it makes of the mask, and waits for
+// it there).
+template <typename T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 constexpr int kFThreads = 512;
 constexpr int PX = 72;             // row stride (halves) of the half's [64][64] k, q, u tables
 constexpr int GSH = 68;            // row stride (floats) of the half's g table
@@ -92,7 +105,8 @@ constexpr int kPartFloats = 3 * C + 4;  // per (chunk, half): decay, erase, writ
 constexpr int kArenaP12 = D * P1 * 2 + 4 * C * P1 * 2 + 2 * C * P2 * 2 + C * P1 * 2;  // 140,288 B
 constexpr int kArena = kArenaP12 + 2 * C * 4 + 64 * 4;                                  // + FAC + DGAM
 
-template <int MODE, bool DCH>
+// GCH (general gates only): erase and write both per channel, fixed at compile time
+template <int MODE, bool DCH, bool GCH>
 __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArgs g, const char* __restrict__ ws,
                                                                float* __restrict__ part, int64_t nitems) {
   constexpr bool FG2 = MODE == kModeFg2, SYM = MODE == kModeSym;
@@ -147,75 +161,142 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
   const bool own_ok = t_own < tlen;
   const int64_t x_own = tok(own_ok ? t_own : 0) * D;
   const bool shared_gate = g.dwrite == nullptr;
+  // gate kinds: one gate per head on the symmetric path, FG2's rate per channel
+  const bool ech = FG2 || GCH || (!SYM && p.erase_channel);
+  const bool wch = GCH || (!FG2 && !SYM && p.write_channel);
 
-  // ---- phase 1: loads ---------------------------------------------------------------------
+  // ---- phase 1: loads (every global load of the phase issued before the first LDS store; rows
+  // past the last token read the last token and are zeroed at the store) --------------------------
+  const int tlast = tlen > 0 ? tlen - 1 : 0;
+  const char* pk = ws + pkt * PK::bytes;
+  auto phase1_loads = [&](auto wch_c) {
+  constexpr bool WCH = decltype(wch_c)::value;
+  u32x4 rS[4], rZ[2], rM[2], rV[2], rA[2], rK[2];
+  f32x4 rO[4], rW[2][2];
+  float rw1[2] = {0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 2048 / kFThreads; ++i) {  // S
-    const int u = tid + kFThreads * i, d = u >> 4, j = (u & 15) * 8;
-    *reinterpret_cast<uint4*>(SG + d * P1 + j) = *reinterpret_cast<const uint4*>(Sg + d * D + j);
+  for (int i = 0; i < 4; ++i) {  // S
+    const int u = tid + kFThreads * i;
+    rS[i] = *reinterpret_cast<const u32x4*>(Sg + (u >> 4) * D + (u & 15) * 8);
   }
 #pragma unroll
-  for (int i = 0; i < 1024 / kFThreads; ++i) {  // Z, M (or delta)
+  for (int i = 0; i < 2; ++i) {  // Z, M (or delta)
+    const int u = tid + kFThreads * i;
+    rZ[i] = *reinterpret_cast<const u32x4*>(Zg + (u >> 4) * D + (u & 15) * 8);
+    rM[i] = *reinterpret_cast<const u32x4*>(Mg + (u >> 4) * D + (u & 15) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // dO
+    const int f = tid + kFThreads * i, t = min(f >> 5, tlast);
+    rO[i] = *reinterpret_cast<const f32x4*>(g.dO + tok(t) * D + (f & 31) * 4);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // v and its write gate (FG2: the rate)
+    const int u = tid + kFThreads * i, j = (u & 15) * 8;
+    const int64_t x = tok(min(u >> 4, tlast));
+    rV[i] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.v) + x * D + j);
+    if (WCH) {
+      const float* src = (FG2 ? p.erase : p.write) + x * D + j;
+      rW[i][0] = *reinterpret_cast<const f32x4*>(src);
+      rW[i][1] = *reinterpret_cast<const f32x4*>(src + 4);
+    } else {
+      rw1[i] = p.write[x];
+    }
+  }
+  const char* akk = SYM ? static_cast<const char*>(p.ck_A) + pkt * (6 * 1024) : pk + PK::mat + 2 * PK::matb;
+  if constexpr (!FG2) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {  // A_kk, A_qk (six stored blocks each; units past 767 repeat 767)
+      const int u = min(tid + kFThreads * i, 767);
+      const int m = u / 384, k = (u % 384) / 64, w64 = u % 64;
+      rA[i] = *reinterpret_cast<const u32x4*>((m ? pk + PK::mat + PK::matb : akk) + 1024 * k + 16 * w64);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)  // K+ (one gate) or K^end
+      rK[i] = *reinterpret_cast<const u32x4*>(pk + (SYM ? PK::kp : PK::kmt) + 16 * (tid + kFThreads * i));
+  }
+  float fac = 0.f;
+  if constexpr (SCAL) {
+    const float* gv = reinterpret_cast<const float*>(pk + PK::gate);
+    fac = gv[(tid < C ? GV_FP : GV_FM) + (tid & 63)];
+  }
+  asm volatile("" ::: "memory");  // every load above is issued before the first store below
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = tid + kFThreads * i;
+    *reinterpret_cast<u32x4*>(SG + (u >> 4) * P1 + (u & 15) * 8) = rS[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = tid + kFThreads * i;
+    *reinterpret_cast<u32x4*>(ZZ + (u >> 4) * P1 + (u & 15) * 8) = rZ[i];
+    *reinterpret_cast<u32x4*>(MM + (u >> 4) * P1 + (u & 15) * 8) = rM[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int f = tid + kFThreads * i, t = f >> 5;
+    pin(rO[i]);
+    const f32x4 x = t < tlen ? rO[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<half4v*>(DO + t * P1 + (f & 31) * 4) = cvt4(x);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // Vt = w * v (FG2: sqrt(beta) v)
     const int u = tid + kFThreads * i, t = u >> 4, j = (u & 15) * 8;
-    *reinterpret_cast<uint4*>(ZZ + t * P1 + j) = *reinterpret_cast<const uint4*>(Zg + t * D + j);
-    *reinterpret_cast<uint4*>(MM + t * P1 + j) = *reinterpret_cast<const uint4*>(Mg + t * D + j);
-  }
-#pragma unroll
-  for (int i = 0; i < 2048 / kFThreads; ++i) {  // dO, zero past the last token
-    const int f = tid + kFThreads * i, t = f >> 5, j = (f & 31) * 4;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < tlen) x = *reinterpret_cast<const float4*>(g.dO + tok(t) * D + j);
-    *reinterpret_cast<half4v*>(DO + t * P1 + j) = h4(x);
-  }
-#pragma unroll
-  for (int i = 0; i < 1024 / kFThreads; ++i) {  // Vt = w * v (FG2: sqrt(beta) v)
-    const int u = tid + kFThreads * i, t = u >> 4, j = (u & 15) * 8;
-    float vf[8];
-    for (int e = 0; e < 8; ++e) vf[e] = 0.f;
-    if (t < tlen) {
-      const int64_t x = tok(t);
-      bf16x8_to_f32(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) + x * D + j), vf);
-      if (FG2) {
-        for (int e = 0; e < 8; ++e) vf[e] *= sqrtf(p.erase[x * D + j + e]);
-      } else if (p.write_channel) {
-        for (int e = 0; e < 8; ++e) vf[e] *= p.write[x * D + j + e];
-      } else {
-        const float w = p.write[x];
-        for (int e = 0; e < 8; ++e) vf[e] *= w;
+    float vf[8], wf[8];
+    bf16x8_to_f32(make_uint4(rV[i][0], rV[i][1], rV[i][2], rV[i][3]), vf);
+    if (WCH) {
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wf[e] = rW[i][0][e];
+        wf[4 + e] = rW[i][1][e];
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vf[e] *= FG2 ? sqrtf(wf[e]) : wf[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vf[e] *= rw1[i];
+    }
+    if (t >= tlen) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vf[e] = 0.f;
     }
     *reinterpret_cast<half8*>(VV + t * P1 + j) = cvt8(vf);
   }
   if constexpr (!FG2) {
-    const char* pk = ws + pkt * PK::bytes;
-    const char* akk = SYM ? static_cast<const char*>(p.ck_A) + pkt * (6 * 1024) : pk + PK::mat + 2 * PK::matb;
-    for (int u = tid; u < 768; u += kFThreads) {
-      const int m = u / 384, k = (u % 384) / 64, w64 = u % 64, r = w64 >> 2;
-      const int lu = (w64 & 3) ^ ((r >> 2) & 3);
-      const int I = k < 2 ? k : 2 + ((k - 2) >> 1), Hh = k < 2 ? 0 : ((k - 2) & 1);
-      const char* src = m ? pk + PK::mat + PK::matb : akk;
-      *reinterpret_cast<uint4*>((m ? AQ : AK) + (16 * I + r) * P2 + 32 * Hh + 8 * lu) =
-          *reinterpret_cast<const uint4*>(src + 1024 * k + 16 * w64);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + kFThreads * i;
+      pin(rA[i]);
+      if (u < 768) {
+        const int m = u / 384, k = (u % 384) / 64, w64 = u % 64, r = w64 >> 2;
+        const int lu = (w64 & 3) ^ ((r >> 2) & 3);
+        const int I = k < 2 ? k : 2 + ((k - 2) >> 1), Hh = k < 2 ? 0 : ((k - 2) & 1);
+        *reinterpret_cast<u32x4*>((m ? AQ : AK) + (16 * I + r) * P2 + 32 * Hh + 8 * lu) = rA[i];
+      }
     }
     if (tid < 256) {
       const int m = tid >> 7, r = (tid >> 2) & 31, c8 = 32 + 8 * (tid & 3);
       *reinterpret_cast<uint4*>((m ? AQ : AK) + r * P2 + c8) = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 1024 / kFThreads; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const int u = tid + kFThreads * i, t = u >> 4, pos = u & 15;
-      *reinterpret_cast<uint4*>(KE + t * P1 + 8 * (pos ^ swz_key<16>(t))) =
-          *reinterpret_cast<const uint4*>(pk + (SYM ? PK::kp : PK::kmt) + 16 * u);
+      *reinterpret_cast<u32x4*>(KE + t * P1 + 8 * (pos ^ swz_key<16>(t))) = rK[i];
     }
     if constexpr (SCAL) {
-      if (tid < C) {
-        const float* gv = reinterpret_cast<const float*>(pk + PK::gate);
-        FAC[tid] = gv[GV_FP + tid];
-        FAC[C + tid] = gv[GV_FM + tid];
-      }
+      pin(fac);
+      if (tid < 2 * C) FAC[tid] = fac;
     }
   }
-  __syncthreads();
+  };
+  // one gate per head on the symmetric path, FG2's rate per channel: the branch is resolved here;
+  // the general path takes a whole copy of the sequence per kind (no merge between the loads)
+  if constexpr (FG2) phase1_loads(BoolC<true>{});
+  else if constexpr (SYM) phase1_loads(BoolC<false>{});
+  else if (GCH || p.write_channel) phase1_loads(BoolC<true>{});
+  else phase1_loads(BoolC<false>{});
+  lds_barrier();
 
   auto tileNN = [&](const _Float16* A, const _Float16* Bm, int m0, int n0) {
     f32x4 acc = z4;
@@ -241,14 +322,13 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
         acc = mfma16x16x32(fragT(MM, P1, 16 * tn, 32 * ks, lane), frag(AK, P2, 16 * tm, 32 * ks, lane), acc);
       mt[k] = acc;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int n = wave + 8 * k, tm = n >> 3, tn = n & 7;
       *reinterpret_cast<half4v*>(MM + (16 * tm + l16) * P1 + 16 * tn + 4 * lg) = cvt4(mt[k]);
     }
     if constexpr (DCH) {
-      const char* pk = ws + pkt * PK::bytes;
 #pragma unroll
       for (int i = 0; i < 1024 / kFThreads; ++i) {
         const int u = tid + kFThreads * i, t = u >> 4, pos = u & 15;
@@ -256,7 +336,41 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
             *reinterpret_cast<const uint4*>(pk + PK::kmt + 16 * u);
       }
     }
-    __syncthreads();
+    lds_barrier();
+  }
+
+  // ---- the global loads of phases 2 and 3 (G, and the half's k, q, gates and log-decays), issued
+  // here so that they land during the phase-1 products; rows past the last token read the last
+  // token and are zeroed where they are used
+  u32x4 rG[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = tid + kFThreads * i;
+    rG[i] = *reinterpret_cast<const u32x4*>(Gg + (u >> 4) * D + (u & 15) * 8);
+  }
+  const int x3_t = tid >> 3, x3_c8 = (tid & 7) * 8;  // phase 3: 8 channels of token x3_t
+  u32x4 r3k, r3q;
+  f32x4 r3e[2];
+  float r3e1 = 0.f;
+  {
+    const int64_t xt = tok(min(x3_t, tlast));
+    const int64_t x = xt * D + ch0 + x3_c8;
+    r3k = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.k) + x);
+    r3q = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.q) + x);
+    if (ech) {
+      r3e[0] = *reinterpret_cast<const f32x4*>(p.erase + x);
+      r3e[1] = *reinterpret_cast<const f32x4*>(p.erase + x + 4);
+    } else {
+      r3e1 = p.erase[xt];
+    }
+  }
+  const int ld_c = tid & 63, ld_seg = tid >> 6;  // phase 3 (per-channel decay): tokens 8 seg .. + 7 of channel c
+  float r3g[DCH ? 8 : 1];
+  if constexpr (DCH) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r3g[e] = p.log_decay[tok(min(8 * ld_seg + e, tlast)) * D + ch0 + ld_c];
+  } else {
+    r3g[0] = p.log_decay[tok(min(lane, tlast))];
   }
 
   // ---- phase 1: the Gram adjoints (every tile, kept as fp16) and the products with S -----------
@@ -302,7 +416,7 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
     }
     pvt[ct] = acc;
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- phase 2: G; dGamma of the half's channels; the products with G ------------------------
   // dGamma of the half's channels: this thread's 16 S values of row ch0 + tid / 8 go to registers,
@@ -310,13 +424,13 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
   const int dg_d = ch0 + (tid >> 3), dg_j = (tid & 7) * 16;
   const half8 s_a = *reinterpret_cast<const half8*>(SG + dg_d * P1 + dg_j);
   const half8 s_b = *reinterpret_cast<const half8*>(SG + dg_d * P1 + dg_j + 8);
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
-  for (int i = 0; i < 2048 / kFThreads; ++i) {
-    const int u = tid + kFThreads * i, d = u >> 4, j = (u & 15) * 8;
-    *reinterpret_cast<uint4*>(SG + d * P1 + j) = *reinterpret_cast<const uint4*>(Gg + d * D + j);
+  for (int i = 0; i < 4; ++i) {
+    const int u = tid + kFThreads * i;
+    *reinterpret_cast<u32x4*>(SG + (u >> 4) * P1 + (u & 15) * 8) = rG[i];
   }
-  __syncthreads();
+  lds_barrier();
   {
     const half8 g_a = *reinterpret_cast<const half8*>(SG + dg_d * P1 + dg_j);
     const half8 g_b = *reinterpret_cast<const half8*>(SG + dg_d * P1 + dg_j + 8);
@@ -344,7 +458,7 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
       pvt[ct] += kg;
     }
   }
-  __syncthreads();  // every phase-1/2 read of the LDS is done
+  lds_barrier();  // every phase-1/2 read of the LDS is done
 
   // ---- phase 3: dA, g, k, q, u of the half --------------------------------------------------
 #pragma unroll
@@ -355,50 +469,54 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
     *reinterpret_cast<half4v*>(DA + which * C * P2 + (16 * tm + l16) * P2 + 16 * tn + 4 * lg) = dah[k];
   }
   {
-    const int t = tid >> 3, c8 = (tid & 7) * 8;  // 8 channels of token t
+    const bool ok = x3_t < tlen;
+    pin(r3k);
+    pin(r3q);
     float kf[8], qf[8], uf[8];
+    bf16x8_to_f32(make_uint4(r3k[0], r3k[1], r3k[2], r3k[3]), kf);
+    bf16x8_to_f32(make_uint4(r3q[0], r3q[1], r3q[2], r3q[3]), qf);
+    if (ech) {
+      pin(r3e[0]);
+      pin(r3e[1]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) kf[e] = qf[e] = uf[e] = 0.f;
-    if (t < tlen) {
-      const int64_t x = tok(t) * D + ch0 + c8;
-      bf16x8_to_f32(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + x), kf);
-      bf16x8_to_f32(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + x), qf);
-      if (FG2 || p.erase_channel) {
-        float ef[8];
-        unpack8(*reinterpret_cast<const float4*>(p.erase + x), *reinterpret_cast<const float4*>(p.erase + x + 4), ef);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (FG2) kf[e] *= sqrtf(ef[e]);
-          else uf[e] = kf[e] * ef[e];
-        }
-      } else {
-        const float e1 = p.erase[tok(t)];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) uf[e] = kf[e] * e1;
+      for (int e = 0; e < 8; ++e) {
+        const float ef = e < 4 ? r3e[0][e] : r3e[1][e - 4];
+        if (FG2) kf[e] *= sqrtf(ef);
+        else uf[e] = kf[e] * ef;
       }
+    } else {
+      pin(r3e1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) uf[e] = kf[e] * r3e1;
     }
-    *reinterpret_cast<half8*>(XK + t * PX + c8) = cvt8(kf);
-    *reinterpret_cast<half8*>(XQ + t * PX + c8) = cvt8(qf);
-    if constexpr (!FG2) *reinterpret_cast<half8*>(XU + t * PX + c8) = cvt8(uf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kf[e] = ok ? kf[e] : 0.f;
+      qf[e] = ok ? qf[e] : 0.f;
+      uf[e] = ok ? uf[e] : 0.f;
+    }
+    *reinterpret_cast<half8*>(XK + x3_t * PX + x3_c8) = cvt8(kf);
+    *reinterpret_cast<half8*>(XQ + x3_t * PX + x3_c8) = cvt8(qf);
+    if constexpr (!FG2) *reinterpret_cast<half8*>(XU + x3_t * PX + x3_c8) = cvt8(uf);
   }
   if constexpr (DCH) {
-    const int c = tid & 63, seg = tid >> 6;  // tokens 8 seg .. + 7 of channel c of the half
     float gl8[8], acc = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int t = 8 * seg + e;
-      acc += t < tlen ? p.log_decay[tok(t) * D + ch0 + c] : 0.f;
+      pin(r3g[e]);
+      acc += 8 * ld_seg + e < tlen ? r3g[e] : 0.f;
       gl8[e] = acc;
     }
-    TOT[seg * 64 + c] = acc;
-    __syncthreads();
+    TOT[ld_seg * 64 + ld_c] = acc;
+    lds_barrier();
     float base = 0.f;
-    for (int s2 = 0; s2 < seg; ++s2) base += TOT[s2 * 64 + c];
+    for (int s2 = 0; s2 < ld_seg; ++s2) base += TOT[s2 * 64 + ld_c];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) GL[(8 * seg + e) * GSH + c] = (base + gl8[e]) * kLog2e;
+    for (int e = 0; e < 8; ++e) GL[(8 * ld_seg + e) * GSH + ld_c] = (base + gl8[e]) * kLog2e;
   } else {
+    pin(r3g[0]);
     if (wave == 0) {
-      float x = lane < tlen ? p.log_decay[tok(lane)] : 0.f;
+      float x = lane < tlen ? r3g[0] : 0.f;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const float y = __shfl_up(x, o);
@@ -407,7 +525,7 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
       GL[lane] = x * kLog2e;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // c: channel within the half
   auto gl = [&](int t, int c) { return DCH ? GL[t * GSH + c] : GL[t]; };
@@ -431,28 +549,28 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
   constexpr float kSpan = 6.f * kLog2e;
 
   // the chain rule's raw inputs of this lane's channels, issued before the products
-  uint2 vbs[2], kbs[2];
+  // (rows past the last token read token 0 of the chunk; their outputs are not stored)
+  u32x2 vbs[2], kbs[2];
   f32x4 e4s[2], w4s[2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int64_t xo = x_own + ch0 + 32 * pq + 16 * ct + 4 * lg;
-    vbs[ct] = kbs[ct] = make_uint2(0, 0);
-    e4s[ct] = w4s[ct] = f32x4{1.f, 1.f, 1.f, 1.f};
-    if (own_ok) {
-      vbs[ct] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.v) + xo);
-      if (FG2) {
-        kbs[ct] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.k) + xo);
-        e4s[ct] = *reinterpret_cast<const f32x4*>(p.erase + xo);
-      } else {
-        if (p.erase_channel) e4s[ct] = *reinterpret_cast<const f32x4*>(p.erase + xo);
-        else e4s[ct] = f32x4{1.f, 1.f, 1.f, 1.f} * p.erase[x_own / D];
-        if (p.write_channel) w4s[ct] = *reinterpret_cast<const f32x4*>(p.write + xo);
-        else w4s[ct] = f32x4{1.f, 1.f, 1.f, 1.f} * p.write[x_own / D];
-      }
+    kbs[ct] = u32x2{0u, 0u};
+    w4s[ct] = f32x4{1.f, 1.f, 1.f, 1.f};
+    vbs[ct] = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.v) + xo);
+    if (FG2) {
+      kbs[ct] = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.k) + xo);
+      e4s[ct] = *reinterpret_cast<const f32x4*>(p.erase + xo);
+    } else {
+      if (ech) e4s[ct] = *reinterpret_cast<const f32x4*>(p.erase + xo);
+      else e4s[ct] = f32x4{1.f, 1.f, 1.f, 1.f} * p.erase[x_own / D];
+      if (wch) w4s[ct] = *reinterpret_cast<const f32x4*>(p.write + xo);
+      else w4s[ct] = f32x4{1.f, 1.f, 1.f, 1.f} * p.write[x_own / D];
     }
   }
   float s_e = 0.f, s_w = 0.f, s_g = 0.f;
   f32x4 dgv[2], gnv[2];
+
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int c0 = 32 * pq + 16 * ct;  // channel tile within the half
@@ -573,8 +691,18 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
     }
 
     // ---- chain rule, outputs (global channels ch0 + cq ..) -----------------------------------
-    const int64_t xo = x_own + ch0 + cq;
-    const uint2 vb = vbs[ct], kb = kbs[ct];
+    if (ct == 0) {
+      // both tiles' raw inputs in registers before the first output store: a use of a loaded value
+      // after a global store waits for the store as well (one counter serves both)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        pin(vbs[c2]);
+        pin(e4s[c2]);
+        if (FG2) pin(kbs[c2]);
+        if (wch) pin(w4s[c2]);
+      }
+    }
+    const u32x2 vb = own_ok ? vbs[ct] : u32x2{0u, 0u}, kb = kbs[ct];
     const f32x4 e4 = e4s[ct], w4 = w4s[ct];
     float vv[4], kraw[4];
     vv[0] = __uint_as_float(vb.x << 16);
@@ -619,11 +747,12 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
     dgv[ct] = dgt;
     gnv[ct] = gnt;
     if (own_ok) {
+      const int64_t xo = x_own + ch0 + cq;
       *reinterpret_cast<f32x4*>(g.dq + xo) = o_dq;
       *reinterpret_cast<f32x4*>(g.dk + xo) = o_dk;
       *reinterpret_cast<f32x4*>(g.dv + xo) = o_dv;
-      if (FG2 || p.erase_channel) *reinterpret_cast<f32x4*>(g.derase + xo) = o_de;
-      if (!FG2 && !shared_gate && p.write_channel) *reinterpret_cast<f32x4*>(g.dwrite + xo) = o_dw;
+      if (ech) *reinterpret_cast<f32x4*>(g.derase + xo) = o_de;
+      if (!shared_gate && wch) *reinterpret_cast<f32x4*>(g.dwrite + xo) = o_dw;
     }
   }
 
@@ -659,7 +788,7 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
     RED[(1 * 2 + pq) * 64 + t_own] = s_e;
     RED[(2 * 2 + pq) * 64 + t_own] = s_w;
   }
-  __syncthreads();
+  lds_barrier();
   if constexpr (DCH) {
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -685,7 +814,7 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
   }
   // the half's per-token sums (the two channel pairs added in a fixed order)
   if (part) {
-    __syncthreads();
+    lds_barrier();
     float* pp = part + (item * 2 + half) * kPartFloats;
     if (tid < 3 * C) {
       const int which = tid / C, t = tid - which * C;
@@ -749,19 +878,24 @@ hipError_t launch_chunk_grad(const Problem& p, const BwdArgs& g, const void* pac
   const dim3 grid(unsigned((2 * nchunks + 15) / 16 * 16)), block(kFThreads);  // whole groups of 8 x 2
   if (fg2) {
     if (p.decay_channel)
-      hipLaunchKernelGGL((chunk_grad_kernel<kModeFg2, true>), grid, block, 0, stream, p, g, ws, part, nchunks);
+      hipLaunchKernelGGL((chunk_grad_kernel<kModeFg2, true, false>), grid, block, 0, stream, p, g, ws, part, nchunks);
     else
-      hipLaunchKernelGGL((chunk_grad_kernel<kModeFg2, false>), grid, block, 0, stream, p, g, ws, part, nchunks);
+      hipLaunchKernelGGL((chunk_grad_kernel<kModeFg2, false, false>), grid, block, 0, stream, p, g, ws, part, nchunks);
   } else if (p.symmetric) {
     if (p.decay_channel)
-      hipLaunchKernelGGL((chunk_grad_kernel<kModeSym, true>), grid, block, 0, stream, p, g, ws, part, nchunks);
+      hipLaunchKernelGGL((chunk_grad_kernel<kModeSym, true, false>), grid, block, 0, stream, p, g, ws, part, nchunks);
     else
-      hipLaunchKernelGGL((chunk_grad_kernel<kModeSym, false>), grid, block, 0, stream, p, g, ws, part, nchunks);
+      hipLaunchKernelGGL((chunk_grad_kernel<kModeSym, false, false>), grid, block, 0, stream, p, g, ws, part, nchunks);
+  } else if (p.erase_channel && p.write_channel) {
+    if (p.decay_channel)
+      hipLaunchKernelGGL((chunk_grad_kernel<kModeGen, true, true>), grid, block, 0, stream, p, g, ws, part, nchunks);
+    else
+      hipLaunchKernelGGL((chunk_grad_kernel<kModeGen, false, true>), grid, block, 0, stream, p, g, ws, part, nchunks);
   } else {
     if (p.decay_channel)
-      hipLaunchKernelGGL((chunk_grad_kernel<kModeGen, true>), grid, block, 0, stream, p, g, ws, part, nchunks);
+      hipLaunchKernelGGL((chunk_grad_kernel<kModeGen, true, false>), grid, block, 0, stream, p, g, ws, part, nchunks);
     else
-      hipLaunchKernelGGL((chunk_grad_kernel<kModeGen, false>), grid, block, 0, stream, p, g, ws, part, nchunks);
+      hipLaunchKernelGGL((chunk_grad_kernel<kModeGen, false, false>), grid, block, 0, stream, p, g, ws, part, nchunks);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !part) return e;
