@@ -93,6 +93,32 @@ __device__ __forceinline__ void pin(T& x) {
   asm volatile("" : "+v"(x));
 }
 
+// Sums across lanes on the VALU (DPP and the gfx950 row swaps) rather than through the LDS
+// crossbar.  row_suffix: lane l of each 16-lane row gets the sum of lanes l .. 15 of its row
+// (row shift left: lane l reads lane l + N, zero past the row's end).  cross_row_sum: every lane
+// gets the sum of the four lanes with its position in the four rows (swapping rows 1 <-> 0 and
+// 3 <-> 2 of a value with itself and adding both halves sums a pair of rows; the half-wave swap
+// adds the other pair).
+template <int N>
+__device__ __forceinline__ float row_from_above(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_suffix(float x) {
+  x += row_from_above<1>(x);
+  x += row_from_above<2>(x);
+  x += row_from_above<4>(x);
+  x += row_from_above<8>(x);
+  return x;
+}
+__device__ __forceinline__ float cross_row_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned w = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <bool B>
 struct BoolC {
   static constexpr bool value = B;
@@ -440,8 +466,9 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
       x = fmaf(float(g_a[e]), float(s_a[e]), x);
       x = fmaf(float(g_b[e]), float(s_b[e]), x);
     }
-#pragma unroll
-    for (int o = 4; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    x += row_from_above<4>(x);  // lanes 8 j .. 8 j + 7 summed into lane 8 j
+    x += row_from_above<2>(x);
+    x += row_from_above<1>(x);
     if ((lane & 7) == 0) DGAM[tid >> 3] = x;
   }
 #pragma unroll
@@ -761,28 +788,18 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
   for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float v = dgv[ct][e];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float y = __shfl_down(v, o, 16);
-        if (l16 + o < 16) v += y;
-      }
+      const float v = row_suffix(dgv[ct][e]);
       dgv[ct][e] = v;
-      float n = gnv[ct][e];
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) n += __shfl_xor(n, o);
+      const float n = row_suffix(gnv[ct][e]);  // lane 0 of the row: the block's sum
       const int c = 32 * pq + 16 * ct + 4 * lg + e;
       if (l16 == 0) {
         BT[blk * 64 + c] = v;
         GNS[blk * 64 + c] = n;
       }
     }
-#pragma unroll
-  for (int o = 16; o <= 32; o <<= 1) {
-    s_e += __shfl_xor(s_e, o);
-    s_w += __shfl_xor(s_w, o);
-    s_g += __shfl_xor(s_g, o);
-  }
+  s_e = cross_row_sum(s_e);
+  s_w = cross_row_sum(s_w);
+  s_g = cross_row_sum(s_g);
   if (lg == 0) {
     RED[(0 * 2 + pq) * 64 + t_own] = s_g;
     RED[(1 * 2 + pq) * 64 + t_own] = s_e;
@@ -808,8 +825,7 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
     // g_C's share summed over the half's channels
     const int c = lane;
     float n = exp2f(gl(C - 1, c)) * DGAM[c] + GNS[c] + GNS[64 + c] + GNS[128 + c] + GNS[192 + c];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o);
+    n = cross_row_sum(row_suffix(n));
     if (lane == 0) MISC[0] = n;
   }
   // the half's per-token sums (the two channel pairs added in a fixed order)
