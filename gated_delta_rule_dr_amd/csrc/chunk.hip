@@ -159,7 +159,13 @@ __device__ __forceinline__ void write_tri_t(char* mat, const _Float16* TH, int t
 // T = (I + A)^{-1} for the strictly lower-triangular fp32 A in AF (row stride AFS), into TH
 // (fp16, zero upper triangle, which the caller has cleared).  Ends with a barrier.
 __device__ __forceinline__ void solve_t(const float* AF, _Float16* TH, int tid) {
-  const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, lg = lane >> 4;
+  // (the lane index through an empty asm: the identity's entries (r == col) and the lane's LDS
+  // addresses are then formed here, in every call, instead of being hoisted out of a caller's
+  // chunk loop as invariants that spill, each reload of which waits for every outstanding
+  // packet store)
+  int lane = tid & 63;
+  asm volatile("" : "+v"(lane));
+  const int wave = tid >> 6, l16 = lane & 15, lg = lane >> 4;
     // Diagonal 16x16 blocks: fp32 forward substitution, one lane per (block, column).
     if (wave == 0) {
       const int bl = lg, col = l16;
@@ -665,7 +671,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_ch_kernel(Problem p, c
         gv[GV_FC + d] = __expf(D0 + D1 + D2 + D3);
         gv[GV_FCM + d] = 1.f;
       } else if (w == 2 && i == 0) {
-        gv[GV_BETA + lane] = GB[lane];
+        int ln = lane;  // (through an empty asm: the address is formed here, not kept in a register)
+        asm volatile("" : "+v"(ln));
+        gv[GV_BETA + ln] = GB[ln];
       }
     }
     for (int i = tid; i < C * CS; i += kThreads) TH[i] = (_Float16)0.f;
