@@ -56,26 +56,53 @@
 namespace dr {
 namespace {
 
-// The same as fp16 into the [dk][dv] matrix at dst (a chunk's checkpoint for the gradients).
+// The 4 x 4 transpose within each quad of lanes: lane b of a quad holds x = row b of a 4 x 4
+// block (x[r] = A[b][r]) and receives column b (A[r][b]).  Two DPP exchanges: the off-diagonal
+// 2 x 2 blocks between lanes 2 apart, then the off-diagonal elements of each 2 x 2 block between
+// neighbouring lanes.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 x) {
+  const int b = threadIdx.x & 3;
+  auto xchg = [](float v, int ctrl) {  // v of the quad partner that ctrl names
+    return ctrl == 0x4e ? __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4e, 0xf, 0xf, false))
+                        : __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xb1, 0xf, 0xf, false));
+  };
+  const bool hi2 = (b & 2) != 0, odd = (b & 1) != 0;
+  // lanes 0, 1 send elements 2, 3 and take the partner's 0, 1 there; lanes 2, 3 the other way
+  const float s0 = xchg(hi2 ? x[0] : x[2], 0x4e), s1 = xchg(hi2 ? x[1] : x[3], 0x4e);
+  f32x4 y = x;
+  if (hi2) { y[0] = s0; y[1] = s1; } else { y[2] = s0; y[3] = s1; }
+  // even lanes send elements 1, 3 and take the partner's 0, 2 there; odd lanes the other way
+  const float t0 = xchg(odd ? y[0] : y[1], 0xb1), t1 = xchg(odd ? y[2] : y[3], 0xb1);
+  f32x4 z = y;
+  if (odd) { z[0] = t0; z[2] = t1; } else { z[1] = t0; z[3] = t1; }
+  return z;
+}
+
+// The same as fp16 into a chunk's state checkpoint at dst ([dv / 16][dk][16]: 16-column tiles).
+// The lane holds rows 4 lg + 0..3 of column l16 of each 16 x 16 tile; after the quad transpose it
+// holds four consecutive columns of one row and stores them as one 8-byte piece, so that each wave
+// writes 16 whole rows of a tile, 512 contiguous bytes.
 template <int NCT>
 __device__ __forceinline__ void store_state_h(void* dst, int j0, const f32x4 (&S)[NCT]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, lg = lane >> 4;
+  const int b = l16 & 3, a4 = l16 & 12;
   _Float16* d = static_cast<_Float16*>(dst);
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) d[(16 * wave + 4 * lg + r) * D + j0 + 16 * ct + l16] = (_Float16)S[ct][r];
+    *reinterpret_cast<half4v*>(d + ((j0 >> 4) + ct) * (D * 16) + (16 * wave + 4 * lg + b) * 16 + a4) =
+        cvt4(quad_transpose(S[ct]));
 }
 
 // Halves per chunk of the one-gate A_kk side buffer (the six stored 16 x 32 blocks).
 constexpr int64_t kAkkHalves = 6 * 512;
 
-// Rows t0 .. t0 + 3 of column j of a per-chunk fp16 [C][D] matrix (packet index pkt) from an
-// accumulator tile's four values.
+// Rows t0 .. t0 + 3 of column j of a per-chunk fp16 [D / 16][C][16] matrix (packet index pkt)
+// from an accumulator tile's four values (j = j_tile + l16): after the quad transpose the lane
+// stores four consecutive columns of row t0 + l16 % 4 as one 8-byte piece.
 __device__ __forceinline__ void store_rows(void* base, int64_t pkt, int t0, int j, f32x4 x) {
-  _Float16* dst = static_cast<_Float16*>(base) + pkt * C * D + int64_t(t0) * D + j;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) dst[r * D] = (_Float16)x[r];
+  const int b = threadIdx.x & 3, jb = j - b;
+  _Float16* dst = static_cast<_Float16*>(base) + pkt * C * D + (jb >> 4) * (C * 16) + (t0 + b) * 16 + (jb & 15);
+  *reinterpret_cast<half4v*>(dst) = cvt4(quad_transpose(x));
 }
 
 

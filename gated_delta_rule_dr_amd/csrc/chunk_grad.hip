@@ -119,6 +119,11 @@ __device__ __forceinline__ float cross_row_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Half offsets of element (d, j) of a state checkpoint and of (t, j) of a row checkpoint within a
+// chunk: 16-column tiles, [dv / 16][dk][16] and [dv / 16][C][16] (j % 8 == 0 for a 16-byte piece).
+__device__ __forceinline__ int ck_state_off(int d, int j) { return (j >> 4) * (D * 16) + d * 16 + (j & 15); }
+__device__ __forceinline__ int ck_rows_off(int t, int j) { return (j >> 4) * (C * 16) + t * 16 + (j & 15); }
+
 template <bool B>
 struct BoolC {
   static constexpr bool value = B;
@@ -201,15 +206,15 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
   f32x4 rO[4], rW[2][2];
   float rw1[2] = {0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {  // S
+  for (int i = 0; i < 4; ++i) {  // S (checkpoint layout: 16-column tiles)
     const int u = tid + kFThreads * i;
-    rS[i] = *reinterpret_cast<const u32x4*>(Sg + (u >> 4) * D + (u & 15) * 8);
+    rS[i] = *reinterpret_cast<const u32x4*>(Sg + ck_state_off(u >> 4, (u & 15) * 8));
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {  // Z, M (or delta)
     const int u = tid + kFThreads * i;
-    rZ[i] = *reinterpret_cast<const u32x4*>(Zg + (u >> 4) * D + (u & 15) * 8);
-    rM[i] = *reinterpret_cast<const u32x4*>(Mg + (u >> 4) * D + (u & 15) * 8);
+    rZ[i] = *reinterpret_cast<const u32x4*>(Zg + ck_rows_off(u >> 4, (u & 15) * 8));
+    rM[i] = *reinterpret_cast<const u32x4*>(Mg + ck_rows_off(u >> 4, (u & 15) * 8));
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {  // dO
@@ -372,7 +377,7 @@ __global__ __launch_bounds__(kFThreads) void chunk_grad_kernel(Problem p, BwdArg
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int u = tid + kFThreads * i;
-    rG[i] = *reinterpret_cast<const u32x4*>(Gg + (u >> 4) * D + (u & 15) * 8);
+    rG[i] = *reinterpret_cast<const u32x4*>(Gg + ck_state_off(u >> 4, (u & 15) * 8));
   }
   const int x3_t = tid >> 3, x3_c8 = (tid & 7) * 8;  // phase 3: 8 channels of token x3_t
   u32x4 r3k, r3q;

@@ -37,12 +37,13 @@ struct Problem {
   const int* nchunks_total = nullptr;  // number of entries in `chunks`
   const int* order = nullptr;          // [B] sequences, longest first (scan workgroup order)
   // Gradients through the chunk path: the state at the start of every chunk (forward scans) and
-  // its adjoint at the end of every chunk (adjoint scan), fp16 [packet][dk][dv]; null otherwise.
+  // its adjoint at the end of every chunk (adjoint scan), fp16 [packet][dv / 16][dk][16] (16-column
+  // tiles, each a contiguous 4 KB, so that the scans write whole lines); null otherwise.
   void* ck_S = nullptr;
   void* ck_G = nullptr;
-  // ... and, as fp16 [packet][token][dv], the forward's in-chunk reads M (general gates; with
-  // FG2's rate the symmetric scan's delta instead) and the adjoint scan's Z (the adjoint of
-  // K+ S + A_kk Vt); null otherwise.
+  // ... and, as fp16 [packet][dv / 16][token][16], the forward's in-chunk reads M (general gates;
+  // with one gate or FG2's rate the symmetric scan's delta instead) and the adjoint scan's Z (the
+  // adjoint of K+ S + A_kk Vt); null otherwise.
   void* ck_M = nullptr;
   void* ck_Z = nullptr;
   // ... and with one per-head gate, the prep's A_kk (fp16, the packet's six-block triangular
