@@ -208,6 +208,39 @@ def test_bwd_full_shape_sampled_heads(dr):
         assert max(errs.values()) <= TOL_CHUNK, (b, h, errs)
 
 
+@pytest.mark.parametrize("name, heads", [("kda_channel_bf16_t16k", ((0, 0), (1, 31))),
+                                         ("gdn2_decoupled_bf16_t64k", ((0, 17),))])
+def test_bwd_full_shape_long(dr, name, heads):
+    # the KDA workload (B2 H32 T16384) and the long-context decoupled workload (B1 H32 T65536) at
+    # full size through the chunk path; the oracle follows the sampled heads over the whole sequence
+    from gated_delta_rule_dr_amd.workloads import generate, workload
+
+    wl = workload(name)
+    print(f"bwd full shape {name}", flush=True)
+    inp = generate(wl, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(703)
+    dO = torch.randn((wl.B, wl.T, wl.H, wl.dv), generator=g, device="cuda")
+    dST = torch.randn((wl.B, wl.H, wl.dk, wl.dv), generator=g, device="cuda")
+    out = dr.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"], inp["S0"],
+                       dO=dO, dS_T=dST)
+    torch.cuda.synchronize()
+    for b, h in heads:
+        cut = lambda x: None if x is None else x[b:b + 1, :, h:h + 1].cpu()
+        ref = recurrence_bwd(cut(inp["q"]), cut(inp["k"]), cut(inp["v"]), cut(inp["log_decay"]), cut(inp["erase"]),
+                             cut(inp["write"]), None if inp["S0"] is None else inp["S0"][b:b + 1, h:h + 1].cpu(),
+                             dO=cut(dO), dS_T=dST[b:b + 1, h:h + 1].cpu())
+        errs = {}
+        for key in ("dq", "dk", "dv", "dlog_decay", "derase", "dwrite"):
+            if ref[key] is None:
+                assert out[key] is None
+                continue
+            errs[key] = _err(out[key][b:b + 1, :, h:h + 1], ref[key])
+        errs["dS0"] = _err(out["dS0"][b:b + 1, h:h + 1], ref["dS0"])
+        print(f"bwd full shape {name} (b={b}, h={h}): " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
+              flush=True)
+        assert max(errs.values()) <= TOL_CHUNK, (name, b, h, errs)
+
+
 @pytest.mark.parametrize("variant", ["scalar", "kda", "decoupled", "fg2"])
 @pytest.mark.parametrize("edge", ["no_decay", "no_erase", "full_gates"])
 def test_bwd_chunk_path_edge_gates(dr, variant, edge):
