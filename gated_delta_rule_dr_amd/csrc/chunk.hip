@@ -1617,8 +1617,6 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     const Set X = set_of(Flag<B1>()), Y = set_of(Flag<!B1>());
     const int cn = c + 1 < nchunks ? c + 1 : c;  // chunk whose copies this step issues
     vm_wait<kB2min + kB3 + (kEarly ? kB1b : 0)>();  // batch 1 of this chunk, older stores
-    // (checkpoint stores only make the later partial waits stricter: they wait for these too)
-    if constexpr (CKPT) store_state_h(static_cast<_Float16*>(p.ck_S) + (sq.pkt0 + c) * D * D, j0, S);
     if constexpr (!kStage) {
       if (c > 0 && o_wave) store_out(c - 1, false);
     } else {
@@ -1765,9 +1763,15 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     }
     vm_wait<kB3 + kB1b + kB1a>();  // batch 2 of this chunk
     lds_barrier();
+    // Checkpoint stores go out right after a wait, so that they have the stages up to the next wait
+    // to complete (a partial wait also waits for every store issued before it); S still holds the
+    // chunk's incoming state until the S stage.
+    if constexpr (CKPT) store_state_h(static_cast<_Float16*>(p.ck_S) + (sq.pkt0 + c) * D * D, j0, S);
     fetch2(Y, cn);
 
     // ---- D: delta = T R, stored transposed ---------------------------------------------
+    static_assert(4 * NCT <= kScanWaves, "one delta tile per wave");
+    f32x4 dck;  // this wave's delta tile (wave < 4 NCT), for the checkpoint
 #pragma unroll
     for (int n = wave; n < 4 * NCT; n += kScanWaves) {
       const int i = n & 3, ct = n >> 2;
@@ -1786,9 +1790,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
 #pragma unroll
       for (int r = 0; r < 4; ++r) hv[r] = (_Float16)acc[r];
       *reinterpret_cast<half4v*>(DT + swz<8>(16 * ct + l16, 16 * i + 4 * lg)) = hv;
-      if constexpr (CKPT) {
-        if (p.ck_M) store_rows(p.ck_M, sq.pkt0 + c, 16 * i + 4 * lg, j0 + 16 * ct + l16, acc);
-      }
+      dck = acc;
       if constexpr (SCAL) {
         // K^end^T delta = k^T (Diag(e^{g_C - g}) delta): the state update takes the scaled copy
         const float4 fm = *reinterpret_cast<const float4*>(X.gv + GV_FM + 16 * i + 4 * lg);
@@ -1801,6 +1803,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_sym_kernel(Problem p,
     }
     if constexpr (!SCAL) vm_wait<kB1b + kB1a + kB2min>();  // batch 3 of this chunk
     lds_barrier();
+    if constexpr (CKPT) {  // delta, after the wait (see the state's checkpoint above)
+      if (wave < 4 * NCT) store_rows(p.ck_M, sq.pkt0 + c, 16 * (wave & 3) + 4 * lg, j0 + 16 * (wave >> 2) + l16, dck);
+    }
     fetch3(Y, cn);
     if constexpr (kEarly) fetch1b(X, F, c + 2 < nchunks ? c + 2 : nchunks - 1);  // c + 2 uses set X
 
@@ -1969,7 +1974,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_adjoint_scan_kernel(Proble
     uint4 tl[SCAL ? 4 : 6];  // Q+, K+ (, E) units tid and tid + 512
     uint4 mr[2];             // stored blocks of T and W1: units tid, tid + 512 (< 768)
     float4 gv;               // gate vector floats 4 tid .. (tid < ngate / 4)
-    float dv[VPT];
+    float dv[VPT];           // dO (rows past the last token hold the last token's, masked at use)
+    bool ok;                 // this thread's token lies inside the sequence
   };
   auto load = [&](Pref& P, int c) {
     const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
@@ -1979,19 +1985,21 @@ __global__ __launch_bounds__(kScanThreads) void chunk_adjoint_scan_kernel(Proble
       P.tl[2 + i] = ldb16(pk, PK::kp + 16 * (tid + kScanThreads * i));
       if constexpr (!SCAL) P.tl[4 + i] = ldb16(pk, (GEN ? PK::umt : PK::kmt) + 16 * (tid + kScanThreads * i));
     }
+    // every load unconditional (units past the stored ones repeat the last), so that no load sits
+    // in a branch and each is waited for only where it is used
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int u = tid + kScanThreads * j, m = u / 384, k = (u % 384) / 64;
-      if (u < 768) P.mr[j] = ldb16(pk, PK::mat + (m ? W1 : 0) * PK::matb + 1024 * k + 16 * (u % 64));
+      const int u = min(tid + kScanThreads * j, 767), m = u / 384, k = (u % 384) / 64;
+      P.mr[j] = ldb16(pk, PK::mat + (m ? W1 : 0) * PK::matb + 1024 * k + 16 * (u % 64));
     }
-    if (tid < PK::ngate / 4) P.gv = ldf16(pk, PK::gate + 16 * tid);
-    const bool ok = c * C + vtok < T;
-    const int64_t e = ok ? d_off + c * tstride : d_last;
+    P.gv = ldf16(pk, PK::gate + 16 * min(tid, PK::ngate / 4 - 1));
+    P.ok = c * C + vtok < T;
+    const int64_t e = P.ok ? d_off + c * tstride : d_last;
 #pragma unroll
     for (int i = 0; i < VPT; i += 2) {
       const f32x2 x = *(gptr<const f32x2>)(dOin + e + i);
-      P.dv[i] = ok ? x.x : 0.f;
-      P.dv[i + 1] = ok ? x.y : 0.f;
+      P.dv[i] = x.x;
+      P.dv[i + 1] = x.y;
     }
   };
 
@@ -2000,8 +2008,16 @@ __global__ __launch_bounds__(kScanThreads) void chunk_adjoint_scan_kernel(Proble
   const int zct = NCT == 2 ? wave >> 2 : 0;
   const bool zwave = NCT == 2 || wave < 4;
 
+  // Checkpoint stores go out right after the chunk's one wait for its staged loads (in the L stage),
+  // so that they have the whole chunk to complete before the next one (a wait for a load also waits
+  // for every store issued before it): G at the chunk end (G still holds it until the update), and
+  // the previous step's Z, held in registers until then.
+  f32x4 zpend = {0.f, 0.f, 0.f, 0.f};
+  int zpend_c = -1;
+  auto store_z = [&](int cz) {
+    if (zwave) store_rows(p.ck_Z, sq.pkt0 + cz, zi, j0 + 16 * zct + l16, zpend);
+  };
   auto step = [&](int c, Pref& P) {
-    if (p.ck_G) store_state_h(static_cast<_Float16*>(p.ck_G) + (sq.pkt0 + c) * D * D, j0, G);
     // ---- L: the chunk's packet, dO^T and G~^T into LDS ------------------------------------
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -2018,14 +2034,16 @@ __global__ __launch_bounds__(kScanThreads) void chunk_adjoint_scan_kernel(Proble
     }
     if (tid < PK::ngate / 4) *reinterpret_cast<float4*>(GV + 4 * tid) = P.gv;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) DOT[swz<8>(vcol + i, vtok)] = (_Float16)P.dv[i];
+    for (int i = 0; i < VPT; ++i) DOT[swz<8>(vcol + i, vtok)] = (_Float16)(P.ok ? P.dv[i] : 0.f);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
       *reinterpret_cast<half4v*>(GT + swz<16>(16 * ct + l16, 16 * wave + 4 * lg)) = cvt4(G[ct]);
     lds_barrier();
+    store_state_h(static_cast<_Float16*>(p.ck_G) + (sq.pkt0 + c) * D * D, j0, G);
+    if (zpend_c >= 0) store_z(zpend_c);
     if constexpr (SCAL) {  // Diag(e^{g}) dO^T for Q+^T dO
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) DOG[swz<8>(vcol + i, vtok)] = (_Float16)(P.dv[i] * GV[GV_FP + vtok]);
+      for (int i = 0; i < VPT; ++i) DOG[swz<8>(vcol + i, vtok)] = (_Float16)((P.ok ? P.dv[i] : 0.f) * GV[GV_FP + vtok]);
     }
     const int cn = c > 0 ? c - 1 : 0;
     load(P, cn);
@@ -2066,8 +2084,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_adjoint_scan_kernel(Proble
         hv[r] = (_Float16)(f * z[r]);
       }
       *reinterpret_cast<half4v*>(ZT + swz<8>(16 * zct + l16, zi)) = hv;
-      if (p.ck_Z) store_rows(p.ck_Z, sq.pkt0 + c, zi, j0 + 16 * zct + l16, zu);
+      zpend = zu;
     }
+    zpend_c = c;
     lds_barrier();
     // ---- G <- Diag(e^{g_C}) G + Q+^T dO + K+^T Z (this wave's rows) -------------------------
     {
@@ -2096,6 +2115,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_adjoint_scan_kernel(Proble
   Pref PA;
   load(PA, nchunks - 1);
   for (int c = nchunks - 1; c >= 0; --c) step(c, PA);
+  if (zpend_c >= 0) store_z(zpend_c);
   if (dS0) store_state(dS0 + int64_t(bh) * D * D, j0, G);
 }
 
