@@ -60,7 +60,7 @@ def test_fg2_chunk_path(dr, T, decay_channel):
     assert eo <= TOL_BF16 and eS <= TOL_BF16, (eo, eS)
 
 
-@pytest.mark.parametrize("B,H,T", [(1, 64, 150), (2, 3, 300)])
+@pytest.mark.parametrize("B,H,T", [(4, 64, 70), (2, 64, 66), (1, 64, 150), (2, 3, 300)])
 @pytest.mark.parametrize("decay_channel", [True, False])
 def test_fg2_chunk_path_slice_widths(dr, B, H, T, decay_channel):
     # B*H >= 64 runs 32-column value slices, fewer 16-column ones

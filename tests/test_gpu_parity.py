@@ -93,10 +93,11 @@ def test_chunk_path_bf16_d128(dr, T, variant):
     assert eo <= TOL_BF16 and eS <= TOL_BF16, (eo, eS)
 
 
-@pytest.mark.parametrize("B,H,T", [(1, 64, 100), (2, 64, 70), (2, 3, 300)])
+@pytest.mark.parametrize("B,H,T", [(4, 64, 66), (1, 64, 100), (2, 64, 70), (2, 3, 300)])
 @pytest.mark.parametrize("variant", ["scalar", "kda", "decoupled"])
 def test_chunk_path_slice_widths(dr, B, H, T, variant):
-    # B*H selects the value-slice width of the chunk kernel (64, 32 or 16 columns)
+    # B*H selects the value-slice width of the scans (32 columns from 64 (b, h) pairs, 16
+    # below); 256 pairs fill the compute units twice over
     inp = _case(B, T, H, 128, 128, "bf16", variant, True, 17 + T + H)
     o, S = _run(dr, inp)
     ro, rS = _oracle(inp)
