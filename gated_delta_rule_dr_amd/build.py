@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdr.so")
-SOURCES = ["dr_api.cpp", "recurrent.hip", "decode.hip", "chunk.hip", "varlen.hip", "backward.hip", "chunk_grad.hip"]
+SOURCES = ["dr_api.cpp", "recurrent.hip", "decode.hip", "chunk.hip", "scan_wide.hip", "varlen.hip", "backward.hip", "chunk_grad.hip"]
 ARCH = os.environ.get("DR_OFFLOAD_ARCH", "gfx950")
 
 

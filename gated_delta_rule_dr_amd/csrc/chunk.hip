@@ -56,28 +56,6 @@
 namespace dr {
 namespace {
 
-// The 4 x 4 transpose within each quad of lanes: lane b of a quad holds x = row b of a 4 x 4
-// block (x[r] = A[b][r]) and receives column b (A[r][b]).  Two DPP exchanges: the off-diagonal
-// 2 x 2 blocks between lanes 2 apart, then the off-diagonal elements of each 2 x 2 block between
-// neighbouring lanes.
-__device__ __forceinline__ f32x4 quad_transpose(f32x4 x) {
-  const int b = threadIdx.x & 3;
-  auto xchg = [](float v, int ctrl) {  // v of the quad partner that ctrl names
-    return ctrl == 0x4e ? __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4e, 0xf, 0xf, false))
-                        : __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xb1, 0xf, 0xf, false));
-  };
-  const bool hi2 = (b & 2) != 0, odd = (b & 1) != 0;
-  // lanes 0, 1 send elements 2, 3 and take the partner's 0, 1 there; lanes 2, 3 the other way
-  const float s0 = xchg(hi2 ? x[0] : x[2], 0x4e), s1 = xchg(hi2 ? x[1] : x[3], 0x4e);
-  f32x4 y = x;
-  if (hi2) { y[0] = s0; y[1] = s1; } else { y[2] = s0; y[3] = s1; }
-  // even lanes send elements 1, 3 and take the partner's 0, 2 there; odd lanes the other way
-  const float t0 = xchg(odd ? y[0] : y[1], 0xb1), t1 = xchg(odd ? y[2] : y[3], 0xb1);
-  f32x4 z = y;
-  if (odd) { z[0] = t0; z[2] = t1; } else { z[1] = t0; z[3] = t1; }
-  return z;
-}
-
 // The same as fp16 into a chunk's state checkpoint at dst ([dv / 16][dk][16]: 16-column tiles).
 // The lane holds rows 4 lg + 0..3 of column l16 of each 16 x 16 tile; after the quad transpose it
 // holds four consecutive columns of one row and stores them as one 8-byte piece, so that each wave
@@ -2161,6 +2139,8 @@ hipError_t launch_scan_gen(const Problem& p, const char* ws, hipStream_t stream)
   return hipGetLastError();
 }
 
+int64_t round256(int64_t n) { return (n + 255) / 256 * 256; }
+
 template <bool DCH, bool GEN, bool FG2 = false>
 hipError_t launch_variant(const Problem& p, void* workspace, hipStream_t stream) {
   const int nchunks = (p.T + C - 1) / C;
@@ -2188,6 +2168,12 @@ hipError_t launch_variant(const Problem& p, void* workspace, hipStream_t stream)
   // (each stages its chunk's operand tiles) as wide as that allows.
   const int64_t bh = int64_t(p.B) * p.H;
   if constexpr (GEN) {
+    // a dense batch without checkpoints: the full-width segmented scan (one workgroup per
+    // (b, h, segment) with all value columns), its segment maps after the packets
+    if (!p.chunks && !p.ck_S)
+      return launch_scan_wide(p, ws, reinterpret_cast<float*>(ws + round256(int64_t(p.B) * p.H * nchunks *
+                                                                              Packet<DCH, GEN>::bytes)),
+                              stream);
     return bh >= 64 ? launch_scan_gen<DCH, 32>(p, ws, stream) : launch_scan_gen<DCH, 16>(p, ws, stream);
   } else {
     return bh >= 64 ? launch_scan_sym<DCH, 32, FG2>(p, ws, stream) : launch_scan_sym<DCH, 16, FG2>(p, ws, stream);
@@ -2199,13 +2185,14 @@ int64_t packet_bytes(bool symmetric, bool decay_channel, bool rate_sqrt) {
   return !symmetric ? Packet<true, true>::bytes : decay_channel ? Packet<true, false>::bytes : Packet<false, false>::bytes;
 }
 
-int64_t round256(int64_t n) { return (n + 255) / 256 * 256; }
-
 }  // namespace
 
 size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric, bool decay_channel, bool rate_sqrt) {
   const int64_t nchunks = (int64_t(T) + C - 1) / C;
-  return size_t(int64_t(B) * H * nchunks * packet_bytes(symmetric, decay_channel, rate_sqrt));
+  const int64_t packets = int64_t(B) * H * nchunks * packet_bytes(symmetric, decay_channel, rate_sqrt);
+  // general gates: the full-width scan's segment maps and entering states follow the packets
+  if (!symmetric && !rate_sqrt) return size_t(round256(packets) + int64_t(wide_workspace_bytes(B, T, H)));
+  return size_t(packets);
 }
 
 // Packed sequences: packets of at most varlen_max_chunks chunks per head, then the chunk

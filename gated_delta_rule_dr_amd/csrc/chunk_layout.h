@@ -75,6 +75,28 @@ __device__ __forceinline__ float4 ldf16(gptr<const char> base, int64_t off) {
   return make_float4(x.x, x.y, x.z, x.w);
 }
 
+// The 4 x 4 transpose within each quad of lanes: lane b of a quad holds x = row b of a 4 x 4
+// block (x[r] = A[b][r]) and receives column b (A[r][b]).  Two DPP exchanges: the off-diagonal
+// 2 x 2 blocks between lanes 2 apart, then the off-diagonal elements of each 2 x 2 block between
+// neighbouring lanes.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 x) {
+  const int b = threadIdx.x & 3;
+  auto xchg = [](float v, int ctrl) {  // v of the quad partner that ctrl names
+    return ctrl == 0x4e ? __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4e, 0xf, 0xf, false))
+                        : __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xb1, 0xf, 0xf, false));
+  };
+  const bool hi2 = (b & 2) != 0, odd = (b & 1) != 0;
+  // lanes 0, 1 send elements 2, 3 and take the partner's 0, 1 there; lanes 2, 3 the other way
+  const float s0 = xchg(hi2 ? x[0] : x[2], 0x4e), s1 = xchg(hi2 ? x[1] : x[3], 0x4e);
+  f32x4 y = x;
+  if (hi2) { y[0] = s0; y[1] = s1; } else { y[2] = s0; y[3] = s1; }
+  // even lanes send elements 1, 3 and take the partner's 0, 2 there; odd lanes the other way
+  const float t0 = xchg(odd ? y[0] : y[1], 0xb1), t1 = xchg(odd ? y[2] : y[3], 0xb1);
+  f32x4 z = y;
+  if (odd) { z[0] = t0; z[2] = t1; } else { z[1] = t0; z[3] = t1; }
+  return z;
+}
+
 // ------------------------------------------------------------------------------------------
 // Per-chunk packet in the workspace (byte offsets).  Matrices are fp16 64 x 64 with zero upper
 // triangles, in the order T, A_qk (, A_kk, A_qu for general gates); tiles are fp16; the gate

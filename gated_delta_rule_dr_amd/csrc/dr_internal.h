@@ -73,6 +73,11 @@ hipError_t launch_decode128(const Problem& p, hipStream_t stream);
 // state-independent factors per chunk of every (b, h).
 size_t chunk128_workspace_bytes(int B, int T, int H, bool symmetric, bool decay_channel, bool rate_sqrt);
 hipError_t launch_chunk128(const Problem& p, void* workspace, hipStream_t stream);
+// The full-width segmented scan of separate erase and write gates over a dense batch (after the
+// prep has written the packets at `ws`): `extra` holds wide_workspace_bytes(B, T, H) bytes for
+// the segments' maps and entering states (null when that is 0).
+size_t wide_workspace_bytes(int B, int T, int H);
+hipError_t launch_scan_wide(const Problem& p, const char* ws, float* extra, hipStream_t stream);
 
 // The adjoint scan over the packets that launch_chunk128 left in `workspace` (same problem): the
 // state's adjoint at the end of every chunk into p.ck_G and at the start of the sequence into

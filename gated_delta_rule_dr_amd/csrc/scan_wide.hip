@@ -1,0 +1,508 @@
+// Full-width segmented scan for separate erase and write gates (general gates, a dense batch,
+// bf16 q/k/v, dk = dv = 128, chunk 64).
+//
+// The state-passing scan ([FG²] §2, the WY form of a chunk's rank-1 updates; [L2S] method,
+// architecture and implementation: chunk states rebuilt from boundary states) reads every
+// chunk's packet of state-independent factors (the prep's output).  A scan workgroup that owns
+// a narrow slice of value columns must still stream the whole packet, so a head's packet bytes
+// cross the L2 -> L1 path once per slice.  Here one workgroup owns all 128 value columns of a
+// head (wave w: columns 16 w .. 16 w + 15, all 128 key rows in registers), so each packet
+// crosses that path once.  To keep the compute units busy when there are few heads, the
+// sequence is cut into P segments: the chunk map is affine in the state,
+//     S_out = F S_in + H,
+// so each segment's pair (F, H) is computed from S = I and S = 0 in parallel, a small kernel
+// chains S_in[s + 1] = F[s] S_in[s] + H[s], and every segment then runs from its true S_in.
+//
+// Chunk algebra (general gates, u = e ⊙ k, Vt = w ⊙ v; tiles referenced at the chunk start, see
+// the prep): Y = K+ S + A_kk Vt, M = T Y, O = Q+ S + A_qk Vt − A_qu M,
+// S ← Diag(e^{g_C}) S + K^endᵀ Vt − U^endᵀ M, with every matrix operand in fp16 and every
+// accumulation and the state in fp32 — the same roundings as the sliced scan.
+//
+// Interleaved rows.  A 16 x 16 accumulator tile leaves each lane four consecutive rows of one
+// column; the next product needs eight consecutive contraction rows per lane.  So the state's
+// tiles and the in-chunk token tiles (Y, M, O) order their rows in pairs: tile 2 k + s, lane
+// group g, element i holds row 32 k + 8 g + 4 s + i.  The two tiles of a pair then form the
+// next product's B fragment directly (rows 32 k + 8 g + 0..7), and the packet operands that
+// produce them are read at the matching rows (an A operand's rows are free per lane), so all
+// packet reads stay whole 16-byte fragment reads.
+
+#include "chunk_layout.h"
+#include "dr_device.h"
+#include "dr_internal.h"
+
+namespace dr {
+namespace {
+
+constexpr int kWideThreads = 512;  // eight waves, one per 16 value columns
+
+template <bool B>
+struct WFlag {
+  static constexpr bool value = B;
+};
+
+// LDS of the full-width scan: the packet's tiles and matrices in the packet's own layout (units
+// copy straight across), Vt transposed, and the chunk's end-of-chunk decay factors.
+struct WideLayout {
+  static constexpr int kp = 0;                      // K+     [64][128] half, swizzled
+  static constexpr int qp = kp + C * D * 2;         // Q+
+  static constexpr int kmt = qp + C * D * 2;        // K^end
+  static constexpr int umt = kmt + C * D * 2;       // U^end
+  static constexpr int mat = umt + C * D * 2;       // T, A_qk, A_kk, A_qu: eight 16 x 32 blocks each
+  static constexpr int vt = mat + 4 * C * C * 2;    // Vt^T   [128][64] half, swz<8>
+  static constexpr int fc = vt + D * C * 2;         // e^{g_C} [128] fp32
+  static constexpr int total = fc + D * 4;
+};
+
+// Row held by lane row m of interleaved tile I (see the file comment).
+__device__ __forceinline__ int ilv(int I, int m) { return 32 * (I >> 1) + 8 * (m >> 2) + 4 * (I & 1) + (m & 3); }
+
+// A fragment (16 rows x 32 contraction) of a swizzled [*][128] tile at this lane's own row.
+__device__ __forceinline__ half8 frag_row16(const _Float16* base, int row, int k0, int lane) {
+  return *reinterpret_cast<const half8*>(base + swz<16>(row, k0 + 8 * (lane >> 4)));
+}
+
+// A fragment of a lower-triangular matrix (eight 16 x 32 blocks in LDS, layout tri_in) at this
+// lane's own row, contraction columns 32 H .. + 31.
+__device__ __forceinline__ half8 frag_tri_row(const _Float16* base, int row, int H, int lane) {
+  return *reinterpret_cast<const half8*>(base + (2 * (row >> 4) + H) * 512 + tri_in(row, 8 * (lane >> 4)));
+}
+
+// A fragment of the transpose of a swizzled [64][128] tile, A[row][k = t] = base[t][row], for the
+// rows of interleaved key tile r: lane 16 g + m receives base[t0 + 8 g + 0..7][ilv(r, m)].  The
+// transposing read gives lane 16 g + 4 a + b element b of the 8-byte piece that lane
+// 16 g + a + 4 j supplies (j: the token); each supplier names the piece of channels
+// ilv(r, 4 a) .. + 3.
+__device__ __forceinline__ half8 frag_ts_ilv(const _Float16* base, int r, int t0, int lane) {
+  const int m = lane & 15;
+  const int t = t0 + 8 * (lane >> 4) + (m >> 2);
+  const int d = 32 * (r >> 1) + 8 * (m & 3) + 4 * (r & 1);
+  const half4v lo = ld_tr16(base + swz<16>(t, d));
+  const half4v hi = ld_tr16(base + swz<16>(t + 4, d));
+  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ half8 cat8(half4v a, half4v b) {
+  return half8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__device__ __forceinline__ half4v cvt4n(f32x4 a) {
+  half4v h;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) h[r] = (_Float16)(-a[r]);
+  return h;
+}
+
+__device__ __forceinline__ u32x4 ldu4(gptr<const char> base, int64_t off) { return *(gptr<const u32x4>)(base + off); }
+
+// Stored matrix unit (16 bytes) j of thread tid when only T and A_kk are read: units 0 .. 383
+// (T) and 768 .. 1151 (A_kk) in order; a thread without a second unit repeats its first.
+__device__ __forceinline__ int mat_unit_fh(int tid, int j) {
+  const int idx = j == 0 || tid >= 256 ? tid : tid + kWideThreads;
+  return idx < 384 ? idx : idx + 384;
+}
+
+// This wave's 16 columns of an fp32 [128][128] state, to or from the interleaved accumulator
+// tiles: after the quad transpose each lane holds four consecutive columns of one row, one
+// 16-byte access per tile.
+__device__ __forceinline__ void state_store(float* dst, const f32x4 (&S)[8]) {
+  const int lane = threadIdx.x & 63, jw = 16 * (threadIdx.x >> 6), l16 = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+    *reinterpret_cast<f32x4*>(dst + ilv(r, 4 * lg + (l16 & 3)) * D + jw + (l16 & 12)) = quad_transpose(S[r]);
+}
+__device__ __forceinline__ void state_load(const float* src, f32x4 (&S)[8]) {
+  const int lane = threadIdx.x & 63, jw = 16 * (threadIdx.x >> 6), l16 = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+    S[r] = src ? quad_transpose(*reinterpret_cast<const f32x4*>(src + ilv(r, 4 * lg + (l16 & 3)) * D + jw + (l16 & 12)))
+               : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// The segments of a full-width scan: segment 0 of L0 chunks, then P - 1 segments of L chunks.
+struct WidePlan {
+  int nch, L0, L, P;
+  float* fh;   // [B * H][P][2][128][128] fp32: F then H of every segment
+  float* sin;  // [B * H][P][128][128] fp32: the state entering every segment (index 0 unused)
+};
+
+// One segment [c0, c1) of one (b, h), all 128 value columns.
+//   FH = false: from s_in (null: zero), o for the segment, the final state to s_out (if given);
+//   FH = true: the segment's affine map, F from S = I with no values and H from S = 0, to
+//   f_out and h_out.
+template <bool FH, bool WCH>
+__device__ __forceinline__ void wide_segment(const Problem& p, const char* ws, char* smem, int bh, int c0, int c1,
+                                             const float* s_in, float* s_out, float* f_out, float* h_out) {
+  using PK = Packet<true, true>;  // the general-gate packet (one layout for both decay kinds)
+  _Float16* KP = reinterpret_cast<_Float16*>(smem + WideLayout::kp);
+  _Float16* QP = reinterpret_cast<_Float16*>(smem + WideLayout::qp);
+  _Float16* KMT = reinterpret_cast<_Float16*>(smem + WideLayout::kmt);
+  _Float16* UMT = reinterpret_cast<_Float16*>(smem + WideLayout::umt);
+  _Float16* MAT = reinterpret_cast<_Float16*>(smem + WideLayout::mat);
+  _Float16* TH = MAT;
+  _Float16* AQ = MAT + 4096;
+  _Float16* AKK = MAT + 2 * 4096;
+  _Float16* AQU = MAT + 3 * 4096;
+  _Float16* VT = reinterpret_cast<_Float16*>(smem + WideLayout::vt);
+  float* FC = reinterpret_cast<float*>(smem + WideLayout::fc);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int jw = 16 * wave;
+  const int H = p.H, h = bh % H;
+  const int T = p.T, nch = (T + C - 1) / C;
+  const int64_t tok0 = int64_t(bh / H) * T;
+  const gptr<const char> pbase = opaque_gptr(ws) + int64_t(bh) * nch * PK::bytes;
+  const gptr<const char> vin = opaque_gptr(static_cast<const char*>(p.v));
+  const gptr<const char> wrin = opaque_gptr(reinterpret_cast<const char*>(p.write));
+
+  // State (F with FH) and, with FH, the offset H: interleaved key tiles, see state_store.
+  f32x4 S[8], Hs[8];
+  if constexpr (FH) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        S[r][i] = ilv(r, 4 * lg + i) == jw + l16 ? 1.f : 0.f;
+        Hs[r][i] = 0.f;
+      }
+  } else {
+    state_load(s_in, S);
+  }
+
+  // Staged loads of one chunk: this thread's 16-byte units of the four tiles (K+, Q+, K^end,
+  // U^end: units tid and tid + 512 of each) and of the matrices' stored blocks (units tid,
+  // tid + 512, tid + 1024), the decay factors, and 16 value columns of token tid / 8 with their
+  // write gates.  Tokens past the end load token T - 1 (zeroed where they are used), so every
+  // load is issued unconditionally.
+  struct Stage {
+    u32x4 tl[8];
+    u32x4 mr[FH ? 2 : 3];
+    u32x4 fc;
+    u32x4 v[2];
+    u32x4 w[WCH ? 4 : 1];
+  };
+  auto load = [&](Stage& P, int c) {
+    // (the thread index through an empty asm: offsets are formed here, per chunk, instead of
+    // being hoisted out of the chunk loop as invariants that spill)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int vtok = tid >> 3, vcol = 16 * (tid & 7);
+    const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = 16 * (tid + kWideThreads * i);
+      P.tl[i] = ldu4(pk, PK::kp + u);
+      if constexpr (!FH) P.tl[2 + i] = ldu4(pk, PK::qp + u);
+      P.tl[4 + i] = ldu4(pk, PK::kmt + u);
+      P.tl[6 + i] = ldu4(pk, PK::umt + u);
+    }
+    if constexpr (FH) {
+      // T and A_kk only (stored units 0 .. 383 and 768 .. 1151): threads below 256 take two
+      // units, the others one (their second load repeats the first, unused)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) P.mr[j] = ldu4(pk, PK::mat + 16 * mat_unit_fh(tid, j));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) P.mr[j] = ldu4(pk, PK::mat + 16 * (tid + kWideThreads * j));
+    }
+    P.fc = ldu4(pk, PK::gate + 4 * (GV_FC + 4 * (tid & 31)));
+    const int t = c * C + vtok;
+    const int64_t row = (tok0 + (t < T ? t : T - 1)) * H + h;
+    P.v[0] = ldu4(vin, (row * D + vcol) * 2);
+    P.v[1] = ldu4(vin, (row * D + vcol + 8) * 2);
+    if constexpr (WCH) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) P.w[i] = ldu4(wrin, (row * D + vcol + 4 * i) * 4);
+    } else {
+      P.w[0] = u32x4{*(gptr<const uint32_t>)(wrin + row * 4), 0u, 0u, 0u};
+    }
+  };
+
+  // The staged chunk into LDS: units copy straight across; Vt^T from the values and write gates.
+  auto to_lds = [&](const Stage& P, int c) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int vtok = tid >> 3, vcol = 16 * (tid & 7);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = 8 * (tid + kWideThreads * i);
+      *reinterpret_cast<u32x4*>(KP + u) = P.tl[i];
+      if constexpr (!FH) *reinterpret_cast<u32x4*>(QP + u) = P.tl[2 + i];
+      *reinterpret_cast<u32x4*>(KMT + u) = P.tl[4 + i];
+      *reinterpret_cast<u32x4*>(UMT + u) = P.tl[6 + i];
+    }
+    // stored block k of matrix m (1 KB each, see tri_pos) to LDS block 2 I + H of that matrix
+#pragma unroll
+    for (int j = 0; j < (FH ? 2 : 3); ++j) {
+      const int u = FH ? mat_unit_fh(tid, j) : tid + kWideThreads * j, m = u / 384, k = (u % 384) / 64;
+      const int lb = k < 2 ? 2 * k : k + 2;
+      if (!FH || j == 0 || tid < 256) *reinterpret_cast<u32x4*>(MAT + 4096 * m + 512 * lb + 8 * (u % 64)) = P.mr[j];
+    }
+    if (tid < 32) *reinterpret_cast<u32x4*>(FC + 4 * tid) = P.fc;
+    const bool ok = c * C + vtok < T;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t word = P.v[i >> 3][(i & 7) >> 1];
+      const float vf = __uint_as_float((i & 1) ? (word & 0xffff0000u) : (word << 16));
+      const float wf = WCH ? __uint_as_float(P.w[i >> 2][i & 3]) : __uint_as_float(P.w[0][0]);
+      VT[swz<8>(vcol + i, vtok)] = (_Float16)(ok ? wf * vf : 0.f);
+    }
+  };
+
+  // One chunk from LDS.  TAIL: the chunk extends past the last token (its o rows are masked).
+  auto compute = [&](auto tail, int c) {
+    constexpr bool TAIL = decltype(tail)::value;
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int l16 = lane & 15, lg = lane >> 4;
+    // B fragments: the state (contraction over key channels) and Vt (over tokens)
+    half8 bS[4], bH[4], bV[2];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bS[kk] = cat8(cvt4(S[2 * kk]), cvt4(S[2 * kk + 1]));
+      if constexpr (FH) bH[kk] = cat8(cvt4(Hs[2 * kk]), cvt4(Hs[2 * kk + 1]));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) bV[ks] = frag_s<8>(VT, jw, 32 * ks, lane);
+
+    // Y = K+ S + A_kk Vt (with FH: K+ F, and K+ H + A_kk Vt), token rows interleaved
+    f32x4 Y[4], YH[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      const int tr = ilv(I, l16);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acch = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const half8 a = frag_row16(KP, tr, 32 * kk, lane);
+        acc = mfma16x16x32(a, bS[kk], acc);
+        if constexpr (FH) acch = mfma16x16x32(a, bH[kk], acch);
+      }
+#pragma unroll
+      for (int ks = 0; ks <= (I >> 1); ++ks) {
+        const half8 a = frag_tri_row(AKK, tr, ks, lane);
+        if constexpr (FH) acch = mfma16x16x32(a, bV[ks], acch);
+        else acc = mfma16x16x32(a, bV[ks], acc);
+      }
+      Y[I] = acc;
+      if constexpr (FH) YH[I] = acch;
+    }
+    // M = T Y; its negation as the B fragment of the O and state products
+    half8 bM[2], bMH[2];
+    {
+      const half8 bY[2] = {cat8(cvt4(Y[0]), cvt4(Y[1])), cat8(cvt4(Y[2]), cvt4(Y[3]))};
+      half8 bYH[2];
+      if constexpr (FH) {
+        bYH[0] = cat8(cvt4(YH[0]), cvt4(YH[1]));
+        bYH[1] = cat8(cvt4(YH[2]), cvt4(YH[3]));
+      }
+      f32x4 M[4], MH[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const int tr = ilv(I, l16);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acch = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt <= (I >> 1); ++kt) {
+          const half8 a = frag_tri_row(TH, tr, kt, lane);
+          acc = mfma16x16x32(a, bY[kt], acc);
+          if constexpr (FH) acch = mfma16x16x32(a, bYH[kt], acch);
+        }
+        M[I] = acc;
+        if constexpr (FH) MH[I] = acch;
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        bM[kt] = cat8(cvt4n(M[2 * kt]), cvt4n(M[2 * kt + 1]));
+        if constexpr (FH) bMH[kt] = cat8(cvt4n(MH[2 * kt]), cvt4n(MH[2 * kt + 1]));
+      }
+    }
+
+    // O = Q+ S + A_qk Vt − A_qu M: lane (after the quad transpose) holds four consecutive
+    // columns of one token row
+    if constexpr (!FH) {
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const int tr = ilv(I, l16);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mfma16x16x32(frag_row16(QP, tr, 32 * kk, lane), bS[kk], acc);
+#pragma unroll
+        for (int ks = 0; ks <= (I >> 1); ++ks) {
+          acc = mfma16x16x32(frag_tri_row(AQ, tr, ks, lane), bV[ks], acc);
+          acc = mfma16x16x32(frag_tri_row(AQU, tr, ks, lane), bM[ks], acc);
+        }
+        const int t = c * C + ilv(I, 4 * lg + (l16 & 3));
+        const f32x4 ot = quad_transpose(acc);
+        if (!TAIL || t < T) store_o4(p.o, ((tok0 + t) * H + h) * D + jw + (l16 & 12), ot, p.o_bf16);
+      }
+    }
+
+    // S ← Diag(e^{g_C}) S + K^endᵀ Vt − U^endᵀ M (with FH: F without the values)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acch = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const half8 ak = frag_ts_ilv(KMT, r, 32 * ks, lane);
+        if constexpr (FH) acch = mfma16x16x32(ak, bV[ks], acch);
+        else acc = mfma16x16x32(ak, bV[ks], acc);
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const half8 au = frag_ts_ilv(UMT, r, 32 * kt, lane);
+        acc = mfma16x16x32(au, bM[kt], acc);
+        if constexpr (FH) acch = mfma16x16x32(au, bMH[kt], acch);
+      }
+      const f32x4 f = *reinterpret_cast<const f32x4*>(FC + ilv(r, 4 * lg));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        S[r][i] = fmaf(f[i], S[r][i], acc[i]);
+        if constexpr (FH) Hs[r][i] = fmaf(f[i], Hs[r][i], acch[i]);
+      }
+    }
+  };
+
+  // the upper blocks (0,1) and (1,1) of the four matrices are zero and never copied
+  *reinterpret_cast<u32x4*>(MAT + 4096 * (tid >> 7) + 512 * (1 + 2 * ((tid >> 6) & 1)) + 8 * lane) =
+      u32x4{0u, 0u, 0u, 0u};
+  Stage P;
+  load(P, c0);
+  const bool ragged = (T % C) != 0;
+  for (int c = c0; c < c1; ++c) {
+    to_lds(P, c);
+    lds_barrier();
+    load(P, c + 1 < c1 ? c + 1 : c);  // the next chunk (past the segment: this one again, unused)
+    if (ragged && c == nch - 1) compute(WFlag<true>(), c);
+    else compute(WFlag<false>(), c);
+    lds_barrier();
+  }
+
+  if constexpr (FH) {
+    state_store(f_out, S);
+    state_store(h_out, Hs);
+  } else if (s_out) {
+    state_store(s_out, S);
+  }
+}
+
+// Phase 1 (SECOND = false): workgroup (bh, 0) runs segment 0 from S0 with its outputs; (bh, s),
+// s = 1 .. P - 2, forms segment s's affine map.  Phase 2 (SECOND = true): workgroup (bh, y) runs
+// segment y + 1 from its entering state with its outputs; the last writes S_T.
+template <bool WCH, bool SECOND>
+__global__ __launch_bounds__(kWideThreads) void chunk_scan_wide_kernel(Problem p, const char* __restrict__ ws,
+                                                                       WidePlan wp) {
+  __shared__ __attribute__((aligned(16))) char smem[WideLayout::total];
+  const int bh = blockIdx.x;
+  const int seg = SECOND ? int(blockIdx.y) + 1 : int(blockIdx.y);
+  const int c0 = seg == 0 ? 0 : wp.L0 + (seg - 1) * wp.L;
+  const int c1 = seg == 0 ? wp.L0 : (c0 + wp.L < wp.nch ? c0 + wp.L : wp.nch);
+  const int64_t mat = int64_t(D) * D;
+  float* const sin = wp.sin + int64_t(bh) * wp.P * mat;
+  if (!SECOND && seg > 0) {
+    float* const fh = wp.fh + (int64_t(bh) * wp.P + seg) * 2 * mat;
+    wide_segment<true, WCH>(p, ws, smem, bh, c0, c1, nullptr, nullptr, fh, fh + mat);
+    return;
+  }
+  const float* s_in = seg == 0 ? (p.S0 ? p.S0 + int64_t(bh) * mat : nullptr) : sin + seg * mat;
+  float* s_out = seg == wp.P - 1 ? (p.S_T ? p.S_T + int64_t(bh) * mat : nullptr) : (SECOND ? nullptr : sin + mat);
+  wide_segment<false, WCH>(p, ws, smem, bh, c0, c1, s_in, s_out, nullptr, nullptr);
+}
+
+// S_in[s + 1] = F[s] S_in[s] + H[s] for s = 1 .. P - 2, in fp32: workgroup (bh, js) takes value
+// columns 16 js .. + 15 (the columns do not mix).  Thread: key row tid / 2, eight columns.
+constexpr int kComposeThreads = 256;
+__global__ __launch_bounds__(kComposeThreads) void wide_compose_kernel(WidePlan wp) {
+  __shared__ float sS[D][17];
+  const int tid = threadIdx.x, d = tid >> 1, jh = 8 * (tid & 1);
+  const int j0 = 16 * int(blockIdx.y);
+  const int64_t mat = int64_t(D) * D;
+  float* const sin = wp.sin + int64_t(blockIdx.x) * wp.P * mat;
+  const float* const fh = wp.fh + int64_t(blockIdx.x) * wp.P * 2 * mat;
+  // the state entering segment 1
+#pragma unroll
+  for (int k = 0; k < 8; ++k) sS[d][jh + k] = sin[mat + d * D + j0 + jh + k];
+  __syncthreads();
+  for (int s = 1; s + 1 < wp.P; ++s) {
+    const float* F = fh + s * 2 * mat;
+    const float* Hm = F + mat;
+    float acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = Hm[d * D + j0 + jh + k];
+    for (int e = 0; e < D; e += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(F + d * D + e);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        acc[k] = fmaf(f.x, sS[e][jh + k], acc[k]);
+        acc[k] = fmaf(f.y, sS[e + 1][jh + k], acc[k]);
+        acc[k] = fmaf(f.z, sS[e + 2][jh + k], acc[k]);
+        acc[k] = fmaf(f.w, sS[e + 3][jh + k], acc[k]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      sS[d][jh + k] = acc[k];
+      sin[(s + 1) * mat + d * D + j0 + jh + k] = acc[k];
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+// Segments: enough (b, h, segment) workgroups to fill 256 compute units in each phase, at most
+// eight segments beyond the first and at least two chunks each on average.  Both phases are
+// bound by the bytes each compute unit streams: segment 0 runs its outputs in the first phase
+// (the full packet, the values and the o stores) beside the other segments' maps (no Q+, A_qk,
+// A_qu, no stores), so it is 0.6 times as long as the others, which also run their outputs in
+// the second phase.
+void wide_plan(int64_t bh, int T, int& nch, int& L0, int& L, int& P) {
+  nch = (T + C - 1) / C;
+  int64_t p = bh >= 256 ? 1 : 1 + (256 / bh < 8 ? 256 / bh : 8);
+  if (p > nch / 2) p = nch / 2 > 1 ? nch / 2 : 1;
+  P = int(p);
+  if (P <= 1) {
+    P = 1;
+    L0 = L = nch;
+    return;
+  }
+  // (P - 1) L + L0 = nch with L0 about 0.6 L, L0 >= 1
+  L = int(5 * int64_t(nch) / (5 * p - 2));
+  L0 = nch - (P - 1) * L;
+}
+
+size_t wide_workspace_bytes(int B, int T, int H) {
+  int nch = 0, L0 = 0, L = 0, P = 0;
+  wide_plan(int64_t(B) * H, T, nch, L0, L, P);
+  if (P <= 1) return 0;
+  return size_t(int64_t(B) * H * P * 3 * D * D * 4);
+}
+
+hipError_t launch_scan_wide(const Problem& p, const char* ws, float* extra, hipStream_t stream) {
+  const int64_t bh = int64_t(p.B) * p.H;
+  WidePlan wp{};
+  wide_plan(bh, p.T, wp.nch, wp.L0, wp.L, wp.P);
+  wp.fh = extra;
+  wp.sin = extra ? extra + bh * wp.P * 2 * D * D : nullptr;
+  const bool wch = p.write_channel != 0;
+  const dim3 g1(unsigned(bh), unsigned(wp.P > 1 ? wp.P - 1 : 1));
+  if (wch)
+    hipLaunchKernelGGL((chunk_scan_wide_kernel<true, false>), g1, dim3(kWideThreads), 0, stream, p, ws, wp);
+  else
+    hipLaunchKernelGGL((chunk_scan_wide_kernel<false, false>), g1, dim3(kWideThreads), 0, stream, p, ws, wp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || wp.P == 1) return e;
+  if (wp.P > 2) {
+    hipLaunchKernelGGL(wide_compose_kernel, dim3(unsigned(bh), unsigned(D / 16)), dim3(kComposeThreads), 0, stream,
+                       wp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const dim3 g2(unsigned(bh), unsigned(wp.P - 1));
+  if (wch)
+    hipLaunchKernelGGL((chunk_scan_wide_kernel<true, true>), g2, dim3(kWideThreads), 0, stream, p, ws, wp);
+  else
+    hipLaunchKernelGGL((chunk_scan_wide_kernel<false, true>), g2, dim3(kWideThreads), 0, stream, p, ws, wp);
+  return hipGetLastError();
+}
+
+}  // namespace dr

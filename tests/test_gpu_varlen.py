@@ -111,7 +111,10 @@ def test_varlen_token_path_matches_oracle(dr, variant, dtype, d):
 
 @pytest.mark.parametrize("variant", ["scalar", "kda", "decoupled"])
 def test_varlen_equal_lengths_equal_dense_batch(dr, variant):
-    # the same chunks through the same kernels: bit-identical to the dense [N, L] batch
+    # one per-head gate or a per-channel decay with one gate: the same chunks through the same
+    # kernels, bit-identical to the dense [N, L] batch.  Separate erase and write gates: a dense
+    # batch takes the full-width segmented scan (the same chunk algebra and roundings, products
+    # summed in another order), so both meet the bar against the oracle instead.
     N, L, H = 3, 150, 4
     inp = _packed([L] * N, H, variant, seed=5)
     o, S = _run(dr, inp)
@@ -120,7 +123,14 @@ def test_varlen_equal_lengths_equal_dense_batch(dr, variant):
     od, Sd = dr.chunk_fwd(dense["q"], dense["k"], dense["v"], dense["log_decay"], dense["erase"],
                           dense["write"], inp["S0"].cuda())
     torch.cuda.synchronize()
-    assert torch.equal(o.reshape(od.shape), od) and torch.equal(S, Sd)
+    if variant != "decoupled":
+        assert torch.equal(o.reshape(od.shape), od) and torch.equal(S, Sd)
+        return
+    ro, rS = _oracle(inp)
+    cu = inp["cu_seqlens"].numpy()
+    for x, y in ((o, S), (od.reshape(o.shape), Sd)):
+        eo, eS = _errs_per_sequence(x, y, ro, rS, cu)
+        assert eo <= TOL_BF16 and eS <= TOL_BF16, (eo, eS)
 
 
 def test_varlen_decode_handoff(dr):
