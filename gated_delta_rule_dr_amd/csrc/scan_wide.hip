@@ -39,6 +39,10 @@ template <bool B>
 struct WFlag {
   static constexpr bool value = B;
 };
+template <int N>
+struct WInt {
+  static constexpr int value = N;
+};
 
 // LDS of the full-width scan: the packet's tiles and matrices in the packet's own layout (units
 // copy straight across), Vt transposed, and the chunk's end-of-chunk decay factors.
@@ -48,7 +52,7 @@ struct WideLayout {
   static constexpr int kmt = qp + C * D * 2;        // K^end
   static constexpr int umt = kmt + C * D * 2;       // U^end
   static constexpr int mat = umt + C * D * 2;       // T, A_qk, A_kk, A_qu: eight 16 x 32 blocks each
-  static constexpr int vt = mat + 4 * C * C * 2;    // Vt^T   [128][64] half, swz<8>
+  static constexpr int vt = mat + 4 * C * C * 2;    // Vt     [64][128] half, swizzled
   static constexpr int fc = vt + D * C * 2;         // e^{g_C} [128] fp32
   static constexpr int total = fc + D * 4;
 };
@@ -182,40 +186,47 @@ __device__ __forceinline__ void wide_segment(const Problem& p, const char* ws, c
     u32x4 v[2];
     u32x4 w[WCH ? 4 : 1];
   };
-  auto load = [&](Stage& P, int c) {
+  // The loads of one chunk, in three batches that the chunk's compute stages separate (each
+  // wave then computes while the compute unit's memory path drains the previous batch).
+  auto load = [&](auto batch, Stage& P, int c) {
+    constexpr int BATCH = decltype(batch)::value;
     // (the thread index through an empty asm: offsets are formed here, per chunk, instead of
     // being hoisted out of the chunk loop as invariants that spill)
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int vtok = tid >> 3, vcol = 16 * (tid & 7);
     const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
+    if constexpr (BATCH == 0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int u = 16 * (tid + kWideThreads * i);
-      P.tl[i] = ldu4(pk, PK::kp + u);
-      if constexpr (!FH) P.tl[2 + i] = ldu4(pk, PK::qp + u);
-      P.tl[4 + i] = ldu4(pk, PK::kmt + u);
-      P.tl[6 + i] = ldu4(pk, PK::umt + u);
-    }
-    if constexpr (FH) {
-      // T and A_kk only (stored units 0 .. 383 and 768 .. 1151): threads below 256 take two
-      // units, the others one (their second load repeats the first, unused)
+      for (int i = 0; i < 2; ++i) {
+        const int u = 16 * (tid + kWideThreads * i);
+        P.tl[i] = ldu4(pk, PK::kp + u);
+        if constexpr (!FH) P.tl[2 + i] = ldu4(pk, PK::qp + u);
+        P.tl[4 + i] = ldu4(pk, PK::kmt + u);
+        P.tl[6 + i] = ldu4(pk, PK::umt + u);
+      }
+    } else if constexpr (BATCH == 1) {
+      if constexpr (FH) {
+        // T and A_kk only (stored units 0 .. 383 and 768 .. 1151): threads below 256 take two
+        // units, the others one (their second load repeats the first, unused)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) P.mr[j] = ldu4(pk, PK::mat + 16 * mat_unit_fh(tid, j));
+        for (int j = 0; j < 2; ++j) P.mr[j] = ldu4(pk, PK::mat + 16 * mat_unit_fh(tid, j));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) P.mr[j] = ldu4(pk, PK::mat + 16 * (tid + kWideThreads * j));
+      }
+      P.fc = ldu4(pk, PK::gate + 4 * (GV_FC + 4 * (tid & 31)));
     } else {
+      const int t = c * C + vtok;
+      const int64_t row = (tok0 + (t < T ? t : T - 1)) * H + h;
+      P.v[0] = ldu4(vin, (row * D + vcol) * 2);
+      P.v[1] = ldu4(vin, (row * D + vcol + 8) * 2);
+      if constexpr (WCH) {
 #pragma unroll
-      for (int j = 0; j < 3; ++j) P.mr[j] = ldu4(pk, PK::mat + 16 * (tid + kWideThreads * j));
-    }
-    P.fc = ldu4(pk, PK::gate + 4 * (GV_FC + 4 * (tid & 31)));
-    const int t = c * C + vtok;
-    const int64_t row = (tok0 + (t < T ? t : T - 1)) * H + h;
-    P.v[0] = ldu4(vin, (row * D + vcol) * 2);
-    P.v[1] = ldu4(vin, (row * D + vcol + 8) * 2);
-    if constexpr (WCH) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) P.w[i] = ldu4(wrin, (row * D + vcol + 4 * i) * 4);
-    } else {
-      P.w[0] = u32x4{*(gptr<const uint32_t>)(wrin + row * 4), 0u, 0u, 0u};
+        for (int i = 0; i < 4; ++i) P.w[i] = ldu4(wrin, (row * D + vcol + 4 * i) * 4);
+      } else {
+        P.w[0] = u32x4{*(gptr<const uint32_t>)(wrin + row * 4), 0u, 0u, 0u};
+      }
     }
   };
 
@@ -242,84 +253,72 @@ __device__ __forceinline__ void wide_segment(const Problem& p, const char* ws, c
     if (tid < 32) *reinterpret_cast<u32x4*>(FC + 4 * tid) = P.fc;
     const bool ok = c * C + vtok < T;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t word = P.v[i >> 3][(i & 7) >> 1];
-      const float vf = __uint_as_float((i & 1) ? (word & 0xffff0000u) : (word << 16));
-      const float wf = WCH ? __uint_as_float(P.w[i >> 2][i & 3]) : __uint_as_float(P.w[0][0]);
-      VT[swz<8>(vcol + i, vtok)] = (_Float16)(ok ? wf * vf : 0.f);
+    for (int u = 0; u < 2; ++u) {
+      half8 hv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * u + e;
+        const uint32_t word = P.v[u][e >> 1];
+        const float vf = __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
+        const float wf = WCH ? __uint_as_float(P.w[i >> 2][i & 3]) : __uint_as_float(P.w[0][0]);
+        hv[e] = (_Float16)(ok ? wf * vf : 0.f);
+      }
+      *reinterpret_cast<half8*>(VT + swz<16>(vtok, vcol + 8 * u)) = hv;
     }
   };
 
-  // One chunk from LDS.  TAIL: the chunk extends past the last token (its o rows are masked).
-  auto compute = [&](auto tail, int c) {
-    constexpr bool TAIL = decltype(tail)::value;
+  // One state's chunk from LDS: Y = K+ X (+ A_kk Vt), M = T Y, with OUT the output O = Q+ X +
+  // A_qk Vt − A_qu M, then X ← Diag(e^{g_C}) X (+ K^endᵀ Vt) − U^endᵀ M.  VALS: the values
+  // enter (the state and H; not F).  TAIL: the chunk extends past the last token (its o rows are
+  // masked).
+  auto advance = [&](auto vals, auto out, auto tail, f32x4(&X)[8], int c, auto&& after_y, auto&& after_m) {
+    constexpr bool VALS = decltype(vals)::value, OUT = decltype(out)::value, TAIL = decltype(tail)::value;
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
     const int l16 = lane & 15, lg = lane >> 4;
     // B fragments: the state (contraction over key channels) and Vt (over tokens)
-    half8 bS[4], bH[4], bV[2];
+    half8 bS[4], bV[2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bS[kk] = cat8(cvt4(S[2 * kk]), cvt4(S[2 * kk + 1]));
-      if constexpr (FH) bH[kk] = cat8(cvt4(Hs[2 * kk]), cvt4(Hs[2 * kk + 1]));
+    for (int kk = 0; kk < 4; ++kk) bS[kk] = cat8(cvt4(X[2 * kk]), cvt4(X[2 * kk + 1]));
+    if constexpr (VALS) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) bV[ks] = frag_ts(VT, jw, 32 * ks, lane);
     }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) bV[ks] = frag_s<8>(VT, jw, 32 * ks, lane);
-
-    // Y = K+ S + A_kk Vt (with FH: K+ F, and K+ H + A_kk Vt), token rows interleaved
-    f32x4 Y[4], YH[4];
+    // Y, token rows interleaved
+    f32x4 Y[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       const int tr = ilv(I, l16);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acch = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const half8 a = frag_row16(KP, tr, 32 * kk, lane);
-        acc = mfma16x16x32(a, bS[kk], acc);
-        if constexpr (FH) acch = mfma16x16x32(a, bH[kk], acch);
-      }
+      for (int kk = 0; kk < 4; ++kk) acc = mfma16x16x32(frag_row16(KP, tr, 32 * kk, lane), bS[kk], acc);
+      if constexpr (VALS) {
 #pragma unroll
-      for (int ks = 0; ks <= (I >> 1); ++ks) {
-        const half8 a = frag_tri_row(AKK, tr, ks, lane);
-        if constexpr (FH) acch = mfma16x16x32(a, bV[ks], acch);
-        else acc = mfma16x16x32(a, bV[ks], acc);
+        for (int ks = 0; ks <= (I >> 1); ++ks) acc = mfma16x16x32(frag_tri_row(AKK, tr, ks, lane), bV[ks], acc);
       }
       Y[I] = acc;
-      if constexpr (FH) YH[I] = acch;
     }
+    after_y();
     // M = T Y; its negation as the B fragment of the O and state products
-    half8 bM[2], bMH[2];
+    half8 bM[2];
     {
       const half8 bY[2] = {cat8(cvt4(Y[0]), cvt4(Y[1])), cat8(cvt4(Y[2]), cvt4(Y[3]))};
-      half8 bYH[2];
-      if constexpr (FH) {
-        bYH[0] = cat8(cvt4(YH[0]), cvt4(YH[1]));
-        bYH[1] = cat8(cvt4(YH[2]), cvt4(YH[3]));
-      }
-      f32x4 M[4], MH[4];
+      f32x4 M[4];
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         const int tr = ilv(I, l16);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acch = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kt = 0; kt <= (I >> 1); ++kt) {
-          const half8 a = frag_tri_row(TH, tr, kt, lane);
-          acc = mfma16x16x32(a, bY[kt], acc);
-          if constexpr (FH) acch = mfma16x16x32(a, bYH[kt], acch);
-        }
+        for (int kt = 0; kt <= (I >> 1); ++kt) acc = mfma16x16x32(frag_tri_row(TH, tr, kt, lane), bY[kt], acc);
         M[I] = acc;
-        if constexpr (FH) MH[I] = acch;
       }
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        bM[kt] = cat8(cvt4n(M[2 * kt]), cvt4n(M[2 * kt + 1]));
-        if constexpr (FH) bMH[kt] = cat8(cvt4n(MH[2 * kt]), cvt4n(MH[2 * kt + 1]));
-      }
+      for (int kt = 0; kt < 2; ++kt) bM[kt] = cat8(cvt4n(M[2 * kt]), cvt4n(M[2 * kt + 1]));
     }
-
-    // O = Q+ S + A_qk Vt − A_qu M: lane (after the quad transpose) holds four consecutive
+    after_m();
+    // O = Q+ X + A_qk Vt − A_qu M: lane (after the quad transpose) holds four consecutive
     // columns of one token row
-    if constexpr (!FH) {
+    if constexpr (OUT) {
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         const int tr = ilv(I, l16);
@@ -336,29 +335,34 @@ __device__ __forceinline__ void wide_segment(const Problem& p, const char* ws, c
         if (!TAIL || t < T) store_o4(p.o, ((tok0 + t) * H + h) * D + jw + (l16 & 12), ot, p.o_bf16);
       }
     }
-
-    // S ← Diag(e^{g_C}) S + K^endᵀ Vt − U^endᵀ M (with FH: F without the values)
+    // X ← Diag(e^{g_C}) X + K^endᵀ Vt − U^endᵀ M
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acch = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (VALS) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const half8 ak = frag_ts_ilv(KMT, r, 32 * ks, lane);
-        if constexpr (FH) acch = mfma16x16x32(ak, bV[ks], acch);
-        else acc = mfma16x16x32(ak, bV[ks], acc);
+        for (int ks = 0; ks < 2; ++ks) acc = mfma16x16x32(frag_ts_ilv(KMT, r, 32 * ks, lane), bV[ks], acc);
       }
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const half8 au = frag_ts_ilv(UMT, r, 32 * kt, lane);
-        acc = mfma16x16x32(au, bM[kt], acc);
-        if constexpr (FH) acch = mfma16x16x32(au, bMH[kt], acch);
-      }
+      for (int kt = 0; kt < 2; ++kt) acc = mfma16x16x32(frag_ts_ilv(UMT, r, 32 * kt, lane), bM[kt], acc);
       const f32x4 f = *reinterpret_cast<const f32x4*>(FC + ilv(r, 4 * lg));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        S[r][i] = fmaf(f[i], S[r][i], acc[i]);
-        if constexpr (FH) Hs[r][i] = fmaf(f[i], Hs[r][i], acch[i]);
-      }
+      for (int i = 0; i < 4; ++i) X[r][i] = fmaf(f[i], X[r][i], acc[i]);
+    }
+  };
+  // One chunk; the next chunk's second and third load batches are issued after its first
+  // products.
+  auto compute = [&](auto tail, int c, Stage& P, int cn) {
+    auto b1 = [&] { load(WInt<1>(), P, cn); };
+    auto b2 = [&] { load(WInt<2>(), P, cn); };
+    auto none = [] {};
+    if constexpr (FH) {
+      // F, then H: one state's working set at a time
+      advance(WFlag<false>(), WFlag<false>(), tail, S, c, b1, b2);
+      __builtin_amdgcn_sched_barrier(0);
+      advance(WFlag<true>(), WFlag<false>(), tail, Hs, c, none, none);
+    } else {
+      advance(WFlag<true>(), WFlag<true>(), tail, S, c, b1, b2);
     }
   };
 
@@ -366,14 +370,17 @@ __device__ __forceinline__ void wide_segment(const Problem& p, const char* ws, c
   *reinterpret_cast<u32x4*>(MAT + 4096 * (tid >> 7) + 512 * (1 + 2 * ((tid >> 6) & 1)) + 8 * lane) =
       u32x4{0u, 0u, 0u, 0u};
   Stage P;
-  load(P, c0);
+  load(WInt<0>(), P, c0);
+  load(WInt<1>(), P, c0);
+  load(WInt<2>(), P, c0);
   const bool ragged = (T % C) != 0;
   for (int c = c0; c < c1; ++c) {
     to_lds(P, c);
     lds_barrier();
-    load(P, c + 1 < c1 ? c + 1 : c);  // the next chunk (past the segment: this one again, unused)
-    if (ragged && c == nch - 1) compute(WFlag<true>(), c);
-    else compute(WFlag<false>(), c);
+    const int cn = c + 1 < c1 ? c + 1 : c;  // the next chunk (past the segment: this one again, unused)
+    load(WInt<0>(), P, cn);
+    if (ragged && c == nch - 1) compute(WFlag<true>(), c, P, cn);
+    else compute(WFlag<false>(), c, P, cn);
     lds_barrier();
   }
 
@@ -409,41 +416,50 @@ __global__ __launch_bounds__(kWideThreads) void chunk_scan_wide_kernel(Problem p
 }
 
 // S_in[s + 1] = F[s] S_in[s] + H[s] for s = 1 .. P - 2, in fp32: workgroup (bh, js) takes value
-// columns 16 js .. + 15 (the columns do not mix).  Thread: key row tid / 2, eight columns.
+// columns 16 js .. + 15 (the columns do not mix).  Thread: key row tid / 2, eight columns; the
+// entering state's rows are read from LDS as 16-byte pieces that all lanes of a column half share.
 constexpr int kComposeThreads = 256;
 __global__ __launch_bounds__(kComposeThreads) void wide_compose_kernel(WidePlan wp) {
-  __shared__ float sS[D][17];
+  __shared__ __attribute__((aligned(16))) float sS[2][D][16];
   const int tid = threadIdx.x, d = tid >> 1, jh = 8 * (tid & 1);
   const int j0 = 16 * int(blockIdx.y);
   const int64_t mat = int64_t(D) * D;
   float* const sin = wp.sin + int64_t(blockIdx.x) * wp.P * mat;
   const float* const fh = wp.fh + int64_t(blockIdx.x) * wp.P * 2 * mat;
   // the state entering segment 1
-#pragma unroll
-  for (int k = 0; k < 8; ++k) sS[d][jh + k] = sin[mat + d * D + j0 + jh + k];
+  *reinterpret_cast<float4*>(&sS[0][d][jh]) = *reinterpret_cast<const float4*>(sin + mat + d * D + j0 + jh);
+  *reinterpret_cast<float4*>(&sS[0][d][jh + 4]) = *reinterpret_cast<const float4*>(sin + mat + d * D + j0 + jh + 4);
   __syncthreads();
   for (int s = 1; s + 1 < wp.P; ++s) {
+    const float(*cur)[16] = sS[(s - 1) & 1];
     const float* F = fh + s * 2 * mat;
     const float* Hm = F + mat;
     float acc[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = Hm[d * D + j0 + jh + k];
+    {
+      const float4 h0 = *reinterpret_cast<const float4*>(Hm + d * D + j0 + jh);
+      const float4 h1 = *reinterpret_cast<const float4*>(Hm + d * D + j0 + jh + 4);
+      acc[0] = h0.x; acc[1] = h0.y; acc[2] = h0.z; acc[3] = h0.w;
+      acc[4] = h1.x; acc[5] = h1.y; acc[6] = h1.z; acc[7] = h1.w;
+    }
     for (int e = 0; e < D; e += 4) {
       const float4 f = *reinterpret_cast<const float4*>(F + d * D + e);
+      const float fe[4] = {f.x, f.y, f.z, f.w};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        acc[k] = fmaf(f.x, sS[e][jh + k], acc[k]);
-        acc[k] = fmaf(f.y, sS[e + 1][jh + k], acc[k]);
-        acc[k] = fmaf(f.z, sS[e + 2][jh + k], acc[k]);
-        acc[k] = fmaf(f.w, sS[e + 3][jh + k], acc[k]);
+      for (int q = 0; q < 4; ++q) {
+        const float4 a = *reinterpret_cast<const float4*>(&cur[e + q][jh]);
+        const float4 b = *reinterpret_cast<const float4*>(&cur[e + q][jh + 4]);
+        acc[0] = fmaf(fe[q], a.x, acc[0]); acc[1] = fmaf(fe[q], a.y, acc[1]);
+        acc[2] = fmaf(fe[q], a.z, acc[2]); acc[3] = fmaf(fe[q], a.w, acc[3]);
+        acc[4] = fmaf(fe[q], b.x, acc[4]); acc[5] = fmaf(fe[q], b.y, acc[5]);
+        acc[6] = fmaf(fe[q], b.z, acc[6]); acc[7] = fmaf(fe[q], b.w, acc[7]);
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      sS[d][jh + k] = acc[k];
-      sin[(s + 1) * mat + d * D + j0 + jh + k] = acc[k];
-    }
+    float* nxt = &sS[s & 1][d][jh];
+    *reinterpret_cast<float4*>(nxt) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4*>(nxt + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    float* out = sin + (s + 1) * mat + d * D + j0 + jh;
+    *reinterpret_cast<float4*>(out) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
     __syncthreads();
   }
 }
@@ -454,8 +470,8 @@ __global__ __launch_bounds__(kComposeThreads) void wide_compose_kernel(WidePlan 
 // eight segments beyond the first and at least two chunks each on average.  Both phases are
 // bound by the bytes each compute unit streams: segment 0 runs its outputs in the first phase
 // (the full packet, the values and the o stores) beside the other segments' maps (no Q+, A_qk,
-// A_qu, no stores), so it is 0.6 times as long as the others, which also run their outputs in
-// the second phase.
+// A_qu, no stores; measured at 0.73 of an output chunk's time), so it is 0.7 times as long as
+// the others, which also run their outputs in the second phase.
 void wide_plan(int64_t bh, int T, int& nch, int& L0, int& L, int& P) {
   nch = (T + C - 1) / C;
   int64_t p = bh >= 256 ? 1 : 1 + (256 / bh < 8 ? 256 / bh : 8);
@@ -466,8 +482,8 @@ void wide_plan(int64_t bh, int T, int& nch, int& L0, int& L, int& P) {
     L0 = L = nch;
     return;
   }
-  // (P - 1) L + L0 = nch with L0 about 0.6 L, L0 >= 1
-  L = int(5 * int64_t(nch) / (5 * p - 2));
+  // (P - 1) L + L0 = nch with L0 about 0.7 L, L0 >= 1
+  L = int(10 * int64_t(nch) / (10 * p - 3));
   L0 = nch - (P - 1) * L;
 }
 
