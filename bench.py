@@ -50,7 +50,8 @@ PREFILL = "gdn2_decoupled_bf16_t64k"
 EXTRA_PREFILL = ("gdn_scalar_bf16_t4k", "kda_channel_bf16_t16k", "fg2_channel_bf16_t16k",
                  "gdn_scalar_bf16_varlen_t16k")
 DECODE = "decode_kda_n256_h32"
-CHUNK_SRC = os.path.join(ROOT, "gated_delta_rule_dr_amd", "csrc", "chunk.hip")
+# the chunk path's kernel sources: a counter record is used only if it was taken on these
+CHUNK_SRC = [os.path.join(ROOT, "gated_delta_rule_dr_amd", "csrc", n) for n in ("chunk.hip", "scan_wide.hip")]
 DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_dr_amd", "csrc", "decode.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -170,9 +171,13 @@ def decode_bytes(wl) -> int:
     return state + io
 
 
-def source_hash(path) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    """First 16 hex digits of the sha256 of the files' bytes, concatenated in order."""
+    h = hashlib.sha256()
+    for path in [paths] if isinstance(paths, str) else paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def counter_traffic(kernel: str, workload: str, src: str):
@@ -394,6 +399,9 @@ def kernel_desc(wl) -> str:
     scan = "chunk_scan_kernel" if general else "chunk_scan_sym_kernel"
     if wl.seq_median:
         return f"dr_chunk_fwd_varlen = varlen_setup_kernel + {prep} + {scan} (one call)"
+    if general:  # a dense batch with separate erase and write gates: the full-width segmented scan
+        return (f"dr_chunk_fwd = {prep} + chunk_scan_wide_kernel (segment maps) + wide_compose_kernel + "
+                "chunk_scan_wide_kernel (segment outputs) (one call)")
     return f"dr_chunk_fwd = {prep} + {scan} (one call)"
 
 

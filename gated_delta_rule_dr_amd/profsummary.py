@@ -4,7 +4,7 @@
     python -m gated_delta_rule_dr_amd.profsummary trace  <kernel_stats.csv> <out.md> "<command>"
     python -m gated_delta_rule_dr_amd.profsummary traffic <fetch_counter_collection.csv> \\
         <write_counter_collection.csv> <copy_ref_mib> <kernel-substring>[;<kernel-substring>...] \\
-        <source-file> <algorithmic-bytes-per-call> <out.json> "<fetch command>" "<write command>"
+        <source-files;...> <algorithmic-bytes-per-call> <out.json> "<fetch command>" "<write command>"
     python -m gated_delta_rule_dr_amd.profsummary mfma <counter_collection.csv> <kernel_stats.csv> \\
         <kernel-substring>[;...] <out.md> "<counter command>" "<trace command>"
 
@@ -96,8 +96,12 @@ def traffic(fetch_csv, write_csv, copy_mib, patterns, source, alg_bytes, out_jso
                             "hbm_write_bytes": w_kib * 1024.0 * w_fac}
         read_b += f_kib * 1024.0 * f_fac
         write_b += w_kib * 1024.0 * w_fac
-    with open(source, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    # the kernel sources the record covers (';'-separated), hashed in order as bench.source_hash does
+    h = hashlib.sha256()
+    for path in source.split(";"):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    sha = h.hexdigest()[:16]
     rec = {
         "kernels": kernels,
         "source": source,
