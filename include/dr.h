@@ -117,7 +117,11 @@ const char* dr_status_str(int status);
  * B * H * ceil(T / 64) * P bytes with P = 46080 (per-head decay, one per-head erase/write gate),
  * 63488 (per-channel decay, one per-head erase/write gate), 62464 (per-head decay,
  * DR_GATE_RATE_SQRT) or 79872 (per-channel decay, DR_GATE_RATE_SQRT; these two add the scaled
- * values v~ as fp16 [64][128]) or 92160 (otherwise); the
+ * values v~ as fp16 [64][128]) or 92160 (otherwise); with separate erase and write gates
+ * that count is rounded up to a multiple of 256 and followed by the segment maps of the
+ * segmented scan: B * H * S * 196608 bytes (fp32 F, H and the entering state per segment), where
+ * S = 1 + min(256 / (B * H), 8) segments, at most half the chunk count, and no maps when S is 1
+ * (B * H >= 256, or fewer than four chunks).  The
  * token-by-token path needs none.  The caller allocates it
  * (any device memory, 16-byte aligned, not overlapping the other arguments) and may reuse it
  * once the call's work has finished. */
@@ -149,11 +153,12 @@ int dr_chunk_fwd(const dr_desc* desc, const void* q, const void* k, const void* 
  * fixed device array inside the library (dr_chunk_fwd_noalloc_max_bytes() = 64 MiB), one per
  * device, allocated when the library's device code is loaded on that device and held until the
  * process ends; the call itself allocates nothing.  A problem whose dr_chunk_fwd_workspace_bytes
- * exceeds it returns DR_E_SCRATCH before any device work (about 700 to 1,450 chunks of 64 tokens
- * across all (b, h), by gate kind: e.g. H = 32 heads of up to 1,400 tokens with separate
- * erase/write gates).  All calls on one device share its array: calls that may overlap in time
- * on one device (different streams, or different host threads without ordering) race and must
- * be serialised by the caller.  Nothing in the array needs clearing between calls (each call
+ * exceeds it returns DR_E_SCRATCH before any device work (by gate kind, about 840 to 1,450
+ * chunks of 64 tokens across all (b, h) with one erase/write gate; with separate erase and write
+ * gates up to 728 chunks when B * H >= 256, and for fewer heads less because of the segment maps:
+ * e.g. H = 32 heads of up to 704 tokens).  All calls on one device share its array: calls
+ * that may overlap in time on one device (different streams, or different host threads without
+ * ordering) race and must be serialised by the caller.  Nothing in the array needs clearing between calls (each call
  * writes every byte it reads).  The first call on a device resolves the array's device
  * address (hipGetSymbolAddress); a failure there returns DR_E_HIP. */
 size_t dr_chunk_fwd_noalloc_max_bytes(void);

@@ -140,6 +140,18 @@ def test_workspace_query_and_errors():
     assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(g2)) == 2 * 4 * 2 * gen
     g3 = _good_desc(write_is_erase=0, decay_kind=_abi.DR_GATE_CHANNEL, erase_kind=_abi.DR_GATE_CHANNEL)
     assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(g3)) == 2 * 4 * 2 * gen
+    # separate erase and write gates: the packets, rounded up to 256 bytes, then the segmented
+    # scan's maps (fp32 F, H and entering state per segment, 3 x 64 KiB) for S segments,
+    # S = 1 + min(256 / (B * H), 8) and at most half the chunks: 2 x 4 heads of 10 chunks -> S = 5;
+    # 1 x 32 heads of 1,024 chunks -> S = 9; 4 x 64 heads -> S = 1 (no maps)
+    maps = 3 * 128 * 128 * 4
+    up = lambda n: (n + 255) // 256 * 256
+    g4 = _good_desc(write_is_erase=0, T=640)
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(g4)) == up(2 * 4 * 10 * gen) + 2 * 4 * 5 * maps
+    g5 = _good_desc(write_is_erase=0, B=1, H=32, T=65536)
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(g5)) == up(32 * 1024 * gen) + 32 * 9 * maps
+    g6 = _good_desc(write_is_erase=0, B=4, H=64, T=640)
+    assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(g6)) == 4 * 64 * 10 * gen
     # token path and empty sequences need none
     assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(chunk=1))) == 0
     assert L.dr_chunk_fwd_workspace_bytes(ctypes.byref(_good_desc(qkv_dtype=_abi.DR_F32))) == 0
