@@ -2168,9 +2168,9 @@ hipError_t launch_variant(const Problem& p, void* workspace, hipStream_t stream)
   // (each stages its chunk's operand tiles) as wide as that allows.
   const int64_t bh = int64_t(p.B) * p.H;
   if constexpr (GEN) {
-    // a dense batch without checkpoints: the full-width segmented scan (one workgroup per
-    // (b, h, segment) with all value columns), its segment maps after the packets
-    if (!p.chunks && !p.ck_S)
+    // a dense batch: the full-width segmented scan (one workgroup per (b, h, segment) with all
+    // value columns), its segment maps after the packets
+    if (!p.chunks)
       return launch_scan_wide(p, ws, reinterpret_cast<float*>(ws + round256(int64_t(p.B) * p.H * nchunks *
                                                                               Packet<DCH, GEN>::bytes)),
                               stream);

@@ -133,7 +133,9 @@ struct WidePlan {
 //   FH = false: from s_in (null: zero), o for the segment, the final state to s_out (if given);
 //   FH = true: the segment's affine map, F from S = I with no values and H from S = 0, to
 //   f_out and h_out.
-template <bool FH, bool WCH>
+// CKPT (with FH = false): also every chunk's incoming state and its M, as fp16 16-column tiles
+// (p.ck_S: [packet][dv / 16][dk][16], p.ck_M: [packet][dv / 16][token][16]), for the gradients.
+template <bool FH, bool WCH, bool CKPT>
 __device__ __forceinline__ void wide_segment(const Problem& p, const char* ws, char* smem, int bh, int c0, int c1,
                                              const float* s_in, float* s_out, float* f_out, float* h_out) {
   using PK = Packet<true, true>;  // the general-gate packet (one layout for both decay kinds)
@@ -276,6 +278,13 @@ __device__ __forceinline__ void wide_segment(const Problem& p, const char* ws, c
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
     const int l16 = lane & 15, lg = lane >> 4;
+    if constexpr (CKPT && OUT) {
+      // the chunk's incoming state: wave w's tile, each lane four consecutive columns of a row
+      _Float16* dst = static_cast<_Float16*>(p.ck_S) + (int64_t(bh) * nch + c) * D * D + jw * D;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        *reinterpret_cast<half4v*>(dst + ilv(r, 4 * lg + (l16 & 3)) * 16 + (l16 & 12)) = cvt4(quad_transpose(X[r]));
+    }
     // B fragments: the state (contraction over key channels) and Vt (over tokens)
     half8 bS[4], bV[2];
 #pragma unroll
@@ -314,6 +323,12 @@ __device__ __forceinline__ void wide_segment(const Problem& p, const char* ws, c
       }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) bM[kt] = cat8(cvt4n(M[2 * kt]), cvt4n(M[2 * kt + 1]));
+      if constexpr (CKPT && OUT) {
+        _Float16* dst = static_cast<_Float16*>(p.ck_M) + (int64_t(bh) * nch + c) * C * D + jw * C;
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+          *reinterpret_cast<half4v*>(dst + ilv(I, 4 * lg + (l16 & 3)) * 16 + (l16 & 12)) = cvt4(quad_transpose(M[I]));
+      }
     }
     after_m();
     // O = Q+ X + A_qk Vt − A_qu M: lane (after the quad transpose) holds four consecutive
@@ -395,7 +410,7 @@ __device__ __forceinline__ void wide_segment(const Problem& p, const char* ws, c
 // Phase 1 (SECOND = false): workgroup (bh, 0) runs segment 0 from S0 with its outputs; (bh, s),
 // s = 1 .. P - 2, forms segment s's affine map.  Phase 2 (SECOND = true): workgroup (bh, y) runs
 // segment y + 1 from its entering state with its outputs; the last writes S_T.
-template <bool WCH, bool SECOND>
+template <bool WCH, bool SECOND, bool CKPT>
 __global__ __launch_bounds__(kWideThreads) void chunk_scan_wide_kernel(Problem p, const char* __restrict__ ws,
                                                                        WidePlan wp) {
   __shared__ __attribute__((aligned(16))) char smem[WideLayout::total];
@@ -407,12 +422,12 @@ __global__ __launch_bounds__(kWideThreads) void chunk_scan_wide_kernel(Problem p
   float* const sin = wp.sin + int64_t(bh) * wp.P * mat;
   if (!SECOND && seg > 0) {
     float* const fh = wp.fh + (int64_t(bh) * wp.P + seg) * 2 * mat;
-    wide_segment<true, WCH>(p, ws, smem, bh, c0, c1, nullptr, nullptr, fh, fh + mat);
+    wide_segment<true, WCH, false>(p, ws, smem, bh, c0, c1, nullptr, nullptr, fh, fh + mat);
     return;
   }
   const float* s_in = seg == 0 ? (p.S0 ? p.S0 + int64_t(bh) * mat : nullptr) : sin + seg * mat;
   float* s_out = seg == wp.P - 1 ? (p.S_T ? p.S_T + int64_t(bh) * mat : nullptr) : (SECOND ? nullptr : sin + mat);
-  wide_segment<false, WCH>(p, ws, smem, bh, c0, c1, s_in, s_out, nullptr, nullptr);
+  wide_segment<false, WCH, CKPT>(p, ws, smem, bh, c0, c1, s_in, s_out, nullptr, nullptr);
 }
 
 // S_in[s + 1] = F[s] S_in[s] + H[s] for s = 1 .. P - 2, in fp32: workgroup (bh, js) takes value
@@ -441,8 +456,13 @@ __global__ __launch_bounds__(kComposeThreads) void wide_compose_kernel(WidePlan 
       acc[0] = h0.x; acc[1] = h0.y; acc[2] = h0.z; acc[3] = h0.w;
       acc[4] = h1.x; acc[5] = h1.y; acc[6] = h1.z; acc[7] = h1.w;
     }
+    // the row's 32 loads are issued together (one wait per step instead of one per load)
+    float4 fr[D / 4];
+#pragma unroll
+    for (int e4 = 0; e4 < D / 4; ++e4) fr[e4] = *reinterpret_cast<const float4*>(F + d * D + 4 * e4);
+#pragma unroll
     for (int e = 0; e < D; e += 4) {
-      const float4 f = *reinterpret_cast<const float4*>(F + d * D + e);
+      const float4 f = fr[e / 4];
       const float fe[4] = {f.x, f.y, f.z, f.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -500,12 +520,18 @@ hipError_t launch_scan_wide(const Problem& p, const char* ws, float* extra, hipS
   wide_plan(bh, p.T, wp.nch, wp.L0, wp.L, wp.P);
   wp.fh = extra;
   wp.sin = extra ? extra + bh * wp.P * 2 * D * D : nullptr;
-  const bool wch = p.write_channel != 0;
-  const dim3 g1(unsigned(bh), unsigned(wp.P > 1 ? wp.P - 1 : 1));
-  if (wch)
-    hipLaunchKernelGGL((chunk_scan_wide_kernel<true, false>), g1, dim3(kWideThreads), 0, stream, p, ws, wp);
-  else
-    hipLaunchKernelGGL((chunk_scan_wide_kernel<false, false>), g1, dim3(kWideThreads), 0, stream, p, ws, wp);
+  const int kind = (p.write_channel ? 1 : 0) + (p.ck_S ? 2 : 0);
+  // phase one or two, by write-gate kind and checkpoints
+  auto launch = [&](auto second, dim3 g) {
+    constexpr bool S2 = decltype(second)::value;
+    switch (kind) {
+      case 0: hipLaunchKernelGGL((chunk_scan_wide_kernel<false, S2, false>), g, dim3(kWideThreads), 0, stream, p, ws, wp); break;
+      case 1: hipLaunchKernelGGL((chunk_scan_wide_kernel<true, S2, false>), g, dim3(kWideThreads), 0, stream, p, ws, wp); break;
+      case 2: hipLaunchKernelGGL((chunk_scan_wide_kernel<false, S2, true>), g, dim3(kWideThreads), 0, stream, p, ws, wp); break;
+      default: hipLaunchKernelGGL((chunk_scan_wide_kernel<true, S2, true>), g, dim3(kWideThreads), 0, stream, p, ws, wp); break;
+    }
+  };
+  launch(WFlag<false>(), dim3(unsigned(bh), unsigned(wp.P > 1 ? wp.P - 1 : 1)));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || wp.P == 1) return e;
   if (wp.P > 2) {
@@ -513,11 +539,7 @@ hipError_t launch_scan_wide(const Problem& p, const char* ws, float* extra, hipS
                        wp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const dim3 g2(unsigned(bh), unsigned(wp.P - 1));
-  if (wch)
-    hipLaunchKernelGGL((chunk_scan_wide_kernel<true, true>), g2, dim3(kWideThreads), 0, stream, p, ws, wp);
-  else
-    hipLaunchKernelGGL((chunk_scan_wide_kernel<false, true>), g2, dim3(kWideThreads), 0, stream, p, ws, wp);
+  launch(WFlag<true>(), dim3(unsigned(bh), unsigned(wp.P - 1)));
   return hipGetLastError();
 }
 
