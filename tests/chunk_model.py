@@ -519,3 +519,63 @@ def chunk_backward(q, k, v, log_decay, erase, write=None, S0=None, dO=None, dS_T
         w_nd = np.asarray(write).ndim
         res["derase"], res["dwrite"] = de, (out["dw"].sum(-1) if w_nd == 1 else out["dw"])
     return res
+
+
+# ------------------------------------------------------------------------------------------
+# Segment-parallel evaluation (the full-width scan's algebra).  The chunk map is affine in the
+# incoming state, S_out = F S_in + H, so a sequence cut into segments of whole chunks can form
+# every segment's (F, H) independently -- F from S = I with no values, H from S = 0 -- chain
+# S_in[s + 1] = F[s] S_in[s] + H[s], and run every segment from its true entering state
+# ("Linearized 2-Simplicial Attention" page, method: states rebuilt from boundary states;
+# "FG2-GDN" page, section 3: the chunked structure that per-channel rates keep).
+# ------------------------------------------------------------------------------------------
+def wide_plan(bh, T, chunk=64):
+    """The library's segment plan for B * H = bh heads of T tokens: (segments, first length,
+    other length) in chunks -- P - 1 = min(256 / bh, 8), at most half the chunks, the first
+    segment 0.7 times as long as the others."""
+    nch = -(-T // chunk)
+    if nch == 0:
+        return 1, 0, 0
+    p = 1 if bh >= 256 else 1 + min(256 // bh, 8)
+    if p > nch // 2:
+        p = nch // 2 if nch // 2 > 1 else 1
+    if p <= 1:
+        return 1, nch, nch
+    L = 10 * nch // (10 * p - 3)
+    return p, nch - (p - 1) * L, L
+
+
+def segmented_forward(q, k, v, log_decay, erase, write=None, S0=None, bounds=None, chunk=64):
+    """chunk_forward of one (b, h) evaluated segment by segment.  bounds: the chunk indices where
+    segments start (first 0).  Returns (o, S_T, F, H) with F, H of every segment but the last."""
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    T, dk = k.shape
+    nch = -(-T // chunk)
+    starts = [b * chunk for b in bounds] + [T]
+    sym = np.asarray(erase).ndim == 1 and write is None
+
+    def part(a, s, e):
+        return None if a is None else np.asarray(a, np.float64)[s:e]
+
+    o = np.zeros((T, v.shape[1]))
+    S_in = np.zeros((dk, v.shape[1])) if S0 is None else np.array(S0, np.float64)
+    Fs, Hs = [], []
+    for i in range(len(starts) - 1):
+        s, e = starts[i], starts[i + 1]
+        args = (part(q, s, e), part(k, s, e))
+        gates = (part(log_decay, s, e), part(erase, s, e))
+        if i < len(starts) - 2:
+            # the segment's map: F from S = I without values, H from S = 0
+            _, F = chunk_forward(*args, np.zeros((e - s, dk)), *gates, None if write is None else
+                                 np.zeros((e - s, dk)), np.eye(dk), chunk, symmetric=sym)
+            _, Hm = chunk_forward(*args, part(v, s, e), *gates, part(write, s, e), None, chunk, symmetric=sym)
+            Fs.append(F)
+            Hs.append(Hm)
+        o[s:e], S_out = chunk_forward(*args, part(v, s, e), *gates, part(write, s, e), S_in, chunk, symmetric=sym)
+        if i < len(starts) - 2:
+            # what the compose step gives the next segment, from the maps alone
+            S_in = Fs[-1] @ S_in + Hs[-1]
+        else:
+            S_in = S_out
+    assert nch == 0 or starts[-2] < T
+    return o, S_in, Fs, Hs

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+from chunk_model import wide_plan
 from metrics import err_S, err_o
 from oracle import recurrence
 
@@ -30,18 +31,6 @@ def dr():
 
     m.abi_version()
     return m
-
-
-def _plan(bh, T):
-    """The segment plan the library uses (segments, first length, other length)."""
-    nch = (T + 63) // 64
-    p = 1 if bh >= 256 else 1 + min(256 // bh, 8)
-    if p > nch // 2:
-        p = nch // 2 if nch // 2 > 1 else 1
-    if p <= 1:
-        return 1, nch, nch
-    L = 10 * nch // (10 * p - 3)
-    return p, nch - (p - 1) * L, L
 
 
 def _inputs(B, T, H, write_per_channel, s0, seed):
@@ -64,7 +53,7 @@ SHAPES = [(1, 130, 2, 1), (1, 300, 1, 2), (1, 64 * 6 + 10, 1, 3), (2, 520, 1, 4)
 @pytest.mark.parametrize("B,T,H,P", SHAPES)
 @pytest.mark.parametrize("write_per_channel", [True, False])
 def test_wide_scan_segment_plans(dr, B, T, H, P, write_per_channel):
-    assert _plan(B * H, T)[0] == P
+    assert wide_plan(B * H, T)[0] == P
     inp = _inputs(B, T, H, write_per_channel, s0=True, seed=T + H + int(write_per_channel))
     d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
     o, S = dr.chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], d["S0"])
