@@ -492,7 +492,7 @@ __global__ __launch_bounds__(kComposeThreads) void wide_compose_kernel(WidePlan 
 // (the full packet, the values and the o stores) beside the other segments' maps (no Q+, A_qk,
 // A_qu, no stores; measured at 0.73 of an output chunk's time), so it is 0.7 times as long as
 // the others, which also run their outputs in the second phase.
-void wide_plan(int64_t bh, int T, int& nch, int& L0, int& L, int& P) {
+static void wide_plan(int64_t bh, int T, int& nch, int& L0, int& L, int& P) {
   nch = (T + C - 1) / C;
   int64_t p = bh >= 256 ? 1 : 1 + (256 / bh < 8 ? 256 / bh : 8);
   if (p > nch / 2) p = nch / 2 > 1 ? nch / 2 : 1;
