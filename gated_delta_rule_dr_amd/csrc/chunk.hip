@@ -2225,6 +2225,14 @@ hipError_t launch_chunk128_varlen(Problem p, const int* cu, void* workspace, hip
 hipError_t launch_chunk128_adjoint(const Problem& p, const void* workspace, const float* dO, const float* dS_T,
                                    float* dS0, hipStream_t stream) {
   const char* ws = static_cast<const char*>(workspace);
+  if (!p.symmetric && !p.rate_sqrt && !p.chunks) {
+    // separate erase and write gates over a dense batch: the full-width segmented adjoint scan,
+    // its segment maps where the forward's were (after the packets)
+    const int64_t nchunks = (int64_t(p.T) + C - 1) / C;
+    float* extra = reinterpret_cast<float*>(const_cast<char*>(ws) +
+                                            round256(int64_t(p.B) * p.H * nchunks * Packet<true, true>::bytes));
+    return launch_adjoint_wide(p, ws, extra, dO, dS_T, dS0, stream);
+  }
   if (p.rate_sqrt)
     return p.decay_channel ? launch_adjoint_scan<true, false, true>(p, ws, dO, dS_T, dS0, stream)
                            : launch_adjoint_scan<false, false, true>(p, ws, dO, dS_T, dS0, stream);

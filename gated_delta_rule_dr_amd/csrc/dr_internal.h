@@ -78,6 +78,10 @@ hipError_t launch_chunk128(const Problem& p, void* workspace, hipStream_t stream
 // the segments' maps and entering states (null when that is 0).
 size_t wide_workspace_bytes(int B, int T, int H);
 hipError_t launch_scan_wide(const Problem& p, const char* ws, float* extra, hipStream_t stream);
+// The same segmentation for the gradients' adjoint scan (general gates, dense batch): G and Z of
+// every chunk into p.ck_G, p.ck_Z, dS0 (when not null), from dO and dS_T (null: zero).
+hipError_t launch_adjoint_wide(const Problem& p, const char* ws, float* extra, const float* dO, const float* dS_T,
+                               float* dS0, hipStream_t stream);
 
 // The adjoint scan over the packets that launch_chunk128 left in `workspace` (same problem): the
 // state's adjoint at the end of every chunk into p.ck_G and at the start of the sequence into

@@ -430,10 +430,294 @@ __global__ __launch_bounds__(kWideThreads) void chunk_scan_wide_kernel(Problem p
   wide_segment<false, WCH, CKPT>(p, ws, smem, bh, c0, c1, s_in, s_out, nullptr, nullptr);
 }
 
-// S_in[s + 1] = F[s] S_in[s] + H[s] for s = 1 .. P - 2, in fp32: workgroup (bh, js) takes value
-// columns 16 js .. + 15 (the columns do not mix).  Thread: key row tid / 2, eight columns; the
-// entering state's rows are read from LDS as 16-byte pieces that all lanes of a column half share.
+// ------------------------------------------------------------------------------------------
+// Full-width segmented adjoint scan (the gradients' reverse scan, general gates, dense batch).
+// Per chunk, in reverse, with G the state's adjoint at the chunk's end ([L2S] method: the backward
+// is a second scan; [FG²] §2: the WY form of the chunk):
+//   X1 = A_quᵀ dO + U^end G,   Z = −Tᵀ X1,   G ← Diag(e^{g_C}) G + Q⁺ᵀ dO + K⁺ᵀ Z,
+// every product on fp16 operands (X1 rounded to fp16 before its product, as in the sliced adjoint
+// scan), storing G (before its update) and Z of every chunk for the gradient kernels.  G is affine
+// in its value at the segment's end, so segments split as in the forward: the last segment runs
+// from dS_T with its stores in the first pass beside the middle segments' maps (F from G = I
+// without dO, H from G = 0), the compose kernel chains them backwards, and the second pass runs
+// segments 0 .. P - 2 from their true end adjoint; segment 0 ends with dS0.
+// ------------------------------------------------------------------------------------------
+struct AdjLayout {
+  static constexpr int qp = 0;                      // Q+     [64][128] half, swizzled
+  static constexpr int kp = qp + C * D * 2;         // K+
+  static constexpr int umt = kp + C * D * 2;        // U^end
+  static constexpr int mat = umt + C * D * 2;       // T, A_qu: eight 16 x 32 blocks each
+  static constexpr int dop = mat + 2 * C * C * 2;   // dO     [64][128] half, swizzled
+  static constexpr int fc = dop + C * D * 2;        // e^{g_C} [128] fp32
+  static constexpr int total = fc + D * 4;
+};
+
+// A fragment of the transpose of a lower-triangular matrix (eight 16 x 32 blocks in LDS, layout
+// tri_in) at the rows of interleaved token tile I: lane 16 g + m receives
+// base[r0 + 8 g + 0..7][ilv(I, m)] (each supplier lane names the piece of columns ilv(I, 4 a) .. + 3).
+__device__ __forceinline__ half8 frag_tri_t_ilv(const _Float16* base, int I, int r0, int lane) {
+  const int m = lane & 15;
+  const int r = r0 + 8 * (lane >> 4) + (m >> 2);
+  const int c = 32 * (I >> 1) + 8 * (m & 3) + 4 * (I & 1);
+  const half4v lo = ld_tr16(base + (2 * (r >> 4) + (c >> 5)) * 512 + tri_in(r, c));
+  const half4v hi = ld_tr16(base + (2 * ((r + 4) >> 4) + (c >> 5)) * 512 + tri_in(r + 4, c));
+  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Stored matrix unit (16 bytes) j of thread tid when T and A_qu are read: units 0 .. 383 (T) and
+// 1152 .. 1535 (A_qu) in order; a thread without a second unit repeats its first.
+__device__ __forceinline__ int mat_unit_adj(int tid, int j) {
+  const int idx = j == 0 || tid >= 256 ? tid : tid + kWideThreads;
+  return idx < 384 ? idx : idx + 768;
+}
+
+// One segment [c0, c1) of one (b, h) of the adjoint scan, all 128 value columns, chunks in reverse.
+//   FH = false: from g_in (null: zero), with the checkpoint stores; the adjoint at the segment's
+//   start to g_out (if given);  FH = true: the segment's map (F from G = I without dO, H from
+//   G = 0) to f_out and h_out.
+template <bool FH>
+__device__ __forceinline__ void wide_adjoint_segment(const Problem& p, const char* ws, char* smem, int bh, int c0,
+                                                     int c1, const float* dO, const float* g_in, float* g_out,
+                                                     float* f_out, float* h_out) {
+  using PK = Packet<true, true>;
+  _Float16* QP = reinterpret_cast<_Float16*>(smem + AdjLayout::qp);
+  _Float16* KP = reinterpret_cast<_Float16*>(smem + AdjLayout::kp);
+  _Float16* UMT = reinterpret_cast<_Float16*>(smem + AdjLayout::umt);
+  _Float16* TH = reinterpret_cast<_Float16*>(smem + AdjLayout::mat);
+  _Float16* AQU = TH + 4096;
+  _Float16* DOP = reinterpret_cast<_Float16*>(smem + AdjLayout::dop);
+  float* FC = reinterpret_cast<float*>(smem + AdjLayout::fc);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int jw = 16 * wave;
+  const int H = p.H, h = bh % H;
+  const int T = p.T, nch = (T + C - 1) / C;
+  const int64_t tok0 = int64_t(bh / H) * T;
+  const gptr<const char> pbase = opaque_gptr(ws) + int64_t(bh) * nch * PK::bytes;
+  const gptr<const char> dOin = opaque_gptr(reinterpret_cast<const char*>(dO));
+
+  f32x4 G[8], Hs[8];
+  if constexpr (FH) {
+    const int l16 = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        G[r][i] = ilv(r, 4 * lg + i) == jw + l16 ? 1.f : 0.f;
+        Hs[r][i] = 0.f;
+      }
+  } else {
+    state_load(g_in, G);
+  }
+
+  struct Stage {
+    u32x4 tl[6];  // Q+, K+, U^end units tid and tid + 512
+    u32x4 mr[2];  // stored blocks of T and A_qu (mat_unit_adj)
+    u32x4 fc;
+    u32x4 dv[4];  // dO: 16 columns of token tid / 8
+  };
+  auto load = [&](auto batch, Stage& P, int c) {
+    constexpr int BATCH = decltype(batch)::value;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const gptr<const char> pk = pbase + int64_t(c) * PK::bytes;
+    if constexpr (BATCH == 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int u = 16 * (tid + kWideThreads * i);
+        P.tl[i] = ldu4(pk, PK::qp + u);
+        P.tl[2 + i] = ldu4(pk, PK::kp + u);
+        P.tl[4 + i] = ldu4(pk, PK::umt + u);
+      }
+    } else if constexpr (BATCH == 1) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) P.mr[j] = ldu4(pk, PK::mat + 16 * mat_unit_adj(tid, j));
+      P.fc = ldu4(pk, PK::gate + 4 * (GV_FC + 4 * (tid & 31)));
+    } else {
+      const int vtok = tid >> 3, vcol = 16 * (tid & 7);
+      const int t = c * C + vtok;
+      const int64_t row = (tok0 + (t < T ? t : T - 1)) * H + h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) P.dv[i] = ldu4(dOin, (row * D + vcol + 4 * i) * 4);
+    }
+  };
+  auto to_lds = [&](const Stage& P, int c) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int vtok = tid >> 3, vcol = 16 * (tid & 7);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = 8 * (tid + kWideThreads * i);
+      *reinterpret_cast<u32x4*>(QP + u) = P.tl[i];
+      *reinterpret_cast<u32x4*>(KP + u) = P.tl[2 + i];
+      *reinterpret_cast<u32x4*>(UMT + u) = P.tl[4 + i];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int u = mat_unit_adj(tid, j), m = u / 384, k = (u % 384) / 64;
+      const int lb = k < 2 ? 2 * k : k + 2;
+      if (j == 0 || tid < 256) *reinterpret_cast<u32x4*>(TH + 4096 * (m ? 1 : 0) + 512 * lb + 8 * (u % 64)) = P.mr[j];
+    }
+    if (tid < 32) *reinterpret_cast<u32x4*>(FC + 4 * tid) = P.fc;
+    const bool ok = c * C + vtok < T;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      half8 hv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = (_Float16)(ok ? __uint_as_float(P.dv[2 * u + (e >> 2)][e & 3]) : 0.f);
+      *reinterpret_cast<half8*>(DOP + swz<16>(vtok, vcol + 8 * u)) = hv;
+    }
+  };
+
+  // One state's chunk: X1, Z, the update.  VALS: dO enters (the adjoint and H; not F).  OUT: the
+  // checkpoint stores (G before its update, Z).
+  auto advance = [&](auto vals, auto out, f32x4(&X)[8], int c, auto&& after_x, auto&& after_z) {
+    constexpr bool VALS = decltype(vals)::value, OUT = decltype(out)::value;
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int64_t pkt = int64_t(bh) * nch + c;
+    if constexpr (OUT) {
+      _Float16* dst = static_cast<_Float16*>(p.ck_G) + pkt * D * D + jw * D;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        *reinterpret_cast<half4v*>(dst + ilv(r, 4 * lg + (l16 & 3)) * 16 + (l16 & 12)) = cvt4(quad_transpose(X[r]));
+    }
+    half8 bG[4], bD[2];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) bG[kk] = cat8(cvt4(X[2 * kk]), cvt4(X[2 * kk + 1]));
+    if constexpr (VALS) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) bD[ks] = frag_ts(DOP, jw, 32 * ks, lane);
+    }
+    // X1 = A_qu^T dO + U^end G, token rows interleaved (A_qu^T has zero blocks below the diagonal)
+    half8 bX[2];
+    {
+      f32x4 X1[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const int tr = ilv(I, l16);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mfma16x16x32(frag_row16(UMT, tr, 32 * kk, lane), bG[kk], acc);
+        if constexpr (VALS) {
+#pragma unroll
+          for (int ks = I >> 1; ks < 2; ++ks) acc = mfma16x16x32(frag_tri_t_ilv(AQU, I, 32 * ks, lane), bD[ks], acc);
+        }
+        X1[I] = acc;
+      }
+      bX[0] = cat8(cvt4(X1[0]), cvt4(X1[1]));
+      bX[1] = cat8(cvt4(X1[2]), cvt4(X1[3]));
+    }
+    after_x();
+    // Z = -T^T X1
+    half8 bZ[2];
+    {
+      f32x4 Zm[4];  // T^T X1 (Z negated)
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = I >> 1; kt < 2; ++kt) acc = mfma16x16x32(frag_tri_t_ilv(TH, I, 32 * kt, lane), bX[kt], acc);
+        Zm[I] = acc;
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) bZ[kt] = cat8(cvt4n(Zm[2 * kt]), cvt4n(Zm[2 * kt + 1]));
+      if constexpr (OUT) {
+        _Float16* dst = static_cast<_Float16*>(p.ck_Z) + pkt * C * D + jw * C;
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+          *reinterpret_cast<half4v*>(dst + ilv(I, 4 * lg + (l16 & 3)) * 16 + (l16 & 12)) = cvt4n(quad_transpose(Zm[I]));
+      }
+    }
+    after_z();
+    // G <- Diag(e^{g_C}) G + Q+^T dO + K+^T Z
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (VALS) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) acc = mfma16x16x32(frag_ts_ilv(QP, r, 32 * ks, lane), bD[ks], acc);
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) acc = mfma16x16x32(frag_ts_ilv(KP, r, 32 * kt, lane), bZ[kt], acc);
+      const f32x4 fcv = *reinterpret_cast<const f32x4*>(FC + ilv(r, 4 * lg));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X[r][i] = fmaf(fcv[i], X[r][i], acc[i]);
+    }
+  };
+  auto compute = [&](int c, Stage& P, int cn) {
+    auto b1 = [&] { load(WInt<1>(), P, cn); };
+    auto b2 = [&] { load(WInt<2>(), P, cn); };
+    auto none = [] {};
+    if constexpr (FH) {
+      advance(WFlag<false>(), WFlag<false>(), G, c, b1, b2);
+      __builtin_amdgcn_sched_barrier(0);
+      advance(WFlag<true>(), WFlag<false>(), Hs, c, none, none);
+    } else {
+      advance(WFlag<true>(), WFlag<true>(), G, c, b1, b2);
+    }
+  };
+
+  // the upper blocks (0,1) and (1,1) of both matrices are zero and never copied
+  if (tid < 256)
+    *reinterpret_cast<u32x4*>(TH + 4096 * (tid >> 7) + 512 * (1 + 2 * ((tid >> 6) & 1)) + 8 * lane) =
+        u32x4{0u, 0u, 0u, 0u};
+  Stage P;
+  load(WInt<0>(), P, c1 - 1);
+  load(WInt<1>(), P, c1 - 1);
+  load(WInt<2>(), P, c1 - 1);
+  for (int c = c1 - 1; c >= c0; --c) {
+    to_lds(P, c);
+    lds_barrier();
+    const int cn = c > c0 ? c - 1 : c;  // the next chunk back (past the segment: this one, unused)
+    load(WInt<0>(), P, cn);
+    compute(c, P, cn);
+    lds_barrier();
+  }
+  if constexpr (FH) {
+    state_store(f_out, G);
+    state_store(h_out, Hs);
+  } else if (g_out) {
+    state_store(g_out, G);
+  }
+}
+
+// Adjoint segments: 0 .. P - 2 of L chunks, the last (P - 1) of L0.  Pass 1 (SECOND = false):
+// workgroup (bh, 0) runs the last segment from dS_T with its stores; (bh, s), s = 1 .. P - 2, forms
+// segment s's map.  Pass 2: workgroup (bh, s) runs segment s from its end adjoint; segment 0
+// writes dS0.
+template <bool SECOND>
+__global__ __launch_bounds__(kWideThreads) void chunk_adjoint_wide_kernel(Problem p, const char* __restrict__ ws,
+                                                                          WidePlan wp, const float* dO,
+                                                                          const float* dS_T, float* dS0) {
+  __shared__ __attribute__((aligned(16))) char smem[AdjLayout::total];
+  const int bh = blockIdx.x;
+  const int y = int(blockIdx.y);
+  const int64_t mat = int64_t(D) * D;
+  float* const gin = wp.sin + int64_t(bh) * wp.P * mat;
+  float* const ds0 = dS0 ? dS0 + int64_t(bh) * mat : nullptr;
+  if (!SECOND && y > 0) {
+    float* const fh = wp.fh + (int64_t(bh) * wp.P + y) * 2 * mat;
+    wide_adjoint_segment<true>(p, ws, smem, bh, y * wp.L, (y + 1) * wp.L, dO, nullptr, nullptr, fh, fh + mat);
+    return;
+  }
+  const int seg = SECOND ? y : wp.P - 1;
+  const int c0 = seg * wp.L, c1 = seg == wp.P - 1 ? wp.nch : c0 + wp.L;
+  const float* g_in = SECOND ? gin + seg * mat : (dS_T ? dS_T + int64_t(bh) * mat : nullptr);
+  float* g_out = seg == 0 ? ds0 : (SECOND ? nullptr : gin + (wp.P - 2) * mat);
+  wide_adjoint_segment<false>(p, ws, smem, bh, c0, c1, dO, g_in, g_out, nullptr, nullptr);
+}
+
+// The entering states from the segment maps, in fp32.  Forward (REV = false): S_in[s + 1] =
+// F[s] S_in[s] + H[s] for s = 1 .. P - 2, from S_in[1].  Adjoint (REV = true): G_in[s - 1] =
+// F[s] G_in[s] + H[s] for s = P - 2 .. 1, from G_in[P - 2] (G_in[s]: the state's adjoint at the
+// end of segment s).  Workgroup (bh, js) takes value columns 16 js .. + 15 (the columns do not
+// mix).  Thread: key row tid / 2, eight columns; the entering state's rows are read from LDS as
+// 16-byte pieces that all lanes of a column half share.
 constexpr int kComposeThreads = 256;
+template <bool REV>
 __global__ __launch_bounds__(kComposeThreads) void wide_compose_kernel(WidePlan wp) {
   __shared__ __attribute__((aligned(16))) float sS[2][D][16];
   const int tid = threadIdx.x, d = tid >> 1, jh = 8 * (tid & 1);
@@ -441,12 +725,14 @@ __global__ __launch_bounds__(kComposeThreads) void wide_compose_kernel(WidePlan 
   const int64_t mat = int64_t(D) * D;
   float* const sin = wp.sin + int64_t(blockIdx.x) * wp.P * mat;
   const float* const fh = wp.fh + int64_t(blockIdx.x) * wp.P * 2 * mat;
-  // the state entering segment 1
-  *reinterpret_cast<float4*>(&sS[0][d][jh]) = *reinterpret_cast<const float4*>(sin + mat + d * D + j0 + jh);
-  *reinterpret_cast<float4*>(&sS[0][d][jh + 4]) = *reinterpret_cast<const float4*>(sin + mat + d * D + j0 + jh + 4);
+  const int s_first = REV ? wp.P - 2 : 1;
+  *reinterpret_cast<float4*>(&sS[0][d][jh]) = *reinterpret_cast<const float4*>(sin + s_first * mat + d * D + j0 + jh);
+  *reinterpret_cast<float4*>(&sS[0][d][jh + 4]) =
+      *reinterpret_cast<const float4*>(sin + s_first * mat + d * D + j0 + jh + 4);
   __syncthreads();
-  for (int s = 1; s + 1 < wp.P; ++s) {
-    const float(*cur)[16] = sS[(s - 1) & 1];
+  for (int n = 0; n + 2 < wp.P; ++n) {
+    const int s = REV ? wp.P - 2 - n : 1 + n;
+    const float(*cur)[16] = sS[n & 1];
     const float* F = fh + s * 2 * mat;
     const float* Hm = F + mat;
     float acc[8];
@@ -474,10 +760,10 @@ __global__ __launch_bounds__(kComposeThreads) void wide_compose_kernel(WidePlan 
         acc[6] = fmaf(fe[q], b.z, acc[6]); acc[7] = fmaf(fe[q], b.w, acc[7]);
       }
     }
-    float* nxt = &sS[s & 1][d][jh];
+    float* nxt = &sS[(n + 1) & 1][d][jh];
     *reinterpret_cast<float4*>(nxt) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     *reinterpret_cast<float4*>(nxt + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
-    float* out = sin + (s + 1) * mat + d * D + j0 + jh;
+    float* out = sin + (REV ? s - 1 : s + 1) * mat + d * D + j0 + jh;
     *reinterpret_cast<float4*>(out) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
     __syncthreads();
@@ -535,11 +821,32 @@ hipError_t launch_scan_wide(const Problem& p, const char* ws, float* extra, hipS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || wp.P == 1) return e;
   if (wp.P > 2) {
-    hipLaunchKernelGGL(wide_compose_kernel, dim3(unsigned(bh), unsigned(D / 16)), dim3(kComposeThreads), 0, stream,
-                       wp);
+    hipLaunchKernelGGL((wide_compose_kernel<false>), dim3(unsigned(bh), unsigned(D / 16)), dim3(kComposeThreads), 0,
+                       stream, wp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   launch(WFlag<true>(), dim3(unsigned(bh), unsigned(wp.P - 1)));
+  return hipGetLastError();
+}
+
+hipError_t launch_adjoint_wide(const Problem& p, const char* ws, float* extra, const float* dO, const float* dS_T,
+                               float* dS0, hipStream_t stream) {
+  const int64_t bh = int64_t(p.B) * p.H;
+  WidePlan wp{};
+  wide_plan(bh, p.T, wp.nch, wp.L0, wp.L, wp.P);
+  wp.fh = extra;
+  wp.sin = extra ? extra + bh * wp.P * 2 * D * D : nullptr;
+  hipLaunchKernelGGL((chunk_adjoint_wide_kernel<false>), dim3(unsigned(bh), unsigned(wp.P > 1 ? wp.P - 1 : 1)),
+                     dim3(kWideThreads), 0, stream, p, ws, wp, dO, dS_T, dS0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || wp.P == 1) return e;
+  if (wp.P > 2) {
+    hipLaunchKernelGGL((wide_compose_kernel<true>), dim3(unsigned(bh), unsigned(D / 16)), dim3(kComposeThreads), 0,
+                       stream, wp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((chunk_adjoint_wide_kernel<true>), dim3(unsigned(bh), unsigned(wp.P - 1)), dim3(kWideThreads), 0,
+                     stream, p, ws, wp, dO, dS_T, dS0);
   return hipGetLastError();
 }
 

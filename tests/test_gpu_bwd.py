@@ -75,6 +75,20 @@ def test_bwd_variants_d128(dr, T, variant, chunk):
     assert max(errs.values()) <= (TOL_CHUNK if chunk == 64 else TOL), errs
 
 
+@pytest.mark.parametrize("T", [394, 520])
+def test_bwd_segmented_scans(dr, T):
+    # separate erase and write gates over a dense batch: both full-width scans (the forward with
+    # its checkpoints and the adjoint) cut 2 x 2 heads of 7 and 9 chunks into 3 and 4 segments, so
+    # the maps, the compose step in both directions and the entering states all take part
+    from chunk_model import wide_plan
+
+    assert wide_plan(4, T)[0] == (3 if T == 394 else 4)
+    inp, dO, dST = _case(2, T, 2, 128, 128, "bf16", "decoupled", True, 700 + T)
+    errs = _check(dr, inp, dO, dST)
+    print(f"bwd segmented T={T}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert max(errs.values()) <= TOL_CHUNK, errs
+
+
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32)])
 @pytest.mark.parametrize("variant", ["scalar", "decoupled"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
