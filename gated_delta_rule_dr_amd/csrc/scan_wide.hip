@@ -12,6 +12,9 @@
 //     S_out = F S_in + H,
 // so each segment's pair (F, H) is computed from S = I and S = 0 in parallel, a small kernel
 // chains S_in[s + 1] = F[s] S_in[s] + H[s], and every segment then runs from its true S_in.
+// The same file holds the gradients' side of it: the forward with each chunk's incoming state
+// and M stored for the gradient kernels, and the adjoint scan (the state's adjoint carried
+// backwards) segmented the same way.
 //
 // Chunk algebra (general gates, u = e ⊙ k, Vt = w ⊙ v; tiles referenced at the chunk start, see
 // the prep): Y = K+ S + A_kk Vt, M = T Y, O = Q+ S + A_qk Vt − A_qu M,
@@ -45,7 +48,7 @@ struct WInt {
 };
 
 // LDS of the full-width scan: the packet's tiles and matrices in the packet's own layout (units
-// copy straight across), Vt transposed, and the chunk's end-of-chunk decay factors.
+// copy straight across), Vt, and the chunk's end-of-chunk decay factors.
 struct WideLayout {
   static constexpr int kp = 0;                      // K+     [64][128] half, swizzled
   static constexpr int qp = kp + C * D * 2;         // Q+
@@ -126,7 +129,8 @@ __device__ __forceinline__ void state_load(const float* src, f32x4 (&S)[8]) {
 struct WidePlan {
   int nch, L0, L, P;
   float* fh;   // [B * H][P][2][128][128] fp32: F then H of every segment
-  float* sin;  // [B * H][P][128][128] fp32: the state entering every segment (index 0 unused)
+  float* sin;  // [B * H][P][128][128] fp32: the forward's state entering every segment (index 0
+               // unused), or the adjoint's value at the end of every segment (index P - 1 unused)
 };
 
 // One segment [c0, c1) of one (b, h), all 128 value columns.
