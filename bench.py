@@ -226,9 +226,9 @@ def time_prefill(dr, torch, wl, steps, warmup):
 
 
 def time_segment_scan(dr, torch, wl, nseg, reps=3):
-    """The segment-parallel alternative to the sequential chunk scan, composed from the library's
-    own packed-sequence call (a measurement for the design record; dr_chunk_fwd does not take
-    this route).  Each head's T tokens split into nseg segments; because the chunk map is affine
+    """The segment-parallel scan composed from the library's own packed-sequence call, whose scans
+    are the sliced ones (a measurement for the design record: dr_chunk_fwd runs the same algebra in
+    its own full-width kernels, one workgroup per (b, h, segment) with all value columns).  Each head's T tokens split into nseg segments; because the chunk map is affine
     in (S0, v), one packed call over the first nseg - 1 segments with v = 0 and S0 = I gives the
     segments' state maps F, a second with S0 = 0 their offsets H; the segments' incoming states
     S_in[s] = F[s - 1] S_in[s - 1] + H[s - 1] are chained (nseg - 1 small matrix products per
@@ -431,8 +431,8 @@ def main():
     ap.add_argument("--workload", default=PREFILL,
                     help="prefill workload of the main line (default: %(default)s)")
     ap.add_argument("--segment-scan", type=int, default=0, metavar="P",
-                    help="also time the segment-parallel scan alternative with P segments per head on "
-                         "the main workload (composed from dr_chunk_fwd_varlen; design record only)")
+                    help="also time the segment-parallel scan composed from dr_chunk_fwd_varlen (sliced "
+                         "scans) with P segments per head on the main workload (design record only)")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="also run one plain elementwise copy of this many MiB (a known-size "
                          "reference for HBM byte counters)")
